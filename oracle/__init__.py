@@ -1,0 +1,378 @@
+"""CPU oracle of the single-rank MoE hot path -- TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The product path (``combine_dp_gather_amd``)
+never does, and this package imports nothing from it.
+
+Every step is a plain definition: integer work in C (``moe_oracle.c``: exact gate
+logits, top-k selection, the dispatch counting sort) and floating-point expert
+maths in numpy float64.  Pages followed:
+
+* the SGLang walkthrough "SGLang 源码完全拆解(十七): DP Attention 与专家并行"
+  (below: "the SGLang page"),
+* the vLLM walkthrough "vLLM 源码完全拆解(二十七): Dual Batch Overlap" ("the vLLM page"),
+* the DP note at zdszero.github.io ("DP"), section "跳过同步：用约定代替通信".
+
+Pinned by ``tests/test_oracle_*.py`` against brute force, closed forms, library
+routines (stable sort, float64 matmul) and invariants; see each function.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import subprocess
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "moe_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+MAX_LEN, SUM_LEN = "max", "sum"
+
+
+def build(force: bool = False) -> str:
+    """Compile moe_oracle.c with gcc (no fast-math, no contraction, OpenMP)."""
+    stale = (not os.path.exists(_LIB_PATH)) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)
+    if force or stale:
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
+                               "-fopenmp", "-fPIC", "-shared", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        P = ctypes.c_void_p
+        i64, i32, d = ctypes.c_int64, ctypes.c_int, ctypes.c_double
+        lib.oracle_gate_logits.argtypes = [P, P, P, i64, i64, i64, P]
+        lib.oracle_exp.argtypes = [d]
+        lib.oracle_exp.restype = d
+        lib.oracle_sigmoid.argtypes = [d]
+        lib.oracle_sigmoid.restype = d
+        lib.oracle_select_softmax.argtypes = [P, P, i64, i32, i32, i32, P, P]
+        lib.oracle_select_grouped.argtypes = [P, P, P, i64, i32, i32, i32, i32, i32, i32, P, P]
+        lib.oracle_dispatch.argtypes = [P, i64, i32, P, P, i32, i32, i32, i32, i32, i64,
+                                        P, P, P, P, P, P]
+        lib.oracle_e4m3_decode.argtypes = [P, i64, P]
+        _lib = lib
+    return _lib
+
+
+def _p(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+# ============================================================================ O1 gather layout
+
+def gather_layout(num_tokens: Sequence[int], mode: str = "auto", is_extend: bool = False,
+                  max_len_with_idle: bool = False, static_bound: int = 0):
+    """Global-buffer layout of one DP gather.  Returns (mode, G, offsets[W+1], sizes[W]).
+
+    * offsets: prefix sums of the replica token counts (SGLang page, section
+      "本 rank 的切片位置怎么算": replica i starts at the sum of the counts before it).
+    * MAX_LEN pads every replica to max(n); SUM_LEN concatenates (section
+      "DpPaddingMode：补齐到最长还是补齐到总和").  MAX_LEN offsets are i*max(n).
+    * auto: prefill with more than one replica -> SUM_LEN, unless max_len_with_idle and
+      some replica is idle -> MAX_LEN; otherwise MAX_LEN iff 2*sum >= max*width
+      (the cost rule of the same section; back-end specific branches dropped).
+    * static_bound B > 0: every replica counts as B tokens and the offset of
+      replica i is i*B (DP note, section "跳过同步：用约定代替通信").
+    * all replicas idle: G = 0, nothing runs (SGLang page, section "空闲副本也必须参与").
+    """
+    n = [int(v) for v in num_tokens]
+    W = len(n)
+    if W == 0 or any(v < 0 for v in n):
+        raise ValueError("bad num_tokens")
+    if static_bound > 0:
+        if any(v > static_bound for v in n):
+            raise ValueError("replica exceeds the static bound")
+        n = [static_bound] * W
+    mx, sm = max(n), sum(n)
+    if mode == "auto":
+        if is_extend and W > 1:
+            mode = MAX_LEN if (max_len_with_idle and min(n) == 0) else SUM_LEN
+        else:
+            mode = MAX_LEN if sm * 2 >= mx * W else SUM_LEN
+    if mode not in (MAX_LEN, SUM_LEN):
+        raise ValueError(mode)
+    if sm == 0:
+        return mode, 0, [0] * (W + 1), n
+    if mode == SUM_LEN:
+        offs = [0]
+        for v in n:
+            offs.append(offs[-1] + v)
+        return mode, sm, offs, n
+    return mode, W * mx, [i * mx for i in range(W + 1)], n
+
+
+def gather(layout, replicas: Sequence[np.ndarray], H: int, dtype) -> tuple:
+    """global[off_i + r] = x_i[r] for r < n_i; every other row 0 with row_valid 0
+    (SGLang page, section "两种 gather": zero the buffer, then write each slice at its
+    offset)."""
+    mode, G, offs, sizes = layout
+    glob = np.zeros((G, H), dtype=dtype)
+    valid = np.zeros(G, dtype=np.int32)
+    for i, x in enumerate(replicas):
+        ni = sizes[i]
+        if ni == 0:
+            continue
+        glob[offs[i]:offs[i] + ni] = x[:ni]
+        valid[offs[i]:offs[i] + ni] = 1
+    return glob, valid
+
+
+def scatter(layout, out: np.ndarray) -> List[np.ndarray]:
+    """y_i[r] = out[off_i + r] for r < n_i: the inverse of gather with the same counts
+    (SGLang page, section "scatter：把 MoE 的输出还回本副本").  One GPU holds the whole
+    expert set of this rank, so no cross-rank sum takes place."""
+    mode, G, offs, sizes = layout
+    return [out[offs[i]:offs[i] + sizes[i]].copy() for i in range(len(sizes))]
+
+
+# ============================================================================ O2 routing
+
+def as_f32(a: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) or fp32 -> fp32 (exact)."""
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << np.uint32(16)).view(np.float32)
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+def gate_logits(x: np.ndarray, w: np.ndarray, row_valid: Optional[np.ndarray] = None) -> np.ndarray:
+    """fp32 router logits, ascending-h fmaf chain per (row, expert)."""
+    lib = _load()
+    xf, wf = as_f32(x), as_f32(w)
+    G, H = xf.shape
+    E = wf.shape[0]
+    out = np.empty((G, E), dtype=np.float32)
+    rv = None if row_valid is None else np.ascontiguousarray(row_valid, dtype=np.int32)
+    if G:
+        lib.oracle_gate_logits(_p(xf), _p(wf), _p(rv), G, E, H, _p(out))
+    return out
+
+
+def exp_defined(x: float) -> float:
+    return _load().oracle_exp(float(x))
+
+
+def sigmoid_defined(x: float) -> float:
+    return _load().oracle_sigmoid(float(x))
+
+
+def select_softmax(logits: np.ndarray, k: int, renormalize: bool = False,
+                   row_valid: Optional[np.ndarray] = None):
+    lib = _load()
+    lg = np.ascontiguousarray(logits, dtype=np.float32)
+    G, E = lg.shape
+    ids = np.empty((G, k), dtype=np.int32)
+    w = np.empty((G, k), dtype=np.float32)
+    rv = None if row_valid is None else np.ascontiguousarray(row_valid, dtype=np.int32)
+    if G:
+        lib.oracle_select_softmax(_p(lg), _p(rv), G, E, k, int(renormalize), _p(ids), _p(w))
+    return ids, w
+
+
+def select_grouped(logits: np.ndarray, bias: Optional[np.ndarray], n_group: int, topk_group: int,
+                   k: int, renormalize: bool = True, group_topn: int = 2,
+                   row_valid: Optional[np.ndarray] = None):
+    lib = _load()
+    lg = np.ascontiguousarray(logits, dtype=np.float32)
+    G, E = lg.shape
+    assert E % n_group == 0
+    ids = np.empty((G, k), dtype=np.int32)
+    w = np.empty((G, k), dtype=np.float32)
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+    rv = None if row_valid is None else np.ascontiguousarray(row_valid, dtype=np.int32)
+    if G:
+        lib.oracle_select_grouped(_p(lg), _p(b), _p(rv), G, E, n_group, topk_group, group_topn,
+                                  k, int(renormalize), _p(ids), _p(w))
+    return ids, w
+
+
+def route(cfg, x: np.ndarray, row_valid: np.ndarray, router_w: np.ndarray, bias):
+    """Gate logits then the config's selection rule."""
+    logits = gate_logits(x, router_w, row_valid)
+    if cfg.route == "softmax":
+        ids, w = select_softmax(logits, cfg.top_k, cfg.renormalize, row_valid)
+    else:
+        ids, w = select_grouped(logits, bias, cfg.n_group, cfg.topk_group, cfg.top_k,
+                                cfg.renormalize, cfg.group_topn, row_valid)
+    return logits, ids, w
+
+
+# ============================================================================ O3 dispatch
+
+def dispatch(ids: np.ndarray, phys_of: np.ndarray, n_rep: np.ndarray, p0: int, El: int,
+             align: int = 1, cap: Optional[int] = None) -> dict:
+    """Counting-sort plan for the rank's slots (see oracle_dispatch in moe_oracle.c)."""
+    lib = _load()
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    G, k = ids.shape
+    P = G * k
+    if cap is None:
+        cap = G * min(k, El) + El * (align - 1)
+    phys = np.ascontiguousarray(phys_of, dtype=np.int32)
+    nrep = np.ascontiguousarray(n_rep, dtype=np.int32)
+    E, max_rep = phys.shape
+    counts = np.zeros(El, dtype=np.int32)
+    seg = np.zeros(El + 1, dtype=np.int64)
+    sorted_pair = np.full(max(cap, 1), -2, dtype=np.int32)
+    pair_row = np.full(max(P, 1), -2, dtype=np.int32)
+    num_rows = np.zeros(1, dtype=np.int64)
+    err = np.zeros(1, dtype=np.int32)
+    lib.oracle_dispatch(_p(ids), G, k, _p(phys), _p(nrep), max_rep, E, p0, El, align, cap,
+                        _p(counts), _p(seg), _p(sorted_pair), _p(pair_row), _p(num_rows), _p(err))
+    rows = int(min(num_rows[0], cap))
+    return dict(counts=counts, seg_offsets=seg, sorted_pair=sorted_pair[:rows],
+                pair_row=pair_row[:P], num_rows=int(num_rows[0]), error_flag=int(err[0]),
+                cap=int(cap), k=k)
+
+
+def permute_rows(global_x: np.ndarray, plan: dict) -> np.ndarray:
+    """x_perm[row] = global_x[sorted_pair[row] // k]; alignment pad rows are 0."""
+    sp = plan["sorted_pair"]
+    xp = np.zeros((len(sp),) + global_x.shape[1:], dtype=global_x.dtype)
+    m = sp >= 0
+    xp[m] = global_x[sp[m] // plan["k"]]
+    return xp
+
+
+# ============================================================================ O4 SwiGLU experts
+
+def e4m3_decode(q: np.ndarray) -> np.ndarray:
+    lib = _load()
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    out = np.empty(q.shape, dtype=np.float64)
+    lib.oracle_e4m3_decode(_p(q), q.size, _p(out))
+    return out
+
+
+def dequant_block(q: np.ndarray, s: np.ndarray, block: int = 128) -> np.ndarray:
+    """value = e4m3(q) * scale[r // 128, c // 128], exact in float64."""
+    v = e4m3_decode(q)
+    return v * np.repeat(np.repeat(s.astype(np.float64), block, axis=-2), block, axis=-1)
+
+
+def expert_weights_f64(inp, slot: int):
+    """(Wg [I,H], Wu [I,H], Wd [H,I]) of one local slot in float64."""
+    if inp.w13 is not None:
+        return (as_f32(inp.w13[slot, 0]).astype(np.float64),
+                as_f32(inp.w13[slot, 1]).astype(np.float64),
+                as_f32(inp.w2[slot]).astype(np.float64))
+    return (dequant_block(inp.w13_q[slot, 0], inp.w13_s[slot, 0]),
+            dequant_block(inp.w13_q[slot, 1], inp.w13_s[slot, 1]),
+            dequant_block(inp.w2_q[slot], inp.w2_s[slot]))
+
+
+def swiglu(x: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray) -> np.ndarray:
+    """y = (silu(x Wg^T) * (x Wu^T)) Wd^T in float64, silu(z) = z / (1 + e^-z).
+    gate_proj/up_proj are [I, H] and down_proj [H, I] (SGLang page, section "EP 下专家
+    权重切不均匀的问题"); MM1, activation, MM2 in that order (vLLM page, modular-kernel
+    block figure caption)."""
+    gt = x @ wg.T
+    u = x @ wu.T
+    h = gt / (1.0 + np.exp(-gt)) * u
+    return h @ wd.T
+
+
+def expert_ffn(x_perm: np.ndarray, plan: dict, inp) -> np.ndarray:
+    """y_perm rows of every segment; alignment pad rows stay 0.  float64."""
+    rows = len(plan["sorted_pair"])
+    H = inp.cfg.hidden
+    y = np.zeros((rows, H), dtype=np.float64)
+    seg, counts = plan["seg_offsets"], plan["counts"]
+    xf = as_f32(x_perm).astype(np.float64)
+    for e in range(len(counts)):
+        a = int(seg[e])
+        b = min(int(seg[e]) + int(counts[e]), rows)
+        if b <= a:
+            continue
+        wg, wu, wd = expert_weights_f64(inp, e)
+        y[a:b] = swiglu(xf[a:b], wg, wu, wd)
+    return y
+
+
+# ============================================================================ O5 combine
+
+def combine(y_perm: np.ndarray, plan: dict, weights: np.ndarray, G: int,
+            routed_scale: float = 1.0) -> np.ndarray:
+    """out[g] = scale * sum_{j ascending, pair_row >= 0} w[g,j] * y[pair_row[g*k+j]] (float64);
+    rows with no local pair are 0.  The finalize step applies the top-k weights after the
+    un-permute (vLLM page, modular-kernel figure caption), and the combine call itself is
+    given no weights (vLLM page, section "第 3 段：combine 前再交一次棒")."""
+    k = plan["k"]
+    yf = as_f32(y_perm).astype(np.float64) if y_perm.dtype != np.float64 else y_perm
+    H = yf.shape[1] if yf.ndim == 2 else 0
+    out = np.zeros((G, H), dtype=np.float64)
+    pr = plan["pair_row"].reshape(G, k)
+    w = weights.astype(np.float64)
+    for j in range(k):
+        m = pr[:, j] >= 0
+        out[m] += w[m, j:j + 1] * yf[pr[m, j]]
+    return out * routed_scale
+
+
+# ============================================================================ per-token form
+
+def token_output(inp, g: int, x_row: np.ndarray, ids_row: np.ndarray, w_row: np.ndarray,
+                 weights_cache: Optional[dict] = None) -> np.ndarray:
+    """Output of one global row computed directly:  scale * sum_j w_j * FFN_{slot(g,j)}(x_g)
+    over the pairs that land on a local slot.  Equal to dispatch -> experts -> combine for
+    that row; used to sample full-size outputs one row at a time."""
+    cfg = inp.cfg
+    x = as_f32(x_row).astype(np.float64)[None, :]
+    out = np.zeros(cfg.hidden, dtype=np.float64)
+    for j in range(len(ids_row)):
+        l = int(ids_row[j])
+        if l < 0:
+            continue
+        p = int(inp.phys_of[l, g % int(inp.n_rep[l])])
+        e = p - cfg.first_local
+        if not (0 <= e < cfg.num_local):
+            continue
+        if weights_cache is not None and e in weights_cache:
+            wts = weights_cache[e]
+        else:
+            wts = expert_weights_f64(inp, e)
+            if weights_cache is not None:
+                weights_cache[e] = wts
+        out += float(w_row[j]) * swiglu(x, *wts)[0]
+    return out * cfg.routed_scale
+
+
+# ============================================================================ whole layer
+
+def run_layer(inp, mode: str = "sum", align: int = 1, cap: Optional[int] = None) -> dict:
+    """All six steps on the inputs of one workload; returns every intermediate."""
+    cfg = inp.cfg
+    dt = np.float32 if cfg.dtype == "f32" else np.uint16
+    layout = gather_layout(cfg.num_tokens, mode, static_bound=cfg.static_bound)
+    G = layout[1]
+    gx, valid = gather(layout, inp.replicas, cfg.hidden, dt)
+    logits, ids, w = route(cfg, gx, valid, inp.router_w, inp.bias)
+    plan = dispatch(ids, inp.phys_of, inp.n_rep, cfg.first_local, cfg.num_local, align, cap)
+    xp = permute_rows(gx, plan)
+    y = expert_ffn(xp, plan, inp)
+    out = combine(y, plan, w, G, cfg.routed_scale)
+    return dict(layout=layout, global_x=gx, row_valid=valid, logits=logits, ids=ids, weights=w,
+                plan=plan, x_perm=xp, y_perm=y, out=out, replicas_out=scatter(layout, out))
+
+
+def rel_err(got: np.ndarray, ref: np.ndarray) -> float:
+    """max|got - ref| / max|ref| (infinity-norm relative error)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if ref.size == 0:
+        return 0.0
+    den = float(np.max(np.abs(ref)))
+    num = float(np.max(np.abs(got - ref)))
+    return num / den if den > 0 else num
