@@ -1,0 +1,197 @@
+#!/usr/bin/env python3
+"""Throughput of one rank's MoE layer (DP gather -> route -> dispatch -> SwiGLU grouped GEMM
+-> combine -> scatter) on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload cfg4]
+
+A step is one pass of all six C-ABI calls over one batch whose inputs are already resident
+in HBM.  Prints one JSON line: tokens/s, the roofline of the dominant kernel (timed with HIP
+events on the stream the kernels run on), per-kernel breakdown, and the CPU oracle timed on
+a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
+BF16_MFMA_PEAK_TFLOPS = 2500.0   # dense bf16 MFMA, TFLOP/s
+FP32_VALU_PEAK_TFLOPS = 78.6     # 256 CU x 64 FMA/clk x 2 x 2.4 GHz (no packed fp32)
+
+WORKLOAD_TEXT = {
+    "cfg1": "tiny-fp32: 1 replica x 64 tokens, H=256, E=8 top-2 softmax, I=128",
+    "cfg2": "dp4-gather: replicas [37,0,128,5], H=2048, E=64 top-6 softmax, I=1408",
+    "cfg3": "dsv3-decode-ep16-B24: 16 replicas x 24 (static bound), H=7168, E=256 grouped top-8, "
+            "16 local experts, I=2048",
+    "cfg4": "dsv3-prefill-ep16: 8 DP replicas x 4096 tokens, H=7168, E=256 grouped (8 groups, "
+            "top-4 groups, top-8), 16 local experts of 256, I=2048",
+    "cfg5": "dsv3-zipf-fp8: 8 x 2048 tokens, H=7168, E=256 grouped + Zipf bias, 16 slots / 12 "
+            "logical, fp8 weights, I=2048",
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(inp, sample_per_replica: int):
+    """The oracle as it stands on the first rows of every replica (a bounded sample)."""
+    import oracle
+    from dataclasses import replace
+    import moe_synth
+    cfg = inp.cfg
+    n = [min(sample_per_replica, v) for v in cfg.num_tokens]
+    scfg = replace(cfg, num_tokens=tuple(n), static_bound=0)
+    sinp = moe_synth.MoEInputs(cfg=scfg, replicas=[r[:k] for r, k in zip(inp.replicas, n)],
+                               router_w=inp.router_w, bias=inp.bias, w13=inp.w13, w2=inp.w2,
+                               w13_q=inp.w13_q, w13_s=inp.w13_s, w2_q=inp.w2_q, w2_s=inp.w2_s,
+                               phys_of=inp.phys_of, n_rep=inp.n_rep)
+    oracle.build()
+    t0 = time.perf_counter()
+    oracle.run_layer(sinp, "sum")
+    dt = time.perf_counter() - t0
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": round(sum(n) / dt, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {sample_per_replica} tokens of each replica ({sum(n)} tokens), all six "
+                      f"steps, oracle wall time {dt:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="cfg4")
+    ap.add_argument("--mode", default="sum", choices=["sum", "max", "auto"])
+    ap.add_argument("--cpu-sample", type=int, default=256, help="tokens per replica for the oracle")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU: this path has no multi-GPU mode "
+              f"(--gpus {args.gpus} requested)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import moe_synth
+    from combine_dp_gather_amd.layer import DeviceWeights, MoELayer, spec_of
+
+    cfg = moe_synth.CONFIGS[args.workload]
+    t0 = time.time()
+    inp = moe_synth.make_inputs(cfg)
+    log(f"[bench] inputs {cfg.name} generated in {time.time() - t0:.1f}s")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    act = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
+    w = DeviceWeights(inp, dev)
+    layer = MoELayer(spec_of(cfg), w, cfg.num_tokens, act, mode=args.mode,
+                     static_bound=cfg.static_bound, device=dev)
+    bf = cfg.dtype == "bf16"
+    reps = []
+    for r in inp.replicas:
+        t = torch.from_numpy(np.ascontiguousarray(r))
+        reps.append((t.view(torch.bfloat16) if bf else t).to(dev))
+    torch.cuda.synchronize()
+    log(f"[bench] resident in HBM; G={layer.G}")
+
+    stream = torch.cuda.current_stream()
+    names = ["gather", "route", "dispatch", "gemm_up", "gemm_down", "combine", "scatter"]
+    calls = [lambda: layer.gather(reps), layer.route, layer.dispatch,
+             lambda: layer.experts_up(), lambda: layer.experts_down(), layer.combine, layer.scatter]
+
+    def step(evs=None):
+        for i, c in enumerate(calls):
+            if evs is not None:
+                evs[i][0].record(stream)
+            c()
+            if evs is not None:
+                evs[i][1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    R = int(layer.plan.counts.sum().item())
+    overflow = int(layer.plan.error_flag.item())
+    log(f"[bench] warmup done; routed local pairs R={R} overflow={overflow}")
+
+    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+           for _ in names] for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    t_wall = time.perf_counter()
+    for s in range(args.steps):
+        step(ev[s])
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    total_ms = start.elapsed_time(stop)
+    per = {n: float(np.mean([ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)]))
+           for i, n in enumerate(names)}
+    ms_per_step = total_ms / args.steps
+    T = cfg.T
+    H, I, E, k, G = cfg.hidden, cfg.inter, cfg.num_experts, cfg.top_k, layer.G
+    es = 2 if bf else 4
+    # algorithmic work per call (bytes or flops), per-unit figures x units
+    work = {
+        "gather": ("hbm", (T + G) * H * es + 4 * G),                   # read T rows, write G rows
+        "route": ("alu", 2.0 * G * E * H),                             # exact fp32 fma chain
+        "dispatch": ("hbm", 2 * R * H * es + 3 * 4 * G * k + 8 * R),  # x_perm copy + id passes
+        "gemm_up": ("mfma", 4.0 * R * H * I),                          # gate+up: 2*R*H*2I
+        "gemm_down": ("mfma", 2.0 * R * I * H),
+        "combine": ("hbm", R * H * es + G * H * es + 8 * G * k),      # read R rows, write G rows
+        "scatter": ("hbm", 2 * T * H * es),
+    }
+    peaks = {"hbm": HBM_PEAK_GBS, "alu": FP32_VALU_PEAK_TFLOPS, "mfma": BF16_MFMA_PEAK_TFLOPS}
+    kernels = {}
+    for n in names:
+        bound, amount = work[n]
+        t_s = per[n] / 1e3
+        if bound == "hbm":
+            ach = amount / t_s / 1e9 if t_s > 0 else 0.0
+            unit = "GB/s"
+        else:
+            ach = amount / t_s / 1e12 if t_s > 0 else 0.0
+            unit = "TFLOP/s"
+        kernels[n] = {"ms": round(per[n], 4), "bound": bound, "achieved": round(ach, 2),
+                      "peak": peaks[bound], "unit": unit, "frac": round(ach / peaks[bound], 4)}
+    dom = "gemm_up"
+    roof = dict(kernels[dom])
+    roof.pop("ms")
+    roof["kernel"] = "grouped_gemm_bf16_kernel<up> (gate+up SwiGLU)"
+    roof["traffic"] = None
+    result = {
+        "metric": "MoE-layer tokens/s at 1 GPU; grouped-GEMM % peak MFMA; dispatch/combine % HBM",
+        "value": round(T * args.steps / (total_ms / 1e3), 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if bf else "f32",
+        "data": "synthetic (seeded PCG64; random-init DeepSeek-V3-shaped expert weights)",
+        "config": {"workload": WORKLOAD_TEXT[args.workload], "name": cfg.name,
+                   "tokens": T, "global_rows": G, "gather_mode": args.mode,
+                   "routed_local_pairs": R, "parallelism": "one EP rank's share on 1 GPU"},
+        "roofline": roof,
+        "kernels": kernels,
+        "wall_s_timed": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_sample)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,280 @@
+// Dispatch: the (token, k) pairs of this rank's local expert slots, counting-sorted into one
+// contiguous segment per slot, and the permuted copy of the activations.
+//
+// SGLang walkthrough "SGLang 源码完全拆解(十七): DP Attention 与专家并行":
+//   - section "normal dispatch 的调用链": get_dispatch_layout's per-expert counts come first,
+//     expert_alignment rounds each expert's rows up for the grouped GEMM tiles, and the
+//     dispatch "handle" records where every pair went so that combine can bring it back;
+//   - section "推理时怎么“选副本”": with redundant experts every rank must pick the same
+//     physical replica for a token (rank_invariant), so the pick depends only on the global
+//     row index: replica g mod n_rep.
+//
+// Kernels (one rank, one GPU, no atomics deciding any order):
+//   1. count:   each block takes kChunk consecutive pairs and builds a per-slot histogram in
+//               LDS (integer LDS atomics: the counts do not depend on their order);
+//   2. scan:    one block turns the per-block histograms into per-block bases (column prefix
+//               over blocks), per-slot counts and the aligned exclusive scan seg_offsets;
+//   3. place:   each wave of a block owns a quarter of the block's pairs, walks it 64 pairs
+//               at a time and ranks equal slots with ballots (rank = popcount of the lanes
+//               below with the same slot), so rows follow ascending pair index: stable;
+//   4. permute: x_perm[row] = global_x[sorted_pair[row] / k], one wave per row, 16-byte
+//               vectors, rows bounded by the device-side num_rows (no host sync).
+#include "moe_dev.h"
+
+namespace moe {
+namespace {
+
+constexpr int D_THREADS = 256;
+constexpr int D_WAVES = D_THREADS / kWave;
+constexpr int kPairsPerThread = 16;
+constexpr int kChunk = D_THREADS * kPairsPerThread;  // 4096 pairs per block
+constexpr int kWaveChunk = kChunk / D_WAVES;         // 1024 pairs per wave
+constexpr int kMaxSlots = 1024;
+
+struct MapArgs {
+    const int32_t* phys_of;
+    const int32_t* n_rep;
+    int32_t E, max_rep, p0, El;
+};
+
+// local slot of pair f (global row g = f / k, logical id l), or -1
+__device__ __forceinline__ int pair_slot(int32_t l, int64_t g, const MapArgs& m) {
+    if (l < 0 || l >= m.E) return -1;
+    int32_t p = l;
+    if (m.phys_of) {
+        int32_t nr = m.n_rep[l];
+        nr = nr < 1 ? 1 : nr;
+        const int32_t r = static_cast<int32_t>(g % nr);
+        if (r >= m.max_rep) return -1;
+        p = m.phys_of[static_cast<int64_t>(l) * m.max_rep + r];
+    }
+    p -= m.p0;
+    return (p >= 0 && p < m.El) ? p : -1;
+}
+
+__global__ __launch_bounds__(D_THREADS) void count_kernel(const int32_t* __restrict__ ids,
+                                                          int64_t P, int k, MapArgs m,
+                                                          int32_t* __restrict__ blk_counts) {
+    __shared__ int32_t hist[kMaxSlots];
+    for (int e = threadIdx.x; e < m.El; e += D_THREADS) hist[e] = 0;
+    __syncthreads();
+    const int64_t base = static_cast<int64_t>(blockIdx.x) * kChunk;
+#pragma unroll 4
+    for (int i = 0; i < kPairsPerThread; ++i) {
+        const int64_t f = base + i * D_THREADS + threadIdx.x;
+        if (f < P) {
+            const int s = pair_slot(ids[f], f / k, m);
+            if (s >= 0) atomicAdd(&hist[s], 1);
+        }
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < m.El; e += D_THREADS)
+        blk_counts[static_cast<int64_t>(blockIdx.x) * m.El + e] = hist[e];
+}
+
+constexpr int SCAN_THREADS = 1024;
+
+__global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(
+    const int32_t* __restrict__ blk_counts, int64_t NB, int El, int align, int64_t cap,
+    int32_t* __restrict__ blk_base, int32_t* __restrict__ counts, int64_t* __restrict__ seg,
+    int64_t* __restrict__ num_rows, int32_t* __restrict__ error_flag,
+    int32_t* __restrict__ sorted_pair) {
+    __shared__ int64_t sc[SCAN_THREADS];
+    const int e = threadIdx.x;
+    int64_t padded = 0;
+    int32_t total = 0;
+    if (e < El) {
+        int32_t run = 0;
+        for (int64_t b = 0; b < NB; ++b) {
+            blk_base[b * El + e] = run;
+            run += blk_counts[b * El + e];
+        }
+        total = run;
+        counts[e] = run;
+        padded = (static_cast<int64_t>(run) + align - 1) / align * align;
+    }
+    // inclusive scan of the padded counts over slots (Hillis-Steele in LDS)
+    sc[e] = padded;
+    __syncthreads();
+    for (int off = 1; off < SCAN_THREADS; off <<= 1) {
+        const int64_t v = (e >= off) ? sc[e - off] : 0;
+        __syncthreads();
+        sc[e] += v;
+        __syncthreads();
+    }
+    if (e < El) {
+        const int64_t end = sc[e];
+        const int64_t start = end - padded;
+        seg[e + 1] = end;
+        if (e == 0) seg[0] = 0;
+        // alignment pad rows hold no pair
+        for (int64_t r = start + total; r < end && r < cap; ++r) sorted_pair[r] = -1;
+        if (e == El - 1) {
+            *num_rows = end;
+            *error_flag = end > cap ? 1 : 0;
+        }
+    }
+}
+
+__global__ __launch_bounds__(D_THREADS) void place_kernel(
+    const int32_t* __restrict__ ids, int64_t P, int k, MapArgs m,
+    const int32_t* __restrict__ blk_base, const int64_t* __restrict__ seg, int64_t cap,
+    int32_t* __restrict__ sorted_pair, int32_t* __restrict__ pair_row) {
+    __shared__ int32_t whist[D_WAVES][kMaxSlots];
+    __shared__ int64_t wbase[D_WAVES][kMaxSlots];
+    const int wv = threadIdx.x / kWave;
+    const int lane = lane_id();
+    const int El = m.El;
+    for (int i = threadIdx.x; i < D_WAVES * El; i += D_THREADS) whist[i / El][i % El] = 0;
+    __syncthreads();
+    const int64_t wstart = static_cast<int64_t>(blockIdx.x) * kChunk + wv * kWaveChunk;
+    // per-wave histogram of its pairs
+    for (int step = 0; step < kWaveChunk / kWave; ++step) {
+        const int64_t f = wstart + step * kWave + lane;
+        if (f < P) {
+            const int s = pair_slot(ids[f], f / k, m);
+            if (s >= 0) atomicAdd(&whist[wv][s], 1);
+        }
+    }
+    __syncthreads();
+    // first row of each wave's run of each slot
+    for (int e = threadIdx.x; e < El; e += D_THREADS) {
+        int64_t run = seg[e] + blk_base[static_cast<int64_t>(blockIdx.x) * El + e];
+        for (int w = 0; w < D_WAVES; ++w) {
+            wbase[w][e] = run;
+            run += whist[w][e];
+        }
+    }
+    __syncthreads();
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+    for (int step = 0; step < kWaveChunk / kWave; ++step) {
+        const int64_t f = wstart + step * kWave + lane;
+        const bool inb = f < P;
+        const int s = inb ? pair_slot(ids[f], f / k, m) : -1;
+        // lanes with the same slot: one ballot per distinct slot in the wave
+        uint64_t pending = __ballot(s >= 0);
+        uint64_t mine = 0;
+        while (pending) {
+            const int leader = __ffsll(static_cast<long long>(pending)) - 1;
+            const int ls = __shfl(s, leader);
+            const uint64_t same = __ballot(s == ls);
+            if (s == ls) mine = same;
+            pending &= ~same;
+        }
+        int64_t row = -1;
+        if (s >= 0) row = wbase[wv][s] + __popcll(mine & below);
+        // the lowest lane of each slot advances the wave's running row for it
+        if (s >= 0 && (mine & below) == 0) wbase[wv][s] += __popcll(mine);
+        if (inb) {
+            if (row >= 0 && row < cap) {
+                sorted_pair[row] = static_cast<int32_t>(f);
+                pair_row[f] = static_cast<int32_t>(row);
+            } else {
+                pair_row[f] = -1;
+            }
+        }
+    }
+}
+
+template <typename V>
+__global__ __launch_bounds__(D_THREADS) void permute_kernel(
+    const V* __restrict__ x, const int32_t* __restrict__ sorted_pair,
+    const int64_t* __restrict__ num_rows, int64_t cap, int k, int64_t row_units,
+    V* __restrict__ x_perm) {
+    int64_t rows = *num_rows;
+    rows = rows < cap ? rows : cap;
+    const int lane = lane_id();
+    const int64_t nw = static_cast<int64_t>(gridDim.x) * D_WAVES;
+    for (int64_t r = static_cast<int64_t>(blockIdx.x) * D_WAVES + threadIdx.x / kWave; r < rows;
+         r += nw) {
+        const int32_t f = sorted_pair[r];
+        V* __restrict__ d = x_perm + r * row_units;
+        if (f >= 0) {
+            const V* __restrict__ s = x + static_cast<int64_t>(f / k) * row_units;
+            int64_t c = lane;
+            for (; c + 3 * kWave < row_units; c += 4 * kWave) {
+                const V v0 = s[c], v1 = s[c + kWave], v2 = s[c + 2 * kWave], v3 = s[c + 3 * kWave];
+                d[c] = v0;
+                d[c + kWave] = v1;
+                d[c + 2 * kWave] = v2;
+                d[c + 3 * kWave] = v3;
+            }
+            for (; c < row_units; c += kWave) d[c] = s[c];
+        } else {
+            for (int64_t c = lane; c < row_units; c += kWave) d[c] = V{};
+        }
+    }
+}
+
+template <typename V>
+moe_status launch_permute(const void* x, const moe_plan* plan, int64_t row_bytes, void* x_perm,
+                          hipStream_t stream) {
+    const int64_t row_units = row_bytes / static_cast<int64_t>(sizeof(V));
+    int64_t blocks = ceil_div(plan->cap, D_WAVES);
+    if (blocks > 2048) blocks = 2048;
+    hipLaunchKernelGGL(permute_kernel<V>, dim3(static_cast<unsigned>(blocks)), dim3(D_THREADS), 0,
+                       stream, static_cast<const V*>(x), plan->sorted_pair, plan->num_rows,
+                       plan->cap, plan->top_k, row_units, static_cast<V*>(x_perm));
+    MOE_LAUNCH_CHECK();
+    return MOE_OK;
+}
+
+int64_t num_blocks(int64_t G, int32_t k) { return ceil_div(G * k, kChunk); }
+
+}  // namespace
+}  // namespace moe
+
+extern "C" size_t moe_dispatch_workspace_size(int64_t G, int32_t k, int32_t num_slots) {
+    if (G < 0 || k < 1 || num_slots < 1) return 0;
+    const int64_t nb = moe::num_blocks(G, k);
+    return static_cast<size_t>(2 * nb * num_slots) * sizeof(int32_t) + 256;
+}
+
+extern "C" moe_status moe_dispatch(const void* global_x, const int32_t* topk_ids, int64_t G,
+                                   int32_t k, int64_t H, moe_dtype dt, const moe_expert_map* map,
+                                   const moe_plan* plan, void* x_perm, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream) {
+    using namespace moe;
+    MOE_CHECK_ARG(map && plan);
+    MOE_CHECK_ARG(G >= 0 && k >= 1 && H > 0);
+    MOE_CHECK_ARG(dt == MOE_F32 || dt == MOE_BF16);
+    MOE_CHECK_ARG(plan->G == G && plan->top_k == k);
+    MOE_CHECK_ARG(plan->num_slots == map->num_slots);
+    MOE_CHECK_ARG(map->num_slots >= 1 && map->num_slots <= kMaxSlots);
+    MOE_CHECK_ARG(map->num_logical >= 1 && map->first_slot >= 0);
+    MOE_CHECK_ARG(map->phys_of == nullptr || (map->n_rep != nullptr && map->max_rep >= 1));
+    MOE_CHECK_ARG(plan->align >= 1 && plan->cap >= 0);
+    MOE_CHECK_ARG(plan->counts && plan->seg_offsets && plan->num_rows && plan->error_flag);
+    MOE_CHECK_ARG(G * k < (int64_t(1) << 31));
+    if (G > 0) MOE_CHECK_ARG(topk_ids && plan->pair_row && global_x);
+    if (plan->cap > 0) MOE_CHECK_ARG(plan->sorted_pair && x_perm);
+    const int64_t P = G * k;
+    const int64_t NB = num_blocks(G, k);
+    const int El = map->num_slots;
+    if (workspace_bytes < moe_dispatch_workspace_size(G, k, El)) return MOE_ERR_CAPACITY;
+    MOE_CHECK_ARG(NB == 0 || workspace != nullptr);
+    MapArgs m{map->phys_of, map->n_rep, map->num_logical, map->max_rep, map->first_slot, El};
+    int32_t* blk_counts = static_cast<int32_t*>(workspace);
+    int32_t* blk_base = blk_counts + NB * El;
+    if (NB > 0) {
+        hipLaunchKernelGGL(count_kernel, dim3(static_cast<unsigned>(NB)), dim3(D_THREADS), 0, stream,
+                           topk_ids, P, k, m, blk_counts);
+        MOE_LAUNCH_CHECK();
+    }
+    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(SCAN_THREADS), 0, stream, blk_counts, NB, El,
+                       plan->align, plan->cap, blk_base, plan->counts, plan->seg_offsets,
+                       plan->num_rows, plan->error_flag, plan->sorted_pair);
+    MOE_LAUNCH_CHECK();
+    if (NB == 0) return MOE_OK;
+    hipLaunchKernelGGL(place_kernel, dim3(static_cast<unsigned>(NB)), dim3(D_THREADS), 0, stream,
+                       topk_ids, P, k, m, blk_base, plan->seg_offsets, plan->cap,
+                       plan->sorted_pair, plan->pair_row);
+    MOE_LAUNCH_CHECK();
+    if (plan->cap == 0) return MOE_OK;
+    const int64_t row_bytes = H * dtype_size(dt);
+    if (row_bytes % 16 == 0 && aligned(global_x, 16) && aligned(x_perm, 16))
+        return launch_permute<uint4>(global_x, plan, row_bytes, x_perm, stream);
+    if (row_bytes % 4 == 0 && aligned(global_x, 4) && aligned(x_perm, 4))
+        return launch_permute<uint32_t>(global_x, plan, row_bytes, x_perm, stream);
+    return launch_permute<uint16_t>(global_x, plan, row_bytes, x_perm, stream);
+}

@@ -1,0 +1,435 @@
+// SwiGLU experts as two grouped GEMMs over the dispatch segments.
+//
+// Per local slot e and every row r of its segment (SGLang walkthrough "SGLang 源码完全拆解
+// (十七): DP Attention 与专家并行", section "EP 下专家权重切不均匀的问题": gate_proj and up_proj
+// are [I, H], down_proj [H, I], and experts stay whole per rank so each GEMM keeps its full
+// size; vLLM walkthrough "vLLM 源码完全拆解(二十七)", modular-kernel figure: MM1, activation,
+// MM2 between permute and unpermute):
+//     h[r, i] = silu(sum_h x[r,h] Wg[e][i,h]) * (sum_h x[r,h] Wu[e][i,h])
+//     y[r, c] = sum_i h[r,i] Wd[e][c,i]
+//
+// bf16 path (gfx950 MFMA v_mfma_f32_32x32x16_bf16, fp32 accumulate):
+//   - block tile 256 rows x 256 columns, K slices of 64, 4 waves in a 2x2 grid, each wave
+//     128x128 = 4x4 MFMA blocks (256 fp32 accumulators per lane);
+//   - up kernel: the 256 columns are 128 gate columns and the same 128 up columns, so each
+//     lane holds gate and up for identical (row, i) and applies SiLU*up in registers;
+//   - operands staged global -> registers -> LDS (row stride 72 bf16: 16-byte skew per row
+//     keeps the 16-byte fragment reads of 8 consecutive rows on distinct banks),
+//     double-buffered so the next slice's loads are in flight during the MFMAs;
+//   - persistent grid (one block per CU): tiles (slot, m-tile, n-tile) are numbered on the
+//     device from counts[] (no host sync) and taken round-robin; rows past a segment's end
+//     load as zeros and are never stored; every output tile has exactly one owner.
+#include <hip/hip_runtime.h>
+
+#include "moe_dev.h"
+
+namespace moe {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx16_t __attribute__((ext_vector_type(16)));
+
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int M_THREADS = 256;
+constexpr int LDS_STRIDE = BK + 8;  // bf16 elements per LDS row
+constexpr int kMaxSlots = 1024;
+constexpr int UP_COLS = BN / 2;     // i-columns per up tile (gate and up each)
+
+struct GemmArgs {
+    const uint16_t* A;       // [cap, K] bf16 rows in segment order
+    const uint16_t* B;       // up: w13 [E_l, 2, I, H]; down: w2 [E_l, H, I]
+    uint16_t* C;             // up: h [cap, I]; down: y [cap, H]
+    const int32_t* counts;   // [E_l]
+    const int64_t* seg;      // [E_l + 1]
+    int64_t cap;
+    int64_t K;               // up: H; down: I
+    int64_t N;               // up: I; down: H
+    int32_t El;
+    int32_t NT;              // column tiles per m-tile
+};
+
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+
+typedef int v4i_t __attribute__((ext_vector_type(4)));
+constexpr int kBufferFlags = 0x00020000;  // raw buffer, 32-bit data format (gfx9 family)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                             static_cast<int>(bytes), kBufferFlags);
+}
+
+template <bool UP>
+__global__ __launch_bounds__(M_THREADS, 1) void grouped_gemm_bf16_kernel(GemmArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LDS_STRIDE];
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * LDS_STRIDE];
+    __shared__ int32_t tile_prefix[kMaxSlots + 1];  // m-tiles before slot e
+    __shared__ int32_t part[M_THREADS];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wv = tid >> 6;
+    const int wm = wv >> 1, wn = wv & 1;
+
+    // ---- number the tiles: slot e owns ceil(rows_e / BM) m-tiles
+    {
+        const int El = a.El;
+        int32_t loc[4];
+        int32_t s = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int e = tid * 4 + q;
+            int32_t mt = 0;
+            if (e < El) {
+                int64_t c = a.counts[e];
+                const int64_t room = a.cap - a.seg[e];
+                c = c < room ? c : (room > 0 ? room : 0);
+                mt = static_cast<int32_t>((c + BM - 1) / BM);
+            }
+            loc[q] = mt;
+            s += mt;
+        }
+        part[tid] = s;
+        __syncthreads();
+        for (int off = 1; off < M_THREADS; off <<= 1) {
+            const int32_t v = tid >= off ? part[tid - off] : 0;
+            __syncthreads();
+            part[tid] += v;
+            __syncthreads();
+        }
+        int32_t run = part[tid] - s;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int e = tid * 4 + q;
+            if (e < El) tile_prefix[e] = run;
+            run += loc[q];
+        }
+        if (tid == M_THREADS - 1) tile_prefix[El] = part[tid];
+        __syncthreads();
+    }
+    const int32_t total_mt = tile_prefix[a.El];
+    const int64_t total_tiles = static_cast<int64_t>(total_mt) * a.NT;
+    const uint32_t row_bytes = static_cast<uint32_t>(a.K) * 2u;
+    const int lr = tid >> 3;       // first LDS row this thread fills (then + 32 p)
+    const int ch = tid & 7;        // 16-byte chunk of the 128-byte K slice
+
+    for (int64_t t = blockIdx.x; t < total_tiles; t += gridDim.x) {
+        const int32_t em = static_cast<int32_t>(t / a.NT);
+        const int32_t nt = static_cast<int32_t>(t % a.NT);
+        int lo = 0, hi = a.El;
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (tile_prefix[mid] <= em) lo = mid;
+            else hi = mid;
+        }
+        const int e = lo;
+        const int32_t mtile = em - tile_prefix[e];
+        const int64_t seg_start = a.seg[e];
+        int64_t seg_end = seg_start + a.counts[e];
+        seg_end = seg_end < a.cap ? seg_end : a.cap;
+        const int64_t row0 = seg_start + static_cast<int64_t>(mtile) * BM;
+        const int64_t nrows64 = seg_end - row0;
+        const uint32_t nrows = static_cast<uint32_t>(nrows64 < BM ? nrows64 : BM);
+
+        // A: rows past the segment end fall outside the resource and load as zeros
+        const __amdgpu_buffer_rsrc_t ra_rsrc = make_rsrc(a.A + row0 * a.K, nrows * row_bytes);
+        const uint16_t* bbase;
+        uint32_t bbytes;
+        if (UP) {
+            bbase = a.B + static_cast<int64_t>(e) * 2 * a.N * a.K;
+            bbytes = static_cast<uint32_t>(2 * a.N) * row_bytes;
+        } else {
+            bbase = a.B + static_cast<int64_t>(e) * a.N * a.K;
+            bbytes = static_cast<uint32_t>(a.N) * row_bytes;
+        }
+        const __amdgpu_buffer_rsrc_t rb_rsrc = make_rsrc(bbase, bbytes);
+        uint32_t aoff[8], boff[8];
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+            const int r = lr + 32 * p;
+            aoff[p] = static_cast<uint32_t>(r) * row_bytes + ch * 16;
+            uint32_t brow;
+            if (UP) brow = static_cast<uint32_t>((r >> 7) * a.N + nt * UP_COLS + (r & (UP_COLS - 1)));
+            else brow = static_cast<uint32_t>(nt * BN + r);
+            boff[p] = brow * row_bytes + ch * 16;
+        }
+
+        floatx16_t acc[4][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+        v4i_t ra[8], rb[8];
+        auto gload = [&](int64_t kt) {
+            const int soff = static_cast<int>(kt * BK * 2);
+#pragma unroll
+            for (int p = 0; p < 8; ++p) {
+                ra[p] = __builtin_amdgcn_raw_buffer_load_b128(ra_rsrc, aoff[p], soff, 0);
+                rb[p] = __builtin_amdgcn_raw_buffer_load_b128(rb_rsrc, boff[p], soff, 0);
+            }
+        };
+        auto sstore = [&](int buf) {
+#pragma unroll
+            for (int p = 0; p < 8; ++p) {
+                const int r = lr + 32 * p;
+                *reinterpret_cast<v4i_t*>(&As[buf][r * LDS_STRIDE + ch * 8]) = ra[p];
+                *reinterpret_cast<v4i_t*>(&Bs[buf][r * LDS_STRIDE + ch * 8]) = rb[p];
+            }
+        };
+
+        const int64_t KT = a.K / BK;
+        gload(0);
+        sstore(0);
+        __syncthreads();
+        const int frow = lane & 31;
+        const int fk = (lane >> 5) * 8;
+        for (int64_t kt = 0; kt < KT; ++kt) {
+            const int cur = static_cast<int>(kt & 1);
+            if (kt + 1 < KT) gload(kt + 1);
+            const uint16_t* Ab = As[cur] + (wm * 128 + frow) * LDS_STRIDE + fk;
+            const uint16_t* Bb = Bs[cur] + fk;
+#pragma unroll
+            for (int ks = 0; ks < BK / 16; ++ks) {
+                bf16x8_t af[4], bfr[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    af[i] = *reinterpret_cast<const bf16x8_t*>(Ab + i * 32 * LDS_STRIDE + ks * 16);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    // up: wave column blocks 0,1 are gate, 2,3 the matching up blocks
+                    int brow;
+                    if (UP) brow = (j >> 1) * UP_COLS + wn * 64 + (j & 1) * 32 + frow;
+                    else brow = wn * 128 + j * 32 + frow;
+                    bfr[j] = *reinterpret_cast<const bf16x8_t*>(Bb + brow * LDS_STRIDE + ks * 16);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+            }
+            if (kt + 1 < KT) sstore(cur ^ 1);
+            __syncthreads();
+        }
+
+        // ---- epilogue: lane holds rows 8*(v/4) + 4*(lane/32) + v%4 of column lane%32.
+        // The lane's row base is made opaque per tile so the 64 row offsets below stay
+        // immediates instead of being hoisted out of the tile loop into registers.
+        int rbase = wm * 128 + (lane >> 5) * 4;
+        asm volatile("" : "+v"(rbase));
+        const int64_t colbase = UP ? static_cast<int64_t>(nt) * UP_COLS + wn * 64 + (lane & 31)
+                                   : static_cast<int64_t>(nt) * BN + wn * 128 + (lane & 31);
+        uint16_t* cbase = a.C + (row0 + rbase) * a.N + colbase;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int roff = i * 32 + (v >> 2) * 8 + (v & 3);
+                if (rbase + roff >= static_cast<int>(nrows)) continue;
+                uint16_t* cp = cbase + static_cast<int64_t>(roff) * a.N;
+                if (UP) {
+                    cp[0] = f32_to_bf16(silu_mul(acc[i][0][v], acc[i][2][v]));
+                    cp[32] = f32_to_bf16(silu_mul(acc[i][1][v], acc[i][3][v]));
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) cp[j * 32] = f32_to_bf16(acc[i][j][v]);
+                }
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------ simple path
+// One thread per output element; used for fp32 activations and for shapes the MFMA tiles
+// do not cover.  Rows are looked up in seg_offsets by binary search.
+struct SimpleArgs {
+    const void* A;
+    const void* B;
+    void* C;
+    const int32_t* counts;
+    const int64_t* seg;
+    const int64_t* num_rows;
+    int64_t cap, K, N;
+    int32_t El;
+};
+
+template <typename T>
+__device__ __forceinline__ float ld(const T* p, int64_t i) {
+    if constexpr (sizeof(T) == 2) return bf16_to_f32(p[i]);
+    else return p[i];
+}
+template <typename T>
+__device__ __forceinline__ void st(T* p, int64_t i, float v) {
+    if constexpr (sizeof(T) == 2) p[i] = f32_to_bf16(v);
+    else p[i] = v;
+}
+
+__device__ __forceinline__ int find_slot(const int64_t* seg, int El, int64_t row) {
+    int lo = 0, hi = El;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (seg[mid] <= row) lo = mid;
+        else hi = mid;
+    }
+    return lo;
+}
+
+template <typename T, bool UP>
+__global__ __launch_bounds__(256) void simple_gemm_kernel(SimpleArgs a) {
+    int64_t rows = *a.num_rows;
+    rows = rows < a.cap ? rows : a.cap;
+    const int64_t total = rows * a.N;
+    const T* A = static_cast<const T*>(a.A);
+    const T* B = static_cast<const T*>(a.B);
+    T* C = static_cast<T*>(a.C);
+    for (int64_t o = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; o < total;
+         o += static_cast<int64_t>(gridDim.x) * 256) {
+        const int64_t row = o / a.N, col = o % a.N;
+        const int e = find_slot(a.seg, a.El, row);
+        if (row >= a.seg[e] + a.counts[e]) continue;  // alignment pad row
+        const T* x = A + row * a.K;
+        if (UP) {
+            const T* wg = B + ((static_cast<int64_t>(e) * 2 + 0) * a.N + col) * a.K;
+            const T* wu = B + ((static_cast<int64_t>(e) * 2 + 1) * a.N + col) * a.K;
+            float g = 0.f, u = 0.f;
+            for (int64_t k = 0; k < a.K; ++k) {
+                const float xv = ld(x, k);
+                g = __builtin_fmaf(xv, ld(wg, k), g);
+                u = __builtin_fmaf(xv, ld(wu, k), u);
+            }
+            st(C, row * a.N + col, g / (1.0f + expf(-g)) * u);
+        } else {
+            const T* wd = B + (static_cast<int64_t>(e) * a.N + col) * a.K;
+            float y = 0.f;
+            for (int64_t k = 0; k < a.K; ++k) y = __builtin_fmaf(ld(x, k), ld(wd, k), y);
+            st(C, row * a.N + col, y);
+        }
+    }
+}
+
+int num_cus() {
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cus[dev] == 0) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+            v = 256;
+        cus[dev] = v;
+    }
+    return cus[dev];
+}
+
+moe_status check_common(moe_dtype act_dt, const moe_plan* plan, const moe_expert_weights* w,
+                        int64_t H, int64_t I) {
+    MOE_CHECK_ARG(plan && w);
+    MOE_CHECK_ARG(act_dt == MOE_F32 || act_dt == MOE_BF16);
+    MOE_CHECK_ARG(H > 0 && I > 0);
+    MOE_CHECK_ARG(plan->num_slots >= 1 && plan->num_slots <= kMaxSlots);
+    MOE_CHECK_ARG(plan->counts && plan->seg_offsets && plan->num_rows && plan->cap >= 0);
+    MOE_CHECK_ARG(w->w13 && w->w2);
+    if (w->dtype == MOE_FP8_E4M3) return MOE_ERR_UNSUPPORTED;
+    MOE_CHECK_ARG(w->dtype == act_dt);
+    return MOE_OK;
+}
+
+bool mfma_ok(moe_dtype act_dt, int64_t H, int64_t I, const void* A, const void* B, const void* C) {
+    // buffer resources cover one expert's weights and one 256-row A tile: < 4 GiB each
+    const bool small = 2 * H * I * 2 < (int64_t(1) << 32) && int64_t(BM) * H * 2 < (int64_t(1) << 32) &&
+                       int64_t(BM) * I * 2 < (int64_t(1) << 32);
+    return act_dt == MOE_BF16 && H % BN == 0 && I % UP_COLS == 0 && small && aligned(A, 16) &&
+           aligned(B, 16) && aligned(C, 2);
+}
+
+moe_status run_stage(bool up, const void* A, moe_dtype act_dt, const moe_plan* plan,
+                     const moe_expert_weights* w, int64_t H, int64_t I, void* C, hipStream_t stream) {
+    if (plan->cap == 0) return MOE_OK;
+    MOE_CHECK_ARG(A && C);
+    const void* B = up ? w->w13 : w->w2;
+    const int64_t K = up ? H : I;
+    const int64_t N = up ? I : H;
+    if (mfma_ok(act_dt, H, I, A, B, C)) {
+        GemmArgs g;
+        g.A = static_cast<const uint16_t*>(A);
+        g.B = static_cast<const uint16_t*>(B);
+        g.C = static_cast<uint16_t*>(C);
+        g.counts = plan->counts;
+        g.seg = plan->seg_offsets;
+        g.cap = plan->cap;
+        g.K = K;
+        g.N = N;
+        g.El = plan->num_slots;
+        g.NT = static_cast<int32_t>(up ? I / UP_COLS : H / BN);
+        const dim3 grid(static_cast<unsigned>(num_cus()));
+        if (up) hipLaunchKernelGGL(grouped_gemm_bf16_kernel<true>, grid, dim3(M_THREADS), 0, stream, g);
+        else hipLaunchKernelGGL(grouped_gemm_bf16_kernel<false>, grid, dim3(M_THREADS), 0, stream, g);
+        MOE_LAUNCH_CHECK();
+        return MOE_OK;
+    }
+    SimpleArgs s{A, B, C, plan->counts, plan->seg_offsets, plan->num_rows, plan->cap, K, N,
+                 plan->num_slots};
+    int64_t blocks = ceil_div(plan->cap * N, 256);
+    if (blocks > 65536) blocks = 65536;
+    const dim3 grid(static_cast<unsigned>(blocks));
+    if (act_dt == MOE_BF16) {
+        if (up) hipLaunchKernelGGL((simple_gemm_kernel<uint16_t, true>), grid, dim3(256), 0, stream, s);
+        else hipLaunchKernelGGL((simple_gemm_kernel<uint16_t, false>), grid, dim3(256), 0, stream, s);
+    } else {
+        if (up) hipLaunchKernelGGL((simple_gemm_kernel<float, true>), grid, dim3(256), 0, stream, s);
+        else hipLaunchKernelGGL((simple_gemm_kernel<float, false>), grid, dim3(256), 0, stream, s);
+    }
+    MOE_LAUNCH_CHECK();
+    return MOE_OK;
+}
+
+size_t h_bytes(int64_t cap, int64_t I, moe_dtype act_dt) {
+    return (static_cast<size_t>(cap * I) * dtype_size(act_dt) + 255) & ~static_cast<size_t>(255);
+}
+
+}  // namespace
+}  // namespace moe
+
+extern "C" size_t moe_expert_gemm_workspace_size(int64_t cap, int64_t H, int64_t I,
+                                                 moe_dtype act_dt, moe_dtype w_dt) {
+    (void)H;
+    (void)w_dt;
+    if (cap < 0 || I <= 0) return 0;
+    return moe::h_bytes(cap, I, act_dt);
+}
+
+extern "C" moe_status moe_expert_gemm_up(const void* x_perm, moe_dtype act_dt, const moe_plan* plan,
+                                         const moe_expert_weights* w, int64_t H, int64_t I, void* h,
+                                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    (void)workspace;
+    (void)workspace_bytes;
+    moe_status st = moe::check_common(act_dt, plan, w, H, I);
+    if (st != MOE_OK) return st;
+    return moe::run_stage(true, x_perm, act_dt, plan, w, H, I, h, stream);
+}
+
+extern "C" moe_status moe_expert_gemm_down(const void* h, moe_dtype act_dt, const moe_plan* plan,
+                                           const moe_expert_weights* w, int64_t H, int64_t I,
+                                           void* y_perm, void* workspace, size_t workspace_bytes,
+                                           hipStream_t stream) {
+    (void)workspace;
+    (void)workspace_bytes;
+    moe_status st = moe::check_common(act_dt, plan, w, H, I);
+    if (st != MOE_OK) return st;
+    return moe::run_stage(false, h, act_dt, plan, w, H, I, y_perm, stream);
+}
+
+extern "C" moe_status moe_expert_gemm(const void* x_perm, moe_dtype act_dt, const moe_plan* plan,
+                                      const moe_expert_weights* w, int64_t H, int64_t I,
+                                      void* y_perm, void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream) {
+    moe_status st = moe::check_common(act_dt, plan, w, H, I);
+    if (st != MOE_OK) return st;
+    if (plan->cap == 0) return MOE_OK;
+    if (workspace_bytes < moe::h_bytes(plan->cap, I, act_dt)) return MOE_ERR_CAPACITY;
+    MOE_CHECK_ARG(workspace && moe::aligned(workspace, 256));
+    st = moe::run_stage(true, x_perm, act_dt, plan, w, H, I, workspace, stream);
+    if (st != MOE_OK) return st;
+    return moe::run_stage(false, workspace, act_dt, plan, w, H, I, y_perm, stream);
+}

@@ -1,0 +1,58 @@
+// Shared device/host helpers of the HIP library (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+#define MOE_CHECK_ARG(cond)                      \
+    do {                                         \
+        if (!(cond)) return MOE_ERR_INVALID_ARG; \
+    } while (0)
+
+#define MOE_LAUNCH_CHECK()                                       \
+    do {                                                         \
+        if (hipGetLastError() != hipSuccess) return MOE_ERR_HIP; \
+    } while (0)
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+inline int dtype_size(moe_dtype dt) {
+    switch (dt) {
+        case MOE_F32: return 4;
+        case MOE_BF16: return 2;
+        case MOE_FP8_E4M3: return 1;
+    }
+    return 0;
+}
+
+// bf16 bits -> fp32 (exact)
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even; NaN stays NaN
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+// pack two fp32 into two bf16 (lo in the low half)
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+inline bool aligned(const void* p, uintptr_t a) {
+    return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
+}
+
+}  // namespace moe

@@ -1,0 +1,167 @@
+"""One rank's MoE layer as the six C-ABI calls in order, with torch-allocated buffers.
+
+gather -> route -> dispatch -> expert GEMMs -> combine -> scatter: the step order of the
+SGLang walkthrough "SGLang 源码完全拆解(十七): DP Attention 与专家并行" (DP gather before the
+MoE, section "两种 gather"; op_gate, op_select_experts, dispatch, experts, combine in the
+operations list of section "operations 与 yield"; scatter back, section "scatter：把 MoE 的
+输出还回本副本").  Python only allocates and passes pointers; every step runs in HIP.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import List, Optional, Sequence
+
+import numpy as np
+import torch
+
+from . import (PlanBuffers, layout_offsets, layout_sizes, make_expert_map, make_expert_weights,
+               make_route_cfg, moe_combine, moe_dispatch, moe_dispatch_workspace_size,
+               moe_expert_gemm, moe_expert_gemm_down, moe_expert_gemm_up,
+               moe_expert_gemm_workspace_size, moe_gather, moe_gather_layout, moe_route,
+               moe_scatter)
+
+
+def _to_dev(a: Optional[np.ndarray], device, bf16: bool = False) -> Optional[torch.Tensor]:
+    if a is None:
+        return None
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if bf16:
+        assert a.dtype == np.uint16
+        t = t.view(torch.bfloat16)
+    return t.to(device)
+
+
+@dataclass
+class LayerSpec:
+    hidden: int
+    inter: int
+    num_experts: int
+    top_k: int
+    route: str                  # "softmax" | "grouped"
+    num_local: int
+    first_local: int = 0
+    n_group: int = 1
+    topk_group: int = 1
+    group_topn: int = 2
+    renormalize: bool = False
+    routed_scale: float = 1.0
+
+
+class DeviceWeights:
+    """Router and expert weights resident in HBM."""
+
+    def __init__(self, inp, device="cuda"):
+        cfg = inp.cfg
+        bf = cfg.dtype == "bf16"
+        self.router = _to_dev(inp.router_w, device, bf)
+        self.bias = _to_dev(inp.bias, device)
+        if inp.w13 is not None:
+            self.w13 = _to_dev(inp.w13, device, bf)
+            self.w2 = _to_dev(inp.w2, device, bf)
+            self.s13 = self.s2 = None
+        else:
+            self.w13 = _to_dev(inp.w13_q, device)
+            self.w2 = _to_dev(inp.w2_q, device)
+            self.s13 = _to_dev(inp.w13_s, device)
+            self.s2 = _to_dev(inp.w2_s, device)
+        trivial = cfg.slot_logical is None
+        self.phys_of = None if trivial else _to_dev(inp.phys_of, device)
+        self.n_rep = None if trivial else _to_dev(inp.n_rep, device)
+        self.ew = make_expert_weights(self.w13, self.w2, self.s13, self.s2)
+
+
+def spec_of(cfg) -> LayerSpec:
+    return LayerSpec(hidden=cfg.hidden, inter=cfg.inter, num_experts=cfg.num_experts,
+                     top_k=cfg.top_k, route=cfg.route, num_local=cfg.num_local,
+                     first_local=cfg.first_local, n_group=cfg.n_group, topk_group=cfg.topk_group,
+                     group_topn=cfg.group_topn, renormalize=cfg.renormalize,
+                     routed_scale=cfg.routed_scale)
+
+
+class MoELayer:
+    """Buffers for one step shape (replica counts, gather mode) and the six calls."""
+
+    def __init__(self, spec: LayerSpec, weights: DeviceWeights, num_tokens: Sequence[int],
+                 act_dtype: torch.dtype, mode: str = "auto", static_bound: int = 0,
+                 is_extend: bool = False, align: int = 1, cap: Optional[int] = None,
+                 device="cuda"):
+        self.spec, self.w, self.device, self.dt = spec, weights, device, act_dtype
+        self.layout = moe_gather_layout(num_tokens, mode, is_extend=is_extend,
+                                        static_bound=static_bound)
+        G = int(self.layout.rows)
+        self.G = G
+        H, I, k = spec.hidden, spec.inter, spec.top_k
+        self.sizes = layout_sizes(self.layout)
+        self.offsets = layout_offsets(self.layout)
+        self.global_x = torch.empty((G, H), dtype=act_dtype, device=device)
+        self.row_valid = torch.empty(max(G, 1), dtype=torch.int32, device=device)
+        self.route_cfg = make_route_cfg(spec.route, spec.num_experts, k, spec.n_group,
+                                        spec.topk_group, spec.group_topn, spec.renormalize)
+        self.logits = torch.empty((max(G, 1), spec.num_experts), dtype=torch.float32, device=device)
+        self.topk_ids = torch.empty((max(G, 1), k), dtype=torch.int32, device=device)
+        self.topk_w = torch.empty((max(G, 1), k), dtype=torch.float32, device=device)
+        self.emap = make_expert_map(spec.num_experts, spec.first_local, spec.num_local,
+                                    weights.phys_of, weights.n_rep)
+        self.plan = PlanBuffers(G, k, spec.num_local, align, cap, device)
+        cap = self.plan.cap
+        self.dispatch_ws = torch.empty(max(moe_dispatch_workspace_size(G, k, spec.num_local), 16),
+                                       dtype=torch.uint8, device=device)
+        self.x_perm = torch.empty((max(cap, 1), H), dtype=act_dtype, device=device)
+        self.h = torch.empty((max(cap, 1), I), dtype=act_dtype, device=device)
+        self.y_perm = torch.empty((max(cap, 1), H), dtype=act_dtype, device=device)
+        self.gemm_ws = torch.empty(max(moe_expert_gemm_workspace_size(cap, H, I, act_dtype,
+                                                                      weights.w13.dtype), 256),
+                                   dtype=torch.uint8, device=device)
+        self.out = torch.empty((G, H), dtype=act_dtype, device=device)
+        self.replicas_out = [torch.empty((n, H), dtype=act_dtype, device=device) for n in self.sizes]
+
+    # the six steps, individually callable
+    def gather(self, replicas):
+        moe_gather(self.layout, replicas, self.global_x, self.row_valid)
+
+    def route(self):
+        if self.G:
+            moe_route(self.global_x, self.row_valid, self.w.router, self.w.bias, self.route_cfg,
+                      self.logits, self.topk_ids, self.topk_w)
+
+    def dispatch(self):
+        if self.G:
+            moe_dispatch(self.global_x, self.topk_ids[:self.G], self.emap, self.plan, self.x_perm,
+                         self.dispatch_ws)
+
+    def experts(self, split: bool = True):
+        if not self.G:
+            return
+        s = self.spec
+        if split:
+            moe_expert_gemm_up(self.x_perm, self.plan, self.w.ew, s.hidden, s.inter, self.h)
+            moe_expert_gemm_down(self.h, self.plan, self.w.ew, s.hidden, s.inter, self.y_perm)
+        else:
+            moe_expert_gemm(self.x_perm, self.plan, self.w.ew, s.hidden, s.inter, self.y_perm,
+                            self.gemm_ws)
+
+    def experts_up(self):
+        if self.G:
+            moe_expert_gemm_up(self.x_perm, self.plan, self.w.ew, self.spec.hidden, self.spec.inter,
+                               self.h)
+
+    def experts_down(self):
+        if self.G:
+            moe_expert_gemm_down(self.h, self.plan, self.w.ew, self.spec.hidden, self.spec.inter,
+                                 self.y_perm)
+
+    def combine(self):
+        if self.G:
+            moe_combine(self.y_perm, self.plan, self.topk_w, self.spec.routed_scale, self.out)
+
+    def scatter(self):
+        moe_scatter(self.layout, self.out, self.replicas_out)
+
+    def forward(self, replicas) -> List[torch.Tensor]:
+        self.gather(replicas)
+        self.route()
+        self.dispatch()
+        self.experts()
+        self.combine()
+        self.scatter()
+        return self.replicas_out

@@ -1,0 +1,265 @@
+/*
+ * moe.h -- C ABI of the single-rank MoE hot path under DP attention + expert parallelism,
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * One rank's MoE layer, as the SGLang walkthrough "SGLang 源码完全拆解(十七): DP Attention
+ * 与专家并行" (below: "the SGLang page") lays it out:
+ *   1. gather the DP replicas' token slices into one global buffer      moe_gather_layout, moe_gather
+ *   2. route every global token to its top-k experts                     moe_route, moe_route_from_logits
+ *   3. dispatch: counting-sort the (token, k) pairs into one contiguous
+ *      segment per local expert slot                                     moe_dispatch
+ *   4. run the SwiGLU experts as grouped GEMMs over those segments       moe_expert_gemm (_up, _down)
+ *   5. combine: weighted un-permute back to token order                  moe_combine
+ *   6. scatter the global rows back to each replica's slice              moe_scatter
+ *
+ * Conventions shared by every call
+ *   - All tensors are dense, row-major, contiguous.  Device pointers are HIP device memory
+ *     owned by the caller; the library allocates nothing and keeps no state between calls.
+ *   - Host arrays and structs passed by pointer are read before the call returns.
+ *   - Work is enqueued on the given stream; no call synchronises the host with the device,
+ *     so every call can be captured in a HIP graph.  Device buffers must stay alive until
+ *     the stream has run the work.
+ *   - Argument errors are detected on the host and returned synchronously with nothing
+ *     enqueued.  A failed launch returns MOE_ERR_HIP.  Conditions that only the device can
+ *     see (dispatch capacity overflow) are reported through a device flag.
+ *   - Calls are reentrant; calls on different streams may run concurrently as long as
+ *     they do not share output or workspace buffers.
+ *   - bf16 values are IEEE binary32 numbers with the low 16 bits dropped (2 bytes each);
+ *     fp8 values are OCP e4m3fn bytes.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = 1,  /* a pointer, size or enum value is out of range; nothing enqueued */
+    MOE_ERR_UNSUPPORTED = 2,  /* a valid combination this build does not implement */
+    MOE_ERR_CAPACITY = 3,     /* a caller buffer (workspace, table) is too small */
+    MOE_ERR_HIP = 4           /* the HIP runtime refused a launch */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
+
+/* DpPaddingMode of the SGLang page, section "DpPaddingMode：补齐到最长还是补齐到总和":
+ * MAX_LEN pads every replica to the longest one, SUM_LEN concatenates the replicas. */
+typedef enum { MOE_PAD_AUTO = 0, MOE_PAD_MAX_LEN = 1, MOE_PAD_SUM_LEN = 2 } moe_pad_mode;
+
+#define MOE_MAX_REPLICAS 256
+
+/* Resolved layout of one gather (filled by moe_gather_layout, read by gather and scatter). */
+typedef struct {
+    int32_t mode;                              /* MOE_PAD_MAX_LEN or MOE_PAD_SUM_LEN */
+    int32_t num_replicas;                      /* W */
+    int64_t rows;                              /* G: rows of the global buffer */
+    int64_t offsets[MOE_MAX_REPLICAS + 1];     /* first global row of each replica slot; [W] = G */
+    int32_t sizes[MOE_MAX_REPLICAS];           /* rows each replica holds (n_i, or B) */
+} moe_gather_layout_t;
+
+/* Status as text (static storage). */
+const char* moe_status_string(moe_status s);
+/* Library version string, e.g. "0.1.0 gfx950". */
+const char* moe_version(void);
+
+/* ------------------------------------------------------------------------------------------
+ * moe_gather_layout -- host only.
+ * Offsets of each replica's slice in the global buffer: prefix sums of the replica token
+ * counts (SGLang page, section "本 rank 的切片位置怎么算").  mode AUTO follows the heuristic
+ * of section "DpPaddingMode": prefill (is_extend) with more than one replica -> SUM_LEN,
+ * unless max_len_with_idle and some replica is idle -> MAX_LEN; otherwise MAX_LEN iff
+ * 2*sum >= max*W.  MAX_LEN offsets are i*max(n).  static_bound B > 0 sizes every replica B
+ * and places replica i at i*B (DP note, section "跳过同步：用约定代替通信"); a count above B is
+ * an error.  All replicas idle gives rows = 0: every later call is then a no-op (SGLang page,
+ * section "空闲副本也必须参与").
+ *   num_tokens  host int32[W], each >= 0;  1 <= W <= MOE_MAX_REPLICAS
+ *   out         host struct, filled on success
+ * Errors: MOE_ERR_INVALID_ARG for NULL pointers, W out of range, negative counts, counts
+ * above a static bound, or a bad mode.
+ * ---------------------------------------------------------------------------------------- */
+moe_status moe_gather_layout(const int32_t* num_tokens, int32_t W, moe_pad_mode mode,
+                             int32_t is_extend, int32_t max_len_with_idle, int32_t static_bound,
+                             moe_gather_layout_t* out);
+
+/* ------------------------------------------------------------------------------------------
+ * moe_gather -- the DP gather (SGLang page, section "两种 gather：all_reduce 与 all_gather"):
+ * the global buffer is zero except for each replica's rows written at its offset.  On one
+ * GPU every replica buffer is local, so the write replaces the collective.
+ *   L          layout from moe_gather_layout
+ *   replica_x  host array of W device pointers; replica i is [sizes[i], H] of dtype dt.
+ *              The pointer of a replica with 0 rows may be NULL.
+ *   H          hidden size (> 0);  dt: MOE_F32 or MOE_BF16
+ *   global_x   device [rows, H] dt, written in full (pad rows = 0)
+ *   row_valid  device int32[rows]: 1 for a real token row, 0 for a pad row
+ * ---------------------------------------------------------------------------------------- */
+moe_status moe_gather(const moe_gather_layout_t* L, const void* const* replica_x, int64_t H,
+                      moe_dtype dt, void* global_x, int32_t* row_valid, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------
+ * moe_scatter -- the inverse of moe_gather with the same layout: y_i[r] = out[offset_i + r]
+ * for r < sizes[i] (SGLang page, section "scatter：把 MoE 的输出还回本副本": the counts that
+ * placed the rows also cut them).  The cross-rank sum of reduce_scatterv needs other GPUs and
+ * is not part of this call.
+ *   out        device [rows, H] dt
+ *   replica_y  host array of W device pointers to [sizes[i], H] dt (NULL allowed if 0 rows)
+ * ---------------------------------------------------------------------------------------- */
+moe_status moe_scatter(const moe_gather_layout_t* L, const void* out, int64_t H, moe_dtype dt,
+                       void* const* replica_y, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Routing (op_gate + op_select_experts of the SGLang page, section "operations 与 yield";
+ * TopKOutput of section "normal dispatch 的调用链").
+ * ---------------------------------------------------------------------------------------- */
+typedef enum { MOE_ROUTE_SOFTMAX = 0, MOE_ROUTE_GROUPED_SIGMOID = 1 } moe_route_kind;
+
+typedef struct {
+    int32_t kind;          /* moe_route_kind */
+    int32_t num_experts;   /* E (logical), 1..1024 */
+    int32_t top_k;         /* k, 1..32 and <= E */
+    int32_t n_group;       /* grouped: groups of E/n_group contiguous experts (E % n_group == 0) */
+    int32_t topk_group;    /* grouped: groups kept, 1..n_group; k <= topk_group*E/n_group */
+    int32_t group_topn;    /* grouped: keys summed per group score, 1..E/n_group (DeepSeek-V3: 2) */
+    int32_t renormalize;   /* weights divided by their sum over the k picks */
+} moe_route_cfg;
+
+/* moe_route -- gate logits then top-k selection.
+ *   global_x   device [G, H] dt (MOE_F32 or MOE_BF16); row_valid device int32[G]
+ *   w_router   device [E, H] dt
+ *   bias       device fp32[E] or NULL (grouped only: selection bias, never in the weights)
+ *   logits     device fp32[G, E], written: logits[g,e] = fmaf chain over h = 0..H-1 in
+ *              ascending order starting from +0 (the exact-order gate; 0 for pad rows)
+ *   topk_ids   device int32[G, k]: expert ids, slots in descending key order, ties to the
+ *              lower id; -1 for pad rows
+ *   topk_w     device fp32[G, k]: weights; 0 for pad rows
+ * Selection: softmax -- the k largest logits, weight = softmax over all E (optionally
+ * renormalised).  Grouped sigmoid -- key = sigmoid(l) + bias in fp64 with a Cody-Waite exp,
+ * group score = sum of the group_topn largest keys of the group, the topk_group best groups
+ * are kept, then the k largest keys inside them; weight = sigmoid(l) (bias excluded),
+ * optionally renormalised.  Ties go to the lower group / expert index. */
+moe_status moe_route(const void* global_x, const int32_t* row_valid, int64_t G, int64_t H,
+                     moe_dtype dt, const void* w_router, const float* bias,
+                     const moe_route_cfg* cfg, float* logits, int32_t* topk_ids, float* topk_w,
+                     hipStream_t stream);
+
+/* moe_route_from_logits -- the selection step alone, on caller logits fp32[G, E]. */
+moe_status moe_route_from_logits(const float* logits, const int32_t* row_valid, int64_t G,
+                                 const float* bias, const moe_route_cfg* cfg, int32_t* topk_ids,
+                                 float* topk_w, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Dispatch (get_dispatch_layout's per-expert counts, expert_alignment and the dispatch
+ * "handle" of the SGLang page, section "normal dispatch 的调用链"; physical replica choice of
+ * section "推理时怎么“选副本”").
+ * ---------------------------------------------------------------------------------------- */
+typedef struct {
+    int32_t num_logical;     /* E */
+    int32_t max_rep;         /* columns of phys_of */
+    const int32_t* phys_of;  /* device int32[E, max_rep]: physical slots of each logical expert */
+    const int32_t* n_rep;    /* device int32[E]: valid columns of each row (>= 1) */
+    int32_t first_slot;      /* p0: first physical slot owned by this rank */
+    int32_t num_slots;       /* E_l: slots [p0, p0+E_l) are local, 1..1024 */
+} moe_expert_map;
+/* A pair (g, j) with logical id l goes to physical slot phys_of[l][g mod n_rep[l]]: the same
+ * choice on every rank (rank_invariant).  With phys_of == NULL the map is the identity
+ * (slot l holds logical l). */
+
+typedef struct {
+    int32_t* counts;        /* device int32[E_l]: pairs per local slot */
+    int64_t* seg_offsets;   /* device int64[E_l+1]: segment e is rows [seg[e], seg[e+1]),
+                               seg[e+1] - seg[e] = counts[e] rounded up to align */
+    int32_t* sorted_pair;   /* device int32[cap]: flat pair index f = g*k + j of each row,
+                               ascending f inside a segment; -1 on alignment pad rows */
+    int32_t* pair_row;      /* device int32[G*k]: row of pair f, -1 if not local (or dropped) */
+    int64_t* num_rows;      /* device int64[1]: seg[E_l] */
+    int32_t* error_flag;    /* device int32[1]: 1 if num_rows > cap (rows >= cap are dropped) */
+    int64_t cap;            /* rows of sorted_pair / x_perm / y_perm */
+    int64_t G;              /* global rows */
+    int32_t top_k;          /* k */
+    int32_t num_slots;      /* E_l */
+    int32_t align;          /* segment alignment in rows (>= 1; 128 matches the grouped GEMM tile) */
+    int32_t reserved;
+} moe_plan;
+
+/* Device workspace (bytes) moe_dispatch needs for G rows, k picks and E_l slots. */
+size_t moe_dispatch_workspace_size(int64_t G, int32_t k, int32_t num_slots);
+
+/* moe_dispatch -- counts, aligned exclusive scan, stable counting sort, permuted copy.
+ *   global_x  device [G, H] dt;  topk_ids device int32[G, k] (ids outside [0, E) are skipped)
+ *   map       expert map (see above); plan: caller buffers, filled here
+ *   x_perm    device [cap, H] dt: row r = global_x[sorted_pair[r] / k]; alignment pad rows 0;
+ *             rows >= num_rows are not written
+ *   workspace device, >= moe_dispatch_workspace_size(G, k, E_l) bytes, 16-byte aligned
+ * cap >= G*min(k, E_l) + E_l*(align-1) can never overflow. */
+moe_status moe_dispatch(const void* global_x, const int32_t* topk_ids, int64_t G, int32_t k,
+                        int64_t H, moe_dtype dt, const moe_expert_map* map, const moe_plan* plan,
+                        void* x_perm, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Experts: per local slot e, over the rows of its segment,
+ *     h = silu(x Wg[e]^T) * (x Wu[e]^T),   y = h Wd[e]^T,   silu(z) = z / (1 + e^-z)
+ * gate_proj / up_proj [I, H] and down_proj [H, I] as in the SGLang page, section "EP 下专家
+ * 权重切不均匀的问题"; permute, MM1, activation, MM2 in the order of the vLLM walkthrough
+ * "vLLM 源码完全拆解(二十七): Dual Batch Overlap" (figure of the modular-kernel blocks).
+ * ---------------------------------------------------------------------------------------- */
+typedef struct {
+    int32_t dtype;          /* MOE_F32, MOE_BF16 (same as activations) or MOE_FP8_E4M3 */
+    int32_t reserved;
+    const void* w13;        /* device [E_l, 2, I, H]: [e][0] = gate_proj, [e][1] = up_proj */
+    const void* w2;         /* device [E_l, H, I]: down_proj */
+    const float* s13;       /* fp8 only: device fp32[E_l, 2, I/128, H/128] block scales */
+    const float* s2;        /* fp8 only: device fp32[E_l, H/128, I/128] block scales */
+} moe_expert_weights;
+/* fp8 weights: value = e4m3(q) * scale of its 128x128 block. */
+
+/* Device workspace (bytes) moe_expert_gemm needs (the intermediate h and, for fp8 weights,
+ * the quantised activations). */
+size_t moe_expert_gemm_workspace_size(int64_t cap, int64_t H, int64_t I, moe_dtype act_dt,
+                                      moe_dtype w_dt);
+
+/* moe_expert_gemm -- both grouped GEMMs.
+ *   x_perm    device [cap, H] act_dt (MOE_F32 or MOE_BF16), from moe_dispatch
+ *   plan      the plan moe_dispatch filled (counts, seg_offsets and cap are read on the device)
+ *   y_perm    device [cap, H] act_dt: rows of each segment's pairs; alignment pad rows and
+ *             rows >= num_rows are not written
+ *   workspace device, >= moe_expert_gemm_workspace_size(...) bytes, 256-byte aligned
+ * Accumulation is fp32; h and y are rounded to act_dt (nearest even).
+ * bf16 / fp8 need H % 256 == 0 and I % 128 == 0, else MOE_ERR_UNSUPPORTED. */
+moe_status moe_expert_gemm(const void* x_perm, moe_dtype act_dt, const moe_plan* plan,
+                           const moe_expert_weights* w, int64_t H, int64_t I, void* y_perm,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* The two halves of moe_expert_gemm, for callers that time or overlap them separately.
+ *   _up:   x_perm -> h      (h: device [cap, I] act_dt, caller memory)
+ *   _down: h      -> y_perm
+ * With fp8 weights each half quantises its activations into the workspace first. */
+moe_status moe_expert_gemm_up(const void* x_perm, moe_dtype act_dt, const moe_plan* plan,
+                              const moe_expert_weights* w, int64_t H, int64_t I, void* h,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+moe_status moe_expert_gemm_down(const void* h, moe_dtype act_dt, const moe_plan* plan,
+                                const moe_expert_weights* w, int64_t H, int64_t I, void* y_perm,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------
+ * moe_combine -- out[g] = routed_scale * sum_{j = 0..k-1, pair_row[g*k+j] >= 0}
+ *                          topk_w[g, j] * y_perm[pair_row[g*k+j]]
+ * accumulated in fp32 in ascending j and rounded once to dt; rows with no local pair are 0.
+ * The top-k weights are applied after the un-permute (vLLM walkthrough, figure of the
+ * modular-kernel blocks: finalize applies them; combine itself takes no weights).  A gather
+ * form: each output row is written by one owner, with no atomics, so results are
+ * deterministic.
+ *   y_perm device [cap, H] dt; topk_w device fp32[G, k]; out device [G, H] dt
+ * ---------------------------------------------------------------------------------------- */
+moe_status moe_combine(const void* y_perm, moe_dtype dt, const moe_plan* plan,
+                       const float* topk_w, float routed_scale, int64_t H, void* out,
+                       hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

@@ -1,0 +1,62 @@
+"""Shared set-up of the GPU tests: seeded inputs on the device, the layer's six calls, and
+conversions of device results back to numpy for comparison with the oracle."""
+from __future__ import annotations
+
+import sys
+from dataclasses import replace
+
+import numpy as np
+import torch
+
+import moe_synth
+
+TOL_BF16 = 2e-2     # max relative error (infinity norm) for bf16 outputs, fp32 accumulate
+TOL_FP8 = 5e-2      # fp8 weights
+TOL_F32 = 1e-4      # fp32 path (the oracle accumulates in fp64)
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def tol_for(cfg):
+    if cfg.weight_format == "fp8_block":
+        return TOL_FP8
+    return TOL_F32 if cfg.dtype == "f32" else TOL_BF16
+
+
+def act_dtype(cfg):
+    return torch.float32 if cfg.dtype == "f32" else torch.bfloat16
+
+
+def to_np(t: torch.Tensor) -> np.ndarray:
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.uint16).numpy()
+    return t.numpy()
+
+
+def replicas_to_device(inp, device="cuda"):
+    bf = inp.cfg.dtype == "bf16"
+    out = []
+    for r in inp.replicas:
+        t = torch.from_numpy(np.ascontiguousarray(r))
+        if bf:
+            t = t.view(torch.bfloat16)
+        out.append(t.to(device))
+    return out
+
+
+def resized(name, tokens, **kw):
+    cfg = moe_synth.CONFIGS[name]
+    return replace(cfg, num_tokens=tuple(tokens), static_bound=0, name=f"{name}-{len(tokens)}r", **kw)
+
+
+def build_layer(inp, mode="sum", align=1, cap=None):
+    from combine_dp_gather_amd.layer import DeviceWeights, MoELayer, spec_of
+    cfg = inp.cfg
+    w = DeviceWeights(inp)
+    layer = MoELayer(spec_of(cfg), w, cfg.num_tokens, act_dtype(cfg), mode=mode,
+                     static_bound=cfg.static_bound, align=align, cap=cap)
+    return layer

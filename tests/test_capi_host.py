@@ -1,0 +1,134 @@
+"""C-ABI checks that need no GPU: the library loads, exports every declared entry point,
+computes gather layouts like the oracle, and rejects bad arguments before touching HIP."""
+import ctypes
+import json
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+@pytest.fixture(scope="module")
+def m():
+    import combine_dp_gather_amd as m
+    if not os.path.exists(os.path.join(ROOT, "combine_dp_gather_amd", "libmoe_hip.so")):
+        from combine_dp_gather_amd import build
+        build.build()
+    m.lib()
+    return m
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(m):
+    from combine_dp_gather_amd import _lib
+    names = declared_functions()
+    assert len(names) >= 14
+    lib = ctypes.CDLL(_lib.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) <= set(_lib.SIGNATURES)
+    assert m.moe_version().endswith("gfx950")
+
+
+def test_layout_matches_oracle_golden(m):
+    cases = json.load(open(os.path.join(ROOT, "tests", "golden", "gather_layouts.json")))["cases"]
+    for c in cases:
+        L = m.moe_gather_layout(c["num_tokens"], c["mode"], c["is_extend"], c["max_len_with_idle"],
+                                c["static_bound"])
+        assert m.layout_mode(L) == c["expect_mode"]
+        assert L.rows == c["expect_G"]
+        assert m.layout_offsets(L) == c["expect_offsets"]
+
+
+def test_layout_matches_oracle_random(m):
+    rng = np.random.default_rng(0)
+    for _ in range(300):
+        W = int(rng.integers(1, 40))
+        n = [int(v) for v in rng.integers(0, 100, W) * (rng.random(W) > 0.2)]
+        mode = ["auto", "max", "sum"][int(rng.integers(3))]
+        ext = bool(rng.integers(2))
+        idle = bool(rng.integers(2))
+        B = int(rng.integers(0, 2)) * 100
+        L = m.moe_gather_layout(n, mode, ext, idle, B)
+        om, G, offs, sizes = oracle.gather_layout(n, mode, ext, idle, B)
+        assert (m.layout_mode(L), L.rows, m.layout_offsets(L), m.layout_sizes(L)) == (om, G, offs, sizes)
+
+
+def test_layout_rejects(m):
+    from combine_dp_gather_amd import MoEError
+    for bad in ([], [1, -2]):
+        with pytest.raises(MoEError):
+            m.moe_gather_layout(bad, "sum")
+    with pytest.raises(MoEError):
+        m.moe_gather_layout([30], "sum", static_bound=24)
+    with pytest.raises(MoEError):
+        m.moe_gather_layout([1] * 257, "sum")
+
+
+def test_argument_errors_return_before_any_launch(m):
+    from combine_dp_gather_amd import _lib
+    lib = m.lib()
+    L = m.moe_gather_layout([3, 4], "sum")
+    # NULL replica array / bad dtype / bad H
+    assert lib.moe_gather(None, None, 16, _lib.MOE_BF16, None, None, None) == _lib.MOE_ERR_INVALID_ARG
+    assert lib.moe_gather(ctypes.byref(L), None, 16, _lib.MOE_BF16, None, None, None) == _lib.MOE_ERR_INVALID_ARG
+    arr = (ctypes.c_void_p * 2)(None, None)
+    assert lib.moe_gather(ctypes.byref(L), ctypes.cast(arr, ctypes.c_void_p), 0, _lib.MOE_BF16,
+                          None, None, None) == _lib.MOE_ERR_INVALID_ARG
+    assert lib.moe_gather(ctypes.byref(L), ctypes.cast(arr, ctypes.c_void_p), 16, 7, None, None,
+                          None) == _lib.MOE_ERR_INVALID_ARG
+    # all replicas idle: a no-op that succeeds without any pointer
+    L0 = m.moe_gather_layout([0, 0], "max")
+    assert lib.moe_gather(ctypes.byref(L0), ctypes.cast(arr, ctypes.c_void_p), 16, _lib.MOE_BF16,
+                          None, None, None) == _lib.MOE_OK
+    # routing configuration checks
+    bad = [m.make_route_cfg("softmax", 0, 1), m.make_route_cfg("softmax", 8, 9),
+           m.make_route_cfg("softmax", 2048, 2), m.make_route_cfg("grouped", 256, 8, 7, 4),
+           m.make_route_cfg("grouped", 256, 8, 8, 9), m.make_route_cfg("grouped", 256, 8, 8, 4, 40),
+           m.make_route_cfg("grouped", 16, 8, 4, 1)]
+    for c in bad:
+        assert lib.moe_route_from_logits(1, None, 4, None, ctypes.byref(c), 1, 1, None) == \
+            _lib.MOE_ERR_INVALID_ARG
+    good = m.make_route_cfg("grouped", 256, 8, 8, 4, 2, True)
+    assert lib.moe_route_from_logits(1, None, 0, None, ctypes.byref(good), None, None, None) == _lib.MOE_OK
+    # dispatch: plan / map mismatch, workspace too small
+    emap = _lib.ExpertMap(16, 1, None, None, 0, 16)
+    plan = _lib.Plan(1, 1, 1, 1, 1, 1, 100, 10, 2, 16, 1, 0)
+    assert lib.moe_dispatch(1, 1, 10, 3, 64, _lib.MOE_BF16, ctypes.byref(emap), ctypes.byref(plan),
+                            1, 1, 1 << 20, None) == _lib.MOE_ERR_INVALID_ARG
+    assert lib.moe_dispatch(1, 1, 10, 2, 64, _lib.MOE_BF16, ctypes.byref(emap), ctypes.byref(plan),
+                            1, 1, 0, None) == _lib.MOE_ERR_CAPACITY
+    # experts: fp8 weights are not implemented by this build; dtype mismatch is invalid
+    w = _lib.ExpertWeights(_lib.MOE_FP8_E4M3, 0, 1, 1, 1, 1)
+    assert lib.moe_expert_gemm(1, _lib.MOE_BF16, ctypes.byref(plan), ctypes.byref(w), 256, 128, 1, 1,
+                               1 << 30, None) == _lib.MOE_ERR_UNSUPPORTED
+    w = _lib.ExpertWeights(_lib.MOE_F32, 0, 1, 1, None, None)
+    assert lib.moe_expert_gemm(1, _lib.MOE_BF16, ctypes.byref(plan), ctypes.byref(w), 256, 128, 1, 1,
+                               1 << 30, None) == _lib.MOE_ERR_INVALID_ARG
+    # combine: bad dtype
+    assert lib.moe_combine(1, 9, ctypes.byref(plan), 1, 1.0, 64, 1, None) == _lib.MOE_ERR_INVALID_ARG
+
+
+def test_workspace_sizes(m):
+    assert m.moe_dispatch_workspace_size(0, 8, 16) >= 0
+    a = m.moe_dispatch_workspace_size(32768, 8, 16)
+    assert a >= 2 * (32768 * 8 // 4096) * 16 * 4
+    import torch
+    assert m.moe_expert_gemm_workspace_size(1000, 7168, 2048, torch.bfloat16, torch.bfloat16) >= 1000 * 2048 * 2
+
+
+def test_status_strings(m):
+    lib = m.lib()
+    assert lib.moe_status_string(0) == b"ok"
+    assert b"invalid" in lib.moe_status_string(1)
