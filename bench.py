@@ -73,6 +73,8 @@ def main():
     ap.add_argument("--mode", default="sum", choices=["sum", "max", "auto"])
     ap.add_argument("--cpu-sample", type=int, default=256, help="tokens per replica for the oracle")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="first run a plain device copy of MIB MiB (reference for HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU: this path has no multi-GPU mode "
@@ -82,6 +84,16 @@ def main():
     import torch
     import moe_synth
     from combine_dp_gather_amd.layer import DeviceWeights, MoELayer, spec_of
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy calibration: {n} bytes read and written per copy")
+        del src, dst
 
     cfg = moe_synth.CONFIGS[args.workload]
     t0 = time.time()

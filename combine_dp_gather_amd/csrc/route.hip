@@ -175,13 +175,16 @@ __global__ __launch_bounds__(G_THREADS) void gate_exact_kernel(const T* __restri
 }
 
 // ------------------------------------------------------------------ selection
-// One wave per global row.  Lane l holds experts e = l + 64*j, j < kMaxPerLane.
+// One wave per global row.  Lane l holds the V consecutive experts e = l*V + j (V = E/64
+// rounded up to a power of two), so a group of E/n_group experts covers E/(n_group*V)
+// neighbouring lanes and group statistics reduce with xor shuffles inside those lanes.
 constexpr int S_THREADS = 256;
+constexpr int S_WAVES = S_THREADS / kWave;
 constexpr int kMaxE = 1024;
-constexpr int kMaxPerLane = kMaxE / kWave;  // 16
 constexpr int kMaxTopK = 32;
 constexpr int kMaxGroups = 64;
-constexpr int kMaxGroupTopn = 8;
+constexpr int kMaxGroupTopn = 4;
+constexpr int kNone = INT32_MAX;
 
 // exp by Cody-Waite reduction and a degree-13 Taylor polynomial (Horner with fused steps):
 //   n = rint(x / ln2), r = x - n*ln2 (ln2 split in a 32-bit head and a tail),
@@ -212,16 +215,18 @@ __device__ double exp_cody_waite(double x) {
 
 __device__ __forceinline__ double sigmoid64(double l) { return 1.0 / (1.0 + exp_cody_waite(-l)); }
 
-// (value, index) wave argmax: larger value wins, equal values go to the lower index.
-// Lanes without a candidate pass idx = INT32_MAX.
+// a ranks before b: larger key, equal keys by lower id; kNone never ranks first
+__device__ __forceinline__ bool ranks_before(double ka, int ia, double kb, int ib) {
+    return ia != kNone && (ib == kNone || ka > kb || (ka == kb && ia < ib));
+}
+
+// (key, id) wave argmax with the same order; every lane ends with the winner
 __device__ __forceinline__ void wave_argmax(double& v, int& idx) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
         const double ov = __shfl_xor(v, off);
         const int oi = __shfl_xor(idx, off);
-        const bool take = (oi != INT32_MAX) &&
-                          (idx == INT32_MAX || ov > v || (ov == v && oi < idx));
-        if (take) {
+        if (ranks_before(ov, oi, v, idx)) {
             v = ov;
             idx = oi;
         }
@@ -234,6 +239,31 @@ __device__ __forceinline__ double wave_sum(double v) {
     return v;
 }
 
+__device__ __forceinline__ double readlane_f64(double v, int l) {
+    const long long b = __double_as_longlong(v);
+    const int lo = __builtin_amdgcn_readlane(static_cast<int>(b & 0xffffffffll), l);
+    const int hi = __builtin_amdgcn_readlane(static_cast<int>(b >> 32), l);
+    return __longlong_as_double((static_cast<long long>(hi) << 32) |
+                                static_cast<long long>(static_cast<unsigned>(lo)));
+}
+
+// sort a lane's V entries best-first (odd-even transposition: static indices only)
+template <int V>
+__device__ __forceinline__ void sort_lane(double (&k)[V], double (&s)[V], int (&id)[V]) {
+#pragma unroll
+    for (int r = 0; r < V; ++r) {
+#pragma unroll
+        for (int i = r & 1; i + 1 < V; i += 2) {
+            if (ranks_before(k[i + 1], id[i + 1], k[i], id[i])) {
+                const double tk = k[i], ts = s[i];
+                const int ti = id[i];
+                k[i] = k[i + 1]; s[i] = s[i + 1]; id[i] = id[i + 1];
+                k[i + 1] = tk; s[i + 1] = ts; id[i + 1] = ti;
+            }
+        }
+    }
+}
+
 struct SelectArgs {
     const float* logits;
     const int32_t* row_valid;
@@ -244,151 +274,136 @@ struct SelectArgs {
     float* w;
 };
 
+template <int V>
 __global__ __launch_bounds__(S_THREADS) void select_kernel(SelectArgs a) {
-    __shared__ double keys_lds[S_THREADS / kWave][kMaxE];
-    const int wv = threadIdx.x / kWave;
     const int lane = lane_id();
-    const int64_t g = static_cast<int64_t>(blockIdx.x) * (S_THREADS / kWave) + wv;
+    const int64_t g = static_cast<int64_t>(blockIdx.x) * S_WAVES + threadIdx.x / kWave;
+    if (g >= a.G) return;  // no block barrier below
     const int E = a.E, k = a.k;
-    // every wave stays to the end (the grouped path has a block barrier); rows past G and
-    // pad rows only skip the work
-    const bool in_range = g < a.G;
-    const bool active = in_range && (a.row_valid == nullptr || a.row_valid[g] != 0);
-    const float* lg = a.logits + (in_range ? g : 0) * E;
-    const int per_lane = (E + kWave - 1) / kWave;
-    double key[kMaxPerLane];
-    double score[kMaxPerLane];  // sigmoid (grouped) or logit (softmax)
-    bool allow[kMaxPerLane];
+    int32_t* ids = a.ids + g * k;
+    float* wout = a.w + g * k;
+    if (a.row_valid && a.row_valid[g] == 0) {  // pad row: no expert load
+        if (lane < k) {
+            ids[lane] = -1;
+            wout[lane] = 0.f;
+        }
+        return;
+    }
+    const float* lg = a.logits + g * E;
+    const bool grouped = a.kind == MOE_ROUTE_GROUPED_SIGMOID;
+    double key[V], score[V];
+    int id[V];
 #pragma unroll
-    for (int j = 0; j < kMaxPerLane; ++j) {
-        const int e = lane + j * kWave;
-        allow[j] = false;
-        key[j] = 0.0;
+    for (int j = 0; j < V; ++j) {
+        const int e = lane * V + j;
+        key[j] = -__builtin_huge_val();
         score[j] = 0.0;
-        if (active && j < per_lane && e < E) {
+        id[j] = kNone;
+        if (e < E) {
             const double l = static_cast<double>(lg[e]);
-            if (a.kind == MOE_ROUTE_SOFTMAX) {
-                score[j] = l;
-                key[j] = l;
-            } else {
+            if (grouped) {
                 score[j] = sigmoid64(l);
                 key[j] = score[j] + (a.bias ? static_cast<double>(a.bias[e]) : 0.0);
+            } else {
+                score[j] = l;
+                key[j] = l;
             }
-            allow[j] = true;
+            id[j] = e;
         }
     }
-    double den = 1.0, mx = 0.0;
-    if (a.kind == MOE_ROUTE_SOFTMAX) {
-        double m = -DBL_MAX;
+    double mx = 0.0, den = 1.0;
+    if (!grouped) {
+        double m = -__builtin_huge_val();
 #pragma unroll
-        for (int j = 0; j < kMaxPerLane; ++j)
-            if (allow[j] && key[j] > m) m = key[j];
+        for (int j = 0; j < V; ++j)
+            if (id[j] != kNone && key[j] > m) m = key[j];
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) m = fmax(m, __shfl_xor(m, off));
         mx = m;
         double s = 0.0;
 #pragma unroll
-        for (int j = 0; j < kMaxPerLane; ++j)
-            if (allow[j]) s += exp(key[j] - mx);
+        for (int j = 0; j < V; ++j)
+            if (id[j] != kNone) s += exp(key[j] - mx);
         den = wave_sum(s);
-    } else {
-        double* kl = keys_lds[wv];
-#pragma unroll
-        for (int j = 0; j < kMaxPerLane; ++j) {
-            const int e = lane + j * kWave;
-            if (allow[j]) kl[e] = key[j];
-        }
-        __syncthreads();
-        // group scores: lane q < n_group scans group q's keys in ascending expert order and
-        // keeps the group_topn largest (a strictly larger key displaces, so equal keys keep
-        // the lower id first); the score adds them largest first
+    }
+    sort_lane<V>(key, score, id);
+    if (grouped) {
         const int per = E / a.n_group;
-        double gscore = 0.0;
-        int gidx = INT32_MAX;
-        if (active && lane < a.n_group) {
-            double top[kMaxGroupTopn];
-            int cnt = 0;
-            for (int e = lane * per; e < (lane + 1) * per; ++e) {
-                const double v = kl[e];
-                int p;
-                if (cnt < a.group_topn) {
-                    p = cnt++;
-                } else if (v > top[a.group_topn - 1]) {
-                    p = a.group_topn - 1;
-                } else {
-                    continue;
-                }
-                while (p > 0 && v > top[p - 1]) {
-                    top[p] = top[p - 1];
-                    --p;
-                }
-                top[p] = v;
-            }
-            double acc = 0.0;
-            for (int j = 0; j < a.group_topn; ++j) acc += top[j];
-            gscore = acc;
-            gidx = lane;
-        }
-        // keep the topk_group best groups (ties to the lower group)
-        uint64_t kept = 0;
-        bool mine_taken = false;
-        if (active) {
-            for (int t = 0; t < a.topk_group; ++t) {
-                double v = mine_taken ? 0.0 : gscore;
-                int i = mine_taken ? INT32_MAX : gidx;
-                wave_argmax(v, i);
-                kept |= (1ull << i);
-                if (i == gidx) mine_taken = true;
-            }
-        }
+        const int lpg = per / V;  // lanes per group (the launcher checks this path applies)
+        const int mygroup = (lane * V) / per;
+        // the group's group_topn largest keys, largest first: merge the lanes' sorted
+        // top-4 lists pairwise (bitonic: elementwise max against the reversed partner,
+        // then a 2-stage half-cleaner)
+        double t[kMaxGroupTopn];
 #pragma unroll
-        for (int j = 0; j < kMaxPerLane; ++j) {
-            const int e = lane + j * kWave;
-            if (allow[j]) allow[j] = (kept >> (e / per)) & 1ull;
+        for (int j = 0; j < kMaxGroupTopn; ++j) t[j] = j < V ? key[j < V ? j : 0] : -__builtin_huge_val();
+        for (int off = 1; off < lpg; off <<= 1) {
+            double o[kMaxGroupTopn];
+#pragma unroll
+            for (int j = 0; j < kMaxGroupTopn; ++j) o[j] = __shfl_xor(t[j], off);
+            double c[kMaxGroupTopn];
+#pragma unroll
+            for (int j = 0; j < kMaxGroupTopn; ++j) c[j] = fmax(t[j], o[kMaxGroupTopn - 1 - j]);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const double hi = fmax(c[j], c[j + 2]), lo = fmin(c[j], c[j + 2]);
+                c[j] = hi;
+                c[j + 2] = lo;
+            }
+#pragma unroll
+            for (int j = 0; j < 4; j += 2) {
+                const double hi = fmax(c[j], c[j + 1]), lo = fmin(c[j], c[j + 1]);
+                c[j] = hi;
+                c[j + 1] = lo;
+            }
+#pragma unroll
+            for (int j = 0; j < kMaxGroupTopn; ++j) t[j] = c[j];
+        }
+        double gscore = 0.0;
+#pragma unroll
+        for (int j = 0; j < kMaxGroupTopn; ++j)
+            if (j < a.group_topn) gscore += t[j];
+        // rank of this lane's group among all groups (higher score first, ties: lower group)
+        int rank = 0;
+        for (int q = 0; q < a.n_group; ++q) {
+            const double sq = readlane_f64(gscore, q * lpg);
+            rank += (sq > gscore || (sq == gscore && q < mygroup)) ? 1 : 0;
+        }
+        if (rank >= a.topk_group || lane * V >= E) {
+#pragma unroll
+            for (int j = 0; j < V; ++j) {
+                key[j] = -__builtin_huge_val();
+                id[j] = kNone;
+            }
         }
     }
-    if (!in_range) return;
-    int32_t* ids = a.ids + g * k;
-    float* wout = a.w + g * k;
-    if (!active) {
-        for (int j = lane; j < k; j += kWave) {
-            ids[j] = -1;
-            wout[j] = 0.f;
-        }
-        return;
-    }
-    // top-k over the allowed keys, descending, ties to the lower id; lane t keeps pick t
+    // k picks, best first: the wave argmax of the lanes' heads; the owner pops its head
     double my_score = 0.0;
     int my_id = -1;
     for (int t = 0; t < k; ++t) {
-        double v = 0.0;
-        int i = INT32_MAX;
-#pragma unroll
-        for (int j = 0; j < kMaxPerLane; ++j) {
-            if (!allow[j]) continue;
-            if (i == INT32_MAX || key[j] > v) {  // ascending e per lane: ties keep the lower id
-                v = key[j];
-                i = lane + j * kWave;
-            }
-        }
+        double v = key[0];
+        int i = id[0];
         wave_argmax(v, i);
-        double sc = 0.0;
+        const int owner = i / V;
+        const double sc = readlane_f64(score[0], owner);
+        if (lane == owner) {
 #pragma unroll
-        for (int j = 0; j < kMaxPerLane; ++j) {
-            if (allow[j] && lane + j * kWave == i) {
-                allow[j] = false;
-                sc = score[j];
+            for (int j = 0; j + 1 < V; ++j) {
+                key[j] = key[j + 1];
+                score[j] = score[j + 1];
+                id[j] = id[j + 1];
             }
+            key[V - 1] = -__builtin_huge_val();
+            id[V - 1] = kNone;
         }
-        sc = __shfl(sc, i & (kWave - 1));
         if (lane == t) {
             my_score = sc;
             my_id = i;
         }
     }
-    const double p = (a.kind == MOE_ROUTE_SOFTMAX) ? exp(my_score - mx) / den : my_score;
+    const double p = grouped ? my_score : exp(my_score - mx) / den;
     double sum = 0.0;
-    for (int t = 0; t < k; ++t) sum += __shfl(p, t);  // slot order
+    for (int t = 0; t < k; ++t) sum += readlane_f64(p, t);  // slot order
     if (lane < k) {
         ids[lane] = my_id;
         wout[lane] = static_cast<float>(a.renorm ? p / sum : p);
@@ -411,6 +426,12 @@ moe_status check_route_cfg(const moe_route_cfg* c) {
     return MOE_OK;
 }
 
+int lanes_per_expert_chunk(int E) {
+    int v = 1;
+    while (v * kWave < E) v <<= 1;
+    return v;
+}
+
 moe_status launch_select(const float* logits, const int32_t* row_valid, int64_t G,
                          const float* bias, const moe_route_cfg* c, int32_t* ids, float* w,
                          hipStream_t stream) {
@@ -428,10 +449,21 @@ moe_status launch_select(const float* logits, const int32_t* row_valid, int64_t 
     a.renorm = c->renormalize;
     a.ids = ids;
     a.w = w;
-    const int rows_per_block = S_THREADS / kWave;
-    const int64_t blocks = ceil_div(G, rows_per_block);
-    hipLaunchKernelGGL(select_kernel, dim3(static_cast<unsigned>(blocks)), dim3(S_THREADS), 0,
-                       stream, a);
+    const int V = lanes_per_expert_chunk(a.E);
+    if (a.kind == MOE_ROUTE_GROUPED_SIGMOID) {
+        // groups must be whole lanes: per % V == 0, per / V a power of two
+        const int per = a.E / a.n_group;
+        const int lpg = per / V;
+        if (per % V != 0 || lpg < 1 || (lpg & (lpg - 1)) != 0) return MOE_ERR_UNSUPPORTED;
+    }
+    const dim3 grid(static_cast<unsigned>(ceil_div(G, S_WAVES)));
+    switch (V) {
+        case 1: hipLaunchKernelGGL(select_kernel<1>, grid, dim3(S_THREADS), 0, stream, a); break;
+        case 2: hipLaunchKernelGGL(select_kernel<2>, grid, dim3(S_THREADS), 0, stream, a); break;
+        case 4: hipLaunchKernelGGL(select_kernel<4>, grid, dim3(S_THREADS), 0, stream, a); break;
+        case 8: hipLaunchKernelGGL(select_kernel<8>, grid, dim3(S_THREADS), 0, stream, a); break;
+        default: hipLaunchKernelGGL(select_kernel<16>, grid, dim3(S_THREADS), 0, stream, a); break;
+    }
     MOE_LAUNCH_CHECK();
     return MOE_OK;
 }
