@@ -29,9 +29,10 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx16_t __attribute__((ext_vector_type(16)));
 
-constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int BM = 256, BN = 256;
+constexpr int BK = 32;      // K slice per pipeline stage
+constexpr int STAGES = 4;   // LDS stages: STAGES-1 slices in flight
 constexpr int M_THREADS = 256;
-constexpr int LDS_STRIDE = BK + 8;  // bf16 elements per LDS row
 constexpr int kMaxSlots = 1024;
 constexpr int UP_COLS = BN / 2;     // i-columns per up tile (gate and up each)
 
@@ -58,16 +59,39 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
                                              static_cast<int>(bytes), kBufferFlags);
 }
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Tiles are numbered (m-tile over all slots) x (column tile).  Launched with one block per
+// CU; the hardware hands workgroup b to XCD b % 8, so block b takes, in round r, tile q of
+// super-tile r*8 + b%8 (q = b/8): the 32 blocks of one XCD work on one SM x SN patch of
+// tiles at a time and share its A rows and B columns through that XCD's L2.
+struct TileOrder {
+    int32_t SM, SN;  // super-tile = SM m-tiles x SN column tiles, SM*SN = blocks per XCD
+};
+
+// LDS layout of a stage: 256 rows x BK bf16 per operand, rows of BK/8 16-byte chunks.  The
+// LDS serves a 16-byte-per-lane read 16 lanes at a time from 64 banks (256 bytes); the
+// fragment reads have 16 consecutive rows asking for the same logical chunk, so the chunk
+// index is xor-ed with swz(row) = (row / rows-per-256-bytes) mod chunks-per-row, which puts
+// those 16 rows on 16 distinct 16-byte slots of the 256-byte bank window.
+constexpr int CPR = BK / 8;            // 16-byte chunks per row
+constexpr int RPB = 64 / CPR;          // rows per 1 KB DMA block (one wave instruction)
+constexpr int NBLK = BM / RPB;         // DMA blocks per operand per stage
+constexpr int LPW = 2 * NBLK / 4;      // DMA instructions per wave per stage
+static_assert(BK == 32 || BK == 64, "swizzle written for 32- or 64-wide K slices");
+__device__ __forceinline__ int swz(int row) { return BK == 64 ? ((row >> 1) & 7) : ((row >> 2) & 3); }
+
 template <bool UP>
-__global__ __launch_bounds__(M_THREADS, 1) void grouped_gemm_bf16_kernel(GemmArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LDS_STRIDE];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * LDS_STRIDE];
+__global__ __launch_bounds__(M_THREADS, 1) void grouped_gemm_bf16_kernel(GemmArgs a, TileOrder to) {
+    __shared__ __attribute__((aligned(1024))) uint16_t As[STAGES][BM * BK];
+    __shared__ __attribute__((aligned(1024))) uint16_t Bs[STAGES][BN * BK];
     __shared__ int32_t tile_prefix[kMaxSlots + 1];  // m-tiles before slot e
     __shared__ int32_t part[M_THREADS];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wv = tid >> 6;
+    // wave index as a scalar: the DMA's LDS destination must be wave-uniform
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wv >> 1, wn = wv & 1;
 
     // ---- number the tiles: slot e owns ceil(rows_e / BM) m-tiles
@@ -107,22 +131,33 @@ __global__ __launch_bounds__(M_THREADS, 1) void grouped_gemm_bf16_kernel(GemmArg
         __syncthreads();
     }
     const int32_t total_mt = tile_prefix[a.El];
-    const int64_t total_tiles = static_cast<int64_t>(total_mt) * a.NT;
     const uint32_t row_bytes = static_cast<uint32_t>(a.K) * 2u;
-    const int lr = tid >> 3;       // first LDS row this thread fills (then + 32 p)
-    const int ch = tid & 7;        // 16-byte chunk of the 128-byte K slice
+    const int nsn = a.NT / to.SN;
+    const int64_t total_super = static_cast<int64_t>((total_mt + to.SM - 1) / to.SM) * nsn;
+    const int xcd = blockIdx.x & 7;
+    const int q = blockIdx.x >> 3;
+    // this lane's 16-byte chunk inside a DMA block of RPB rows x CPR chunks
+    const int dma_row = lane / CPR;
+    // fragment reads: row lane%32 of a 32-row block, logical chunk 2*ks + lane/32
+    const int frow = lane & 31;
+    int fchunk[BK / 16];
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) fchunk[ks] = ((2 * ks + (lane >> 5)) ^ swz(frow)) * 8;
 
-    for (int64_t t = blockIdx.x; t < total_tiles; t += gridDim.x) {
-        const int32_t em = static_cast<int32_t>(t / a.NT);
-        const int32_t nt = static_cast<int32_t>(t % a.NT);
+    for (int64_t sup = xcd; sup < total_super; sup += 8) {
+        const int32_t em = static_cast<int32_t>(sup / nsn) * to.SM + q / to.SN;
+        const int32_t nt = static_cast<int32_t>(sup % nsn) * to.SN + q % to.SN;
+        if (em >= total_mt) continue;
         int lo = 0, hi = a.El;
         while (hi - lo > 1) {
             const int mid = (lo + hi) >> 1;
             if (tile_prefix[mid] <= em) lo = mid;
             else hi = mid;
         }
-        const int e = lo;
-        const int32_t mtile = em - tile_prefix[e];
+        // the tile coordinates are block-uniform: keep them in scalar registers so the
+        // buffer descriptors below are scalar too
+        const int e = __builtin_amdgcn_readfirstlane(lo);
+        const int32_t mtile = __builtin_amdgcn_readfirstlane(em - tile_prefix[e]);
         const int64_t seg_start = a.seg[e];
         int64_t seg_end = seg_start + a.counts[e];
         seg_end = seg_end < a.cap ? seg_end : a.cap;
@@ -130,28 +165,51 @@ __global__ __launch_bounds__(M_THREADS, 1) void grouped_gemm_bf16_kernel(GemmArg
         const int64_t nrows64 = seg_end - row0;
         const uint32_t nrows = static_cast<uint32_t>(nrows64 < BM ? nrows64 : BM);
 
-        // A: rows past the segment end fall outside the resource and load as zeros
-        const __amdgpu_buffer_rsrc_t ra_rsrc = make_rsrc(a.A + row0 * a.K, nrows * row_bytes);
-        const uint16_t* bbase;
-        uint32_t bbytes;
-        if (UP) {
-            bbase = a.B + static_cast<int64_t>(e) * 2 * a.N * a.K;
-            bbytes = static_cast<uint32_t>(2 * a.N) * row_bytes;
+        // waves 0,1 stream A (NBLK/2 blocks each), waves 2,3 stream B
+        const bool loads_a = wv < 2;
+        const uint16_t* dbase;
+        uint32_t dbytes;
+        if (loads_a) {
+            // rows past the segment end fall outside the resource: they read as zeros
+            dbase = a.A + row0 * a.K;
+            dbytes = nrows * row_bytes;
+        } else if (UP) {
+            dbase = a.B + static_cast<int64_t>(e) * 2 * a.N * a.K;
+            dbytes = static_cast<uint32_t>(2 * a.N) * row_bytes;
         } else {
-            bbase = a.B + static_cast<int64_t>(e) * a.N * a.K;
-            bbytes = static_cast<uint32_t>(a.N) * row_bytes;
+            dbase = a.B + static_cast<int64_t>(e) * a.N * a.K;
+            dbytes = static_cast<uint32_t>(a.N) * row_bytes;
         }
-        const __amdgpu_buffer_rsrc_t rb_rsrc = make_rsrc(bbase, bbytes);
-        uint32_t aoff[8], boff[8];
+        // wave-uniform by construction; say so, so the descriptor lives in scalar registers
+        const uint64_t db64 = reinterpret_cast<uint64_t>(dbase);
+        const uint32_t dlo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(db64));
+        const uint32_t dhi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(db64 >> 32));
+        dbase = reinterpret_cast<const uint16_t*>((static_cast<uint64_t>(dhi) << 32) | dlo);
+        dbytes = __builtin_amdgcn_readfirstlane(dbytes);
+        const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(dbase, dbytes);
+        uint32_t voff[LPW];
 #pragma unroll
-        for (int p = 0; p < 8; ++p) {
-            const int r = lr + 32 * p;
-            aoff[p] = static_cast<uint32_t>(r) * row_bytes + ch * 16;
-            uint32_t brow;
-            if (UP) brow = static_cast<uint32_t>((r >> 7) * a.N + nt * UP_COLS + (r & (UP_COLS - 1)));
-            else brow = static_cast<uint32_t>(nt * BN + r);
-            boff[p] = brow * row_bytes + ch * 16;
+        for (int p = 0; p < LPW; ++p) {
+            const int r = ((wv & 1) * LPW + p) * RPB + dma_row;  // tile row 0..255
+            uint32_t grow;
+            if (loads_a) grow = static_cast<uint32_t>(r);
+            else if (UP) grow = static_cast<uint32_t>((r >> 7) * a.N + nt * UP_COLS + (r & (UP_COLS - 1)));
+            else grow = static_cast<uint32_t>(nt * BN + r);
+            voff[p] = grow * row_bytes + static_cast<uint32_t>(((lane % CPR) ^ swz(r)) * 16);
         }
+        auto issue = [&](int buf, int64_t kt) {
+            const int soff = static_cast<int>(kt * BK * 2);
+            // computed at the call, not hoisted: one scalar add per DMA instead of a table of
+            // LDS addresses held in scalar registers for every stage
+            int off = buf * (BM * BK) + (wv & 1) * LPW * 512;
+            asm volatile("" : "+s"(off));
+            uint16_t* base = (loads_a ? &As[0][0] : &Bs[0][0]) + off;
+#pragma unroll
+            for (int p = 0; p < LPW; ++p) {
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(base + p * 512), 16, voff[p],
+                                                        soff, 0, 0);
+            }
+        };
 
         floatx16_t acc[4][4];
 #pragma unroll
@@ -161,58 +219,70 @@ __global__ __launch_bounds__(M_THREADS, 1) void grouped_gemm_bf16_kernel(GemmArg
 #pragma unroll
                 for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-        v4i_t ra[8], rb[8];
-        auto gload = [&](int64_t kt) {
-            const int soff = static_cast<int>(kt * BK * 2);
-#pragma unroll
-            for (int p = 0; p < 8; ++p) {
-                ra[p] = __builtin_amdgcn_raw_buffer_load_b128(ra_rsrc, aoff[p], soff, 0);
-                rb[p] = __builtin_amdgcn_raw_buffer_load_b128(rb_rsrc, boff[p], soff, 0);
-            }
-        };
-        auto sstore = [&](int buf) {
-#pragma unroll
-            for (int p = 0; p < 8; ++p) {
-                const int r = lr + 32 * p;
-                *reinterpret_cast<v4i_t*>(&As[buf][r * LDS_STRIDE + ch * 8]) = ra[p];
-                *reinterpret_cast<v4i_t*>(&Bs[buf][r * LDS_STRIDE + ch * 8]) = rb[p];
-            }
-        };
+        const uint16_t* a_rd = &As[0][0] + (wm * 128 + frow) * BK;
+        const uint16_t* b_rd = &Bs[0][0] + frow * BK;
+        // B block j of the wave: up -> blocks 0,1 gate, 2,3 the matching up rows
+#define MOE_BROW(j) (UP ? ((j) >> 1) * UP_COLS + wn * 64 + ((j) & 1) * 32 : wn * 128 + (j) * 32)
+#define MOE_LOAD_FRAGS(FA, FB, BUF)                                                           \
+    do {                                                                                      \
+        const uint16_t* Ab_ = a_rd + (BUF) * (BM * BK);                                       \
+        const uint16_t* Bb_ = b_rd + (BUF) * (BN * BK);                                       \
+        _Pragma("unroll") for (int ks_ = 0; ks_ < BK / 16; ++ks_) {                           \
+            _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) FA[ks_][i_] =                    \
+                *reinterpret_cast<const bf16x8_t*>(Ab_ + i_ * 32 * BK + fchunk[ks_]);         \
+            _Pragma("unroll") for (int j_ = 0; j_ < 4; ++j_) FB[ks_][j_] =                    \
+                *reinterpret_cast<const bf16x8_t*>(Bb_ + MOE_BROW(j_) * BK + fchunk[ks_]);    \
+        }                                                                                     \
+    } while (0)
+#define MOE_MFMA_KS(FA, FB, KS)                                                               \
+    do {                                                                                      \
+        _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_)                                      \
+            _Pragma("unroll") for (int j_ = 0; j_ < 4; ++j_) acc[i_][j_] =                    \
+                __builtin_amdgcn_mfma_f32_32x32x16_bf16(FA[KS][i_], FB[KS][j_], acc[i_][j_],  \
+                                                        0, 0, 0);                             \
+    } while (0)
+        // Pipeline: slices of BK along K, STAGES LDS buffers.  Step kt always refills, so
+        // exactly STAGES-2 slices issued after slice kt+1 can still be in flight when slice
+        // kt+1 is needed; refills past the last slice re-read the last slice (clamped) and are
+        // never consumed.
+#define MOE_SYNC(N)                                                                           \
+    do {                                                                                      \
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(N) : "memory");                  \
+        __builtin_amdgcn_s_barrier();                                                         \
+        asm volatile("" ::: "memory");                                                        \
+    } while (0)
+        // slice KT_: first half of its MFMAs; meet (slice KT_+1 landed everywhere, every wave
+        // done reading slice KT_); refill slice KT_'s buffer; read slice KT_+1's fragments
+        // into the other register set; second half of slice KT_'s MFMAs
+#define MOE_STEP(CA, CB, NA, NB, KT_)                                                         \
+    do {                                                                                      \
+        MOE_MFMA_KS(CA, CB, 0);                                                               \
+        MOE_SYNC((STAGES - 2) * LPW);                                                         \
+        issue(static_cast<int>((KT_) % STAGES),                                               \
+              (KT_) + STAGES < KT ? (KT_) + STAGES : KT - 1);                                 \
+        MOE_LOAD_FRAGS(NA, NB, static_cast<int>(((KT_) + 1) % STAGES));                       \
+        _Pragma("unroll") for (int ks2_ = 1; ks2_ < BK / 16; ++ks2_) MOE_MFMA_KS(CA, CB, ks2_); \
+    } while (0)
 
-        const int64_t KT = a.K / BK;
-        gload(0);
-        sstore(0);
+        const int64_t KT = a.K / BK;  // even: K is a multiple of 2*BK
+        // the previous tile's trailing DMAs and every wave's reads of the stage buffers are done
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
         __syncthreads();
-        const int frow = lane & 31;
-        const int fk = (lane >> 5) * 8;
-        for (int64_t kt = 0; kt < KT; ++kt) {
-            const int cur = static_cast<int>(kt & 1);
-            if (kt + 1 < KT) gload(kt + 1);
-            const uint16_t* Ab = As[cur] + (wm * 128 + frow) * LDS_STRIDE + fk;
-            const uint16_t* Bb = Bs[cur] + fk;
+        // prologue: slices 0..STAGES-1 in flight, slice 0's fragments in registers
 #pragma unroll
-            for (int ks = 0; ks < BK / 16; ++ks) {
-                bf16x8_t af[4], bfr[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    af[i] = *reinterpret_cast<const bf16x8_t*>(Ab + i * 32 * LDS_STRIDE + ks * 16);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    // up: wave column blocks 0,1 are gate, 2,3 the matching up blocks
-                    int brow;
-                    if (UP) brow = (j >> 1) * UP_COLS + wn * 64 + (j & 1) * 32 + frow;
-                    else brow = wn * 128 + j * 32 + frow;
-                    bfr[j] = *reinterpret_cast<const bf16x8_t*>(Bb + brow * LDS_STRIDE + ks * 16);
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-            }
-            if (kt + 1 < KT) sstore(cur ^ 1);
-            __syncthreads();
+        for (int st = 0; st < STAGES; ++st) issue(st, st < KT ? st : KT - 1);
+        MOE_SYNC((STAGES - 1) * LPW);
+        bf16x8_t fa0[BK / 16][4], fb0[BK / 16][4], fa1[BK / 16][4], fb1[BK / 16][4];
+        MOE_LOAD_FRAGS(fa0, fb0, 0);
+        for (int64_t kt = 0; kt < KT; kt += 2) {
+            MOE_STEP(fa0, fb0, fa1, fb1, kt);
+            MOE_STEP(fa1, fb1, fa0, fb0, kt + 1);
         }
+#undef MOE_STEP
+#undef MOE_SYNC
+#undef MOE_MFMA_KS
+#undef MOE_LOAD_FRAGS
+#undef MOE_BROW
 
         // ---- epilogue: lane holds rows 8*(v/4) + 4*(lane/32) + v%4 of column lane%32.
         // The lane's row base is made opaque per tile so the 64 row offsets below stay
@@ -239,6 +309,8 @@ __global__ __launch_bounds__(M_THREADS, 1) void grouped_gemm_bf16_kernel(GemmArg
             }
         }
     }
+    // no DMA into LDS may outlive the workgroup
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 // ------------------------------------------------------------------ simple path
@@ -362,9 +434,22 @@ moe_status run_stage(bool up, const void* A, moe_dtype act_dt, const moe_plan* p
         g.N = N;
         g.El = plan->num_slots;
         g.NT = static_cast<int32_t>(up ? I / UP_COLS : H / BN);
-        const dim3 grid(static_cast<unsigned>(num_cus()));
-        if (up) hipLaunchKernelGGL(grouped_gemm_bf16_kernel<true>, grid, dim3(M_THREADS), 0, stream, g);
-        else hipLaunchKernelGGL(grouped_gemm_bf16_kernel<false>, grid, dim3(M_THREADS), 0, stream, g);
+        // one block per CU, 8 XCDs: a super-tile of SM x SN tiles per XCD per round
+        const int blocks = num_cus();
+        const int per_xcd = blocks / 8;
+        TileOrder to;
+        to.SN = 1;
+        for (int sn : {8, 4, 2}) {
+            if (g.NT % sn == 0 && per_xcd % sn == 0) {
+                to.SN = sn;
+                break;
+            }
+        }
+        to.SM = per_xcd / to.SN;
+        if (blocks % 8 != 0 || to.SM < 1) return MOE_ERR_UNSUPPORTED;
+        const dim3 grid(static_cast<unsigned>(blocks));
+        if (up) hipLaunchKernelGGL(grouped_gemm_bf16_kernel<true>, grid, dim3(M_THREADS), 0, stream, g, to);
+        else hipLaunchKernelGGL(grouped_gemm_bf16_kernel<false>, grid, dim3(M_THREADS), 0, stream, g, to);
         MOE_LAUNCH_CHECK();
         return MOE_OK;
     }
