@@ -18,97 +18,54 @@ namespace moe {
 namespace {
 
 // ------------------------------------------------------------------ gate logits
-constexpr int GB_M = 128, GB_N = 128, GB_K = 32, G_THREADS = 256;
-constexpr int G_PAD = 4;  // LDS row padding (floats)
+// Exact-order gate on the fp32 matrix cores.  v_mfma_f32_32x32x1_2b_f32 adds exactly one
+// product to each of its 2x32x32 accumulators per instruction, with a single rounding, so a
+// chain of them over h = 0..H-1 is the fmaf chain of the definition above, bit for bit
+// (checked against the VALU fma chain on bf16-valued, full fp32 and subnormal operands).
+// Block: 128 rows x 256 experts (x is read from HBM once), 4 waves of 64 rows x 128 experts.
+// A wave runs four independent accumulator chains (2 blocks of 32x32 each): A = its 64 rows,
+// B = two 32-expert groups per chain, the halves of the wave swapped between chain pairs so
+// the four chains cover all 2x4 row/expert blocks.  32-deep K slices are staged in LDS in
+// the input type (row stride padded by 4 elements: conflict-free reads of 4 consecutive k).
+typedef float floatx32_t __attribute__((ext_vector_type(32)));
+constexpr int GB_M = 128, GB_N = 256, GB_K = 32, G_THREADS = 256;
+constexpr int G_PAD = 4;
 
 template <typename T>
-struct GateLoad;
+struct GateIO;
 
-// bf16: one 16-byte load = 8 consecutive h of one row
 template <>
-struct GateLoad<uint16_t> {
-    static constexpr int kPerThread = (GB_M * GB_K) / (8 * G_THREADS);  // 2
-    __device__ static void load(const uint16_t* __restrict__ src, int64_t rows, int64_t H,
-                                int64_t r0, int64_t k0, uint4 (&buf)[kPerThread]) {
-#pragma unroll
-        for (int p = 0; p < kPerThread; ++p) {
-            const int idx = threadIdx.x + p * G_THREADS;  // 0..511
-            const int r = idx >> 2, c = (idx & 3) * 8;
-            const int64_t gr = r0 + r, gk = k0 + c;
-            uint4 v = {0, 0, 0, 0};
-            if (gr < rows) {
-                const uint16_t* ptr = src + gr * H + gk;
-                if (gk + 8 <= H && ((reinterpret_cast<uintptr_t>(ptr) & 15) == 0)) {
-                    v = *reinterpret_cast<const uint4*>(ptr);
-                } else {
-                    uint16_t t[8];
-#pragma unroll
-                    for (int q = 0; q < 8; ++q) t[q] = (gk + q < H) ? ptr[q] : 0;
-                    v.x = t[0] | (uint32_t(t[1]) << 16);
-                    v.y = t[2] | (uint32_t(t[3]) << 16);
-                    v.z = t[4] | (uint32_t(t[5]) << 16);
-                    v.w = t[6] | (uint32_t(t[7]) << 16);
-                }
-            }
-            buf[p] = v;
-        }
-    }
-    __device__ static void store(float (*lds)[GB_M + G_PAD], const uint4 (&buf)[kPerThread]) {
-#pragma unroll
-        for (int p = 0; p < kPerThread; ++p) {
-            const int idx = threadIdx.x + p * G_THREADS;
-            const int r = idx >> 2, c = (idx & 3) * 8;
-            const uint32_t w[4] = {buf[p].x, buf[p].y, buf[p].z, buf[p].w};
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                lds[c + 2 * q][r] = __uint_as_float(w[q] << 16);
-                lds[c + 2 * q + 1][r] = __uint_as_float(w[q] & 0xffff0000u);
-            }
-        }
+struct GateIO<uint16_t> {  // bf16 rows; 16-byte chunk = 8 k values
+    static constexpr int kChunk = 8;
+    typedef uint2 Quad;  // 4 consecutive k
+    __device__ static float val(const Quad& q, int t) {
+        const uint32_t w = t < 2 ? q.x : q.y;
+        return __uint_as_float((t & 1) ? (w & 0xffff0000u) : (w << 16));
     }
 };
-
-// fp32: one 16-byte load = 4 consecutive h of one row
 template <>
-struct GateLoad<float> {
-    static constexpr int kPerThread = (GB_M * GB_K) / (4 * G_THREADS);  // 4
-    __device__ static void load(const float* __restrict__ src, int64_t rows, int64_t H, int64_t r0,
-                                int64_t k0, float4 (&buf)[kPerThread]) {
-#pragma unroll
-        for (int p = 0; p < kPerThread; ++p) {
-            const int idx = threadIdx.x + p * G_THREADS;  // 0..1023
-            const int r = idx >> 3, c = (idx & 7) * 4;
-            const int64_t gr = r0 + r, gk = k0 + c;
-            float4 v = {0.f, 0.f, 0.f, 0.f};
-            if (gr < rows) {
-                const float* ptr = src + gr * H + gk;
-                if (gk + 4 <= H && ((reinterpret_cast<uintptr_t>(ptr) & 15) == 0)) {
-                    v = *reinterpret_cast<const float4*>(ptr);
-                } else {
-                    v.x = (gk + 0 < H) ? ptr[0] : 0.f;
-                    v.y = (gk + 1 < H) ? ptr[1] : 0.f;
-                    v.z = (gk + 2 < H) ? ptr[2] : 0.f;
-                    v.w = (gk + 3 < H) ? ptr[3] : 0.f;
-                }
-            }
-            buf[p] = v;
-        }
-    }
-    __device__ static void store(float (*lds)[GB_M + G_PAD], const float4 (&buf)[kPerThread]) {
-#pragma unroll
-        for (int p = 0; p < kPerThread; ++p) {
-            const int idx = threadIdx.x + p * G_THREADS;
-            const int r = idx >> 3, c = (idx & 7) * 4;
-            lds[c + 0][r] = buf[p].x;
-            lds[c + 1][r] = buf[p].y;
-            lds[c + 2][r] = buf[p].z;
-            lds[c + 3][r] = buf[p].w;
-        }
+struct GateIO<float> {  // fp32 rows; 16-byte chunk = 4 k values
+    static constexpr int kChunk = 4;
+    typedef float4 Quad;
+    __device__ static float val(const Quad& q, int t) {
+        return t == 0 ? q.x : (t == 1 ? q.y : (t == 2 ? q.z : q.w));
     }
 };
 
 template <typename T>
-using GateBuf = typename std::conditional<std::is_same<T, float>::value, float4, uint4>::type;
+__device__ __forceinline__ uint4 load_chunk(const T* __restrict__ src, int64_t rows, int64_t H,
+                                            int64_t r, int64_t k) {
+    constexpr int C = GateIO<T>::kChunk;
+    uint4 v = {0, 0, 0, 0};
+    if (r >= rows) return v;
+    const T* p = src + r * H + k;
+    if (k + C <= H && ((reinterpret_cast<uintptr_t>(p) & 15) == 0)) return *reinterpret_cast<const uint4*>(p);
+    T t[C];
+#pragma unroll
+    for (int q = 0; q < C; ++q) t[q] = (k + q < H) ? p[q] : T(0);
+    __builtin_memcpy(&v, t, 16);
+    return v;
+}
 
 template <typename T>
 __global__ __launch_bounds__(G_THREADS) void gate_exact_kernel(const T* __restrict__ x,
@@ -116,60 +73,104 @@ __global__ __launch_bounds__(G_THREADS) void gate_exact_kernel(const T* __restri
                                                                const int32_t* __restrict__ row_valid,
                                                                int64_t G, int64_t E, int64_t H,
                                                                float* __restrict__ logits) {
-    __shared__ float As[2][GB_K][GB_M + G_PAD];
-    __shared__ float Bs[2][GB_K][GB_N + G_PAD];
-    using L = GateLoad<T>;
-    const int64_t m0 = static_cast<int64_t>(blockIdx.y) * GB_M;
-    const int64_t n0 = static_cast<int64_t>(blockIdx.x) * GB_N;
-    const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+    constexpr int C = GateIO<T>::kChunk;
+    constexpr int LD = GB_K + G_PAD;                 // LDS row stride (elements)
+    constexpr int XCH = GB_M * GB_K / C / G_THREADS;  // x chunks per thread per slice
+    constexpr int WCH = GB_N * GB_K / C / G_THREADS;  // w chunks per thread per slice
+    __shared__ __attribute__((aligned(16))) T xs[2][GB_M * LD];
+    __shared__ __attribute__((aligned(16))) T ws[2][GB_N * LD];
+    typedef typename GateIO<T>::Quad Quad;
 
-    GateBuf<T> abuf[L::kPerThread], bbuf[L::kPerThread];
-    float acc[8][8];
+    const int64_t m0 = static_cast<int64_t>(blockIdx.x) * GB_M;
+    const int64_t n0 = static_cast<int64_t>(blockIdx.y) * GB_N;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int wm = wv >> 1, wn = wv & 1;
+    const int half = lane >> 5;
+
+    uint4 xr[XCH], wr[WCH];
+    auto gload = [&](int64_t k0) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+        for (int p = 0; p < XCH; ++p) {
+            const int idx = tid + p * G_THREADS;
+            xr[p] = load_chunk(x, G, H, m0 + idx / (GB_K / C), k0 + (idx % (GB_K / C)) * C);
+        }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = 0.f;
+        for (int p = 0; p < WCH; ++p) {
+            const int idx = tid + p * G_THREADS;
+            wr[p] = load_chunk(w, E, H, n0 + idx / (GB_K / C), k0 + (idx % (GB_K / C)) * C);
+        }
+    };
+    auto sstore = [&](int buf) {
+#pragma unroll
+        for (int p = 0; p < XCH; ++p) {
+            const int idx = tid + p * G_THREADS;
+            T* d = &xs[buf][(idx / (GB_K / C)) * LD + (idx % (GB_K / C)) * C];
+            reinterpret_cast<uint2*>(d)[0] = make_uint2(xr[p].x, xr[p].y);
+            reinterpret_cast<uint2*>(d)[1] = make_uint2(xr[p].z, xr[p].w);
+        }
+#pragma unroll
+        for (int p = 0; p < WCH; ++p) {
+            const int idx = tid + p * G_THREADS;
+            T* d = &ws[buf][(idx / (GB_K / C)) * LD + (idx % (GB_K / C)) * C];
+            reinterpret_cast<uint2*>(d)[0] = make_uint2(wr[p].x, wr[p].y);
+            reinterpret_cast<uint2*>(d)[1] = make_uint2(wr[p].z, wr[p].w);
+        }
+    };
+
+    // operand rows of this lane: A row (wave row = lane), B expert row for each chain
+    const int arow = wm * 64 + lane;
+    int brow[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) brow[c] = wn * 128 + 32 * ((c & 2) + ((c & 1) ^ half)) + (lane & 31);
+
+    floatx32_t acc[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int v = 0; v < 32; ++v) acc[c][v] = 0.f;
 
     const int64_t KT = (H + GB_K - 1) / GB_K;
-    L::load(x, G, H, m0, 0, abuf);
-    L::load(w, E, H, n0, 0, bbuf);
-    L::store(As[0], abuf);
-    L::store(Bs[0], bbuf);
+    gload(0);
+    sstore(0);
     __syncthreads();
     for (int64_t kt = 0; kt < KT; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < KT) {
-            L::load(x, G, H, m0, (kt + 1) * GB_K, abuf);
-            L::load(w, E, H, n0, (kt + 1) * GB_K, bbuf);
-        }
-#pragma unroll 4
-        for (int kk = 0; kk < GB_K; ++kk) {
-            const float4 a0 = *reinterpret_cast<const float4*>(&As[cur][kk][ty * 8]);
-            const float4 a1 = *reinterpret_cast<const float4*>(&As[cur][kk][ty * 8 + 4]);
-            const float4 b0 = *reinterpret_cast<const float4*>(&Bs[cur][kk][tx * 8]);
-            const float4 b1 = *reinterpret_cast<const float4*>(&Bs[cur][kk][tx * 8 + 4]);
-            const float a[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-            const float b[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+        const int cur = static_cast<int>(kt & 1);
+        if (kt + 1 < KT) gload((kt + 1) * GB_K);
+        const T* xa = &xs[cur][arow * LD];
+        const T* wb[4];
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
+        for (int c = 0; c < 4; ++c) wb[c] = &ws[cur][brow[c] * LD];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) acc[i][j] = __builtin_fmaf(a[i], b[j], acc[i][j]);
+        for (int kg = 0; kg < GB_K / 4; ++kg) {
+            const Quad qa = *reinterpret_cast<const Quad*>(xa + kg * 4);
+            Quad qb[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) qb[c] = *reinterpret_cast<const Quad*>(wb[c] + kg * 4);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const float av = GateIO<T>::val(qa, t);
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    acc[c] = __builtin_amdgcn_mfma_f32_32x32x1f32(av, GateIO<T>::val(qb[c], t), acc[c], 0, 0, 0);
+            }
         }
-        if (kt + 1 < KT) {
-            L::store(As[cur ^ 1], abuf);
-            L::store(Bs[cur ^ 1], bbuf);
-        }
+        if (kt + 1 < KT) sstore(cur ^ 1);
         __syncthreads();
     }
+    // block b of chain c: rows 32b + 8*(v/4) + 4*(lane/32) + v%4, expert group (c&2)+((c&1)^b)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int64_t g = m0 + ty * 8 + i;
-        if (g >= G) break;
-        const bool valid = row_valid == nullptr || row_valid[g] != 0;
+    for (int c = 0; c < 4; ++c) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int64_t e = n0 + tx * 8 + j;
-            if (e < E) logits[g * E + e] = valid ? acc[i][j] : 0.f;
+        for (int b = 0; b < 2; ++b) {
+            const int64_t e = n0 + wn * 128 + 32 * ((c & 2) + ((c & 1) ^ b)) + (lane & 31);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int64_t g = m0 + wm * 64 + 32 * b + 8 * (v >> 2) + 4 * half + (v & 3);
+                if (g < G && e < E) {
+                    const bool valid = row_valid == nullptr || row_valid[g] != 0;
+                    logits[g * E + e] = valid ? acc[c][16 * b + v] : 0.f;
+                }
+            }
         }
     }
 }
@@ -495,8 +496,8 @@ extern "C" moe_status moe_route(const void* global_x, const int32_t* row_valid, 
     MOE_CHECK_ARG(global_x && w_router && logits && topk_ids && topk_w);
     MOE_CHECK_ARG(G <= (int64_t)1 << 31);
     const int64_t E = cfg->num_experts;
-    dim3 grid(static_cast<unsigned>(moe::ceil_div(E, moe::GB_N)),
-              static_cast<unsigned>(moe::ceil_div(G, moe::GB_M)));
+    dim3 grid(static_cast<unsigned>(moe::ceil_div(G, moe::GB_M)),
+              static_cast<unsigned>(moe::ceil_div(E, moe::GB_N)));
     if (dt == MOE_BF16) {
         hipLaunchKernelGGL(moe::gate_exact_kernel<uint16_t>, grid, dim3(moe::G_THREADS), 0, stream,
                            static_cast<const uint16_t*>(global_x),
