@@ -8,22 +8,38 @@
 //     h[r, i] = silu(sum_h x[r,h] Wg[e][i,h]) * (sum_h x[r,h] Wu[e][i,h])
 //     y[r, c] = sum_i h[r,i] Wd[e][c,i]
 //
-// bf16 path (gfx950 MFMA v_mfma_f32_32x32x16_bf16, fp32 accumulate):
-//   - block tile 256 rows x 256 columns, K slices of 64, 4 waves in a 2x2 grid, each wave
-//     128x128 = 4x4 MFMA blocks (256 fp32 accumulators per lane);
+// bf16 path (gfx950 v_mfma_f32_32x32x16_bf16, fp32 accumulate):
+//   - block tile 256 rows x 256 columns, 4 waves in a 2x2 grid, each wave 128x128 = 4x4 MFMA
+//     blocks (256 fp32 accumulators per lane, in AGPRs);
 //   - up kernel: the 256 columns are 128 gate columns and the same 128 up columns, so each
 //     lane holds gate and up for identical (row, i) and applies SiLU*up in registers;
-//   - operands staged global -> registers -> LDS (row stride 72 bf16: 16-byte skew per row
-//     keeps the 16-byte fragment reads of 8 consecutive rows on distinct banks),
-//     double-buffered so the next slice's loads are in flight during the MFMAs;
-//   - persistent grid (one block per CU): tiles (slot, m-tile, n-tile) are numbered on the
-//     device from counts[] (no host sync) and taken round-robin; rows past a segment's end
-//     load as zeros and are never stored; every output tile has exactly one owner.
+//   - operands move global -> LDS by buffer DMA (no register staging), 32-deep K slices in 4
+//     LDS stages (3 slices in flight); fragments of the next slice are read into a second
+//     register set while the current slice's second half of MFMAs runs;
+//   - persistent grid (one block per CU), XCD-grouped tile order (gemm_common.h); rows past
+//     a segment's end read as zeros and are never stored; each output tile has one owner.
+// The fp8 path (block-scaled weights) lives in expert_gemm_fp8.hip.
 #include <hip/hip_runtime.h>
 
+#include "gemm_common.h"
 #include "moe_dev.h"
 
 namespace moe {
+namespace gemm {
+int num_cus() {
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cus[dev] == 0) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+            v = 256;
+        cus[dev] = v;
+    }
+    return cus[dev];
+}
+}  // namespace gemm
+
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -31,9 +47,8 @@ typedef float floatx16_t __attribute__((ext_vector_type(16)));
 
 constexpr int BM = 256, BN = 256;
 constexpr int BK = 32;      // K slice per pipeline stage
-constexpr int STAGES = 4;   // LDS stages: STAGES-1 slices in flight
-constexpr int M_THREADS = 256;
-constexpr int kMaxSlots = 1024;
+constexpr int STAGES = 4;   // LDS stages
+constexpr int M_THREADS = gemm::kThreads;
 constexpr int UP_COLS = BN / 2;     // i-columns per up tile (gate and up each)
 
 struct GemmArgs {
@@ -51,24 +66,6 @@ struct GemmArgs {
 
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
 
-typedef int v4i_t __attribute__((ext_vector_type(4)));
-constexpr int kBufferFlags = 0x00020000;  // raw buffer, 32-bit data format (gfx9 family)
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
-                                             static_cast<int>(bytes), kBufferFlags);
-}
-
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-// Tiles are numbered (m-tile over all slots) x (column tile).  Launched with one block per
-// CU; the hardware hands workgroup b to XCD b % 8, so block b takes, in round r, tile q of
-// super-tile r*8 + b%8 (q = b/8): the 32 blocks of one XCD work on one SM x SN patch of
-// tiles at a time and share its A rows and B columns through that XCD's L2.
-struct TileOrder {
-    int32_t SM, SN;  // super-tile = SM m-tiles x SN column tiles, SM*SN = blocks per XCD
-};
-
 // LDS layout of a stage: 256 rows x BK bf16 per operand, rows of BK/8 16-byte chunks.  The
 // LDS serves a 16-byte-per-lane read 16 lanes at a time from 64 banks (256 bytes); the
 // fragment reads have 16 consecutive rows asking for the same logical chunk, so the chunk
@@ -82,11 +79,11 @@ static_assert(BK == 32 || BK == 64, "swizzle written for 32- or 64-wide K slices
 __device__ __forceinline__ int swz(int row) { return BK == 64 ? ((row >> 1) & 7) : ((row >> 2) & 3); }
 
 template <bool UP>
-__global__ __launch_bounds__(M_THREADS, 1) void grouped_gemm_bf16_kernel(GemmArgs a, TileOrder to) {
+__global__ __launch_bounds__(M_THREADS, 1) void grouped_gemm_bf16_kernel(GemmArgs a, gemm::TileOrder to) {
     __shared__ __attribute__((aligned(1024))) uint16_t As[STAGES][BM * BK];
     __shared__ __attribute__((aligned(1024))) uint16_t Bs[STAGES][BN * BK];
-    __shared__ int32_t tile_prefix[kMaxSlots + 1];  // m-tiles before slot e
-    __shared__ int32_t part[M_THREADS];
+    __shared__ int32_t tile_prefix[gemm::kMaxSlots + 1];  // m-tiles before slot e
+    __shared__ int32_t part[gemm::kThreads];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -94,43 +91,7 @@ __global__ __launch_bounds__(M_THREADS, 1) void grouped_gemm_bf16_kernel(GemmArg
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wv >> 1, wn = wv & 1;
 
-    // ---- number the tiles: slot e owns ceil(rows_e / BM) m-tiles
-    {
-        const int El = a.El;
-        int32_t loc[4];
-        int32_t s = 0;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int e = tid * 4 + q;
-            int32_t mt = 0;
-            if (e < El) {
-                int64_t c = a.counts[e];
-                const int64_t room = a.cap - a.seg[e];
-                c = c < room ? c : (room > 0 ? room : 0);
-                mt = static_cast<int32_t>((c + BM - 1) / BM);
-            }
-            loc[q] = mt;
-            s += mt;
-        }
-        part[tid] = s;
-        __syncthreads();
-        for (int off = 1; off < M_THREADS; off <<= 1) {
-            const int32_t v = tid >= off ? part[tid - off] : 0;
-            __syncthreads();
-            part[tid] += v;
-            __syncthreads();
-        }
-        int32_t run = part[tid] - s;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int e = tid * 4 + q;
-            if (e < El) tile_prefix[e] = run;
-            run += loc[q];
-        }
-        if (tid == M_THREADS - 1) tile_prefix[El] = part[tid];
-        __syncthreads();
-    }
-    const int32_t total_mt = tile_prefix[a.El];
+    const int32_t total_mt = gemm::number_tiles<BM>(a.counts, a.seg, a.cap, a.El, tile_prefix, part);
     const uint32_t row_bytes = static_cast<uint32_t>(a.K) * 2u;
     const int nsn = a.NT / to.SN;
     const int64_t total_super = static_cast<int64_t>((total_mt + to.SM - 1) / to.SM) * nsn;
@@ -148,15 +109,8 @@ __global__ __launch_bounds__(M_THREADS, 1) void grouped_gemm_bf16_kernel(GemmArg
         const int32_t em = static_cast<int32_t>(sup / nsn) * to.SM + q / to.SN;
         const int32_t nt = static_cast<int32_t>(sup % nsn) * to.SN + q % to.SN;
         if (em >= total_mt) continue;
-        int lo = 0, hi = a.El;
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (tile_prefix[mid] <= em) lo = mid;
-            else hi = mid;
-        }
-        // the tile coordinates are block-uniform: keep them in scalar registers so the
-        // buffer descriptors below are scalar too
-        const int e = __builtin_amdgcn_readfirstlane(lo);
+        // the tile coordinates are block-uniform: scalar registers, scalar descriptors
+        const int e = gemm::slot_of_tile(tile_prefix, a.El, em);
         const int32_t mtile = __builtin_amdgcn_readfirstlane(em - tile_prefix[e]);
         const int64_t seg_start = a.seg[e];
         int64_t seg_end = seg_start + a.counts[e];
@@ -180,13 +134,7 @@ __global__ __launch_bounds__(M_THREADS, 1) void grouped_gemm_bf16_kernel(GemmArg
             dbase = a.B + static_cast<int64_t>(e) * a.N * a.K;
             dbytes = static_cast<uint32_t>(a.N) * row_bytes;
         }
-        // wave-uniform by construction; say so, so the descriptor lives in scalar registers
-        const uint64_t db64 = reinterpret_cast<uint64_t>(dbase);
-        const uint32_t dlo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(db64));
-        const uint32_t dhi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(db64 >> 32));
-        dbase = reinterpret_cast<const uint16_t*>((static_cast<uint64_t>(dhi) << 32) | dlo);
-        dbytes = __builtin_amdgcn_readfirstlane(dbytes);
-        const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(dbase, dbytes);
+        const __amdgpu_buffer_rsrc_t rsrc = gemm::make_rsrc_uniform(dbase, dbytes);
         uint32_t voff[LPW];
 #pragma unroll
         for (int p = 0; p < LPW; ++p) {
@@ -206,7 +154,7 @@ __global__ __launch_bounds__(M_THREADS, 1) void grouped_gemm_bf16_kernel(GemmArg
             uint16_t* base = (loads_a ? &As[0][0] : &Bs[0][0]) + off;
 #pragma unroll
             for (int p = 0; p < LPW; ++p) {
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(base + p * 512), 16, voff[p],
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (gemm::lds_void_t*)(base + p * 512), 16, voff[p],
                                                         soff, 0, 0);
             }
         };
@@ -381,28 +329,20 @@ __global__ __launch_bounds__(256) void simple_gemm_kernel(SimpleArgs a) {
     }
 }
 
-int num_cus() {
-    static int cus[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cus[dev] == 0) {
-        int v = 0;
-        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
-            v = 256;
-        cus[dev] = v;
-    }
-    return cus[dev];
-}
-
 moe_status check_common(moe_dtype act_dt, const moe_plan* plan, const moe_expert_weights* w,
                         int64_t H, int64_t I) {
     MOE_CHECK_ARG(plan && w);
     MOE_CHECK_ARG(act_dt == MOE_F32 || act_dt == MOE_BF16);
     MOE_CHECK_ARG(H > 0 && I > 0);
-    MOE_CHECK_ARG(plan->num_slots >= 1 && plan->num_slots <= kMaxSlots);
+    MOE_CHECK_ARG(plan->num_slots >= 1 && plan->num_slots <= gemm::kMaxSlots);
     MOE_CHECK_ARG(plan->counts && plan->seg_offsets && plan->num_rows && plan->cap >= 0);
     MOE_CHECK_ARG(w->w13 && w->w2);
-    if (w->dtype == MOE_FP8_E4M3) return MOE_ERR_UNSUPPORTED;
+    if (w->dtype == MOE_FP8_E4M3) {
+        // block-scaled e4m3 weights take bf16 activations (quantised per 1x128 group inside)
+        if (act_dt != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+        MOE_CHECK_ARG(w->s13 && w->s2);
+        return MOE_OK;
+    }
     MOE_CHECK_ARG(w->dtype == act_dt);
     return MOE_OK;
 }
@@ -435,18 +375,9 @@ moe_status run_stage(bool up, const void* A, moe_dtype act_dt, const moe_plan* p
         g.El = plan->num_slots;
         g.NT = static_cast<int32_t>(up ? I / UP_COLS : H / BN);
         // one block per CU, 8 XCDs: a super-tile of SM x SN tiles per XCD per round
-        const int blocks = num_cus();
-        const int per_xcd = blocks / 8;
-        TileOrder to;
-        to.SN = 1;
-        for (int sn : {8, 4, 2}) {
-            if (g.NT % sn == 0 && per_xcd % sn == 0) {
-                to.SN = sn;
-                break;
-            }
-        }
-        to.SM = per_xcd / to.SN;
-        if (blocks % 8 != 0 || to.SM < 1) return MOE_ERR_UNSUPPORTED;
+        const int blocks = gemm::num_cus();
+        gemm::TileOrder to;
+        if (!gemm::pick_tile_order(g.NT, blocks, &to)) return MOE_ERR_UNSUPPORTED;
         const dim3 grid(static_cast<unsigned>(blocks));
         if (up) hipLaunchKernelGGL(grouped_gemm_bf16_kernel<true>, grid, dim3(M_THREADS), 0, stream, g, to);
         else hipLaunchKernelGGL(grouped_gemm_bf16_kernel<false>, grid, dim3(M_THREADS), 0, stream, g, to);
@@ -478,19 +409,22 @@ size_t h_bytes(int64_t cap, int64_t I, moe_dtype act_dt) {
 
 extern "C" size_t moe_expert_gemm_workspace_size(int64_t cap, int64_t H, int64_t I,
                                                  moe_dtype act_dt, moe_dtype w_dt) {
-    (void)H;
-    (void)w_dt;
-    if (cap < 0 || I <= 0) return 0;
-    return moe::h_bytes(cap, I, act_dt);
+    if (cap < 0 || I <= 0 || H <= 0) return 0;
+    size_t n = moe::h_bytes(cap, I, act_dt);
+    if (w_dt == MOE_FP8_E4M3) {
+        const size_t a = moe::gemm::fp8_stage_workspace(cap, H), b = moe::gemm::fp8_stage_workspace(cap, I);
+        n += a > b ? a : b;
+    }
+    return n;
 }
 
 extern "C" moe_status moe_expert_gemm_up(const void* x_perm, moe_dtype act_dt, const moe_plan* plan,
                                          const moe_expert_weights* w, int64_t H, int64_t I, void* h,
                                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
-    (void)workspace;
-    (void)workspace_bytes;
     moe_status st = moe::check_common(act_dt, plan, w, H, I);
     if (st != MOE_OK) return st;
+    if (w->dtype == MOE_FP8_E4M3)
+        return moe::gemm::run_fp8_stage(true, x_perm, plan, w, H, I, h, workspace, workspace_bytes, stream);
     return moe::run_stage(true, x_perm, act_dt, plan, w, H, I, h, stream);
 }
 
@@ -498,10 +432,10 @@ extern "C" moe_status moe_expert_gemm_down(const void* h, moe_dtype act_dt, cons
                                            const moe_expert_weights* w, int64_t H, int64_t I,
                                            void* y_perm, void* workspace, size_t workspace_bytes,
                                            hipStream_t stream) {
-    (void)workspace;
-    (void)workspace_bytes;
     moe_status st = moe::check_common(act_dt, plan, w, H, I);
     if (st != MOE_OK) return st;
+    if (w->dtype == MOE_FP8_E4M3)
+        return moe::gemm::run_fp8_stage(false, h, plan, w, H, I, y_perm, workspace, workspace_bytes, stream);
     return moe::run_stage(false, h, act_dt, plan, w, H, I, y_perm, stream);
 }
 
@@ -512,8 +446,18 @@ extern "C" moe_status moe_expert_gemm(const void* x_perm, moe_dtype act_dt, cons
     moe_status st = moe::check_common(act_dt, plan, w, H, I);
     if (st != MOE_OK) return st;
     if (plan->cap == 0) return MOE_OK;
-    if (workspace_bytes < moe::h_bytes(plan->cap, I, act_dt)) return MOE_ERR_CAPACITY;
+    if (workspace_bytes < moe_expert_gemm_workspace_size(plan->cap, H, I, act_dt,
+                                                         static_cast<moe_dtype>(w->dtype)))
+        return MOE_ERR_CAPACITY;
     MOE_CHECK_ARG(workspace && moe::aligned(workspace, 256));
+    const size_t hb = moe::h_bytes(plan->cap, I, act_dt);
+    if (w->dtype == MOE_FP8_E4M3) {
+        void* rest = static_cast<char*>(workspace) + hb;
+        const size_t rest_bytes = workspace_bytes - hb;
+        st = moe::gemm::run_fp8_stage(true, x_perm, plan, w, H, I, workspace, rest, rest_bytes, stream);
+        if (st != MOE_OK) return st;
+        return moe::gemm::run_fp8_stage(false, workspace, plan, w, H, I, y_perm, rest, rest_bytes, stream);
+    }
     st = moe::run_stage(true, x_perm, act_dt, plan, w, H, I, workspace, stream);
     if (st != MOE_OK) return st;
     return moe::run_stage(false, workspace, act_dt, plan, w, H, I, y_perm, stream);

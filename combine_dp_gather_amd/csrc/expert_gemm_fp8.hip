@@ -1,0 +1,340 @@
+// fp8 expert GEMMs: OCP e4m3 weights with one fp32 scale per 128x128 block, bf16
+// activations quantised on the fly to e4m3 with one fp32 scale per 1x128 group.
+//
+// The 128-wide per-token-group activation quantisation and its block-aligned companion,
+// the 128x128 weight blocks, follow the SGLang walkthrough "SGLang 源码完全拆解(十七)", section
+// "prefll 侧的一个必要步骤：per-token-group 量化" (group size hard-wired to 128, matching
+// expert_alignment 128).  Values: weight = e4m3(q) * s_w[block], activation ~ e4m3(q) * s_a.
+//
+// quant kernel: one wave per row, one 128-column group per step: amax by wave reduction,
+//   scale = amax / 448 (1 for an all-zero group), codes = RNE(x * 448 / amax) clamped to
+//   +-448 (the hardware conversion turns larger magnitudes into NaN).  Scales are stored
+//   transposed, [K/128][cap], so a tile's 256 scales of one K group are contiguous.
+// GEMM kernel (gfx950 v_mfma_f32_32x32x64_f8f6f4, e4m3 x e4m3, fp32 accumulate):
+//   - block tile 256 rows x 128 columns (up: 64 gate + the same 64 up columns), 4 waves in
+//     2x2, each 128 x 64 = 4x2 MFMA blocks;
+//   - one pipeline stage = one 128-deep K group = one scale block: the MFMAs of a stage
+//     accumulate into a fresh partial sum, then acc += (s_a[row] * s_w) * partial;
+//   - A, B and the stage's activation scales arrive in LDS by buffer DMA, 3 stages
+//     (2 in flight); 128-byte rows with 16-byte chunks xor-swizzled by (row/2) mod 8 for the
+//     64-bank LDS;
+//   - same persistent XCD-grouped tile order and ragged-segment numbering as the bf16 path.
+#include <hip/hip_runtime.h>
+
+#include "gemm_common.h"
+#include "moe_dev.h"
+
+namespace moe {
+namespace {
+
+typedef int intx8_t __attribute__((ext_vector_type(8)));
+typedef float floatx16_t __attribute__((ext_vector_type(16)));
+
+constexpr int QB = 128;              // quantisation group / scale block
+constexpr float kE4M3Max = 448.0f;
+
+// ------------------------------------------------------------------ activation quant
+__global__ __launch_bounds__(256) void quant_fp8_kernel(const uint16_t* __restrict__ act,
+                                                        const int64_t* __restrict__ num_rows,
+                                                        int64_t cap, int64_t K,
+                                                        uint8_t* __restrict__ q,
+                                                        float* __restrict__ s_t) {
+    int64_t rows = *num_rows;
+    rows = rows < cap ? rows : cap;
+    const int lane = lane_id();
+    const int64_t nw = static_cast<int64_t>(gridDim.x) * 4;
+    const int64_t groups = K / QB;
+    for (int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / kWave; r < rows; r += nw) {
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(act + r * K);
+        uint16_t* dst = reinterpret_cast<uint16_t*>(q + r * K);
+        for (int64_t g = 0; g < groups; ++g) {
+            const uint32_t w = src[g * (QB / 2) + lane];
+            const float x0 = __uint_as_float(w << 16), x1 = __uint_as_float(w & 0xffff0000u);
+            float m = fmaxf(fabsf(x0), fabsf(x1));
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+            const float inv = m > 0.f ? kE4M3Max / m : 1.f;
+            const float y0 = fminf(fmaxf(x0 * inv, -kE4M3Max), kE4M3Max);
+            const float y1 = fminf(fmaxf(x1 * inv, -kE4M3Max), kE4M3Max);
+            const int packed = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
+            dst[g * (QB / 2) + lane] = static_cast<uint16_t>(packed & 0xffff);
+            if (lane == 0) s_t[g * cap + r] = m > 0.f ? m / kE4M3Max : 1.f;
+        }
+    }
+}
+
+// ------------------------------------------------------------------ fp8 grouped GEMM
+constexpr int F_BM = 256, F_BN = 128;
+constexpr int F_STAGES = 3;
+constexpr int F_ROW = 128;                   // bytes per LDS row (one K group of fp8)
+constexpr int F_A_BLKS = F_BM * F_ROW / 1024;  // 1 KB DMA blocks of A per stage (32)
+constexpr int F_B_BLKS = F_BN * F_ROW / 1024;  // (16)
+constexpr int F_LPW = F_A_BLKS / 4 + F_B_BLKS / 4 + 1;  // DMAs per wave per stage (+1: scales)
+constexpr int F_UP_COLS = F_BN / 2;          // up: 64 gate + 64 up columns
+
+__device__ __forceinline__ int fswz(int row) { return (row >> 1) & 7; }
+
+struct Fp8Args {
+    const uint8_t* A;       // [cap, K] e4m3 activations
+    const float* SA;        // [K/128, cap] activation scales
+    const uint8_t* B;       // up: w13 [E_l, 2, I, H]; down: w2 [E_l, H, I]
+    const float* SB;        // up: s13 [E_l, 2, I/128, H/128]; down: s2 [E_l, H/128, I/128]
+    uint16_t* C;            // up: h [cap, I] bf16; down: y [cap, H] bf16
+    const int32_t* counts;
+    const int64_t* seg;
+    int64_t cap, K, N;      // up: K=H, N=I; down: K=I, N=H
+    int32_t El, NT;
+};
+
+__device__ __forceinline__ float silu_mul8(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+
+template <bool UP>
+__global__ __launch_bounds__(gemm::kThreads, 1) void grouped_gemm_fp8_kernel(Fp8Args a, gemm::TileOrder to) {
+    __shared__ __attribute__((aligned(1024))) uint8_t As[F_STAGES][F_BM * F_ROW];
+    __shared__ __attribute__((aligned(1024))) uint8_t Bs[F_STAGES][F_BN * F_ROW];
+    __shared__ __attribute__((aligned(16))) float Ss[F_STAGES][F_BM];
+    __shared__ int32_t tile_prefix[gemm::kMaxSlots + 1];
+    __shared__ int32_t part[gemm::kThreads];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wv >> 1, wn = wv & 1;
+
+    const int32_t total_mt = gemm::number_tiles<F_BM>(a.counts, a.seg, a.cap, a.El, tile_prefix, part);
+    const uint32_t row_bytes = static_cast<uint32_t>(a.K);
+    const int64_t KG = a.K / QB;  // K groups = pipeline steps
+    const int64_t SKG = a.N / QB;  // weight scale blocks along the output dimension
+    const int nsn = a.NT / to.SN;
+    const int64_t total_super = static_cast<int64_t>((total_mt + to.SM - 1) / to.SM) * nsn;
+    const int xcd = blockIdx.x & 7;
+    const int q = blockIdx.x >> 3;
+    const int frow = lane & 31;
+    // fragment k bytes of sub-step ks: 64*ks + 32*(lane/32) .. +32 = logical chunks c, c+1
+    int fch[2][2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) fch[ks][h] = ((4 * ks + 2 * (lane >> 5) + h) ^ fswz(frow)) * 16;
+
+    for (int64_t sup = xcd; sup < total_super; sup += 8) {
+        const int32_t em = static_cast<int32_t>(sup / nsn) * to.SM + q / to.SN;
+        const int32_t nt = static_cast<int32_t>(sup % nsn) * to.SN + q % to.SN;
+        if (em >= total_mt) continue;
+        const int e = gemm::slot_of_tile(tile_prefix, a.El, em);
+        const int32_t mtile = __builtin_amdgcn_readfirstlane(em - tile_prefix[e]);
+        const int64_t seg_start = a.seg[e];
+        int64_t seg_end = seg_start + a.counts[e];
+        seg_end = seg_end < a.cap ? seg_end : a.cap;
+        const int64_t row0 = seg_start + static_cast<int64_t>(mtile) * F_BM;
+        const int64_t nrows64 = seg_end - row0;
+        const uint32_t nrows = static_cast<uint32_t>(nrows64 < F_BM ? nrows64 : F_BM);
+
+        // descriptors: A rows of this tile (rows past the segment end read as zeros), this
+        // slot's weights, and the activation scales from row0 to the end of the array
+        const __amdgpu_buffer_rsrc_t ra = gemm::make_rsrc_uniform(a.A + row0 * a.K, nrows * row_bytes);
+        const int64_t wslot = UP ? 2 * a.N * a.K : a.N * a.K;
+        const __amdgpu_buffer_rsrc_t rb = gemm::make_rsrc_uniform(a.B + e * wslot, static_cast<uint32_t>(wslot));
+        const __amdgpu_buffer_rsrc_t rs = gemm::make_rsrc_uniform(
+            a.SA + row0, static_cast<uint32_t>((KG * a.cap - row0) * 4));
+        // per-lane DMA offsets: A blocks 8w..8w+7, B blocks 4w..4w+3, 64 scales at 64w
+        uint32_t aoff[F_A_BLKS / 4], boff[F_B_BLKS / 4];
+#pragma unroll
+        for (int p = 0; p < F_A_BLKS / 4; ++p) {
+            const int r = (wv * (F_A_BLKS / 4) + p) * 8 + (lane >> 3);
+            aoff[p] = static_cast<uint32_t>(r) * row_bytes + static_cast<uint32_t>(((lane & 7) ^ fswz(r)) * 16);
+        }
+#pragma unroll
+        for (int p = 0; p < F_B_BLKS / 4; ++p) {
+            const int r = (wv * (F_B_BLKS / 4) + p) * 8 + (lane >> 3);  // B tile row 0..127
+            uint32_t grow;
+            if (UP) grow = static_cast<uint32_t>((r >> 6) * a.N + nt * F_UP_COLS + (r & (F_UP_COLS - 1)));
+            else grow = static_cast<uint32_t>(nt * F_BN + r);
+            boff[p] = grow * row_bytes + static_cast<uint32_t>(((lane & 7) ^ fswz(r)) * 16);
+        }
+        // the scale DMA carries its K-group offset in the per-lane offset, so the descriptor's
+        // range check sees it (rows at or past cap in the last group read as zeros)
+        const uint32_t soff_lane = static_cast<uint32_t>((wv * 64 + lane) * 4);
+        const uint32_t scap_bytes = static_cast<uint32_t>(a.cap * 4);
+        auto issue = [&](int buf, int64_t kg) {
+            int abase = buf * (F_BM * F_ROW) + wv * (F_A_BLKS / 4) * 1024;
+            int bbase = buf * (F_BN * F_ROW) + wv * (F_B_BLKS / 4) * 1024;
+            int sbase = buf * F_BM + wv * 64;
+            asm volatile("" : "+s"(abase), "+s"(bbase), "+s"(sbase));
+            const int koff = static_cast<int>(kg * QB);
+#pragma unroll
+            for (int p = 0; p < F_A_BLKS / 4; ++p)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (gemm::lds_void_t*)(&As[0][0] + abase + p * 1024), 16,
+                                                        aoff[p], koff, 0, 0);
+#pragma unroll
+            for (int p = 0; p < F_B_BLKS / 4; ++p)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (gemm::lds_void_t*)(&Bs[0][0] + bbase + p * 1024), 16,
+                                                        boff[p], koff, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (gemm::lds_void_t*)(&Ss[0][0] + sbase), 4,
+                                                    soff_lane + static_cast<uint32_t>(kg) * scap_bytes, 0, 0, 0);
+        };
+        // weight block scale of column block j for K group kg
+        auto wscale = [&](int j, int64_t kg) -> float {
+            if (UP) {
+                const int64_t ib = (static_cast<int64_t>(nt) * F_UP_COLS) / QB;
+                return a.SB[((static_cast<int64_t>(e) * 2 + j) * SKG + ib) * KG + kg];
+            }
+            const int64_t cb = (static_cast<int64_t>(nt) * F_BN) / QB;
+            return a.SB[(static_cast<int64_t>(e) * SKG + cb) * KG + kg];
+        };
+
+        floatx16_t acc[4][2];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+        const floatx16_t zero = {};
+
+        const uint8_t* a_rd = &As[0][0] + (wm * 128 + frow) * F_ROW;
+        // B rows of the wave's two column blocks: up -> gate rows wn*32.., up rows 64+wn*32..
+        const int brow0 = UP ? wn * 32 : wn * 64;
+        const int brow1 = UP ? F_UP_COLS + wn * 32 : wn * 64 + 32;
+        const uint8_t* b_rd0 = &Bs[0][0] + (brow0 + frow) * F_ROW;
+        const uint8_t* b_rd1 = &Bs[0][0] + (brow1 + frow) * F_ROW;
+        // scale rows of the lane: wm*128 + 32i + 8g + 4*(lane/32) + 0..3
+        const float* s_rd = &Ss[0][0] + wm * 128 + 4 * (lane >> 5);
+
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        __syncthreads();
+        // prologue: K groups 0 .. STAGES-2 in flight
+#pragma unroll
+        for (int st = 0; st < F_STAGES - 1; ++st) issue(st, st < KG ? st : KG - 1);
+        for (int64_t kg = 0; kg < KG; ++kg) {
+            const int cur = static_cast<int>(kg % F_STAGES);
+            // group kg landed everywhere; every wave is done with group kg-1's buffer
+            asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"((F_STAGES - 2) * F_LPW) : "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            intx8_t fa[4][2], fb[2][2];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint8_t* p = a_rd + cur * (F_BM * F_ROW) + i * 32 * F_ROW;
+                    const gemm::v4i_t lo = *reinterpret_cast<const gemm::v4i_t*>(p + fch[ks][0]);
+                    const gemm::v4i_t hi = *reinterpret_cast<const gemm::v4i_t*>(p + fch[ks][1]);
+                    fa[i][ks] = intx8_t{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+                }
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const uint8_t* p = (j ? b_rd1 : b_rd0) + cur * (F_BN * F_ROW);
+                    const gemm::v4i_t lo = *reinterpret_cast<const gemm::v4i_t*>(p + fch[ks][0]);
+                    const gemm::v4i_t hi = *reinterpret_cast<const gemm::v4i_t*>(p + fch[ks][1]);
+                    fb[j][ks] = intx8_t{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+                }
+            }
+            float4 sa[4][4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    sa[i][g] = *reinterpret_cast<const float4*>(s_rd + cur * F_BM + 32 * i + 8 * g);
+            // refill the buffer group kg-1 used with group kg + STAGES - 1
+            const int64_t nxt = kg + F_STAGES - 1;
+            issue(static_cast<int>(nxt % F_STAGES), nxt < KG ? nxt : KG - 1);
+            const float sw0 = wscale(0, kg), sw1 = wscale(1, kg);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    floatx16_t t = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i][0], fb[j][0], zero,
+                                                                                   0, 0, 0, 0, 0, 0);
+                    t = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i][1], fb[j][1], t, 0, 0, 0, 0, 0, 0);
+                    const float sw = j ? sw1 : sw0;
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const float s4[4] = {sa[i][g].x, sa[i][g].y, sa[i][g].z, sa[i][g].w};
+#pragma unroll
+                        for (int u = 0; u < 4; ++u)
+                            acc[i][j][4 * g + u] = __builtin_fmaf(s4[u] * sw, t[4 * g + u], acc[i][j][4 * g + u]);
+                    }
+                }
+            }
+        }
+        // epilogue: lane holds rows 8*(v/4) + 4*(lane/32) + v%4 of column lane%32
+        int rbase = wm * 128 + (lane >> 5) * 4;
+        asm volatile("" : "+v"(rbase));
+        const int64_t colbase = UP ? static_cast<int64_t>(nt) * F_UP_COLS + wn * 32 + (lane & 31)
+                                   : static_cast<int64_t>(nt) * F_BN + wn * 64 + (lane & 31);
+        uint16_t* cbase = a.C + (row0 + rbase) * a.N + colbase;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int roff = i * 32 + (v >> 2) * 8 + (v & 3);
+                if (rbase + roff >= static_cast<int>(nrows)) continue;
+                uint16_t* cp = cbase + static_cast<int64_t>(roff) * a.N;
+                if (UP) {
+                    cp[0] = f32_to_bf16(silu_mul8(acc[i][0][v], acc[i][1][v]));
+                } else {
+                    cp[0] = f32_to_bf16(acc[i][0][v]);
+                    cp[32] = f32_to_bf16(acc[i][1][v]);
+                }
+            }
+        }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+size_t align256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
+
+}  // namespace
+
+namespace gemm {
+
+size_t fp8_stage_workspace(int64_t cap, int64_t K) {
+    return align256(static_cast<size_t>(cap * K)) + align256(static_cast<size_t>(K / QB * cap) * 4);
+}
+
+moe_status run_fp8_stage(bool up, const void* act, const moe_plan* plan,
+                         const moe_expert_weights* w, int64_t H, int64_t I, void* out,
+                         void* workspace, size_t ws_bytes, hipStream_t stream) {
+    if (plan->cap == 0) return MOE_OK;
+    const int64_t K = up ? H : I, N = up ? I : H;
+    if (H % QB != 0 || I % QB != 0) return MOE_ERR_UNSUPPORTED;
+    if (2 * H * I >= (int64_t(1) << 32) || int64_t(F_BM) * K >= (int64_t(1) << 32) ||
+        plan->cap * (K / QB) * 4 >= (int64_t(1) << 32))
+        return MOE_ERR_UNSUPPORTED;  // descriptor ranges are 32-bit
+    MOE_CHECK_ARG(act && out && w->s13 && w->s2);
+    MOE_CHECK_ARG(aligned(act, 16) && aligned(w->w13, 16) && aligned(w->w2, 16));
+    if (ws_bytes < fp8_stage_workspace(plan->cap, K)) return MOE_ERR_CAPACITY;
+    MOE_CHECK_ARG(workspace && aligned(workspace, 256));
+    uint8_t* qa = static_cast<uint8_t*>(workspace);
+    float* sa = reinterpret_cast<float*>(qa + align256(static_cast<size_t>(plan->cap * K)));
+    int64_t qblocks = ceil_div(plan->cap, 4);
+    if (qblocks > 4096) qblocks = 4096;
+    hipLaunchKernelGGL(quant_fp8_kernel, dim3(static_cast<unsigned>(qblocks)), dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(act), plan->num_rows, plan->cap, K, qa, sa);
+    MOE_LAUNCH_CHECK();
+    Fp8Args g;
+    g.A = qa;
+    g.SA = sa;
+    g.B = static_cast<const uint8_t*>(up ? w->w13 : w->w2);
+    g.SB = up ? w->s13 : w->s2;
+    g.C = static_cast<uint16_t*>(out);
+    g.counts = plan->counts;
+    g.seg = plan->seg_offsets;
+    g.cap = plan->cap;
+    g.K = K;
+    g.N = N;
+    g.El = plan->num_slots;
+    g.NT = static_cast<int32_t>(up ? I / F_UP_COLS : H / F_BN);
+    const int blocks = num_cus();
+    TileOrder to;
+    if (!pick_tile_order(g.NT, blocks, &to)) return MOE_ERR_UNSUPPORTED;
+    const dim3 grid(static_cast<unsigned>(blocks));
+    if (up) hipLaunchKernelGGL(grouped_gemm_fp8_kernel<true>, grid, dim3(kThreads), 0, stream, g, to);
+    else hipLaunchKernelGGL(grouped_gemm_fp8_kernel<false>, grid, dim3(kThreads), 0, stream, g, to);
+    MOE_LAUNCH_CHECK();
+    return MOE_OK;
+}
+
+}  // namespace gemm
+}  // namespace moe

@@ -134,8 +134,8 @@ class MoELayer:
             return
         s = self.spec
         if split:
-            moe_expert_gemm_up(self.x_perm, self.plan, self.w.ew, s.hidden, s.inter, self.h)
-            moe_expert_gemm_down(self.h, self.plan, self.w.ew, s.hidden, s.inter, self.y_perm)
+            self.experts_up()
+            self.experts_down()
         else:
             moe_expert_gemm(self.x_perm, self.plan, self.w.ew, s.hidden, s.inter, self.y_perm,
                             self.gemm_ws)
@@ -143,12 +143,12 @@ class MoELayer:
     def experts_up(self):
         if self.G:
             moe_expert_gemm_up(self.x_perm, self.plan, self.w.ew, self.spec.hidden, self.spec.inter,
-                               self.h)
+                               self.h, self.gemm_ws)
 
     def experts_down(self):
         if self.G:
             moe_expert_gemm_down(self.h, self.plan, self.w.ew, self.spec.hidden, self.spec.inter,
-                                 self.y_perm)
+                                 self.y_perm, self.gemm_ws)
 
     def combine(self):
         if self.G:

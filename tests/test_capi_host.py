@@ -109,10 +109,18 @@ def test_argument_errors_return_before_any_launch(m):
                             1, 1, 1 << 20, None) == _lib.MOE_ERR_INVALID_ARG
     assert lib.moe_dispatch(1, 1, 10, 2, 64, _lib.MOE_BF16, ctypes.byref(emap), ctypes.byref(plan),
                             1, 1, 0, None) == _lib.MOE_ERR_CAPACITY
-    # experts: fp8 weights are not implemented by this build; dtype mismatch is invalid
+    # experts: fp8 weights need bf16 activations and both scale tables; a misaligned
+    # workspace is rejected; dtype mismatch is invalid
     w = _lib.ExpertWeights(_lib.MOE_FP8_E4M3, 0, 1, 1, 1, 1)
-    assert lib.moe_expert_gemm(1, _lib.MOE_BF16, ctypes.byref(plan), ctypes.byref(w), 256, 128, 1, 1,
+    assert lib.moe_expert_gemm(1, _lib.MOE_F32, ctypes.byref(plan), ctypes.byref(w), 256, 128, 1, 1,
                                1 << 30, None) == _lib.MOE_ERR_UNSUPPORTED
+    assert lib.moe_expert_gemm(1, _lib.MOE_BF16, ctypes.byref(plan), ctypes.byref(w), 256, 128, 1, 1,
+                               1 << 30, None) == _lib.MOE_ERR_INVALID_ARG
+    assert lib.moe_expert_gemm(1, _lib.MOE_BF16, ctypes.byref(plan), ctypes.byref(w), 256, 128, 1, 256,
+                               16, None) == _lib.MOE_ERR_CAPACITY
+    w_noscale = _lib.ExpertWeights(_lib.MOE_FP8_E4M3, 0, 1, 1, None, None)
+    assert lib.moe_expert_gemm(1, _lib.MOE_BF16, ctypes.byref(plan), ctypes.byref(w_noscale), 256, 128,
+                               1, 256, 1 << 30, None) == _lib.MOE_ERR_INVALID_ARG
     w = _lib.ExpertWeights(_lib.MOE_F32, 0, 1, 1, None, None)
     assert lib.moe_expert_gemm(1, _lib.MOE_BF16, ctypes.byref(plan), ctypes.byref(w), 256, 128, 1, 1,
                                1 << 30, None) == _lib.MOE_ERR_INVALID_ARG

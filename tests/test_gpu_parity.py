@@ -104,6 +104,13 @@ def test_cfg3_decode_static_bound(mode):
     run_and_compare(moe_synth.CONFIGS["cfg3"], mode)
 
 
+def test_cfg5_fp8_block_scaled_small():
+    # Zipf-biased routing, 16 slots holding 12 logical experts (4 hot ones twice), e4m3
+    # weights with 128x128 block scales; reduced H and I keep several tiles per slot
+    cfg = resized("cfg5", (300, 0, 277, 41), hidden=1024, inter=512)
+    run_and_compare(cfg)
+
+
 def test_multi_tile_ragged_segments():
     # E=64 with 16 local slots gives ~2T/16 rows per slot: several 256-row tiles plus a
     # ragged tail per slot; replica counts ragged with an idle replica
