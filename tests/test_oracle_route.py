@@ -36,11 +36,16 @@ def round_f32(v: Fraction) -> float:
     return s * float(Fraction(fl) * Fraction(2) ** (e - 23))
 
 
-def fma_chain(x, w):
-    acc = 0.0
-    for a, b in zip(x, w):
-        acc = round_f32(Fraction(float(a)) * Fraction(float(b)) + Fraction(acc))
-    return acc
+def fma_chain(x, w, chunk=128):
+    """fp32 fma chain per 128-wide chunk, chunk sums added left to right, in exact rational
+    arithmetic rounded to fp32 at every step."""
+    total = 0.0
+    for c0 in range(0, len(x), chunk):
+        part = 0.0
+        for a, b in zip(x[c0:c0 + chunk], w[c0:c0 + chunk]):
+            part = round_f32(Fraction(float(a)) * Fraction(float(b)) + Fraction(part))
+        total = round_f32(Fraction(total) + Fraction(part))
+    return total
 
 
 def test_round_f32_matches_numpy_cast():
@@ -52,7 +57,7 @@ def test_round_f32_matches_numpy_cast():
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_gate_logits_bitwise_vs_exact_fma(dtype):
     rng = np.random.default_rng(1)
-    G, E, H = 5, 6, 37
+    G, E, H = 4, 5, 300      # two full chunks and a ragged one
     x = rng.standard_normal((G, H)).astype(np.float32)
     w = (rng.standard_normal((E, H)) * 0.02).astype(np.float32)
     if dtype == "bf16":
@@ -65,15 +70,33 @@ def test_gate_logits_bitwise_vs_exact_fma(dtype):
 
 
 def test_gate_logits_bf16_equals_plain_f32_adds():
-    # bf16 x bf16 products are exact in fp32, so the fma chain is a chain of fp32 adds
+    # bf16 x bf16 products are exact in fp32, so each chunk's fma chain is a chain of fp32
+    # adds; chunk sums then add left to right
     rng = np.random.default_rng(2)
-    x = moe_synth.to_bf16_bits(rng.standard_normal((4, 300)).astype(np.float32))
-    w = moe_synth.to_bf16_bits((rng.standard_normal((9, 300)) * 0.02).astype(np.float32))
+    H = 300
+    x = moe_synth.to_bf16_bits(rng.standard_normal((4, H)).astype(np.float32))
+    w = moe_synth.to_bf16_bits((rng.standard_normal((9, H)) * 0.02).astype(np.float32))
     xf, wf = oracle.as_f32(x), oracle.as_f32(w)
-    ref = np.zeros((4, 9), dtype=np.float32)
-    for h in range(300):
-        ref = ref + (xf[:, h:h + 1] * wf[None, :, h])
-    assert np.array_equal(oracle.gate_logits(x, w), ref)
+    total = np.zeros((4, 9), dtype=np.float32)
+    for c0 in range(0, H, 128):
+        part = np.zeros((4, 9), dtype=np.float32)
+        for h in range(c0, min(c0 + 128, H)):
+            part = part + (xf[:, h:h + 1] * wf[None, :, h])
+        total = total + part
+    assert np.array_equal(oracle.gate_logits(x, w), total)
+
+
+def test_gate_chunk_order_matters():
+    # the chunked order differs from one long chain for some inputs: the pin above would
+    # catch an oracle that silently dropped the chunking
+    rng = np.random.default_rng(5)
+    x = moe_synth.to_bf16_bits(rng.standard_normal((64, 1024)).astype(np.float32))
+    w = moe_synth.to_bf16_bits((rng.standard_normal((8, 1024)) * 0.02).astype(np.float32))
+    xf, wf = oracle.as_f32(x), oracle.as_f32(w)
+    chain = np.zeros((64, 8), dtype=np.float32)
+    for h in range(1024):
+        chain = chain + (xf[:, h:h + 1] * wf[None, :, h])
+    assert not np.array_equal(oracle.gate_logits(x, w), chain)
 
 
 def test_gate_logits_one_hot_and_pad_rows():
