@@ -18,24 +18,35 @@ namespace moe {
 namespace {
 
 // ------------------------------------------------------------------ gate logits
-// Exact-order gate on the fp32 matrix cores.  v_mfma_f32_32x32x1_2b_f32 adds exactly one
-// product to each of its 2x32x32 accumulators per instruction, with a single rounding, so a
-// chain of them over h = 0..H-1 is the fmaf chain of the definition above, bit for bit
-// (checked against the VALU fma chain on bf16-valued, full fp32 and subnormal operands).
-// Block: 128 rows x 256 experts (x is read from HBM once), 4 waves of 64 rows x 128 experts.
-// A wave runs four independent accumulator chains (2 blocks of 32x32 each): A = its 64 rows,
-// B = two 32-expert groups per chain, the halves of the wave swapped between chain pairs so
-// the four chains cover all 2x4 row/expert blocks.  32-deep K slices are staged in LDS in
-// the input type (row stride padded by 4 elements: conflict-free reads of 4 consecutive k).
+// Exact-order gate.  Reading of the gate's arithmetic (the pages fix none): fp32 fused
+// multiply-adds in ascending h inside each 128-wide chunk of h, starting from +0; the chunk
+// sums are added left to right to a running fp32 total starting from +0.
+//
+// On the matrix cores: v_mfma_f32_32x32x1_2b_f32 adds exactly one product to each of its
+// 2x32x32 accumulators per instruction with a single rounding, so a chain of them over a
+// chunk is the fmaf chain of the definition, bit for bit (checked against the VALU fma chain
+// on bf16-valued, full fp32 and subnormal operands).  A wave owns 64 rows x 128 experts as
+// four accumulator chains (A = its 64 rows; B = two 32-expert groups per chain, the wave's
+// halves swapped between chain pairs so the four chains cover all 2x4 row/expert blocks).
+//   - large batches: a block of 128 rows x 256 experts (x read from HBM once) walks all of
+//     h in 32-wide slices, prefetching across chunk boundaries; after a chunk's last slice
+//     its sums are added to the running total and the chains restart from +0;
+//   - small batches: one block per (row tile, expert tile, chunk) writes the chunk's sums to
+//     a workspace and a reduction adds them left to right -- chunks run in parallel, so the
+//     latency is one chunk's chain, not the whole row's.
+// Operands are staged through LDS in the input type, row stride padded by 4 elements.
 typedef float floatx32_t __attribute__((ext_vector_type(32)));
+constexpr int GATE_CHUNK = 128;
 constexpr int GB_M = 128, GB_N = 256, GB_K = 32, G_THREADS = 256;
 constexpr int G_PAD = 4;
+constexpr int SLICES_PER_CHUNK = GATE_CHUNK / GB_K;
+static_assert(GATE_CHUNK % GB_K == 0, "a slice never straddles two chunks");
 
 template <typename T>
 struct GateIO;
 
 template <>
-struct GateIO<uint16_t> {  // bf16 rows; 16-byte chunk = 8 k values
+struct GateIO<uint16_t> {  // bf16 rows; 16-byte piece = 8 k values
     static constexpr int kChunk = 8;
     typedef uint2 Quad;  // 4 consecutive k
     __device__ static float val(const Quad& q, int t) {
@@ -44,7 +55,7 @@ struct GateIO<uint16_t> {  // bf16 rows; 16-byte chunk = 8 k values
     }
 };
 template <>
-struct GateIO<float> {  // fp32 rows; 16-byte chunk = 4 k values
+struct GateIO<float> {  // fp32 rows; 16-byte piece = 4 k values
     static constexpr int kChunk = 4;
     typedef float4 Quad;
     __device__ static float val(const Quad& q, int t) {
@@ -52,12 +63,13 @@ struct GateIO<float> {  // fp32 rows; 16-byte chunk = 4 k values
     }
 };
 
+// 16 bytes of row r starting at column k; columns at or past H (or rows past `rows`) are 0
 template <typename T>
-__device__ __forceinline__ uint4 load_chunk(const T* __restrict__ src, int64_t rows, int64_t H,
+__device__ __forceinline__ uint4 load_piece(const T* __restrict__ src, int64_t rows, int64_t H,
                                             int64_t r, int64_t k) {
     constexpr int C = GateIO<T>::kChunk;
     uint4 v = {0, 0, 0, 0};
-    if (r >= rows) return v;
+    if (r >= rows || k >= H) return v;
     const T* p = src + r * H + k;
     if (k + C <= H && ((reinterpret_cast<uintptr_t>(p) & 15) == 0)) return *reinterpret_cast<const uint4*>(p);
     T t[C];
@@ -67,79 +79,84 @@ __device__ __forceinline__ uint4 load_chunk(const T* __restrict__ src, int64_t r
     return v;
 }
 
+// Staging of one slice: x rows [m0, m0+128) and w rows [n0, n0+256), columns k0 .. k0+GB_K,
+// in LDS as [row][k] with row stride LD.
 template <typename T>
-__global__ __launch_bounds__(G_THREADS) void gate_exact_kernel(const T* __restrict__ x,
-                                                               const T* __restrict__ w,
-                                                               const int32_t* __restrict__ row_valid,
-                                                               int64_t G, int64_t E, int64_t H,
-                                                               float* __restrict__ logits) {
-    constexpr int C = GateIO<T>::kChunk;
-    constexpr int LD = GB_K + G_PAD;                 // LDS row stride (elements)
-    constexpr int XCH = GB_M * GB_K / C / G_THREADS;  // x chunks per thread per slice
-    constexpr int WCH = GB_N * GB_K / C / G_THREADS;  // w chunks per thread per slice
-    __shared__ __attribute__((aligned(16))) T xs[2][GB_M * LD];
-    __shared__ __attribute__((aligned(16))) T ws[2][GB_N * LD];
-    typedef typename GateIO<T>::Quad Quad;
-
-    const int64_t m0 = static_cast<int64_t>(blockIdx.x) * GB_M;
-    const int64_t n0 = static_cast<int64_t>(blockIdx.y) * GB_N;
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int wm = wv >> 1, wn = wv & 1;
-    const int half = lane >> 5;
-
+struct GateStage {
+    static constexpr int C = GateIO<T>::kChunk;
+    static constexpr int LD = GB_K + G_PAD;
+    static constexpr int PER_ROW = GB_K / C;  // 16-byte pieces per row
+    static constexpr int XCH = GB_M * PER_ROW / G_THREADS;
+    static constexpr int WCH = GB_N * PER_ROW / G_THREADS;
     uint4 xr[XCH], wr[WCH];
-    auto gload = [&](int64_t k0) {
+    __device__ void load(const T* x, const T* w, int64_t G, int64_t E, int64_t H, int64_t m0,
+                         int64_t n0, int64_t k0) {
 #pragma unroll
         for (int p = 0; p < XCH; ++p) {
-            const int idx = tid + p * G_THREADS;
-            xr[p] = load_chunk(x, G, H, m0 + idx / (GB_K / C), k0 + (idx % (GB_K / C)) * C);
+            const int idx = threadIdx.x + p * G_THREADS;
+            xr[p] = load_piece(x, G, H, m0 + idx / PER_ROW, k0 + (idx % PER_ROW) * C);
         }
 #pragma unroll
         for (int p = 0; p < WCH; ++p) {
-            const int idx = tid + p * G_THREADS;
-            wr[p] = load_chunk(w, E, H, n0 + idx / (GB_K / C), k0 + (idx % (GB_K / C)) * C);
+            const int idx = threadIdx.x + p * G_THREADS;
+            wr[p] = load_piece(w, E, H, n0 + idx / PER_ROW, k0 + (idx % PER_ROW) * C);
         }
-    };
-    auto sstore = [&](int buf) {
+    }
+    __device__ void store(T* xs, T* ws) {
 #pragma unroll
         for (int p = 0; p < XCH; ++p) {
-            const int idx = tid + p * G_THREADS;
-            T* d = &xs[buf][(idx / (GB_K / C)) * LD + (idx % (GB_K / C)) * C];
+            const int idx = threadIdx.x + p * G_THREADS;
+            T* d = xs + (idx / PER_ROW) * LD + (idx % PER_ROW) * C;
             reinterpret_cast<uint2*>(d)[0] = make_uint2(xr[p].x, xr[p].y);
             reinterpret_cast<uint2*>(d)[1] = make_uint2(xr[p].z, xr[p].w);
         }
 #pragma unroll
         for (int p = 0; p < WCH; ++p) {
-            const int idx = tid + p * G_THREADS;
-            T* d = &ws[buf][(idx / (GB_K / C)) * LD + (idx % (GB_K / C)) * C];
+            const int idx = threadIdx.x + p * G_THREADS;
+            T* d = ws + (idx / PER_ROW) * LD + (idx % PER_ROW) * C;
             reinterpret_cast<uint2*>(d)[0] = make_uint2(wr[p].x, wr[p].y);
             reinterpret_cast<uint2*>(d)[1] = make_uint2(wr[p].z, wr[p].w);
         }
-    };
+    }
+};
 
-    // operand rows of this lane: A row (wave row = lane), B expert row for each chain
+// chain c of a wave: expert group (c & 2) + ((c & 1) ^ half) of the wave's 128 experts
+__device__ __forceinline__ int chain_group(int c, int half) { return (c & 2) + ((c & 1) ^ half); }
+
+// Slices [s0, s1) of h (slice s = columns 32s .. 32s+31).  acc holds the current chunk's
+// chains; at the end of each chunk, when TOTAL, acc is added to total and restarted at +0.
+// Without TOTAL the range must be one chunk and acc holds its sums on return.
+template <typename T, bool TOTAL>
+__device__ __forceinline__ void gate_slices(const T* x, const T* w, int64_t G, int64_t E, int64_t H,
+                                            int64_t m0, int64_t n0, int64_t s0, int64_t s1, T* xs,
+                                            T* ws, floatx32_t (&acc)[4], floatx32_t (&total)[4]) {
+    typedef GateStage<T> S;
+    typedef typename GateIO<T>::Quad Quad;
+    constexpr int LD = S::LD;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int wm = wv >> 1, wn = wv & 1, half = lane >> 5;
     const int arow = wm * 64 + lane;
     int brow[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) brow[c] = wn * 128 + 32 * ((c & 2) + ((c & 1) ^ half)) + (lane & 31);
-
-    floatx32_t acc[4];
+    for (int c = 0; c < 4; ++c) brow[c] = wn * 128 + 32 * chain_group(c, half) + (lane & 31);
 #pragma unroll
     for (int c = 0; c < 4; ++c)
 #pragma unroll
         for (int v = 0; v < 32; ++v) acc[c][v] = 0.f;
-
-    const int64_t KT = (H + GB_K - 1) / GB_K;
-    gload(0);
-    sstore(0);
+    S st;
+    st.load(x, w, G, E, H, m0, n0, s0 * GB_K);
+    st.store(xs, ws);
     __syncthreads();
-    for (int64_t kt = 0; kt < KT; ++kt) {
-        const int cur = static_cast<int>(kt & 1);
-        if (kt + 1 < KT) gload((kt + 1) * GB_K);
-        const T* xa = &xs[cur][arow * LD];
+    for (int64_t sl = s0; sl < s1; ++sl) {
+        const int cur = static_cast<int>((sl - s0) & 1);
+        const T* xc = xs + cur * (GB_M * LD);
+        const T* wc = ws + cur * (GB_N * LD);
+        const bool more = sl + 1 < s1;
+        if (more) st.load(x, w, G, E, H, m0, n0, (sl + 1) * GB_K);
+        const T* xa = xc + arow * LD;
         const T* wb[4];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) wb[c] = &ws[cur][brow[c] * LD];
+        for (int c = 0; c < 4; ++c) wb[c] = wc + brow[c] * LD;
 #pragma unroll
         for (int kg = 0; kg < GB_K / 4; ++kg) {
             const Quad qa = *reinterpret_cast<const Quad*>(xa + kg * 4);
@@ -154,25 +171,127 @@ __global__ __launch_bounds__(G_THREADS) void gate_exact_kernel(const T* __restri
                     acc[c] = __builtin_amdgcn_mfma_f32_32x32x1f32(av, GateIO<T>::val(qb[c], t), acc[c], 0, 0, 0);
             }
         }
-        if (kt + 1 < KT) sstore(cur ^ 1);
+        if (TOTAL && (sl % SLICES_PER_CHUNK) == SLICES_PER_CHUNK - 1) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+#pragma unroll
+                for (int v = 0; v < 32; ++v) {
+                    total[c][v] = total[c][v] + acc[c][v];
+                    acc[c][v] = 0.f;
+                }
+        }
+        if (more) st.store(xs + (cur ^ 1) * (GB_M * LD), ws + (cur ^ 1) * (GB_N * LD));
         __syncthreads();
     }
-    // block b of chain c: rows 32b + 8*(v/4) + 4*(lane/32) + v%4, expert group (c&2)+((c&1)^b)
+}
+
+// out[g, e] for the lane's accumulator element (chain c, block b, register v)
+__device__ __forceinline__ void chain_coords(int c, int b, int v, int lane, int64_t m0, int64_t n0,
+                                             int64_t& g, int64_t& e) {
+    const int wv = threadIdx.x >> 6, wm = wv >> 1, wn = wv & 1, half = lane >> 5;
+    e = n0 + wn * 128 + 32 * chain_group(c, b) + (lane & 31);
+    g = m0 + wm * 64 + 32 * b + 8 * (v >> 2) + 4 * half + (v & 3);
+}
+
+// large batches: all chunks in one block, running total in registers
+template <typename T>
+__global__ __launch_bounds__(G_THREADS) void gate_exact_kernel(const T* __restrict__ x,
+                                                               const T* __restrict__ w,
+                                                               const int32_t* __restrict__ row_valid,
+                                                               int64_t G, int64_t E, int64_t H,
+                                                               float* __restrict__ logits) {
+    constexpr int LD = GateStage<T>::LD;
+    __shared__ __attribute__((aligned(16))) T xs[2 * GB_M * LD];
+    __shared__ __attribute__((aligned(16))) T ws[2 * GB_N * LD];
+    const int64_t m0 = static_cast<int64_t>(blockIdx.x) * GB_M;
+    const int64_t n0 = static_cast<int64_t>(blockIdx.y) * GB_N;
+    const int lane = threadIdx.x & 63;
+    floatx32_t acc[4], total[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < 4; ++c)
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            const int64_t e = n0 + wn * 128 + 32 * ((c & 2) + ((c & 1) ^ b)) + (lane & 31);
+        for (int v = 0; v < 32; ++v) total[c][v] = 0.f;
+    // the last chunk may be ragged: its slices past H read zeros, which add +0 products
+    const int64_t nslices = ceil_div(H, GATE_CHUNK) * SLICES_PER_CHUNK;
+    gate_slices<T, true>(x, w, G, E, H, m0, n0, 0, nslices, xs, ws, acc, total);
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const int64_t g = m0 + wm * 64 + 32 * b + 8 * (v >> 2) + 4 * half + (v & 3);
+                int64_t g, e;
+                chain_coords(c, b, v, lane, m0, n0, g, e);
                 if (g < G && e < E) {
                     const bool valid = row_valid == nullptr || row_valid[g] != 0;
-                    logits[g * E + e] = valid ? acc[c][16 * b + v] : 0.f;
+                    logits[g * E + e] = valid ? total[c][16 * b + v] : 0.f;
                 }
             }
-        }
+}
+
+// small batches: blockIdx.z = chunk; writes the chunk's sums to parts[chunk][G][E]
+template <typename T>
+__global__ __launch_bounds__(G_THREADS) void gate_chunk_kernel(const T* __restrict__ x,
+                                                               const T* __restrict__ w, int64_t G,
+                                                               int64_t E, int64_t H,
+                                                               float* __restrict__ parts) {
+    constexpr int LD = GateStage<T>::LD;
+    __shared__ __attribute__((aligned(16))) T xs[2 * GB_M * LD];
+    __shared__ __attribute__((aligned(16))) T ws[2 * GB_N * LD];
+    const int64_t m0 = static_cast<int64_t>(blockIdx.x) * GB_M;
+    const int64_t n0 = static_cast<int64_t>(blockIdx.y) * GB_N;
+    const int64_t ch = blockIdx.z;
+    const int lane = threadIdx.x & 63;
+    floatx32_t acc[4], unused[4];
+    gate_slices<T, false>(x, w, G, E, H, m0, n0, ch * SLICES_PER_CHUNK, (ch + 1) * SLICES_PER_CHUNK,
+                          xs, ws, acc, unused);
+    float* out = parts + ch * G * E;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                int64_t g, e;
+                chain_coords(c, b, v, lane, m0, n0, g, e);
+                if (g < G && e < E) out[g * E + e] = acc[c][16 * b + v];
+            }
+}
+
+// logits = ((+0 + part_0) + part_1) + ... in chunk order
+__global__ __launch_bounds__(256) void gate_reduce_kernel(const float* __restrict__ parts,
+                                                          const int32_t* __restrict__ row_valid,
+                                                          int64_t G, int64_t E, int64_t nchunks,
+                                                          float* __restrict__ logits) {
+    const int64_t n = G * E;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
+         i += static_cast<int64_t>(gridDim.x) * 256) {
+        float t = 0.f;
+        for (int64_t c = 0; c < nchunks; ++c) t = t + parts[c * n + i];
+        const int64_t g = i / E;
+        logits[i] = (row_valid == nullptr || row_valid[g] != 0) ? t : 0.f;
     }
+}
+
+int gate_num_cus() {
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cus[dev] == 0) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+            v = 256;
+        cus[dev] = v;
+    }
+    return cus[dev];
+}
+
+// workspace the chunk-parallel gate needs; 0 when the batch is large enough for the
+// running-total kernel to fill the GPU
+size_t gate_split_bytes(int64_t G, int64_t E, int64_t H) {
+    const int64_t tiles = ceil_div(G, GB_M) * ceil_div(E, GB_N);
+    if (tiles * 2 >= gate_num_cus()) return 0;
+    return static_cast<size_t>(ceil_div(H, GATE_CHUNK) * G * E) * sizeof(float);
 }
 
 // ------------------------------------------------------------------ selection
@@ -484,10 +603,16 @@ extern "C" moe_status moe_route_from_logits(const float* logits, const int32_t* 
     return moe::launch_select(logits, row_valid, G, bias, cfg, topk_ids, topk_w, stream);
 }
 
+extern "C" size_t moe_route_workspace_size(int64_t G, int32_t num_experts, int64_t H) {
+    if (G <= 0 || num_experts <= 0 || H <= 0) return 0;
+    return moe::gate_split_bytes(G, num_experts, H);
+}
+
 extern "C" moe_status moe_route(const void* global_x, const int32_t* row_valid, int64_t G,
                                 int64_t H, moe_dtype dt, const void* w_router, const float* bias,
                                 const moe_route_cfg* cfg, float* logits, int32_t* topk_ids,
-                                float* topk_w, hipStream_t stream) {
+                                float* topk_w, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
     moe_status st = moe::check_route_cfg(cfg);
     if (st != MOE_OK) return st;
     MOE_CHECK_ARG(G >= 0 && H > 0);
@@ -496,14 +621,34 @@ extern "C" moe_status moe_route(const void* global_x, const int32_t* row_valid, 
     MOE_CHECK_ARG(global_x && w_router && logits && topk_ids && topk_w);
     MOE_CHECK_ARG(G <= (int64_t)1 << 31);
     const int64_t E = cfg->num_experts;
-    dim3 grid(static_cast<unsigned>(moe::ceil_div(G, moe::GB_M)),
-              static_cast<unsigned>(moe::ceil_div(E, moe::GB_N)));
-    if (dt == MOE_BF16) {
-        hipLaunchKernelGGL(moe::gate_exact_kernel<uint16_t>, grid, dim3(moe::G_THREADS), 0, stream,
-                           static_cast<const uint16_t*>(global_x),
-                           static_cast<const uint16_t*>(w_router), row_valid, G, E, H, logits);
+    const size_t split = moe::gate_split_bytes(G, E, H);
+    const bool use_split = split > 0 && workspace != nullptr && workspace_bytes >= split &&
+                           moe::aligned(workspace, 16);
+    const dim3 tiles(static_cast<unsigned>(moe::ceil_div(G, moe::GB_M)),
+                     static_cast<unsigned>(moe::ceil_div(E, moe::GB_N)));
+    if (use_split) {
+        const int64_t nch = moe::ceil_div(H, moe::GATE_CHUNK);
+        const dim3 grid(tiles.x, tiles.y, static_cast<unsigned>(nch));
+        float* parts = static_cast<float*>(workspace);
+        if (dt == MOE_BF16)
+            hipLaunchKernelGGL(moe::gate_chunk_kernel<uint16_t>, grid, dim3(moe::G_THREADS), 0, stream,
+                               static_cast<const uint16_t*>(global_x), static_cast<const uint16_t*>(w_router),
+                               G, E, H, parts);
+        else
+            hipLaunchKernelGGL(moe::gate_chunk_kernel<float>, grid, dim3(moe::G_THREADS), 0, stream,
+                               static_cast<const float*>(global_x), static_cast<const float*>(w_router),
+                               G, E, H, parts);
+        MOE_LAUNCH_CHECK();
+        int64_t rb = moe::ceil_div(G * E, 256);
+        if (rb > 4096) rb = 4096;
+        hipLaunchKernelGGL(moe::gate_reduce_kernel, dim3(static_cast<unsigned>(rb)), dim3(256), 0, stream,
+                           parts, row_valid, G, E, nch, logits);
+    } else if (dt == MOE_BF16) {
+        hipLaunchKernelGGL(moe::gate_exact_kernel<uint16_t>, tiles, dim3(moe::G_THREADS), 0, stream,
+                           static_cast<const uint16_t*>(global_x), static_cast<const uint16_t*>(w_router),
+                           row_valid, G, E, H, logits);
     } else {
-        hipLaunchKernelGGL(moe::gate_exact_kernel<float>, grid, dim3(moe::G_THREADS), 0, stream,
+        hipLaunchKernelGGL(moe::gate_exact_kernel<float>, tiles, dim3(moe::G_THREADS), 0, stream,
                            static_cast<const float*>(global_x), static_cast<const float*>(w_router),
                            row_valid, G, E, H, logits);
     }

@@ -136,6 +136,15 @@ def test_workspace_sizes(m):
     assert m.moe_expert_gemm_workspace_size(1000, 7168, 2048, torch.bfloat16, torch.bfloat16) >= 1000 * 2048 * 2
 
 
+def test_route_workspace_size(m):
+    # small batches get the chunk-partial table fp32[ceil(H/128), G, E]; batches with enough
+    # 128x256 tiles to fill the GPU need none
+    assert m.moe_route_workspace_size(384, 256, 7168) == 56 * 384 * 256 * 4
+    assert m.moe_route_workspace_size(300, 64, 1000) == 8 * 300 * 64 * 4
+    assert m.moe_route_workspace_size(32768, 256, 7168) == 0
+    assert m.moe_route_workspace_size(0, 256, 7168) == 0
+
+
 def test_status_strings(m):
     lib = m.lib()
     assert lib.moe_status_string(0) == b"ok"

@@ -193,6 +193,35 @@ def test_identity_experts_combine_returns_weighted_sum():
     assert torch.allclose(ref, x, atol=1e-5)
 
 
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
+def test_gate_kernels_bitwise(dt):
+    # both gate kernels -- chunk-parallel with the partial table (small G) and the
+    # running-total one (large G, or no workspace) -- against the oracle, bit for bit, with a
+    # ragged last chunk (H = 7 * 128 + 104) and ragged row / expert tiles
+    import combine_dp_gather_amd as m
+    rng = np.random.default_rng(21)
+    cfg = m.make_route_cfg("softmax", 200, 4)
+    for G, H in ((300, 1000), (128 * 128 + 37, 232)):
+        say(f"[gate] dtype={dt} G={G} H={H} E=200")
+        x = torch.from_numpy(rng.standard_normal((G, H)).astype(np.float32)).to(dt)
+        w = torch.from_numpy((rng.standard_normal((200, H)) * 0.05).astype(np.float32)).to(dt)
+        rv = np.ones(G, dtype=np.int32)
+        rv[::17] = 0
+        xb = x.view(torch.int16).numpy().view(np.uint16) if dt == torch.bfloat16 else x.numpy()
+        wb = w.view(torch.int16).numpy().view(np.uint16) if dt == torch.bfloat16 else w.numpy()
+        ref = oracle.gate_logits(xb, wb, row_valid=rv)
+        xd, wd, rvd = x.cuda(), w.cuda(), torch.from_numpy(rv).cuda()
+        ws_bytes = m.moe_route_workspace_size(G, 200, H)
+        assert (ws_bytes > 0) == (G < 1000)
+        for ws in ([None, torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")] if ws_bytes else [None]):
+            lg = torch.full((G, 200), float("nan"), device="cuda")
+            ids = torch.empty((G, 4), dtype=torch.int32, device="cuda")
+            tw = torch.empty((G, 4), dtype=torch.float32, device="cuda")
+            m.moe_route(xd, rvd, wd, None, cfg, lg, ids, tw, ws)
+            torch.cuda.synchronize()
+            assert np.array_equal(lg.cpu().numpy().view(np.uint32), ref.view(np.uint32)), ws is None
+
+
 def test_route_from_logits_ties_and_fake_balance():
     import combine_dp_gather_amd as m
     # constructed exact ties: equal logits -> lowest ids, in order
