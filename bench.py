@@ -39,6 +39,17 @@ WORKLOAD_TEXT = {
 }
 
 
+# profile summaries are named for the kernel and the workload they cover
+PROFILE_WORKLOAD = {"cfg4": "prefill_8x4096_bf16", "cfg5": "prefill_8x2048_fp8",
+                    "cfg3": "decode_16x24_bf16", "cfg2": "dp4_gather_bf16", "cfg1": "tiny_fp32"}
+GEMM_SOURCES = {
+    "bf16": ["combine_dp_gather_amd/csrc/expert_gemm.hip", "combine_dp_gather_amd/csrc/gemm_common.h",
+             "combine_dp_gather_amd/csrc/moe_dev.h"],
+    "fp8": ["combine_dp_gather_amd/csrc/expert_gemm_fp8.hip", "combine_dp_gather_amd/csrc/gemm_common.h",
+            "combine_dp_gather_amd/csrc/moe_dev.h"],
+}
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -72,7 +83,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="cfg4")
     ap.add_argument("--mode", default="sum", choices=["sum", "max", "auto"])
-    ap.add_argument("--cpu-sample", type=int, default=256, help="tokens per replica for the oracle")
+    ap.add_argument("--cpu-sample", type=int, default=2048, help="tokens per replica for the oracle")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run a plain device copy of MIB MiB (reference for HBM counters)")
@@ -151,6 +162,7 @@ def main():
     ms_per_step = total_ms / args.steps
     T = cfg.T
     H, I, E, k, G = cfg.hidden, cfg.inter, cfg.num_experts, cfg.top_k, layer.G
+    E_slots = cfg.num_local
     es = 2 if bf else 4
     mm = "mfma8" if cfg.weight_format == "fp8_block" else "mfma"
     # algorithmic work per call (bytes or flops), per-unit figures x units
@@ -182,9 +194,16 @@ def main():
     roof = dict(kernels[dom])
     roof.pop("ms")
     roof.pop("peak_kind")
-    roof["kernel"] = ("grouped_gemm_fp8_kernel<up> (gate+up SwiGLU)" if mm == "mfma8"
-                      else "grouped_gemm_bf16_kernel<up> (gate+up SwiGLU)")
-    roof["traffic"] = None
+    fmt = "fp8" if mm == "mfma8" else "bf16"
+    kname = f"grouped_gemm_{fmt}_kernel<true>"
+    roof["kernel"] = kname + (" (gate+up SwiGLU" + (", with its activation quantisation" if fmt == "fp8" else "")
+                              + ")")
+    from combine_dp_gather_amd.profiling import read_traffic_summary
+    summary = os.path.join(ROOT, "profiles",
+                           f"{kname.replace('<true>', '_up')}__{PROFILE_WORKLOAD[args.workload]}__traffic.txt")
+    tb = read_traffic_summary(summary, GEMM_SOURCES[fmt])
+    roof["traffic"] = round(tb) if tb is not None else None
+    roof["algorithmic_bytes"] = R * H * es + E_slots * 2 * I * H * (1 if fmt == "fp8" else es) + R * I * es
     result = {
         "metric": "MoE-layer tokens/s at 1 GPU; grouped-GEMM % peak MFMA; dispatch/combine % HBM",
         "value": round(T * args.steps / (total_ms / 1e3), 2),

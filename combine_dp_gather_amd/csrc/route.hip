@@ -12,6 +12,7 @@
 // K slices staged through LDS as fp32 (bf16 widened exactly), double-buffered.
 #include <float.h>
 
+#include "gemm_common.h"
 #include "moe_dev.h"
 
 namespace moe {
@@ -71,7 +72,6 @@ __device__ __forceinline__ uint4 load_piece(const T* __restrict__ src, int64_t r
     uint4 v = {0, 0, 0, 0};
     if (r >= rows || k >= H) return v;
     const T* p = src + r * H + k;
-    if (k + C <= H && ((reinterpret_cast<uintptr_t>(p) & 15) == 0)) return *reinterpret_cast<const uint4*>(p);
     T t[C];
 #pragma unroll
     for (int q = 0; q < C; ++q) t[q] = (k + q < H) ? p[q] : T(0);
@@ -79,8 +79,12 @@ __device__ __forceinline__ uint4 load_piece(const T* __restrict__ src, int64_t r
     return v;
 }
 
+typedef unsigned int gate_u32x4 __attribute__((ext_vector_type(4)));
+
 // Staging of one slice: x rows [m0, m0+128) and w rows [n0, n0+256), columns k0 .. k0+GB_K,
-// in LDS as [row][k] with row stride LD.
+// in LDS as [row][k] with row stride LD.  The fast load is a 16-byte buffer load per piece
+// from a descriptor over the block's rows only, so rows past G (or E) read as zeros; the
+// element-wise load covers a slice that runs past H and unaligned inputs.
 template <typename T>
 struct GateStage {
     static constexpr int C = GateIO<T>::kChunk;
@@ -89,8 +93,22 @@ struct GateStage {
     static constexpr int XCH = GB_M * PER_ROW / G_THREADS;
     static constexpr int WCH = GB_N * PER_ROW / G_THREADS;
     uint4 xr[XCH], wr[WCH];
-    __device__ void load(const T* x, const T* w, int64_t G, int64_t E, int64_t H, int64_t m0,
-                         int64_t n0, int64_t k0) {
+    __device__ void load_fast(__amdgpu_buffer_rsrc_t rx, __amdgpu_buffer_rsrc_t rw,
+                              const uint32_t (&xoff)[XCH], const uint32_t (&woff)[WCH], int64_t k0) {
+        const int so = static_cast<int>(k0 * static_cast<int64_t>(sizeof(T)));
+#pragma unroll
+        for (int p = 0; p < XCH; ++p) {
+            const gate_u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rx, static_cast<int>(xoff[p]), so, 0);
+            xr[p] = make_uint4(v.x, v.y, v.z, v.w);
+        }
+#pragma unroll
+        for (int p = 0; p < WCH; ++p) {
+            const gate_u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rw, static_cast<int>(woff[p]), so, 0);
+            wr[p] = make_uint4(v.x, v.y, v.z, v.w);
+        }
+    }
+    __device__ void load_slow(const T* x, const T* w, int64_t G, int64_t E,
+                              int64_t H, int64_t m0, int64_t n0, int64_t k0) {
 #pragma unroll
         for (int p = 0; p < XCH; ++p) {
             const int idx = threadIdx.x + p * G_THREADS;
@@ -102,20 +120,32 @@ struct GateStage {
             wr[p] = load_piece(w, E, H, n0 + idx / PER_ROW, k0 + (idx % PER_ROW) * C);
         }
     }
-    __device__ void store(T* xs, T* ws) {
+    // LDS holds fp32: bf16 widens here, once per element, so the matrix-core loop reads its
+    // operands straight from LDS
+    __device__ static void put(float* d, const uint4& v) {
+        float4 lo, hi;
+        if constexpr (sizeof(T) == 2) {
+            lo = make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
+                             __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u));
+            hi = make_float4(__uint_as_float(v.z << 16), __uint_as_float(v.z & 0xffff0000u),
+                             __uint_as_float(v.w << 16), __uint_as_float(v.w & 0xffff0000u));
+            reinterpret_cast<float4*>(d)[0] = lo;
+            reinterpret_cast<float4*>(d)[1] = hi;
+        } else {
+            reinterpret_cast<float4*>(d)[0] =
+                make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
+        }
+    }
+    __device__ void store(float* xs, float* ws) {
 #pragma unroll
         for (int p = 0; p < XCH; ++p) {
             const int idx = threadIdx.x + p * G_THREADS;
-            T* d = xs + (idx / PER_ROW) * LD + (idx % PER_ROW) * C;
-            reinterpret_cast<uint2*>(d)[0] = make_uint2(xr[p].x, xr[p].y);
-            reinterpret_cast<uint2*>(d)[1] = make_uint2(xr[p].z, xr[p].w);
+            put(xs + (idx / PER_ROW) * LD + (idx % PER_ROW) * C, xr[p]);
         }
 #pragma unroll
         for (int p = 0; p < WCH; ++p) {
             const int idx = threadIdx.x + p * G_THREADS;
-            T* d = ws + (idx / PER_ROW) * LD + (idx % PER_ROW) * C;
-            reinterpret_cast<uint2*>(d)[0] = make_uint2(wr[p].x, wr[p].y);
-            reinterpret_cast<uint2*>(d)[1] = make_uint2(wr[p].z, wr[p].w);
+            put(ws + (idx / PER_ROW) * LD + (idx % PER_ROW) * C, wr[p]);
         }
     }
 };
@@ -123,15 +153,18 @@ struct GateStage {
 // chain c of a wave: expert group (c & 2) + ((c & 1) ^ half) of the wave's 128 experts
 __device__ __forceinline__ int chain_group(int c, int half) { return (c & 2) + ((c & 1) ^ half); }
 
-// Slices [s0, s1) of h (slice s = columns 32s .. 32s+31).  acc holds the current chunk's
-// chains; at the end of each chunk, when TOTAL, acc is added to total and restarted at +0.
-// Without TOTAL the range must be one chunk and acc holds its sums on return.
+// Chunks [ch0, ch1) of h for the block's 128 x 256 tile (chunk c = slices 4c .. 4c+3, slice
+// s = columns 32s .. 32s+31).  Each chunk's chains start from +0 and see only matrix-core
+// adds, so they stay in the accumulator registers; with TOTAL the chunk's sums are then
+// added to `total`, else (a single chunk) they are left in acc.  `fast` (block-uniform): the
+// inputs are 16-byte aligned with rows a multiple of 16 bytes.
 template <typename T, bool TOTAL>
-__device__ __forceinline__ void gate_slices(const T* x, const T* w, int64_t G, int64_t E, int64_t H,
-                                            int64_t m0, int64_t n0, int64_t s0, int64_t s1, T* xs,
-                                            T* ws, floatx32_t (&acc)[4], floatx32_t (&total)[4]) {
+__device__ __forceinline__ void gate_chunks(const T* x, const T* w, int64_t G, int64_t E, int64_t H,
+                                            int64_t m0, int64_t n0, int64_t ch0, int64_t ch1,
+                                            bool fast, float* xs, float* ws, floatx32_t (&acc)[4],
+                                            floatx32_t (&total)[4]) {
     typedef GateStage<T> S;
-    typedef typename GateIO<T>::Quad Quad;
+    typedef typename GateIO<float>::Quad Quad;
     constexpr int LD = S::LD;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int wm = wv >> 1, wn = wv & 1, half = lane >> 5;
@@ -139,49 +172,76 @@ __device__ __forceinline__ void gate_slices(const T* x, const T* w, int64_t G, i
     int brow[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) brow[c] = wn * 128 + 32 * chain_group(c, half) + (lane & 31);
+    // descriptors over the block's own rows: byte offsets stay below 256 * H * sizeof(T)
+    const int64_t xrows = G - m0 < GB_M ? G - m0 : GB_M;
+    const int64_t wrows = E - n0 < GB_N ? E - n0 : GB_N;
+    const __amdgpu_buffer_rsrc_t rx =
+        gemm::make_rsrc_uniform(x + m0 * H, static_cast<uint32_t>(xrows * H * static_cast<int64_t>(sizeof(T))));
+    const __amdgpu_buffer_rsrc_t rw =
+        gemm::make_rsrc_uniform(w + n0 * H, static_cast<uint32_t>(wrows * H * static_cast<int64_t>(sizeof(T))));
+    uint32_t xoff[S::XCH], woff[S::WCH];
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
+    for (int p = 0; p < S::XCH; ++p) {
+        const int idx = threadIdx.x + p * G_THREADS;
+        xoff[p] = static_cast<uint32_t>(((idx / S::PER_ROW) * H + (idx % S::PER_ROW) * S::C) * sizeof(T));
+    }
 #pragma unroll
-        for (int v = 0; v < 32; ++v) acc[c][v] = 0.f;
+    for (int p = 0; p < S::WCH; ++p) {
+        const int idx = threadIdx.x + p * G_THREADS;
+        woff[p] = static_cast<uint32_t>(((idx / S::PER_ROW) * H + (idx % S::PER_ROW) * S::C) * sizeof(T));
+    }
     S st;
-    st.load(x, w, G, E, H, m0, n0, s0 * GB_K);
+    const int64_t s_begin = ch0 * SLICES_PER_CHUNK, s_end = ch1 * SLICES_PER_CHUNK;
+    auto load = [&](int64_t sl) {
+        const int64_t k0 = sl * GB_K;
+        if (fast && k0 + GB_K <= H)
+            st.load_fast(rx, rw, xoff, woff, k0);
+        else
+            st.load_slow(x, w, G, E, H, m0, n0, k0);
+    };
+    load(s_begin);
     st.store(xs, ws);
     __syncthreads();
-    for (int64_t sl = s0; sl < s1; ++sl) {
-        const int cur = static_cast<int>((sl - s0) & 1);
-        const T* xc = xs + cur * (GB_M * LD);
-        const T* wc = ws + cur * (GB_N * LD);
-        const bool more = sl + 1 < s1;
-        if (more) st.load(x, w, G, E, H, m0, n0, (sl + 1) * GB_K);
-        const T* xa = xc + arow * LD;
-        const T* wb[4];
+    for (int64_t ch = ch0; ch < ch1; ++ch) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) wb[c] = wc + brow[c] * LD;
+        for (int c = 0; c < 4; ++c)
 #pragma unroll
-        for (int kg = 0; kg < GB_K / 4; ++kg) {
-            const Quad qa = *reinterpret_cast<const Quad*>(xa + kg * 4);
-            Quad qb[4];
+            for (int v = 0; v < 32; ++v) acc[c][v] = 0.f;
+#pragma unroll 1
+        for (int q = 0; q < SLICES_PER_CHUNK; ++q) {
+            const int64_t sl = ch * SLICES_PER_CHUNK + q;
+            const int cur = static_cast<int>((sl - s_begin) & 1);
+            const float* xc = xs + cur * (GB_M * LD);
+            const float* wc = ws + cur * (GB_N * LD);
+            const bool more = sl + 1 < s_end;
+            if (more) load(sl + 1);
+            const float* xa = xc + arow * LD;
+            const float* wb[4];
 #pragma unroll
-            for (int c = 0; c < 4; ++c) qb[c] = *reinterpret_cast<const Quad*>(wb[c] + kg * 4);
+            for (int c = 0; c < 4; ++c) wb[c] = wc + brow[c] * LD;
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const float av = GateIO<T>::val(qa, t);
+            for (int kg = 0; kg < GB_K / 4; ++kg) {
+                const Quad qa = *reinterpret_cast<const Quad*>(xa + kg * 4);
+                Quad qb[4];
 #pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    acc[c] = __builtin_amdgcn_mfma_f32_32x32x1f32(av, GateIO<T>::val(qb[c], t), acc[c], 0, 0, 0);
+                for (int c = 0; c < 4; ++c) qb[c] = *reinterpret_cast<const Quad*>(wb[c] + kg * 4);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const float av = GateIO<float>::val(qa, t);
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        acc[c] = __builtin_amdgcn_mfma_f32_32x32x1f32(av, GateIO<float>::val(qb[c], t), acc[c], 0, 0, 0);
+                }
             }
+            if (more) st.store(xs + (cur ^ 1) * (GB_M * LD), ws + (cur ^ 1) * (GB_N * LD));
+            __syncthreads();
         }
-        if (TOTAL && (sl % SLICES_PER_CHUNK) == SLICES_PER_CHUNK - 1) {
+        if (TOTAL) {
 #pragma unroll
             for (int c = 0; c < 4; ++c)
 #pragma unroll
-                for (int v = 0; v < 32; ++v) {
-                    total[c][v] = total[c][v] + acc[c][v];
-                    acc[c][v] = 0.f;
-                }
+                for (int v = 0; v < 32; ++v) total[c][v] = total[c][v] + acc[c][v];
         }
-        if (more) st.store(xs + (cur ^ 1) * (GB_M * LD), ws + (cur ^ 1) * (GB_N * LD));
-        __syncthreads();
     }
 }
 
@@ -199,10 +259,10 @@ __global__ __launch_bounds__(G_THREADS) void gate_exact_kernel(const T* __restri
                                                                const T* __restrict__ w,
                                                                const int32_t* __restrict__ row_valid,
                                                                int64_t G, int64_t E, int64_t H,
-                                                               float* __restrict__ logits) {
+                                                               bool fast, float* __restrict__ logits) {
     constexpr int LD = GateStage<T>::LD;
-    __shared__ __attribute__((aligned(16))) T xs[2 * GB_M * LD];
-    __shared__ __attribute__((aligned(16))) T ws[2 * GB_N * LD];
+    __shared__ __attribute__((aligned(16))) float xs[2 * GB_M * LD];
+    __shared__ __attribute__((aligned(16))) float ws[2 * GB_N * LD];
     const int64_t m0 = static_cast<int64_t>(blockIdx.x) * GB_M;
     const int64_t n0 = static_cast<int64_t>(blockIdx.y) * GB_N;
     const int lane = threadIdx.x & 63;
@@ -211,9 +271,8 @@ __global__ __launch_bounds__(G_THREADS) void gate_exact_kernel(const T* __restri
     for (int c = 0; c < 4; ++c)
 #pragma unroll
         for (int v = 0; v < 32; ++v) total[c][v] = 0.f;
-    // the last chunk may be ragged: its slices past H read zeros, which add +0 products
-    const int64_t nslices = ceil_div(H, GATE_CHUNK) * SLICES_PER_CHUNK;
-    gate_slices<T, true>(x, w, G, E, H, m0, n0, 0, nslices, xs, ws, acc, total);
+    // the last chunk may be ragged: its columns past H read zeros, which add +0 products
+    gate_chunks<T, true>(x, w, G, E, H, m0, n0, 0, ceil_div(H, GATE_CHUNK), fast, xs, ws, acc, total);
 #pragma unroll
     for (int c = 0; c < 4; ++c)
 #pragma unroll
@@ -233,18 +292,17 @@ __global__ __launch_bounds__(G_THREADS) void gate_exact_kernel(const T* __restri
 template <typename T>
 __global__ __launch_bounds__(G_THREADS) void gate_chunk_kernel(const T* __restrict__ x,
                                                                const T* __restrict__ w, int64_t G,
-                                                               int64_t E, int64_t H,
+                                                               int64_t E, int64_t H, bool fast,
                                                                float* __restrict__ parts) {
     constexpr int LD = GateStage<T>::LD;
-    __shared__ __attribute__((aligned(16))) T xs[2 * GB_M * LD];
-    __shared__ __attribute__((aligned(16))) T ws[2 * GB_N * LD];
+    __shared__ __attribute__((aligned(16))) float xs[2 * GB_M * LD];
+    __shared__ __attribute__((aligned(16))) float ws[2 * GB_N * LD];
     const int64_t m0 = static_cast<int64_t>(blockIdx.x) * GB_M;
     const int64_t n0 = static_cast<int64_t>(blockIdx.y) * GB_N;
     const int64_t ch = blockIdx.z;
     const int lane = threadIdx.x & 63;
     floatx32_t acc[4], unused[4];
-    gate_slices<T, false>(x, w, G, E, H, m0, n0, ch * SLICES_PER_CHUNK, (ch + 1) * SLICES_PER_CHUNK,
-                          xs, ws, acc, unused);
+    gate_chunks<T, false>(x, w, G, E, H, m0, n0, ch, ch + 1, fast, xs, ws, acc, unused);
     float* out = parts + ch * G * E;
 #pragma unroll
     for (int c = 0; c < 4; ++c)
@@ -626,6 +684,11 @@ extern "C" moe_status moe_route(const void* global_x, const int32_t* row_valid, 
                            moe::aligned(workspace, 16);
     const dim3 tiles(static_cast<unsigned>(moe::ceil_div(G, moe::GB_M)),
                      static_cast<unsigned>(moe::ceil_div(E, moe::GB_N)));
+    // 16-byte buffer loads need aligned bases and rows; the per-block descriptors span at
+    // most 256 rows, which must stay below 2 GiB
+    const size_t esz = dt == MOE_BF16 ? 2 : 4;
+    const bool fast = moe::aligned(global_x, 16) && moe::aligned(w_router, 16) && (H * esz) % 16 == 0 &&
+                      static_cast<int64_t>(moe::GB_N) * H * static_cast<int64_t>(esz) < ((int64_t)1 << 31);
     if (use_split) {
         const int64_t nch = moe::ceil_div(H, moe::GATE_CHUNK);
         const dim3 grid(tiles.x, tiles.y, static_cast<unsigned>(nch));
@@ -633,11 +696,11 @@ extern "C" moe_status moe_route(const void* global_x, const int32_t* row_valid, 
         if (dt == MOE_BF16)
             hipLaunchKernelGGL(moe::gate_chunk_kernel<uint16_t>, grid, dim3(moe::G_THREADS), 0, stream,
                                static_cast<const uint16_t*>(global_x), static_cast<const uint16_t*>(w_router),
-                               G, E, H, parts);
+                               G, E, H, fast, parts);
         else
             hipLaunchKernelGGL(moe::gate_chunk_kernel<float>, grid, dim3(moe::G_THREADS), 0, stream,
                                static_cast<const float*>(global_x), static_cast<const float*>(w_router),
-                               G, E, H, parts);
+                               G, E, H, fast, parts);
         MOE_LAUNCH_CHECK();
         int64_t rb = moe::ceil_div(G * E, 256);
         if (rb > 4096) rb = 4096;
@@ -646,11 +709,11 @@ extern "C" moe_status moe_route(const void* global_x, const int32_t* row_valid, 
     } else if (dt == MOE_BF16) {
         hipLaunchKernelGGL(moe::gate_exact_kernel<uint16_t>, tiles, dim3(moe::G_THREADS), 0, stream,
                            static_cast<const uint16_t*>(global_x), static_cast<const uint16_t*>(w_router),
-                           row_valid, G, E, H, logits);
+                           row_valid, G, E, H, fast, logits);
     } else {
         hipLaunchKernelGGL(moe::gate_exact_kernel<float>, tiles, dim3(moe::G_THREADS), 0, stream,
                            static_cast<const float*>(global_x), static_cast<const float*>(w_router),
-                           row_valid, G, E, H, logits);
+                           row_valid, G, E, H, fast, logits);
     }
     MOE_LAUNCH_CHECK();
     return moe::launch_select(logits, row_valid, G, bias, cfg, topk_ids, topk_w, stream);
