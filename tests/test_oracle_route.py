@@ -247,3 +247,18 @@ def test_fake_uniform_logits_balanced():
     assert hist.min() > 0.6 * mean and hist.max() < 1.4 * mean
     bal = (hist.mean() + 1e-5) / (hist.max() + 1e-5)
     assert bal > 0.7
+
+
+def test_zipf_bias_gives_slope_near_minus_1_2():
+    # skewed-load workload: popularity p_e ~ (e+1)^-1.2 imposed through the router bias
+    # (bias = beta * ln(p_e / p_0)); with beta = 0.12 the realised rank-frequency slope of
+    # the routed ids over the 64 most used experts is -1.2 within 0.1 (4096 tokens)
+    from dataclasses import replace
+    cfg = moe_synth.CONFIGS["cfg5"]
+    small = replace(cfg, num_tokens=(2048, 2048))
+    inp = moe_synth.make_inputs(small, with_experts=False)
+    x = np.concatenate(inp.replicas)
+    _, ids, _ = oracle.route(small, x, np.ones(len(x), np.int32), inp.router_w, inp.bias)
+    freq = np.sort(np.bincount(ids.ravel(), minlength=cfg.num_experts))[::-1][:64].astype(np.float64)
+    slope = np.polyfit(np.log(np.arange(1, 65)), np.log(freq), 1)[0]
+    assert -1.3 < slope < -1.1, slope
