@@ -13,9 +13,11 @@
 //     blocks (256 fp32 accumulators per lane, in AGPRs);
 //   - up kernel: the 256 columns are 128 gate columns and the same 128 up columns, so each
 //     lane holds gate and up for identical (row, i) and applies SiLU*up in registers;
-//   - operands move global -> LDS by buffer DMA (no register staging), 32-deep K slices in 4
-//     LDS stages (3 slices in flight); fragments of the next slice are read into a second
-//     register set while the current slice's second half of MFMAs runs;
+//   - operands move global -> LDS by buffer DMA (no register staging) in 64-deep K slices:
+//     each row contributes one whole 128-byte line per slice, which the DMA path moves about
+//     1.5x faster than half lines.  Two LDS stages of 64 KB: slice kt+1 is in flight while
+//     slice kt is consumed, in two halves whose fragments are read during the previous
+//     half's MFMAs; the reads and refill DMAs are spread between the MFMAs;
 //   - persistent grid (one block per CU), XCD-grouped tile order (gemm_common.h); rows past
 //     a segment's end read as zeros and are never stored; each output tile has one owner.
 // The fp8 path (block-scaled weights) lives in expert_gemm_fp8.hip.
@@ -46,8 +48,8 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx16_t __attribute__((ext_vector_type(16)));
 
 constexpr int BM = 256, BN = 256;
-constexpr int BK = 32;      // K slice per pipeline stage
-constexpr int STAGES = 4;   // LDS stages
+constexpr int BK = 64;      // K slice per pipeline stage: whole 128-byte lines per row
+constexpr int STAGES = 2;   // LDS stages (2 x 64 KB)
 constexpr int M_THREADS = gemm::kThreads;
 constexpr int UP_COLS = BN / 2;     // i-columns per up tile (gate and up each)
 
@@ -135,26 +137,37 @@ __global__ __launch_bounds__(M_THREADS, 1) void grouped_gemm_bf16_kernel(GemmArg
             dbytes = static_cast<uint32_t>(a.N) * row_bytes;
         }
         const __amdgpu_buffer_rsrc_t rsrc = gemm::make_rsrc_uniform(dbase, dbytes);
-        uint32_t voff[LPW];
+        // DMA p of this wave covers tile rows r = ((wv & 1) * LPW + p) * RPB + dma_row.  Its
+        // global row is row(p = 0) + p * RPB for every operand (A rows; up: gate or up half,
+        // chosen by wv & 1; down: w2 rows), and its swizzled chunk depends only on p's parity
+        // (swz(r) = (r / 2) mod 8 with RPB = 8), so two base offsets plus a scalar row step
+        // give all LPW offsets.  The row stays in voffset: the descriptor's range check on it
+        // is what zero-fills rows past the segment end.
+        static_assert(RPB == 8 && BK == 64, "offset scheme assumes 8-row DMA blocks");
+        uint32_t vbase[2];
 #pragma unroll
-        for (int p = 0; p < LPW; ++p) {
-            const int r = ((wv & 1) * LPW + p) * RPB + dma_row;  // tile row 0..255
+        for (int par = 0; par < 2; ++par) {
+            const int r = ((wv & 1) * LPW + par) * RPB + dma_row;  // tile row of DMA p = par
             uint32_t grow;
-            if (loads_a) grow = static_cast<uint32_t>(r);
-            else if (UP) grow = static_cast<uint32_t>((r >> 7) * a.N + nt * UP_COLS + (r & (UP_COLS - 1)));
-            else grow = static_cast<uint32_t>(nt * BN + r);
-            voff[p] = grow * row_bytes + static_cast<uint32_t>(((lane % CPR) ^ swz(r)) * 16);
+            if (loads_a) grow = static_cast<uint32_t>(r - par * RPB);
+            else if (UP) grow = static_cast<uint32_t>((wv & 1) * a.N + nt * UP_COLS + dma_row);
+            else grow = static_cast<uint32_t>(nt * BN + (wv & 1) * LPW * RPB + dma_row);
+            vbase[par] = grow * row_bytes + static_cast<uint32_t>(((lane % CPR) ^ swz(r)) * 16);
         }
+        const uint32_t rstep = static_cast<uint32_t>(RPB) * row_bytes;
         auto issue = [&](int buf, int64_t kt) {
             const int soff = static_cast<int>(kt * BK * 2);
-            // computed at the call, not hoisted: one scalar add per DMA instead of a table of
-            // LDS addresses held in scalar registers for every stage
+            // the LDS base and the two offset bases are made opaque per call so the LPW
+            // offsets are recomputed here (one add each) instead of being hoisted out of the
+            // K loop into LPW registers
             int off = buf * (BM * BK) + (wv & 1) * LPW * 512;
-            asm volatile("" : "+s"(off));
+            uint32_t vb0 = vbase[0], vb1 = vbase[1];
+            asm volatile("" : "+s"(off), "+v"(vb0), "+v"(vb1));
             uint16_t* base = (loads_a ? &As[0][0] : &Bs[0][0]) + off;
 #pragma unroll
             for (int p = 0; p < LPW; ++p) {
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (gemm::lds_void_t*)(base + p * 512), 16, voff[p],
+                const uint32_t vo = ((p & 1) ? vb1 : vb0) + static_cast<uint32_t>(p) * rstep;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (gemm::lds_void_t*)(base + p * 512), 16, vo,
                                                         soff, 0, 0);
             }
         };
@@ -171,65 +184,75 @@ __global__ __launch_bounds__(M_THREADS, 1) void grouped_gemm_bf16_kernel(GemmArg
         const uint16_t* b_rd = &Bs[0][0] + frow * BK;
         // B block j of the wave: up -> blocks 0,1 gate, 2,3 the matching up rows
 #define MOE_BROW(j) (UP ? ((j) >> 1) * UP_COLS + wn * 64 + ((j) & 1) * 32 : wn * 128 + (j) * 32)
-#define MOE_LOAD_FRAGS(FA, FB, BUF)                                                           \
+        // fragments of one half slice (K 32 = two 16-deep MFMA steps) from stage BUF
+#define MOE_LOAD_HALF(FA, FB, BUF, HALF)                                                      \
     do {                                                                                      \
         const uint16_t* Ab_ = a_rd + (BUF) * (BM * BK);                                       \
         const uint16_t* Bb_ = b_rd + (BUF) * (BN * BK);                                       \
-        _Pragma("unroll") for (int ks_ = 0; ks_ < BK / 16; ++ks_) {                           \
+        _Pragma("unroll") for (int ks_ = 0; ks_ < 2; ++ks_) {                                 \
             _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) FA[ks_][i_] =                    \
-                *reinterpret_cast<const bf16x8_t*>(Ab_ + i_ * 32 * BK + fchunk[ks_]);         \
+                *reinterpret_cast<const bf16x8_t*>(Ab_ + i_ * 32 * BK + fchunk[2 * (HALF) + ks_]); \
             _Pragma("unroll") for (int j_ = 0; j_ < 4; ++j_) FB[ks_][j_] =                    \
-                *reinterpret_cast<const bf16x8_t*>(Bb_ + MOE_BROW(j_) * BK + fchunk[ks_]);    \
+                *reinterpret_cast<const bf16x8_t*>(Bb_ + MOE_BROW(j_) * BK + fchunk[2 * (HALF) + ks_]); \
         }                                                                                     \
     } while (0)
-#define MOE_MFMA_KS(FA, FB, KS)                                                               \
+#define MOE_MFMA_HALF(FA, FB)                                                                 \
     do {                                                                                      \
-        _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_)                                      \
-            _Pragma("unroll") for (int j_ = 0; j_ < 4; ++j_) acc[i_][j_] =                    \
-                __builtin_amdgcn_mfma_f32_32x32x16_bf16(FA[KS][i_], FB[KS][j_], acc[i_][j_],  \
-                                                        0, 0, 0);                             \
+        _Pragma("unroll") for (int ks_ = 0; ks_ < 2; ++ks_)                                   \
+            _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_)                                  \
+                _Pragma("unroll") for (int j_ = 0; j_ < 4; ++j_) acc[i_][j_] =                \
+                    __builtin_amdgcn_mfma_f32_32x32x16_bf16(FA[ks_][i_], FB[ks_][j_],         \
+                                                            acc[i_][j_], 0, 0, 0);            \
     } while (0)
-        // Pipeline: slices of BK along K, STAGES LDS buffers.  Step kt always refills, so
-        // exactly STAGES-2 slices issued after slice kt+1 can still be in flight when slice
-        // kt+1 is needed; refills past the last slice re-read the last slice (clamped) and are
-        // never consumed.
-#define MOE_SYNC(N)                                                                           \
-    do {                                                                                      \
-        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(N) : "memory");                  \
-        __builtin_amdgcn_s_barrier();                                                         \
-        asm volatile("" ::: "memory");                                                        \
-    } while (0)
-        // slice KT_: first half of its MFMAs; meet (slice KT_+1 landed everywhere, every wave
-        // done reading slice KT_); refill slice KT_'s buffer; read slice KT_+1's fragments
-        // into the other register set; second half of slice KT_'s MFMAs
-#define MOE_STEP(CA, CB, NA, NB, KT_)                                                         \
-    do {                                                                                      \
-        MOE_MFMA_KS(CA, CB, 0);                                                               \
-        MOE_SYNC((STAGES - 2) * LPW);                                                         \
-        issue(static_cast<int>((KT_) % STAGES),                                               \
-              (KT_) + STAGES < KT ? (KT_) + STAGES : KT - 1);                                 \
-        MOE_LOAD_FRAGS(NA, NB, static_cast<int>(((KT_) + 1) % STAGES));                       \
-        _Pragma("unroll") for (int ks2_ = 1; ks2_ < BK / 16; ++ks2_) MOE_MFMA_KS(CA, CB, ks2_); \
-    } while (0)
-
-        const int64_t KT = a.K / BK;  // even: K is a multiple of 2*BK
+        // Pipeline: K slices of BK in two LDS stages; slice kt lives in stage kt % 2 and is
+        // consumed in two halves, each half's fragments read while the previous half's MFMAs
+        // run.  The one barrier per slice (before its second half) proves both that slice
+        // kt+1 has landed and that every wave has finished reading stage kt % 2, which is
+        // then refilled with slice kt+2.  Every slice issues exactly one refill (past the
+        // last slice it re-reads the last one, never consumed), so the in-flight count at the
+        // barrier is always that one slice.
+        const int64_t KT = a.K / BK;
         // the previous tile's trailing DMAs and every wave's reads of the stage buffers are done
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
         __syncthreads();
-        // prologue: slices 0..STAGES-1 in flight, slice 0's fragments in registers
-#pragma unroll
-        for (int st = 0; st < STAGES; ++st) issue(st, st < KT ? st : KT - 1);
-        MOE_SYNC((STAGES - 1) * LPW);
-        bf16x8_t fa0[BK / 16][4], fb0[BK / 16][4], fa1[BK / 16][4], fb1[BK / 16][4];
-        MOE_LOAD_FRAGS(fa0, fb0, 0);
-        for (int64_t kt = 0; kt < KT; kt += 2) {
-            MOE_STEP(fa0, fb0, fa1, fb1, kt);
-            MOE_STEP(fa1, fb1, fa0, fb0, kt + 1);
+        issue(0, 0);
+        issue(1, KT > 1 ? 1 : 0);
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPW) : "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        bf16x8_t f0a[2][4], f0b[2][4], f1a[2][4], f1b[2][4];
+        MOE_LOAD_HALF(f0a, f0b, 0, 0);
+        // Within each half the scheduler interleaves one fragment read (and, in the second
+        // half, one DMA issue) with every two MFMAs, so LDS and DMA traffic spread over the
+        // half and few reads are outstanding when the next half starts.
+#define MOE_INTERLEAVE(WITH_DMA)                                                              \
+    do {                                                                                      \
+        _Pragma("unroll") for (int g_ = 0; g_ < 16; ++g_) {                                   \
+            if (WITH_DMA) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                  \
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                \
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                                \
+        }                                                                                     \
+    } while (0)
+        for (int64_t kt = 0; kt < KT; ++kt) {
+            const int buf = static_cast<int>(kt & 1);
+            __builtin_amdgcn_sched_barrier(0);
+            MOE_LOAD_HALF(f1a, f1b, buf, 1);
+            MOE_MFMA_HALF(f0a, f0b);
+            MOE_INTERLEAVE(false);
+            __builtin_amdgcn_sched_barrier(0);
+            // slice kt+1 landed and every wave is done reading stage `buf`
+            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            issue(buf, kt + 2 < KT ? kt + 2 : KT - 1);
+            MOE_LOAD_HALF(f0a, f0b, buf ^ 1, 0);
+            MOE_MFMA_HALF(f1a, f1b);
+            MOE_INTERLEAVE(true);
+            __builtin_amdgcn_sched_barrier(0);
         }
-#undef MOE_STEP
-#undef MOE_SYNC
-#undef MOE_MFMA_KS
-#undef MOE_LOAD_FRAGS
+#undef MOE_INTERLEAVE
+#undef MOE_MFMA_HALF
+#undef MOE_LOAD_HALF
 #undef MOE_BROW
 
         // ---- epilogue: lane holds rows 8*(v/4) + 4*(lane/32) + v%4 of column lane%32.
