@@ -23,20 +23,23 @@ namespace {
 // multiply-adds in ascending h inside each 128-wide chunk of h, starting from +0; the chunk
 // sums are added left to right to a running fp32 total starting from +0.
 //
-// On the matrix cores: v_mfma_f32_32x32x1_2b_f32 adds exactly one product to each of its
-// 2x32x32 accumulators per instruction with a single rounding, so a chain of them over a
-// chunk is the fmaf chain of the definition, bit for bit (checked against the VALU fma chain
-// on bf16-valued, full fp32 and subnormal operands).  A wave owns 64 rows x 128 experts as
-// four accumulator chains (A = its 64 rows; B = two 32-expert groups per chain, the wave's
-// halves swapped between chain pairs so the four chains cover all 2x4 row/expert blocks).
+// On the matrix cores: v_mfma_f32_32x32x2f32 adds two products to each 32x32 accumulator
+// per instruction as two fused multiply-adds in sequence (the lower half-wave's k first), each
+// with one rounding -- bit for bit the fmaf chain of the definition (checked against the
+// sequential fma chain, and shown to differ from a single-rounding pair, on bf16-valued and
+// full fp32 operands).  Lanes 0-31 therefore carry the even k of each pair and lanes 32-63
+// the odd k; LDS keeps every row's slice split by parity (evens, then odds) so that one
+// 16-byte read gives a lane its operands for four consecutive instructions.  A wave owns 64
+// rows x 128 experts as eight 32x32 chains (2 row blocks x 4 expert blocks).
 //   - large batches: a block of 128 rows x 256 experts (x read from HBM once) walks all of
 //     h in 32-wide slices, prefetching across chunk boundaries; after a chunk's last slice
 //     its sums are added to the running total and the chains restart from +0;
 //   - small batches: one block per (row tile, expert tile, chunk) writes the chunk's sums to
 //     a workspace and a reduction adds them left to right -- chunks run in parallel, so the
 //     latency is one chunk's chain, not the whole row's.
-// Operands are staged through LDS in the input type, row stride padded by 4 elements.
-typedef float floatx32_t __attribute__((ext_vector_type(32)));
+// Zero operands past H (ragged last chunk) change nothing: a chain started at +0 never holds
+// -0, so adding a +-0 product leaves every bit in place.
+typedef float floatx16_t __attribute__((ext_vector_type(16)));
 constexpr int GATE_CHUNK = 128;
 constexpr int GB_M = 128, GB_N = 256, GB_K = 32, G_THREADS = 256;
 constexpr int G_PAD = 4;
@@ -120,38 +123,36 @@ struct GateStage {
             wr[p] = load_piece(w, E, H, n0 + idx / PER_ROW, k0 + (idx % PER_ROW) * C);
         }
     }
-    // LDS holds fp32: bf16 widens here, once per element, so the matrix-core loop reads its
-    // operands straight from LDS
-    __device__ static void put(float* d, const uint4& v) {
-        float4 lo, hi;
+    // LDS holds fp32 (bf16 widens here, once per element) split by parity: slice column k
+    // of a row sits at k / 2 (even k) or GB_K / 2 + k / 2 (odd k).  `kk` is the piece's
+    // first column in the slice.
+    __device__ static void put(float* row, int kk, const uint4& v) {
         if constexpr (sizeof(T) == 2) {
-            lo = make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
-                             __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u));
-            hi = make_float4(__uint_as_float(v.z << 16), __uint_as_float(v.z & 0xffff0000u),
-                             __uint_as_float(v.w << 16), __uint_as_float(v.w & 0xffff0000u));
-            reinterpret_cast<float4*>(d)[0] = lo;
-            reinterpret_cast<float4*>(d)[1] = hi;
+            reinterpret_cast<float4*>(row + kk / 2)[0] =
+                make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.y << 16),
+                            __uint_as_float(v.z << 16), __uint_as_float(v.w << 16));
+            reinterpret_cast<float4*>(row + GB_K / 2 + kk / 2)[0] =
+                make_float4(__uint_as_float(v.x & 0xffff0000u), __uint_as_float(v.y & 0xffff0000u),
+                            __uint_as_float(v.z & 0xffff0000u), __uint_as_float(v.w & 0xffff0000u));
         } else {
-            reinterpret_cast<float4*>(d)[0] =
-                make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
+            reinterpret_cast<float2*>(row + kk / 2)[0] = make_float2(__uint_as_float(v.x), __uint_as_float(v.z));
+            reinterpret_cast<float2*>(row + GB_K / 2 + kk / 2)[0] =
+                make_float2(__uint_as_float(v.y), __uint_as_float(v.w));
         }
     }
     __device__ void store(float* xs, float* ws) {
 #pragma unroll
         for (int p = 0; p < XCH; ++p) {
             const int idx = threadIdx.x + p * G_THREADS;
-            put(xs + (idx / PER_ROW) * LD + (idx % PER_ROW) * C, xr[p]);
+            put(xs + (idx / PER_ROW) * LD, (idx % PER_ROW) * C, xr[p]);
         }
 #pragma unroll
         for (int p = 0; p < WCH; ++p) {
             const int idx = threadIdx.x + p * G_THREADS;
-            put(ws + (idx / PER_ROW) * LD + (idx % PER_ROW) * C, wr[p]);
+            put(ws + (idx / PER_ROW) * LD, (idx % PER_ROW) * C, wr[p]);
         }
     }
 };
-
-// chain c of a wave: expert group (c & 2) + ((c & 1) ^ half) of the wave's 128 experts
-__device__ __forceinline__ int chain_group(int c, int half) { return (c & 2) + ((c & 1) ^ half); }
 
 // Chunks [ch0, ch1) of h for the block's 128 x 256 tile (chunk c = slices 4c .. 4c+3, slice
 // s = columns 32s .. 32s+31).  Each chunk's chains start from +0 and see only matrix-core
@@ -161,17 +162,18 @@ __device__ __forceinline__ int chain_group(int c, int half) { return (c & 2) + (
 template <typename T, bool TOTAL>
 __device__ __forceinline__ void gate_chunks(const T* x, const T* w, int64_t G, int64_t E, int64_t H,
                                             int64_t m0, int64_t n0, int64_t ch0, int64_t ch1,
-                                            bool fast, float* xs, float* ws, floatx32_t (&acc)[4],
-                                            floatx32_t (&total)[4]) {
+                                            bool fast, float* xs, float* ws, floatx16_t (&acc)[8],
+                                            floatx16_t (&total)[8]) {
     typedef GateStage<T> S;
     typedef typename GateIO<float>::Quad Quad;
     constexpr int LD = S::LD;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int wm = wv >> 1, wn = wv & 1, half = lane >> 5;
-    const int arow = wm * 64 + lane;
-    int brow[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) brow[c] = wn * 128 + 32 * chain_group(c, half) + (lane & 31);
+    const int wm = wv >> 1, wn = wv & 1;
+    // lane's operand rows: x rows wm*64 + 32 rb + lane%32, w rows wn*128 + 32 cb + lane%32;
+    // its k parity (lane / 32) picks the even or odd half of the row
+    const int par = (lane >> 5) * (GB_K / 2);
+    const int arow = wm * 64 + (lane & 31);
+    const int brow = wn * 128 + (lane & 31);
     // descriptors over the block's own rows: byte offsets stay below 256 * H * sizeof(T)
     const int64_t xrows = G - m0 < GB_M ? G - m0 : GB_M;
     const int64_t wrows = E - n0 < GB_N ? E - n0 : GB_N;
@@ -204,33 +206,34 @@ __device__ __forceinline__ void gate_chunks(const T* x, const T* w, int64_t G, i
     __syncthreads();
     for (int64_t ch = ch0; ch < ch1; ++ch) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
+        for (int c = 0; c < 8; ++c)
 #pragma unroll
-            for (int v = 0; v < 32; ++v) acc[c][v] = 0.f;
+            for (int v = 0; v < 16; ++v) acc[c][v] = 0.f;
 #pragma unroll 1
         for (int q = 0; q < SLICES_PER_CHUNK; ++q) {
             const int64_t sl = ch * SLICES_PER_CHUNK + q;
             const int cur = static_cast<int>((sl - s_begin) & 1);
-            const float* xc = xs + cur * (GB_M * LD);
-            const float* wc = ws + cur * (GB_N * LD);
+            const float* xc = xs + cur * (GB_M * LD) + arow * LD + par;
+            const float* wc = ws + cur * (GB_N * LD) + brow * LD + par;
             const bool more = sl + 1 < s_end;
             if (more) load(sl + 1);
-            const float* xa = xc + arow * LD;
-            const float* wb[4];
 #pragma unroll
-            for (int c = 0; c < 4; ++c) wb[c] = wc + brow[c] * LD;
+            for (int kq = 0; kq < GB_K / 8; ++kq) {  // four k pairs per 16-byte read
+                float4 qa[2], qb[4];
 #pragma unroll
-            for (int kg = 0; kg < GB_K / 4; ++kg) {
-                const Quad qa = *reinterpret_cast<const Quad*>(xa + kg * 4);
-                Quad qb[4];
+                for (int rb = 0; rb < 2; ++rb) qa[rb] = *reinterpret_cast<const float4*>(xc + rb * 32 * LD + kq * 4);
 #pragma unroll
-                for (int c = 0; c < 4; ++c) qb[c] = *reinterpret_cast<const Quad*>(wb[c] + kg * 4);
+                for (int cb = 0; cb < 4; ++cb) qb[cb] = *reinterpret_cast<const float4*>(wc + cb * 32 * LD + kq * 4);
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
-                    const float av = GateIO<float>::val(qa, t);
 #pragma unroll
-                    for (int c = 0; c < 4; ++c)
-                        acc[c] = __builtin_amdgcn_mfma_f32_32x32x1f32(av, GateIO<float>::val(qb[c], t), acc[c], 0, 0, 0);
+                    for (int rb = 0; rb < 2; ++rb) {
+                        const float av = GateIO<float>::val(qa[rb], t);
+#pragma unroll
+                        for (int cb = 0; cb < 4; ++cb)
+                            acc[rb * 4 + cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+                                av, GateIO<float>::val(qb[cb], t), acc[rb * 4 + cb], 0, 0, 0);
+                    }
                 }
             }
             if (more) st.store(xs + (cur ^ 1) * (GB_M * LD), ws + (cur ^ 1) * (GB_N * LD));
@@ -238,19 +241,19 @@ __device__ __forceinline__ void gate_chunks(const T* x, const T* w, int64_t G, i
         }
         if (TOTAL) {
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
+            for (int c = 0; c < 8; ++c)
 #pragma unroll
-                for (int v = 0; v < 32; ++v) total[c][v] = total[c][v] + acc[c][v];
+                for (int v = 0; v < 16; ++v) total[c][v] = total[c][v] + acc[c][v];
         }
     }
 }
 
-// out[g, e] for the lane's accumulator element (chain c, block b, register v)
-__device__ __forceinline__ void chain_coords(int c, int b, int v, int lane, int64_t m0, int64_t n0,
-                                             int64_t& g, int64_t& e) {
-    const int wv = threadIdx.x >> 6, wm = wv >> 1, wn = wv & 1, half = lane >> 5;
-    e = n0 + wn * 128 + 32 * chain_group(c, b) + (lane & 31);
-    g = m0 + wm * 64 + 32 * b + 8 * (v >> 2) + 4 * half + (v & 3);
+// out[g, e] for the lane's accumulator element (chain c = 4 rb + cb, register v)
+__device__ __forceinline__ void chain_coords(int c, int v, int lane, int64_t m0, int64_t n0, int64_t& g,
+                                             int64_t& e) {
+    const int wv = threadIdx.x >> 6, wm = wv >> 1, wn = wv & 1;
+    e = n0 + wn * 128 + 32 * (c & 3) + (lane & 31);
+    g = m0 + wm * 64 + 32 * (c >> 2) + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
 }
 
 // large batches: all chunks in one block, running total in registers
@@ -266,26 +269,24 @@ __global__ __launch_bounds__(G_THREADS) void gate_exact_kernel(const T* __restri
     const int64_t m0 = static_cast<int64_t>(blockIdx.x) * GB_M;
     const int64_t n0 = static_cast<int64_t>(blockIdx.y) * GB_N;
     const int lane = threadIdx.x & 63;
-    floatx32_t acc[4], total[4];
+    floatx16_t acc[8], total[8];
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
+    for (int c = 0; c < 8; ++c)
 #pragma unroll
-        for (int v = 0; v < 32; ++v) total[c][v] = 0.f;
+        for (int v = 0; v < 16; ++v) total[c][v] = 0.f;
     // the last chunk may be ragged: its columns past H read zeros, which add +0 products
     gate_chunks<T, true>(x, w, G, E, H, m0, n0, 0, ceil_div(H, GATE_CHUNK), fast, xs, ws, acc, total);
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
+    for (int c = 0; c < 8; ++c)
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                int64_t g, e;
-                chain_coords(c, b, v, lane, m0, n0, g, e);
-                if (g < G && e < E) {
-                    const bool valid = row_valid == nullptr || row_valid[g] != 0;
-                    logits[g * E + e] = valid ? total[c][16 * b + v] : 0.f;
-                }
+        for (int v = 0; v < 16; ++v) {
+            int64_t g, e;
+            chain_coords(c, v, lane, m0, n0, g, e);
+            if (g < G && e < E) {
+                const bool valid = row_valid == nullptr || row_valid[g] != 0;
+                logits[g * E + e] = valid ? total[c][v] : 0.f;
             }
+        }
 }
 
 // small batches: blockIdx.z = chunk; writes the chunk's sums to parts[chunk][G][E]
@@ -301,19 +302,17 @@ __global__ __launch_bounds__(G_THREADS) void gate_chunk_kernel(const T* __restri
     const int64_t n0 = static_cast<int64_t>(blockIdx.y) * GB_N;
     const int64_t ch = blockIdx.z;
     const int lane = threadIdx.x & 63;
-    floatx32_t acc[4], unused[4];
+    floatx16_t acc[8], unused[8];
     gate_chunks<T, false>(x, w, G, E, H, m0, n0, ch, ch + 1, fast, xs, ws, acc, unused);
     float* out = parts + ch * G * E;
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
+    for (int c = 0; c < 8; ++c)
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                int64_t g, e;
-                chain_coords(c, b, v, lane, m0, n0, g, e);
-                if (g < G && e < E) out[g * E + e] = acc[c][16 * b + v];
-            }
+        for (int v = 0; v < 16; ++v) {
+            int64_t g, e;
+            chain_coords(c, v, lane, m0, n0, g, e);
+            if (g < G && e < E) out[g * E + e] = acc[c][v];
+        }
 }
 
 // logits = ((+0 + part_0) + part_1) + ... in chunk order

@@ -201,10 +201,11 @@ def test_gate_kernels_bitwise(dt):
     import combine_dp_gather_amd as m
     rng = np.random.default_rng(21)
     cfg = m.make_route_cfg("softmax", 200, 4)
-    for G, H in ((300, 1000), (128 * 128 + 37, 232)):
-        say(f"[gate] dtype={dt} G={G} H={H} E=200")
-        x = torch.from_numpy(rng.standard_normal((G, H)).astype(np.float32)).to(dt)
-        w = torch.from_numpy((rng.standard_normal((200, H)) * 0.05).astype(np.float32)).to(dt)
+    # third case: magnitudes whose products and partial sums are subnormal fp32
+    for G, H, scale in ((300, 1000, 1.0), (128 * 128 + 37, 232, 1.0), (300, 384, 2.0 ** -66)):
+        say(f"[gate] dtype={dt} G={G} H={H} E=200 scale={scale}")
+        x = torch.from_numpy((rng.standard_normal((G, H)) * scale).astype(np.float32)).to(dt)
+        w = torch.from_numpy((rng.standard_normal((200, H)) * 0.05 * scale).astype(np.float32)).to(dt)
         rv = np.ones(G, dtype=np.int32)
         rv[::17] = 0
         xb = x.view(torch.int16).numpy().view(np.uint16) if dt == torch.bfloat16 else x.numpy()
@@ -213,6 +214,8 @@ def test_gate_kernels_bitwise(dt):
         xd, wd, rvd = x.cuda(), w.cuda(), torch.from_numpy(rv).cuda()
         ws_bytes = m.moe_route_workspace_size(G, 200, H)
         assert (ws_bytes > 0) == (G < 1000)
+        if scale < 1:
+            assert np.any((ref != 0) & (np.abs(ref) < np.finfo(np.float32).tiny))
         for ws in ([None, torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")] if ws_bytes else [None]):
             lg = torch.full((G, 200), float("nan"), device="cuda")
             ids = torch.empty((G, 4), dtype=torch.int32, device="cuda")
