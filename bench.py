@@ -76,6 +76,57 @@ def cpu_baseline(inp, sample_per_replica: int):
                       f"steps, oracle wall time {dt:.2f} s"}
 
 
+def _time_ms(fn, iters=10):
+    import torch
+    for _ in range(2):
+        fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(iters):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / iters
+
+
+def ceilings(cfg, R: int) -> dict:
+    """Practical ceilings on this GPU, for context next to the spec peaks: a plain device
+    copy, and the vendor library GEMM over the same per-slot shapes as the grouped GEMMs."""
+    import torch
+    out = {}
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    ms = _time_ms(lambda: dst.copy_(src))
+    out["device_copy_GBps"] = round(2 * n / ms / 1e6, 1)
+    del src, dst
+    if cfg.dtype == "bf16":
+        H, I, El = cfg.hidden, cfg.inter, cfg.num_local
+        rows = max(R // El, 1)
+        bf = torch.bfloat16
+        x = torch.randn(El, rows, H, device="cuda", dtype=bf)
+        w13 = torch.randn(El, 2 * I, H, device="cuda", dtype=bf)
+        w2 = torch.randn(El, H, I, device="cuda", dtype=bf)
+        h = torch.randn(El, rows, I, device="cuda", dtype=bf)
+        o1 = torch.empty(El, rows, 2 * I, device="cuda", dtype=bf)
+        o2 = torch.empty(El, rows, H, device="cuda", dtype=bf)
+
+        def up():
+            for e in range(El):
+                torch.matmul(x[e], w13[e].t(), out=o1[e])
+
+        def down():
+            for e in range(El):
+                torch.matmul(h[e], w2[e].t(), out=o2[e])
+        for name, fn, fl in (("gemm_up", up, 4.0 * El * rows * H * I), ("gemm_down", down, 2.0 * El * rows * H * I)):
+            ms = _time_ms(fn)
+            out[f"vendor_{name}_ms"] = round(ms, 4)
+            out[f"vendor_{name}_TFLOPs"] = round(fl / ms / 1e9, 1)
+        out["vendor_gemm_shape"] = f"{El} slots x {rows} rows, H={H}, I={I}, bf16 (torch.matmul per slot)"
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -83,8 +134,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="cfg4")
     ap.add_argument("--mode", default="sum", choices=["sum", "max", "auto"])
-    ap.add_argument("--cpu-sample", type=int, default=2048, help="tokens per replica for the oracle")
+    ap.add_argument("--cpu-sample", type=int, default=4096, help="tokens per replica for the oracle")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="also measure practical ceilings: a plain 1 GiB device copy and the vendor "
+                         "GEMM (torch.matmul) on the same per-expert shapes")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run a plain device copy of MIB MiB (reference for HBM counters)")
     args = ap.parse_args()
@@ -165,13 +219,21 @@ def main():
     E_slots = cfg.num_local
     es = 2 if bf else 4
     mm = "mfma8" if cfg.weight_format == "fp8_block" else "mfma"
+    wb = 1 if mm == "mfma8" else es   # weight bytes per element
+
+    def gemm_work(kind, flops, bytes_):
+        # below the ridge point (peak flop/s over HBM bytes/s) the GEMM streams its weights
+        # and HBM bounds it: report bytes against HBM; above it, flops against the MFMA peak
+        ridge = (FP8_MFMA_PEAK_TFLOPS if kind == "mfma8" else BF16_MFMA_PEAK_TFLOPS) * 1e12 / (HBM_PEAK_GBS * 1e9)
+        return (kind, flops) if flops / bytes_ >= ridge else ("hbm", bytes_)
     # algorithmic work per call (bytes or flops), per-unit figures x units
     work = {
         "gather": ("hbm", (T + G) * H * es + 4 * G),                   # read T rows, write G rows
         "route": ("mfma32", 2.0 * G * E * H),                          # exact fp32 fma chain + select
         "dispatch": ("hbm", 2 * R * H * es + 3 * 4 * G * k + 8 * R),  # x_perm copy + id passes
-        "gemm_up": (mm, 4.0 * R * H * I),                              # gate+up: 2*R*H*2I
-        "gemm_down": (mm, 2.0 * R * I * H),
+        "gemm_up": gemm_work(mm, 4.0 * R * H * I,                     # gate+up: 2*R*H*2I
+                             E_slots * 2 * I * H * wb + R * H * es + R * I * es),
+        "gemm_down": gemm_work(mm, 2.0 * R * I * H, E_slots * H * I * wb + R * I * es + R * H * es),
         "combine": ("hbm", R * H * es + G * H * es + 8 * G * k),      # read R rows, write G rows
         "scatter": ("hbm", 2 * T * H * es),
     }
@@ -199,8 +261,7 @@ def main():
     roof["kernel"] = kname + (" (gate+up SwiGLU" + (", with its activation quantisation" if fmt == "fp8" else "")
                               + ")")
     from combine_dp_gather_amd.profiling import read_traffic_summary
-    summary = os.path.join(ROOT, "profiles",
-                           f"{kname.replace('<true>', '_up')}__{PROFILE_WORKLOAD[args.workload]}__traffic.txt")
+    summary = os.path.join(ROOT, "profiles", f"grouped_gemm_{fmt}_up__{PROFILE_WORKLOAD[args.workload]}__traffic.txt")
     tb = read_traffic_summary(summary, GEMM_SOURCES[fmt])
     roof["traffic"] = round(tb) if tb is not None else None
     roof["algorithmic_bytes"] = R * H * es + E_slots * 2 * I * H * (1 if fmt == "fp8" else es) + R * I * es
@@ -224,6 +285,8 @@ def main():
         "kernels": kernels,
         "wall_s_timed": round(wall, 3),
     }
+    if args.ceilings:
+        result["ceilings"] = ceilings(cfg, R)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(inp, args.cpu_sample)
