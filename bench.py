@@ -252,6 +252,18 @@ def main():
         kernels[n] = {"ms": round(per[n], 4), "bound": "mfma" if bound.startswith("mfma") else bound,
                       "peak_kind": bound, "achieved": round(ach, 2), "peak": peaks[bound], "unit": unit,
                       "frac": round(ach / peaks[bound], 4)}
+    if bf:
+        # the FAST gate (bf16 matrix cores, near-tie tolerant ids) timed on its own; the step
+        # above routes with the exact gate
+        import combine_dp_gather_amd as m
+        rc = m.make_route_cfg(cfg.route, E, k, cfg.n_group, cfg.topk_group, cfg.group_topn, cfg.renormalize,
+                              gate="fast")
+        ms = _time_ms(lambda: m.moe_route(layer.global_x, layer.row_valid, w.router, w.bias, rc, layer.logits,
+                                          layer.topk_ids, layer.topk_w), iters=10)
+        fb = G * H * 2 + E * H * 2 + G * E * 4 + G * k * 8
+        kernels["route_fast"] = {"ms": round(ms, 4), "bound": "hbm", "achieved": round(fb / (ms / 1e3) / 1e9, 2),
+                                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(fb / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                                 "note": "FAST gate + select, timed apart from the step (which uses the exact gate)"}
     dom = "gemm_up"
     roof = dict(kernels[dom])
     roof.pop("ms")

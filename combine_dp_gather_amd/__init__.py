@@ -111,9 +111,10 @@ def moe_scatter(L: GatherLayout, out: torch.Tensor, replicas_out: Sequence[torch
 # ------------------------------------------------------------------ routing
 
 def make_route_cfg(kind: str, num_experts: int, top_k: int, n_group: int = 1, topk_group: int = 1,
-                   group_topn: int = 2, renormalize: bool = False) -> RouteCfg:
+                   group_topn: int = 2, renormalize: bool = False, gate: str = "exact") -> RouteCfg:
     k = MOE_ROUTE_SOFTMAX if kind == "softmax" else MOE_ROUTE_GROUPED_SIGMOID
-    return RouteCfg(k, num_experts, top_k, n_group, topk_group, group_topn, int(renormalize))
+    mode = {"exact": _lib.MOE_GATE_EXACT, "fast": _lib.MOE_GATE_FAST}[gate]
+    return RouteCfg(k, num_experts, top_k, n_group, topk_group, group_topn, int(renormalize), mode)
 
 
 def moe_route_workspace_size(G: int, num_experts: int, H: int) -> int:

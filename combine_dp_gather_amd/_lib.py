@@ -10,6 +10,7 @@ LIB_PATH = os.path.join(HERE, "libmoe_hip.so")
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_CAPACITY, MOE_ERR_HIP = range(5)
 MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
 MOE_PAD_AUTO, MOE_PAD_MAX_LEN, MOE_PAD_SUM_LEN = 0, 1, 2
+MOE_GATE_EXACT, MOE_GATE_FAST = 0, 1
 MOE_ROUTE_SOFTMAX, MOE_ROUTE_GROUPED_SIGMOID = 0, 1
 MOE_MAX_REPLICAS = 256
 
@@ -23,7 +24,8 @@ class GatherLayout(ctypes.Structure):
 
 class RouteCfg(ctypes.Structure):
     _fields_ = [("kind", c_i32), ("num_experts", c_i32), ("top_k", c_i32), ("n_group", c_i32),
-                ("topk_group", c_i32), ("group_topn", c_i32), ("renormalize", c_i32)]
+                ("topk_group", c_i32), ("group_topn", c_i32), ("renormalize", c_i32),
+                ("gate_mode", c_i32)]
 
 
 class ExpertMap(ctypes.Structure):

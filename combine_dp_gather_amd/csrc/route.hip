@@ -330,6 +330,130 @@ __global__ __launch_bounds__(256) void gate_reduce_kernel(const float* __restric
     }
 }
 
+// ------------------------------------------------------------------ fast gate
+// FAST mode: logits on the bf16 matrix cores (v_mfma_f32_32x32x16_bf16, fp32 accumulate).
+// Products of bf16 values are exact in fp32, so only the summation order differs from the
+// exact gate.  A block computes 128 rows x 256 experts (x read from HBM once), 4 waves of
+// 64 x 128 (eight 32x32 accumulators each), 64-deep K slices staged through LDS as bf16
+// with rows padded to 144 bytes (16 consecutive rows of a 16-byte fragment read land on
+// distinct bank groups); the next slice is loaded into registers while this one computes.
+typedef __bf16 gate_bf16x8_t __attribute__((ext_vector_type(8)));
+constexpr int FB_M = 128, FB_N = 256, FB_K = 64, FB_LD = FB_K + 8;
+
+struct FastStage {
+    static constexpr int PER_ROW = FB_K / 8;                 // 16-byte pieces per row
+    static constexpr int XCH = FB_M * PER_ROW / G_THREADS;   // 4
+    static constexpr int WCH = FB_N * PER_ROW / G_THREADS;   // 8
+    uint4 xr[XCH], wr[WCH];
+    __device__ void load(const uint16_t* x, const uint16_t* w, __amdgpu_buffer_rsrc_t rx,
+                         __amdgpu_buffer_rsrc_t rw, bool fast, int64_t G, int64_t E, int64_t H,
+                         int64_t m0, int64_t n0, int64_t k0) {
+        if (fast && k0 + FB_K <= H) {
+            const int so = static_cast<int>(k0 * 2);
+#pragma unroll
+            for (int p = 0; p < XCH; ++p) {
+                const int idx = threadIdx.x + p * G_THREADS;
+                const uint32_t off = static_cast<uint32_t>(((idx / PER_ROW) * H + (idx % PER_ROW) * 8) * 2);
+                const gate_u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rx, static_cast<int>(off), so, 0);
+                xr[p] = make_uint4(v.x, v.y, v.z, v.w);
+            }
+#pragma unroll
+            for (int p = 0; p < WCH; ++p) {
+                const int idx = threadIdx.x + p * G_THREADS;
+                const uint32_t off = static_cast<uint32_t>(((idx / PER_ROW) * H + (idx % PER_ROW) * 8) * 2);
+                const gate_u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rw, static_cast<int>(off), so, 0);
+                wr[p] = make_uint4(v.x, v.y, v.z, v.w);
+            }
+        } else {
+#pragma unroll
+            for (int p = 0; p < XCH; ++p) {
+                const int idx = threadIdx.x + p * G_THREADS;
+                xr[p] = load_piece(x, G, H, m0 + idx / PER_ROW, k0 + (idx % PER_ROW) * 8);
+            }
+#pragma unroll
+            for (int p = 0; p < WCH; ++p) {
+                const int idx = threadIdx.x + p * G_THREADS;
+                wr[p] = load_piece(w, E, H, n0 + idx / PER_ROW, k0 + (idx % PER_ROW) * 8);
+            }
+        }
+    }
+    __device__ void store(uint16_t* xs, uint16_t* ws) {
+#pragma unroll
+        for (int p = 0; p < XCH; ++p) {
+            const int idx = threadIdx.x + p * G_THREADS;
+            *reinterpret_cast<uint4*>(xs + (idx / PER_ROW) * FB_LD + (idx % PER_ROW) * 8) = xr[p];
+        }
+#pragma unroll
+        for (int p = 0; p < WCH; ++p) {
+            const int idx = threadIdx.x + p * G_THREADS;
+            *reinterpret_cast<uint4*>(ws + (idx / PER_ROW) * FB_LD + (idx % PER_ROW) * 8) = wr[p];
+        }
+    }
+};
+
+__global__ __launch_bounds__(G_THREADS) void gate_fast_kernel(const uint16_t* __restrict__ x,
+                                                              const uint16_t* __restrict__ w,
+                                                              const int32_t* __restrict__ row_valid,
+                                                              int64_t G, int64_t E, int64_t H, bool fast,
+                                                              float* __restrict__ logits) {
+    __shared__ __attribute__((aligned(16))) uint16_t xs[2][FB_M * FB_LD];
+    __shared__ __attribute__((aligned(16))) uint16_t ws[2][FB_N * FB_LD];
+    const int64_t m0 = static_cast<int64_t>(blockIdx.x) * FB_M;
+    const int64_t n0 = static_cast<int64_t>(blockIdx.y) * FB_N;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int wm = wv >> 1, wn = wv & 1;
+    const int64_t xrows = G - m0 < FB_M ? G - m0 : FB_M;
+    const int64_t wrows = E - n0 < FB_N ? E - n0 : FB_N;
+    const __amdgpu_buffer_rsrc_t rx = gemm::make_rsrc_uniform(x + m0 * H, static_cast<uint32_t>(xrows * H * 2));
+    const __amdgpu_buffer_rsrc_t rw = gemm::make_rsrc_uniform(w + n0 * H, static_cast<uint32_t>(wrows * H * 2));
+    floatx16_t acc[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[c][v] = 0.f;
+    // fragment reads: row lane%32 of each 32-row block, k 8*(lane/32) .. +8 of each 16-deep step
+    const int arow = wm * 64 + (lane & 31), brow = wn * 128 + (lane & 31);
+    const int kof = (lane >> 5) * 8;
+    const int64_t KT = ceil_div(H, FB_K);
+    FastStage st;
+    st.load(x, w, rx, rw, fast, G, E, H, m0, n0, 0);
+    st.store(xs[0], ws[0]);
+    __syncthreads();
+    for (int64_t kt = 0; kt < KT; ++kt) {
+        const int cur = static_cast<int>(kt & 1);
+        const bool more = kt + 1 < KT;
+        if (more) st.load(x, w, rx, rw, fast, G, E, H, m0, n0, (kt + 1) * FB_K);
+        const uint16_t* xa = xs[cur] + arow * FB_LD + kof;
+        const uint16_t* wb = ws[cur] + brow * FB_LD + kof;
+#pragma unroll
+        for (int ks = 0; ks < FB_K / 16; ++ks) {
+            gate_bf16x8_t fa[2], fb[4];
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) fa[rb] = *reinterpret_cast<const gate_bf16x8_t*>(xa + rb * 32 * FB_LD + ks * 16);
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) fb[cb] = *reinterpret_cast<const gate_bf16x8_t*>(wb + cb * 32 * FB_LD + ks * 16);
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                for (int cb = 0; cb < 4; ++cb)
+                    acc[rb * 4 + cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[rb], fb[cb], acc[rb * 4 + cb], 0, 0, 0);
+        }
+        if (more) st.store(xs[cur ^ 1], ws[cur ^ 1]);
+        __syncthreads();
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            int64_t g, e;
+            chain_coords(c, v, lane, m0, n0, g, e);
+            if (g < G && e < E) {
+                const bool valid = row_valid == nullptr || row_valid[g] != 0;
+                logits[g * E + e] = valid ? acc[c][v] : 0.f;
+            }
+        }
+}
+
 int gate_num_cus() {
     static int cus[64] = {0};
     int dev = 0;
@@ -590,6 +714,7 @@ __global__ __launch_bounds__(S_THREADS) void select_kernel(SelectArgs a) {
 moe_status check_route_cfg(const moe_route_cfg* c) {
     MOE_CHECK_ARG(c);
     MOE_CHECK_ARG(c->kind == MOE_ROUTE_SOFTMAX || c->kind == MOE_ROUTE_GROUPED_SIGMOID);
+    MOE_CHECK_ARG(c->gate_mode == MOE_GATE_EXACT || c->gate_mode == MOE_GATE_FAST);
     MOE_CHECK_ARG(c->num_experts >= 1 && c->num_experts <= kMaxE);
     MOE_CHECK_ARG(c->top_k >= 1 && c->top_k <= kMaxTopK && c->top_k <= c->num_experts);
     if (c->kind == MOE_ROUTE_GROUPED_SIGMOID) {
@@ -678,6 +803,18 @@ extern "C" moe_status moe_route(const void* global_x, const int32_t* row_valid, 
     MOE_CHECK_ARG(global_x && w_router && logits && topk_ids && topk_w);
     MOE_CHECK_ARG(G <= (int64_t)1 << 31);
     const int64_t E = cfg->num_experts;
+    if (cfg->gate_mode == MOE_GATE_FAST) {
+        if (dt != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+        const bool fast = moe::aligned(global_x, 16) && moe::aligned(w_router, 16) && (H * 2) % 16 == 0 &&
+                          static_cast<int64_t>(moe::FB_N) * H * 2 < ((int64_t)1 << 31);
+        const dim3 grid(static_cast<unsigned>(moe::ceil_div(G, moe::FB_M)),
+                        static_cast<unsigned>(moe::ceil_div(E, moe::FB_N)));
+        hipLaunchKernelGGL(moe::gate_fast_kernel, grid, dim3(moe::G_THREADS), 0, stream,
+                           static_cast<const uint16_t*>(global_x), static_cast<const uint16_t*>(w_router),
+                           row_valid, G, E, H, fast, logits);
+        MOE_LAUNCH_CHECK();
+        return moe::launch_select(logits, row_valid, G, bias, cfg, topk_ids, topk_w, stream);
+    }
     const size_t split = moe::gate_split_bytes(G, E, H);
     const bool use_split = split > 0 && workspace != nullptr && workspace_bytes >= split &&
                            moe::aligned(workspace, 16);

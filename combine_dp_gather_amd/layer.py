@@ -45,6 +45,7 @@ class LayerSpec:
     group_topn: int = 2
     renormalize: bool = False
     routed_scale: float = 1.0
+    gate: str = "exact"         # "exact" (defined summation order) | "fast" (bf16 matrix cores)
 
 
 class DeviceWeights:
@@ -96,7 +97,7 @@ class MoELayer:
         self.global_x = torch.empty((G, H), dtype=act_dtype, device=device)
         self.row_valid = torch.empty(max(G, 1), dtype=torch.int32, device=device)
         self.route_cfg = make_route_cfg(spec.route, spec.num_experts, k, spec.n_group,
-                                        spec.topk_group, spec.group_topn, spec.renormalize)
+                                        spec.topk_group, spec.group_topn, spec.renormalize, spec.gate)
         self.logits = torch.empty((max(G, 1), spec.num_experts), dtype=torch.float32, device=device)
         self.topk_ids = torch.empty((max(G, 1), k), dtype=torch.int32, device=device)
         self.topk_w = torch.empty((max(G, 1), k), dtype=torch.float32, device=device)

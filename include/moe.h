@@ -118,6 +118,13 @@ moe_status moe_scatter(const moe_gather_layout_t* L, const void* out, int64_t H,
  * ---------------------------------------------------------------------------------------- */
 typedef enum { MOE_ROUTE_SOFTMAX = 0, MOE_ROUTE_GROUPED_SIGMOID = 1 } moe_route_kind;
 
+/* Gate arithmetic.  EXACT: the defined summation order below, so logits and ids are the same
+ * bits on every run, every rank and the reference.  FAST: bf16 matrix-core products with fp32
+ * accumulation in tile order -- the same products, summed in another order, so logits differ
+ * in the last bits and an id can differ only where two keys are that close (a near tie).
+ * FAST reads x once from HBM and takes bf16 inputs only. */
+typedef enum { MOE_GATE_EXACT = 0, MOE_GATE_FAST = 1 } moe_gate_mode;
+
 typedef struct {
     int32_t kind;          /* moe_route_kind */
     int32_t num_experts;   /* E (logical), 1..1024 */
@@ -126,6 +133,7 @@ typedef struct {
     int32_t topk_group;    /* grouped: groups kept, 1..n_group; k <= topk_group*E/n_group */
     int32_t group_topn;    /* grouped: keys summed per group score, 1..E/n_group (DeepSeek-V3: 2) */
     int32_t renormalize;   /* weights divided by their sum over the k picks */
+    int32_t gate_mode;     /* moe_gate_mode (moe_route only; ignored by moe_route_from_logits) */
 } moe_route_cfg;
 
 /* moe_route_workspace_size -- bytes of device workspace moe_route can use for G rows, E
@@ -139,11 +147,13 @@ size_t moe_route_workspace_size(int64_t G, int32_t num_experts, int64_t H);
  *   global_x   device [G, H] dt (MOE_F32 or MOE_BF16); row_valid device int32[G] or NULL
  *   w_router   device [E, H] dt
  *   bias       device fp32[E] or NULL (grouped only: selection bias, never in the weights)
- *   logits     device fp32[G, E], written.  The pages fix no summation order for the gate's
- *              matrix product; this library defines one so that the integer routing is
+ *   logits     device fp32[G, E], written.  EXACT mode (cfg->gate_mode): the pages fix no
+ *              summation order for the gate's matrix product; this library defines one so
+ *              that the integer routing is
  *              reproducible: for each 128-wide chunk c of h, part_c = fmaf chain over the
  *              chunk's h in ascending order from +0; logits[g,e] = ((+0 + part_0) + part_1)
- *              + ... in fp32, chunks left to right.  0 for pad rows.
+ *              + ... in fp32, chunks left to right.  FAST mode: bf16 MFMA products, fp32
+ *              sums in tile order (MOE_ERR_UNSUPPORTED for MOE_F32 inputs).  0 for pad rows.
  *   topk_ids   device int32[G, k]: expert ids, slots in descending key order, ties to the
  *              lower id; -1 for pad rows
  *   topk_w     device fp32[G, k]: weights; 0 for pad rows

@@ -100,6 +100,14 @@ def test_argument_errors_return_before_any_launch(m):
     for c in bad:
         assert lib.moe_route_from_logits(1, None, 4, None, ctypes.byref(c), 1, 1, None) == \
             _lib.MOE_ERR_INVALID_ARG
+    badmode = m.make_route_cfg("grouped", 256, 8, 8, 4, 2, True)
+    badmode.gate_mode = 2
+    assert lib.moe_route_from_logits(1, None, 4, None, ctypes.byref(badmode), 1, 1, None) == \
+        _lib.MOE_ERR_INVALID_ARG
+    # the fast gate takes bf16 inputs only; rejected before any launch
+    fast = m.make_route_cfg("grouped", 256, 8, 8, 4, 2, True, gate="fast")
+    assert lib.moe_route(1, None, 4, 256, _lib.MOE_F32, 1, None, ctypes.byref(fast), 1, 1, 1, None, 0,
+                         None) == _lib.MOE_ERR_UNSUPPORTED
     good = m.make_route_cfg("grouped", 256, 8, 8, 4, 2, True)
     assert lib.moe_route_from_logits(1, None, 0, None, ctypes.byref(good), None, None, None) == _lib.MOE_OK
     # dispatch: plan / map mismatch, workspace too small
