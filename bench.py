@@ -136,6 +136,9 @@ def main():
     ap.add_argument("--mode", default="sum", choices=["sum", "max", "auto"])
     ap.add_argument("--cpu-sample", type=int, default=4096, help="tokens per replica for the oracle")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fp8-act", default="bf16", choices=["bf16", "e4m3"],
+                    help="fp8-weight workloads: keep activations bf16 (weights dequantised in the "
+                         "kernel) or quantise them per 1x128 group for the fp8 matrix cores")
     ap.add_argument("--ceilings", action="store_true",
                     help="also measure practical ceilings: a plain 1 GiB device copy and the vendor "
                          "GEMM (torch.matmul) on the same per-expert shapes")
@@ -168,7 +171,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     act = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
-    w = DeviceWeights(inp, dev)
+    w = DeviceWeights(inp, dev, fp8_act=args.fp8_act)
     layer = MoELayer(spec_of(cfg), w, cfg.num_tokens, act, mode=args.mode,
                      static_bound=cfg.static_bound, device=dev)
     bf = cfg.dtype == "bf16"
@@ -218,8 +221,10 @@ def main():
     H, I, E, k, G = cfg.hidden, cfg.inter, cfg.num_experts, cfg.top_k, layer.G
     E_slots = cfg.num_local
     es = 2 if bf else 4
-    mm = "mfma8" if cfg.weight_format == "fp8_block" else "mfma"
-    wb = 1 if mm == "mfma8" else es   # weight bytes per element
+    fp8w = cfg.weight_format == "fp8_block"
+    # the arithmetic type of the matrix cores: fp8 only when the activations are quantised too
+    mm = "mfma8" if fp8w and args.fp8_act == "e4m3" else "mfma"
+    wb = 1 if fp8w else es   # weight bytes per element
 
     def gemm_work(kind, flops, bytes_):
         # below the ridge point (peak flop/s over HBM bytes/s) the GEMM streams its weights
@@ -269,7 +274,7 @@ def main():
     roof.pop("ms")
     roof.pop("peak_kind")
     fmt = "fp8" if mm == "mfma8" else "bf16"
-    kname = f"grouped_gemm_{fmt}_kernel<true>"
+    kname = f"grouped_gemm_{fmt}_kernel<true>" if not fp8w or fmt == "fp8" else "grouped_gemm_bf16_kernel<true, true>"
     roof["kernel"] = kname + (" (gate+up SwiGLU" + (", with its activation quantisation" if fmt == "fp8" else "")
                               + ")")
     from combine_dp_gather_amd.profiling import read_traffic_summary
@@ -288,7 +293,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": ("bf16 activations, fp8 e4m3 weights" if mm == "mfma8" else "bf16") if bf else "f32",
+        "dtype": (("bf16 activations, fp8 e4m3 weights (fp8 matrix cores)" if mm == "mfma8" else
+                   "bf16 activations, fp8 e4m3 weights dequantised to bf16 in the kernel") if fp8w else "bf16")
+                 if bf else "f32",
         "data": "synthetic (seeded PCG64; random-init DeepSeek-V3-shaped expert weights)",
         "config": {"workload": WORKLOAD_TEXT[args.workload], "name": cfg.name,
                    "tokens": T, "global_rows": G, "gather_mode": args.mode,

@@ -190,8 +190,11 @@ def moe_dispatch(global_x: torch.Tensor, topk_ids: torch.Tensor, emap: ExpertMap
 # ------------------------------------------------------------------ experts
 
 def make_expert_weights(w13: torch.Tensor, w2: torch.Tensor, s13: Optional[torch.Tensor] = None,
-                        s2: Optional[torch.Tensor] = None) -> ExpertWeights:
-    w = ExpertWeights(_dtype_code(w13), 0, _ptr(w13), _ptr(w2), _ptr(s13), _ptr(s2))
+                        s2: Optional[torch.Tensor] = None, fp8_act: str = "bf16") -> ExpertWeights:
+    """fp8_act (e4m3 weights only): "bf16" keeps activations bf16 and dequantises weight
+    fragments in the kernel; "e4m3" quantises activations per 1x128 group for fp8 MFMA."""
+    mode = {"bf16": _lib.MOE_FP8_ACT_BF16, "e4m3": _lib.MOE_FP8_ACT_E4M3}[fp8_act]
+    w = ExpertWeights(_dtype_code(w13), mode, _ptr(w13), _ptr(w2), _ptr(s13), _ptr(s2))
     w._keep = (w13, w2, s13, s2)
     return w
 

@@ -11,6 +11,7 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_CAPACITY, MOE_ERR_HIP 
 MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
 MOE_PAD_AUTO, MOE_PAD_MAX_LEN, MOE_PAD_SUM_LEN = 0, 1, 2
 MOE_GATE_EXACT, MOE_GATE_FAST = 0, 1
+MOE_FP8_ACT_BF16, MOE_FP8_ACT_E4M3 = 0, 1
 MOE_ROUTE_SOFTMAX, MOE_ROUTE_GROUPED_SIGMOID = 0, 1
 MOE_MAX_REPLICAS = 256
 
@@ -40,7 +41,7 @@ class Plan(ctypes.Structure):
 
 
 class ExpertWeights(ctypes.Structure):
-    _fields_ = [("dtype", c_i32), ("reserved", c_i32), ("w13", c_vp), ("w2", c_vp), ("s13", c_vp),
+    _fields_ = [("dtype", c_i32), ("fp8_act", c_i32), ("w13", c_vp), ("w2", c_vp), ("s13", c_vp),
                 ("s2", c_vp)]
 
 

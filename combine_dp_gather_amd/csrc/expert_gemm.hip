@@ -20,7 +20,14 @@
 //     half's MFMAs; the reads and refill DMAs are spread between the MFMAs;
 //   - persistent grid (one block per CU), XCD-grouped tile order (gemm_common.h); rows past
 //     a segment's end read as zeros and are never stored; each output tile has one owner.
-// The fp8 path (block-scaled weights) lives in expert_gemm_fp8.hip.
+//
+// fp8 weights with bf16 activations (the default way for e4m3 weights) run in the same
+// kernel: weight rows are staged as fp8 (half the bytes), a lane reads one 16-byte chunk per
+// weight block and half slice and dequantises it (exact e4m3 -> fp32, times the block's
+// fp32 scale, RNE to bf16) into the fragments of two MFMA steps; the activation fragments
+// use the matching K assignment.  The tile's block scales are staged in LDS per tile.
+// fp8 weights with per-1x128-group e4m3 activations (fp8 matrix cores, fp32 promotion per K
+// group) live in expert_gemm_fp8.hip.
 #include <hip/hip_runtime.h>
 
 #include "gemm_common.h"
@@ -52,10 +59,13 @@ constexpr int BK = 64;      // K slice per pipeline stage: whole 128-byte lines 
 constexpr int STAGES = 2;   // LDS stages (2 x 64 KB)
 constexpr int M_THREADS = gemm::kThreads;
 constexpr int UP_COLS = BN / 2;     // i-columns per up tile (gate and up each)
+constexpr int kMaxKG8 = 128;        // fp8 weights: at most 128 K groups (K <= 16384)
 
 struct GemmArgs {
     const uint16_t* A;       // [cap, K] bf16 rows in segment order
-    const uint16_t* B;       // up: w13 [E_l, 2, I, H]; down: w2 [E_l, H, I]
+    const uint16_t* B;       // up: w13 [E_l, 2, I, H]; down: w2 [E_l, H, I] (bf16 weights)
+    const uint8_t* B8;       // the same layouts in e4m3 (fp8 weights, dequantised in the kernel)
+    const float* SB;         // fp8: 128x128 block scales, up [E_l, 2, I/128, H/128], down [E_l, H/128, I/128]
     uint16_t* C;             // up: h [cap, I]; down: y [cap, H]
     const int32_t* counts;   // [E_l]
     const int64_t* seg;      // [E_l + 1]
@@ -67,6 +77,17 @@ struct GemmArgs {
 };
 
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+// 8 consecutive e4m3 weights times their fp32 block scale, rounded once more to bf16: the
+// conversion to fp32 is exact, the product is rounded to fp32, then RNE to bf16
+__device__ __forceinline__ bf16x8_t dequant8(uint2 u, float s) {
+    const f32x2_t p0 = __builtin_amdgcn_cvt_pk_f32_fp8(u.x, false), p1 = __builtin_amdgcn_cvt_pk_f32_fp8(u.x, true);
+    const f32x2_t p2 = __builtin_amdgcn_cvt_pk_f32_fp8(u.y, false), p3 = __builtin_amdgcn_cvt_pk_f32_fp8(u.y, true);
+    const bf16x8_t r = {(__bf16)(p0[0] * s), (__bf16)(p0[1] * s), (__bf16)(p1[0] * s), (__bf16)(p1[1] * s),
+                        (__bf16)(p2[0] * s), (__bf16)(p2[1] * s), (__bf16)(p3[0] * s), (__bf16)(p3[1] * s)};
+    return r;
+}
 
 // LDS layout of a stage: 256 rows x BK bf16 per operand, rows of BK/8 16-byte chunks.  The
 // LDS serves a 16-byte-per-lane read 16 lanes at a time from 64 banks (256 bytes); the
@@ -80,12 +101,19 @@ constexpr int LPW = 2 * NBLK / 4;      // DMA instructions per wave per stage
 static_assert(BK == 32 || BK == 64, "swizzle written for 32- or 64-wide K slices");
 __device__ __forceinline__ int swz(int row) { return BK == 64 ? ((row >> 1) & 7) : ((row >> 2) & 3); }
 
-template <bool UP>
+// W8: the weights are e4m3 with 128x128 block scales.  They are staged as fp8 (a weight
+// stage is 256 rows x 128 bytes = two 64-deep slices, refilled two slices ahead) and each
+// fragment is dequantised to bf16 on its way from LDS to the matrix cores; activations stay
+// bf16 and the same bf16 MFMAs run.
+template <bool UP, bool W8>
 __global__ __launch_bounds__(M_THREADS, 1) void grouped_gemm_bf16_kernel(GemmArgs a, gemm::TileOrder to) {
     __shared__ __attribute__((aligned(1024))) uint16_t As[STAGES][BM * BK];
     __shared__ __attribute__((aligned(1024))) uint16_t Bs[STAGES][BN * BK];
     __shared__ int32_t tile_prefix[gemm::kMaxSlots + 1];  // m-tiles before slot e
     __shared__ int32_t part[gemm::kThreads];
+    // fp8: the tile's weight block scales along K, [2][K/128] (up: gate, up half; down: the two
+    // 128-column blocks of the tile), staged at tile start so the K loop reads them from LDS
+    __shared__ float sbuf[2][kMaxKG8];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -95,6 +123,8 @@ __global__ __launch_bounds__(M_THREADS, 1) void grouped_gemm_bf16_kernel(GemmArg
 
     const int32_t total_mt = gemm::number_tiles<BM>(a.counts, a.seg, a.cap, a.El, tile_prefix, part);
     const uint32_t row_bytes = static_cast<uint32_t>(a.K) * 2u;
+    const int64_t KG = a.K / 128;      // fp8 scale blocks along K
+    const int64_t NB = a.N / 128;      // fp8 scale blocks along the output dimension
     const int nsn = a.NT / to.SN;
     const int64_t total_super = static_cast<int64_t>((total_mt + to.SM - 1) / to.SM) * nsn;
     const int xcd = blockIdx.x & 7;
@@ -106,6 +136,15 @@ __global__ __launch_bounds__(M_THREADS, 1) void grouped_gemm_bf16_kernel(GemmArg
     int fchunk[BK / 16];
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) fchunk[ks] = ((2 * ks + (lane >> 5)) ^ swz(frow)) * 8;
+    // fp8 weights: within half h of a slice, a lane reads one 16-byte weight chunk, 2h + lane/32,
+    // and feeds its first 8 values to step 0 and the last 8 to step 1.  The activation
+    // fragments follow the same K assignment (step ks of half h: the 8 values at 32h +
+    // 16 (lane/32) + 8 ks), so every product still pairs equal K.
+    int fchunk8[2][2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) fchunk8[h][ks] = ((4 * h + 2 * (lane >> 5) + ks) ^ swz(frow)) * 8;
 
     for (int64_t sup = xcd; sup < total_super; sup += 8) {
         const int32_t em = static_cast<int32_t>(sup / nsn) * to.SM + q / to.SN;
@@ -129,6 +168,10 @@ __global__ __launch_bounds__(M_THREADS, 1) void grouped_gemm_bf16_kernel(GemmArg
             // rows past the segment end fall outside the resource: they read as zeros
             dbase = a.A + row0 * a.K;
             dbytes = nrows * row_bytes;
+        } else if (W8) {
+            const int64_t rows = UP ? 2 * a.N : a.N;
+            dbase = reinterpret_cast<const uint16_t*>(a.B8 + static_cast<int64_t>(e) * rows * a.K);
+            dbytes = static_cast<uint32_t>(rows * a.K);
         } else if (UP) {
             dbase = a.B + static_cast<int64_t>(e) * 2 * a.N * a.K;
             dbytes = static_cast<uint32_t>(2 * a.N) * row_bytes;
@@ -137,6 +180,8 @@ __global__ __launch_bounds__(M_THREADS, 1) void grouped_gemm_bf16_kernel(GemmArg
             dbytes = static_cast<uint32_t>(a.N) * row_bytes;
         }
         const __amdgpu_buffer_rsrc_t rsrc = gemm::make_rsrc_uniform(dbase, dbytes);
+        // bytes per operand row: fp8 weight rows are K bytes
+        const uint32_t op_row_bytes = (W8 && !loads_a) ? static_cast<uint32_t>(a.K) : row_bytes;
         // DMA p of this wave covers tile rows r = ((wv & 1) * LPW + p) * RPB + dma_row.  Its
         // global row is row(p = 0) + p * RPB for every operand (A rows; up: gate or up half,
         // chosen by wv & 1; down: w2 rows), and its swizzled chunk depends only on p's parity
@@ -152,15 +197,20 @@ __global__ __launch_bounds__(M_THREADS, 1) void grouped_gemm_bf16_kernel(GemmArg
             if (loads_a) grow = static_cast<uint32_t>(r - par * RPB);
             else if (UP) grow = static_cast<uint32_t>((wv & 1) * a.N + nt * UP_COLS + dma_row);
             else grow = static_cast<uint32_t>(nt * BN + (wv & 1) * LPW * RPB + dma_row);
-            vbase[par] = grow * row_bytes + static_cast<uint32_t>(((lane % CPR) ^ swz(r)) * 16);
+            vbase[par] = grow * op_row_bytes + static_cast<uint32_t>(((lane % CPR) ^ swz(r)) * 16);
         }
-        const uint32_t rstep = static_cast<uint32_t>(RPB) * row_bytes;
-        auto issue = [&](int buf, int64_t kt) {
-            const int soff = static_cast<int>(kt * BK * 2);
+        const uint32_t rstep = static_cast<uint32_t>(RPB) * op_row_bytes;
+        // A waves: issue(buf, kt) fills stage kt % 2 (= buf) with slice kt, K bytes
+        // [128 kt, +128).  fp8 weight waves: a weight stage holds slices (2m, 2m+1), bytes
+        // [128 m, +128) of the fp8 rows, in stage m % 2; issue_b(t) loads the pair starting at
+        // even slice t.  It is called after the barrier of odd slices kt, for t = kt + 3: the
+        // stage's previous pair (kt - 1, kt) has been read by then, so the pair is in flight
+        // for two slices before its first half-slice is read.
+        auto issue_dma = [&](int stage_off, int soff) {
             // the LDS base and the two offset bases are made opaque per call so the LPW
             // offsets are recomputed here (one add each) instead of being hoisted out of the
             // K loop into LPW registers
-            int off = buf * (BM * BK) + (wv & 1) * LPW * 512;
+            int off = stage_off + (wv & 1) * LPW * 512;
             uint32_t vb0 = vbase[0], vb1 = vbase[1];
             asm volatile("" : "+s"(off), "+v"(vb0), "+v"(vb1));
             uint16_t* base = (loads_a ? &As[0][0] : &Bs[0][0]) + off;
@@ -170,6 +220,14 @@ __global__ __launch_bounds__(M_THREADS, 1) void grouped_gemm_bf16_kernel(GemmArg
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (gemm::lds_void_t*)(base + p * 512), 16, vo,
                                                         soff, 0, 0);
             }
+        };
+        auto issue = [&](int buf, int64_t kt) {
+            if (W8 && !loads_a) return;
+            issue_dma(buf * (BM * BK), static_cast<int>(kt * BK * 2));
+        };
+        auto issue_b = [&](int64_t t) {
+            if (!W8 || loads_a) return;
+            issue_dma(static_cast<int>((t >> 1) & 1) * (BN * BK), static_cast<int>(t * BK));
         };
 
         floatx16_t acc[4][4];
@@ -182,18 +240,42 @@ __global__ __launch_bounds__(M_THREADS, 1) void grouped_gemm_bf16_kernel(GemmArg
 
         const uint16_t* a_rd = &As[0][0] + (wm * 128 + frow) * BK;
         const uint16_t* b_rd = &Bs[0][0] + frow * BK;
+        const uint8_t* b8_rd = reinterpret_cast<const uint8_t*>(&Bs[0][0]) + frow * 128;
+        // fp8 block scale of B block j for slice kt (K group kt / 2): up -> blocks 0,1 use
+        // the gate half's scale of i-block nt, 2,3 the up half's; down -> column block
+        // 2 nt + wn (the wave's 128 columns).  The prefetch after the last slice asks for
+        // slice KT: its fragments are never used, and the index stays inside the row.
+        auto wscale = [&](int j, int64_t kt) -> float {
+            if (!W8) return 1.f;
+            const int64_t kg = (kt >> 1) < KG ? (kt >> 1) : KG - 1;
+            return sbuf[UP ? (j >> 1) : wn][kg];
+        };
         // B block j of the wave: up -> blocks 0,1 gate, 2,3 the matching up rows
 #define MOE_BROW(j) (UP ? ((j) >> 1) * UP_COLS + wn * 64 + ((j) & 1) * 32 : wn * 128 + (j) * 32)
         // fragments of one half slice (K 32 = two 16-deep MFMA steps) from stage BUF
-#define MOE_LOAD_HALF(FA, FB, BUF, HALF)                                                      \
+#define MOE_LOAD_HALF(FA, FB, BUF, HALF, SLICE, SPAR)                                         \
     do {                                                                                      \
         const uint16_t* Ab_ = a_rd + (BUF) * (BM * BK);                                       \
         const uint16_t* Bb_ = b_rd + (BUF) * (BN * BK);                                       \
-        _Pragma("unroll") for (int ks_ = 0; ks_ < 2; ++ks_) {                                 \
-            _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) FA[ks_][i_] =                    \
-                *reinterpret_cast<const bf16x8_t*>(Ab_ + i_ * 32 * BK + fchunk[2 * (HALF) + ks_]); \
-            _Pragma("unroll") for (int j_ = 0; j_ < 4; ++j_) FB[ks_][j_] =                    \
-                *reinterpret_cast<const bf16x8_t*>(Bb_ + MOE_BROW(j_) * BK + fchunk[2 * (HALF) + ks_]); \
+        if (W8) {                                                                             \
+            _Pragma("unroll") for (int ks_ = 0; ks_ < 2; ++ks_)                               \
+                _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) FA[ks_][i_] =                \
+                    *reinterpret_cast<const bf16x8_t*>(Ab_ + i_ * 32 * BK + fchunk8[HALF][ks_]); \
+            _Pragma("unroll") for (int j_ = 0; j_ < 4; ++j_) {                                \
+                const uint4 raw_ = *reinterpret_cast<const uint4*>(                           \
+                    b8_rd + (((SLICE) >> 1) & 1) * (BN * 128) + MOE_BROW(j_) * 128 +          \
+                    ((4 * (SPAR) + 2 * (HALF) + (lane >> 5)) ^ swz(frow)) * 16);              \
+                const float sc_ = wscale(j_, SLICE);                                          \
+                FB[0][j_] = dequant8(make_uint2(raw_.x, raw_.y), sc_);                        \
+                FB[1][j_] = dequant8(make_uint2(raw_.z, raw_.w), sc_);                        \
+            }                                                                                 \
+        } else {                                                                              \
+            _Pragma("unroll") for (int ks_ = 0; ks_ < 2; ++ks_) {                             \
+                _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) FA[ks_][i_] =                \
+                    *reinterpret_cast<const bf16x8_t*>(Ab_ + i_ * 32 * BK + fchunk[2 * (HALF) + ks_]); \
+                _Pragma("unroll") for (int j_ = 0; j_ < 4; ++j_) FB[ks_][j_] =                \
+                    *reinterpret_cast<const bf16x8_t*>(Bb_ + MOE_BROW(j_) * BK + fchunk[2 * (HALF) + ks_]); \
+            }                                                                                 \
         }                                                                                     \
     } while (0)
 #define MOE_MFMA_HALF(FA, FB)                                                                 \
@@ -215,13 +297,26 @@ __global__ __launch_bounds__(M_THREADS, 1) void grouped_gemm_bf16_kernel(GemmArg
         // the previous tile's trailing DMAs and every wave's reads of the stage buffers are done
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
         __syncthreads();
+        if (W8) {
+            for (int t = tid; t < 2 * KG; t += M_THREADS) {
+                const int r = t / static_cast<int>(KG), kg = t % static_cast<int>(KG);
+                sbuf[r][kg] = UP ? a.SB[((static_cast<int64_t>(e) * 2 + r) * NB + nt) * KG + kg]
+                                 : a.SB[(static_cast<int64_t>(e) * NB + 2 * nt + r) * KG + kg];
+            }
+            // the prologue barrier below publishes sbuf; its loads are drained here so the
+            // DMA counts that follow start from zero
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
         issue(0, 0);
         issue(1, KT > 1 ? 1 : 0);
+        issue_b(0);
+        issue_b(KT > 2 ? 2 : 0);
+        // slice 0 landed: every wave has exactly LPW DMAs issued after it
         asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPW) : "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
         bf16x8_t f0a[2][4], f0b[2][4], f1a[2][4], f1b[2][4];
-        MOE_LOAD_HALF(f0a, f0b, 0, 0);
+        MOE_LOAD_HALF(f0a, f0b, 0, 0, 0, 0);
         // Within each half the scheduler interleaves one fragment read (and, in the second
         // half, one DMA issue) with every two MFMAs, so LDS and DMA traffic spread over the
         // half and few reads are outstanding when the next half starts.
@@ -233,23 +328,35 @@ __global__ __launch_bounds__(M_THREADS, 1) void grouped_gemm_bf16_kernel(GemmArg
             __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                                \
         }                                                                                     \
     } while (0)
-        for (int64_t kt = 0; kt < KT; ++kt) {
-            const int buf = static_cast<int>(kt & 1);
-            __builtin_amdgcn_sched_barrier(0);
-            MOE_LOAD_HALF(f1a, f1b, buf, 1);
-            MOE_MFMA_HALF(f0a, f0b);
-            MOE_INTERLEAVE(false);
-            __builtin_amdgcn_sched_barrier(0);
-            // slice kt+1 landed and every wave is done reading stage `buf`
-            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-            __builtin_amdgcn_s_barrier();
-            __builtin_amdgcn_sched_barrier(0);
-            issue(buf, kt + 2 < KT ? kt + 2 : KT - 1);
-            MOE_LOAD_HALF(f0a, f0b, buf ^ 1, 0);
-            MOE_MFMA_HALF(f1a, f1b);
-            MOE_INTERLEAVE(true);
-            __builtin_amdgcn_sched_barrier(0);
+        // one slice; PAR = kt % 2 is a compile-time constant (the loop below steps by two
+        // and KT is even), which is also the slice's stage
+#define MOE_SLICE(KT_, PAR)                                                                   \
+    do {                                                                                      \
+        __builtin_amdgcn_sched_barrier(0);                                                    \
+        MOE_LOAD_HALF(f1a, f1b, PAR, 1, KT_, PAR);                                            \
+        MOE_MFMA_HALF(f0a, f0b);                                                              \
+        MOE_INTERLEAVE(false);                                                                \
+        __builtin_amdgcn_sched_barrier(0);                                                    \
+        /* slice KT_+1 landed and every wave is done reading stage PAR; at even slices the   \
+           fp8 weight waves' newest pair is not needed before the next barrier */            \
+        if (W8 && (PAR) == 0 && !loads_a)                                                     \
+            asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(LPW) : "memory");            \
+        else                                                                                  \
+            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");                      \
+        __builtin_amdgcn_s_barrier();                                                         \
+        __builtin_amdgcn_sched_barrier(0);                                                    \
+        issue(PAR, (KT_) + 2 < KT ? (KT_) + 2 : KT - 1);                                      \
+        if ((PAR) == 1) issue_b((KT_) + 3 < KT ? (KT_) + 3 : KT - 2);                         \
+        MOE_LOAD_HALF(f0a, f0b, (PAR) ^ 1, 0, (KT_) + 1, (PAR) ^ 1);                          \
+        MOE_MFMA_HALF(f1a, f1b);                                                              \
+        MOE_INTERLEAVE(true);                                                                 \
+        __builtin_amdgcn_sched_barrier(0);                                                    \
+    } while (0)
+        for (int64_t kt = 0; kt < KT; kt += 2) {
+            MOE_SLICE(kt, 0);
+            MOE_SLICE(kt + 1, 1);
         }
+#undef MOE_SLICE
 #undef MOE_INTERLEAVE
 #undef MOE_MFMA_HALF
 #undef MOE_LOAD_HALF
@@ -361,7 +468,9 @@ moe_status check_common(moe_dtype act_dt, const moe_plan* plan, const moe_expert
     MOE_CHECK_ARG(plan->counts && plan->seg_offsets && plan->num_rows && plan->cap >= 0);
     MOE_CHECK_ARG(w->w13 && w->w2);
     if (w->dtype == MOE_FP8_E4M3) {
-        // block-scaled e4m3 weights take bf16 activations (quantised per 1x128 group inside)
+        // block-scaled e4m3 weights take bf16 activations (kept bf16, or quantised per 1x128
+        // group inside, by fp8_act)
+        MOE_CHECK_ARG(w->fp8_act == MOE_FP8_ACT_BF16 || w->fp8_act == MOE_FP8_ACT_E4M3);
         if (act_dt != MOE_BF16) return MOE_ERR_UNSUPPORTED;
         MOE_CHECK_ARG(w->s13 && w->s2);
         return MOE_OK;
@@ -385,10 +494,15 @@ moe_status run_stage(bool up, const void* A, moe_dtype act_dt, const moe_plan* p
     const void* B = up ? w->w13 : w->w2;
     const int64_t K = up ? H : I;
     const int64_t N = up ? I : H;
+    const bool w8 = w->dtype == MOE_FP8_E4M3;
+    // no fp8 fallback; the staged block scales hold up to kMaxKG8 K groups
+    if (w8 && (!mfma_ok(act_dt, H, I, A, B, C) || K / 128 > kMaxKG8)) return MOE_ERR_UNSUPPORTED;
     if (mfma_ok(act_dt, H, I, A, B, C)) {
         GemmArgs g;
         g.A = static_cast<const uint16_t*>(A);
         g.B = static_cast<const uint16_t*>(B);
+        g.B8 = static_cast<const uint8_t*>(B);
+        g.SB = up ? w->s13 : w->s2;
         g.C = static_cast<uint16_t*>(C);
         g.counts = plan->counts;
         g.seg = plan->seg_offsets;
@@ -402,8 +516,13 @@ moe_status run_stage(bool up, const void* A, moe_dtype act_dt, const moe_plan* p
         gemm::TileOrder to;
         if (!gemm::pick_tile_order(g.NT, blocks, &to)) return MOE_ERR_UNSUPPORTED;
         const dim3 grid(static_cast<unsigned>(blocks));
-        if (up) hipLaunchKernelGGL(grouped_gemm_bf16_kernel<true>, grid, dim3(M_THREADS), 0, stream, g, to);
-        else hipLaunchKernelGGL(grouped_gemm_bf16_kernel<false>, grid, dim3(M_THREADS), 0, stream, g, to);
+        if (w8) {
+            if (up) hipLaunchKernelGGL((grouped_gemm_bf16_kernel<true, true>), grid, dim3(M_THREADS), 0, stream, g, to);
+            else hipLaunchKernelGGL((grouped_gemm_bf16_kernel<false, true>), grid, dim3(M_THREADS), 0, stream, g, to);
+        } else {
+            if (up) hipLaunchKernelGGL((grouped_gemm_bf16_kernel<true, false>), grid, dim3(M_THREADS), 0, stream, g, to);
+            else hipLaunchKernelGGL((grouped_gemm_bf16_kernel<false, false>), grid, dim3(M_THREADS), 0, stream, g, to);
+        }
         MOE_LAUNCH_CHECK();
         return MOE_OK;
     }
@@ -446,7 +565,7 @@ extern "C" moe_status moe_expert_gemm_up(const void* x_perm, moe_dtype act_dt, c
                                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
     moe_status st = moe::check_common(act_dt, plan, w, H, I);
     if (st != MOE_OK) return st;
-    if (w->dtype == MOE_FP8_E4M3)
+    if (w->dtype == MOE_FP8_E4M3 && w->fp8_act == MOE_FP8_ACT_E4M3)
         return moe::gemm::run_fp8_stage(true, x_perm, plan, w, H, I, h, workspace, workspace_bytes, stream);
     return moe::run_stage(true, x_perm, act_dt, plan, w, H, I, h, stream);
 }
@@ -457,7 +576,7 @@ extern "C" moe_status moe_expert_gemm_down(const void* h, moe_dtype act_dt, cons
                                            hipStream_t stream) {
     moe_status st = moe::check_common(act_dt, plan, w, H, I);
     if (st != MOE_OK) return st;
-    if (w->dtype == MOE_FP8_E4M3)
+    if (w->dtype == MOE_FP8_E4M3 && w->fp8_act == MOE_FP8_ACT_E4M3)
         return moe::gemm::run_fp8_stage(false, h, plan, w, H, I, y_perm, workspace, workspace_bytes, stream);
     return moe::run_stage(false, h, act_dt, plan, w, H, I, y_perm, stream);
 }
@@ -474,7 +593,7 @@ extern "C" moe_status moe_expert_gemm(const void* x_perm, moe_dtype act_dt, cons
         return MOE_ERR_CAPACITY;
     MOE_CHECK_ARG(workspace && moe::aligned(workspace, 256));
     const size_t hb = moe::h_bytes(plan->cap, I, act_dt);
-    if (w->dtype == MOE_FP8_E4M3) {
+    if (w->dtype == MOE_FP8_E4M3 && w->fp8_act == MOE_FP8_ACT_E4M3) {
         void* rest = static_cast<char*>(workspace) + hb;
         const size_t rest_bytes = workspace_bytes - hb;
         st = moe::gemm::run_fp8_stage(true, x_perm, plan, w, H, I, workspace, rest, rest_bytes, stream);

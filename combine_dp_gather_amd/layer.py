@@ -51,7 +51,7 @@ class LayerSpec:
 class DeviceWeights:
     """Router and expert weights resident in HBM."""
 
-    def __init__(self, inp, device="cuda"):
+    def __init__(self, inp, device="cuda", fp8_act: str = "bf16"):
         cfg = inp.cfg
         bf = cfg.dtype == "bf16"
         self.router = _to_dev(inp.router_w, device, bf)
@@ -68,7 +68,7 @@ class DeviceWeights:
         trivial = cfg.slot_logical is None
         self.phys_of = None if trivial else _to_dev(inp.phys_of, device)
         self.n_rep = None if trivial else _to_dev(inp.n_rep, device)
-        self.ew = make_expert_weights(self.w13, self.w2, self.s13, self.s2)
+        self.ew = make_expert_weights(self.w13, self.w2, self.s13, self.s2, fp8_act)
 
 
 def spec_of(cfg) -> LayerSpec:

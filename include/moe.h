@@ -229,9 +229,19 @@ moe_status moe_dispatch(const void* global_x, const int32_t* topk_ids, int64_t G
  * 权重切不均匀的问题"; permute, MM1, activation, MM2 in the order of the vLLM walkthrough
  * "vLLM 源码完全拆解(二十七): Dual Batch Overlap" (figure of the modular-kernel blocks).
  * ---------------------------------------------------------------------------------------- */
+/* How e4m3 weights meet the activations (fp8 weights only).
+ *   MOE_FP8_ACT_BF16  activations stay bf16; each weight fragment is dequantised in the kernel
+ *                     (e4m3 * block scale, rounded to bf16) and the bf16 matrix cores run.
+ *                     Half the weight bytes of bf16, no activation rounding.  Default.
+ *   MOE_FP8_ACT_E4M3  activations are quantised per 1x128 group to e4m3 (scale = amax/448,
+ *                     the per-token-group quantisation of the SGLang page, section "prefll 侧的
+ *                     一个必要步骤：per-token-group 量化"), fp8 matrix cores, and each 128-deep K
+ *                     group's partial sum is promoted by (activation scale * weight scale). */
+typedef enum { MOE_FP8_ACT_BF16 = 0, MOE_FP8_ACT_E4M3 = 1 } moe_fp8_act;
+
 typedef struct {
     int32_t dtype;          /* MOE_F32, MOE_BF16 (same as activations) or MOE_FP8_E4M3 */
-    int32_t reserved;
+    int32_t fp8_act;        /* fp8 weights: moe_fp8_act; ignored otherwise */
     const void* w13;        /* device [E_l, 2, I, H]: [e][0] = gate_proj, [e][1] = up_proj */
     const void* w2;         /* device [E_l, H, I]: down_proj */
     const float* s13;       /* fp8 only: device fp32[E_l, 2, I/128, H/128] block scales */
@@ -259,7 +269,8 @@ moe_status moe_expert_gemm(const void* x_perm, moe_dtype act_dt, const moe_plan*
 /* The two halves of moe_expert_gemm, for callers that time or overlap them separately.
  *   _up:   x_perm -> h      (h: device [cap, I] act_dt, caller memory)
  *   _down: h      -> y_perm
- * With fp8 weights each half quantises its activations into the workspace first. */
+ * With fp8 weights in MOE_FP8_ACT_E4M3 mode each half quantises its activations into the
+ * workspace first. */
 moe_status moe_expert_gemm_up(const void* x_perm, moe_dtype act_dt, const moe_plan* plan,
                               const moe_expert_weights* w, int64_t H, int64_t I, void* h,
                               void* workspace, size_t workspace_bytes, hipStream_t stream);

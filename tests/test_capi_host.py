@@ -129,6 +129,9 @@ def test_argument_errors_return_before_any_launch(m):
     w_noscale = _lib.ExpertWeights(_lib.MOE_FP8_E4M3, 0, 1, 1, None, None)
     assert lib.moe_expert_gemm(1, _lib.MOE_BF16, ctypes.byref(plan), ctypes.byref(w_noscale), 256, 128,
                                1, 256, 1 << 30, None) == _lib.MOE_ERR_INVALID_ARG
+    w_badmode = _lib.ExpertWeights(_lib.MOE_FP8_E4M3, 2, 1, 1, 1, 1)
+    assert lib.moe_expert_gemm(1, _lib.MOE_BF16, ctypes.byref(plan), ctypes.byref(w_badmode), 256, 128, 1,
+                               256, 1 << 30, None) == _lib.MOE_ERR_INVALID_ARG
     w = _lib.ExpertWeights(_lib.MOE_F32, 0, 1, 1, None, None)
     assert lib.moe_expert_gemm(1, _lib.MOE_BF16, ctypes.byref(plan), ctypes.byref(w), 256, 128, 1, 1,
                                1 << 30, None) == _lib.MOE_ERR_INVALID_ARG

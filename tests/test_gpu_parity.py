@@ -15,12 +15,12 @@ from gpu_helpers import (build_layer, replicas_to_device, resized, say, to_np, t
 pytestmark = pytest.mark.gpu
 
 
-def run_and_compare(cfg, mode="sum", align=1, cap=None, check_mode_pair=None):
+def run_and_compare(cfg, mode="sum", align=1, cap=None, check_mode_pair=None, fp8_act="bf16"):
     say(f"[parity] {cfg.name} tokens={cfg.num_tokens} H={cfg.hidden} I={cfg.inter} "
         f"E={cfg.num_experts} k={cfg.top_k} mode={mode} align={align} cap={cap}")
     inp = moe_synth.make_inputs(cfg)
     ref = oracle.run_layer(inp, mode, align=align, cap=cap)
-    layer = build_layer(inp, mode, align, cap)
+    layer = build_layer(inp, mode, align, cap, fp8_act)
     reps = replicas_to_device(inp)
     layer.forward(reps)
     torch.cuda.synchronize()
@@ -104,11 +104,14 @@ def test_cfg3_decode_static_bound(mode):
     run_and_compare(moe_synth.CONFIGS["cfg3"], mode)
 
 
-def test_cfg5_fp8_block_scaled_small():
+@pytest.mark.parametrize("fp8_act", ["bf16", "e4m3"])
+def test_cfg5_fp8_block_scaled_small(fp8_act):
     # Zipf-biased routing, 16 slots holding 12 logical experts (4 hot ones twice), e4m3
-    # weights with 128x128 block scales; reduced H and I keep several tiles per slot
+    # weights with 128x128 block scales; reduced H and I keep several tiles per slot.
+    # Both ways of meeting the activations: bf16 with in-kernel weight dequantisation, and
+    # per-1x128-group e4m3 activations on the fp8 matrix cores
     cfg = resized("cfg5", (300, 0, 277, 41), hidden=1024, inter=512)
-    run_and_compare(cfg)
+    run_and_compare(cfg, fp8_act=fp8_act)
 
 
 def test_multi_tile_ragged_segments():
