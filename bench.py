@@ -139,6 +139,8 @@ def main():
     ap.add_argument("--fp8-act", default="bf16", choices=["bf16", "e4m3"],
                     help="fp8-weight workloads: keep activations bf16 (weights dequantised in the "
                          "kernel) or quantise them per 1x128 group for the fp8 matrix cores")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one step (all six calls) in a HIP graph and time its replays")
     ap.add_argument("--ceilings", action="store_true",
                     help="also measure practical ceilings: a plain 1 GiB device copy and the vendor "
                          "GEMM (torch.matmul) on the same per-expert shapes")
@@ -202,6 +204,16 @@ def main():
     overflow = int(layer.plan.error_flag.item())
     log(f"[bench] warmup done; routed local pairs R={R} overflow={overflow}")
 
+    graph = None
+    if args.graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+
     ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
            for _ in names] for _ in range(args.steps)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -209,11 +221,19 @@ def main():
     start.record(stream)
     t_wall = time.perf_counter()
     for s in range(args.steps):
-        step(ev[s])
+        if graph is not None:
+            graph.replay()
+        else:
+            step(ev[s])
     stop.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
     total_ms = start.elapsed_time(stop)
+    if graph is not None:
+        # the per-call breakdown comes from eager steps after the timed replays
+        for s in range(args.steps):
+            step(ev[s])
+        torch.cuda.synchronize()
     per = {n: float(np.mean([ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)]))
            for i, n in enumerate(names)}
     ms_per_step = total_ms / args.steps
@@ -298,6 +318,7 @@ def main():
                  if bf else "f32",
         "data": "synthetic (seeded PCG64; random-init DeepSeek-V3-shaped expert weights)",
         "config": {"workload": WORKLOAD_TEXT[args.workload], "name": cfg.name,
+                   "launch": "one HIP graph per step" if args.graph else "eager calls",
                    "tokens": T, "global_rows": G, "gather_mode": args.mode,
                    "routed_local_pairs": R, "parallelism": "one EP rank's share on 1 GPU"},
         "roofline": roof,
