@@ -294,14 +294,15 @@ def main():
     roof.pop("ms")
     roof.pop("peak_kind")
     fmt = "fp8" if mm == "mfma8" else "bf16"
-    kname = f"grouped_gemm_{fmt}_kernel<true>" if not fp8w or fmt == "fp8" else "grouped_gemm_bf16_kernel<true, true>"
+    kname = ("grouped_gemm_fp8_kernel" if fmt == "fp8"
+             else f"grouped_gemm_bf16_kernel<true, {'true' if fp8w else 'false'}>")
     roof["kernel"] = kname + (" (gate+up SwiGLU" + (", with its activation quantisation" if fmt == "fp8" else "")
                               + ")")
     from combine_dp_gather_amd.profiling import read_traffic_summary
     summary = os.path.join(ROOT, "profiles", f"grouped_gemm_{fmt}_up__{PROFILE_WORKLOAD[args.workload]}__traffic.txt")
     tb = read_traffic_summary(summary, GEMM_SOURCES[fmt])
     roof["traffic"] = round(tb) if tb is not None else None
-    roof["algorithmic_bytes"] = R * H * es + E_slots * 2 * I * H * (1 if fmt == "fp8" else es) + R * I * es
+    roof["algorithmic_bytes"] = R * H * es + E_slots * 2 * I * H * (1 if fp8w else es) + R * I * es
     result = {
         "metric": "MoE-layer tokens/s at 1 GPU; grouped-GEMM % peak MFMA; dispatch/combine % HBM",
         "value": round(T * args.steps / (total_ms / 1e3), 2),
