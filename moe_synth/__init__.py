@@ -35,6 +35,8 @@ TID_X = 0            # replica i uses TID_X + i  (i < 1000)
 TID_ROUTER = 1000
 TID_BIAS = 1001
 TID_EXPERT = 2000    # local expert e uses TID_EXPERT + 3e + {0 gate, 1 up, 2 down}
+TID_RESIDUAL = 4000  # replica i's residual stream uses TID_RESIDUAL + i (i < 1000)
+TID_NORM = 5000      # the RMSNorm weight of the layer's entry step
 
 
 @dataclass(frozen=True)
@@ -323,6 +325,29 @@ def make_inputs(cfg: MoEConfig, with_experts=True) -> MoEInputs:
                 q2[s], s2[s] = q2[first_slot[lg]], s2[first_slot[lg]]
         inp.w13_q, inp.w13_s, inp.w2_q, inp.w2_s = q13, s13, q2, s2
     return inp
+
+
+@dataclass
+class EntryInputs:
+    """Inputs of the fused entry step: per replica the attention block's output (the
+    replica's token rows, the same arrays make_inputs draws) and the residual stream, plus
+    the RMSNorm weight.  Residual rows are drawn wider (std residual_std) than the attention
+    output, as a residual stream that has accumulated many layers is."""
+    hidden: List[np.ndarray]
+    residual: List[np.ndarray]
+    gamma: np.ndarray
+    eps: float
+
+
+def make_entry_inputs(cfg: MoEConfig, hidden: List[np.ndarray], residual_std: float = 4.0,
+                      eps: float = 1e-6) -> EntryInputs:
+    """Residual rows shaped like ``hidden`` (the replicas of make_inputs) and a weight drawn
+    U(0.5, 1.5), stored in the workload's dtype."""
+    fmt = "f32" if cfg.dtype == "f32" else "bf16"
+    reqs = [_Req(cfg.seed, TID_RESIDUAL + i, x.shape, a=residual_std, fmt=fmt) for i, x in enumerate(hidden)]
+    reqs.append(_Req(cfg.seed, TID_NORM, (cfg.hidden,), dist="uniform", a=0.5, b=1.5, fmt=fmt))
+    drawn = draw_all(reqs)
+    return EntryInputs(hidden=list(hidden), residual=drawn[:-1], gamma=drawn[-1], eps=eps)
 
 
 def fake_uniform_logits(seed: int, G: int, E: int) -> np.ndarray:

@@ -137,6 +137,67 @@ def scatter(layout, out: np.ndarray) -> List[np.ndarray]:
     return [out[offs[i]:offs[i] + sizes[i]].copy() for i in range(len(sizes))]
 
 
+# ============================================================================ O0 fused entry step
+
+def bf16_rne(a: np.ndarray) -> np.ndarray:
+    """float64 -> bf16 bit patterns, round to nearest with ties to even, taken straight from
+    the float64 value (no float32 step, so no double rounding).  Non-zero inputs must lie in
+    bf16's normal range; the step never produces anything else on these workloads."""
+    a = np.ascontiguousarray(a, dtype=np.float64)
+    mag = np.abs(a)
+    if not np.all(np.isfinite(a)) or np.any((mag != 0) & ((mag < 2.0 ** -126) | (mag >= 2.0 ** 128))):
+        raise ValueError("bf16_rne: value outside bf16's normal range")
+    u = a.view(np.uint64)
+    # keep the top 7 of float64's 52 stored fraction bits: add just under half of the
+    # dropped range, plus the kept lowest bit (ties to even), then clear the dropped bits
+    drop = np.uint64(45)
+    keep_lsb = (u >> drop) & np.uint64(1)
+    r = (u + np.uint64((1 << 44) - 1) + keep_lsb) & ~np.uint64((1 << 45) - 1)
+    v = r.view(np.float64)
+    if np.any(np.abs(v) >= 2.0 ** 128):
+        raise ValueError("bf16_rne: rounds past bf16's largest value")
+    # v has at most 8 significant bits and a float32 exponent: float32 holds it exactly
+    return (v.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def entry_gather(layout, hidden: Sequence[Optional[np.ndarray]], residual: Sequence[Optional[np.ndarray]],
+                 gamma: np.ndarray, eps: float, H: int):
+    """The layer's entry step fused with the DP gather, on one replica set.
+
+    SGLang page, section "边界判定的融合" (under "两层通信怎么省"): when the residual update
+    is a plain add and the norm a plain RMSNorm, one pass writes the sum into the residual,
+    reads the normalised FFN input from it, and gathers that input; the attention-TP sum owed
+    before it has no counterpart on one rank.  Per replica row (plain readings):
+
+        residual <- round(hidden + residual)          (the stored dtype; the sum is exact in float64)
+        x        =  residual * gamma / sqrt(mean_h(residual^2) + eps)
+
+    RMSNorm is the plain definition (root mean square over the hidden dimension, eps inside
+    the root, an elementwise weight); it reads the residual as stored, i.e. after rounding.
+
+    Returns (x_global float64 [G, H], row_valid int32 [G], new residuals in the input dtype,
+    one per replica; None for idle replicas).  Pad rows of x_global are 0."""
+    mode, G, offs, sizes = layout
+    g = as_f32(gamma).astype(np.float64)
+    new_res, normed = [], []
+    for i in range(len(sizes)):
+        n = sizes[i]
+        if n == 0:
+            new_res.append(None)
+            normed.append(None)
+            continue
+        h, r = hidden[i][:n], residual[i][:n]
+        bf = np.asarray(r).dtype == np.uint16
+        s = as_f32(h).astype(np.float64) + as_f32(r).astype(np.float64)
+        rq = bf16_rne(s) if bf else s.astype(np.float32)
+        rv = as_f32(rq).astype(np.float64)
+        ms = np.mean(rv * rv, axis=1, keepdims=True)
+        normed.append(rv / np.sqrt(ms + float(eps)) * g)
+        new_res.append(rq.reshape(n, H))
+    gx, valid = gather(layout, [np.zeros((0, H)) if y is None else y for y in normed], H, np.float64)
+    return gx, valid, new_res
+
+
 # ============================================================================ O2 routing
 
 def as_f32(a: np.ndarray) -> np.ndarray:
