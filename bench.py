@@ -144,6 +144,9 @@ def main():
     ap.add_argument("--ceilings", action="store_true",
                     help="also measure practical ceilings: a plain 1 GiB device copy and the vendor "
                          "GEMM (torch.matmul) on the same per-expert shapes")
+    ap.add_argument("--entry", action="store_true",
+                    help="run the fused entry step (residual add + RMSNorm + gather) in the step "
+                         "in place of the plain gather; without it the fused step is timed apart")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run a plain device copy of MIB MiB (reference for HBM counters)")
     args = ap.parse_args()
@@ -181,12 +184,22 @@ def main():
     for r in inp.replicas:
         t = torch.from_numpy(np.ascontiguousarray(r))
         reps.append((t.view(torch.bfloat16) if bf else t).to(dev))
+    # the entry step's residual stream and norm weight (the replicas are the attention output)
+    ent = moe_synth.make_entry_inputs(cfg, inp.replicas)
+    res_dev = []
+    for r in ent.residual:
+        t = torch.from_numpy(np.ascontiguousarray(r))
+        res_dev.append((t.view(torch.bfloat16) if bf else t).to(dev))
+    gamma_dev = torch.from_numpy(np.ascontiguousarray(ent.gamma))
+    gamma_dev = (gamma_dev.view(torch.bfloat16) if bf else gamma_dev).to(dev)
     torch.cuda.synchronize()
     log(f"[bench] resident in HBM; G={layer.G}")
 
     stream = torch.cuda.current_stream()
-    names = ["gather", "route", "dispatch", "gemm_up", "gemm_down", "combine", "scatter"]
-    calls = [lambda: layer.gather(reps), layer.route, layer.dispatch,
+    first = ("entry", lambda: layer.entry(reps, res_dev, gamma_dev, ent.eps)) if args.entry else \
+        ("gather", lambda: layer.gather(reps))
+    names = [first[0], "route", "dispatch", "gemm_up", "gemm_down", "combine", "scatter"]
+    calls = [first[1], layer.route, layer.dispatch,
              lambda: layer.experts_up(), lambda: layer.experts_down(), layer.combine, layer.scatter]
 
     def step(evs=None):
@@ -254,6 +267,8 @@ def main():
     # algorithmic work per call (bytes or flops), per-unit figures x units
     work = {
         "gather": ("hbm", (T + G) * H * es + 4 * G),                   # read T rows, write G rows
+        # read attention output and residual, write residual and the gathered row; norm weight
+        "entry": ("hbm", 3 * T * H * es + G * H * es + 4 * G + H * es),
         "route": ("mfma32", 2.0 * G * E * H),                          # exact fp32 fma chain + select
         "dispatch": ("hbm", 2 * R * H * es + 3 * 4 * G * k + 8 * R),  # x_perm copy + id passes
         "gemm_up": gemm_work(mm, 4.0 * R * H * I,                     # gate+up: 2*R*H*2I
@@ -289,6 +304,15 @@ def main():
         kernels["route_fast"] = {"ms": round(ms, 4), "bound": "hbm", "achieved": round(fb / (ms / 1e3) / 1e9, 2),
                                  "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(fb / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
                                  "note": "FAST gate + select, timed apart from the step (which uses the exact gate)"}
+    if not args.entry:
+        # the fused entry step timed on its own (the step above uses the plain gather); it
+        # updates the residual in place, so every call adds the attention output once more
+        ms = _time_ms(lambda: layer.entry(reps, res_dev, gamma_dev, ent.eps), iters=10)
+        eb = work["entry"][1]
+        kernels["entry"] = {"ms": round(ms, 4), "bound": "hbm", "achieved": round(eb / (ms / 1e3) / 1e9, 2),
+                            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(eb / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                            "note": "fused residual add + RMSNorm + gather, timed apart from the step "
+                                    "(which uses the plain gather)"}
     dom = "gemm_up"
     roof = dict(kernels[dom])
     roof.pop("ms")
@@ -320,6 +344,7 @@ def main():
         "data": "synthetic (seeded PCG64; random-init DeepSeek-V3-shaped expert weights)",
         "config": {"workload": WORKLOAD_TEXT[args.workload], "name": cfg.name,
                    "launch": "one HIP graph per step" if args.graph else "eager calls",
+                   "first_step": "fused residual add + RMSNorm + gather" if args.entry else "plain gather",
                    "tokens": T, "global_rows": G, "gather_mode": args.mode,
                    "routed_local_pairs": R, "parallelism": "one EP rank's share on 1 GPU"},
         "roofline": roof,

@@ -18,7 +18,7 @@ from ._lib import (MOE_BF16, MOE_F32, MOE_FP8_E4M3, MOE_PAD_AUTO, MOE_PAD_MAX_LE
                    GatherLayout, MoEError, Plan, RouteCfg, check)
 
 __all__ = [
-    "moe_gather_layout", "moe_gather", "moe_scatter", "moe_route", "moe_route_from_logits",
+    "moe_gather_layout", "moe_gather", "moe_entry_gather", "moe_scatter", "moe_route", "moe_route_from_logits",
     "moe_dispatch", "moe_dispatch_workspace_size", "moe_expert_gemm", "moe_expert_gemm_up",
     "moe_expert_gemm_down", "moe_expert_gemm_workspace_size", "moe_combine", "moe_version",
     "PlanBuffers", "make_route_cfg", "make_expert_map", "make_expert_weights", "MoEError",
@@ -98,6 +98,18 @@ def moe_gather(L: GatherLayout, replicas: Sequence[torch.Tensor], global_x: torc
     check("moe_gather", lib().moe_gather(ctypes.byref(L), ctypes.cast(arr, ctypes.c_void_p), H,
                                          _dtype_code(global_x), _ptr(global_x), _ptr(row_valid),
                                          _stream(stream)))
+
+
+def moe_entry_gather(L: GatherLayout, hidden: Sequence[torch.Tensor], residual: Sequence[torch.Tensor],
+                     norm_weight: torch.Tensor, eps: float, global_x: torch.Tensor,
+                     row_valid: torch.Tensor, stream=None) -> None:
+    """Residual add + RMSNorm + DP gather in one pass; ``residual`` tensors are updated in place."""
+    H = global_x.shape[1]
+    ha, ra = _ptr_array(hidden), _ptr_array(residual)
+    check("moe_entry_gather", lib().moe_entry_gather(
+        ctypes.byref(L), ctypes.cast(ha, ctypes.c_void_p), ctypes.cast(ra, ctypes.c_void_p),
+        _ptr(norm_weight), float(eps), H, _dtype_code(global_x), _ptr(global_x), _ptr(row_valid),
+        _stream(stream)))
 
 
 def moe_scatter(L: GatherLayout, out: torch.Tensor, replicas_out: Sequence[torch.Tensor],

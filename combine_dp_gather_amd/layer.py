@@ -17,7 +17,7 @@ import torch
 from . import (PlanBuffers, layout_offsets, layout_sizes, make_expert_map, make_expert_weights,
                make_route_cfg, moe_combine, moe_dispatch, moe_dispatch_workspace_size,
                moe_expert_gemm, moe_expert_gemm_down, moe_expert_gemm_up,
-               moe_expert_gemm_workspace_size, moe_gather, moe_gather_layout, moe_route,
+               moe_entry_gather, moe_expert_gemm_workspace_size, moe_gather, moe_gather_layout, moe_route,
                moe_route_workspace_size, moe_scatter)
 
 
@@ -122,6 +122,10 @@ class MoELayer:
     def gather(self, replicas):
         moe_gather(self.layout, replicas, self.global_x, self.row_valid)
 
+    def entry(self, hidden, residual, norm_weight, eps: float):
+        """The fused entry step in place of the gather: residual add, RMSNorm, gather."""
+        moe_entry_gather(self.layout, hidden, residual, norm_weight, eps, self.global_x, self.row_valid)
+
     def route(self):
         if self.G:
             moe_route(self.global_x, self.row_valid, self.w.router, self.w.bias, self.route_cfg,
@@ -160,8 +164,13 @@ class MoELayer:
     def scatter(self):
         moe_scatter(self.layout, self.out, self.replicas_out)
 
-    def forward(self, replicas) -> List[torch.Tensor]:
-        self.gather(replicas)
+    def forward(self, replicas, entry=None) -> List[torch.Tensor]:
+        """One step.  ``entry = (residual, norm_weight, eps)`` runs the fused entry step on
+        ``replicas`` (the attention outputs) instead of the plain gather."""
+        if entry is None:
+            self.gather(replicas)
+        else:
+            self.entry(replicas, *entry)
         self.route()
         self.dispatch()
         self.experts()

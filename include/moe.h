@@ -5,6 +5,7 @@
  * One rank's MoE layer, as the SGLang walkthrough "SGLang 源码完全拆解(十七): DP Attention
  * 与专家并行" (below: "the SGLang page") lays it out:
  *   1. gather the DP replicas' token slices into one global buffer      moe_gather_layout, moe_gather
+ *      (or, fused with the layer's residual add + RMSNorm entry step,       moe_entry_gather)
  *   2. route every global token to its top-k experts                     moe_route, moe_route_from_logits
  *   3. dispatch: counting-sort the (token, k) pairs into one contiguous
  *      segment per local expert slot                                     moe_dispatch
@@ -100,6 +101,38 @@ moe_status moe_gather_layout(const int32_t* num_tokens, int32_t W, moe_pad_mode 
  * ---------------------------------------------------------------------------------------- */
 moe_status moe_gather(const moe_gather_layout_t* L, const void* const* replica_x, int64_t H,
                       moe_dtype dt, void* global_x, int32_t* row_valid, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------
+ * moe_entry_gather -- the layer's entry step fused with the DP gather (SGLang page, section
+ * "边界判定的融合" under "两层通信怎么省": with a plain residual add and a plain RMSNorm one
+ * pass writes the sum into the residual, reads the normalised FFN input and gathers it).
+ * For every real row r of replica i:
+ *     residual_i[r] <- round(h_i[r] + residual_i[r])                  (in place, dtype dt)
+ *     global_x[offsets[i] + r] = round(residual_i[r] * norm_weight
+ *                                      / sqrt(mean over H of residual_i[r]^2 + eps))
+ * The norm reads the residual as stored (after rounding); sums and the mean of squares are
+ * fp32.  Pad rows of the global buffer are 0, and row_valid is written as by moe_gather, so
+ * this call replaces moe_gather on the path.  The attention-TP all-reduce that precedes the
+ * update on a multi-GPU rank is not part of it.
+ *   L                 layout from moe_gather_layout
+ *   replica_h         host array of W device pointers; replica i is [sizes[i], H] of dt
+ *                     (the attention output).  NULL allowed for a replica with 0 rows.
+ *   replica_residual  host array of W device pointers, [sizes[i], H] of dt, read and
+ *                     overwritten.  It may be the same buffer as replica_h[i] (each element
+ *                     is read before it is written) but must not overlap global_x.
+ *   norm_weight       device [H] of dt
+ *   eps               >= 0, added to the mean of squares inside the root
+ *   H, dt             hidden size (> 0); MOE_F32 or MOE_BF16
+ *   global_x          device [rows, H] dt, written in full;  row_valid: device int32[rows]
+ * Errors: MOE_ERR_INVALID_ARG as moe_gather, plus a NULL norm_weight or residual pointer of a
+ * non-idle replica, or a negative or non-finite eps.  Rows of 16-byte-aligned buffers with
+ * H * sizeof(dt) a multiple of 16 and at most 16 KiB run from registers in one read of each
+ * input; any other shape takes a slower two-pass path with the same results.
+ * ---------------------------------------------------------------------------------------- */
+moe_status moe_entry_gather(const moe_gather_layout_t* L, const void* const* replica_h,
+                            void* const* replica_residual, const void* norm_weight, float eps,
+                            int64_t H, moe_dtype dt, void* global_x, int32_t* row_valid,
+                            hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------------
  * moe_scatter -- the inverse of moe_gather with the same layout: y_i[r] = out[offset_i + r]

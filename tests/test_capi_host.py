@@ -160,3 +160,36 @@ def test_status_strings(m):
     lib = m.lib()
     assert lib.moe_status_string(0) == b"ok"
     assert b"invalid" in lib.moe_status_string(1)
+
+
+def test_entry_gather_argument_errors(m):
+    """Fused entry step: NULL norm weight or residual of a non-idle replica, bad eps, bad H or
+    dtype are rejected before any launch; an all-idle layout is a no-op."""
+    from combine_dp_gather_amd import _lib
+    lib = m.lib()
+    L = m.moe_gather_layout([3, 4], "sum")
+    fake = ctypes.c_void_p(4096)  # never dereferenced: every case fails its host checks first
+    hs = (ctypes.c_void_p * 2)(fake, fake)
+    none2 = (ctypes.c_void_p * 2)(None, None)
+
+    def call(layout, h, r, w, eps, H=16, dt=_lib.MOE_BF16, gx=fake, rv=fake):
+        return lib.moe_entry_gather(layout, ctypes.cast(h, ctypes.c_void_p) if h is not None else None,
+                                    ctypes.cast(r, ctypes.c_void_p) if r is not None else None, w, eps, H,
+                                    dt, gx, rv, None)
+
+    E = _lib.MOE_ERR_INVALID_ARG
+    assert call(None, hs, hs, fake, 1e-6) == E
+    assert call(ctypes.byref(L), None, hs, fake, 1e-6) == E
+    assert call(ctypes.byref(L), hs, None, fake, 1e-6) == E
+    assert call(ctypes.byref(L), hs, none2, fake, 1e-6) == E        # residual of a real replica
+    assert call(ctypes.byref(L), none2, hs, fake, 1e-6) == E        # input of a real replica
+    assert call(ctypes.byref(L), hs, hs, None, 1e-6) == E           # norm weight
+    assert call(ctypes.byref(L), hs, hs, fake, -1.0) == E
+    assert call(ctypes.byref(L), hs, hs, fake, float("nan")) == E
+    assert call(ctypes.byref(L), hs, hs, fake, float("inf")) == E
+    assert call(ctypes.byref(L), hs, hs, fake, 1e-6, H=0) == E
+    assert call(ctypes.byref(L), hs, hs, fake, 1e-6, dt=_lib.MOE_FP8_E4M3) == E
+    assert call(ctypes.byref(L), hs, hs, fake, 1e-6, gx=None) == E
+    assert call(ctypes.byref(L), hs, hs, fake, 1e-6, rv=None) == E
+    L0 = m.moe_gather_layout([0, 0], "max")
+    assert call(ctypes.byref(L0), none2, none2, None, 1e-6, gx=None, rv=None) == _lib.MOE_OK
