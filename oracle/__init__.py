@@ -432,6 +432,176 @@ def run_layer(inp, mode: str = "sum", align: int = 1, cap: Optional[int] = None)
                 plan=plan, x_perm=xp, y_perm=y, out=out, replicas_out=scatter(layout, out))
 
 
+# ============================================================================ O7 EPLB statistics
+
+def physical_counts(ids: np.ndarray, phys_of: np.ndarray, n_rep: np.ndarray, num_physical: int) -> np.ndarray:
+    """Tokens per physical expert slot in one step: every valid (row g, pick j) goes to the
+    rank-invariant replica phys_of[id, g mod n_rep[id]] (SGLang page, section "推理时怎么“选副本”":
+    without an all-to-all back end every rank must pick the same replica).  Ids outside
+    [0, E) (pad rows) and slots outside [0, num_physical) count nowhere.  int64[num_physical]."""
+    G, k = ids.shape
+    E = phys_of.shape[0]
+    out = np.zeros(num_physical, dtype=np.int64)
+    g = np.repeat(np.arange(G, dtype=np.int64), k)
+    e = ids.reshape(-1).astype(np.int64)
+    ok = (e >= 0) & (e < E)
+    g, e = g[ok], e[ok]
+    p = phys_of[e, g % n_rep[e]].astype(np.int64)
+    p = p[(p >= 0) & (p < num_physical)]
+    np.add.at(out, p, 1)
+    return out
+
+
+def physical_to_logical_count(phys_count: np.ndarray, phy2log: np.ndarray, num_logical: int) -> np.ndarray:
+    """Each physical slot's count added to the logical expert it holds (section "统计:把物理计数
+    还原成逻辑计数": the scatter-add that turns per-slot counts into per-expert load).
+    phys_count and phy2log are [L, P]; returns int64 [L, E]."""
+    L, P = phys_count.shape
+    out = np.zeros((L, num_logical), dtype=np.int64)
+    for l in range(L):
+        for p in range(P):
+            out[l, phy2log[l, p]] += phys_count[l, p]
+    return out
+
+
+def gpu_counts(phys_count: np.ndarray, num_gpus: int) -> np.ndarray:
+    """[..., P] per-slot counts -> [..., num_gpus] per-GPU sums; GPU r holds the contiguous
+    slots [r P/M, (r+1) P/M) (section "三步算法", step 3: phy2pphy = pack * slots-per-GPU + rank)."""
+    P = phys_count.shape[-1]
+    assert P % num_gpus == 0
+    return phys_count.reshape(*phys_count.shape[:-1], num_gpus, P // num_gpus).sum(axis=-1)
+
+
+def utilization_rate(gpu_count: np.ndarray) -> np.ndarray:
+    """Balancedness over the last axis (section "不均衡的代价与冗余专家的思路"):
+    (mean + 1e-5) / (max + 1e-5) of the per-GPU token counts; 1 is perfect balance."""
+    c = np.asarray(gpu_count, dtype=np.float64)
+    return (c.mean(axis=-1) + 1e-5) / (c.max(axis=-1) + 1e-5)
+
+
+def balanced_packing(weight: Sequence[float], num_packs: int):
+    """Spread n items over num_packs packs of n / num_packs items each, balancing pack loads.
+
+    The page describes it only in words (section "三步算法", step 1: balance the packs' total
+    load).  Reading (greedy, heaviest first): items in descending weight, ties in ascending
+    index; each goes to the lightest pack that still has room, ties to the lower pack index.
+    Returns (pack of each item, its position inside the pack in assignment order)."""
+    n = len(weight)
+    assert n % num_packs == 0
+    per = n // num_packs
+    order = sorted(range(n), key=lambda i: (-weight[i], i))
+    load = [0.0] * num_packs
+    size = [0] * num_packs
+    pack = [0] * n
+    rank = [0] * n
+    for i in order:
+        best = -1
+        for q in range(num_packs):
+            if size[q] < per and (best < 0 or load[q] < load[best]):
+                best = q
+        pack[i] = best
+        rank[i] = size[best]
+        load[best] += weight[i]
+        size[best] += 1
+    return pack, rank
+
+
+def replicate_experts(weight: Sequence[float], num_phy: int):
+    """Give num_phy slots to n logical experts, heavy experts several (section "三步算法", step 2:
+    loaded experts get more slots, light ones one).  Reading (greedy): every expert first gets
+    one slot in index order; each further slot goes to the expert with the largest load per
+    replica weight / count, ties to the lower index.  This greedy minimises the largest
+    per-replica load.  Returns (logical expert of each slot, replica rank of the slot,
+    replica count of each expert)."""
+    n = len(weight)
+    assert num_phy >= n
+    phy2log = list(range(n))
+    rank = [0] * n
+    cnt = [1] * n
+    for _ in range(n, num_phy):
+        best = 0
+        for e in range(1, n):
+            if weight[e] / cnt[e] > weight[best] / cnt[best]:
+                best = e
+        phy2log.append(best)
+        rank.append(cnt[best])
+        cnt[best] += 1
+    return phy2log, rank, cnt
+
+
+def rebalance_hierarchical(weight: np.ndarray, num_physical: int, num_groups: int, num_nodes: int,
+                           num_gpus: int):
+    """Expert placement from per-layer logical loads (section "三步算法:分组、复制、再打包").
+
+    1. Whole expert groups are packed onto nodes by group load (balanced_packing).
+    2. Inside each node, its logical experts get the node's P / nodes slots
+       (replicate_experts); replicas never leave their node.
+    3. Inside each node, the slots are packed onto the node's GPUs by per-replica load (the
+       expert's load divided by its replica count), P / gpus slots per GPU; a slot's global
+       index is node * (P / nodes) + gpu-in-node * (P / gpus) + position on the GPU.
+
+    Sums run in ascending index order.  weight: [L, E] float64.  Returns (phy2log [L, P],
+    phy_rank [L, P], log_count [L, E]) as int32."""
+    weight = np.asarray(weight, dtype=np.float64)
+    L, E = weight.shape
+    P = num_physical
+    if E % num_groups or num_groups % num_nodes or num_gpus % num_nodes or P % num_gpus:
+        raise ValueError("shapes do not divide")
+    group_size = E // num_groups
+    groups_per_node = num_groups // num_nodes
+    e_node, p_node = E // num_nodes, P // num_nodes
+    gpus_per_node, per_gpu = num_gpus // num_nodes, P // num_gpus
+    if p_node < e_node:
+        raise ValueError("fewer slots than experts on a node")
+    phy2log = np.empty((L, P), dtype=np.int32)
+    phy_rank = np.empty((L, P), dtype=np.int32)
+    log_count = np.empty((L, E), dtype=np.int32)
+    for l in range(L):
+        w = [float(v) for v in weight[l]]
+        group_load = []
+        for q in range(num_groups):
+            acc = 0.0
+            for e in range(q * group_size, (q + 1) * group_size):
+                acc += w[e]
+            group_load.append(acc)
+        gnode, gpos = balanced_packing(group_load, num_nodes)
+        # logical experts of node n in node order: its groups by position, each group's
+        # experts in ascending id
+        node_experts = [[0] * e_node for _ in range(num_nodes)]
+        for q in range(num_groups):
+            for t in range(group_size):
+                node_experts[gnode[q]][gpos[q] * group_size + t] = q * group_size + t
+        for nd in range(num_nodes):
+            ex = node_experts[nd]
+            wl = [w[e] for e in ex]
+            s2m, srank, mcnt = replicate_experts(wl, p_node)
+            share = [wl[s2m[i]] / mcnt[s2m[i]] for i in range(p_node)]
+            gpu, pos = balanced_packing(share, gpus_per_node)
+            for i in range(p_node):
+                slot = nd * p_node + gpu[i] * per_gpu + pos[i]
+                phy2log[l, slot] = ex[s2m[i]]
+                phy_rank[l, slot] = srank[i]
+            for m_ in range(e_node):
+                log_count[l, ex[m_]] = mcnt[m_]
+    return phy2log, phy_rank, log_count
+
+
+def logical_to_physical(phy2log: np.ndarray, phy_rank: np.ndarray, num_logical: int, max_rep: int):
+    """Dispatch table of one layer from a placement: phys_of[e, r] = the slot holding replica r
+    of expert e (-1 past its count), n_rep[e] = its replica count (ExpertLocationMetadata's
+    logical_to_all_physical_map and its num_valid, section "逻辑与物理的两套映射")."""
+    P = phy2log.shape[0]
+    phys_of = np.full((num_logical, max_rep), -1, dtype=np.int32)
+    n_rep = np.zeros(num_logical, dtype=np.int32)
+    for p in range(P):
+        e, r = int(phy2log[p]), int(phy_rank[p])
+        if r >= max_rep:
+            raise ValueError("more replicas than max_rep")
+        phys_of[e, r] = p
+        n_rep[e] += 1
+    return phys_of, n_rep
+
+
 def rel_err(got: np.ndarray, ref: np.ndarray) -> float:
     """max|got - ref| / max|ref| (infinity-norm relative error)."""
     got = np.asarray(got, dtype=np.float64)
