@@ -54,6 +54,60 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# placement the --eplb cycle computes: DeepSeek-V3's 256 experts in 8 groups on 256 + 32
+# redundant slots, 2 nodes of 9 GPUs, 16 slots per GPU
+EPLB = {"P": 288, "groups": 8, "nodes": 2, "gpus": 18}
+
+
+def eplb_cycle(cfg, inp, layer, reps, args, dev, act):
+    """One statistics window (a step under the workload's own slot table), the placement, and
+    the layer rebuilt under the new table.  Returns (cfg, inp, weights, layer, summary)."""
+    import torch
+    import moe_synth
+    import combine_dp_gather_amd as m
+    from dataclasses import replace
+    from combine_dp_gather_amd.layer import DeviceWeights, MoELayer, spec_of
+    E, k = cfg.num_experts, cfg.top_k
+    phys_h, nrep_h = inp.phys_of, inp.n_rep
+    Ph = int(phys_h.max()) + 1
+    p2l_h = np.zeros(Ph, dtype=np.int32)
+    for e in range(E):
+        for r in range(int(nrep_h[e])):
+            p2l_h[phys_h[e, r]] = e
+    layer.gather(reps)
+    layer.route()
+    counts = torch.zeros(Ph, dtype=torch.int64, device=dev)
+    m.moe_expert_load(layer.topk_ids[:layer.G], layer.emap, Ph, counts)
+    logical = torch.empty((1, E), dtype=torch.int64, device=dev)
+    m.moe_physical_to_logical_count(counts[None], torch.from_numpy(p2l_h[None]).to(dev), logical)
+    loads = logical.cpu().numpy().astype(np.float64)
+    p2l, rank, cnt = m.moe_eplb_rebalance(loads, EPLB["P"], EPLB["groups"], EPLB["nodes"], EPLB["gpus"])
+    phys_of, n_rep = m.moe_eplb_logical_to_physical(p2l[0], rank[0], E, int(cnt.max()))
+    # balancedness over the GPUs: the old table's slots padded to P, then the new table
+    old = np.zeros(EPLB["P"], dtype=np.int64)
+    old[:Ph] = counts.cpu().numpy()
+    before = float(m.moe_eplb_balancedness(old[None], EPLB["gpus"])[0])
+    cfg2 = replace(cfg, slot_logical=tuple(int(v) for v in p2l[0, :cfg.num_local]))
+    inp2 = moe_synth.make_inputs(cfg2)
+    inp2.phys_of, inp2.n_rep = phys_of, n_rep
+    del layer
+    torch.cuda.empty_cache()
+    w2 = DeviceWeights(inp2, dev, fp8_act=args.fp8_act)
+    layer2 = MoELayer(spec_of(cfg2), w2, cfg2.num_tokens, act, mode=args.mode,
+                      static_bound=cfg2.static_bound, device=dev)
+    layer2.gather(reps)
+    layer2.route()
+    new = torch.zeros(EPLB["P"], dtype=torch.int64, device=dev)
+    m.moe_expert_load(layer2.topk_ids[:layer2.G], layer2.emap, EPLB["P"], new)
+    after = float(m.moe_eplb_balancedness(new.cpu().numpy()[None], EPLB["gpus"])[0])
+    log(f"[bench] EPLB: balancedness over {EPLB['gpus']} GPUs {before:.3f} -> {after:.3f}; "
+        f"this GPU holds logical {p2l[0, :cfg.num_local].tolist()}")
+    summary = {"kind": "EPLB hierarchical", **EPLB, "this_gpu_slots": [0, cfg.num_local],
+               "this_gpu_logical": [int(v) for v in p2l[0, :cfg.num_local]],
+               "balancedness_before": round(before, 4), "balancedness_after": round(after, 4)}
+    return cfg2, inp2, w2, layer2, summary
+
+
 def cpu_baseline(inp, sample_per_replica: int):
     """The oracle as it stands on the first rows of every replica (a bounded sample)."""
     import oracle
@@ -147,6 +201,11 @@ def main():
     ap.add_argument("--entry", action="store_true",
                     help="run the fused entry step (residual add + RMSNorm + gather) in the step "
                          "in place of the plain gather; without it the fused step is timed apart")
+    ap.add_argument("--eplb", action="store_true",
+                    help="skewed workload: count one step's expert load under the workload's own "
+                         "slot table, place the experts with the library (288 slots, 8 groups, "
+                         "2 nodes x 9 GPUs; this GPU holds slots 0-15), and time the step under "
+                         "the new table with the per-step load count included")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run a plain device copy of MIB MiB (reference for HBM counters)")
     args = ap.parse_args()
@@ -194,6 +253,9 @@ def main():
     gamma_dev = (gamma_dev.view(torch.bfloat16) if bf else gamma_dev).to(dev)
     torch.cuda.synchronize()
     log(f"[bench] resident in HBM; G={layer.G}")
+    eplb_info = None
+    if args.eplb:
+        cfg, inp, w, layer, eplb_info = eplb_cycle(cfg, inp, layer, reps, args, dev, act)
 
     stream = torch.cuda.current_stream()
     first = ("entry", lambda: layer.entry(reps, res_dev, gamma_dev, ent.eps)) if args.entry else \
@@ -201,6 +263,12 @@ def main():
     names = [first[0], "route", "dispatch", "gemm_up", "gemm_down", "combine", "scatter"]
     calls = [first[1], layer.route, layer.dispatch,
              lambda: layer.experts_up(), lambda: layer.experts_down(), layer.combine, layer.scatter]
+    if eplb_info is not None:
+        # the statistics recorder's per-step work: this step's load of every physical slot
+        import combine_dp_gather_amd as m
+        load_acc = torch.zeros(EPLB["P"], dtype=torch.int64, device=dev)
+        names.append("expert_load")
+        calls.append(lambda: m.moe_expert_load(layer.topk_ids[:layer.G], layer.emap, EPLB["P"], load_acc))
 
     def step(evs=None):
         for i, c in enumerate(calls):
@@ -276,6 +344,7 @@ def main():
         "gemm_down": gemm_work(mm, 2.0 * R * I * H, E_slots * H * I * wb + R * I * es + R * H * es),
         "combine": ("hbm", R * H * es + G * H * es + 8 * G * k),      # read R rows, write G rows
         "scatter": ("hbm", 2 * T * H * es),
+        "expert_load": ("hbm", 4 * G * k + 8 * EPLB["P"]),              # read the ids, add the bins
     }
     peaks = {"hbm": HBM_PEAK_GBS, "mfma32": FP32_MFMA_PEAK_TFLOPS, "mfma": BF16_MFMA_PEAK_TFLOPS,
              "mfma8": FP8_MFMA_PEAK_TFLOPS}
@@ -346,7 +415,8 @@ def main():
                    "launch": "one HIP graph per step" if args.graph else "eager calls",
                    "first_step": "fused residual add + RMSNorm + gather" if args.entry else "plain gather",
                    "tokens": T, "global_rows": G, "gather_mode": args.mode,
-                   "routed_local_pairs": R, "parallelism": "one EP rank's share on 1 GPU"},
+                   "routed_local_pairs": R, "parallelism": "one EP rank's share on 1 GPU",
+                   **({"placement": eplb_info} if eplb_info is not None else {})},
         "roofline": roof,
         "kernels": kernels,
         "wall_s_timed": round(wall, 3),

@@ -10,6 +10,7 @@ from __future__ import annotations
 import ctypes
 from typing import List, Optional, Sequence
 
+import numpy as np
 import torch
 
 from . import _lib
@@ -18,7 +19,9 @@ from ._lib import (MOE_BF16, MOE_F32, MOE_FP8_E4M3, MOE_PAD_AUTO, MOE_PAD_MAX_LE
                    GatherLayout, MoEError, Plan, RouteCfg, check)
 
 __all__ = [
-    "moe_gather_layout", "moe_gather", "moe_entry_gather", "moe_scatter", "moe_route", "moe_route_from_logits",
+    "moe_gather_layout", "moe_gather", "moe_entry_gather", "moe_scatter", "moe_expert_load",
+    "moe_physical_to_logical_count", "moe_eplb_balancedness", "moe_eplb_rebalance",
+    "moe_eplb_logical_to_physical", "moe_route", "moe_route_from_logits",
     "moe_dispatch", "moe_dispatch_workspace_size", "moe_expert_gemm", "moe_expert_gemm_up",
     "moe_expert_gemm_down", "moe_expert_gemm_workspace_size", "moe_combine", "moe_version",
     "PlanBuffers", "make_route_cfg", "make_expert_map", "make_expert_weights", "MoEError",
@@ -162,6 +165,64 @@ def make_expert_map(num_logical: int, first_slot: int, num_slots: int,
                   _ptr(n_rep), first_slot, num_slots)
     m._keep = (phys_of, n_rep)
     return m
+
+
+# ------------------------------------------------------------------ expert-load statistics (EPLB)
+
+def moe_expert_load(topk_ids: torch.Tensor, emap, num_physical: int, phys_count: torch.Tensor,
+                    stream=None) -> None:
+    """Adds this step's token count of every physical slot to ``phys_count`` (int64 [P])."""
+    G, k = topk_ids.shape
+    check("moe_expert_load", lib().moe_expert_load(_ptr(topk_ids), G, k, ctypes.byref(emap), num_physical,
+                                                   _ptr(phys_count), _stream(stream)))
+
+
+def moe_physical_to_logical_count(phys_count: torch.Tensor, phy2log: torch.Tensor,
+                                  logical_count: torch.Tensor, stream=None) -> None:
+    """logical_count[l, e] = sum of phys_count[l, p] over the slots holding e (device, int64)."""
+    L, P = phys_count.shape
+    check("moe_physical_to_logical_count",
+          lib().moe_physical_to_logical_count(_ptr(phys_count), _ptr(phy2log), L, P, logical_count.shape[1],
+                                              _ptr(logical_count), _stream(stream)))
+
+
+def _host(a, dtype):
+    a = np.ascontiguousarray(a, dtype=dtype)
+    return a, a.ctypes.data_as(ctypes.c_void_p)
+
+
+def moe_eplb_balancedness(phys_count, num_gpus: int) -> np.ndarray:
+    """Host: per-layer (mean + 1e-5) / (max + 1e-5) of per-GPU counts from int64 [L, P]."""
+    pc, pp = _host(np.atleast_2d(phys_count), np.int64)
+    out = np.empty(pc.shape[0], dtype=np.float64)
+    check("moe_eplb_balancedness", lib().moe_eplb_balancedness(pp, pc.shape[0], pc.shape[1], num_gpus,
+                                                               out.ctypes.data_as(ctypes.c_void_p)))
+    return out
+
+
+def moe_eplb_rebalance(weight, num_physical: int, num_groups: int, num_nodes: int, num_gpus: int):
+    """Host: hierarchical expert placement from loads [L, E] -> (phy2log, phy_rank, log_count)."""
+    w, wp = _host(np.atleast_2d(weight), np.float64)
+    L, E = w.shape
+    phy2log = np.empty((L, num_physical), dtype=np.int32)
+    rank = np.empty((L, num_physical), dtype=np.int32)
+    cnt = np.empty((L, E), dtype=np.int32)
+    check("moe_eplb_rebalance", lib().moe_eplb_rebalance(
+        wp, L, E, num_physical, num_groups, num_nodes, num_gpus, phy2log.ctypes.data_as(ctypes.c_void_p),
+        rank.ctypes.data_as(ctypes.c_void_p), cnt.ctypes.data_as(ctypes.c_void_p)))
+    return phy2log, rank, cnt
+
+
+def moe_eplb_logical_to_physical(phy2log, phy_rank, num_logical: int, max_rep: int):
+    """Host: one layer's dispatch table (phys_of int32 [E, max_rep], n_rep int32 [E])."""
+    a, ap = _host(phy2log, np.int32)
+    r, rp = _host(phy_rank, np.int32)
+    phys_of = np.empty((num_logical, max_rep), dtype=np.int32)
+    n_rep = np.empty(num_logical, dtype=np.int32)
+    check("moe_eplb_logical_to_physical", lib().moe_eplb_logical_to_physical(
+        ap, rp, a.shape[0], num_logical, max_rep, phys_of.ctypes.data_as(ctypes.c_void_p),
+        n_rep.ctypes.data_as(ctypes.c_void_p)))
+    return phys_of, n_rep
 
 
 class PlanBuffers:

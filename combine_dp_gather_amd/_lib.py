@@ -52,6 +52,11 @@ SIGNATURES = {
     "moe_gather_layout": (c_i32, [c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, ctypes.POINTER(GatherLayout)]),
     "moe_gather": (c_i32, [ctypes.POINTER(GatherLayout), c_vp, c_i64, c_i32, c_vp, c_vp, c_vp]),
     "moe_scatter": (c_i32, [ctypes.POINTER(GatherLayout), c_vp, c_i64, c_i32, c_vp, c_vp]),
+    "moe_expert_load": (c_i32, [c_vp, c_i64, c_i32, ctypes.POINTER(ExpertMap), c_i32, c_vp, c_vp]),
+    "moe_physical_to_logical_count": (c_i32, [c_vp, c_vp, c_i32, c_i32, c_i32, c_vp, c_vp]),
+    "moe_eplb_balancedness": (c_i32, [c_vp, c_i32, c_i32, c_i32, c_vp]),
+    "moe_eplb_rebalance": (c_i32, [c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp]),
+    "moe_eplb_logical_to_physical": (c_i32, [c_vp, c_vp, c_i32, c_i32, c_i32, c_vp, c_vp]),
     "moe_entry_gather": (c_i32, [ctypes.POINTER(GatherLayout), c_vp, c_vp, c_vp, ctypes.c_float, c_i64,
                                  c_i32, c_vp, c_vp, c_vp]),
     "moe_route_workspace_size": (c_sz, [c_i64, c_i32, c_i64]),

@@ -12,6 +12,9 @@
  *   4. run the SwiGLU experts as grouped GEMMs over those segments       moe_expert_gemm (_up, _down)
  *   5. combine: weighted un-permute back to token order                  moe_combine
  *   6. scatter the global rows back to each replica's slice              moe_scatter
+ * and, beside the step, the expert-load statistics and placement of EPLB   moe_expert_load,
+ *   moe_physical_to_logical_count, moe_eplb_balancedness, moe_eplb_rebalance,
+ *   moe_eplb_logical_to_physical
  *
  * Conventions shared by every call
  *   - All tensors are dense, row-major, contiguous.  Device pointers are HIP device memory
@@ -324,6 +327,77 @@ moe_status moe_expert_gemm_down(const void* h, moe_dtype act_dt, const moe_plan*
 moe_status moe_combine(const void* y_perm, moe_dtype dt, const moe_plan* plan,
                        const float* topk_w, float routed_scale, int64_t H, void* out,
                        hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Expert-load statistics and expert placement (EPLB; SGLang page, section "EPLB:专家分布不均
+ * 怎么办").
+ * ---------------------------------------------------------------------------------------- */
+
+/* moe_expert_load -- token count of every physical expert slot in one step, ADDED to
+ * phys_count (the caller zeroes it at the start of a statistics window).  Each valid pair
+ * (row g, pick j) counts for the rank-invariant replica phys_of[id, g mod n_rep[id]], the
+ * same pick moe_dispatch makes (section "推理时怎么“选副本”").  Every rank routes every token
+ * when there is no all-to-all back end, so this counts the whole physical picture from one
+ * rank's ids.  Ids outside [0, E) and slots outside [0, num_physical) count nowhere.
+ *   topk_ids      device int32[G, k];  map: as for moe_dispatch (first_slot/num_slots unused)
+ *   num_physical  P, 1..8192
+ *   phys_count    device int64[P], accumulated with atomic adds (integer: order-free)
+ * Errors: MOE_ERR_INVALID_ARG for NULL pointers with G > 0, k outside 1..64, P outside range. */
+moe_status moe_expert_load(const int32_t* topk_ids, int64_t G, int32_t k, const moe_expert_map* map,
+                           int32_t num_physical, int64_t* phys_count, hipStream_t stream);
+
+/* moe_physical_to_logical_count -- logical_count[l, e] = sum of phys_count[l, p] over the
+ * slots p with phy2log[l, p] = e (section "统计:把物理计数还原成逻辑计数"); written in full.
+ *   phys_count device int64[L, P];  phy2log device int32[L, P] (entries outside [0, E) skipped)
+ *   logical_count device int64[L, E], E in 1..4096 */
+moe_status moe_physical_to_logical_count(const int64_t* phys_count, const int32_t* phy2log,
+                                         int32_t num_layers, int32_t num_physical,
+                                         int32_t num_logical, int64_t* logical_count,
+                                         hipStream_t stream);
+
+/* moe_eplb_balancedness -- host only.  Per layer, (mean + 1e-5) / (max + 1e-5) of the per-GPU
+ * token counts, GPU r holding the contiguous slots [r P/M, (r+1) P/M) (section "不均衡的代价
+ * 与冗余专家的思路"); 1 is perfect balance.
+ *   phys_count host int64[L, P];  out host double[L].  P must be a multiple of num_gpus. */
+moe_status moe_eplb_balancedness(const int64_t* phys_count, int32_t num_layers, int32_t num_physical,
+                                 int32_t num_gpus, double* out);
+
+/* moe_eplb_rebalance -- host only.  Hierarchical placement of E logical experts on P physical
+ * slots (section "三步算法:分组、复制、再打包"), per layer:
+ *   1. groups of E/num_groups consecutive experts are packed onto nodes by their summed load
+ *      (sums in ascending expert order), num_groups/num_nodes groups per node;
+ *   2. inside a node its experts get the node's P/num_nodes slots: one each, then each extra
+ *      slot to the expert with the largest load per replica (ties: lower position);
+ *   3. inside a node the slots are packed onto its GPUs by per-replica load (load / replica
+ *      count), P/num_gpus slots per GPU.
+ * Packing is greedy (the page describes it in words only): items heaviest first (ties: lower
+ * index), each to the lightest pack with room (ties: lower pack).  Slot numbering: node-major,
+ * then GPU, then the order the GPU received the slot.
+ *   weight     host double[L, E] loads (finite, >= 0; integer counts give results independent
+ *              of summation order)
+ *   phy2log    host int32[L, P] out: logical expert of each slot
+ *   phy_rank   host int32[L, P] out: replica index of the slot among its expert's slots
+ *   log_count  host int32[L, E] out: replicas per expert (>= 1)
+ * Errors: MOE_ERR_INVALID_ARG unless E % num_groups == 0, num_groups % num_nodes == 0,
+ * num_gpus % num_nodes == 0, P % num_gpus == 0, P/num_nodes >= E/num_nodes, and every weight
+ * is finite and >= 0. */
+moe_status moe_eplb_rebalance(const double* weight, int32_t num_layers, int32_t num_logical,
+                              int32_t num_physical, int32_t num_groups, int32_t num_nodes,
+                              int32_t num_gpus, int32_t* phy2log, int32_t* phy_rank,
+                              int32_t* log_count);
+
+/* moe_eplb_logical_to_physical -- host only.  Dispatch table of one layer's placement
+ * (section "逻辑与物理的两套映射"): phys_of[e, r] = slot of replica r of expert e, -1 past its
+ * count; n_rep[e] = its replica count.  The result is the phys_of / n_rep pair of
+ * moe_expert_map once copied to the device.
+ *   phy2log, phy_rank  host int32[P] (one layer of moe_eplb_rebalance's output)
+ *   phys_of            host int32[E, max_rep] out;  n_rep host int32[E] out
+ * Errors: MOE_ERR_CAPACITY if some replica index >= max_rep; MOE_ERR_INVALID_ARG for an entry
+ * outside [0, E), a repeated (expert, replica) pair, a gap in an expert's replica indices, or
+ * an expert with no slot.  Outputs are unspecified after an error. */
+moe_status moe_eplb_logical_to_physical(const int32_t* phy2log, const int32_t* phy_rank,
+                                        int32_t num_physical, int32_t num_logical, int32_t max_rep,
+                                        int32_t* phys_of, int32_t* n_rep);
 
 #ifdef __cplusplus
 }

@@ -16,9 +16,14 @@ pytestmark = pytest.mark.gpu
 
 
 def run_and_compare(cfg, mode="sum", align=1, cap=None, check_mode_pair=None, fp8_act="bf16"):
+    return run_and_compare_inputs(moe_synth.make_inputs(cfg), mode, align, cap, fp8_act)
+
+
+def run_and_compare_inputs(inp, mode="sum", align=1, cap=None, fp8_act="bf16"):
+    """The six steps on the GPU against the oracle on the same inputs (expert table included)."""
+    cfg = inp.cfg
     say(f"[parity] {cfg.name} tokens={cfg.num_tokens} H={cfg.hidden} I={cfg.inter} "
         f"E={cfg.num_experts} k={cfg.top_k} mode={mode} align={align} cap={cap}")
-    inp = moe_synth.make_inputs(cfg)
     ref = oracle.run_layer(inp, mode, align=align, cap=cap)
     layer = build_layer(inp, mode, align, cap, fp8_act)
     reps = replicas_to_device(inp)
