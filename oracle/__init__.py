@@ -302,6 +302,41 @@ def dispatch(ids: np.ndarray, phys_of: np.ndarray, n_rep: np.ndarray, p0: int, E
                 cap=int(cap), k=k)
 
 
+def dispatch_masked(ids: np.ndarray, phys_of: np.ndarray, n_rep: np.ndarray, p0: int, El: int,
+                    stride: int) -> dict:
+    """Fixed-capacity ("masked") plan: slot e owns rows [e * stride, (e + 1) * stride) whatever
+    the routing, as the low-latency path's pre-allocated per-expert buffers do (SGLang page,
+    section "normal 与 low-latency:一对互补的模式": a fixed maximum per expert, exceeding it is a
+    runtime error).  The slot's pairs fill its rows in ascending flat index; pairs past the
+    stride are dropped (pair_row -1) and raise error_flag; counts are the rows filled; the
+    rest of each segment is -1 in sorted_pair.  num_rows = El * stride."""
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    G, k = ids.shape
+    P = G * k
+    E = phys_of.shape[0]
+    sorted_pair = np.full(El * stride, -1, dtype=np.int32)
+    pair_row = np.full(P, -1, dtype=np.int32)
+    counts = np.zeros(El, dtype=np.int32)
+    err = 0
+    for f in range(P):
+        l = int(ids.flat[f])
+        if l < 0 or l >= E:
+            continue
+        p = int(phys_of[l, (f // k) % int(n_rep[l])]) - p0
+        if p < 0 or p >= El:
+            continue
+        if counts[p] < stride:
+            row = p * stride + int(counts[p])
+            sorted_pair[row] = f
+            pair_row[f] = row
+            counts[p] += 1
+        else:
+            err = 1
+    seg = np.arange(El + 1, dtype=np.int64) * stride
+    return dict(counts=counts, seg_offsets=seg, sorted_pair=sorted_pair, pair_row=pair_row,
+                num_rows=El * stride, error_flag=err, cap=El * stride, k=k)
+
+
 def permute_rows(global_x: np.ndarray, plan: dict) -> np.ndarray:
     """x_perm[row] = global_x[sorted_pair[row] // k]; alignment pad rows are 0."""
     sp = plan["sorted_pair"]
@@ -416,15 +451,20 @@ def token_output(inp, g: int, x_row: np.ndarray, ids_row: np.ndarray, w_row: np.
 
 # ============================================================================ whole layer
 
-def run_layer(inp, mode: str = "sum", align: int = 1, cap: Optional[int] = None) -> dict:
-    """All six steps on the inputs of one workload; returns every intermediate."""
+def run_layer(inp, mode: str = "sum", align: int = 1, cap: Optional[int] = None,
+              seg_stride: int = 0) -> dict:
+    """All six steps on the inputs of one workload; returns every intermediate.  seg_stride > 0
+    dispatches into the fixed-capacity layout (dispatch_masked) instead of packed segments."""
     cfg = inp.cfg
     dt = np.float32 if cfg.dtype == "f32" else np.uint16
     layout = gather_layout(cfg.num_tokens, mode, static_bound=cfg.static_bound)
     G = layout[1]
     gx, valid = gather(layout, inp.replicas, cfg.hidden, dt)
     logits, ids, w = route(cfg, gx, valid, inp.router_w, inp.bias)
-    plan = dispatch(ids, inp.phys_of, inp.n_rep, cfg.first_local, cfg.num_local, align, cap)
+    if seg_stride > 0:
+        plan = dispatch_masked(ids, inp.phys_of, inp.n_rep, cfg.first_local, cfg.num_local, seg_stride)
+    else:
+        plan = dispatch(ids, inp.phys_of, inp.n_rep, cfg.first_local, cfg.num_local, align, cap)
     xp = permute_rows(gx, plan)
     y = expert_ffn(xp, plan, inp)
     out = combine(y, plan, w, G, cfg.routed_scale)

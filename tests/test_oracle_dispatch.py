@@ -105,3 +105,58 @@ def test_empty_and_all_pad():
     assert plan["num_rows"] == 0 and np.all(plan["counts"] == 0)
     plan = oracle.dispatch(np.full((5, 2), -1, np.int32), phys, np.ones(E, np.int32), 0, E, 128)
     assert plan["num_rows"] == 0 and np.all(plan["pair_row"] == -1)
+
+
+# ------------------------------------------------------------------ fixed-capacity (masked) layout
+
+def _random_case(seed, G=300, k=6, E=40, El=12, p0=5, max_rep=3):
+    rng = np.random.default_rng(seed)
+    ids = np.stack([rng.choice(E, k, replace=False) for _ in range(G)]).astype(np.int32)
+    ids[::9] = -1
+    n_rep = rng.integers(1, max_rep + 1, E).astype(np.int32)
+    phys = np.full((E, max_rep), -1, np.int32)
+    pool = rng.permutation(E * max_rep)
+    c = 0
+    for e in range(E):
+        phys[e, :n_rep[e]] = pool[c:c + n_rep[e]]
+        c += n_rep[e]
+    return ids, phys, n_rep, p0, El
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_masked_layout_with_room_is_the_packed_plan_moved(seed):
+    """With a stride no slot overflows, each slot's rows are the packed plan's rows of that
+    slot (from the C counting sort), in the same order, starting at e * stride."""
+    ids, phys, n_rep, p0, El = _random_case(seed)
+    packed = oracle.dispatch(ids, phys, n_rep, p0, El)
+    stride = int(packed["counts"].max()) + 3
+    mk = oracle.dispatch_masked(ids, phys, n_rep, p0, El, stride)
+    assert mk["error_flag"] == 0 and mk["num_rows"] == El * stride
+    assert np.array_equal(mk["counts"], packed["counts"])
+    assert np.array_equal(mk["seg_offsets"], np.arange(El + 1) * stride)
+    for e in range(El):
+        a, c = int(packed["seg_offsets"][e]), int(packed["counts"][e])
+        assert np.array_equal(mk["sorted_pair"][e * stride:e * stride + c], packed["sorted_pair"][a:a + c])
+        assert np.all(mk["sorted_pair"][e * stride + c:(e + 1) * stride] == -1)
+    # pair_row inverts sorted_pair
+    for f in np.nonzero(mk["pair_row"] >= 0)[0]:
+        assert mk["sorted_pair"][mk["pair_row"][f]] == f
+    assert np.array_equal(mk["pair_row"] >= 0, packed["pair_row"] >= 0)
+
+
+@pytest.mark.parametrize("stride", [1, 4, 9])
+def test_masked_layout_overflow_keeps_the_first_pairs(stride):
+    """A slot over capacity keeps its stride lowest flat indices (brute force on the packed
+    plan's per-slot lists) and raises the flag; everything else is dropped."""
+    ids, phys, n_rep, p0, El = _random_case(11)
+    packed = oracle.dispatch(ids, phys, n_rep, p0, El)
+    mk = oracle.dispatch_masked(ids, phys, n_rep, p0, El, stride)
+    assert mk["error_flag"] == int(packed["counts"].max() > stride)
+    assert np.array_equal(mk["counts"], np.minimum(packed["counts"], stride))
+    kept = set()
+    for e in range(El):
+        a, c = int(packed["seg_offsets"][e]), int(packed["counts"][e])
+        lst = packed["sorted_pair"][a:a + c][:stride]
+        kept |= set(lst.tolist())
+        assert np.array_equal(mk["sorted_pair"][e * stride:e * stride + len(lst)], lst)
+    assert set(np.nonzero(mk["pair_row"] >= 0)[0].tolist()) == kept
