@@ -94,7 +94,7 @@ def eplb_cycle(cfg, inp, layer, reps, args, dev, act):
     torch.cuda.empty_cache()
     w2 = DeviceWeights(inp2, dev, fp8_act=args.fp8_act)
     layer2 = MoELayer(spec_of(cfg2), w2, cfg2.num_tokens, act, mode=args.mode,
-                      static_bound=cfg2.static_bound, device=dev)
+                      static_bound=cfg2.static_bound, device=dev, seg_stride=args.seg_stride)
     layer2.gather(reps)
     layer2.route()
     new = torch.zeros(EPLB["P"], dtype=torch.int64, device=dev)
@@ -201,6 +201,9 @@ def main():
     ap.add_argument("--entry", action="store_true",
                     help="run the fused entry step (residual add + RMSNorm + gather) in the step "
                          "in place of the plain gather; without it the fused step is timed apart")
+    ap.add_argument("--seg-stride", type=int, default=0, metavar="ROWS",
+                    help="dispatch into the fixed-capacity layout, ROWS rows per local slot (the "
+                         "global row count never overflows); 0: packed segments")
     ap.add_argument("--eplb", action="store_true",
                     help="skewed workload: count one step's expert load under the workload's own "
                          "slot table, place the experts with the library (288 slots, 8 groups, "
@@ -237,7 +240,7 @@ def main():
     act = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
     w = DeviceWeights(inp, dev, fp8_act=args.fp8_act)
     layer = MoELayer(spec_of(cfg), w, cfg.num_tokens, act, mode=args.mode,
-                     static_bound=cfg.static_bound, device=dev)
+                     static_bound=cfg.static_bound, device=dev, seg_stride=args.seg_stride)
     bf = cfg.dtype == "bf16"
     reps = []
     for r in inp.replicas:
@@ -414,6 +417,8 @@ def main():
         "config": {"workload": WORKLOAD_TEXT[args.workload], "name": cfg.name,
                    "launch": "one HIP graph per step" if args.graph else "eager calls",
                    "first_step": "fused residual add + RMSNorm + gather" if args.entry else "plain gather",
+                   "dispatch_layout": (f"fixed capacity, {args.seg_stride} rows per slot" if args.seg_stride
+                                       else "packed segments"),
                    "tokens": T, "global_rows": G, "gather_mode": args.mode,
                    "routed_local_pairs": R, "parallelism": "one EP rank's share on 1 GPU",
                    **({"placement": eplb_info} if eplb_info is not None else {})},

@@ -229,9 +229,10 @@ class PlanBuffers:
     """Device buffers of one dispatch plan (torch-allocated) and the C struct over them."""
 
     def __init__(self, G: int, k: int, num_slots: int, align: int = 1, cap: Optional[int] = None,
-                 device="cuda"):
+                 device="cuda", seg_stride: int = 0):
+        """seg_stride > 0 selects the fixed-capacity layout (slot e at rows e * seg_stride)."""
         if cap is None:
-            cap = G * min(k, num_slots) + num_slots * (align - 1)
+            cap = num_slots * seg_stride if seg_stride > 0 else G * min(k, num_slots) + num_slots * (align - 1)
         i32, i64 = torch.int32, torch.int64
         self.counts = torch.zeros(num_slots, dtype=i32, device=device)
         self.seg_offsets = torch.zeros(num_slots + 1, dtype=i64, device=device)
@@ -240,9 +241,10 @@ class PlanBuffers:
         self.num_rows = torch.zeros(1, dtype=i64, device=device)
         self.error_flag = torch.zeros(1, dtype=i32, device=device)
         self.cap, self.G, self.k, self.num_slots, self.align = cap, G, k, num_slots, align
+        self.seg_stride = seg_stride
         self.struct = Plan(_ptr(self.counts), _ptr(self.seg_offsets), _ptr(self.sorted_pair),
                            _ptr(self.pair_row), _ptr(self.num_rows), _ptr(self.error_flag),
-                           cap, G, k, num_slots, align, 0)
+                           cap, G, k, num_slots, align, seg_stride)
 
 
 def moe_dispatch_workspace_size(G: int, k: int, num_slots: int) -> int:

@@ -37,7 +37,7 @@ class ExpertMap(ctypes.Structure):
 class Plan(ctypes.Structure):
     _fields_ = [("counts", c_vp), ("seg_offsets", c_vp), ("sorted_pair", c_vp), ("pair_row", c_vp),
                 ("num_rows", c_vp), ("error_flag", c_vp), ("cap", c_i64), ("G", c_i64),
-                ("top_k", c_i32), ("num_slots", c_i32), ("align", c_i32), ("reserved", c_i32)]
+                ("top_k", c_i32), ("num_slots", c_i32), ("align", c_i32), ("seg_stride", c_i32)]
 
 
 class ExpertWeights(ctypes.Structure):

@@ -74,24 +74,38 @@ __global__ __launch_bounds__(D_THREADS) void count_kernel(const int32_t* __restr
 
 constexpr int SCAN_THREADS = 1024;
 
+// stride > 0: fixed-capacity layout, slot e owns rows [e * stride, (e + 1) * stride) and keeps
+// at most stride pairs; stride == 0: packed segments of the counts rounded up to align.
 __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(
-    const int32_t* __restrict__ blk_counts, int64_t NB, int El, int align, int64_t cap,
-    int32_t* __restrict__ blk_base, int32_t* __restrict__ counts, int64_t* __restrict__ seg,
-    int64_t* __restrict__ num_rows, int32_t* __restrict__ error_flag,
+    const int32_t* __restrict__ blk_counts, int64_t NB, int El, int align, int64_t stride,
+    int64_t cap, int32_t* __restrict__ blk_base, int32_t* __restrict__ counts,
+    int64_t* __restrict__ seg, int64_t* __restrict__ num_rows, int32_t* __restrict__ error_flag,
     int32_t* __restrict__ sorted_pair) {
     __shared__ int64_t sc[SCAN_THREADS];
+    __shared__ int32_t kept[kMaxSlots];
+    __shared__ int32_t over;
     const int e = threadIdx.x;
+    if (e == 0) over = 0;
+    __syncthreads();
     int64_t padded = 0;
-    int32_t total = 0;
     if (e < El) {
         int32_t run = 0;
         for (int64_t b = 0; b < NB; ++b) {
             blk_base[b * El + e] = run;
             run += blk_counts[b * El + e];
         }
-        total = run;
-        counts[e] = run;
-        padded = (static_cast<int64_t>(run) + align - 1) / align * align;
+        int32_t keep = run;
+        if (stride > 0) {
+            if (run > stride) {
+                keep = static_cast<int32_t>(stride);
+                over = 1;
+            }
+            padded = stride;
+        } else {
+            padded = (static_cast<int64_t>(run) + align - 1) / align * align;
+        }
+        counts[e] = keep;
+        kept[e] = keep;
     }
     // inclusive scan of the padded counts over slots (Hillis-Steele in LDS)
     sc[e] = padded;
@@ -103,16 +117,20 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(
         __syncthreads();
     }
     if (e < El) {
-        const int64_t end = sc[e];
-        const int64_t start = end - padded;
-        seg[e + 1] = end;
+        seg[e + 1] = sc[e];
         if (e == 0) seg[0] = 0;
-        // alignment pad rows hold no pair
-        for (int64_t r = start + total; r < end && r < cap; ++r) sorted_pair[r] = -1;
-        if (e == El - 1) {
-            *num_rows = end;
-            *error_flag = end > cap ? 1 : 0;
-        }
+    }
+    // rows of a segment past its pairs (alignment pad, or unused capacity) hold no pair; the
+    // whole block fills them segment by segment
+    for (int q = 0; q < El; ++q) {
+        const int64_t end = sc[q];
+        const int64_t start = (q == 0 ? 0 : sc[q - 1]) + kept[q];
+        for (int64_t r = start + e; r < end && r < cap; r += SCAN_THREADS) sorted_pair[r] = -1;
+    }
+    if (e == 0) {
+        const int64_t end = sc[El - 1];
+        *num_rows = end;
+        *error_flag = (end > cap || over) ? 1 : 0;
     }
 }
 
@@ -120,6 +138,8 @@ __global__ __launch_bounds__(D_THREADS) void place_kernel(
     const int32_t* __restrict__ ids, int64_t P, int k, MapArgs m,
     const int32_t* __restrict__ blk_base, const int64_t* __restrict__ seg, int64_t cap,
     int32_t* __restrict__ sorted_pair, int32_t* __restrict__ pair_row) {
+    // a pair's row must also stay inside its slot's segment: in the fixed-capacity layout the
+    // pairs past the capacity are dropped; packed segments always have room
     __shared__ int32_t whist[D_WAVES][kMaxSlots];
     __shared__ int64_t wbase[D_WAVES][kMaxSlots];
     const int wv = threadIdx.x / kWave;
@@ -166,7 +186,7 @@ __global__ __launch_bounds__(D_THREADS) void place_kernel(
         // the lowest lane of each slot advances the wave's running row for it
         if (s >= 0 && (mine & below) == 0) wbase[wv][s] += __popcll(mine);
         if (inb) {
-            if (row >= 0 && row < cap) {
+            if (row >= 0 && row < cap && row < seg[s + 1]) {
                 sorted_pair[row] = static_cast<int32_t>(f);
                 pair_row[f] = static_cast<int32_t>(row);
             } else {
@@ -180,7 +200,7 @@ template <typename V>
 __global__ __launch_bounds__(D_THREADS) void permute_kernel(
     const V* __restrict__ x, const int32_t* __restrict__ sorted_pair,
     const int64_t* __restrict__ num_rows, int64_t cap, int k, int64_t row_units,
-    V* __restrict__ x_perm) {
+    bool zero_pads, V* __restrict__ x_perm) {
     int64_t rows = *num_rows;
     rows = rows < cap ? rows : cap;
     const int lane = lane_id();
@@ -200,7 +220,7 @@ __global__ __launch_bounds__(D_THREADS) void permute_kernel(
                 d[c + 3 * kWave] = v3;
             }
             for (; c < row_units; c += kWave) d[c] = s[c];
-        } else {
+        } else if (zero_pads) {  // alignment pad rows; unused capacity rows stay unwritten
             for (int64_t c = lane; c < row_units; c += kWave) d[c] = V{};
         }
     }
@@ -214,7 +234,7 @@ moe_status launch_permute(const void* x, const moe_plan* plan, int64_t row_bytes
     if (blocks > 2048) blocks = 2048;
     hipLaunchKernelGGL(permute_kernel<V>, dim3(static_cast<unsigned>(blocks)), dim3(D_THREADS), 0,
                        stream, static_cast<const V*>(x), plan->sorted_pair, plan->num_rows,
-                       plan->cap, plan->top_k, row_units, static_cast<V*>(x_perm));
+                       plan->cap, plan->top_k, row_units, plan->seg_stride == 0, static_cast<V*>(x_perm));
     MOE_LAUNCH_CHECK();
     return MOE_OK;
 }
@@ -243,7 +263,11 @@ extern "C" moe_status moe_dispatch(const void* global_x, const int32_t* topk_ids
     MOE_CHECK_ARG(map->num_slots >= 1 && map->num_slots <= kMaxSlots);
     MOE_CHECK_ARG(map->num_logical >= 1 && map->first_slot >= 0);
     MOE_CHECK_ARG(map->phys_of == nullptr || (map->n_rep != nullptr && map->max_rep >= 1));
-    MOE_CHECK_ARG(plan->align >= 1 && plan->cap >= 0);
+    MOE_CHECK_ARG(plan->align >= 1 && plan->cap >= 0 && plan->seg_stride >= 0);
+    // fixed-capacity layout: every segment inside the caller's rows, row indices in int32
+    if (plan->seg_stride > 0)
+        MOE_CHECK_ARG(plan->seg_stride <= (int64_t(1) << 31) / map->num_slots &&
+                      plan->cap >= static_cast<int64_t>(map->num_slots) * plan->seg_stride);
     MOE_CHECK_ARG(plan->counts && plan->seg_offsets && plan->num_rows && plan->error_flag);
     MOE_CHECK_ARG(G * k < (int64_t(1) << 31));
     if (G > 0) MOE_CHECK_ARG(topk_ids && plan->pair_row && global_x);
@@ -262,7 +286,8 @@ extern "C" moe_status moe_dispatch(const void* global_x, const int32_t* topk_ids
         MOE_LAUNCH_CHECK();
     }
     hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(SCAN_THREADS), 0, stream, blk_counts, NB, El,
-                       plan->align, plan->cap, blk_base, plan->counts, plan->seg_offsets,
+                       plan->align, static_cast<int64_t>(plan->seg_stride), plan->cap, blk_base,
+                       plan->counts, plan->seg_offsets,
                        plan->num_rows, plan->error_flag, plan->sorted_pair);
     MOE_LAUNCH_CHECK();
     if (NB == 0) return MOE_OK;

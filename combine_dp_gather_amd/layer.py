@@ -85,7 +85,7 @@ class MoELayer:
     def __init__(self, spec: LayerSpec, weights: DeviceWeights, num_tokens: Sequence[int],
                  act_dtype: torch.dtype, mode: str = "auto", static_bound: int = 0,
                  is_extend: bool = False, align: int = 1, cap: Optional[int] = None,
-                 device="cuda"):
+                 device="cuda", seg_stride: int = 0):
         self.spec, self.w, self.device, self.dt = spec, weights, device, act_dtype
         self.layout = moe_gather_layout(num_tokens, mode, is_extend=is_extend,
                                         static_bound=static_bound)
@@ -105,7 +105,8 @@ class MoELayer:
         self.route_ws = (torch.empty(route_ws, dtype=torch.uint8, device=device) if route_ws else None)
         self.emap = make_expert_map(spec.num_experts, spec.first_local, spec.num_local,
                                     weights.phys_of, weights.n_rep)
-        self.plan = PlanBuffers(G, k, spec.num_local, align, cap, device)
+        # seg_stride > 0: fixed-capacity layout, every slot's rows at a fixed address
+        self.plan = PlanBuffers(G, k, spec.num_local, align, cap, device, seg_stride)
         cap = self.plan.cap
         self.dispatch_ws = torch.empty(max(moe_dispatch_workspace_size(G, k, spec.num_local), 16),
                                        dtype=torch.uint8, device=device)

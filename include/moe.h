@@ -227,21 +227,33 @@ typedef struct {
  * choice on every rank (rank_invariant).  With phys_of == NULL the map is the identity
  * (slot l holds logical l). */
 
+/* Two segment layouts.  Packed (seg_stride == 0, the normal dispatch of the SGLang page,
+ * section "normal dispatch 的调用链"): segments back to back, each counts[e] rounded up to
+ * align rows, so addresses depend on the routing.  Fixed capacity (seg_stride > 0, the
+ * low-latency path's pre-allocated per-expert buffers of section "normal 与 low-latency:一对
+ * 互补的模式"): slot e always owns rows [e*seg_stride, (e+1)*seg_stride), the masked
+ * [E_l, seg_stride, H] layout; only the counts depend on the routing, and pairs past a slot's
+ * capacity are dropped with error_flag set (the page: exceeding the fixed maximum is a
+ * runtime error).  seg_stride = G can never overflow (a token picks a slot at most once). */
 typedef struct {
-    int32_t* counts;        /* device int32[E_l]: pairs per local slot */
-    int64_t* seg_offsets;   /* device int64[E_l+1]: segment e is rows [seg[e], seg[e+1]),
-                               seg[e+1] - seg[e] = counts[e] rounded up to align */
+    int32_t* counts;        /* device int32[E_l]: pairs per local slot (fixed capacity: kept
+                               pairs, <= seg_stride) */
+    int64_t* seg_offsets;   /* device int64[E_l+1]: segment e is rows [seg[e], seg[e+1]);
+                               packed: seg[e+1] - seg[e] = counts[e] rounded up to align;
+                               fixed capacity: seg[e] = e*seg_stride */
     int32_t* sorted_pair;   /* device int32[cap]: flat pair index f = g*k + j of each row,
-                               ascending f inside a segment; -1 on alignment pad rows */
+                               ascending f inside a segment; -1 on rows past a segment's pairs */
     int32_t* pair_row;      /* device int32[G*k]: row of pair f, -1 if not local (or dropped) */
     int64_t* num_rows;      /* device int64[1]: seg[E_l] */
-    int32_t* error_flag;    /* device int32[1]: 1 if num_rows > cap (rows >= cap are dropped) */
-    int64_t cap;            /* rows of sorted_pair / x_perm / y_perm */
+    int32_t* error_flag;    /* device int32[1]: 1 if num_rows > cap (rows >= cap are dropped),
+                               or, with fixed capacity, if some slot had more than seg_stride pairs */
+    int64_t cap;            /* rows of sorted_pair / x_perm / y_perm (fixed capacity: >= E_l*seg_stride) */
     int64_t G;              /* global rows */
     int32_t top_k;          /* k */
     int32_t num_slots;      /* E_l */
-    int32_t align;          /* segment alignment in rows (>= 1; 128 matches the grouped GEMM tile) */
-    int32_t reserved;
+    int32_t align;          /* packed segment alignment in rows (>= 1; 128 matches the grouped
+                               GEMM tile); ignored with fixed capacity */
+    int32_t seg_stride;     /* 0: packed segments; > 0: fixed capacity per slot, in rows */
 } moe_plan;
 
 /* Device workspace (bytes) moe_dispatch needs for G rows, k picks and E_l slots. */
@@ -251,9 +263,11 @@ size_t moe_dispatch_workspace_size(int64_t G, int32_t k, int32_t num_slots);
  *   global_x  device [G, H] dt;  topk_ids device int32[G, k] (ids outside [0, E) are skipped)
  *   map       expert map (see above); plan: caller buffers, filled here
  *   x_perm    device [cap, H] dt: row r = global_x[sorted_pair[r] / k]; alignment pad rows 0;
- *             rows >= num_rows are not written
+ *             rows >= num_rows are not written, nor (fixed capacity) the unused rows of a
+ *             segment past its counts[e] pairs
  *   workspace device, >= moe_dispatch_workspace_size(G, k, E_l) bytes, 16-byte aligned
- * cap >= G*min(k, E_l) + E_l*(align-1) can never overflow. */
+ * Packed: cap >= G*min(k, E_l) + E_l*(align-1) can never overflow.  Fixed capacity: cap must
+ * be >= E_l*seg_stride (else MOE_ERR_INVALID_ARG), and E_l*seg_stride < 2^31. */
 moe_status moe_dispatch(const void* global_x, const int32_t* topk_ids, int64_t G, int32_t k,
                         int64_t H, moe_dtype dt, const moe_expert_map* map, const moe_plan* plan,
                         void* x_perm, void* workspace, size_t workspace_bytes, hipStream_t stream);

@@ -53,10 +53,10 @@ def resized(name, tokens, **kw):
     return replace(cfg, num_tokens=tuple(tokens), static_bound=0, name=f"{name}-{len(tokens)}r", **kw)
 
 
-def build_layer(inp, mode="sum", align=1, cap=None, fp8_act="bf16"):
+def build_layer(inp, mode="sum", align=1, cap=None, fp8_act="bf16", seg_stride=0):
     from combine_dp_gather_amd.layer import DeviceWeights, MoELayer, spec_of
     cfg = inp.cfg
     w = DeviceWeights(inp, fp8_act=fp8_act)
     layer = MoELayer(spec_of(cfg), w, cfg.num_tokens, act_dtype(cfg), mode=mode,
-                     static_bound=cfg.static_bound, align=align, cap=cap)
+                     static_bound=cfg.static_bound, align=align, cap=cap, seg_stride=seg_stride)
     return layer

@@ -193,3 +193,16 @@ def test_entry_gather_argument_errors(m):
     assert call(ctypes.byref(L), hs, hs, fake, 1e-6, rv=None) == E
     L0 = m.moe_gather_layout([0, 0], "max")
     assert call(ctypes.byref(L0), none2, none2, None, 1e-6, gx=None, rv=None) == _lib.MOE_OK
+
+
+def test_fixed_capacity_plan_errors(m):
+    """A fixed-capacity plan needs cap >= E_l * seg_stride and a non-negative stride."""
+    from combine_dp_gather_amd import _lib
+    lib = m.lib()
+    fake = 4096
+    emap = m.make_expert_map(16, 0, 4)
+    ws = (ctypes.c_uint8 * 64)()
+    for stride, cap in [(-1, 100), (8, 31), (1 << 30, 1 << 40)]:
+        plan = _lib.Plan(fake, fake, fake, fake, fake, fake, cap, 3, 2, 4, 1, stride)
+        assert lib.moe_dispatch(fake, fake, 3, 2, 16, _lib.MOE_BF16, ctypes.byref(emap), ctypes.byref(plan),
+                                fake, ws, 64, None) == _lib.MOE_ERR_INVALID_ARG

@@ -15,17 +15,18 @@ from gpu_helpers import (build_layer, replicas_to_device, resized, say, to_np, t
 pytestmark = pytest.mark.gpu
 
 
-def run_and_compare(cfg, mode="sum", align=1, cap=None, check_mode_pair=None, fp8_act="bf16"):
-    return run_and_compare_inputs(moe_synth.make_inputs(cfg), mode, align, cap, fp8_act)
+def run_and_compare(cfg, mode="sum", align=1, cap=None, check_mode_pair=None, fp8_act="bf16", seg_stride=0):
+    return run_and_compare_inputs(moe_synth.make_inputs(cfg), mode, align, cap, fp8_act, seg_stride)
 
 
-def run_and_compare_inputs(inp, mode="sum", align=1, cap=None, fp8_act="bf16"):
-    """The six steps on the GPU against the oracle on the same inputs (expert table included)."""
+def run_and_compare_inputs(inp, mode="sum", align=1, cap=None, fp8_act="bf16", seg_stride=0):
+    """The six steps on the GPU against the oracle on the same inputs (expert table included).
+    seg_stride > 0: the fixed-capacity dispatch layout on both sides."""
     cfg = inp.cfg
     say(f"[parity] {cfg.name} tokens={cfg.num_tokens} H={cfg.hidden} I={cfg.inter} "
-        f"E={cfg.num_experts} k={cfg.top_k} mode={mode} align={align} cap={cap}")
-    ref = oracle.run_layer(inp, mode, align=align, cap=cap)
-    layer = build_layer(inp, mode, align, cap, fp8_act)
+        f"E={cfg.num_experts} k={cfg.top_k} mode={mode} align={align} cap={cap} seg_stride={seg_stride}")
+    ref = oracle.run_layer(inp, mode, align=align, cap=cap, seg_stride=seg_stride)
+    layer = build_layer(inp, mode, align, cap, fp8_act, seg_stride)
     reps = replicas_to_device(inp)
     layer.forward(reps)
     torch.cuda.synchronize()
@@ -52,7 +53,12 @@ def run_and_compare_inputs(inp, mode="sum", align=1, cap=None, fp8_act="bf16"):
     rows = min(rp["num_rows"], rp["cap"])
     assert np.array_equal(to_np(plan.sorted_pair)[:rows], rp["sorted_pair"])
     assert np.array_equal(to_np(plan.pair_row)[:G * cfg.top_k], rp["pair_row"])
-    assert np.array_equal(to_np(layer.x_perm)[:rows], ref["x_perm"])
+    xp_gpu = to_np(layer.x_perm)[:rows]
+    if seg_stride:  # fixed capacity: rows past a segment's pairs are never written
+        used = rp["sorted_pair"] >= 0
+        assert np.array_equal(xp_gpu[used], ref["x_perm"][used])
+    else:
+        assert np.array_equal(xp_gpu, ref["x_perm"])
     # S4 experts: real rows of every segment
     tol = tol_for(cfg)
     real = np.zeros(rows, dtype=bool)
@@ -270,3 +276,14 @@ def test_route_from_logits_ties_and_fake_balance():
     ref_ids, ref_w = oracle.select_softmax(lg, 6, True)
     assert np.array_equal(ids.cpu().numpy(), ref_ids)
     assert oracle.rel_err(w.cpu().numpy(), ref_w) < 1e-5
+
+
+@pytest.mark.parametrize("name,stride", [("cfg3", 384), ("cfg3", 8), ("cfg2", 170), ("cfg2", 5)])
+def test_fixed_capacity_layout(name, stride):
+    """The masked layout: slot e's rows at e * stride.  stride = G never overflows (decode:
+    16 replicas x the static bound 24; the DP-gather workload: 170 rows); the small strides
+    overflow, drop the late pairs and raise the flag, on both sides alike."""
+    layer, ref = run_and_compare(moe_synth.CONFIGS[name], "sum", seg_stride=stride)
+    flag = int(to_np(layer.plan.error_flag)[0])
+    say(f"  fixed capacity {stride}: error_flag {flag}, counts {to_np(layer.plan.counts).tolist()[:8]}...")
+    assert flag == (1 if stride < 20 else 0)
