@@ -204,6 +204,10 @@ def main():
     ap.add_argument("--seg-stride", type=int, default=0, metavar="ROWS",
                     help="dispatch into the fixed-capacity layout, ROWS rows per local slot (the "
                          "global row count never overflows); 0: packed segments")
+    ap.add_argument("--tbo", action="store_true",
+                    help="run each step as two micro-batches (each replica's tokens halved) on two "
+                         "streams, pipelined by stages; the per-call breakdown comes from "
+                         "single-batch steps run after the timed ones")
     ap.add_argument("--eplb", action="store_true",
                     help="skewed workload: count one step's expert load under the workload's own "
                          "slot table, place the experts with the library (288 slots, 8 groups, "
@@ -288,11 +292,34 @@ def main():
     overflow = int(layer.plan.error_flag.item())
     log(f"[bench] warmup done; routed local pairs R={R} overflow={overflow}")
 
+    tbo = None
+    if args.tbo:
+        from combine_dp_gather_amd.layer import TwoBatchOverlap
+        if args.entry or eplb_info is not None:
+            raise SystemExit("--tbo runs the plain six-call step only")
+        tbo = TwoBatchOverlap(spec_of(cfg), w, layer.sizes, act, mode=args.mode, device=dev,
+                              seg_stride=args.seg_stride)
+        for _ in range(args.warmup):
+            tbo.forward(reps)
+        torch.cuda.synchronize()
+
+    def whole_step():
+        if tbo is not None:
+            tbo.forward(reps)
+        else:
+            step()
+
     graph = None
     if args.graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            whole_step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            step()
+            whole_step()
         for _ in range(args.warmup):
             graph.replay()
         torch.cuda.synchronize()
@@ -307,14 +334,16 @@ def main():
     for s in range(args.steps):
         if graph is not None:
             graph.replay()
+        elif tbo is not None:
+            tbo.forward(reps)
         else:
             step(ev[s])
     stop.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
     total_ms = start.elapsed_time(stop)
-    if graph is not None:
-        # the per-call breakdown comes from eager steps after the timed replays
+    if graph is not None or tbo is not None:
+        # the per-call breakdown comes from eager single-batch steps after the timed ones
         for s in range(args.steps):
             step(ev[s])
         torch.cuda.synchronize()
@@ -416,6 +445,8 @@ def main():
         "data": "synthetic (seeded PCG64; random-init DeepSeek-V3-shaped expert weights)",
         "config": {"workload": WORKLOAD_TEXT[args.workload], "name": cfg.name,
                    "launch": "one HIP graph per step" if args.graph else "eager calls",
+                   "micro_batches": ("2, each replica halved, two streams pipelined by stages" if args.tbo
+                                     else "1"),
                    "first_step": "fused residual add + RMSNorm + gather" if args.entry else "plain gather",
                    "dispatch_layout": (f"fixed capacity, {args.seg_stride} rows per slot" if args.seg_stride
                                        else "packed segments"),

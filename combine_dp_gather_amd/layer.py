@@ -162,8 +162,8 @@ class MoELayer:
         if self.G:
             moe_combine(self.y_perm, self.plan, self.topk_w, self.spec.routed_scale, self.out)
 
-    def scatter(self):
-        moe_scatter(self.layout, self.out, self.replicas_out)
+    def scatter(self, replicas_out=None):
+        moe_scatter(self.layout, self.out, self.replicas_out if replicas_out is None else replicas_out)
 
     def forward(self, replicas, entry=None) -> List[torch.Tensor]:
         """One step.  ``entry = (residual, norm_weight, eps)`` runs the fused entry step on
@@ -177,4 +177,74 @@ class MoELayer:
         self.experts()
         self.combine()
         self.scatter()
+        return self.replicas_out
+
+
+def split_micro_batches(num_tokens: Sequence[int]) -> List[List[tuple]]:
+    """Two micro-batches of one step: each replica's tokens cut at half their count.
+
+    The two-batch-overlap split of the SGLang page (section "Two-batch Overlap:把通信藏进另一个
+    micro-batch 的计算里", compute_split_seq_index): decode batches split at half the token
+    count (one token per sequence), and a prefill batch whose boundary split is unbalanced
+    falls back to cutting a sequence at half the tokens.  The replicas here carry no sequence
+    structure, so every replica is cut at n // 2: micro-batch 0 takes rows [0, n // 2) of
+    each replica, micro-batch 1 the rest (the vLLM page's UBatchSlice token slices).
+    Returns [[(start, stop) per replica] for each micro-batch]."""
+    return [[(0, n // 2) for n in num_tokens], [(n // 2, n) for n in num_tokens]]
+
+
+class TwoBatchOverlap:
+    """One step as two micro-batches on two streams, software-pipelined by stages.
+
+    Each micro-batch runs the six calls on its own buffers (a MoELayer of its shape; weights
+    shared) and on its own stream (both at the default priority).  The calls are grouped in
+    stages, split where the pages put their yield points (after dispatch, after the experts):
+        stage 0: gather, route, dispatch      stage 1: expert GEMMs      stage 2: combine, scatter
+    Micro-batch 1's stage s waits for micro-batch 0's stage s (an event), so on the GPU
+    micro-batch 1's memory-bound stage 0 runs beside micro-batch 0's GEMMs, and its GEMMs
+    beside micro-batch 0's combine and scatter (the delayed start of the pages' decode
+    schedule, one stage deep).  The host only issues work; nothing synchronises it.
+
+    Every per-token result of the path is independent of which tokens share the batch (the
+    gate's order is defined per row, expert rows do not interact, combine sums per token), so
+    the replica outputs equal the single-batch step's bit for bit."""
+
+    STAGES = (("gather", "route", "dispatch"), ("experts",), ("combine", "scatter"))
+
+    def __init__(self, spec: LayerSpec, weights: DeviceWeights, num_tokens: Sequence[int],
+                 act_dtype: torch.dtype, mode: str = "sum", device="cuda", seg_stride: int = 0):
+        self.num_tokens = [int(n) for n in num_tokens]
+        self.slices = split_micro_batches(self.num_tokens)
+        self.layers = [MoELayer(spec, weights, [b - a for a, b in sl], act_dtype, mode=mode, device=device,
+                                seg_stride=seg_stride) for sl in self.slices]
+        H = spec.hidden
+        self.replicas_out = [torch.empty((n, H), dtype=act_dtype, device=device) for n in self.num_tokens]
+        self.side = torch.cuda.Stream(device=device)
+        self.events = [[torch.cuda.Event() for _ in self.STAGES] for _ in range(2)]
+
+    def _stage(self, mb: int, s: int, ins, outs):
+        layer = self.layers[mb]
+        for op in self.STAGES[s]:
+            if op == "gather":
+                layer.gather(ins)
+            elif op == "scatter":
+                layer.scatter(outs)
+            else:
+                getattr(layer, op)()
+
+    def forward(self, replicas) -> List[torch.Tensor]:
+        main = torch.cuda.current_stream()
+        ins = [[r[a:b] for r, (a, b) in zip(replicas, sl)] for sl in self.slices]
+        outs = [[y[a:b] for y, (a, b) in zip(self.replicas_out, sl)] for sl in self.slices]
+        streams = (main, self.side)
+        self.side.wait_stream(main)            # inputs written before the step are visible
+        for s in range(len(self.STAGES)):
+            with torch.cuda.stream(streams[0]):
+                self._stage(0, s, ins[0], outs[0])
+                self.events[0][s].record(streams[0])
+            with torch.cuda.stream(streams[1]):
+                streams[1].wait_event(self.events[0][s])
+                self._stage(1, s, ins[1], outs[1])
+                self.events[1][s].record(streams[1])
+        main.wait_event(self.events[1][-1])    # the step ends when both micro-batches have
         return self.replicas_out
