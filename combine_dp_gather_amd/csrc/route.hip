@@ -6,10 +6,8 @@
 // section "推理时怎么“选副本”" zeroes) and plain softmax top-k.
 //
 // Exact-order gate.  The integer routing decision depends on the logits bit for bit, so
-// the gate fixes one accumulation order: per (row, expert) an fp32 fma chain over h in
-// ascending order from +0.  The kernel is a register-tiled fp32 FMA GEMM whose K loop runs
-// in that order: a 128x128 output tile per 256-thread block, 8x8 outputs per thread, 32-deep
-// K slices staged through LDS as fp32 (bf16 widened exactly), double-buffered.
+// the gate fixes one accumulation order (below) and runs it on the fp32 matrix cores, with
+// 32-deep K slices staged through LDS as fp32 (bf16 widened exactly), double-buffered.
 #include <float.h>
 
 #include "gemm_common.h"
@@ -29,11 +27,13 @@ namespace {
 // sequential fma chain, and shown to differ from a single-rounding pair, on bf16-valued and
 // full fp32 operands).  Lanes 0-31 therefore carry the even k of each pair and lanes 32-63
 // the odd k; LDS keeps every row's slice split by parity (evens, then odds) so that one
-// 16-byte read gives a lane its operands for four consecutive instructions.  A wave owns 64
-// rows x 128 experts as eight 32x32 chains (2 row blocks x 4 expert blocks).
-//   - large batches: a block of 128 rows x 256 experts (x read from HBM once) walks all of
-//     h in 32-wide slices, prefetching across chunk boundaries; after a chunk's last slice
-//     its sums are added to the running total and the chains restart from +0;
+// 16-byte read gives a lane its operands for four consecutive instructions.  A wave owns
+// 32*RB rows x 128 experts as 4*RB 32x32 chains (RB row blocks x 4 expert blocks).
+//   - large batches: a block of 64*RB rows x 256 experts (x read from HBM once) walks all
+//     of h in 32-wide slices, prefetching across chunk boundaries; after a chunk's last slice
+//     its sums are added to the running total and the chains restart from +0.  RB = 1 (64
+//     rows) when those blocks fit in one round on the CUs, else RB = 2 (128 rows), so a
+//     batch of half the prefill size still fills the chip;
 //   - small batches: one block per (row tile, expert tile, chunk) writes the chunk's sums to
 //     a workspace and a reduction adds them left to right -- chunks run in parallel, so the
 //     latency is one chunk's chain, not the whole row's.
@@ -84,16 +84,17 @@ __device__ __forceinline__ uint4 load_piece(const T* __restrict__ src, int64_t r
 
 typedef unsigned int gate_u32x4 __attribute__((ext_vector_type(4)));
 
-// Staging of one slice: x rows [m0, m0+128) and w rows [n0, n0+256), columns k0 .. k0+GB_K,
+// Staging of one slice: x rows [m0, m0+BM) and w rows [n0, n0+256), columns k0 .. k0+GB_K,
 // in LDS as [row][k] with row stride LD.  The fast load is a 16-byte buffer load per piece
 // from a descriptor over the block's rows only, so rows past G (or E) read as zeros; the
 // element-wise load covers a slice that runs past H and unaligned inputs.
-template <typename T>
+template <typename T, int BM = GB_M>
 struct GateStage {
     static constexpr int C = GateIO<T>::kChunk;
     static constexpr int LD = GB_K + G_PAD;
     static constexpr int PER_ROW = GB_K / C;  // 16-byte pieces per row
-    static constexpr int XCH = GB_M * PER_ROW / G_THREADS;
+    static constexpr int XCH = BM * PER_ROW / G_THREADS;
+    static constexpr int WRITES = (XCH + GB_N * PER_ROW / G_THREADS) * 2;  // LDS stores per thread
     static constexpr int WCH = GB_N * PER_ROW / G_THREADS;
     uint4 xr[XCH], wr[WCH];
     __device__ void load_fast(__amdgpu_buffer_rsrc_t rx, __amdgpu_buffer_rsrc_t rw,
@@ -159,23 +160,24 @@ struct GateStage {
 // adds, so they stay in the accumulator registers; with TOTAL the chunk's sums are then
 // added to `total`, else (a single chunk) they are left in acc.  `fast` (block-uniform): the
 // inputs are 16-byte aligned with rows a multiple of 16 bytes.
-template <typename T, bool TOTAL>
+template <typename T, bool TOTAL, int RB = 2>
 __device__ __forceinline__ void gate_chunks(const T* x, const T* w, int64_t G, int64_t E, int64_t H,
                                             int64_t m0, int64_t n0, int64_t ch0, int64_t ch1,
-                                            bool fast, float* xs, float* ws, floatx16_t (&acc)[8],
-                                            floatx16_t (&total)[8]) {
-    typedef GateStage<T> S;
+                                            bool fast, float* xs, float* ws, floatx16_t (&acc)[4 * RB],
+                                            floatx16_t (&total)[4 * RB]) {
+    constexpr int BM = 64 * RB;
+    typedef GateStage<T, BM> S;
     typedef typename GateIO<float>::Quad Quad;
     constexpr int LD = S::LD;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int wm = wv >> 1, wn = wv & 1;
-    // lane's operand rows: x rows wm*64 + 32 rb + lane%32, w rows wn*128 + 32 cb + lane%32;
+    // lane's operand rows: x rows wm*32*RB + 32 rb + lane%32, w rows wn*128 + 32 cb + lane%32;
     // its k parity (lane / 32) picks the even or odd half of the row
     const int par = (lane >> 5) * (GB_K / 2);
-    const int arow = wm * 64 + (lane & 31);
+    const int arow = wm * 32 * RB + (lane & 31);
     const int brow = wn * 128 + (lane & 31);
     // descriptors over the block's own rows: byte offsets stay below 256 * H * sizeof(T)
-    const int64_t xrows = G - m0 < GB_M ? G - m0 : GB_M;
+    const int64_t xrows = G - m0 < BM ? G - m0 : BM;
     const int64_t wrows = E - n0 < GB_N ? E - n0 : GB_N;
     const __amdgpu_buffer_rsrc_t rx =
         gemm::make_rsrc_uniform(x + m0 * H, static_cast<uint32_t>(xrows * H * static_cast<int64_t>(sizeof(T))));
@@ -206,28 +208,28 @@ __device__ __forceinline__ void gate_chunks(const T* x, const T* w, int64_t G, i
     __syncthreads();
     for (int64_t ch = ch0; ch < ch1; ++ch) {
 #pragma unroll
-        for (int c = 0; c < 8; ++c)
+        for (int c = 0; c < 4 * RB; ++c)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[c][v] = 0.f;
 #pragma unroll 1
         for (int q = 0; q < SLICES_PER_CHUNK; ++q) {
             const int64_t sl = ch * SLICES_PER_CHUNK + q;
             const int cur = static_cast<int>((sl - s_begin) & 1);
-            const float* xc = xs + cur * (GB_M * LD) + arow * LD + par;
+            const float* xc = xs + cur * (BM * LD) + arow * LD + par;
             const float* wc = ws + cur * (GB_N * LD) + brow * LD + par;
             const bool more = sl + 1 < s_end;
             if (more) load(sl + 1);
 #pragma unroll
             for (int kq = 0; kq < GB_K / 8; ++kq) {  // four k pairs per 16-byte read
-                float4 qa[2], qb[4];
+                float4 qa[RB], qb[4];
 #pragma unroll
-                for (int rb = 0; rb < 2; ++rb) qa[rb] = *reinterpret_cast<const float4*>(xc + rb * 32 * LD + kq * 4);
+                for (int rb = 0; rb < RB; ++rb) qa[rb] = *reinterpret_cast<const float4*>(xc + rb * 32 * LD + kq * 4);
 #pragma unroll
                 for (int cb = 0; cb < 4; ++cb) qb[cb] = *reinterpret_cast<const float4*>(wc + cb * 32 * LD + kq * 4);
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
 #pragma unroll
-                    for (int rb = 0; rb < 2; ++rb) {
+                    for (int rb = 0; rb < RB; ++rb) {
                         const float av = GateIO<float>::val(qa[rb], t);
 #pragma unroll
                         for (int cb = 0; cb < 4; ++cb)
@@ -236,12 +238,111 @@ __device__ __forceinline__ void gate_chunks(const T* x, const T* w, int64_t G, i
                     }
                 }
             }
-            if (more) st.store(xs + (cur ^ 1) * (GB_M * LD), ws + (cur ^ 1) * (GB_N * LD));
+            if (more) st.store(xs + (cur ^ 1) * (BM * LD), ws + (cur ^ 1) * (GB_N * LD));
             __syncthreads();
         }
         if (TOTAL) {
 #pragma unroll
-            for (int c = 0; c < 8; ++c)
+            for (int c = 0; c < 4 * RB; ++c)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) total[c][v] = total[c][v] + acc[c][v];
+        }
+    }
+}
+
+// Fast path of gate_chunks: 16-byte aligned inputs and H a multiple of the chunk width, so
+// every slice is whole.  The slice loop has no branches (the last slice re-stages itself into
+// the idle buffer, which nothing reads), the refill's global loads are issued at the top of
+// a slice, and its LDS stores are spread between the MFMAs of the slice's second half: with
+// one wave per SIMD the matrix pipe keeps issuing while the next slice is staged.  Each
+// chain's MFMAs keep their k order, so the bits are those of gate_chunks.
+template <typename T, bool TOTAL, int RB>
+__device__ __forceinline__ void gate_chunks_pipe(const T* x, const T* w, int64_t G, int64_t E, int64_t H,
+                                                 int64_t m0, int64_t n0, int64_t ch0, int64_t ch1,
+                                                 float* xs, float* ws, floatx16_t (&acc)[4 * RB],
+                                                 floatx16_t (&total)[4 * RB]) {
+    constexpr int BM = 64 * RB;
+    typedef GateStage<T, BM> S;
+    constexpr int LD = S::LD;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int wm = wv >> 1, wn = wv & 1;
+    const int par = (lane >> 5) * (GB_K / 2);
+    const int arow = wm * 32 * RB + (lane & 31);
+    const int brow = wn * 128 + (lane & 31);
+    const int64_t xrows = G - m0 < BM ? G - m0 : BM;
+    const int64_t wrows = E - n0 < GB_N ? E - n0 : GB_N;
+    const __amdgpu_buffer_rsrc_t rx =
+        gemm::make_rsrc_uniform(x + m0 * H, static_cast<uint32_t>(xrows * H * static_cast<int64_t>(sizeof(T))));
+    const __amdgpu_buffer_rsrc_t rw =
+        gemm::make_rsrc_uniform(w + n0 * H, static_cast<uint32_t>(wrows * H * static_cast<int64_t>(sizeof(T))));
+    uint32_t xoff[S::XCH], woff[S::WCH];
+#pragma unroll
+    for (int p = 0; p < S::XCH; ++p) {
+        const int idx = threadIdx.x + p * G_THREADS;
+        xoff[p] = static_cast<uint32_t>(((idx / S::PER_ROW) * H + (idx % S::PER_ROW) * S::C) * sizeof(T));
+    }
+#pragma unroll
+    for (int p = 0; p < S::WCH; ++p) {
+        const int idx = threadIdx.x + p * G_THREADS;
+        woff[p] = static_cast<uint32_t>(((idx / S::PER_ROW) * H + (idx % S::PER_ROW) * S::C) * sizeof(T));
+    }
+    // the second half of a slice issues 2 * 4 * RB * 4 MFMAs; spread the stores over them
+    constexpr int HALF_MFMA = 32 * RB;
+    constexpr int PER_STORE = HALF_MFMA / S::WRITES > 0 ? HALF_MFMA / S::WRITES : 1;
+    S st;
+    const int64_t s_end = ch1 * SLICES_PER_CHUNK;
+    st.load_fast(rx, rw, xoff, woff, ch0 * SLICES_PER_CHUNK * GB_K);
+    st.store(xs, ws);
+    __syncthreads();
+    static_assert(SLICES_PER_CHUNK % 2 == 0, "the stage of a slice is its index inside the chunk, mod 2");
+    for (int64_t ch = ch0; ch < ch1; ++ch) {
+#pragma unroll
+        for (int c = 0; c < 4 * RB; ++c)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[c][v] = 0.f;
+#pragma unroll
+        for (int q = 0; q < SLICES_PER_CHUNK; ++q) {
+            const int64_t sl = ch * SLICES_PER_CHUNK + q;
+            const int cur = q & 1;
+            const int64_t nxt = sl + 1 < s_end ? sl + 1 : sl;
+            const float* xc = xs + cur * (BM * LD) + arow * LD + par;
+            const float* wc = ws + cur * (GB_N * LD) + brow * LD + par;
+            __builtin_amdgcn_sched_barrier(0);
+            st.load_fast(rx, rw, xoff, woff, nxt * GB_K);
+            // four k pairs per 16-byte read of each operand row
+#define MOE_GATE_KQ(KQ)                                                                         \
+    do {                                                                                        \
+        float4 qa[RB], qb[4];                                                                   \
+        _Pragma("unroll") for (int rb = 0; rb < RB; ++rb) qa[rb] =                              \
+            *reinterpret_cast<const float4*>(xc + rb * 32 * LD + (KQ) * 4);                     \
+        _Pragma("unroll") for (int cb = 0; cb < 4; ++cb) qb[cb] =                               \
+            *reinterpret_cast<const float4*>(wc + cb * 32 * LD + (KQ) * 4);                     \
+        _Pragma("unroll") for (int t = 0; t < 4; ++t)                                           \
+            _Pragma("unroll") for (int rb = 0; rb < RB; ++rb) {                                 \
+                const float av = GateIO<float>::val(qa[rb], t);                                 \
+                _Pragma("unroll") for (int cb = 0; cb < 4; ++cb) acc[rb * 4 + cb] =             \
+                    __builtin_amdgcn_mfma_f32_32x32x2f32(av, GateIO<float>::val(qb[cb], t),     \
+                                                         acc[rb * 4 + cb], 0, 0, 0);            \
+            }                                                                                   \
+    } while (0)
+            MOE_GATE_KQ(0);
+            MOE_GATE_KQ(1);
+            __builtin_amdgcn_sched_barrier(0);
+            st.store(xs + (cur ^ 1) * (BM * LD), ws + (cur ^ 1) * (GB_N * LD));
+            MOE_GATE_KQ(2);
+            MOE_GATE_KQ(3);
+#undef MOE_GATE_KQ
+#pragma unroll
+            for (int g = 0; g < S::WRITES; ++g) {
+                __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);          // one LDS store
+                __builtin_amdgcn_sched_group_barrier(0x008, PER_STORE, 0);  // then MFMAs
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            __syncthreads();
+        }
+        if (TOTAL) {
+#pragma unroll
+            for (int c = 0; c < 4 * RB; ++c)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) total[c][v] = total[c][v] + acc[c][v];
         }
@@ -249,39 +350,43 @@ __device__ __forceinline__ void gate_chunks(const T* x, const T* w, int64_t G, i
 }
 
 // out[g, e] for the lane's accumulator element (chain c = 4 rb + cb, register v)
+template <int RB = 2>
 __device__ __forceinline__ void chain_coords(int c, int v, int lane, int64_t m0, int64_t n0, int64_t& g,
                                              int64_t& e) {
     const int wv = threadIdx.x >> 6, wm = wv >> 1, wn = wv & 1;
     e = n0 + wn * 128 + 32 * (c & 3) + (lane & 31);
-    g = m0 + wm * 64 + 32 * (c >> 2) + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+    g = m0 + wm * 32 * RB + 32 * (c >> 2) + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
 }
 
-// large batches: all chunks in one block, running total in registers
-template <typename T>
+// large batches: all chunks in one block of 64*RB rows, running total in registers
+template <typename T, int RB>
 __global__ __launch_bounds__(G_THREADS) void gate_exact_kernel(const T* __restrict__ x,
                                                                const T* __restrict__ w,
                                                                const int32_t* __restrict__ row_valid,
                                                                int64_t G, int64_t E, int64_t H,
                                                                bool fast, float* __restrict__ logits) {
-    constexpr int LD = GateStage<T>::LD;
-    __shared__ __attribute__((aligned(16))) float xs[2 * GB_M * LD];
+    constexpr int BM = 64 * RB;
+    constexpr int LD = GateStage<T, BM>::LD;
+    __shared__ __attribute__((aligned(16))) float xs[2 * BM * LD];
     __shared__ __attribute__((aligned(16))) float ws[2 * GB_N * LD];
-    const int64_t m0 = static_cast<int64_t>(blockIdx.x) * GB_M;
+    const int64_t m0 = static_cast<int64_t>(blockIdx.x) * BM;
     const int64_t n0 = static_cast<int64_t>(blockIdx.y) * GB_N;
     const int lane = threadIdx.x & 63;
-    floatx16_t acc[8], total[8];
+    floatx16_t acc[4 * RB], total[4 * RB];
 #pragma unroll
-    for (int c = 0; c < 8; ++c)
+    for (int c = 0; c < 4 * RB; ++c)
 #pragma unroll
         for (int v = 0; v < 16; ++v) total[c][v] = 0.f;
-    // the last chunk may be ragged: its columns past H read zeros, which add +0 products
-    gate_chunks<T, true>(x, w, G, E, H, m0, n0, 0, ceil_div(H, GATE_CHUNK), fast, xs, ws, acc, total);
+    if (fast && H % GATE_CHUNK == 0)
+        gate_chunks_pipe<T, true, RB>(x, w, G, E, H, m0, n0, 0, H / GATE_CHUNK, xs, ws, acc, total);
+    else  // the last chunk may be ragged: its columns past H read zeros, which add +0 products
+        gate_chunks<T, true, RB>(x, w, G, E, H, m0, n0, 0, ceil_div(H, GATE_CHUNK), fast, xs, ws, acc, total);
 #pragma unroll
-    for (int c = 0; c < 8; ++c)
+    for (int c = 0; c < 4 * RB; ++c)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
             int64_t g, e;
-            chain_coords(c, v, lane, m0, n0, g, e);
+            chain_coords<RB>(c, v, lane, m0, n0, g, e);
             if (g < G && e < E) {
                 const bool valid = row_valid == nullptr || row_valid[g] != 0;
                 logits[g * E + e] = valid ? total[c][v] : 0.f;
@@ -820,6 +925,10 @@ extern "C" moe_status moe_route(const void* global_x, const int32_t* row_valid, 
                            moe::aligned(workspace, 16);
     const dim3 tiles(static_cast<unsigned>(moe::ceil_div(G, moe::GB_M)),
                      static_cast<unsigned>(moe::ceil_div(E, moe::GB_N)));
+    // 64-row blocks when they all fit in one round on the CUs (a 64-row block takes a bit
+    // over half a 128-row block's time), else 128-row blocks
+    const dim3 tiles64(static_cast<unsigned>(moe::ceil_div(G, 64)), tiles.y);
+    const bool rows128 = static_cast<int64_t>(tiles64.x) * tiles64.y > moe::gate_num_cus();
     // 16-byte buffer loads need aligned bases and rows; the per-block descriptors span at
     // most 256 rows, which must stay below 2 GiB
     const size_t esz = dt == MOE_BF16 ? 2 : 4;
@@ -843,13 +952,23 @@ extern "C" moe_status moe_route(const void* global_x, const int32_t* row_valid, 
         hipLaunchKernelGGL(moe::gate_reduce_kernel, dim3(static_cast<unsigned>(rb)), dim3(256), 0, stream,
                            parts, row_valid, G, E, nch, logits);
     } else if (dt == MOE_BF16) {
-        hipLaunchKernelGGL(moe::gate_exact_kernel<uint16_t>, tiles, dim3(moe::G_THREADS), 0, stream,
-                           static_cast<const uint16_t*>(global_x), static_cast<const uint16_t*>(w_router),
-                           row_valid, G, E, H, fast, logits);
+        const uint16_t* xb = static_cast<const uint16_t*>(global_x);
+        const uint16_t* wb = static_cast<const uint16_t*>(w_router);
+        if (rows128)
+            hipLaunchKernelGGL((moe::gate_exact_kernel<uint16_t, 2>), tiles, dim3(moe::G_THREADS), 0, stream, xb,
+                               wb, row_valid, G, E, H, fast, logits);
+        else
+            hipLaunchKernelGGL((moe::gate_exact_kernel<uint16_t, 1>), tiles64, dim3(moe::G_THREADS), 0, stream, xb,
+                               wb, row_valid, G, E, H, fast, logits);
     } else {
-        hipLaunchKernelGGL(moe::gate_exact_kernel<float>, tiles, dim3(moe::G_THREADS), 0, stream,
-                           static_cast<const float*>(global_x), static_cast<const float*>(w_router),
-                           row_valid, G, E, H, fast, logits);
+        const float* xf = static_cast<const float*>(global_x);
+        const float* wf = static_cast<const float*>(w_router);
+        if (rows128)
+            hipLaunchKernelGGL((moe::gate_exact_kernel<float, 2>), tiles, dim3(moe::G_THREADS), 0, stream, xf, wf,
+                               row_valid, G, E, H, fast, logits);
+        else
+            hipLaunchKernelGGL((moe::gate_exact_kernel<float, 1>), tiles64, dim3(moe::G_THREADS), 0, stream, xf,
+                               wf, row_valid, G, E, H, fast, logits);
     }
     MOE_LAUNCH_CHECK();
     return moe::launch_select(logits, row_valid, G, bias, cfg, topk_ids, topk_w, stream);
