@@ -93,7 +93,8 @@ def test_argument_errors_return_before_any_launch(m):
     assert lib.moe_gather(ctypes.byref(L0), ctypes.cast(arr, ctypes.c_void_p), 16, _lib.MOE_BF16,
                           None, None, None) == _lib.MOE_OK
     # routing configuration checks
-    bad = [m.make_route_cfg("softmax", 0, 1), m.make_route_cfg("softmax", 8, 9),
+    bad = [m.make_route_cfg("softmax", 0, 1), m.make_route_cfg("softmax", 8, 9), m.make_route_cfg("softmax", 64, 33),
+           m.make_route_cfg("grouped", 1024, 8, 128, 4), m.make_route_cfg("grouped", 1024, 8, 64, 8, 5),
            m.make_route_cfg("softmax", 2048, 2), m.make_route_cfg("grouped", 256, 8, 7, 4),
            m.make_route_cfg("grouped", 256, 8, 8, 9), m.make_route_cfg("grouped", 256, 8, 8, 4, 40),
            m.make_route_cfg("grouped", 16, 8, 4, 1)]
