@@ -908,8 +908,14 @@ extern "C" moe_status moe_route(const void* global_x, const int32_t* row_valid, 
     MOE_CHECK_ARG(global_x && w_router && logits && topk_ids && topk_w);
     MOE_CHECK_ARG(G <= (int64_t)1 << 31);
     const int64_t E = cfg->num_experts;
-    if (cfg->gate_mode == MOE_GATE_FAST) {
-        if (dt != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+    const size_t split = moe::gate_split_bytes(G, E, H);
+    const bool use_split = split > 0 && workspace != nullptr && workspace_bytes >= split &&
+                           moe::aligned(workspace, 16);
+    // FAST mode on a batch small enough for the chunk-parallel exact gate takes that gate:
+    // it is faster there (a handful of 128-row tiles would run the whole of h in sequence),
+    // and its logits are the exact ones
+    if (cfg->gate_mode == MOE_GATE_FAST && dt != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+    if (cfg->gate_mode == MOE_GATE_FAST && !use_split) {
         const bool fast = moe::aligned(global_x, 16) && moe::aligned(w_router, 16) && (H * 2) % 16 == 0 &&
                           static_cast<int64_t>(moe::FB_N) * H * 2 < ((int64_t)1 << 31);
         const dim3 grid(static_cast<unsigned>(moe::ceil_div(G, moe::FB_M)),
@@ -920,9 +926,6 @@ extern "C" moe_status moe_route(const void* global_x, const int32_t* row_valid, 
         MOE_LAUNCH_CHECK();
         return moe::launch_select(logits, row_valid, G, bias, cfg, topk_ids, topk_w, stream);
     }
-    const size_t split = moe::gate_split_bytes(G, E, H);
-    const bool use_split = split > 0 && workspace != nullptr && workspace_bytes >= split &&
-                           moe::aligned(workspace, 16);
     const dim3 tiles(static_cast<unsigned>(moe::ceil_div(G, moe::GB_M)),
                      static_cast<unsigned>(moe::ceil_div(E, moe::GB_N)));
     // 64-row blocks when they all fit in one round on the CUs (a 64-row block takes a bit

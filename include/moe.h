@@ -189,7 +189,9 @@ size_t moe_route_workspace_size(int64_t G, int32_t num_experts, int64_t H);
  *              reproducible: for each 128-wide chunk c of h, part_c = fmaf chain over the
  *              chunk's h in ascending order from +0; logits[g,e] = ((+0 + part_0) + part_1)
  *              + ... in fp32, chunks left to right.  FAST mode: bf16 MFMA products, fp32
- *              sums in tile order (MOE_ERR_UNSUPPORTED for MOE_F32 inputs).  0 for pad rows.
+ *              sums in tile order (MOE_ERR_UNSUPPORTED for MOE_F32 inputs); a batch small
+ *              enough for the chunk-parallel table, with that workspace given, runs the EXACT
+ *              gate instead (faster at that size, exact logits).  0 for pad rows.
  *   topk_ids   device int32[G, k]: expert ids, slots in descending key order, ties to the
  *              lower id; -1 for pad rows
  *   topk_w     device fp32[G, k]: weights; 0 for pad rows
