@@ -17,7 +17,9 @@
 //     each row contributes one whole 128-byte line per slice, which the DMA path moves about
 //     1.5x faster than half lines.  Two LDS stages of 64 KB: slice kt+1 is in flight while
 //     slice kt is consumed, in two halves whose fragments are read during the previous
-//     half's MFMAs; the reads and refill DMAs are spread between the MFMAs;
+//     half's MFMAs; the reads and refill DMAs are spread between the MFMAs.  With bf16
+//     weights A is refilled after a mid-slice barrier and B after an end-of-slice barrier,
+//     so the other operand's DMAs are always in flight when a wave waits for its own;
 //   - persistent grid (one block per CU), XCD-grouped tile order (gemm_common.h); rows past
 //     a segment's end read as zeros and are never stored; each output tile has one owner.
 //
@@ -288,11 +290,13 @@ __global__ __launch_bounds__(M_THREADS, 1) void grouped_gemm_bf16_kernel(GemmArg
     } while (0)
         // Pipeline: K slices of BK in two LDS stages; slice kt lives in stage kt % 2 and is
         // consumed in two halves, each half's fragments read while the previous half's MFMAs
-        // run.  The one barrier per slice (before its second half) proves both that slice
-        // kt+1 has landed and that every wave has finished reading stage kt % 2, which is
-        // then refilled with slice kt+2.  Every slice issues exactly one refill (past the
-        // last slice it re-reads the last one, never consumed), so the in-flight count at the
-        // barrier is always that one slice.
+        // run.  fp8 weights: one barrier per slice (before its second half) proves both that
+        // slice kt+1 has landed and that every wave has finished reading stage kt % 2, which
+        // is then refilled with slice kt+2.  bf16 weights: the same for A at the mid-slice
+        // barrier; B has its own barrier at the slice end, after which B(kt+1)'s first-half
+        // fragments are read and B(kt+2) is issued.  Every slice issues exactly one refill
+        // per operand (past the last slice it re-reads the last one, never consumed), so the
+        // in-flight count at each wait is known.
         const int64_t KT = a.K / BK;
         // the previous tile's trailing DMAs and every wave's reads of the stage buffers are done
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
@@ -307,12 +311,23 @@ __global__ __launch_bounds__(M_THREADS, 1) void grouped_gemm_bf16_kernel(GemmArg
             // DMA counts that follow start from zero
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         }
-        issue(0, 0);
-        issue(1, KT > 1 ? 1 : 0);
-        issue_b(0);
-        issue_b(KT > 2 ? 2 : 0);
-        // slice 0 landed: every wave has exactly LPW DMAs issued after it
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPW) : "memory");
+        if constexpr (W8) {
+            issue(0, 0);
+            issue(1, KT > 1 ? 1 : 0);
+            issue_b(0);
+            issue_b(KT > 2 ? 2 : 0);
+            // slice 0 landed: every wave has exactly LPW DMAs issued after it
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPW) : "memory");
+        } else {
+            // A waves: slices 0 and 1 in flight; B waves: slice 0 (slice 1 follows in slice 0)
+            issue(0, 0);
+            if (loads_a) {
+                issue(1, KT > 1 ? 1 : 0);
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPW) : "memory");
+            } else {
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            }
+        }
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
         bf16x8_t f0a[2][4], f0b[2][4], f1a[2][4], f1b[2][4];
@@ -352,9 +367,70 @@ __global__ __launch_bounds__(M_THREADS, 1) void grouped_gemm_bf16_kernel(GemmArg
         MOE_INTERLEAVE(true);                                                                 \
         __builtin_amdgcn_sched_barrier(0);                                                    \
     } while (0)
-        for (int64_t kt = 0; kt < KT; kt += 2) {
-            MOE_SLICE(kt, 0);
-            MOE_SLICE(kt + 1, 1);
+        if constexpr (W8) {
+            for (int64_t kt = 0; kt < KT; kt += 2) {
+                MOE_SLICE(kt, 0);
+                MOE_SLICE(kt + 1, 1);
+            }
+        } else {
+            // bf16 weights: A is refilled after a mid-slice barrier and B after an end-of-slice
+            // barrier, so at every barrier the other operand's DMAs are still in flight and
+            // the CU's memory queue never drains.  A-loading and B-loading waves run separate
+            // copies of the loop (their DMA points and waits differ) with the same barriers.
+#define MOE_LOAD_A(FA, BUF, HALF)                                                              \
+    _Pragma("unroll") for (int ks_ = 0; ks_ < 2; ++ks_)                                       \
+        _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) FA[ks_][i_] =                        \
+            *reinterpret_cast<const bf16x8_t*>(a_rd + (BUF) * (BM * BK) + i_ * 32 * BK + fchunk[2 * (HALF) + ks_])
+#define MOE_LOAD_B(FB, BUF, HALF)                                                              \
+    _Pragma("unroll") for (int ks_ = 0; ks_ < 2; ++ks_)                                       \
+        _Pragma("unroll") for (int j_ = 0; j_ < 4; ++j_) FB[ks_][j_] =                        \
+            *reinterpret_cast<const bf16x8_t*>(b_rd + (BUF) * (BN * BK) + MOE_BROW(j_) * BK + fchunk[2 * (HALF) + ks_])
+#define MOE_SLICE2(KT_, PAR, IS_A)                                                             \
+    do {                                                                                       \
+        __builtin_amdgcn_sched_barrier(0);                                                     \
+        MOE_LOAD_A(f1a, PAR, 1);                                                               \
+        MOE_LOAD_B(f1b, PAR, 1);                                                               \
+        if (!(IS_A)) issue((PAR) ^ 1, (KT_) + 1 < KT ? (KT_) + 1 : KT - 1);                   \
+        MOE_MFMA_HALF(f0a, f0b);                                                               \
+        _Pragma("unroll") for (int g_ = 0; g_ < 16; ++g_) {                                    \
+            if (!(IS_A)) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                    \
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                 \
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                                 \
+        }                                                                                      \
+        __builtin_amdgcn_sched_barrier(0);                                                     \
+        if (IS_A) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");                  \
+        else asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");                                \
+        __builtin_amdgcn_s_barrier();                                                          \
+        __builtin_amdgcn_sched_barrier(0);                                                     \
+        if (IS_A) issue(PAR, (KT_) + 2 < KT ? (KT_) + 2 : KT - 1);                             \
+        MOE_LOAD_A(f0a, (PAR) ^ 1, 0);                                                         \
+        MOE_MFMA_HALF(f1a, f1b);                                                               \
+        _Pragma("unroll") for (int g_ = 0; g_ < 16; ++g_) {                                    \
+            if (IS_A) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                       \
+            if (g_ % 2 == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                \
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                                 \
+        }                                                                                      \
+        __builtin_amdgcn_sched_barrier(0);                                                     \
+        if (IS_A) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");                           \
+        else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");                       \
+        __builtin_amdgcn_s_barrier();                                                          \
+        __builtin_amdgcn_sched_barrier(0);                                                     \
+        MOE_LOAD_B(f0b, (PAR) ^ 1, 0);                                                         \
+    } while (0)
+            if (loads_a) {
+                for (int64_t kt = 0; kt < KT; kt += 2) {
+                    MOE_SLICE2(kt, 0, true);
+                    MOE_SLICE2(kt + 1, 1, true);
+                }
+            } else {
+                for (int64_t kt = 0; kt < KT; kt += 2) {
+                    MOE_SLICE2(kt, 0, false);
+                    MOE_SLICE2(kt + 1, 1, false);
+                }
+            }
+#undef MOE_SLICE2
+#undef MOE_LOAD_A
+#undef MOE_LOAD_B
         }
 #undef MOE_SLICE
 #undef MOE_INTERLEAVE
