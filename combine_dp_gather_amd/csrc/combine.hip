@@ -5,9 +5,11 @@
 // combine call of section "第 3 段：combine 前再交一次棒" passes no weights of its own.
 // Here both happen in one pass, in gather form:
 //     out[g] = scale * sum_{j ascending, pair_row[g*k+j] >= 0} w[g,j] * y_perm[pair_row[g*k+j]]
-// One wave owns one output row (no atomics, deterministic).  Lane j < k fetches the pair's
-// row index and weight once; the column loop then reads up to 8 source rows per batch with
-// all loads issued before the fp32 FMAs, so each lane keeps 8 16-byte loads in flight.
+// One block owns one output row (no atomics, deterministic): each wave learns which of the
+// row's k pairs are local from one ballot, then the block streams the row's columns, kUnrollC
+// 16-byte vectors per thread, taking the local pairs two at a time in ascending j with both
+// source rows' loads in flight before the fp32 FMAs.  Source rows are read and the output row
+// written with the streaming (non-temporal) hint.
 #include "moe_dev.h"
 
 namespace moe {
@@ -15,7 +17,7 @@ namespace {
 
 constexpr int C_THREADS = 256;
 constexpr int C_WAVES = C_THREADS / kWave;
-constexpr int kBatchJ = 8;
+constexpr int kUnrollC = 4;  // 16-byte vectors per thread and source row in flight
 
 template <typename T>
 struct Vec;
@@ -60,45 +62,71 @@ __global__ __launch_bounds__(C_THREADS) void combine_kernel(
     using VT = Vec<T>;
     using V = typename VT::V;
     const int lane = lane_id();
-    const int64_t g = static_cast<int64_t>(blockIdx.x) * C_WAVES + threadIdx.x / kWave;
-    if (g >= G) return;
+    const int64_t g = blockIdx.x;
+    // every wave reads the row's k pairs itself: lane j holds pair j, and the ballot of the
+    // local ones is walked lowest lane first, i.e. in ascending j
     int32_t my_row = -1;
     float my_w = 0.f;
     if (lane < k) {
         my_row = pair_row[g * k + lane];
         my_w = w[g * k + lane];
     }
+    const uint64_t local = __ballot(my_row >= 0);
     const int64_t vec_per_row = H / VT::N;
     const V* __restrict__ yv = reinterpret_cast<const V*>(y);
     V* __restrict__ ov = reinterpret_cast<V*>(out) + g * vec_per_row;
-    for (int64_t c = lane; c < vec_per_row; c += kWave) {
-        float acc[VT::N];
+    for (int64_t c0 = threadIdx.x; c0 < vec_per_row; c0 += C_THREADS * kUnrollC) {
+        float acc[kUnrollC][VT::N];
 #pragma unroll
-        for (int q = 0; q < VT::N; ++q) acc[q] = 0.f;
-        for (int j0 = 0; j0 < k; j0 += kBatchJ) {
-            V v[kBatchJ];
-            float wj[kBatchJ];
-            bool use[kBatchJ];
+        for (int u = 0; u < kUnrollC; ++u)
 #pragma unroll
-            for (int t = 0; t < kBatchJ; ++t) {
-                const int j = j0 + t;
-                const int32_t r = __shfl(my_row, j < k ? j : 0);
-                wj[t] = __shfl(my_w, j < k ? j : 0);
-                use[t] = (j < k) && (r >= 0);
-                v[t] = use[t] ? yv[static_cast<int64_t>(r) * vec_per_row + c] : V{};
+            for (int q = 0; q < VT::N; ++q) acc[u][q] = 0.f;
+        uint64_t m = local;
+        while (m) {
+            // two pairs per step: both source rows' vectors are in flight before the FMAs
+            const int j0 = __builtin_ctzll(m);
+            m &= m - 1;
+            const bool two = m != 0;
+            const int j1 = two ? __builtin_ctzll(m) : j0;
+            if (two) m &= m - 1;
+            const int64_t r0 = __builtin_amdgcn_readlane(my_row, j0);
+            const int64_t r1 = __builtin_amdgcn_readlane(my_row, j1);
+            const float w0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), j0));
+            const float w1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), j1));
+            V v0[kUnrollC], v1[kUnrollC];
+#pragma unroll
+            for (int u = 0; u < kUnrollC; ++u) {
+                const int64_t c = c0 + u * C_THREADS;
+                if (c < vec_per_row) {
+                    v0[u] = ld_stream(yv + r0 * vec_per_row + c);
+                    if (two) v1[u] = ld_stream(yv + r1 * vec_per_row + c);
+                }
             }
 #pragma unroll
-            for (int t = 0; t < kBatchJ; ++t) {
-                if (!use[t]) continue;
+            for (int u = 0; u < kUnrollC; ++u) {
                 float f[VT::N];
-                VT::unpack(v[t], f);
+                VT::unpack(v0[u], f);
 #pragma unroll
-                for (int q = 0; q < VT::N; ++q) acc[q] = __builtin_fmaf(wj[t], f[q], acc[q]);
+                for (int q = 0; q < VT::N; ++q) acc[u][q] = __builtin_fmaf(w0, f[q], acc[u][q]);
+            }
+            if (two) {
+#pragma unroll
+                for (int u = 0; u < kUnrollC; ++u) {
+                    float f[VT::N];
+                    VT::unpack(v1[u], f);
+#pragma unroll
+                    for (int q = 0; q < VT::N; ++q) acc[u][q] = __builtin_fmaf(w1, f[q], acc[u][q]);
+                }
             }
         }
 #pragma unroll
-        for (int q = 0; q < VT::N; ++q) acc[q] *= scale;
-        ov[c] = VT::pack(acc);
+        for (int u = 0; u < kUnrollC; ++u) {
+            const int64_t c = c0 + u * C_THREADS;
+            if (c >= vec_per_row) continue;
+#pragma unroll
+            for (int q = 0; q < VT::N; ++q) acc[u][q] *= scale;
+            st_stream(ov + c, VT::pack(acc[u]));
+        }
     }
 }
 
@@ -140,12 +168,15 @@ extern "C" moe_status moe_combine(const void* y_perm, moe_dtype dt, const moe_pl
     if (G == 0) return MOE_OK;
     MOE_CHECK_ARG(plan->pair_row && topk_w && out);
     MOE_CHECK_ARG(plan->cap == 0 || y_perm != nullptr);
+    // vector path: one block per output row; element-wise fallback: one wave per row
+    MOE_CHECK_ARG(G < 0x7fffffff);
+    const dim3 grid_rows(static_cast<unsigned>(G));
     const dim3 grid(static_cast<unsigned>(ceil_div(G, C_WAVES)));
     const int vec = dt == MOE_BF16 ? 8 : 4;
     const bool vec_ok = (H % vec == 0) && aligned(out, 16) && (y_perm == nullptr || aligned(y_perm, 16));
     if (dt == MOE_BF16) {
         if (vec_ok)
-            hipLaunchKernelGGL(combine_kernel<uint16_t>, grid, dim3(C_THREADS), 0, stream,
+            hipLaunchKernelGGL(combine_kernel<uint16_t>, grid_rows, dim3(C_THREADS), 0, stream,
                                static_cast<const uint16_t*>(y_perm), plan->pair_row, topk_w, G, k,
                                H, routed_scale, static_cast<uint16_t*>(out));
         else
@@ -154,7 +185,7 @@ extern "C" moe_status moe_combine(const void* y_perm, moe_dtype dt, const moe_pl
                                H, routed_scale, static_cast<uint16_t*>(out));
     } else {
         if (vec_ok)
-            hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(C_THREADS), 0, stream,
+            hipLaunchKernelGGL(combine_kernel<float>, grid_rows, dim3(C_THREADS), 0, stream,
                                static_cast<const float*>(y_perm), plan->pair_row, topk_w, G, k, H,
                                routed_scale, static_cast<float*>(out));
         else

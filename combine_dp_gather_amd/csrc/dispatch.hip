@@ -17,8 +17,8 @@
 //   3. place:   each wave of a block owns a quarter of the block's pairs, walks it 64 pairs
 //               at a time and ranks equal slots with ballots (rank = popcount of the lanes
 //               below with the same slot), so rows follow ascending pair index: stable;
-//   4. permute: x_perm[row] = global_x[sorted_pair[row] / k], one wave per row, 16-byte
-//               vectors, rows bounded by the device-side num_rows (no host sync).
+//   4. permute: x_perm[row] = global_x[sorted_pair[row] / k], one block per row, streaming
+//               16-byte vectors, rows bounded by the device-side num_rows (no host sync).
 #include "moe_dev.h"
 
 namespace moe {
@@ -26,9 +26,9 @@ namespace {
 
 constexpr int D_THREADS = 256;
 constexpr int D_WAVES = D_THREADS / kWave;
-constexpr int kPairsPerThread = 16;
-constexpr int kChunk = D_THREADS * kPairsPerThread;  // 4096 pairs per block
-constexpr int kWaveChunk = kChunk / D_WAVES;         // 1024 pairs per wave
+constexpr int kPairsPerThread = 4;
+constexpr int kChunk = D_THREADS * kPairsPerThread;  // 1024 pairs per block
+constexpr int kWaveChunk = kChunk / D_WAVES;         // 256 pairs per wave
 constexpr int kMaxSlots = 1024;
 
 struct MapArgs {
@@ -83,17 +83,43 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(
     int32_t* __restrict__ sorted_pair) {
     __shared__ int64_t sc[SCAN_THREADS];
     __shared__ int32_t kept[kMaxSlots];
+    __shared__ int32_t part_sum[SCAN_THREADS];
     __shared__ int32_t over;
-    const int e = threadIdx.x;
-    if (e == 0) over = 0;
+    const int tid = threadIdx.x;
+    if (tid == 0) over = 0;
+    // per-block bases of every slot: the threads are split into `parts` groups of El_pad
+    // (a power of two >= El); thread (part, e) adds slot e's counts over one contiguous range
+    // of blocks, the ranges' sums are scanned over parts in LDS, and each thread then writes
+    // its range's running bases
+    int el_pad = 1;
+    while (el_pad < El) el_pad <<= 1;
+    const int parts = SCAN_THREADS / el_pad;
+    const int e_of = tid & (el_pad - 1), part = tid / el_pad;
+    const int64_t per = (NB + parts - 1) / parts;
+    const int64_t b0 = part * per < NB ? part * per : NB;
+    const int64_t b1 = b0 + per < NB ? b0 + per : NB;
+    int32_t mine = 0;
+    if (e_of < El)
+        for (int64_t b = b0; b < b1; ++b) mine += blk_counts[b * El + e_of];
+    part_sum[tid] = mine;
     __syncthreads();
+    for (int off = 1; off < parts; off <<= 1) {
+        const int32_t v = part >= off ? part_sum[tid - off * el_pad] : 0;
+        __syncthreads();
+        part_sum[tid] += v;
+        __syncthreads();
+    }
+    if (e_of < El) {
+        int32_t run = part_sum[tid] - mine;
+        for (int64_t b = b0; b < b1; ++b) {
+            blk_base[b * El + e_of] = run;
+            run += blk_counts[b * El + e_of];
+        }
+    }
+    const int e = tid;
     int64_t padded = 0;
     if (e < El) {
-        int32_t run = 0;
-        for (int64_t b = 0; b < NB; ++b) {
-            blk_base[b * El + e] = run;
-            run += blk_counts[b * El + e];
-        }
+        const int32_t run = part_sum[(parts - 1) * el_pad + e];
         int32_t keep = run;
         if (stride > 0) {
             if (run > stride) {
@@ -196,6 +222,12 @@ __global__ __launch_bounds__(D_THREADS) void place_kernel(
     }
 }
 
+// One block per x_perm row at a time (grid-stride over rows, bounded by the device-side
+// num_rows): the row's source is one contiguous row of global_x, so the block streams a
+// contiguous span in and out, kPermUnroll 16-byte loads per thread in flight before the stores.
+constexpr int kPermUnroll = 4;
+constexpr int kPermGrid = 8192;
+
 template <typename V>
 __global__ __launch_bounds__(D_THREADS) void permute_kernel(
     const V* __restrict__ x, const int32_t* __restrict__ sorted_pair,
@@ -203,25 +235,24 @@ __global__ __launch_bounds__(D_THREADS) void permute_kernel(
     bool zero_pads, V* __restrict__ x_perm) {
     int64_t rows = *num_rows;
     rows = rows < cap ? rows : cap;
-    const int lane = lane_id();
-    const int64_t nw = static_cast<int64_t>(gridDim.x) * D_WAVES;
-    for (int64_t r = static_cast<int64_t>(blockIdx.x) * D_WAVES + threadIdx.x / kWave; r < rows;
-         r += nw) {
+    for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
         const int32_t f = sorted_pair[r];
+        if (f < 0 && !zero_pads) continue;  // unused capacity rows stay unwritten
         V* __restrict__ d = x_perm + r * row_units;
-        if (f >= 0) {
-            const V* __restrict__ s = x + static_cast<int64_t>(f / k) * row_units;
-            int64_t c = lane;
-            for (; c + 3 * kWave < row_units; c += 4 * kWave) {
-                const V v0 = s[c], v1 = s[c + kWave], v2 = s[c + 2 * kWave], v3 = s[c + 3 * kWave];
-                d[c] = v0;
-                d[c + kWave] = v1;
-                d[c + 2 * kWave] = v2;
-                d[c + 3 * kWave] = v3;
+        // alignment pad rows (f < 0) are written as zeros
+        const V* __restrict__ s = x + static_cast<int64_t>(f < 0 ? 0 : f / k) * row_units;
+        for (int64_t c0 = threadIdx.x; c0 < row_units; c0 += D_THREADS * kPermUnroll) {
+            V v[kPermUnroll];
+#pragma unroll
+            for (int u = 0; u < kPermUnroll; ++u) {
+                const int64_t c = c0 + u * D_THREADS;
+                v[u] = (f >= 0 && c < row_units) ? ld_stream(s + c) : V{};
             }
-            for (; c < row_units; c += kWave) d[c] = s[c];
-        } else if (zero_pads) {  // alignment pad rows; unused capacity rows stay unwritten
-            for (int64_t c = lane; c < row_units; c += kWave) d[c] = V{};
+#pragma unroll
+            for (int u = 0; u < kPermUnroll; ++u) {
+                const int64_t c = c0 + u * D_THREADS;
+                if (c < row_units) st_stream(d + c, v[u]);
+            }
         }
     }
 }
@@ -230,8 +261,7 @@ template <typename V>
 moe_status launch_permute(const void* x, const moe_plan* plan, int64_t row_bytes, void* x_perm,
                           hipStream_t stream) {
     const int64_t row_units = row_bytes / static_cast<int64_t>(sizeof(V));
-    int64_t blocks = ceil_div(plan->cap, D_WAVES);
-    if (blocks > 2048) blocks = 2048;
+    const int64_t blocks = plan->cap < kPermGrid ? plan->cap : kPermGrid;
     hipLaunchKernelGGL(permute_kernel<V>, dim3(static_cast<unsigned>(blocks)), dim3(D_THREADS), 0,
                        stream, static_cast<const V*>(x), plan->sorted_pair, plan->num_rows,
                        plan->cap, plan->top_k, row_units, plan->seg_stride == 0, static_cast<V*>(x_perm));

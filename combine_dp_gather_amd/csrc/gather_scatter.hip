@@ -4,11 +4,13 @@
 //   - section "两种 gather：all_reduce 与 all_gather": zero the global buffer and write each
 //     replica's rows at its offset;
 //   - section "scatter：把 MoE 的输出还回本副本": cut the global rows back with the same counts.
-// On one GPU every replica buffer is local, so both are pure HBM streams: one launch covers
-// up to kBatch replicas (blockIdx.y picks the replica, a uniform value, so its pointer and
-// offsets come from the kernel-argument segment with scalar loads), each thread moves
-// 16-byte vectors with kUnroll loads in flight before the stores.  Pad rows of MAX_LEN
-// slots are written as zeros in the same pass; row_valid is written alongside.
+// On one GPU every replica buffer is local, so both are pure HBM streams.  One launch covers
+// up to kBatch replicas.  Each block copies one contiguous chunk of kChunk vectors of one
+// replica's slot: its kUnroll 16-byte loads per thread are all in flight before the stores,
+// and both use the streaming (non-temporal) hint.  Blocks are numbered over the replicas'
+// chunks back to back; a block finds its replica in the chunk prefix held in the kernel
+// arguments (a uniform, scalar walk over at most kBatch entries).  Pad rows of MAX_LEN slots
+// are written as zeros in the same pass; row_valid is written alongside.
 #include "moe_dev.h"
 
 namespace moe {
@@ -17,63 +19,73 @@ namespace {
 constexpr int kBatch = 32;
 constexpr int kThreads = 256;
 constexpr int kUnroll = 4;
+constexpr int kChunk = kThreads * kUnroll;  // vectors per block (16 KB of 16-byte vectors)
 
 struct SliceBatch {
     const void* ptr[kBatch];
-    int64_t off[kBatch];        // first global row of the slot
-    int64_t slot_rows[kBatch];  // rows of the slot in the global buffer
-    int64_t n[kBatch];          // rows of the replica (<= slot_rows)
+    int64_t off[kBatch];              // first global row of the slot
+    int64_t slot_rows[kBatch];        // rows of the slot in the global buffer
+    int64_t n[kBatch];                // rows of the replica (<= slot_rows)
+    int64_t first_chunk[kBatch + 1];  // chunks of the replicas before j; [cnt] = all chunks
+    int32_t cnt;
 };
+
+// replica of this block: first_chunk[i] <= blockIdx.x < first_chunk[i + 1] (empty replicas
+// have equal bounds and are stepped over)
+__device__ __forceinline__ int replica_of_block(const SliceBatch& b) {
+    const int64_t blk = blockIdx.x;
+    int i = 0;
+    while (i + 1 < b.cnt && blk >= b.first_chunk[i + 1]) ++i;
+    return i;
+}
 
 template <typename V>
 __global__ __launch_bounds__(kThreads) void gather_kernel(SliceBatch b, int64_t row_units,
                                                           V* __restrict__ dst,
                                                           int32_t* __restrict__ row_valid) {
-    const int i = blockIdx.y;
+    const int i = replica_of_block(b);
     const V* __restrict__ src = static_cast<const V*>(b.ptr[i]);
     V* __restrict__ d = dst + b.off[i] * row_units;
     const int64_t total = b.slot_rows[i] * row_units;
     const int64_t ncopy = b.n[i] * row_units;
-    const int64_t tid = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-    const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
-    for (int64_t base = tid; base < total; base += stride * kUnroll) {
-        V v[kUnroll];
+    const int64_t c = static_cast<int64_t>(blockIdx.x) - b.first_chunk[i];
+    const int64_t base = c * kChunk + threadIdx.x;
+    V v[kUnroll];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int64_t idx = base + u * stride;
-            v[u] = (idx < ncopy) ? src[idx] : V{};
-        }
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int64_t idx = base + u * stride;
-            if (idx < total) d[idx] = v[u];
-        }
+    for (int u = 0; u < kUnroll; ++u) {
+        const int64_t idx = base + u * kThreads;
+        v[u] = (idx < ncopy) ? ld_stream(src + idx) : V{};
     }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        const int64_t idx = base + u * kThreads;
+        if (idx < total) st_stream(d + idx, v[u]);
+    }
+    // row_valid of the slot: chunk c covers rows c*kThreads + m*(chunks*kThreads)
     const int64_t rows = b.slot_rows[i];
-    for (int64_t r = tid; r < rows; r += stride) row_valid[b.off[i] + r] = r < b.n[i] ? 1 : 0;
+    const int64_t rstep = (b.first_chunk[i + 1] - b.first_chunk[i]) * kThreads;
+    for (int64_t r = c * kThreads + threadIdx.x; r < rows; r += rstep)
+        row_valid[b.off[i] + r] = r < b.n[i] ? 1 : 0;
 }
 
 template <typename V>
 __global__ __launch_bounds__(kThreads) void scatter_kernel(SliceBatch b, int64_t row_units,
                                                            const V* __restrict__ src) {
-    const int i = blockIdx.y;
+    const int i = replica_of_block(b);
     V* __restrict__ d = static_cast<V*>(const_cast<void*>(b.ptr[i]));
     const V* __restrict__ s = src + b.off[i] * row_units;
     const int64_t total = b.n[i] * row_units;
-    const int64_t tid = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-    const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
-    for (int64_t base = tid; base < total; base += stride * kUnroll) {
-        V v[kUnroll];
+    const int64_t base = (static_cast<int64_t>(blockIdx.x) - b.first_chunk[i]) * kChunk + threadIdx.x;
+    V v[kUnroll];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int64_t idx = base + u * stride;
-            if (idx < total) v[u] = s[idx];
-        }
+    for (int u = 0; u < kUnroll; ++u) {
+        const int64_t idx = base + u * kThreads;
+        if (idx < total) v[u] = ld_stream(s + idx);
+    }
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int64_t idx = base + u * stride;
-            if (idx < total) d[idx] = v[u];
-        }
+    for (int u = 0; u < kUnroll; ++u) {
+        const int64_t idx = base + u * kThreads;
+        if (idx < total) st_stream(d + idx, v[u]);
     }
 }
 
@@ -94,24 +106,25 @@ template <typename V>
 moe_status launch_slices(bool is_gather, const moe_gather_layout_t* L, const void* const* reps,
                          int64_t row_bytes, void* big, int32_t* row_valid, hipStream_t stream) {
     const int64_t row_units = row_bytes / static_cast<int64_t>(sizeof(V));
+    // every launch's block count fits the grid (checked before anything is enqueued)
+    if (ceil_div(L->rows * row_units, kChunk) + kBatch > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
     for (int first = 0; first < L->num_replicas; first += kBatch) {
         const int cnt = (L->num_replicas - first) < kBatch ? (L->num_replicas - first) : kBatch;
         SliceBatch b{};
-        int64_t max_units = 0;
+        b.cnt = cnt;
+        int64_t chunks = 0;
         for (int j = 0; j < cnt; ++j) {
             const int i = first + j;
             b.ptr[j] = reps[i];
             b.off[j] = L->offsets[i];
             b.slot_rows[j] = L->offsets[i + 1] - L->offsets[i];
             b.n[j] = L->sizes[i];
-            const int64_t units = (is_gather ? b.slot_rows[j] : b.n[j]) * row_units;
-            if (units > max_units) max_units = units;
+            b.first_chunk[j] = chunks;
+            chunks += ceil_div((is_gather ? b.slot_rows[j] : b.n[j]) * row_units, kChunk);
         }
-        if (max_units == 0) continue;
-        int64_t gx = ceil_div(max_units, static_cast<int64_t>(kThreads) * kUnroll);
-        const int64_t cap_x = (8192 / cnt) > 1 ? (8192 / cnt) : 1;
-        if (gx > cap_x) gx = cap_x;
-        dim3 grid(static_cast<unsigned>(gx), static_cast<unsigned>(cnt));
+        b.first_chunk[cnt] = chunks;
+        if (chunks == 0) continue;
+        const dim3 grid(static_cast<unsigned>(chunks));
         if (is_gather) {
             hipLaunchKernelGGL(gather_kernel<V>, grid, dim3(kThreads), 0, stream, b, row_units,
                                static_cast<V*>(big), row_valid);

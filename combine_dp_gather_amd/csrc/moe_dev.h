@@ -49,6 +49,43 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
+// Streaming accesses: data touched once per kernel (gather, scatter, permute, combine, the
+// entry step) is loaded and stored with the non-temporal hint, so the caches do not keep it
+// for reuse.  On gfx950 this moves large buffers markedly faster than plain accesses when
+// each block also works on a contiguous span (a device copy: about 6.3 against 4.9 TB/s).
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+template <typename V>
+__device__ __forceinline__ V ld_stream(const V* p) {
+    if constexpr (sizeof(V) == 16) {
+        const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+        V r;
+        __builtin_memcpy(&r, &v, 16);
+        return r;
+    } else if constexpr (sizeof(V) == 8) {
+        const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+        V r;
+        __builtin_memcpy(&r, &v, 8);
+        return r;
+    } else {
+        return __builtin_nontemporal_load(p);
+    }
+}
+template <typename V>
+__device__ __forceinline__ void st_stream(V* p, const V& v) {
+    if constexpr (sizeof(V) == 16) {
+        u32x4_t t;
+        __builtin_memcpy(&t, &v, 16);
+        __builtin_nontemporal_store(t, reinterpret_cast<u32x4_t*>(p));
+    } else if constexpr (sizeof(V) == 8) {
+        u32x2_t t;
+        __builtin_memcpy(&t, &v, 8);
+        __builtin_nontemporal_store(t, reinterpret_cast<u32x2_t*>(p));
+    } else {
+        __builtin_nontemporal_store(v, p);
+    }
+}
+
 __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 inline bool aligned(const void* p, uintptr_t a) {
