@@ -88,14 +88,15 @@ typedef unsigned int gate_u32x4 __attribute__((ext_vector_type(4)));
 // in LDS as [row][k] with row stride LD.  The fast load is a 16-byte buffer load per piece
 // from a descriptor over the block's rows only, so rows past G (or E) read as zeros; the
 // element-wise load covers a slice that runs past H and unaligned inputs.
-template <typename T, int BM = GB_M>
+template <typename T, int BM = GB_M, int NT = G_THREADS>
 struct GateStage {
     static constexpr int C = GateIO<T>::kChunk;
     static constexpr int LD = GB_K + G_PAD;
     static constexpr int PER_ROW = GB_K / C;  // 16-byte pieces per row
-    static constexpr int XCH = BM * PER_ROW / G_THREADS;
-    static constexpr int WRITES = (XCH + GB_N * PER_ROW / G_THREADS) * 2;  // LDS stores per thread
-    static constexpr int WCH = GB_N * PER_ROW / G_THREADS;
+    static constexpr int XCH = BM * PER_ROW / NT;
+    static constexpr int WRITES = (XCH + GB_N * PER_ROW / NT) * 2;  // LDS stores per thread
+    static constexpr int WCH = GB_N * PER_ROW / NT;
+    static_assert(XCH * NT == BM * PER_ROW && WCH * NT == GB_N * PER_ROW, "whole pieces per thread");
     uint4 xr[XCH], wr[WCH];
     __device__ void load_fast(__amdgpu_buffer_rsrc_t rx, __amdgpu_buffer_rsrc_t rw,
                               const uint32_t (&xoff)[XCH], const uint32_t (&woff)[WCH], int64_t k0) {
@@ -115,12 +116,12 @@ struct GateStage {
                               int64_t H, int64_t m0, int64_t n0, int64_t k0) {
 #pragma unroll
         for (int p = 0; p < XCH; ++p) {
-            const int idx = threadIdx.x + p * G_THREADS;
+            const int idx = threadIdx.x + p * NT;
             xr[p] = load_piece(x, G, H, m0 + idx / PER_ROW, k0 + (idx % PER_ROW) * C);
         }
 #pragma unroll
         for (int p = 0; p < WCH; ++p) {
-            const int idx = threadIdx.x + p * G_THREADS;
+            const int idx = threadIdx.x + p * NT;
             wr[p] = load_piece(w, E, H, n0 + idx / PER_ROW, k0 + (idx % PER_ROW) * C);
         }
     }
@@ -144,12 +145,12 @@ struct GateStage {
     __device__ void store(float* xs, float* ws) {
 #pragma unroll
         for (int p = 0; p < XCH; ++p) {
-            const int idx = threadIdx.x + p * G_THREADS;
+            const int idx = threadIdx.x + p * NT;
             put(xs + (idx / PER_ROW) * LD, (idx % PER_ROW) * C, xr[p]);
         }
 #pragma unroll
         for (int p = 0; p < WCH; ++p) {
-            const int idx = threadIdx.x + p * G_THREADS;
+            const int idx = threadIdx.x + p * NT;
             put(ws + (idx / PER_ROW) * LD, (idx % PER_ROW) * C, wr[p]);
         }
     }
@@ -387,6 +388,149 @@ __global__ __launch_bounds__(G_THREADS) void gate_exact_kernel(const T* __restri
         for (int v = 0; v < 16; ++v) {
             int64_t g, e;
             chain_coords<RB>(c, v, lane, m0, n0, g, e);
+            if (g < G && e < E) {
+                const bool valid = row_valid == nullptr || row_valid[g] != 0;
+                logits[g * E + e] = valid ? total[c][v] : 0.f;
+            }
+        }
+}
+
+// Large batches with whole chunks and aligned inputs: the same 128-row x 256-expert block
+// with 8 waves, two per SIMD.  Each wave owns 32 rows x 128 experts as four 32x32 chains
+// (wave wv: rows 32 (wv / 2), experts 128 (wv % 2)), so a wave needs half the accumulator
+// registers of the 4-wave block and its SIMD partner issues MFMAs while it waits on LDS
+// reads, staging or the slice barrier.  Slices are loaded from HBM two slices ahead and the
+// LDS fragments one k-quad ahead; the per-chain k order is that of gate_chunks_pipe, so the
+// bits are the same.
+constexpr int G8_THREADS = 512;
+constexpr int G8_BM = 128;
+constexpr int G8_CB = 4;  // 32-expert chains per wave
+
+template <typename T>
+__global__ __launch_bounds__(G8_THREADS, 1) void gate_exact8_kernel(const T* __restrict__ x,
+                                                                    const T* __restrict__ w,
+                                                                    const int32_t* __restrict__ row_valid,
+                                                                    int64_t G, int64_t E, int64_t H,
+                                                                    float* __restrict__ logits) {
+    typedef GateStage<T, G8_BM, G8_THREADS> S;
+    constexpr int LD = S::LD;
+    __shared__ __attribute__((aligned(16))) float xs[2 * G8_BM * LD];
+    __shared__ __attribute__((aligned(16))) float ws[2 * GB_N * LD];
+    const int64_t m0 = static_cast<int64_t>(blockIdx.x) * G8_BM;
+    const int64_t n0 = static_cast<int64_t>(blockIdx.y) * GB_N;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int wm = wv >> 1, wn = wv & 1;
+    const int par = (lane >> 5) * (GB_K / 2);
+    const int arow = wm * 32 + (lane & 31);
+    const int brow = wn * 128 + (lane & 31);
+    const int64_t xrows = G - m0 < G8_BM ? G - m0 : G8_BM;
+    const int64_t wrows = E - n0 < GB_N ? E - n0 : GB_N;
+    const __amdgpu_buffer_rsrc_t rx =
+        gemm::make_rsrc_uniform(x + m0 * H, static_cast<uint32_t>(xrows * H * static_cast<int64_t>(sizeof(T))));
+    const __amdgpu_buffer_rsrc_t rw =
+        gemm::make_rsrc_uniform(w + n0 * H, static_cast<uint32_t>(wrows * H * static_cast<int64_t>(sizeof(T))));
+    uint32_t xoff[S::XCH], woff[S::WCH];
+#pragma unroll
+    for (int p = 0; p < S::XCH; ++p) {
+        const int idx = threadIdx.x + p * G8_THREADS;
+        xoff[p] = static_cast<uint32_t>(((idx / S::PER_ROW) * H + (idx % S::PER_ROW) * S::C) * sizeof(T));
+    }
+#pragma unroll
+    for (int p = 0; p < S::WCH; ++p) {
+        const int idx = threadIdx.x + p * G8_THREADS;
+        woff[p] = static_cast<uint32_t>(((idx / S::PER_ROW) * H + (idx % S::PER_ROW) * S::C) * sizeof(T));
+    }
+    floatx16_t acc[G8_CB], total[G8_CB];
+#pragma unroll
+    for (int c = 0; c < G8_CB; ++c)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) total[c][v] = 0.f;
+    // Pipeline.  Slice j is held in staging registers st[j % 2] from the top of slice j - 2
+    // (its global loads) to the second half of slice j - 1 (its LDS stores), so a load has a
+    // slice and a half to arrive.  Inside a slice the LDS fragments of k-quad kq + 1 are read
+    // while the MFMAs of k-quad kq run.
+    S st[2];
+    const int64_t nch = H / GATE_CHUNK;
+    const int64_t s_end = nch * SLICES_PER_CHUNK;
+    st[0].load_fast(rx, rw, xoff, woff, 0);
+    st[0].store(xs, ws);
+    st[1].load_fast(rx, rw, xoff, woff, (s_end > 1 ? 1 : 0) * GB_K);
+    __syncthreads();
+    float4 fa[2], fb[2][G8_CB];
+    auto read_frag = [&](int buf, int kq, float4& a, float4 (&b)[G8_CB]) {
+        const float* xc = xs + buf * (G8_BM * LD) + arow * LD + par + kq * 4;
+        const float* wc = ws + buf * (GB_N * LD) + brow * LD + par + kq * 4;
+        a = *reinterpret_cast<const float4*>(xc);
+#pragma unroll
+        for (int cb = 0; cb < G8_CB; ++cb) b[cb] = *reinterpret_cast<const float4*>(wc + cb * 32 * LD);
+    };
+    // the k-quad's 16 MFMAs: 4 k pairs in order, each over the wave's G8_CB chains
+    auto mfma_quad = [&](const float4& a, const float4 (&b)[G8_CB]) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const float av = GateIO<float>::val(a, t);
+#pragma unroll
+            for (int cb = 0; cb < G8_CB; ++cb)
+                acc[cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, GateIO<float>::val(b[cb], t), acc[cb], 0, 0, 0);
+        }
+    };
+    read_frag(0, 0, fa[0], fb[0]);
+    for (int64_t ch = 0; ch < nch; ++ch) {
+#pragma unroll
+        for (int c = 0; c < G8_CB; ++c)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[c][v] = 0.f;
+#pragma unroll
+        for (int q = 0; q < SLICES_PER_CHUNK; ++q) {
+            const int64_t sl = ch * SLICES_PER_CHUNK + q;
+            const int cur = q & 1;
+            const int64_t n2 = sl + 2 < s_end ? sl + 2 : s_end - 1;
+            __builtin_amdgcn_sched_barrier(0);
+            st[q & 1].load_fast(rx, rw, xoff, woff, n2 * GB_K);  // slice sl + 2
+            read_frag(cur, 1, fa[1], fb[1]);
+            mfma_quad(fa[0], fb[0]);
+#pragma unroll
+            for (int g = 0; g < 1 + G8_CB; ++g) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+                __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);  // then MFMAs
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            read_frag(cur, 2, fa[0], fb[0]);
+            mfma_quad(fa[1], fb[1]);
+#pragma unroll
+            for (int g = 0; g < 1 + G8_CB; ++g) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            read_frag(cur, 3, fa[1], fb[1]);
+            st[(q + 1) & 1].store(xs + (cur ^ 1) * (G8_BM * LD), ws + (cur ^ 1) * (GB_N * LD));  // slice sl + 1
+            mfma_quad(fa[0], fb[0]);
+#pragma unroll
+            for (int g = 0; g < 1 + G8_CB; ++g) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // one LDS store
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_quad(fa[1], fb[1]);
+            __builtin_amdgcn_sched_barrier(0);
+            __syncthreads();
+            // k-quad 0 of slice sl + 1 (past the last slice: a stale stage, never used)
+            read_frag(cur ^ 1, 0, fa[0], fb[0]);
+        }
+#pragma unroll
+        for (int c = 0; c < G8_CB; ++c)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) total[c][v] = total[c][v] + acc[c][v];
+    }
+#pragma unroll
+    for (int c = 0; c < G8_CB; ++c)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int64_t e = n0 + wn * 128 + 32 * c + (lane & 31);
+            const int64_t g = m0 + wm * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
             if (g < G && e < E) {
                 const bool valid = row_valid == nullptr || row_valid[g] != 0;
                 logits[g * E + e] = valid ? total[c][v] : 0.f;
@@ -954,6 +1098,15 @@ extern "C" moe_status moe_route(const void* global_x, const int32_t* row_valid, 
         if (rb > 4096) rb = 4096;
         hipLaunchKernelGGL(moe::gate_reduce_kernel, dim3(static_cast<unsigned>(rb)), dim3(256), 0, stream,
                            parts, row_valid, G, E, nch, logits);
+    } else if (rows128 && fast && H % moe::GATE_CHUNK == 0) {
+        if (dt == MOE_BF16)
+            hipLaunchKernelGGL(moe::gate_exact8_kernel<uint16_t>, tiles, dim3(moe::G8_THREADS), 0, stream,
+                               static_cast<const uint16_t*>(global_x), static_cast<const uint16_t*>(w_router),
+                               row_valid, G, E, H, logits);
+        else
+            hipLaunchKernelGGL(moe::gate_exact8_kernel<float>, tiles, dim3(moe::G8_THREADS), 0, stream,
+                               static_cast<const float*>(global_x), static_cast<const float*>(w_router),
+                               row_valid, G, E, H, logits);
     } else if (dt == MOE_BF16) {
         const uint16_t* xb = static_cast<const uint16_t*>(global_x);
         const uint16_t* wb = static_cast<const uint16_t*>(w_router);

@@ -213,13 +213,15 @@ def test_gate_kernels_bitwise(dt):
     # one on 64-row blocks (G = 16347: its 256 blocks of 64 rows fit one round, where 128-row
     # blocks would leave half the CUs idle) and on 128-row blocks (G = 33000), each with a
     # ragged last chunk (H = 7 * 128 + 104, 232) or through the pipelined whole-chunk path
-    # (H = 256, 384) -- against the oracle, bit for bit, with ragged row and expert tiles
+    # (H = 256, 384; at 128-row blocks that is the 8-wave kernel, also with subnormal
+    # products) -- against the oracle, bit for bit, with ragged row and expert tiles
     import combine_dp_gather_amd as m
     rng = np.random.default_rng(21)
     cfg = m.make_route_cfg("softmax", 200, 4)
     # third case: magnitudes whose products and partial sums are subnormal fp32
     for G, H, scale in ((300, 1000, 1.0), (128 * 128 - 37, 232, 1.0), (300, 384, 2.0 ** -66),
-                        (128 * 128 - 37, 256, 1.0), (33000, 384, 1.0), (33000, 232, 1.0)):
+                        (128 * 128 - 37, 256, 1.0), (33000, 384, 1.0), (33000, 232, 1.0),
+                        (33000, 256, 2.0 ** -66)):
         say(f"[gate] dtype={dt} G={G} H={H} E=200 scale={scale}")
         x = torch.from_numpy((rng.standard_normal((G, H)) * scale).astype(np.float32)).to(dt)
         w = torch.from_numpy((rng.standard_normal((200, H)) * 0.05 * scale).astype(np.float32)).to(dt)
