@@ -154,7 +154,17 @@ def ceilings(cfg, R: int) -> dict:
     dst = torch.empty_like(src)
     ms = _time_ms(lambda: dst.copy_(src))
     out["device_copy_GBps"] = round(2 * n / ms / 1e6, 1)
-    del src, dst
+    # the same bytes through this library's streaming copy: a one-replica gather of 1 GiB of
+    # bf16 rows (block-contiguous spans, non-temporal loads and stores)
+    import combine_dp_gather_amd as m
+    H = 8192
+    rows = n // (2 * H)
+    L = m.moe_gather_layout([rows], "sum")
+    xs, xd = src.view(torch.bfloat16).view(rows, H), dst.view(torch.bfloat16).view(rows, H)
+    rv = torch.empty(rows, dtype=torch.int32, device="cuda")
+    ms = _time_ms(lambda: m.moe_gather(L, [xs], xd, rv))
+    out["stream_copy_GBps"] = round((2 * n + 4 * rows) / ms / 1e6, 1)
+    del src, dst, xs, xd, rv
     if cfg.dtype == "bf16":
         H, I, El = cfg.hidden, cfg.inter, cfg.num_local
         rows = max(R // El, 1)

@@ -3,6 +3,10 @@
     # per-kernel durations of a --kernel-trace --stats run
     python -m combine_dp_gather_amd.profiling stats DIR/stats_kernel_stats.csv --cmd "..."
 
+    # matrix-core busy fraction, engine clock and counted flops per kernel of a --pmc run
+    python -m combine_dp_gather_amd.profiling mfma --counters DIR/run_counter_collection.csv \
+        --agent DIR/run_agent_info.csv
+
     # HBM bytes per launch of one kernel from a FETCH_SIZE run and a WRITE_SIZE run, each
     # scaled by what the same counter reads for a plain device copy of known size made in the
     # same process (bench.py --copy-calibration MIB)
@@ -94,6 +98,45 @@ def traffic(fetch_csv: str, write_csv: str, copy_mib: int, kernel: str) -> dict:
     return res
 
 
+def agent_geometry(agent_csv: str) -> dict:
+    """SIMD count, XCD count and the maximum engine clock (MHz) of the GPU agent."""
+    for r in csv.DictReader(open(agent_csv)):
+        if r.get("Agent_Type") == "GPU":
+            return {"simds": int(r["Simd_Count"]), "xcds": int(r["Num_Xcc"]),
+                    "max_mhz": float(r["Max_Engine_Clk_Fcompute"])}
+    raise SystemExit(f"no GPU agent in {agent_csv}")
+
+
+def mfma_util(counter_csv: str, agent_csv: str) -> List[dict]:
+    """Per kernel, averaged over its dispatches: duration, the engine clock it ran at
+    (GRBM_GUI_ACTIVE is summed over the XCDs, so cycles per XCD over the duration), the
+    fraction of SIMD cycles with a busy matrix core (SQ_VALU_MFMA_BUSY_CYCLES over SIMDs x
+    cycles per XCD) and the matrix-core flops the hardware counted (MOPS x 512)."""
+    geo = agent_geometry(agent_csv)
+    vals = collections.defaultdict(lambda: collections.defaultdict(list))
+    spans = collections.defaultdict(dict)
+    for r in csv.DictReader(open(counter_csv)):
+        name = short_name(r["Kernel_Name"])
+        vals[name][r["Counter_Name"]].append(float(r["Counter_Value"]))
+        spans[name][r["Dispatch_Id"]] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    out = []
+    for name, c in vals.items():
+        if not c.get("SQ_VALU_MFMA_BUSY_CYCLES") or not c.get("GRBM_GUI_ACTIVE"):
+            continue
+        mean = {k: sum(v) / len(v) for k, v in c.items()}
+        if mean["SQ_VALU_MFMA_BUSY_CYCLES"] <= 0:
+            continue
+        dur_ns = sum(spans[name].values()) / len(spans[name])
+        cycles = mean["GRBM_GUI_ACTIVE"] / geo["xcds"]
+        flops = 512.0 * sum(mean.get(k, 0.0) for k in ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F16",
+                                                       "SQ_INSTS_VALU_MFMA_MOPS_F32", "SQ_INSTS_VALU_MFMA_MOPS_F64"))
+        out.append({"name": name, "dispatches": len(spans[name]), "avg_us": dur_ns / 1e3,
+                    "clock_mhz": cycles / dur_ns * 1e3,
+                    "mfma_busy": mean["SQ_VALU_MFMA_BUSY_CYCLES"] / (cycles * geo["simds"]),
+                    "counted_flops": flops})
+    return sorted(out, key=lambda r: -r["avg_us"])
+
+
 def read_traffic_summary(path: str, source_paths: Sequence[str]) -> Optional[float]:
     """bytes per launch from a committed summary, or None if absent or the sources changed."""
     if not os.path.exists(path):
@@ -125,7 +168,18 @@ def main():
     t.add_argument("--sources", nargs="+", required=True)
     t.add_argument("--algorithmic-bytes", type=float, default=0.0)
     t.add_argument("--cmd", nargs="*", default=[])
+    u = sub.add_parser("mfma")
+    u.add_argument("--counters", required=True, help="counter_collection.csv of a --pmc run")
+    u.add_argument("--agent", required=True, help="agent_info.csv of the same run")
     a = ap.parse_args()
+    if a.what == "mfma":
+        geo = agent_geometry(a.agent)
+        print(f"GPU: {geo['simds']} SIMDs, {geo['xcds']} XCDs, max engine clock {geo['max_mhz']:.0f} MHz")
+        print(f"{'kernel':50s} {'calls':>5s} {'avg_us':>9s} {'clock_MHz':>9s} {'mfma_busy':>9s} {'counted_flop':>13s}")
+        for r in mfma_util(a.counters, a.agent):
+            print(f"{r['name'][:50]:50s} {r['dispatches']:5d} {r['avg_us']:9.1f} {r['clock_mhz']:9.0f} "
+                  f"{r['mfma_busy']:9.3f} {r['counted_flops']:13.4e}")
+        return
     if a.what == "stats":
         if a.cmd:
             print(f"command: {a.cmd}\n")
