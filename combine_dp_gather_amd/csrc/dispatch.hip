@@ -13,7 +13,8 @@
 //   1. count:   each block takes kChunk consecutive pairs and builds a per-slot histogram in
 //               LDS (integer LDS atomics: the counts do not depend on their order);
 //   2. scan:    one block turns the per-block histograms into per-block bases (column prefix
-//               over blocks), per-slot counts and the aligned exclusive scan seg_offsets;
+//               over blocks), per-slot counts and the aligned exclusive scan seg_offsets; when
+//               the count table is small, the place blocks do this themselves instead;
 //   3. place:   each wave of a block owns a quarter of the block's pairs, walks it 64 pairs
 //               at a time and ranks equal slots with ballots (rank = popcount of the lanes
 //               below with the same slot), so rows follow ascending pair index: stable;
@@ -160,20 +161,65 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(
     }
 }
 
+// Layout of the plan from the per-block counts, computed inside the place kernel when the
+// count table is small (FUSED): every block adds the table itself -- the slot totals over all
+// blocks and its own base over the blocks before it, with integer LDS atomics whose order
+// does not matter -- then runs the aligned exclusive scan over slots.  Block 0 publishes the
+// plan's counts, seg_offsets, num_rows and error_flag, and all blocks share the pad-row fill.
+// This saves the separate scan launch and the per-block base round trip through memory.
+constexpr int64_t kFusedScanLimit = 65536;  // NB * El entries each block adds up
+
+struct ScanArgs {
+    const int32_t* blk_counts;  // [NB][El]
+    int64_t NB;
+    int align;
+    int64_t stride;
+    int32_t* counts;
+    int64_t* seg;
+    int64_t* num_rows;
+    int32_t* error_flag;
+};
+
+template <bool FUSED>
 __global__ __launch_bounds__(D_THREADS) void place_kernel(
     const int32_t* __restrict__ ids, int64_t P, int k, MapArgs m,
-    const int32_t* __restrict__ blk_base, const int64_t* __restrict__ seg, int64_t cap,
-    int32_t* __restrict__ sorted_pair, int32_t* __restrict__ pair_row) {
+    const int32_t* __restrict__ blk_base, const int64_t* __restrict__ seg_in, int64_t cap,
+    ScanArgs sa, int32_t* __restrict__ sorted_pair, int32_t* __restrict__ pair_row) {
     // a pair's row must also stay inside its slot's segment: in the fixed-capacity layout the
     // pairs past the capacity are dropped; packed segments always have room
     __shared__ int32_t whist[D_WAVES][kMaxSlots];
     __shared__ int64_t wbase[D_WAVES][kMaxSlots];
-    const int wv = threadIdx.x / kWave;
+    // FUSED only: slot totals, this block's base, the segment offsets, the kept counts
+    __shared__ int32_t tot[FUSED ? kMaxSlots : 1], before[FUSED ? kMaxSlots : 1];
+    __shared__ int64_t seg_s[FUSED ? kMaxSlots + 1 : 1];
+    __shared__ int64_t part[FUSED ? D_THREADS : 1];
+    __shared__ int32_t over;
+    const int tid = threadIdx.x;
+    const int wv = tid / kWave;
     const int lane = lane_id();
     const int El = m.El;
-    for (int i = threadIdx.x; i < D_WAVES * El; i += D_THREADS) whist[i / El][i % El] = 0;
+    for (int i = tid; i < D_WAVES * El; i += D_THREADS) whist[i / El][i % El] = 0;
+    if constexpr (FUSED) {
+        for (int e = tid; e < El; e += D_THREADS) {
+            tot[e] = 0;
+            before[e] = 0;
+        }
+        if (tid == 0) over = 0;
+    }
     __syncthreads();
     const int64_t wstart = static_cast<int64_t>(blockIdx.x) * kChunk + wv * kWaveChunk;
+    // FUSED: the first U count-table entries of this thread are loaded before the pass over
+    // the ids, so the two global round trips overlap
+    constexpr int U = 16;
+    const int64_t n_tab = FUSED ? sa.NB * El : 0;
+    int32_t c0[U];
+    if constexpr (FUSED) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = tid + u * D_THREADS;
+            c0[u] = i < n_tab ? sa.blk_counts[i] : 0;
+        }
+    }
     // per-wave histogram of its pairs
     for (int step = 0; step < kWaveChunk / kWave; ++step) {
         const int64_t f = wstart + step * kWave + lane;
@@ -182,10 +228,107 @@ __global__ __launch_bounds__(D_THREADS) void place_kernel(
             if (s >= 0) atomicAdd(&whist[wv][s], 1);
         }
     }
-    __syncthreads();
+    const int64_t* seg = seg_in;
+    if constexpr (FUSED) {
+        const int64_t mine_end = static_cast<int64_t>(blockIdx.x) * El;  // entries of earlier blocks
+        auto add = [&](int64_t i, int32_t c) {
+            if (c) {
+                const int e = static_cast<int>(i % El);
+                atomicAdd(&tot[e], c);
+                if (i < mine_end) atomicAdd(&before[e], c);
+            }
+        };
+#pragma unroll
+        for (int u = 0; u < U; ++u) add(tid + u * D_THREADS, c0[u]);
+        for (int64_t i0 = tid + U * D_THREADS; i0 < n_tab; i0 += D_THREADS * U) {
+            int32_t c[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t i = i0 + u * D_THREADS;
+                c[u] = i < n_tab ? sa.blk_counts[i] : 0;
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) add(i0 + u * D_THREADS, c[u]);
+        }
+        __syncthreads();
+        // aligned exclusive scan over slots: thread t owns slots 4t .. 4t+3
+        constexpr int SPT = kMaxSlots / D_THREADS;
+        int64_t padded[SPT];
+        int64_t sum = 0;
+#pragma unroll
+        for (int q = 0; q < SPT; ++q) {
+            const int e = tid * SPT + q;
+            padded[q] = 0;
+            if (e < El) {
+                const int32_t run = tot[e];
+                if (sa.stride > 0) {
+                    if (run > sa.stride) over = 1;
+                    padded[q] = sa.stride;
+                } else {
+                    padded[q] = (static_cast<int64_t>(run) + sa.align - 1) / sa.align * sa.align;
+                }
+            }
+            sum += padded[q];
+        }
+        int64_t incl;
+        if (El <= kWave * SPT) {
+            // every slot sits in wave 0: an inclusive scan by shuffles, no barriers
+            incl = sum;
+#pragma unroll
+            for (int off = 1; off < kWave; off <<= 1) {
+                const int64_t v = __shfl_up(incl, off);
+                if (lane >= off) incl += v;
+            }
+            if (tid == kWave - 1) part[D_THREADS - 1] = incl;
+        } else {
+            part[tid] = sum;
+            __syncthreads();
+            for (int off = 1; off < D_THREADS; off <<= 1) {
+                const int64_t v = tid >= off ? part[tid - off] : 0;
+                __syncthreads();
+                part[tid] += v;
+                __syncthreads();
+            }
+            incl = part[tid];
+        }
+        int64_t run = incl - sum;
+#pragma unroll
+        for (int q = 0; q < SPT; ++q) {
+            const int e = tid * SPT + q;
+            if (e < El) seg_s[e] = run;
+            run += padded[q];
+        }
+        __syncthreads();
+        if (tid == 0) seg_s[El] = part[D_THREADS - 1];
+        __syncthreads();
+        seg = seg_s;
+        const bool publish = blockIdx.x == 0;
+        // rows of a segment past its kept pairs (alignment pad, or unused capacity) hold no
+        // pair; the blocks share them
+        const int64_t gstride = static_cast<int64_t>(gridDim.x) * D_THREADS;
+        auto kept = [&](int e) -> int32_t {
+            return sa.stride > 0 && tot[e] > sa.stride ? static_cast<int32_t>(sa.stride) : tot[e];
+        };
+        for (int e = 0; e < El; ++e) {
+            const int64_t end = seg_s[e + 1];
+            for (int64_t r = seg_s[e] + kept(e) + static_cast<int64_t>(blockIdx.x) * D_THREADS + tid;
+                 r < end && r < cap; r += gstride)
+                sorted_pair[r] = -1;
+        }
+        if (publish) {
+            for (int e = tid; e < El; e += D_THREADS) sa.counts[e] = kept(e);
+            for (int e = tid; e <= El; e += D_THREADS) sa.seg[e] = seg_s[e];
+            if (tid == 0) {
+                *sa.num_rows = seg_s[El];
+                *sa.error_flag = (seg_s[El] > cap || over) ? 1 : 0;
+            }
+        }
+    } else {
+        __syncthreads();
+    }
     // first row of each wave's run of each slot
-    for (int e = threadIdx.x; e < El; e += D_THREADS) {
-        int64_t run = seg[e] + blk_base[static_cast<int64_t>(blockIdx.x) * El + e];
+    for (int e = tid; e < El; e += D_THREADS) {
+        int64_t run = seg[e] + (FUSED ? before[e] : blk_base[static_cast<int64_t>(blockIdx.x) * El + e]);
         for (int w = 0; w < D_WAVES; ++w) {
             wbase[w][e] = run;
             run += whist[w][e];
@@ -315,16 +458,26 @@ extern "C" moe_status moe_dispatch(const void* global_x, const int32_t* topk_ids
                            topk_ids, P, k, m, blk_counts);
         MOE_LAUNCH_CHECK();
     }
-    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(SCAN_THREADS), 0, stream, blk_counts, NB, El,
-                       plan->align, static_cast<int64_t>(plan->seg_stride), plan->cap, blk_base,
-                       plan->counts, plan->seg_offsets,
-                       plan->num_rows, plan->error_flag, plan->sorted_pair);
-    MOE_LAUNCH_CHECK();
-    if (NB == 0) return MOE_OK;
-    hipLaunchKernelGGL(place_kernel, dim3(static_cast<unsigned>(NB)), dim3(D_THREADS), 0, stream,
-                       topk_ids, P, k, m, blk_base, plan->seg_offsets, plan->cap,
-                       plan->sorted_pair, plan->pair_row);
-    MOE_LAUNCH_CHECK();
+    ScanArgs sa{blk_counts, NB, plan->align, static_cast<int64_t>(plan->seg_stride), plan->counts,
+                plan->seg_offsets, plan->num_rows, plan->error_flag};
+    if (NB > 0 && NB * El <= kFusedScanLimit) {
+        // the place blocks derive the layout from the count table themselves
+        hipLaunchKernelGGL(place_kernel<true>, dim3(static_cast<unsigned>(NB)), dim3(D_THREADS), 0, stream,
+                           topk_ids, P, k, m, nullptr, nullptr, plan->cap, sa, plan->sorted_pair,
+                           plan->pair_row);
+        MOE_LAUNCH_CHECK();
+    } else {
+        hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(SCAN_THREADS), 0, stream, blk_counts, NB, El,
+                           plan->align, static_cast<int64_t>(plan->seg_stride), plan->cap, blk_base,
+                           plan->counts, plan->seg_offsets,
+                           plan->num_rows, plan->error_flag, plan->sorted_pair);
+        MOE_LAUNCH_CHECK();
+        if (NB == 0) return MOE_OK;
+        hipLaunchKernelGGL(place_kernel<false>, dim3(static_cast<unsigned>(NB)), dim3(D_THREADS), 0, stream,
+                           topk_ids, P, k, m, blk_base, plan->seg_offsets, plan->cap, sa,
+                           plan->sorted_pair, plan->pair_row);
+        MOE_LAUNCH_CHECK();
+    }
     if (plan->cap == 0) return MOE_OK;
     const int64_t row_bytes = H * dtype_size(dt);
     if (row_bytes % 16 == 0 && aligned(global_x, 16) && aligned(x_perm, 16))
