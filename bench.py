@@ -5,7 +5,8 @@
     python bench.py [--steps K] [--warmup W] [--workload cfg4]
 
 A step is one pass of all six C-ABI calls over one batch whose inputs are already resident
-in HBM.  Prints one JSON line: tokens/s, the roofline of the dominant kernel (timed with HIP
+in HBM.  By default the six calls are captured once in a HIP graph and each timed step is one
+replay (--eager launches them call by call).  Prints one JSON line: tokens/s, the roofline of the dominant kernel (timed with HIP
 events on the stream the kernels run on), per-kernel breakdown, and the CPU oracle timed on
 a bounded sample of the same workload.
 """
@@ -204,7 +205,10 @@ def main():
                     help="fp8-weight workloads: keep activations bf16 (weights dequantised in the "
                          "kernel) or quantise them per 1x128 group for the fp8 matrix cores")
     ap.add_argument("--graph", action="store_true",
-                    help="capture one step (all six calls) in a HIP graph and time its replays")
+                    help="capture one step (all six calls) in a HIP graph and time its replays "
+                         "(the default)")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch the six calls one by one each step instead of replaying a graph")
     ap.add_argument("--ceilings", action="store_true",
                     help="also measure practical ceilings: a plain 1 GiB device copy and the vendor "
                          "GEMM (torch.matmul) on the same per-expert shapes")
@@ -226,6 +230,7 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run a plain device copy of MIB MiB (reference for HBM counters)")
     args = ap.parse_args()
+    args.graph = not args.eager
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU: this path has no multi-GPU mode "
               f"(--gpus {args.gpus} requested)", file=sys.stderr)
