@@ -21,14 +21,17 @@ def _outputs(layer):
            [to_np(y).copy() for y in layer.replicas_out]
 
 
-@pytest.mark.parametrize("name", ["cfg3", "mid", "cfg3-fixed", "cfg3-entry"])
+@pytest.mark.parametrize("name", ["cfg3", "mid", "cfg3-fixed", "cfg3-entry", "cfg4"])
 def test_layer_step_graph_replays_bitwise(name):
     # the decode workload (static bound 24, chunk-parallel gate with its workspace), a
     # mid-sized ragged batch on the running-total gate, the decode workload in the
-    # fixed-capacity layout (16 slots x 384 rows), and the decode workload with the fused
-    # entry step (its residual is restored before every run, since the step updates it)
-    cfg = resized("cfg4", (611, 0, 1203, 377), hidden=2048, inter=1024, num_experts=64) if name == "mid" \
-        else moe_synth.CONFIGS["cfg3"]
+    # fixed-capacity layout (16 slots x 384 rows), the decode workload with the fused
+    # entry step (its residual is restored before every run, since the step updates it),
+    # and the whole prefill batch (8 x 4096 rows, H = 7168), the step bench.py replays
+    if name == "mid":
+        cfg = resized("cfg4", (611, 0, 1203, 377), hidden=2048, inter=1024, num_experts=64)
+    else:
+        cfg = moe_synth.CONFIGS["cfg4" if name == "cfg4" else "cfg3"]
     say(f"[graph] {name}: {cfg.name} tokens={cfg.num_tokens}")
     inp = moe_synth.make_inputs(cfg)
     layer = build_layer(inp, "sum", seg_stride=384 if name == "cfg3-fixed" else 0)

@@ -4,6 +4,8 @@ on the same seeded inputs.
 Bar: bit-exact for the gather buffer, row validity, logits (exact-order gate), expert ids,
 the whole dispatch plan and the permuted rows; max relative error (infinity norm) within
 2e-2 for bf16 outputs and 1e-4 for the fp32 configuration."""
+from dataclasses import replace
+
 import numpy as np
 import pytest
 import torch
@@ -292,3 +294,16 @@ def test_fixed_capacity_layout(name, stride):
     flag = int(to_np(layer.plan.error_flag)[0])
     say(f"  fixed capacity {stride}: error_flag {flag}, counts {to_np(layer.plan.counts).tolist()[:8]}...")
     assert flag == (1 if stride < 20 else 0)
+
+
+@pytest.mark.parametrize("tokens,align,stride", [((8192,), 1, 0), ((8200,), 1, 0), ((8200,), 128, 0),
+                                                  ((8192,), 1, 64), ((8200,), 1, 64)])
+def test_dispatch_fused_and_scan_layouts(tokens, align, stride):
+    """The two ways dispatch derives the plan's layout: with 1024 local slots and top-8, 8192
+    rows make 64 count blocks of 1024 pairs, a 65536-entry count table that the place blocks
+    add up themselves; 8200 rows make 65 blocks and take the separate scan kernel.  Both,
+    with alignment 128 and with the fixed-capacity layout (64 rows per slot, the mean load,
+    so about half the slots overflow), give the oracle's plan bit for bit."""
+    cfg = replace(moe_synth.CONFIGS["cfg2"], num_tokens=tokens, hidden=256, inter=128,
+                  num_experts=1024, num_local=1024, top_k=8, name=f"dispatch-{tokens[0]}")
+    run_and_compare_inputs(moe_synth.make_inputs(cfg), "sum", align=align, seg_stride=stride)
