@@ -60,11 +60,18 @@ __global__ __launch_bounds__(D_THREADS) void count_kernel(const int32_t* __restr
     for (int e = threadIdx.x; e < m.El; e += D_THREADS) hist[e] = 0;
     __syncthreads();
     const int64_t base = static_cast<int64_t>(blockIdx.x) * kChunk;
-#pragma unroll 4
+    // all of the thread's ids are loaded before the first LDS add
+    int32_t idv[kPairsPerThread];
+#pragma unroll
+    for (int i = 0; i < kPairsPerThread; ++i) {
+        const int64_t f = base + i * D_THREADS + threadIdx.x;
+        idv[i] = f < P ? ids[f] : -1;
+    }
+#pragma unroll
     for (int i = 0; i < kPairsPerThread; ++i) {
         const int64_t f = base + i * D_THREADS + threadIdx.x;
         if (f < P) {
-            const int s = pair_slot(ids[f], f / k, m);
+            const int s = pair_slot(idv[i], f / k, m);
             if (s >= 0) atomicAdd(&hist[s], 1);
         }
     }
@@ -220,13 +227,21 @@ __global__ __launch_bounds__(D_THREADS) void place_kernel(
             c0[u] = i < n_tab ? sa.blk_counts[i] : 0;
         }
     }
-    // per-wave histogram of its pairs
-    for (int step = 0; step < kWaveChunk / kWave; ++step) {
+    // per-wave histogram of its pairs; the ids are all loaded before the first LDS add, and
+    // the slots stay in registers for the placement pass
+    constexpr int STEPS = kWaveChunk / kWave;
+    int32_t idv[STEPS];
+#pragma unroll
+    for (int step = 0; step < STEPS; ++step) {
         const int64_t f = wstart + step * kWave + lane;
-        if (f < P) {
-            const int s = pair_slot(ids[f], f / k, m);
-            if (s >= 0) atomicAdd(&whist[wv][s], 1);
-        }
+        idv[step] = f < P ? ids[f] : -1;
+    }
+    int slot[STEPS];
+#pragma unroll
+    for (int step = 0; step < STEPS; ++step) {
+        const int64_t f = wstart + step * kWave + lane;
+        slot[step] = f < P ? pair_slot(idv[step], f / k, m) : -1;
+        if (slot[step] >= 0) atomicAdd(&whist[wv][slot[step]], 1);
     }
     const int64_t* seg = seg_in;
     if constexpr (FUSED) {
@@ -336,10 +351,11 @@ __global__ __launch_bounds__(D_THREADS) void place_kernel(
     }
     __syncthreads();
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
-    for (int step = 0; step < kWaveChunk / kWave; ++step) {
+#pragma unroll
+    for (int step = 0; step < STEPS; ++step) {
         const int64_t f = wstart + step * kWave + lane;
         const bool inb = f < P;
-        const int s = inb ? pair_slot(ids[f], f / k, m) : -1;
+        const int s = slot[step];
         // lanes with the same slot: one ballot per distinct slot in the wave
         uint64_t pending = __ballot(s >= 0);
         uint64_t mine = 0;
