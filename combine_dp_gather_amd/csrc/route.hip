@@ -35,8 +35,8 @@ namespace {
 //     rows) when those blocks fit in one round on the CUs, else RB = 2 (128 rows), so a
 //     batch of half the prefill size still fills the chip;
 //   - small batches: one block per (row tile, expert tile, chunk) writes the chunk's sums to
-//     a workspace and a reduction adds them left to right -- chunks run in parallel, so the
-//     latency is one chunk's chain, not the whole row's.
+//     a workspace and the top-k kernel adds them left to right as it reads them -- chunks
+//     run in parallel, so the latency is one chunk's chain, not the whole row's.
 // Zero operands past H (ragged last chunk) change nothing: a chain started at +0 never holds
 // -0, so adding a +-0 product leaves every bit in place.
 typedef float floatx16_t __attribute__((ext_vector_type(16)));
@@ -564,21 +564,6 @@ __global__ __launch_bounds__(G_THREADS) void gate_chunk_kernel(const T* __restri
         }
 }
 
-// logits = ((+0 + part_0) + part_1) + ... in chunk order
-__global__ __launch_bounds__(256) void gate_reduce_kernel(const float* __restrict__ parts,
-                                                          const int32_t* __restrict__ row_valid,
-                                                          int64_t G, int64_t E, int64_t nchunks,
-                                                          float* __restrict__ logits) {
-    const int64_t n = G * E;
-    for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
-         i += static_cast<int64_t>(gridDim.x) * 256) {
-        float t = 0.f;
-        for (int64_t c = 0; c < nchunks; ++c) t = t + parts[c * n + i];
-        const int64_t g = i / E;
-        logits[i] = (row_valid == nullptr || row_valid[g] != 0) ? t : 0.f;
-    }
-}
-
 // ------------------------------------------------------------------ fast gate
 // FAST mode: logits on the bf16 matrix cores (v_mfma_f32_32x32x16_bf16, fp32 accumulate).
 // Products of bf16 values are exact in fp32, so only the summation order differs from the
@@ -816,6 +801,11 @@ __device__ __forceinline__ void sort_lane(double (&k)[V], double (&s)[V], int (&
 
 struct SelectArgs {
     const float* logits;
+    // small-batch exact gate: the chunk partial sums [nchunks][G][E]; the kernel then adds
+    // them in chunk order (the logits' definition) and writes the logits itself
+    const float* parts;
+    int64_t nchunks;
+    float* logits_out;
     const int32_t* row_valid;
     const float* bias;
     int64_t G;
@@ -832,14 +822,66 @@ __global__ __launch_bounds__(S_THREADS) void select_kernel(SelectArgs a) {
     const int E = a.E, k = a.k;
     int32_t* ids = a.ids + g * k;
     float* wout = a.w + g * k;
-    if (a.row_valid && a.row_valid[g] == 0) {  // pad row: no expert load
+    const bool pad = a.row_valid && a.row_valid[g] == 0;
+    float lv[V];
+    if (a.parts) {
+        // logits = ((+0 + part_0) + part_1) + ... in chunk order; pad rows get 0
+        const int64_t GE = a.G * E;
+        const float* pp = a.parts + g * E + lane * V;
+#pragma unroll
+        for (int j = 0; j < V; ++j) lv[j] = 0.f;
+        if (!pad) {
+            bool done = false;
+            if constexpr (V == 4) {
+                if ((E & 3) == 0) {  // 16-byte loads: every offset is a multiple of 4 floats
+                    if (lane * V < E) {
+                        // kLoads loads in flight, then their adds in chunk order
+                        constexpr int kLoads = 8;
+                        int64_t c = 0;
+                        for (; c + kLoads <= a.nchunks; c += kLoads) {
+                            float4 q[kLoads];
+#pragma unroll
+                            for (int u = 0; u < kLoads; ++u)
+                                q[u] = *reinterpret_cast<const float4*>(pp + (c + u) * GE);
+#pragma unroll
+                            for (int u = 0; u < kLoads; ++u) {
+                                lv[0] = lv[0] + q[u].x;
+                                lv[1] = lv[1] + q[u].y;
+                                lv[2] = lv[2] + q[u].z;
+                                lv[3] = lv[3] + q[u].w;
+                            }
+                        }
+                        for (; c < a.nchunks; ++c) {
+                            const float4 q = *reinterpret_cast<const float4*>(pp + c * GE);
+                            lv[0] = lv[0] + q.x;
+                            lv[1] = lv[1] + q.y;
+                            lv[2] = lv[2] + q.z;
+                            lv[3] = lv[3] + q.w;
+                        }
+                    }
+                    done = true;
+                }
+            }
+            if (!done)
+                for (int64_t c = 0; c < a.nchunks; ++c)
+#pragma unroll
+                    for (int j = 0; j < V; ++j)
+                        if (lane * V + j < E) lv[j] = lv[j] + pp[c * GE + j];
+        }
+#pragma unroll
+        for (int j = 0; j < V; ++j)
+            if (lane * V + j < E) a.logits_out[g * E + lane * V + j] = lv[j];
+    } else {
+#pragma unroll
+        for (int j = 0; j < V; ++j) lv[j] = lane * V + j < E ? a.logits[g * E + lane * V + j] : 0.f;
+    }
+    if (pad) {  // pad row: no expert load
         if (lane < k) {
             ids[lane] = -1;
             wout[lane] = 0.f;
         }
         return;
     }
-    const float* lg = a.logits + g * E;
     const bool grouped = a.kind == MOE_ROUTE_GROUPED_SIGMOID;
     double key[V], score[V];
     int id[V];
@@ -850,7 +892,7 @@ __global__ __launch_bounds__(S_THREADS) void select_kernel(SelectArgs a) {
         score[j] = 0.0;
         id[j] = kNone;
         if (e < E) {
-            const double l = static_cast<double>(lg[e]);
+            const double l = static_cast<double>(lv[j]);
             if (grouped) {
                 score[j] = sigmoid64(l);
                 key[j] = score[j] + (a.bias ? static_cast<double>(a.bias[e]) : 0.0);
@@ -985,9 +1027,12 @@ int lanes_per_expert_chunk(int E) {
 
 moe_status launch_select(const float* logits, const int32_t* row_valid, int64_t G,
                          const float* bias, const moe_route_cfg* c, int32_t* ids, float* w,
-                         hipStream_t stream) {
+                         hipStream_t stream, const float* parts = nullptr, int64_t nchunks = 0) {
     SelectArgs a;
     a.logits = logits;
+    a.parts = parts;
+    a.nchunks = nchunks;
+    a.logits_out = const_cast<float*>(logits);
     a.row_valid = row_valid;
     a.bias = c->kind == MOE_ROUTE_GROUPED_SIGMOID ? bias : nullptr;
     a.G = G;
@@ -1094,10 +1139,8 @@ extern "C" moe_status moe_route(const void* global_x, const int32_t* row_valid, 
                                static_cast<const float*>(global_x), static_cast<const float*>(w_router),
                                G, E, H, fast, parts);
         MOE_LAUNCH_CHECK();
-        int64_t rb = moe::ceil_div(G * E, 256);
-        if (rb > 4096) rb = 4096;
-        hipLaunchKernelGGL(moe::gate_reduce_kernel, dim3(static_cast<unsigned>(rb)), dim3(256), 0, stream,
-                           parts, row_valid, G, E, nch, logits);
+        // the select kernel adds the chunk partials in chunk order and writes the logits
+        return moe::launch_select(logits, row_valid, G, bias, cfg, topk_ids, topk_w, stream, parts, nch);
     } else if (rows128 && fast && H % moe::GATE_CHUNK == 0) {
         if (dt == MOE_BF16)
             hipLaunchKernelGGL(moe::gate_exact8_kernel<uint16_t>, tiles, dim3(moe::G8_THREADS), 0, stream,
