@@ -768,6 +768,31 @@ __device__ __forceinline__ void wave_argmax(double& v, int& idx) {
     }
 }
 
+// 32-bit code of a head for the fast pick: the key rounded to fp32 (round to nearest is
+// monotone, so a strictly larger code means a strictly larger fp64 key), -0 folded into +0
+// (they are equal keys), mapped to an unsigned integer that orders like the float; 0 for an
+// empty head.  Equal codes fall back to the exact (key, id) order.
+__device__ __forceinline__ uint32_t head_code(double k, int id) {
+    if (id == kNone) return 0u;
+    float f = static_cast<float>(k);
+    if (f == 0.0f) f = 0.0f;
+    const uint32_t b = __float_as_uint(f);
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+// wave maximum of an unsigned value, as a scalar: within each 16-lane row by DPP (the quad
+// butterflies, then the half-row and row mirrors), then the four row maxima
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    auto step = [](uint32_t x, uint32_t y) { return x > y ? x : y; };
+    v = step(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(v), static_cast<int>(v), 0xB1, 0xF, 0xF, false)));
+    v = step(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(v), static_cast<int>(v), 0x4E, 0xF, 0xF, false)));
+    v = step(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(v), static_cast<int>(v), 0x141, 0xF, 0xF, false)));
+    v = step(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(v), static_cast<int>(v), 0x140, 0xF, 0xF, false)));
+    const uint32_t r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
+    const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
+    return step(step(r0, r1), step(r2, r3));
+}
+
 __device__ __forceinline__ double wave_sum(double v) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
@@ -969,13 +994,24 @@ __global__ __launch_bounds__(S_THREADS) void select_kernel(SelectArgs a) {
             }
         }
     }
-    // k picks, best first: the wave argmax of the lanes' heads; the owner pops its head
+    // k picks, best first: the best of the lanes' heads, whose owner pops it.  The heads'
+    // 32-bit codes find it in one wave maximum; only when several heads share the largest
+    // code does the exact (key, id) argmax run among them.
     double my_score = 0.0;
     int my_id = -1;
     for (int t = 0; t < k; ++t) {
-        double v = key[0];
-        int i = id[0];
-        wave_argmax(v, i);
+        const uint32_t code = head_code(key[0], id[0]);
+        const uint32_t top = wave_max_u32(code);
+        const uint64_t cand = __ballot(code == top);
+        int i;
+        if (__popcll(cand) == 1) {
+            i = __builtin_amdgcn_readlane(id[0], __ffsll(static_cast<long long>(cand)) - 1);
+        } else {
+            const bool in = (cand >> lane) & 1ull;
+            double v = in ? key[0] : -__builtin_huge_val();
+            i = in ? id[0] : kNone;
+            wave_argmax(v, i);
+        }
         const int owner = i / V;
         const double sc = readlane_f64(score[0], owner);
         if (lane == owner) {

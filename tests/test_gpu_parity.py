@@ -285,6 +285,53 @@ def test_route_from_logits_ties_and_fake_balance():
     assert oracle.rel_err(w.cpu().numpy(), ref_w) < 1e-5
 
 
+def test_route_picks_near_ties():
+    """Keys that differ in fp64 but round to one fp32 value, exactly equal keys, and +0 / -0
+    logits: the picks follow the exact (key, lower id) order, as in the oracle."""
+    import combine_dp_gather_amd as m
+    rng = np.random.default_rng(7)
+    G, E = 64, 256
+    lg = rng.uniform(-1.0, 1.0, (G, E)).astype(np.float32)
+    for r in range(G):
+        # 24 experts spread over the lanes and groups at consecutive fp32 logits near 2: their
+        # sigmoids are ~2.5e-8 apart, below fp32's spacing there, so codes collide in runs
+        cols = rng.permutation(E)[:24]
+        base = np.float32(2.0) if r % 2 == 0 else np.float32(-0.25)
+        vals = [base]
+        for _ in range(23):
+            vals.append(np.nextafter(vals[-1], np.float32(np.inf), dtype=np.float32))
+        vals = np.array(vals, dtype=np.float32)
+        if r % 4 == 3:
+            vals[::3] = vals[0]  # exactly equal keys too: lower id first
+        lg[r, cols] = rng.permutation(vals)
+    bias = np.zeros(E, dtype=np.float32)
+    bias[rng.permutation(E)[:64]] = np.float32(2.0 ** -24)  # shifts a key by about one fp32 step
+    cfg = m.make_route_cfg("grouped", E, 8, 8, 4, 2, True)
+    for b in (None, bias):
+        ids = torch.empty((G, 8), dtype=torch.int32, device="cuda")
+        w = torch.empty((G, 8), dtype=torch.float32, device="cuda")
+        m.moe_route_from_logits(torch.from_numpy(lg).cuda(), None,
+                                None if b is None else torch.from_numpy(b).cuda(), cfg, ids, w)
+        torch.cuda.synchronize()
+        ref_ids, ref_w = oracle.select_grouped(lg, b, 8, 4, 8, True)
+        assert np.array_equal(ids.cpu().numpy(), ref_ids)
+        assert oracle.rel_err(w.cpu().numpy(), ref_w) < 1e-6
+    # softmax router: +0 and -0 logits are equal keys (lower id first), the rest below them
+    lg = -rng.uniform(0.5, 1.0, (16, 64)).astype(np.float32)
+    for r in range(16):
+        cols = rng.permutation(64)[:10]
+        lg[r, cols[:5]] = np.float32(0.0)
+        lg[r, cols[5:]] = np.float32(-0.0)
+    cfgs = m.make_route_cfg("softmax", 64, 6, renormalize=True)
+    ids = torch.empty((16, 6), dtype=torch.int32, device="cuda")
+    w = torch.empty((16, 6), dtype=torch.float32, device="cuda")
+    m.moe_route_from_logits(torch.from_numpy(lg).cuda(), None, None, cfgs, ids, w)
+    torch.cuda.synchronize()
+    ref_ids, ref_w = oracle.select_softmax(lg, 6, True)
+    assert np.array_equal(ids.cpu().numpy(), ref_ids)
+    assert oracle.rel_err(w.cpu().numpy(), ref_w) < 1e-5
+
+
 @pytest.mark.parametrize("name,stride", [("cfg3", 384), ("cfg3", 8), ("cfg2", 170), ("cfg2", 5)])
 def test_fixed_capacity_layout(name, stride):
     """The masked layout: slot e's rows at e * stride.  stride = G never overflows (decode:
