@@ -39,13 +39,15 @@ struct MapArgs {
 };
 
 // local slot of pair f (global row g = f / k, logical id l), or -1
-__device__ __forceinline__ int pair_slot(int32_t l, int64_t g, const MapArgs& m) {
+__device__ __forceinline__ int pair_slot(int32_t l, uint32_t f, uint32_t k, const MapArgs& m) {
     if (l < 0 || l >= m.E) return -1;
     int32_t p = l;
     if (m.phys_of) {
         int32_t nr = m.n_rep[l];
         nr = nr < 1 ? 1 : nr;
-        const int32_t r = static_cast<int32_t>(g % nr);
+        // pair indices fit in 32 bits (the launcher checks G * k < 2^31): 32-bit division
+        const uint32_t g = f / k;
+        const int32_t r = static_cast<int32_t>(g % static_cast<uint32_t>(nr));
         if (r >= m.max_rep) return -1;
         p = m.phys_of[static_cast<int64_t>(l) * m.max_rep + r];
     }
@@ -71,7 +73,7 @@ __global__ __launch_bounds__(D_THREADS) void count_kernel(const int32_t* __restr
     for (int i = 0; i < kPairsPerThread; ++i) {
         const int64_t f = base + i * D_THREADS + threadIdx.x;
         if (f < P) {
-            const int s = pair_slot(idv[i], f / k, m);
+            const int s = pair_slot(idv[i], static_cast<uint32_t>(f), static_cast<uint32_t>(k), m);
             if (s >= 0) atomicAdd(&hist[s], 1);
         }
     }
@@ -136,7 +138,8 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(
             }
             padded = stride;
         } else {
-            padded = (static_cast<int64_t>(run) + align - 1) / align * align;
+            const uint32_t al = static_cast<uint32_t>(align);
+            padded = static_cast<int64_t>((static_cast<uint32_t>(run) + al - 1u) / al) * al;
         }
         counts[e] = keep;
         kept[e] = keep;
@@ -205,7 +208,8 @@ __global__ __launch_bounds__(D_THREADS) void place_kernel(
     const int wv = tid / kWave;
     const int lane = lane_id();
     const int El = m.El;
-    for (int i = tid; i < D_WAVES * El; i += D_THREADS) whist[i / El][i % El] = 0;
+    for (int w = 0; w < D_WAVES; ++w)
+        for (int e = tid; e < El; e += D_THREADS) whist[w][e] = 0;
     if constexpr (FUSED) {
         for (int e = tid; e < El; e += D_THREADS) {
             tot[e] = 0;
@@ -240,18 +244,23 @@ __global__ __launch_bounds__(D_THREADS) void place_kernel(
 #pragma unroll
     for (int step = 0; step < STEPS; ++step) {
         const int64_t f = wstart + step * kWave + lane;
-        slot[step] = f < P ? pair_slot(idv[step], f / k, m) : -1;
+        slot[step] = f < P ? pair_slot(idv[step], static_cast<uint32_t>(f), static_cast<uint32_t>(k), m) : -1;
         if (slot[step] >= 0) atomicAdd(&whist[wv][slot[step]], 1);
     }
     const int64_t* seg = seg_in;
     if constexpr (FUSED) {
         const int64_t mine_end = static_cast<int64_t>(blockIdx.x) * El;  // entries of earlier blocks
+        // the thread's entries are i = tid + n * D_THREADS, n = 0, 1, ...; their slot i % El
+        // advances by D_THREADS % El per entry
+        const int e_step = D_THREADS % El;
+        int e_cur = tid % El;
         auto add = [&](int64_t i, int32_t c) {
             if (c) {
-                const int e = static_cast<int>(i % El);
-                atomicAdd(&tot[e], c);
-                if (i < mine_end) atomicAdd(&before[e], c);
+                atomicAdd(&tot[e_cur], c);
+                if (i < mine_end) atomicAdd(&before[e_cur], c);
             }
+            e_cur += e_step;
+            if (e_cur >= El) e_cur -= El;
         };
 #pragma unroll
         for (int u = 0; u < U; ++u) add(tid + u * D_THREADS, c0[u]);
@@ -280,7 +289,9 @@ __global__ __launch_bounds__(D_THREADS) void place_kernel(
                     if (run > sa.stride) over = 1;
                     padded[q] = sa.stride;
                 } else {
-                    padded[q] = (static_cast<int64_t>(run) + sa.align - 1) / sa.align * sa.align;
+                    // run < 2^31 and align < 2^31: the rounding fits 32 bits
+                    const uint32_t al = static_cast<uint32_t>(sa.align);
+                    padded[q] = static_cast<int64_t>((static_cast<uint32_t>(run) + al - 1u) / al) * al;
                 }
             }
             sum += padded[q];
@@ -319,16 +330,14 @@ __global__ __launch_bounds__(D_THREADS) void place_kernel(
         seg = seg_s;
         const bool publish = blockIdx.x == 0;
         // rows of a segment past its kept pairs (alignment pad, or unused capacity) hold no
-        // pair; the blocks share them
-        const int64_t gstride = static_cast<int64_t>(gridDim.x) * D_THREADS;
+        // pair; a thread takes slots tid, tid + D_THREADS, ... and the blocks share each
+        // slot's rows (block b writes rows b, b + gridDim.x, ... of the range)
         auto kept = [&](int e) -> int32_t {
             return sa.stride > 0 && tot[e] > sa.stride ? static_cast<int32_t>(sa.stride) : tot[e];
         };
-        for (int e = 0; e < El; ++e) {
-            const int64_t end = seg_s[e + 1];
-            for (int64_t r = seg_s[e] + kept(e) + static_cast<int64_t>(blockIdx.x) * D_THREADS + tid;
-                 r < end && r < cap; r += gstride)
-                sorted_pair[r] = -1;
+        for (int e = tid; e < El; e += D_THREADS) {
+            const int64_t end = seg_s[e + 1] < cap ? seg_s[e + 1] : cap;
+            for (int64_t r = seg_s[e] + kept(e) + blockIdx.x; r < end; r += gridDim.x) sorted_pair[r] = -1;
         }
         if (publish) {
             for (int e = tid; e < El; e += D_THREADS) sa.counts[e] = kept(e);
