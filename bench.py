@@ -215,6 +215,9 @@ def main():
     ap.add_argument("--entry", action="store_true",
                     help="run the fused entry step (residual add + RMSNorm + gather) in the step "
                          "in place of the plain gather; without it the fused step is timed apart")
+    ap.add_argument("--exit", action="store_true",
+                    help="run the fused exit (combine written straight into the replicas' buffers) "
+                         "in place of combine + scatter")
     ap.add_argument("--seg-stride", type=int, default=0, metavar="ROWS",
                     help="dispatch into the fixed-capacity layout, ROWS rows per local slot (the "
                          "global row count never overflows); 0: packed segments")
@@ -282,9 +285,14 @@ def main():
     stream = torch.cuda.current_stream()
     first = ("entry", lambda: layer.entry(reps, res_dev, gamma_dev, ent.eps)) if args.entry else \
         ("gather", lambda: layer.gather(reps))
-    names = [first[0], "route", "dispatch", "gemm_up", "gemm_down", "combine", "scatter"]
-    calls = [first[1], layer.route, layer.dispatch,
-             lambda: layer.experts_up(), lambda: layer.experts_down(), layer.combine, layer.scatter]
+    names = [first[0], "route", "dispatch", "gemm_up", "gemm_down"]
+    calls = [first[1], layer.route, layer.dispatch, lambda: layer.experts_up(), lambda: layer.experts_down()]
+    if args.exit:
+        names.append("combine_scatter")
+        calls.append(layer.combine_scatter)
+    else:
+        names += ["combine", "scatter"]
+        calls += [layer.combine, layer.scatter]
     if eplb_info is not None:
         # the statistics recorder's per-step work: this step's load of every physical slot
         import combine_dp_gather_amd as m
@@ -310,7 +318,7 @@ def main():
     tbo = None
     if args.tbo:
         from combine_dp_gather_amd.layer import TwoBatchOverlap
-        if args.entry or eplb_info is not None:
+        if args.entry or args.exit or eplb_info is not None:
             raise SystemExit("--tbo runs the plain six-call step only")
         tbo = TwoBatchOverlap(spec_of(cfg), w, layer.sizes, act, mode=args.mode, device=dev,
                               seg_stride=args.seg_stride)
@@ -391,6 +399,8 @@ def main():
         "gemm_down": gemm_work(mm, 2.0 * R * I * H, E_slots * H * I * wb + R * I * es + R * H * es),
         "combine": ("hbm", R * H * es + G * H * es + 8 * G * k),      # read R rows, write G rows
         "scatter": ("hbm", 2 * T * H * es),
+        # read R rows, write the T real rows straight to the replicas
+        "combine_scatter": ("hbm", R * H * es + T * H * es + 8 * T * k),
         "expert_load": ("hbm", 4 * G * k + 8 * EPLB["P"]),              # read the ids, add the bins
     }
     peaks = {"hbm": HBM_PEAK_GBS, "mfma32": FP32_MFMA_PEAK_TFLOPS, "mfma": BF16_MFMA_PEAK_TFLOPS,
@@ -463,6 +473,7 @@ def main():
                    "micro_batches": ("2, each replica halved, two streams pipelined by stages" if args.tbo
                                      else "1"),
                    "first_step": "fused residual add + RMSNorm + gather" if args.entry else "plain gather",
+                   "last_step": "fused combine + scatter" if args.exit else "combine, then scatter",
                    "dispatch_layout": (f"fixed capacity, {args.seg_stride} rows per slot" if args.seg_stride
                                        else "packed segments"),
                    "tokens": T, "global_rows": G, "gather_mode": args.mode,

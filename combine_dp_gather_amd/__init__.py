@@ -314,3 +314,14 @@ def moe_combine(y_perm: torch.Tensor, plan: PlanBuffers, topk_w: torch.Tensor, r
     check("moe_combine", lib().moe_combine(_ptr(y_perm), _dtype_code(out), ctypes.byref(plan.struct),
                                            _ptr(topk_w), float(routed_scale), H, _ptr(out),
                                            _stream(stream)))
+
+
+def moe_combine_scatter(y_perm: torch.Tensor, plan: PlanBuffers, topk_w: torch.Tensor,
+                        routed_scale: float, L: GatherLayout, replicas_out: Sequence[torch.Tensor],
+                        stream=None) -> None:
+    """The fused exit: combine written straight into the replicas' buffers (combine + scatter)."""
+    H = y_perm.shape[1]
+    arr = _ptr_array(replicas_out)
+    check("moe_combine_scatter", lib().moe_combine_scatter(
+        _ptr(y_perm), _dtype_code(y_perm), ctypes.byref(plan.struct), _ptr(topk_w),
+        float(routed_scale), H, ctypes.byref(L), ctypes.cast(arr, ctypes.c_void_p), _stream(stream)))

@@ -76,6 +76,8 @@ SIGNATURES = {
                                      ctypes.POINTER(ExpertWeights), c_i64, c_i64, c_vp, c_vp, c_sz,
                                      c_vp]),
     "moe_combine": (c_i32, [c_vp, c_i32, ctypes.POINTER(Plan), c_vp, c_f32, c_i64, c_vp, c_vp]),
+    "moe_combine_scatter": (c_i32, [c_vp, c_i32, ctypes.POINTER(Plan), c_vp, c_f32, c_i64,
+                                    ctypes.POINTER(GatherLayout), c_vp, c_vp]),
 }
 
 _lib = None

@@ -55,14 +55,14 @@ struct Vec<float> {  // 4 fp32 in 16 bytes
     __device__ static V pack(const float (&f)[N]) { return V{f[0], f[1], f[2], f[3]}; }
 };
 
+// global row g of the combine, written to the row at dst (the block's 256 threads)
 template <typename T>
-__global__ __launch_bounds__(C_THREADS) void combine_kernel(
-    const T* __restrict__ y, const int32_t* __restrict__ pair_row, const float* __restrict__ w,
-    int64_t G, int k, int64_t H, float scale, T* __restrict__ out) {
+__device__ __forceinline__ void combine_row(const T* __restrict__ y, const int32_t* __restrict__ pair_row,
+                                            const float* __restrict__ w, int64_t g, int k, int64_t H,
+                                            float scale, T* __restrict__ dst) {
     using VT = Vec<T>;
     using V = typename VT::V;
     const int lane = lane_id();
-    const int64_t g = blockIdx.x;
     // every wave reads the row's k pairs itself: lane j holds pair j, and the ballot of the
     // local ones is walked lowest lane first, i.e. in ascending j
     int32_t my_row = -1;
@@ -74,7 +74,7 @@ __global__ __launch_bounds__(C_THREADS) void combine_kernel(
     const uint64_t local = __ballot(my_row >= 0);
     const int64_t vec_per_row = H / VT::N;
     const V* __restrict__ yv = reinterpret_cast<const V*>(y);
-    V* __restrict__ ov = reinterpret_cast<V*>(out) + g * vec_per_row;
+    V* __restrict__ ov = reinterpret_cast<V*>(dst);
     for (int64_t c0 = threadIdx.x; c0 < vec_per_row; c0 += C_THREADS * kUnrollC) {
         float acc[kUnrollC][VT::N];
 #pragma unroll
@@ -128,6 +128,37 @@ __global__ __launch_bounds__(C_THREADS) void combine_kernel(
             st_stream(ov + c, VT::pack(acc[u]));
         }
     }
+}
+
+template <typename T>
+__global__ __launch_bounds__(C_THREADS) void combine_kernel(
+    const T* __restrict__ y, const int32_t* __restrict__ pair_row, const float* __restrict__ w,
+    int64_t G, int k, int64_t H, float scale, T* __restrict__ out) {
+    const int64_t g = blockIdx.x;
+    combine_row(y, pair_row, w, g, k, H, scale, out + g * H);
+}
+
+// Fused exit: the combine of every real row of up to kExitBatch replicas, written straight to
+// the replica's own buffer (the scatter's destination), so the global output buffer is never
+// written or read again.  Blocks are numbered over the replicas' real rows back to back; a
+// block finds its replica in the row prefix held in the kernel arguments.
+constexpr int kExitBatch = 32;
+struct ExitBatch {
+    void* ptr[kExitBatch];
+    int64_t off[kExitBatch];              // first global row of the replica's slot
+    int64_t first[kExitBatch + 1];        // real rows of the replicas before j; [cnt] = all
+    int32_t cnt;
+};
+
+template <typename T>
+__global__ __launch_bounds__(C_THREADS) void combine_scatter_kernel(
+    const T* __restrict__ y, const int32_t* __restrict__ pair_row, const float* __restrict__ w,
+    int k, int64_t H, float scale, ExitBatch b) {
+    const int64_t blk = blockIdx.x;
+    int i = 0;
+    while (i + 1 < b.cnt && blk >= b.first[i + 1]) ++i;
+    const int64_t r = blk - b.first[i];
+    combine_row(y, pair_row, w, b.off[i] + r, k, H, scale, static_cast<T*>(b.ptr[i]) + r * H);
 }
 
 // element-wise fallback for H not a multiple of the vector width or unaligned buffers
@@ -194,5 +225,60 @@ extern "C" moe_status moe_combine(const void* y_perm, moe_dtype dt, const moe_pl
                                routed_scale, static_cast<float*>(out));
     }
     MOE_LAUNCH_CHECK();
+    return MOE_OK;
+}
+
+extern "C" moe_status moe_combine_scatter(const void* y_perm, moe_dtype dt, const moe_plan* plan,
+                                          const float* topk_w, float routed_scale, int64_t H,
+                                          const moe_gather_layout_t* L, void* const* replica_y,
+                                          hipStream_t stream) {
+    using namespace moe;
+    MOE_CHECK_ARG(plan && L && replica_y && H > 0);
+    MOE_CHECK_ARG(dt == MOE_F32 || dt == MOE_BF16);
+    MOE_CHECK_ARG(plan->G >= 0 && plan->top_k >= 1 && plan->top_k <= 64);
+    MOE_CHECK_ARG(L->num_replicas >= 1 && L->num_replicas <= MOE_MAX_REPLICAS);
+    MOE_CHECK_ARG(L->rows == plan->G && L->offsets[L->num_replicas] == L->rows);
+    const int64_t G = plan->G;
+    const int k = plan->top_k;
+    const int vec = dt == MOE_BF16 ? 8 : 4;
+    int64_t real = 0;
+    for (int i = 0; i < L->num_replicas; ++i) {
+        MOE_CHECK_ARG(L->sizes[i] >= 0 && L->offsets[i] >= 0 && L->offsets[i + 1] >= L->offsets[i]);
+        MOE_CHECK_ARG(L->sizes[i] <= L->offsets[i + 1] - L->offsets[i]);
+        if (L->sizes[i] == 0) continue;
+        MOE_CHECK_ARG(replica_y[i] != nullptr);
+        // the fused form takes whole 16-byte vectors only; other shapes use combine + scatter
+        if (!aligned(replica_y[i], 16)) return MOE_ERR_UNSUPPORTED;
+        real += L->sizes[i];
+    }
+    if (G == 0 || real == 0) return MOE_OK;
+    MOE_CHECK_ARG(plan->pair_row && topk_w);
+    MOE_CHECK_ARG(plan->cap == 0 || y_perm != nullptr);
+    if (H % vec != 0 || (y_perm != nullptr && !aligned(y_perm, 16))) return MOE_ERR_UNSUPPORTED;
+    MOE_CHECK_ARG(real < 0x7fffffff);
+    for (int first = 0; first < L->num_replicas; first += kExitBatch) {
+        const int cnt = (L->num_replicas - first) < kExitBatch ? (L->num_replicas - first) : kExitBatch;
+        ExitBatch b{};
+        b.cnt = cnt;
+        int64_t rows = 0;
+        for (int j = 0; j < cnt; ++j) {
+            b.ptr[j] = replica_y[first + j];
+            b.off[j] = L->offsets[first + j];
+            b.first[j] = rows;
+            rows += L->sizes[first + j];
+        }
+        b.first[cnt] = rows;
+        if (rows == 0) continue;
+        const dim3 grid(static_cast<unsigned>(rows));
+        if (dt == MOE_BF16)
+            hipLaunchKernelGGL(combine_scatter_kernel<uint16_t>, grid, dim3(C_THREADS), 0, stream,
+                               static_cast<const uint16_t*>(y_perm), plan->pair_row, topk_w, k, H,
+                               routed_scale, b);
+        else
+            hipLaunchKernelGGL(combine_scatter_kernel<float>, grid, dim3(C_THREADS), 0, stream,
+                               static_cast<const float*>(y_perm), plan->pair_row, topk_w, k, H,
+                               routed_scale, b);
+        MOE_LAUNCH_CHECK();
+    }
     return MOE_OK;
 }

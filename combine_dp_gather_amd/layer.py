@@ -18,7 +18,7 @@ from . import (PlanBuffers, layout_offsets, layout_sizes, make_expert_map, make_
                make_route_cfg, moe_combine, moe_dispatch, moe_dispatch_workspace_size,
                moe_expert_gemm, moe_expert_gemm_down, moe_expert_gemm_up,
                moe_entry_gather, moe_expert_gemm_workspace_size, moe_gather, moe_gather_layout, moe_route,
-               moe_route_workspace_size, moe_scatter)
+               moe_route_workspace_size, moe_scatter, moe_combine_scatter)
 
 
 def _to_dev(a: Optional[np.ndarray], device, bf16: bool = False) -> Optional[torch.Tensor]:
@@ -165,9 +165,17 @@ class MoELayer:
     def scatter(self, replicas_out=None):
         moe_scatter(self.layout, self.out, self.replicas_out if replicas_out is None else replicas_out)
 
-    def forward(self, replicas, entry=None) -> List[torch.Tensor]:
+    def combine_scatter(self, replicas_out=None):
+        """The fused exit in place of combine + scatter (same bits; ``out`` is not written)."""
+        dst = self.replicas_out if replicas_out is None else replicas_out
+        if self.G:
+            moe_combine_scatter(self.y_perm, self.plan, self.topk_w, self.spec.routed_scale,
+                                self.layout, dst)
+
+    def forward(self, replicas, entry=None, fused_exit: bool = False) -> List[torch.Tensor]:
         """One step.  ``entry = (residual, norm_weight, eps)`` runs the fused entry step on
-        ``replicas`` (the attention outputs) instead of the plain gather."""
+        ``replicas`` (the attention outputs) instead of the plain gather; ``fused_exit`` runs
+        the fused combine + scatter."""
         if entry is None:
             self.gather(replicas)
         else:
@@ -175,8 +183,11 @@ class MoELayer:
         self.route()
         self.dispatch()
         self.experts()
-        self.combine()
-        self.scatter()
+        if fused_exit:
+            self.combine_scatter()
+        else:
+            self.combine()
+            self.scatter()
         return self.replicas_out
 
 

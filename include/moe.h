@@ -345,6 +345,26 @@ moe_status moe_combine(const void* y_perm, moe_dtype dt, const moe_plan* plan,
                        hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------------
+ * moe_combine_scatter -- the fused exit: moe_combine followed by moe_scatter in one pass,
+ * y_i[r] = (combine row offset_i + r) for r < sizes[i], written straight into the replica's
+ * buffer; the [G, H] output buffer is neither written nor read.  The same bits as the two
+ * calls.  It is the exit-side counterpart of moe_entry_gather: the SGLang page's section
+ * "边界判定的融合" folds the work at the layer boundary into the gather pass, and here the
+ * scatter's copy is folded into the combine that produces its rows.  Pad rows of MAX_LEN
+ * slots are computed nowhere (the scatter does not copy them).
+ *   y_perm, dt, plan, topk_w, routed_scale, H: as for moe_combine (plan->G must equal L->rows)
+ *   L          layout from moe_gather_layout (the one the gather used)
+ *   replica_y  host array of W device pointers to [sizes[i], H] dt (NULL allowed if 0 rows)
+ * Errors: MOE_ERR_INVALID_ARG as moe_combine and moe_scatter; MOE_ERR_UNSUPPORTED when H is
+ * not a whole number of 16-byte vectors or y_perm or a replica buffer is not 16-byte aligned
+ * (then use moe_combine and moe_scatter).
+ * ---------------------------------------------------------------------------------------- */
+moe_status moe_combine_scatter(const void* y_perm, moe_dtype dt, const moe_plan* plan,
+                               const float* topk_w, float routed_scale, int64_t H,
+                               const moe_gather_layout_t* L, void* const* replica_y,
+                               hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------
  * Expert-load statistics and expert placement (EPLB; SGLang page, section "EPLB:专家分布不均
  * 怎么办").
  * ---------------------------------------------------------------------------------------- */

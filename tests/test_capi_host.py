@@ -138,6 +138,20 @@ def test_argument_errors_return_before_any_launch(m):
                                1 << 30, None) == _lib.MOE_ERR_INVALID_ARG
     # combine: bad dtype
     assert lib.moe_combine(1, 9, ctypes.byref(plan), 1, 1.0, 64, 1, None) == _lib.MOE_ERR_INVALID_ARG
+    # fused exit: bad dtype; layout rows that do not match the plan; an unaligned replica
+    # buffer is refused before anything is enqueued
+    L = m.moe_gather_layout([3, 5], "sum")
+    ptrs = (ctypes.c_void_p * 2)(256, 512)
+    assert lib.moe_combine_scatter(1, 9, ctypes.byref(plan), 1, 1.0, 64, ctypes.byref(L), ptrs,
+                                   None) == _lib.MOE_ERR_INVALID_ARG
+    assert lib.moe_combine_scatter(1, _lib.MOE_BF16, ctypes.byref(plan), 1, 1.0, 64, ctypes.byref(L),
+                                   ptrs, None) == _lib.MOE_ERR_INVALID_ARG
+    plan8 = _lib.Plan(1, 1, 1, 1, 1, 1, 16, 8, 2, 4, 1, 0)
+    bad = (ctypes.c_void_p * 2)(256, 520)
+    assert lib.moe_combine_scatter(256, _lib.MOE_BF16, ctypes.byref(plan8), 256, 1.0, 64, ctypes.byref(L),
+                                   bad, None) == _lib.MOE_ERR_UNSUPPORTED
+    assert lib.moe_combine_scatter(256, _lib.MOE_BF16, ctypes.byref(plan8), 256, 1.0, 64, None, ptrs,
+                                   None) == _lib.MOE_ERR_INVALID_ARG
 
 
 def test_workspace_sizes(m):

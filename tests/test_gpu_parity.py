@@ -190,6 +190,31 @@ def test_gather_then_scatter_identity_and_idle_rows():
         assert torch.all(gx[torch.from_numpy(valid == 0).cuda()] == 0)
 
 
+@pytest.mark.parametrize("name,mode,tokens", [("cfg2", "sum", None), ("cfg2", "max", None),
+                                               ("cfg3", "max", None), ("cfg2", "sum", (3, 0, 40, 0, 7, 1))])
+def test_fused_exit_equals_combine_then_scatter(name, mode, tokens):
+    """moe_combine_scatter writes the same bits into the replica buffers as moe_combine followed
+    by moe_scatter (ragged and idle replicas, both padding modes; the oracle already checks the
+    two-call path), and leaves the global output buffer untouched."""
+    cfg = moe_synth.CONFIGS[name] if tokens is None else resized(name, tokens)
+    inp = moe_synth.make_inputs(cfg)
+    say(f"[fused-exit] {cfg.name} tokens={cfg.num_tokens} mode={mode}")
+    layer = build_layer(inp, mode)
+    reps = replicas_to_device(inp)
+    two = [r.clone() for r in layer.forward(reps)]
+    layer.out.fill_(3.0)
+    fresh = [torch.full_like(r, 5.0) for r in two]
+    layer.combine_scatter(fresh)
+    torch.cuda.synchronize()
+    for a, b in zip(two, fresh):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert torch.all(layer.out == 3.0)
+    again = [r.clone() for r in layer.forward(reps, fused_exit=True)]
+    torch.cuda.synchronize()
+    for a, b in zip(two, again):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
 def test_identity_experts_combine_returns_weighted_sum():
     import combine_dp_gather_amd as m
     cfg = resized("cfg3", (50, 31), hidden=1024, inter=512, num_experts=64, num_local=64)
