@@ -13,20 +13,21 @@ from gpu_helpers import build_layer, replicas_to_device, resized, say, to_np
 pytestmark = pytest.mark.gpu
 
 
-def _outputs(layer):
+def _outputs(layer, with_out=True):
     # sorted_pair is defined up to num_rows; rows past it keep whatever an earlier step left
     rows = int(to_np(layer.plan.num_rows)[0])
     return [to_np(layer.global_x).copy(), to_np(layer.logits).copy(), to_np(layer.topk_ids).copy(),
-            to_np(layer.plan.sorted_pair)[:rows].copy(), to_np(layer.out).copy()] + \
-           [to_np(y).copy() for y in layer.replicas_out]
+            to_np(layer.plan.sorted_pair)[:rows].copy()] + \
+           ([to_np(layer.out).copy()] if with_out else []) + [to_np(y).copy() for y in layer.replicas_out]
 
 
-@pytest.mark.parametrize("name", ["cfg3", "mid", "cfg3-fixed", "cfg3-entry", "cfg4"])
+@pytest.mark.parametrize("name", ["cfg3", "mid", "cfg3-fixed", "cfg3-entry", "cfg3-exit", "cfg4"])
 def test_layer_step_graph_replays_bitwise(name):
     # the decode workload (static bound 24, chunk-parallel gate with its workspace), a
     # mid-sized ragged batch on the running-total gate, the decode workload in the
     # fixed-capacity layout (16 slots x 384 rows), the decode workload with the fused
-    # entry step (its residual is restored before every run, since the step updates it),
+    # entry step (its residual is restored before every run, since the step updates it), the
+    # decode workload with the fused exit (the global output buffer is then not written),
     # and the whole prefill batch (8 x 4096 rows, H = 7168), the step bench.py replays
     if name == "mid":
         cfg = resized("cfg4", (611, 0, 1203, 377), hidden=2048, inter=1024, num_experts=64)
@@ -48,21 +49,23 @@ def test_layer_step_graph_replays_bitwise(name):
             for a, b in zip(entry[0], res0):
                 a.copy_(b)
 
-    def outputs():
-        return _outputs(layer) + ([to_np(r).copy() for r in entry[0]] if entry else [])
+    fused_exit = name == "cfg3-exit"
 
-    layer.forward(reps, entry)
+    def outputs():
+        return _outputs(layer, not fused_exit) + ([to_np(r).copy() for r in entry[0]] if entry else [])
+
+    layer.forward(reps, entry, fused_exit)
     torch.cuda.synchronize()
     eager = outputs()
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        layer.forward(reps, entry)
+        layer.forward(reps, entry, fused_exit)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        layer.forward(reps, entry)
+        layer.forward(reps, entry, fused_exit)
     torch.cuda.synchronize()
     for replay in range(3):
         # eager work between replays: scribble over every output of the step
