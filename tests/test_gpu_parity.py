@@ -369,13 +369,16 @@ def test_fixed_capacity_layout(name, stride):
 
 
 @pytest.mark.parametrize("tokens,align,stride", [((8192,), 1, 0), ((8200,), 1, 0), ((8200,), 128, 0),
-                                                  ((8192,), 1, 64), ((8200,), 1, 64)])
+                                                  ((8192,), 1, 64), ((8200,), 1, 64),
+                                                  ((1024,), 1, 0), ((1025,), 1, 0), ((1024,), 128, 0),
+                                                  ((1024,), 1, 8), ((700, 0, 324), 1, 0)])
 def test_dispatch_fused_and_scan_layouts(tokens, align, stride):
     """The two ways dispatch derives the plan's layout: with 1024 local slots and top-8, 8192
     rows make 64 count blocks of 1024 pairs, a 65536-entry count table that the place blocks
-    add up themselves; 8200 rows make 65 blocks and take the separate scan kernel.  Both,
-    with alignment 128 and with the fixed-capacity layout (64 rows per slot, the mean load,
-    so about half the slots overflow), give the oracle's plan bit for bit."""
+    add up themselves; 8200 rows make 65 blocks and take the separate scan kernel.  Small
+    batches (8 or 9 count blocks, one with an idle replica) take the first way.  All of them,
+    with alignment 128 and with the fixed-capacity layout (64 or 8 rows per slot, so slots
+    overflow), give the oracle's plan bit for bit."""
     cfg = replace(moe_synth.CONFIGS["cfg2"], num_tokens=tokens, hidden=256, inter=128,
                   num_experts=1024, num_local=1024, top_k=8, name=f"dispatch-{tokens[0]}")
     run_and_compare_inputs(moe_synth.make_inputs(cfg), "sum", align=align, seg_stride=stride)
