@@ -445,7 +445,8 @@ def main():
     roof.pop("peak_kind")
     fmt = "fp8" if mm == "mfma8" else "bf16"
     kname = ("grouped_gemm_fp8_kernel" if fmt == "fp8"
-             else f"grouped_gemm_bf16_kernel<true, {'true' if fp8w else 'false'}>")
+             else f"grouped_gemm_bf16_kernel<true, {'true' if fp8w else 'false'}>" if bf
+             else "simple_gemm_kernel<float, true>")
     roof["kernel"] = kname + (" (gate+up SwiGLU" + (", with its activation quantisation" if fmt == "fp8" else "")
                               + ")")
     from combine_dp_gather_amd.profiling import read_traffic_summary
