@@ -191,7 +191,8 @@ def test_gather_then_scatter_identity_and_idle_rows():
 
 
 @pytest.mark.parametrize("name,mode,tokens", [("cfg2", "sum", None), ("cfg2", "max", None),
-                                               ("cfg3", "max", None), ("cfg2", "sum", (3, 0, 40, 0, 7, 1))])
+                                               ("cfg3", "max", None), ("cfg2", "sum", (3, 0, 40, 0, 7, 1)),
+                                               ("cfg1", "sum", None)])
 def test_fused_exit_equals_combine_then_scatter(name, mode, tokens):
     """moe_combine_scatter writes the same bits into the replica buffers as moe_combine followed
     by moe_scatter (ragged and idle replicas, both padding modes; the oracle already checks the
@@ -207,7 +208,7 @@ def test_fused_exit_equals_combine_then_scatter(name, mode, tokens):
     layer.combine_scatter(fresh)
     torch.cuda.synchronize()
     for a, b in zip(two, fresh):
-        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))  # bitwise, any dtype
     assert torch.all(layer.out == 3.0)
     again = [r.clone() for r in layer.forward(reps, fused_exit=True)]
     torch.cuda.synchronize()
