@@ -333,15 +333,20 @@ def test_route_picks_near_ties():
     bias = np.zeros(E, dtype=np.float32)
     bias[rng.permutation(E)[:64]] = np.float32(2.0 ** -24)  # shifts a key by about one fp32 step
     cfg = m.make_route_cfg("grouped", E, 8, 8, 4, 2, True)
-    for b in (None, bias):
-        ids = torch.empty((G, 8), dtype=torch.int32, device="cuda")
-        w = torch.empty((G, 8), dtype=torch.float32, device="cuda")
-        m.moe_route_from_logits(torch.from_numpy(lg).cuda(), None,
-                                None if b is None else torch.from_numpy(b).cuda(), cfg, ids, w)
-        torch.cuda.synchronize()
-        ref_ids, ref_w = oracle.select_grouped(lg, b, 8, 4, 8, True)
-        assert np.array_equal(ids.cpu().numpy(), ref_ids)
-        assert oracle.rel_err(w.cpu().numpy(), ref_w) < 1e-6
+    # the 64 constructed rows, and the same rows tiled to 2049 with every 7th a pad row
+    big = np.tile(lg, (33, 1))[:2049]
+    rv_big = (np.arange(2049) % 7 != 3).astype(np.int32)
+    for rows, rv in ((lg, None), (big, rv_big)):
+        Gr = rows.shape[0]
+        for b in (None, bias):
+            ids = torch.empty((Gr, 8), dtype=torch.int32, device="cuda")
+            w = torch.empty((Gr, 8), dtype=torch.float32, device="cuda")
+            m.moe_route_from_logits(torch.from_numpy(rows).cuda(), None if rv is None else torch.from_numpy(rv).cuda(),
+                                    None if b is None else torch.from_numpy(b).cuda(), cfg, ids, w)
+            torch.cuda.synchronize()
+            ref_ids, ref_w = oracle.select_grouped(rows, b, 8, 4, 8, True, row_valid=rv)
+            assert np.array_equal(ids.cpu().numpy(), ref_ids), (Gr, b is None)
+            assert oracle.rel_err(w.cpu().numpy(), ref_w) < 1e-6
     # softmax router: +0 and -0 logits are equal keys (lower id first), the rest below them
     lg = -rng.uniform(0.5, 1.0, (16, 64)).astype(np.float32)
     for r in range(16):
@@ -349,13 +354,15 @@ def test_route_picks_near_ties():
         lg[r, cols[:5]] = np.float32(0.0)
         lg[r, cols[5:]] = np.float32(-0.0)
     cfgs = m.make_route_cfg("softmax", 64, 6, renormalize=True)
-    ids = torch.empty((16, 6), dtype=torch.int32, device="cuda")
-    w = torch.empty((16, 6), dtype=torch.float32, device="cuda")
-    m.moe_route_from_logits(torch.from_numpy(lg).cuda(), None, None, cfgs, ids, w)
-    torch.cuda.synchronize()
-    ref_ids, ref_w = oracle.select_softmax(lg, 6, True)
-    assert np.array_equal(ids.cpu().numpy(), ref_ids)
-    assert oracle.rel_err(w.cpu().numpy(), ref_w) < 1e-5
+    for rows in (lg, np.tile(lg, (131, 1))[:2095]):
+        Gr = rows.shape[0]
+        ids = torch.empty((Gr, 6), dtype=torch.int32, device="cuda")
+        w = torch.empty((Gr, 6), dtype=torch.float32, device="cuda")
+        m.moe_route_from_logits(torch.from_numpy(rows).cuda(), None, None, cfgs, ids, w)
+        torch.cuda.synchronize()
+        ref_ids, ref_w = oracle.select_softmax(rows, 6, True)
+        assert np.array_equal(ids.cpu().numpy(), ref_ids), Gr
+        assert oracle.rel_err(w.cpu().numpy(), ref_w) < 1e-5
 
 
 @pytest.mark.parametrize("name,stride", [("cfg3", 384), ("cfg3", 8), ("cfg2", 170), ("cfg2", 5)])
