@@ -285,7 +285,7 @@ __global__ __launch_bounds__(M_THREADS, 1) void grouped_gemm_bf16_kernel(GemmArg
         _Pragma("unroll") for (int ks_ = 0; ks_ < 2; ++ks_)                                   \
             _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_)                                  \
                 _Pragma("unroll") for (int j_ = 0; j_ < 4; ++j_) acc[i_][j_] =                \
-                    __builtin_amdgcn_mfma_f32_32x32x16_bf16(FA[ks_][i_], FB[ks_][j_],         \
+                    __builtin_amdgcn_mfma_f32_32x32x16_bf16(FB[ks_][j_], FA[ks_][i_],         \
                                                             acc[i_][j_], 0, 0, 0);            \
     } while (0)
         // Pipeline: K slices of BK in two LDS stages; slice kt lives in stage kt % 2 and is
@@ -438,27 +438,35 @@ __global__ __launch_bounds__(M_THREADS, 1) void grouped_gemm_bf16_kernel(GemmArg
 #undef MOE_LOAD_HALF
 #undef MOE_BROW
 
-        // ---- epilogue: lane holds rows 8*(v/4) + 4*(lane/32) + v%4 of column lane%32.
-        // The lane's row base is made opaque per tile so the 64 row offsets below stay
-        // immediates instead of being hoisted out of the tile loop into registers.
-        int rbase = wm * 128 + (lane >> 5) * 4;
-        asm volatile("" : "+v"(rbase));
-        const int64_t colbase = UP ? static_cast<int64_t>(nt) * UP_COLS + wn * 64 + (lane & 31)
-                                   : static_cast<int64_t>(nt) * BN + wn * 128 + (lane & 31);
-        uint16_t* cbase = a.C + (row0 + rbase) * a.N + colbase;
+        // ---- epilogue: the weight fragment is the MFMAs' first operand, so each 32x32
+        // accumulator block holds its output block transposed: lane l owns row l%32 of the
+        // block and, for q = 0..3, its four consecutive columns 8*q + 4*(l/32) + 0..3, which
+        // go out as one 8-byte store (a row's 16 bytes at each q come from lanes l and l+32).
+        const int rloc = wm * 128 + (lane & 31);
+        const int64_t colbase = UP ? static_cast<int64_t>(nt) * UP_COLS + wn * 64 + (lane >> 5) * 4
+                                   : static_cast<int64_t>(nt) * BN + wn * 128 + (lane >> 5) * 4;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
+            if (rloc + i * 32 >= static_cast<int>(nrows)) continue;
+            uint16_t* cp = a.C + (row0 + rloc + i * 32) * a.N + colbase;
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int roff = i * 32 + (v >> 2) * 8 + (v & 3);
-                if (rbase + roff >= static_cast<int>(nrows)) continue;
-                uint16_t* cp = cbase + static_cast<int64_t>(roff) * a.N;
+            for (int q = 0; q < 4; ++q) {
                 if (UP) {
-                    cp[0] = f32_to_bf16(silu_mul(acc[i][0][v], acc[i][2][v]));
-                    cp[32] = f32_to_bf16(silu_mul(acc[i][1][v], acc[i][3][v]));
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        float h[4];
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) h[t] = silu_mul(acc[i][j][4 * q + t], acc[i][j + 2][4 * q + t]);
+                        *reinterpret_cast<uint2*>(cp + j * 32 + q * 8) =
+                            make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
+                    }
                 } else {
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) cp[j * 32] = f32_to_bf16(acc[i][j][v]);
+                    for (int j = 0; j < 4; ++j) {
+                        const floatx16_t& c = acc[i][j];
+                        *reinterpret_cast<uint2*>(cp + j * 32 + q * 8) =
+                            make_uint2(pack_bf16x2(c[4 * q], c[4 * q + 1]), pack_bf16x2(c[4 * q + 2], c[4 * q + 3]));
+                    }
                 }
             }
         }
@@ -560,7 +568,7 @@ bool mfma_ok(moe_dtype act_dt, int64_t H, int64_t I, const void* A, const void* 
     const bool small = 2 * H * I * 2 < (int64_t(1) << 32) && int64_t(BM) * H * 2 < (int64_t(1) << 32) &&
                        int64_t(BM) * I * 2 < (int64_t(1) << 32);
     return act_dt == MOE_BF16 && H % BN == 0 && I % UP_COLS == 0 && small && aligned(A, 16) &&
-           aligned(B, 16) && aligned(C, 2);
+           aligned(B, 16) && aligned(C, 8);
 }
 
 moe_status run_stage(bool up, const void* A, moe_dtype act_dt, const moe_plan* plan,
