@@ -10,7 +10,9 @@
 //
 // bf16 path (gfx950 v_mfma_f32_32x32x16_bf16, fp32 accumulate):
 //   - block tile 256 rows x 256 columns, 4 waves in a 2x2 grid, each wave 128x128 = 4x4 MFMA
-//     blocks (256 fp32 accumulators per lane, in AGPRs);
+//     blocks (256 fp32 accumulators per lane, in AGPRs).  The weight fragment is the MFMAs'
+//     first operand, so each accumulator block holds its output block transposed and a lane
+//     writes four consecutive columns of one row per 8-byte store;
 //   - up kernel: the 256 columns are 128 gate columns and the same 128 up columns, so each
 //     lane holds gate and up for identical (row, i) and applies SiLU*up in registers;
 //   - operands move global -> LDS by buffer DMA (no register staging) in 64-deep K slices:
