@@ -313,7 +313,11 @@ size_t moe_expert_gemm_workspace_size(int64_t cap, int64_t H, int64_t I, moe_dty
  *             rows >= num_rows are not written
  *   workspace device, >= moe_expert_gemm_workspace_size(...) bytes, 256-byte aligned
  * Accumulation is fp32; h and y are rounded to act_dt (nearest even).
- * bf16 / fp8 need H % 256 == 0 and I % 128 == 0, else MOE_ERR_UNSUPPORTED. */
+ * bf16 / fp8 need H % 256 == 0 and I % 128 == 0, else MOE_ERR_UNSUPPORTED.
+ * The matrix-core kernels also need x_perm, h and the weights 16-byte aligned and each
+ * GEMM's output (h, y_perm) 8-byte aligned.  Otherwise bf16 weights run a slow per-element
+ * kernel; fp8 weights return MOE_ERR_UNSUPPORTED with bf16 activations and
+ * MOE_ERR_INVALID_ARG for misaligned inputs with e4m3 activations. */
 moe_status moe_expert_gemm(const void* x_perm, moe_dtype act_dt, const moe_plan* plan,
                            const moe_expert_weights* w, int64_t H, int64_t I, void* y_perm,
                            void* workspace, size_t workspace_bytes, hipStream_t stream);
