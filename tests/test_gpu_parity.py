@@ -134,6 +134,38 @@ def test_multi_tile_ragged_segments():
     run_and_compare(cfg)
 
 
+def test_expert_gemm_unaligned_buffers_take_element_path():
+    # an output 2 bytes off an 8-byte boundary cannot take the tile epilogue's 8-byte stores,
+    # nor an input off 16 bytes its DMAs: the bf16 GEMMs then run the per-element kernel,
+    # held to the same bar against the oracle
+    from combine_dp_gather_amd import moe_expert_gemm_down, moe_expert_gemm_up
+    cfg = resized("cfg4", (300, 0, 517), hidden=2048, inter=1024, num_experts=64)
+    layer, ref = run_and_compare(cfg)
+    rp = ref["plan"]
+    rows = min(rp["num_rows"], rp["cap"])
+    real = np.zeros(rows, dtype=bool)
+    for e in range(cfg.num_local):
+        a = int(rp["seg_offsets"][e])
+        real[a:min(a + int(rp["counts"][e]), rows)] = True
+    assert real.any()
+    H, I = cfg.hidden, cfg.inter
+    hbuf = torch.zeros(layer.h.numel() + 1, dtype=layer.h.dtype, device=layer.h.device)
+    h_odd = hbuf[1:].view(layer.h.shape)
+    ybuf = torch.zeros(layer.y_perm.numel() + 1, dtype=layer.y_perm.dtype, device=layer.y_perm.device)
+    y_odd = ybuf[1:].view(layer.y_perm.shape)
+    layer.experts_up()  # h from the tile path
+    say("[parity] element-path GEMMs: h and y_perm 2 bytes off alignment")
+    moe_expert_gemm_up(layer.x_perm, layer.plan, layer.w.ew, H, I, h_odd, layer.gemm_ws)
+    moe_expert_gemm_down(h_odd, layer.plan, layer.w.ew, H, I, y_odd, layer.gemm_ws)
+    torch.cuda.synchronize()
+    tol = tol_for(cfg)
+    h_tile = oracle.as_f32(to_np(layer.h)[:rows])[real]
+    err_h = oracle.rel_err(oracle.as_f32(to_np(h_odd)[:rows])[real], h_tile)
+    err_y = oracle.rel_err(oracle.as_f32(to_np(y_odd)[:rows])[real], ref["y_perm"][real])
+    say(f"  h vs tile path {err_h:.3e}, y_perm vs oracle {err_y:.3e}")
+    assert err_h < tol and err_y < tol
+
+
 def test_alignment_128():
     cfg = resized("cfg3", (17, 40, 0, 33), hidden=2048, inter=1024)
     run_and_compare(cfg, "sum", align=128)
