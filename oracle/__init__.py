@@ -208,12 +208,9 @@ def as_f32(a: np.ndarray) -> np.ndarray:
     return np.ascontiguousarray(a, dtype=np.float32)
 
 
-GATE_CHUNK = 128
-
-
 def gate_logits(x: np.ndarray, w: np.ndarray, row_valid: Optional[np.ndarray] = None) -> np.ndarray:
-    """fp32 router logits: fmaf chain in ascending h inside each 128-wide chunk, chunk sums
-    added left to right in fp32 (see moe_oracle.c)."""
+    """fp32 router logits: one fmaf chain per (g, e) in ascending h from +0 (see
+    moe_oracle.c); 0 for rows with row_valid == 0."""
     lib = _load()
     xf, wf = as_f32(x), as_f32(w)
     G, H = xf.shape

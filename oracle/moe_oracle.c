@@ -20,19 +20,16 @@
 
 /* ------------------------------------------------------------------ gate logits
  * Router logits logits[g,e] = sum_h x[g,h] * w[e,h] (op_gate of the SGLang page, section
- * "operations 与 yield").  The pages fix no precision or order; the reading taken is fp32
- * accumulation in chunks of GATE_CHUNK = 128 consecutive h:
- *     total = +0
- *     for each chunk c (ascending):  part = +0
- *                                    for h in chunk c (ascending): part = fmaf(x[g,h], w[e,h], part)
- *                                    total = total + part          (fp32 add)
- * (the last chunk may be shorter), so that the integer routing decision made from these
- * logits can be reproduced bit for bit while the chunks can be evaluated independently.
- * Rows with row_valid[g] == 0 get logits 0.  The loops visit eight experts per h step; each
- * accumulator keeps its own ascending chain, so this is the definition above, unchanged.
+ * "operations 与 yield").  The pages fix no precision or order; the reading taken is the
+ * plain dot product in fp32 as one chain of fused multiply-adds in ascending h:
+ *     acc = +0
+ *     for h = 0 .. H-1:  acc = fmaf(x[g,h], w[e,h], acc)
+ *     logits[g,e] = acc
+ * so that the integer routing decision made from these logits can be reproduced bit for
+ * bit.  Rows with row_valid[g] == 0 get logits 0.  The loops visit eight experts per h
+ * step; each accumulator keeps its own ascending chain, so this is the definition above,
+ * unchanged.
  */
-#define GATE_CHUNK 128
-
 void oracle_gate_logits(const float* x, const float* w, const int32_t* row_valid,
                         int64_t G, int64_t E, int64_t H, float* logits) {
     #pragma omp parallel for schedule(dynamic, 4)
@@ -44,16 +41,11 @@ void oracle_gate_logits(const float* x, const float* w, const int32_t* row_valid
         }
         for (int64_t e0 = 0; e0 < E; e0 += 8) {
             int64_t ne = (E - e0) < 8 ? (E - e0) : 8;
-            float total[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-            for (int64_t c0 = 0; c0 < H; c0 += GATE_CHUNK) {
-                int64_t c1 = c0 + GATE_CHUNK < H ? c0 + GATE_CHUNK : H;
-                float part[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-                for (int64_t h = c0; h < c1; ++h)
-                    for (int64_t j = 0; j < ne; ++j)
-                        part[j] = fmaf(xr[h], w[(e0 + j) * H + h], part[j]);
-                for (int64_t j = 0; j < ne; ++j) total[j] = total[j] + part[j];
-            }
-            for (int64_t j = 0; j < ne; ++j) logits[g * E + e0 + j] = total[j];
+            float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+            for (int64_t h = 0; h < H; ++h)
+                for (int64_t j = 0; j < ne; ++j)
+                    acc[j] = fmaf(xr[h], w[(e0 + j) * H + h], acc[j]);
+            for (int64_t j = 0; j < ne; ++j) logits[g * E + e0 + j] = acc[j];
         }
     }
 }

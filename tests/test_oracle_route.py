@@ -36,16 +36,13 @@ def round_f32(v: Fraction) -> float:
     return s * float(Fraction(fl) * Fraction(2) ** (e - 23))
 
 
-def fma_chain(x, w, chunk=128):
-    """fp32 fma chain per 128-wide chunk, chunk sums added left to right, in exact rational
-    arithmetic rounded to fp32 at every step."""
-    total = 0.0
-    for c0 in range(0, len(x), chunk):
-        part = 0.0
-        for a, b in zip(x[c0:c0 + chunk], w[c0:c0 + chunk]):
-            part = round_f32(Fraction(float(a)) * Fraction(float(b)) + Fraction(part))
-        total = round_f32(Fraction(total) + Fraction(part))
-    return total
+def fma_chain(x, w):
+    """One fp32 fma chain over h in ascending order from +0, in exact rational arithmetic
+    rounded to fp32 at every step."""
+    acc = 0.0
+    for a, b in zip(x, w):
+        acc = round_f32(Fraction(float(a)) * Fraction(float(b)) + Fraction(acc))
+    return acc
 
 
 def test_round_f32_matches_numpy_cast():
@@ -57,7 +54,7 @@ def test_round_f32_matches_numpy_cast():
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_gate_logits_bitwise_vs_exact_fma(dtype):
     rng = np.random.default_rng(1)
-    G, E, H = 4, 5, 300      # two full chunks and a ragged one
+    G, E, H = 4, 5, 300
     x = rng.standard_normal((G, H)).astype(np.float32)
     w = (rng.standard_normal((E, H)) * 0.02).astype(np.float32)
     if dtype == "bf16":
@@ -70,33 +67,52 @@ def test_gate_logits_bitwise_vs_exact_fma(dtype):
 
 
 def test_gate_logits_bf16_equals_plain_f32_adds():
-    # bf16 x bf16 products are exact in fp32, so each chunk's fma chain is a chain of fp32
-    # adds; chunk sums then add left to right
+    # bf16 x bf16 products are exact in fp32, so the fma chain is a chain of IEEE fp32 adds
+    # of the exact products in ascending h, which numpy's float32 add computes independently
     rng = np.random.default_rng(2)
     H = 300
     x = moe_synth.to_bf16_bits(rng.standard_normal((4, H)).astype(np.float32))
     w = moe_synth.to_bf16_bits((rng.standard_normal((9, H)) * 0.02).astype(np.float32))
     xf, wf = oracle.as_f32(x), oracle.as_f32(w)
-    total = np.zeros((4, 9), dtype=np.float32)
-    for c0 in range(0, H, 128):
-        part = np.zeros((4, 9), dtype=np.float32)
-        for h in range(c0, min(c0 + 128, H)):
-            part = part + (xf[:, h:h + 1] * wf[None, :, h])
-        total = total + part
-    assert np.array_equal(oracle.gate_logits(x, w), total)
+    acc = np.zeros((4, 9), dtype=np.float32)
+    for h in range(H):
+        acc = acc + (xf[:, h:h + 1] * wf[None, :, h])
+    assert np.array_equal(oracle.gate_logits(x, w), acc)
 
 
-def test_gate_chunk_order_matters():
-    # the chunked order differs from one long chain for some inputs: the pin above would
-    # catch an oracle that silently dropped the chunking
+def test_gate_logits_order_closed_form():
+    # products 2^24, 1, -2^24 in this h order: ascending from +0 gives 2^24 (2^24 + 1 is a
+    # tie that rounds to the even 2^24), then 0.  Any other order, a pairwise tree or the
+    # exact sum gives 1: the ascending single chain is the only reading that yields 0.
+    w = np.ones((1, 3), dtype=np.float32)
+    x = np.array([[2.0 ** 24, 1.0, -(2.0 ** 24)]], dtype=np.float32)
+    assert oracle.gate_logits(x, w)[0, 0] == 0.0
+    # reversed h order: -2^24 + 1 is exact, + 2^24 gives 1
+    assert oracle.gate_logits(x[:, ::-1].copy(), w)[0, 0] == 1.0
+    # the same three products at h = 127, 128, 129 among zero products: 128-wide chunk
+    # sums would give 2^24 + (1 - 2^24) = 1, the single chain still 0
+    xz = np.zeros((1, 203), dtype=np.float32)
+    xz[0, 127:130] = x[0]
+    assert oracle.gate_logits(xz, np.ones((1, 203), dtype=np.float32))[0, 0] == 0.0
+
+
+def test_gate_is_one_chain_not_chunked():
+    # a chunked reading (128-wide fma chains, chunk sums added left to right) differs from
+    # the single chain on ordinary inputs, so the pins above would catch an oracle that
+    # chunked h; count how many logits (and top-2 picks) the two readings disagree on
     rng = np.random.default_rng(5)
     x = moe_synth.to_bf16_bits(rng.standard_normal((64, 1024)).astype(np.float32))
     w = moe_synth.to_bf16_bits((rng.standard_normal((8, 1024)) * 0.02).astype(np.float32))
     xf, wf = oracle.as_f32(x), oracle.as_f32(w)
-    chain = np.zeros((64, 8), dtype=np.float32)
-    for h in range(1024):
-        chain = chain + (xf[:, h:h + 1] * wf[None, :, h])
-    assert not np.array_equal(oracle.gate_logits(x, w), chain)
+    total = np.zeros((64, 8), dtype=np.float32)
+    for c0 in range(0, 1024, 128):
+        part = np.zeros((64, 8), dtype=np.float32)
+        for h in range(c0, c0 + 128):
+            part = part + (xf[:, h:h + 1] * wf[None, :, h])
+        total = total + part
+    got = oracle.gate_logits(x, w)
+    assert not np.array_equal(got, total)
+    assert np.count_nonzero(got != total) > 8
 
 
 def test_gate_logits_one_hot_and_pad_rows():
