@@ -425,7 +425,7 @@ def main():
         rc = m.make_route_cfg(cfg.route, E, k, cfg.n_group, cfg.topk_group, cfg.group_topn, cfg.renormalize,
                               gate="fast")
         ms = _time_ms(lambda: m.moe_route(layer.global_x, layer.row_valid, w.router, w.bias, rc, layer.logits,
-                                          layer.topk_ids, layer.topk_w, layer.route_ws), iters=10)
+                                          layer.topk_ids, layer.topk_w), iters=10)
         fb = G * H * 2 + E * H * 2 + G * E * 4 + G * k * 8
         kernels["route_fast"] = {"ms": round(ms, 4), "bound": "hbm", "achieved": round(fb / (ms / 1e3) / 1e9, 2),
                                  "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(fb / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),

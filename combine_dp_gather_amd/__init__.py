@@ -132,20 +132,13 @@ def make_route_cfg(kind: str, num_experts: int, top_k: int, n_group: int = 1, to
     return RouteCfg(k, num_experts, top_k, n_group, topk_group, group_topn, int(renormalize), mode)
 
 
-def moe_route_workspace_size(G: int, num_experts: int, H: int) -> int:
-    return int(lib().moe_route_workspace_size(G, num_experts, H))
-
-
 def moe_route(global_x: torch.Tensor, row_valid: torch.Tensor, w_router: torch.Tensor,
               bias: Optional[torch.Tensor], cfg: RouteCfg, logits: torch.Tensor,
-              topk_ids: torch.Tensor, topk_w: torch.Tensor,
-              workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+              topk_ids: torch.Tensor, topk_w: torch.Tensor, stream=None) -> None:
     G, H = global_x.shape
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     check("moe_route", lib().moe_route(_ptr(global_x), _ptr(row_valid), G, H, _dtype_code(global_x),
                                        _ptr(w_router), _ptr(bias), ctypes.byref(cfg), _ptr(logits),
-                                       _ptr(topk_ids), _ptr(topk_w), _ptr(workspace), ws_bytes,
-                                       _stream(stream)))
+                                       _ptr(topk_ids), _ptr(topk_w), _stream(stream)))
 
 
 def moe_route_from_logits(logits: torch.Tensor, row_valid: Optional[torch.Tensor],

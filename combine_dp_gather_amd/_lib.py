@@ -59,9 +59,8 @@ SIGNATURES = {
     "moe_eplb_logical_to_physical": (c_i32, [c_vp, c_vp, c_i32, c_i32, c_i32, c_vp, c_vp]),
     "moe_entry_gather": (c_i32, [ctypes.POINTER(GatherLayout), c_vp, c_vp, c_vp, ctypes.c_float, c_i64,
                                  c_i32, c_vp, c_vp, c_vp]),
-    "moe_route_workspace_size": (c_sz, [c_i64, c_i32, c_i64]),
     "moe_route": (c_i32, [c_vp, c_vp, c_i64, c_i64, c_i32, c_vp, c_vp, ctypes.POINTER(RouteCfg),
-                          c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
+                          c_vp, c_vp, c_vp, c_vp]),
     "moe_route_from_logits": (c_i32, [c_vp, c_vp, c_i64, c_vp, ctypes.POINTER(RouteCfg), c_vp, c_vp,
                                       c_vp]),
     "moe_dispatch_workspace_size": (c_sz, [c_i64, c_i32, c_i32]),

@@ -7,7 +7,7 @@
 //
 // Exact-order gate.  The integer routing decision depends on the logits bit for bit, so
 // the gate fixes one accumulation order (below) and runs it on the fp32 matrix cores, with
-// 32-deep K slices staged through LDS as fp32 (bf16 widened exactly), double-buffered.
+// slices of h staged through LDS as fp32 (bf16 widened exactly), double-buffered.
 #include <float.h>
 
 #include "gemm_common.h"
@@ -17,34 +17,29 @@ namespace moe {
 namespace {
 
 // ------------------------------------------------------------------ gate logits
-// Exact-order gate.  Reading of the gate's arithmetic (the pages fix none): fp32 fused
-// multiply-adds in ascending h inside each 128-wide chunk of h, starting from +0; the chunk
-// sums are added left to right to a running fp32 total starting from +0.
-//
-// On the matrix cores: v_mfma_f32_32x32x2f32 adds two products to each 32x32 accumulator
-// per instruction as two fused multiply-adds in sequence (the lower half-wave's k first), each
-// with one rounding -- bit for bit the fmaf chain of the definition (checked against the
-// sequential fma chain, and shown to differ from a single-rounding pair, on bf16-valued and
-// full fp32 operands).  Lanes 0-31 therefore carry the even k of each pair and lanes 32-63
-// the odd k; LDS keeps every row's slice split by parity (evens, then odds) so that one
-// 16-byte read gives a lane its operands for four consecutive instructions.  A wave owns
-// 32*RB rows x 128 experts as 4*RB 32x32 chains (RB row blocks x 4 expert blocks).
-//   - large batches: a block of 64*RB rows x 256 experts (x read from HBM once) walks all
-//     of h in 32-wide slices, prefetching across chunk boundaries; after a chunk's last slice
-//     its sums are added to the running total and the chains restart from +0.  RB = 1 (64
-//     rows) when those blocks fit in one round on the CUs, else RB = 2 (128 rows), so a
-//     batch of half the prefill size still fills the chip;
-//   - small batches: one block per (row tile, expert tile, chunk) writes the chunk's sums to
-//     a workspace and the top-k kernel adds them left to right as it reads them -- chunks
-//     run in parallel, so the latency is one chunk's chain, not the whole row's.
-// Zero operands past H (ragged last chunk) change nothing: a chain started at +0 never holds
-// -0, so adding a +-0 product leaves every bit in place.
+// Exact-order gate.  Reading of the gate's arithmetic (the pages fix none): the plain dot
+// product as one chain of fp32 fused multiply-adds in ascending h, starting from +0:
+//     acc = +0;  for h = 0 .. H-1:  acc = fmaf(x[g,h], w[e,h], acc)
+// Two matrix-core instructions run this chain bit for bit; both were checked against the
+// sequential fma chain, and shown to differ from other orders and from a single rounding,
+// on full-range fp32, bf16-valued and subnormal operands:
+//   - v_mfma_f32_32x32x2f32 adds two products to each accumulator of a 32x32 block per
+//     instruction as two fused multiply-adds in sequence, the lower half-wave's k first;
+//   - v_mfma_f32_16x16x4f32 adds four products to each accumulator of a 16x16 block as four
+//     fused multiply-adds in sequence, lane group 0 (lanes 0-15) first, then 1, 2, 3.
+// A chain therefore advances 2 h per 64-cycle instruction on the first and 4 h per 32-cycle
+// instruction on the second: whatever the batch, one chain costs at least about 8 cycles
+// per h on the 16x16 form.  Large batches use 32x32 chains (fewer LDS reads per flop, x read
+// from HBM once per 256 experts); small and medium batches give every wave one 16x16 block
+// so that the chains of a small batch spread over as many SIMDs as it has blocks.
+// Padding: operand columns past H are staged as x = -0 and w = +0.  Their product is -0,
+// and adding -0 leaves every fp32 value in place, +0 and -0 included, so a padded chain has
+// the bits of the unpadded one.
 typedef float floatx16_t __attribute__((ext_vector_type(16)));
-constexpr int GATE_CHUNK = 128;
-constexpr int GB_M = 128, GB_N = 256, GB_K = 32, G_THREADS = 256;
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+constexpr int GB_N = 256, GB_K = 32;
+constexpr int G_THREADS = 256;
 constexpr int G_PAD = 4;
-constexpr int SLICES_PER_CHUNK = GATE_CHUNK / GB_K;
-static_assert(GATE_CHUNK % GB_K == 0, "a slice never straddles two chunks");
 
 template <typename T>
 struct GateIO;
@@ -52,49 +47,49 @@ struct GateIO;
 template <>
 struct GateIO<uint16_t> {  // bf16 rows; 16-byte piece = 8 k values
     static constexpr int kChunk = 8;
-    typedef uint2 Quad;  // 4 consecutive k
-    __device__ static float val(const Quad& q, int t) {
-        const uint32_t w = t < 2 ? q.x : q.y;
-        return __uint_as_float((t & 1) ? (w & 0xffff0000u) : (w << 16));
-    }
+    static constexpr uint16_t kNegZero = 0x8000u;
 };
 template <>
 struct GateIO<float> {  // fp32 rows; 16-byte piece = 4 k values
     static constexpr int kChunk = 4;
-    typedef float4 Quad;
-    __device__ static float val(const Quad& q, int t) {
-        return t == 0 ? q.x : (t == 1 ? q.y : (t == 2 ? q.z : q.w));
-    }
+    static constexpr float kNegZero = -0.0f;
 };
 
-// 16 bytes of row r starting at column k; columns at or past H (or rows past `rows`) are 0
+// element t (0..3) of a float4
+__device__ __forceinline__ float f4_at(const float4& q, int t) {
+    return t == 0 ? q.x : (t == 1 ? q.y : (t == 2 ? q.z : q.w));
+}
+
+// 16 bytes of row r starting at column k; columns at or past H read `pad`, rows past `rows`
+// read 0 (those rows' outputs are never stored)
 template <typename T>
 __device__ __forceinline__ uint4 load_piece(const T* __restrict__ src, int64_t rows, int64_t H,
-                                            int64_t r, int64_t k) {
+                                            int64_t r, int64_t k, T pad) {
     constexpr int C = GateIO<T>::kChunk;
     uint4 v = {0, 0, 0, 0};
-    if (r >= rows || k >= H) return v;
+    if (r >= rows) return v;
     const T* p = src + r * H + k;
     T t[C];
 #pragma unroll
-    for (int q = 0; q < C; ++q) t[q] = (k + q < H) ? p[q] : T(0);
+    for (int q = 0; q < C; ++q) t[q] = (k + q < H) ? p[q] : pad;
     __builtin_memcpy(&v, t, 16);
     return v;
 }
 
 typedef unsigned int gate_u32x4 __attribute__((ext_vector_type(4)));
 
-// Staging of one slice: x rows [m0, m0+BM) and w rows [n0, n0+256), columns k0 .. k0+GB_K,
-// in LDS as [row][k] with row stride LD.  The fast load is a 16-byte buffer load per piece
-// from a descriptor over the block's rows only, so rows past G (or E) read as zeros; the
-// element-wise load covers a slice that runs past H and unaligned inputs.
-template <typename T, int BM = GB_M, int NT = G_THREADS>
+// ---- large batches: 32x32 chains
+// Staging of one 32-wide slice of h: x rows [m0, m0+BM) and w rows [n0, n0+256), in LDS as
+// fp32 [row][k] with row stride LD, each row split by parity (evens, then odds) so that one
+// 16-byte read gives a lane its operands for four consecutive 32x32x2 instructions (lanes
+// 0-31 carry the even k of each pair, lanes 32-63 the odd k).  The loads are 16-byte buffer
+// loads from descriptors over the block's rows only, so rows past G (or E) read as zeros.
+template <typename T, int BM, int NT>
 struct GateStage {
     static constexpr int C = GateIO<T>::kChunk;
     static constexpr int LD = GB_K + G_PAD;
     static constexpr int PER_ROW = GB_K / C;  // 16-byte pieces per row
     static constexpr int XCH = BM * PER_ROW / NT;
-    static constexpr int WRITES = (XCH + GB_N * PER_ROW / NT) * 2;  // LDS stores per thread
     static constexpr int WCH = GB_N * PER_ROW / NT;
     static_assert(XCH * NT == BM * PER_ROW && WCH * NT == GB_N * PER_ROW, "whole pieces per thread");
     uint4 xr[XCH], wr[WCH];
@@ -112,22 +107,8 @@ struct GateStage {
             wr[p] = make_uint4(v.x, v.y, v.z, v.w);
         }
     }
-    __device__ void load_slow(const T* x, const T* w, int64_t G, int64_t E,
-                              int64_t H, int64_t m0, int64_t n0, int64_t k0) {
-#pragma unroll
-        for (int p = 0; p < XCH; ++p) {
-            const int idx = threadIdx.x + p * NT;
-            xr[p] = load_piece(x, G, H, m0 + idx / PER_ROW, k0 + (idx % PER_ROW) * C);
-        }
-#pragma unroll
-        for (int p = 0; p < WCH; ++p) {
-            const int idx = threadIdx.x + p * NT;
-            wr[p] = load_piece(w, E, H, n0 + idx / PER_ROW, k0 + (idx % PER_ROW) * C);
-        }
-    }
-    // LDS holds fp32 (bf16 widens here, once per element) split by parity: slice column k
-    // of a row sits at k / 2 (even k) or GB_K / 2 + k / 2 (odd k).  `kk` is the piece's
-    // first column in the slice.
+    // slice column k of a row sits at k / 2 (even k) or GB_K / 2 + k / 2 (odd k); `kk` is the
+    // piece's first column in the slice
     __device__ static void put(float* row, int kk, const uint4& v) {
         if constexpr (sizeof(T) == 2) {
             reinterpret_cast<float4*>(row + kk / 2)[0] =
@@ -156,262 +137,22 @@ struct GateStage {
     }
 };
 
-// Chunks [ch0, ch1) of h for the block's 128 x 256 tile (chunk c = slices 4c .. 4c+3, slice
-// s = columns 32s .. 32s+31).  Each chunk's chains start from +0 and see only matrix-core
-// adds, so they stay in the accumulator registers; with TOTAL the chunk's sums are then
-// added to `total`, else (a single chunk) they are left in acc.  `fast` (block-uniform): the
-// inputs are 16-byte aligned with rows a multiple of 16 bytes.
-template <typename T, bool TOTAL, int RB = 2>
-__device__ __forceinline__ void gate_chunks(const T* x, const T* w, int64_t G, int64_t E, int64_t H,
-                                            int64_t m0, int64_t n0, int64_t ch0, int64_t ch1,
-                                            bool fast, float* xs, float* ws, floatx16_t (&acc)[4 * RB],
-                                            floatx16_t (&total)[4 * RB]) {
-    constexpr int BM = 64 * RB;
-    typedef GateStage<T, BM> S;
-    typedef typename GateIO<float>::Quad Quad;
-    constexpr int LD = S::LD;
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int wm = wv >> 1, wn = wv & 1;
-    // lane's operand rows: x rows wm*32*RB + 32 rb + lane%32, w rows wn*128 + 32 cb + lane%32;
-    // its k parity (lane / 32) picks the even or odd half of the row
-    const int par = (lane >> 5) * (GB_K / 2);
-    const int arow = wm * 32 * RB + (lane & 31);
-    const int brow = wn * 128 + (lane & 31);
-    // descriptors over the block's own rows: byte offsets stay below 256 * H * sizeof(T)
-    const int64_t xrows = G - m0 < BM ? G - m0 : BM;
-    const int64_t wrows = E - n0 < GB_N ? E - n0 : GB_N;
-    const __amdgpu_buffer_rsrc_t rx =
-        gemm::make_rsrc_uniform(x + m0 * H, static_cast<uint32_t>(xrows * H * static_cast<int64_t>(sizeof(T))));
-    const __amdgpu_buffer_rsrc_t rw =
-        gemm::make_rsrc_uniform(w + n0 * H, static_cast<uint32_t>(wrows * H * static_cast<int64_t>(sizeof(T))));
-    uint32_t xoff[S::XCH], woff[S::WCH];
-#pragma unroll
-    for (int p = 0; p < S::XCH; ++p) {
-        const int idx = threadIdx.x + p * G_THREADS;
-        xoff[p] = static_cast<uint32_t>(((idx / S::PER_ROW) * H + (idx % S::PER_ROW) * S::C) * sizeof(T));
-    }
-#pragma unroll
-    for (int p = 0; p < S::WCH; ++p) {
-        const int idx = threadIdx.x + p * G_THREADS;
-        woff[p] = static_cast<uint32_t>(((idx / S::PER_ROW) * H + (idx % S::PER_ROW) * S::C) * sizeof(T));
-    }
-    S st;
-    const int64_t s_begin = ch0 * SLICES_PER_CHUNK, s_end = ch1 * SLICES_PER_CHUNK;
-    auto load = [&](int64_t sl) {
-        const int64_t k0 = sl * GB_K;
-        if (fast && k0 + GB_K <= H)
-            st.load_fast(rx, rw, xoff, woff, k0);
-        else
-            st.load_slow(x, w, G, E, H, m0, n0, k0);
-    };
-    load(s_begin);
-    st.store(xs, ws);
-    __syncthreads();
-    for (int64_t ch = ch0; ch < ch1; ++ch) {
-#pragma unroll
-        for (int c = 0; c < 4 * RB; ++c)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[c][v] = 0.f;
-#pragma unroll 1
-        for (int q = 0; q < SLICES_PER_CHUNK; ++q) {
-            const int64_t sl = ch * SLICES_PER_CHUNK + q;
-            const int cur = static_cast<int>((sl - s_begin) & 1);
-            const float* xc = xs + cur * (BM * LD) + arow * LD + par;
-            const float* wc = ws + cur * (GB_N * LD) + brow * LD + par;
-            const bool more = sl + 1 < s_end;
-            if (more) load(sl + 1);
-#pragma unroll
-            for (int kq = 0; kq < GB_K / 8; ++kq) {  // four k pairs per 16-byte read
-                float4 qa[RB], qb[4];
-#pragma unroll
-                for (int rb = 0; rb < RB; ++rb) qa[rb] = *reinterpret_cast<const float4*>(xc + rb * 32 * LD + kq * 4);
-#pragma unroll
-                for (int cb = 0; cb < 4; ++cb) qb[cb] = *reinterpret_cast<const float4*>(wc + cb * 32 * LD + kq * 4);
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-#pragma unroll
-                    for (int rb = 0; rb < RB; ++rb) {
-                        const float av = GateIO<float>::val(qa[rb], t);
-#pragma unroll
-                        for (int cb = 0; cb < 4; ++cb)
-                            acc[rb * 4 + cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(
-                                av, GateIO<float>::val(qb[cb], t), acc[rb * 4 + cb], 0, 0, 0);
-                    }
-                }
-            }
-            if (more) st.store(xs + (cur ^ 1) * (BM * LD), ws + (cur ^ 1) * (GB_N * LD));
-            __syncthreads();
-        }
-        if (TOTAL) {
-#pragma unroll
-            for (int c = 0; c < 4 * RB; ++c)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) total[c][v] = total[c][v] + acc[c][v];
-        }
-    }
-}
-
-// Fast path of gate_chunks: 16-byte aligned inputs and H a multiple of the chunk width, so
-// every slice is whole.  The slice loop has no branches (the last slice re-stages itself into
-// the idle buffer, which nothing reads), the refill's global loads are issued at the top of
-// a slice, and its LDS stores are spread between the MFMAs of the slice's second half: with
-// one wave per SIMD the matrix pipe keeps issuing while the next slice is staged.  Each
-// chain's MFMAs keep their k order, so the bits are those of gate_chunks.
-template <typename T, bool TOTAL, int RB>
-__device__ __forceinline__ void gate_chunks_pipe(const T* x, const T* w, int64_t G, int64_t E, int64_t H,
-                                                 int64_t m0, int64_t n0, int64_t ch0, int64_t ch1,
-                                                 float* xs, float* ws, floatx16_t (&acc)[4 * RB],
-                                                 floatx16_t (&total)[4 * RB]) {
-    constexpr int BM = 64 * RB;
-    typedef GateStage<T, BM> S;
-    constexpr int LD = S::LD;
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int wm = wv >> 1, wn = wv & 1;
-    const int par = (lane >> 5) * (GB_K / 2);
-    const int arow = wm * 32 * RB + (lane & 31);
-    const int brow = wn * 128 + (lane & 31);
-    const int64_t xrows = G - m0 < BM ? G - m0 : BM;
-    const int64_t wrows = E - n0 < GB_N ? E - n0 : GB_N;
-    const __amdgpu_buffer_rsrc_t rx =
-        gemm::make_rsrc_uniform(x + m0 * H, static_cast<uint32_t>(xrows * H * static_cast<int64_t>(sizeof(T))));
-    const __amdgpu_buffer_rsrc_t rw =
-        gemm::make_rsrc_uniform(w + n0 * H, static_cast<uint32_t>(wrows * H * static_cast<int64_t>(sizeof(T))));
-    uint32_t xoff[S::XCH], woff[S::WCH];
-#pragma unroll
-    for (int p = 0; p < S::XCH; ++p) {
-        const int idx = threadIdx.x + p * G_THREADS;
-        xoff[p] = static_cast<uint32_t>(((idx / S::PER_ROW) * H + (idx % S::PER_ROW) * S::C) * sizeof(T));
-    }
-#pragma unroll
-    for (int p = 0; p < S::WCH; ++p) {
-        const int idx = threadIdx.x + p * G_THREADS;
-        woff[p] = static_cast<uint32_t>(((idx / S::PER_ROW) * H + (idx % S::PER_ROW) * S::C) * sizeof(T));
-    }
-    // the second half of a slice issues 2 * 4 * RB * 4 MFMAs; spread the stores over them
-    constexpr int HALF_MFMA = 32 * RB;
-    constexpr int PER_STORE = HALF_MFMA / S::WRITES > 0 ? HALF_MFMA / S::WRITES : 1;
-    S st;
-    const int64_t s_end = ch1 * SLICES_PER_CHUNK;
-    st.load_fast(rx, rw, xoff, woff, ch0 * SLICES_PER_CHUNK * GB_K);
-    st.store(xs, ws);
-    __syncthreads();
-    static_assert(SLICES_PER_CHUNK % 2 == 0, "the stage of a slice is its index inside the chunk, mod 2");
-    for (int64_t ch = ch0; ch < ch1; ++ch) {
-#pragma unroll
-        for (int c = 0; c < 4 * RB; ++c)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[c][v] = 0.f;
-#pragma unroll
-        for (int q = 0; q < SLICES_PER_CHUNK; ++q) {
-            const int64_t sl = ch * SLICES_PER_CHUNK + q;
-            const int cur = q & 1;
-            const int64_t nxt = sl + 1 < s_end ? sl + 1 : sl;
-            const float* xc = xs + cur * (BM * LD) + arow * LD + par;
-            const float* wc = ws + cur * (GB_N * LD) + brow * LD + par;
-            __builtin_amdgcn_sched_barrier(0);
-            st.load_fast(rx, rw, xoff, woff, nxt * GB_K);
-            // four k pairs per 16-byte read of each operand row
-#define MOE_GATE_KQ(KQ)                                                                         \
-    do {                                                                                        \
-        float4 qa[RB], qb[4];                                                                   \
-        _Pragma("unroll") for (int rb = 0; rb < RB; ++rb) qa[rb] =                              \
-            *reinterpret_cast<const float4*>(xc + rb * 32 * LD + (KQ) * 4);                     \
-        _Pragma("unroll") for (int cb = 0; cb < 4; ++cb) qb[cb] =                               \
-            *reinterpret_cast<const float4*>(wc + cb * 32 * LD + (KQ) * 4);                     \
-        _Pragma("unroll") for (int t = 0; t < 4; ++t)                                           \
-            _Pragma("unroll") for (int rb = 0; rb < RB; ++rb) {                                 \
-                const float av = GateIO<float>::val(qa[rb], t);                                 \
-                _Pragma("unroll") for (int cb = 0; cb < 4; ++cb) acc[rb * 4 + cb] =             \
-                    __builtin_amdgcn_mfma_f32_32x32x2f32(av, GateIO<float>::val(qb[cb], t),     \
-                                                         acc[rb * 4 + cb], 0, 0, 0);            \
-            }                                                                                   \
-    } while (0)
-            MOE_GATE_KQ(0);
-            MOE_GATE_KQ(1);
-            __builtin_amdgcn_sched_barrier(0);
-            st.store(xs + (cur ^ 1) * (BM * LD), ws + (cur ^ 1) * (GB_N * LD));
-            MOE_GATE_KQ(2);
-            MOE_GATE_KQ(3);
-#undef MOE_GATE_KQ
-#pragma unroll
-            for (int g = 0; g < S::WRITES; ++g) {
-                __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);          // one LDS store
-                __builtin_amdgcn_sched_group_barrier(0x008, PER_STORE, 0);  // then MFMAs
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            __syncthreads();
-        }
-        if (TOTAL) {
-#pragma unroll
-            for (int c = 0; c < 4 * RB; ++c)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) total[c][v] = total[c][v] + acc[c][v];
-        }
-    }
-}
-
-// out[g, e] for the lane's accumulator element (chain c = 4 rb + cb, register v)
-template <int RB = 2>
-__device__ __forceinline__ void chain_coords(int c, int v, int lane, int64_t m0, int64_t n0, int64_t& g,
-                                             int64_t& e) {
-    const int wv = threadIdx.x >> 6, wm = wv >> 1, wn = wv & 1;
-    e = n0 + wn * 128 + 32 * (c & 3) + (lane & 31);
-    g = m0 + wm * 32 * RB + 32 * (c >> 2) + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-}
-
-// large batches: all chunks in one block of 64*RB rows, running total in registers
-template <typename T, int RB>
-__global__ __launch_bounds__(G_THREADS) void gate_exact_kernel(const T* __restrict__ x,
-                                                               const T* __restrict__ w,
-                                                               const int32_t* __restrict__ row_valid,
-                                                               int64_t G, int64_t E, int64_t H,
-                                                               bool fast, float* __restrict__ logits) {
-    constexpr int BM = 64 * RB;
-    constexpr int LD = GateStage<T, BM>::LD;
-    __shared__ __attribute__((aligned(16))) float xs[2 * BM * LD];
-    __shared__ __attribute__((aligned(16))) float ws[2 * GB_N * LD];
-    const int64_t m0 = static_cast<int64_t>(blockIdx.x) * BM;
-    const int64_t n0 = static_cast<int64_t>(blockIdx.y) * GB_N;
-    const int lane = threadIdx.x & 63;
-    floatx16_t acc[4 * RB], total[4 * RB];
-#pragma unroll
-    for (int c = 0; c < 4 * RB; ++c)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) total[c][v] = 0.f;
-    if (fast && H % GATE_CHUNK == 0)
-        gate_chunks_pipe<T, true, RB>(x, w, G, E, H, m0, n0, 0, H / GATE_CHUNK, xs, ws, acc, total);
-    else  // the last chunk may be ragged: its columns past H read zeros, which add +0 products
-        gate_chunks<T, true, RB>(x, w, G, E, H, m0, n0, 0, ceil_div(H, GATE_CHUNK), fast, xs, ws, acc, total);
-#pragma unroll
-    for (int c = 0; c < 4 * RB; ++c)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            int64_t g, e;
-            chain_coords<RB>(c, v, lane, m0, n0, g, e);
-            if (g < G && e < E) {
-                const bool valid = row_valid == nullptr || row_valid[g] != 0;
-                logits[g * E + e] = valid ? total[c][v] : 0.f;
-            }
-        }
-}
-
-// Large batches with whole chunks and aligned inputs: the same 128-row x 256-expert block
-// with 8 waves, two per SIMD.  Each wave owns 32 rows x 128 experts as four 32x32 chains
-// (wave wv: rows 32 (wv / 2), experts 128 (wv % 2)), so a wave needs half the accumulator
-// registers of the 4-wave block and its SIMD partner issues MFMAs while it waits on LDS
-// reads, staging or the slice barrier.  Slices are loaded from HBM two slices ahead and the
-// LDS fragments one k-quad ahead; the per-chain k order is that of gate_chunks_pipe, so the
-// bits are the same.
-constexpr int G8_THREADS = 512;
-constexpr int G8_BM = 128;
+// A block of 32 WMR rows x 256 experts with 2 WMR waves, for 16-byte aligned inputs with H
+// a multiple of 64: WMR = 4 (128 rows, 8 waves, two per SIMD) for batches that fill the GPU
+// with such blocks, WMR = 2 (64 rows, 4 waves) for batches half that size.  Each wave owns
+// 32 rows x 128 experts as four 32x32 chains (wave wv: rows 32 (wv / 2), experts 128
+// (wv % 2)) that run over all of h.  Slices are loaded from HBM two slices ahead (two
+// staging register sets) and the LDS fragments one k-quad ahead.
 constexpr int G8_CB = 4;  // 32-expert chains per wave
 
-template <typename T>
-__global__ __launch_bounds__(G8_THREADS, 1) void gate_exact8_kernel(const T* __restrict__ x,
-                                                                    const T* __restrict__ w,
-                                                                    const int32_t* __restrict__ row_valid,
-                                                                    int64_t G, int64_t E, int64_t H,
-                                                                    float* __restrict__ logits) {
+template <typename T, int WMR>
+__global__ __launch_bounds__(128 * WMR, 1) void gate_exact8_kernel(const T* __restrict__ x,
+                                                                   const T* __restrict__ w,
+                                                                   const int32_t* __restrict__ row_valid,
+                                                                   int64_t G, int64_t E, int64_t H,
+                                                                   float* __restrict__ logits) {
+    constexpr int G8_BM = 32 * WMR;
+    constexpr int G8_THREADS = 128 * WMR;
     typedef GateStage<T, G8_BM, G8_THREADS> S;
     constexpr int LD = S::LD;
     __shared__ __attribute__((aligned(16))) float xs[2 * G8_BM * LD];
@@ -440,21 +181,20 @@ __global__ __launch_bounds__(G8_THREADS, 1) void gate_exact8_kernel(const T* __r
         const int idx = threadIdx.x + p * G8_THREADS;
         woff[p] = static_cast<uint32_t>(((idx / S::PER_ROW) * H + (idx % S::PER_ROW) * S::C) * sizeof(T));
     }
-    floatx16_t acc[G8_CB], total[G8_CB];
+    floatx16_t acc[G8_CB];
 #pragma unroll
     for (int c = 0; c < G8_CB; ++c)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) total[c][v] = 0.f;
+        for (int v = 0; v < 16; ++v) acc[c][v] = 0.f;
     // Pipeline.  Slice j is held in staging registers st[j % 2] from the top of slice j - 2
     // (its global loads) to the second half of slice j - 1 (its LDS stores), so a load has a
     // slice and a half to arrive.  Inside a slice the LDS fragments of k-quad kq + 1 are read
     // while the MFMAs of k-quad kq run.
     S st[2];
-    const int64_t nch = H / GATE_CHUNK;
-    const int64_t s_end = nch * SLICES_PER_CHUNK;
+    const int64_t s_end = H / GB_K;  // even
     st[0].load_fast(rx, rw, xoff, woff, 0);
     st[0].store(xs, ws);
-    st[1].load_fast(rx, rw, xoff, woff, (s_end > 1 ? 1 : 0) * GB_K);
+    st[1].load_fast(rx, rw, xoff, woff, GB_K);
     __syncthreads();
     float4 fa[2], fb[2][G8_CB];
     auto read_frag = [&](int buf, int kq, float4& a, float4 (&b)[G8_CB]) {
@@ -468,25 +208,21 @@ __global__ __launch_bounds__(G8_THREADS, 1) void gate_exact8_kernel(const T* __r
     auto mfma_quad = [&](const float4& a, const float4 (&b)[G8_CB]) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            const float av = GateIO<float>::val(a, t);
+            const float av = f4_at(a, t);
 #pragma unroll
             for (int cb = 0; cb < G8_CB; ++cb)
-                acc[cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, GateIO<float>::val(b[cb], t), acc[cb], 0, 0, 0);
+                acc[cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, f4_at(b[cb], t), acc[cb], 0, 0, 0);
         }
     };
     read_frag(0, 0, fa[0], fb[0]);
-    for (int64_t ch = 0; ch < nch; ++ch) {
+    for (int64_t s2 = 0; s2 < s_end; s2 += 2) {
 #pragma unroll
-        for (int c = 0; c < G8_CB; ++c)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[c][v] = 0.f;
-#pragma unroll
-        for (int q = 0; q < SLICES_PER_CHUNK; ++q) {
-            const int64_t sl = ch * SLICES_PER_CHUNK + q;
-            const int cur = q & 1;
+        for (int q = 0; q < 2; ++q) {
+            const int64_t sl = s2 + q;
+            const int cur = q;
             const int64_t n2 = sl + 2 < s_end ? sl + 2 : s_end - 1;
             __builtin_amdgcn_sched_barrier(0);
-            st[q & 1].load_fast(rx, rw, xoff, woff, n2 * GB_K);  // slice sl + 2
+            st[q].load_fast(rx, rw, xoff, woff, n2 * GB_K);  // slice sl + 2
             read_frag(cur, 1, fa[1], fb[1]);
             mfma_quad(fa[0], fb[0]);
 #pragma unroll
@@ -504,7 +240,7 @@ __global__ __launch_bounds__(G8_THREADS, 1) void gate_exact8_kernel(const T* __r
             }
             __builtin_amdgcn_sched_barrier(0);
             read_frag(cur, 3, fa[1], fb[1]);
-            st[(q + 1) & 1].store(xs + (cur ^ 1) * (G8_BM * LD), ws + (cur ^ 1) * (GB_N * LD));  // slice sl + 1
+            st[q ^ 1].store(xs + (cur ^ 1) * (G8_BM * LD), ws + (cur ^ 1) * (GB_N * LD));  // slice sl + 1
             mfma_quad(fa[0], fb[0]);
 #pragma unroll
             for (int g = 0; g < 1 + G8_CB; ++g) {
@@ -520,10 +256,6 @@ __global__ __launch_bounds__(G8_THREADS, 1) void gate_exact8_kernel(const T* __r
             // k-quad 0 of slice sl + 1 (past the last slice: a stale stage, never used)
             read_frag(cur ^ 1, 0, fa[0], fb[0]);
         }
-#pragma unroll
-        for (int c = 0; c < G8_CB; ++c)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) total[c][v] = total[c][v] + acc[c][v];
     }
 #pragma unroll
     for (int c = 0; c < G8_CB; ++c)
@@ -533,35 +265,189 @@ __global__ __launch_bounds__(G8_THREADS, 1) void gate_exact8_kernel(const T* __r
             const int64_t g = m0 + wm * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
             if (g < G && e < E) {
                 const bool valid = row_valid == nullptr || row_valid[g] != 0;
-                logits[g * E + e] = valid ? total[c][v] : 0.f;
+                logits[g * E + e] = valid ? acc[c][v] : 0.f;
             }
         }
 }
 
-// small batches: blockIdx.z = chunk; writes the chunk's sums to parts[chunk][G][E]
+// ---- small and medium batches, and any shape or alignment: 16x16 chains, one per wave
+// Each wave owns 16 rows x 16 experts and stages its own operands, so no wave waits for
+// another: a block is four independent waves (2 x 2 tiles, neighbours in x and w for the
+// L2).  Lane l of a wave holds row (or expert) l % 16 and k group j = l / 16, so instruction
+// t needs column 4t + j of its row.  LDS keeps each staged row of a 64-wide slice of h as
+// fp32 in [j][t] order (column 4t + j at j * 16 + t, rows C16_RS floats apart): one 16-byte
+// read gives a lane its operands for four consecutive instructions.  A wave's LDS accesses
+// complete in order, so a slice's stores and the reads that follow them need no barrier.
+// A dependent 16x16x4 step takes about 44 cycles, so a slice of 16 steps is ~700 cycles
+// while an operand fetch from HBM can take ~1000: slices are loaded C16_D slices ahead
+// into as many register sets, and the stores of the next slice and the reads of its
+// fragments are spread between this slice's MFMAs.
+constexpr int C16_K = 64;           // h per slice
+constexpr int C16_RS = C16_K + 4;   // LDS row stride in floats
+constexpr int C16_D = 4;            // slices in flight (register sets), even
+constexpr int C16_WAVES = 4;        // independent waves per block, as 2 x 2 tiles
+
 template <typename T>
-__global__ __launch_bounds__(G_THREADS) void gate_chunk_kernel(const T* __restrict__ x,
-                                                               const T* __restrict__ w, int64_t G,
-                                                               int64_t E, int64_t H, bool fast,
-                                                               float* __restrict__ parts) {
-    constexpr int LD = GateStage<T>::LD;
-    __shared__ __attribute__((aligned(16))) float xs[2 * GB_M * LD];
-    __shared__ __attribute__((aligned(16))) float ws[2 * GB_N * LD];
-    const int64_t m0 = static_cast<int64_t>(blockIdx.x) * GB_M;
-    const int64_t n0 = static_cast<int64_t>(blockIdx.y) * GB_N;
-    const int64_t ch = blockIdx.z;
-    const int lane = threadIdx.x & 63;
-    floatx16_t acc[8], unused[8];
-    gate_chunks<T, false>(x, w, G, E, H, m0, n0, ch, ch + 1, fast, xs, ws, acc, unused);
-    float* out = parts + ch * G * E;
+struct Chain16Stage {
+    static constexpr int C = GateIO<T>::kChunk;  // values per 16-byte piece
+    static constexpr int PPR = C16_K / C;        // pieces per row and slice
+    static constexpr int NP = 16 * PPR / 64;     // pieces per lane for each of x and w
+    static_assert(NP * 64 == 16 * PPR, "whole pieces per lane");
+    uint4 xr[NP], wr[NP];
+    // x rows [m0, m0 + 16) and w rows [n0, n0 + 16) of the slice starting at column k0.
+    // FAST: whole slices (H a multiple of C16_K), 16-byte aligned rows; the descriptors
+    // cover the wave's own rows, so rows past G (or E) read zeros
+    template <bool FAST>
+    __device__ void load(__amdgpu_buffer_rsrc_t rx, __amdgpu_buffer_rsrc_t rw, const T* x, const T* w,
+                         int64_t G, int64_t E, int64_t H, int64_t m0, int64_t n0, int64_t k0, int lane) {
+        if constexpr (FAST) {
+            const int so = static_cast<int>(k0 * static_cast<int64_t>(sizeof(T)));
 #pragma unroll
-    for (int c = 0; c < 8; ++c)
+            for (int p = 0; p < NP; ++p) {
+                const int idx = lane + 64 * p;
+                const int off = static_cast<int>(((idx / PPR) * H + (idx % PPR) * C) * sizeof(T));
+                const gate_u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rx, off, so, 0);
+                const gate_u32x4 u = __builtin_amdgcn_raw_buffer_load_b128(rw, off, so, 0);
+                xr[p] = make_uint4(v.x, v.y, v.z, v.w);
+                wr[p] = make_uint4(u.x, u.y, u.z, u.w);
+            }
+        } else {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            int64_t g, e;
-            chain_coords(c, v, lane, m0, n0, g, e);
-            if (g < G && e < E) out[g * E + e] = acc[c][v];
+            for (int p = 0; p < NP; ++p) {
+                const int idx = lane + 64 * p;
+                xr[p] = load_piece<T>(x, G, H, m0 + idx / PPR, k0 + (idx % PPR) * C, GateIO<T>::kNegZero);
+                wr[p] = load_piece<T>(w, E, H, n0 + idx / PPR, k0 + (idx % PPR) * C, T(0));
+            }
         }
+    }
+    // piece q of a row covers slice columns q*C .. q*C + C - 1; column c goes to
+    // (c % 4) * 16 + c / 4
+    __device__ static void put(float* row, int q, const uint4& v) {
+        if constexpr (sizeof(T) == 2) {  // columns 8q + u: u and u + 4 share j = u, at t = 2q, 2q + 1
+            reinterpret_cast<float2*>(row + 0 * 16 + 2 * q)[0] =
+                make_float2(__uint_as_float(v.x << 16), __uint_as_float(v.z << 16));
+            reinterpret_cast<float2*>(row + 1 * 16 + 2 * q)[0] =
+                make_float2(__uint_as_float(v.x & 0xffff0000u), __uint_as_float(v.z & 0xffff0000u));
+            reinterpret_cast<float2*>(row + 2 * 16 + 2 * q)[0] =
+                make_float2(__uint_as_float(v.y << 16), __uint_as_float(v.w << 16));
+            reinterpret_cast<float2*>(row + 3 * 16 + 2 * q)[0] =
+                make_float2(__uint_as_float(v.y & 0xffff0000u), __uint_as_float(v.w & 0xffff0000u));
+        } else {  // columns 4q + u: j = u, t = q
+            row[0 * 16 + q] = __uint_as_float(v.x);
+            row[1 * 16 + q] = __uint_as_float(v.y);
+            row[2 * 16 + q] = __uint_as_float(v.z);
+            row[3 * 16 + q] = __uint_as_float(v.w);
+        }
+    }
+    // stage layout: x rows 0 .. 15, then w rows 16 .. 31
+    __device__ void store(float* stage, int lane) const {
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            const int idx = lane + 64 * p;
+            put(stage + (idx / PPR) * C16_RS, idx % PPR, xr[p]);
+            put(stage + (16 + idx / PPR) * C16_RS, idx % PPR, wr[p]);
+        }
+    }
+};
+
+template <int Q>
+struct SliceIdx {
+    static constexpr int kValue = Q;
+};
+
+// FAST (whole slices, aligned rows) is a template parameter: a run-time branch around the
+// loads leaves them in conditional blocks, and the wait counts the compiler then places
+// drain every load in flight once per loop trip.
+template <typename T, bool FAST>
+__global__ __launch_bounds__(64 * C16_WAVES) void gate_chain16_kernel(const T* __restrict__ x,
+                                                                     const T* __restrict__ w,
+                                                                     const int32_t* __restrict__ row_valid,
+                                                                     int64_t G, int64_t E, int64_t H,
+                                                                     float* __restrict__ logits) {
+    typedef Chain16Stage<T> S;
+    constexpr int STAGE = 32 * C16_RS;
+    constexpr int D = C16_D;
+    static_assert(D % 2 == 0, "the LDS stage of a slice is its register set's parity");
+    __shared__ __attribute__((aligned(16))) float lds_all[C16_WAVES * 2 * STAGE];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    float* lds = lds_all + wv * 2 * STAGE;
+    const int64_t m0 = static_cast<int64_t>(blockIdx.x) * 32 + (wv >> 1) * 16;
+    const int64_t n0 = static_cast<int64_t>(blockIdx.y) * 32 + (wv & 1) * 16;
+    if (m0 >= G || n0 >= E) return;  // a wave past the edge has no rows (no block barrier below)
+    const int i16 = lane & 15, j = lane >> 4;
+    const int64_t xrows = G - m0 < 16 ? G - m0 : 16;
+    const int64_t wrows = E - n0 < 16 ? E - n0 : 16;
+    // descriptors over the wave's own rows (used by the fast loads only)
+    const __amdgpu_buffer_rsrc_t rx =
+        gemm::make_rsrc_uniform(x + m0 * H, static_cast<uint32_t>(xrows * H * static_cast<int64_t>(sizeof(T))));
+    const __amdgpu_buffer_rsrc_t rw =
+        gemm::make_rsrc_uniform(w + n0 * H, static_cast<uint32_t>(wrows * H * static_cast<int64_t>(sizeof(T))));
+    // this lane's fragment rows in a stage, at its k group
+    const int aoff = i16 * C16_RS + j * 16;
+    const int boff = (16 + i16) * C16_RS + j * 16;
+    floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
+    const int64_t ns = ceil_div(H, C16_K);
+    // register set q holds slice q (mod D) from its global loads, issued D slices ahead, to
+    // its LDS stores in the slice before
+    S st[D];
+#pragma unroll
+    for (int q = 0; q < D; ++q)
+        st[q].template load<FAST>(rx, rw, x, w, G, E, H, m0, n0, (q < ns ? q : ns - 1) * C16_K, lane);
+    st[0].store(lds, lane);
+    float4 fa[2][4], fb[2][4];
+    auto read_frag = [&](int buf, float4 (&a)[4], float4 (&b)[4]) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            a[s] = *reinterpret_cast<const float4*>(lds + buf * STAGE + aoff + 4 * s);
+            b[s] = *reinterpret_cast<const float4*>(lds + buf * STAGE + boff + 4 * s);
+        }
+    };
+    // instructions 4s .. 4s+3 of a slice: h = 16 s + 4 u + j for u = 0..3
+    auto mfma4 = [&](const float4& a, const float4& b) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(f4_at(a, u), f4_at(b, u), acc, 0, 0, 0);
+    };
+    read_frag(0, fa[0], fb[0]);
+    // slice sl, with Q = sl mod D fixed at compile time: its fragments are in set Q % 2 and
+    // its LDS stage is Q % 2.  The chain issues one MFMA per ~44 cycles; the slice's other
+    // instructions go between them.
+    auto slice = [&](auto QC, int64_t sl) {
+        constexpr int Q = decltype(QC)::kValue;
+        constexpr int P = Q & 1;
+        const int64_t nd = sl + D < ns ? sl + D : ns - 1;
+        __builtin_amdgcn_sched_barrier(0);
+        st[Q].template load<FAST>(rx, rw, x, w, G, E, H, m0, n0, nd * C16_K, lane);  // slice sl + D
+        st[(Q + 1) % D].store(lds + (P ^ 1) * STAGE, lane);  // slice sl + 1 (past the end: never read)
+        mfma4(fa[P][0], fb[P][0]);
+        mfma4(fa[P][1], fb[P][1]);
+        __builtin_amdgcn_sched_barrier(0);
+        read_frag(P ^ 1, fa[P ^ 1], fb[P ^ 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma4(fa[P][2], fb[P][2]);
+        mfma4(fa[P][3], fb[P][3]);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    int64_t sl = 0;
+    for (; sl + D <= ns; sl += D) {
+        slice(SliceIdx<0>(), sl);
+        slice(SliceIdx<1>(), sl + 1);
+        slice(SliceIdx<2>(), sl + 2);
+        slice(SliceIdx<3>(), sl + 3);
+    }
+    static_assert(D == 4, "the unrolled loop and its tail cover four register sets");
+    if (sl < ns) slice(SliceIdx<0>(), sl);
+    if (sl + 1 < ns) slice(SliceIdx<1>(), sl + 1);
+    if (sl + 2 < ns) slice(SliceIdx<2>(), sl + 2);
+    // lane l, register r: row 4 (l / 16) + r, expert l % 16 of the wave's block
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int64_t g = m0 + 4 * j + r;
+        const int64_t e = n0 + i16;
+        if (g < G && e < E) {
+            const bool valid = row_valid == nullptr || row_valid[g] != 0;
+            logits[g * E + e] = valid ? acc[r] : 0.f;
+        }
+    }
 }
 
 // ------------------------------------------------------------------ fast gate
@@ -602,12 +488,12 @@ struct FastStage {
 #pragma unroll
             for (int p = 0; p < XCH; ++p) {
                 const int idx = threadIdx.x + p * G_THREADS;
-                xr[p] = load_piece(x, G, H, m0 + idx / PER_ROW, k0 + (idx % PER_ROW) * 8);
+                xr[p] = load_piece<uint16_t>(x, G, H, m0 + idx / PER_ROW, k0 + (idx % PER_ROW) * 8, 0);
             }
 #pragma unroll
             for (int p = 0; p < WCH; ++p) {
                 const int idx = threadIdx.x + p * G_THREADS;
-                wr[p] = load_piece(w, E, H, n0 + idx / PER_ROW, k0 + (idx % PER_ROW) * 8);
+                wr[p] = load_piece<uint16_t>(w, E, H, n0 + idx / PER_ROW, k0 + (idx % PER_ROW) * 8, 0);
             }
         }
     }
@@ -679,8 +565,9 @@ __global__ __launch_bounds__(G_THREADS) void gate_fast_kernel(const uint16_t* __
     for (int c = 0; c < 8; ++c)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-            int64_t g, e;
-            chain_coords(c, v, lane, m0, n0, g, e);
+            // accumulator c = 4 rb + cb, register v: row block rb, expert block cb
+            const int64_t e = n0 + wn * 128 + 32 * (c & 3) + (lane & 31);
+            const int64_t g = m0 + wm * 64 + 32 * (c >> 2) + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
             if (g < G && e < E) {
                 const bool valid = row_valid == nullptr || row_valid[g] != 0;
                 logits[g * E + e] = valid ? acc[c][v] : 0.f;
@@ -699,14 +586,6 @@ int gate_num_cus() {
         cus[dev] = v;
     }
     return cus[dev];
-}
-
-// workspace the chunk-parallel gate needs; 0 when the batch is large enough for the
-// running-total kernel to fill the GPU
-size_t gate_split_bytes(int64_t G, int64_t E, int64_t H) {
-    const int64_t tiles = ceil_div(G, GB_M) * ceil_div(E, GB_N);
-    if (tiles * 2 >= gate_num_cus()) return 0;
-    return static_cast<size_t>(ceil_div(H, GATE_CHUNK) * G * E) * sizeof(float);
 }
 
 // ------------------------------------------------------------------ selection
@@ -826,11 +705,6 @@ __device__ __forceinline__ void sort_lane(double (&k)[V], double (&s)[V], int (&
 
 struct SelectArgs {
     const float* logits;
-    // small-batch exact gate: the chunk partial sums [nchunks][G][E]; the kernel then adds
-    // them in chunk order (the logits' definition) and writes the logits itself
-    const float* parts;
-    int64_t nchunks;
-    float* logits_out;
     const int32_t* row_valid;
     const float* bias;
     int64_t G;
@@ -849,57 +723,8 @@ __global__ __launch_bounds__(S_THREADS) void select_kernel(SelectArgs a) {
     float* wout = a.w + g * k;
     const bool pad = a.row_valid && a.row_valid[g] == 0;
     float lv[V];
-    if (a.parts) {
-        // logits = ((+0 + part_0) + part_1) + ... in chunk order; pad rows get 0
-        const int64_t GE = a.G * E;
-        const float* pp = a.parts + g * E + lane * V;
 #pragma unroll
-        for (int j = 0; j < V; ++j) lv[j] = 0.f;
-        if (!pad) {
-            bool done = false;
-            if constexpr (V == 4) {
-                if ((E & 3) == 0) {  // 16-byte loads: every offset is a multiple of 4 floats
-                    if (lane * V < E) {
-                        // kLoads loads in flight, then their adds in chunk order
-                        constexpr int kLoads = 8;
-                        int64_t c = 0;
-                        for (; c + kLoads <= a.nchunks; c += kLoads) {
-                            float4 q[kLoads];
-#pragma unroll
-                            for (int u = 0; u < kLoads; ++u)
-                                q[u] = *reinterpret_cast<const float4*>(pp + (c + u) * GE);
-#pragma unroll
-                            for (int u = 0; u < kLoads; ++u) {
-                                lv[0] = lv[0] + q[u].x;
-                                lv[1] = lv[1] + q[u].y;
-                                lv[2] = lv[2] + q[u].z;
-                                lv[3] = lv[3] + q[u].w;
-                            }
-                        }
-                        for (; c < a.nchunks; ++c) {
-                            const float4 q = *reinterpret_cast<const float4*>(pp + c * GE);
-                            lv[0] = lv[0] + q.x;
-                            lv[1] = lv[1] + q.y;
-                            lv[2] = lv[2] + q.z;
-                            lv[3] = lv[3] + q.w;
-                        }
-                    }
-                    done = true;
-                }
-            }
-            if (!done)
-                for (int64_t c = 0; c < a.nchunks; ++c)
-#pragma unroll
-                    for (int j = 0; j < V; ++j)
-                        if (lane * V + j < E) lv[j] = lv[j] + pp[c * GE + j];
-        }
-#pragma unroll
-        for (int j = 0; j < V; ++j)
-            if (lane * V + j < E) a.logits_out[g * E + lane * V + j] = lv[j];
-    } else {
-#pragma unroll
-        for (int j = 0; j < V; ++j) lv[j] = lane * V + j < E ? a.logits[g * E + lane * V + j] : 0.f;
-    }
+    for (int j = 0; j < V; ++j) lv[j] = lane * V + j < E ? a.logits[g * E + lane * V + j] : 0.f;
     if (pad) {  // pad row: no expert load
         if (lane < k) {
             ids[lane] = -1;
@@ -1063,12 +888,9 @@ int lanes_per_expert_chunk(int E) {
 
 moe_status launch_select(const float* logits, const int32_t* row_valid, int64_t G,
                          const float* bias, const moe_route_cfg* c, int32_t* ids, float* w,
-                         hipStream_t stream, const float* parts = nullptr, int64_t nchunks = 0) {
+                         hipStream_t stream) {
     SelectArgs a;
     a.logits = logits;
-    a.parts = parts;
-    a.nchunks = nchunks;
-    a.logits_out = const_cast<float*>(logits);
     a.row_valid = row_valid;
     a.bias = c->kind == MOE_ROUTE_GROUPED_SIGMOID ? bias : nullptr;
     a.G = G;
@@ -1115,95 +937,83 @@ extern "C" moe_status moe_route_from_logits(const float* logits, const int32_t* 
     return moe::launch_select(logits, row_valid, G, bias, cfg, topk_ids, topk_w, stream);
 }
 
-extern "C" size_t moe_route_workspace_size(int64_t G, int32_t num_experts, int64_t H) {
-    if (G <= 0 || num_experts <= 0 || H <= 0) return 0;
-    return moe::gate_split_bytes(G, num_experts, H);
-}
-
 extern "C" moe_status moe_route(const void* global_x, const int32_t* row_valid, int64_t G,
                                 int64_t H, moe_dtype dt, const void* w_router, const float* bias,
                                 const moe_route_cfg* cfg, float* logits, int32_t* topk_ids,
-                                float* topk_w, void* workspace, size_t workspace_bytes,
-                                hipStream_t stream) {
+                                float* topk_w, hipStream_t stream) {
     moe_status st = moe::check_route_cfg(cfg);
     if (st != MOE_OK) return st;
     MOE_CHECK_ARG(G >= 0 && H > 0);
     MOE_CHECK_ARG(dt == MOE_F32 || dt == MOE_BF16);
+    if (cfg->gate_mode == MOE_GATE_FAST && dt != MOE_BF16) return MOE_ERR_UNSUPPORTED;
     if (G == 0) return MOE_OK;
     MOE_CHECK_ARG(global_x && w_router && logits && topk_ids && topk_w);
     MOE_CHECK_ARG(G <= (int64_t)1 << 31);
     const int64_t E = cfg->num_experts;
-    const size_t split = moe::gate_split_bytes(G, E, H);
-    const bool use_split = split > 0 && workspace != nullptr && workspace_bytes >= split &&
-                           moe::aligned(workspace, 16);
-    // FAST mode on a batch small enough for the chunk-parallel exact gate takes that gate:
-    // it is faster there (a handful of 128-row tiles would run the whole of h in sequence),
-    // and its logits are the exact ones
-    if (cfg->gate_mode == MOE_GATE_FAST && dt != MOE_BF16) return MOE_ERR_UNSUPPORTED;
-    if (cfg->gate_mode == MOE_GATE_FAST && !use_split) {
-        const bool fast = moe::aligned(global_x, 16) && moe::aligned(w_router, 16) && (H * 2) % 16 == 0 &&
-                          static_cast<int64_t>(moe::FB_N) * H * 2 < ((int64_t)1 << 31);
+    const int64_t esz = dt == MOE_BF16 ? 2 : 4;
+    const bool aligned = moe::aligned(global_x, 16) && moe::aligned(w_router, 16) && (H * esz) % 16 == 0;
+    // A batch is large when its 128-row (or 64-row) x 256-expert blocks fill every CU (one
+    // block holds a CU's LDS); smaller batches spread 16x16 chains instead.  FAST mode on a
+    // batch too small for its 128-row tiles to cover half the CUs takes the exact gate: its
+    // few tiles would run the whole of h in sequence on part of the GPU, and the exact
+    // logits are the better ones anyway.
+    const int64_t ncu = moe::gate_num_cus();
+    const int64_t etiles = moe::ceil_div(E, moe::GB_N);
+    const bool fills128 = moe::ceil_div(G, 128) * etiles >= ncu;
+    const bool fills64 = moe::ceil_div(G, 64) * etiles >= ncu;
+    const bool exact32 = aligned && H % (2 * moe::GB_K) == 0 &&
+                         static_cast<int64_t>(moe::GB_N) * H * esz < ((int64_t)1 << 31);
+    const bool fast_large = moe::ceil_div(G, moe::FB_M) * moe::ceil_div(E, moe::FB_N) * 2 >= ncu;
+    if (cfg->gate_mode == MOE_GATE_FAST && fast_large) {
+        const bool fast = aligned && static_cast<int64_t>(moe::FB_N) * H * 2 < ((int64_t)1 << 31);
         const dim3 grid(static_cast<unsigned>(moe::ceil_div(G, moe::FB_M)),
                         static_cast<unsigned>(moe::ceil_div(E, moe::FB_N)));
         hipLaunchKernelGGL(moe::gate_fast_kernel, grid, dim3(moe::G_THREADS), 0, stream,
                            static_cast<const uint16_t*>(global_x), static_cast<const uint16_t*>(w_router),
                            row_valid, G, E, H, fast, logits);
-        MOE_LAUNCH_CHECK();
-        return moe::launch_select(logits, row_valid, G, bias, cfg, topk_ids, topk_w, stream);
-    }
-    const dim3 tiles(static_cast<unsigned>(moe::ceil_div(G, moe::GB_M)),
-                     static_cast<unsigned>(moe::ceil_div(E, moe::GB_N)));
-    // 64-row blocks when they all fit in one round on the CUs (a 64-row block takes a bit
-    // over half a 128-row block's time), else 128-row blocks
-    const dim3 tiles64(static_cast<unsigned>(moe::ceil_div(G, 64)), tiles.y);
-    const bool rows128 = static_cast<int64_t>(tiles64.x) * tiles64.y > moe::gate_num_cus();
-    // 16-byte buffer loads need aligned bases and rows; the per-block descriptors span at
-    // most 256 rows, which must stay below 2 GiB
-    const size_t esz = dt == MOE_BF16 ? 2 : 4;
-    const bool fast = moe::aligned(global_x, 16) && moe::aligned(w_router, 16) && (H * esz) % 16 == 0 &&
-                      static_cast<int64_t>(moe::GB_N) * H * static_cast<int64_t>(esz) < ((int64_t)1 << 31);
-    if (use_split) {
-        const int64_t nch = moe::ceil_div(H, moe::GATE_CHUNK);
-        const dim3 grid(tiles.x, tiles.y, static_cast<unsigned>(nch));
-        float* parts = static_cast<float*>(workspace);
-        if (dt == MOE_BF16)
-            hipLaunchKernelGGL(moe::gate_chunk_kernel<uint16_t>, grid, dim3(moe::G_THREADS), 0, stream,
-                               static_cast<const uint16_t*>(global_x), static_cast<const uint16_t*>(w_router),
-                               G, E, H, fast, parts);
-        else
-            hipLaunchKernelGGL(moe::gate_chunk_kernel<float>, grid, dim3(moe::G_THREADS), 0, stream,
-                               static_cast<const float*>(global_x), static_cast<const float*>(w_router),
-                               G, E, H, fast, parts);
-        MOE_LAUNCH_CHECK();
-        // the select kernel adds the chunk partials in chunk order and writes the logits
-        return moe::launch_select(logits, row_valid, G, bias, cfg, topk_ids, topk_w, stream, parts, nch);
-    } else if (rows128 && fast && H % moe::GATE_CHUNK == 0) {
-        if (dt == MOE_BF16)
-            hipLaunchKernelGGL(moe::gate_exact8_kernel<uint16_t>, tiles, dim3(moe::G8_THREADS), 0, stream,
-                               static_cast<const uint16_t*>(global_x), static_cast<const uint16_t*>(w_router),
-                               row_valid, G, E, H, logits);
-        else
-            hipLaunchKernelGGL(moe::gate_exact8_kernel<float>, tiles, dim3(moe::G8_THREADS), 0, stream,
-                               static_cast<const float*>(global_x), static_cast<const float*>(w_router),
-                               row_valid, G, E, H, logits);
-    } else if (dt == MOE_BF16) {
+    } else if (exact32 && (fills128 || fills64)) {
+        // 32x32 chains; the kernel's descriptors span up to 256 rows, which must stay below
+        // 2 GiB
+        const int rows = fills128 ? 128 : 64;
+        const dim3 grid(static_cast<unsigned>(moe::ceil_div(G, rows)), static_cast<unsigned>(etiles));
         const uint16_t* xb = static_cast<const uint16_t*>(global_x);
         const uint16_t* wb = static_cast<const uint16_t*>(w_router);
-        if (rows128)
-            hipLaunchKernelGGL((moe::gate_exact_kernel<uint16_t, 2>), tiles, dim3(moe::G_THREADS), 0, stream, xb,
-                               wb, row_valid, G, E, H, fast, logits);
-        else
-            hipLaunchKernelGGL((moe::gate_exact_kernel<uint16_t, 1>), tiles64, dim3(moe::G_THREADS), 0, stream, xb,
-                               wb, row_valid, G, E, H, fast, logits);
-    } else {
         const float* xf = static_cast<const float*>(global_x);
         const float* wf = static_cast<const float*>(w_router);
-        if (rows128)
-            hipLaunchKernelGGL((moe::gate_exact_kernel<float, 2>), tiles, dim3(moe::G_THREADS), 0, stream, xf, wf,
-                               row_valid, G, E, H, fast, logits);
+        if (dt == MOE_BF16 && fills128)
+            hipLaunchKernelGGL((moe::gate_exact8_kernel<uint16_t, 4>), grid, dim3(512), 0, stream, xb, wb, row_valid,
+                               G, E, H, logits);
+        else if (dt == MOE_BF16)
+            hipLaunchKernelGGL((moe::gate_exact8_kernel<uint16_t, 2>), grid, dim3(256), 0, stream, xb, wb, row_valid,
+                               G, E, H, logits);
+        else if (fills128)
+            hipLaunchKernelGGL((moe::gate_exact8_kernel<float, 4>), grid, dim3(512), 0, stream, xf, wf, row_valid, G,
+                               E, H, logits);
         else
-            hipLaunchKernelGGL((moe::gate_exact_kernel<float, 1>), tiles64, dim3(moe::G_THREADS), 0, stream, xf,
-                               wf, row_valid, G, E, H, fast, logits);
+            hipLaunchKernelGGL((moe::gate_exact8_kernel<float, 2>), grid, dim3(256), 0, stream, xf, wf, row_valid, G,
+                               E, H, logits);
+    } else {
+        const dim3 grid(static_cast<unsigned>(moe::ceil_div(G, 32)), static_cast<unsigned>(moe::ceil_div(E, 32)));
+        // whole 64-wide slices and aligned rows take 16-byte buffer loads, whose per-wave
+        // descriptors span 16 rows; anything else loads element by element
+        const bool fast = aligned && H % moe::C16_K == 0 && 16 * H * esz < ((int64_t)1 << 31);
+        const uint16_t* xb = static_cast<const uint16_t*>(global_x);
+        const uint16_t* wb = static_cast<const uint16_t*>(w_router);
+        const float* xf = static_cast<const float*>(global_x);
+        const float* wf = static_cast<const float*>(w_router);
+        const dim3 block(64 * moe::C16_WAVES);
+        if (dt == MOE_BF16 && fast)
+            hipLaunchKernelGGL((moe::gate_chain16_kernel<uint16_t, true>), grid, block, 0, stream, xb, wb, row_valid,
+                               G, E, H, logits);
+        else if (dt == MOE_BF16)
+            hipLaunchKernelGGL((moe::gate_chain16_kernel<uint16_t, false>), grid, block, 0, stream, xb, wb, row_valid,
+                               G, E, H, logits);
+        else if (fast)
+            hipLaunchKernelGGL((moe::gate_chain16_kernel<float, true>), grid, block, 0, stream, xf, wf, row_valid, G,
+                               E, H, logits);
+        else
+            hipLaunchKernelGGL((moe::gate_chain16_kernel<float, false>), grid, block, 0, stream, xf, wf, row_valid,
+                               G, E, H, logits);
     }
     MOE_LAUNCH_CHECK();
     return moe::launch_select(logits, row_valid, G, bias, cfg, topk_ids, topk_w, stream);

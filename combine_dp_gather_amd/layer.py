@@ -18,7 +18,7 @@ from . import (PlanBuffers, layout_offsets, layout_sizes, make_expert_map, make_
                make_route_cfg, moe_combine, moe_dispatch, moe_dispatch_workspace_size,
                moe_expert_gemm, moe_expert_gemm_down, moe_expert_gemm_up,
                moe_entry_gather, moe_expert_gemm_workspace_size, moe_gather, moe_gather_layout, moe_route,
-               moe_route_workspace_size, moe_scatter, moe_combine_scatter)
+               moe_scatter, moe_combine_scatter)
 
 
 def _to_dev(a: Optional[np.ndarray], device, bf16: bool = False) -> Optional[torch.Tensor]:
@@ -101,8 +101,6 @@ class MoELayer:
         self.logits = torch.empty((max(G, 1), spec.num_experts), dtype=torch.float32, device=device)
         self.topk_ids = torch.empty((max(G, 1), k), dtype=torch.int32, device=device)
         self.topk_w = torch.empty((max(G, 1), k), dtype=torch.float32, device=device)
-        route_ws = moe_route_workspace_size(G, spec.num_experts, H)
-        self.route_ws = (torch.empty(route_ws, dtype=torch.uint8, device=device) if route_ws else None)
         self.emap = make_expert_map(spec.num_experts, spec.first_local, spec.num_local,
                                     weights.phys_of, weights.n_rep)
         # seg_stride > 0: fixed-capacity layout, every slot's rows at a fixed address
@@ -130,7 +128,7 @@ class MoELayer:
     def route(self):
         if self.G:
             moe_route(self.global_x, self.row_valid, self.w.router, self.w.bias, self.route_cfg,
-                      self.logits, self.topk_ids, self.topk_w, self.route_ws)
+                      self.logits, self.topk_ids, self.topk_w)
 
     def dispatch(self):
         if self.G:

@@ -172,31 +172,21 @@ typedef struct {
     int32_t gate_mode;     /* moe_gate_mode (moe_route only; ignored by moe_route_from_logits) */
 } moe_route_cfg;
 
-/* moe_route_workspace_size -- bytes of device workspace moe_route can use for G rows, E
- * experts and hidden size H.  0 means the call needs none; otherwise it is the chunk-partial
- * table fp32[ceil(H/128), G, E] that lets every chunk of h run in parallel on small batches.
- * Without it (NULL or smaller) moe_route still gives the same bits, only with less
- * parallelism. */
-size_t moe_route_workspace_size(int64_t G, int32_t num_experts, int64_t H);
-
 /* moe_route -- gate logits then top-k selection.
  *   global_x   device [G, H] dt (MOE_F32 or MOE_BF16); row_valid device int32[G] or NULL
  *   w_router   device [E, H] dt
  *   bias       device fp32[E] or NULL (grouped only: selection bias, never in the weights)
  *   logits     device fp32[G, E], written.  EXACT mode (cfg->gate_mode): the pages fix no
  *              summation order for the gate's matrix product; this library defines one so
- *              that the integer routing is
- *              reproducible: for each 128-wide chunk c of h, part_c = fmaf chain over the
- *              chunk's h in ascending order from +0; logits[g,e] = ((+0 + part_0) + part_1)
- *              + ... in fp32, chunks left to right.  FAST mode: bf16 MFMA products, fp32
- *              sums in tile order (MOE_ERR_UNSUPPORTED for MOE_F32 inputs); a batch small
- *              enough for the chunk-parallel table, with that workspace given, runs the EXACT
- *              gate instead (faster at that size, exact logits).  0 for pad rows.
+ *              that the integer routing is reproducible: logits[g,e] is one fp32 fused
+ *              multiply-add chain over h in ascending order from +0,
+ *              acc = fmaf(x[g,h], w[e,h], acc).  FAST mode: bf16 MFMA products, fp32 sums in
+ *              tile order (MOE_ERR_UNSUPPORTED for MOE_F32 inputs); a batch too small to
+ *              fill the GPU with 128-row tiles runs the EXACT gate instead (faster at that
+ *              size, exact logits).  0 for pad rows.
  *   topk_ids   device int32[G, k]: expert ids, slots in descending key order, ties to the
  *              lower id; -1 for pad rows
  *   topk_w     device fp32[G, k]: weights; 0 for pad rows
- *   workspace  device, 16-byte aligned, moe_route_workspace_size(G, E, H) bytes, or NULL;
- *              scratch owned by the caller, contents undefined after the call
  * Selection: softmax -- the k largest logits, weight = softmax over all E (optionally
  * renormalised).  Grouped sigmoid -- key = sigmoid(l) + bias in fp64 with a Cody-Waite exp,
  * group score = sum of the group_topn largest keys of the group, the topk_group best groups
@@ -205,7 +195,7 @@ size_t moe_route_workspace_size(int64_t G, int32_t num_experts, int64_t H);
 moe_status moe_route(const void* global_x, const int32_t* row_valid, int64_t G, int64_t H,
                      moe_dtype dt, const void* w_router, const float* bias,
                      const moe_route_cfg* cfg, float* logits, int32_t* topk_ids, float* topk_w,
-                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+                     hipStream_t stream);
 
 /* moe_route_from_logits -- the selection step alone, on caller logits fp32[G, E]. */
 moe_status moe_route_from_logits(const float* logits, const int32_t* row_valid, int64_t G,

@@ -23,8 +23,8 @@ def _outputs(layer, with_out=True):
 
 @pytest.mark.parametrize("name", ["cfg3", "mid", "cfg3-fixed", "cfg3-entry", "cfg3-exit", "cfg4"])
 def test_layer_step_graph_replays_bitwise(name):
-    # the decode workload (static bound 24, chunk-parallel gate with its workspace), a
-    # mid-sized ragged batch on the running-total gate, the decode workload in the
+    # the decode workload (static bound 24, the 16x16-chain gate), a
+    # mid-sized ragged batch, the decode workload in the
     # fixed-capacity layout (16 slots x 384 rows), the decode workload with the fused
     # entry step (its residual is restored before every run, since the step updates it), the
     # decode workload with the fused exit (the global output buffer is then not written),

@@ -269,39 +269,52 @@ def test_identity_experts_combine_returns_weighted_sum():
 
 @pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
 def test_gate_kernels_bitwise(dt):
-    # every gate kernel -- chunk-parallel with the partial table (small G), the running-total
-    # one on 64-row blocks (G = 16347: its 256 blocks of 64 rows fit one round, where 128-row
-    # blocks would leave half the CUs idle) and on 128-row blocks (G = 33000), each with a
-    # ragged last chunk (H = 7 * 128 + 104, 232) or through the pipelined whole-chunk path
-    # (H = 256, 384; at 128-row blocks that is the 8-wave kernel, also with subnormal
-    # products) -- against the oracle, bit for bit, with ragged row and expert tiles
+    # every gate kernel against the oracle's single ascending fma chain, bit for bit, with
+    # ragged row and expert tiles (E = 200) and every 17th row a pad row:
+    #   - 16x16 chains, 16-byte loads (H a multiple of 64): G = 300 at H = 384 (subnormal
+    #     products and partial sums), 448 and the model's 7168;
+    #   - 16x16 chains, element loads (ragged last slice): G = 300 at H = 1000, and a batch
+    #     large enough for 128-row blocks but with H = 232 (G = 16347);
+    #   - the 32x32-chain kernels: G = 16384 (64-row blocks, 4 waves) and 33000 (128-row
+    #     blocks, 8 waves) at H = 256 (also subnormal) and 384;
+    #   - rows whose chain ends at -0 (one tiny negative product in the last real column of
+    #     a ragged H): the padded columns must leave the sign of zero in place.
     import combine_dp_gather_amd as m
     rng = np.random.default_rng(21)
     cfg = m.make_route_cfg("softmax", 200, 4)
-    # third case: magnitudes whose products and partial sums are subnormal fp32
-    for G, H, scale in ((300, 1000, 1.0), (128 * 128 - 37, 232, 1.0), (300, 384, 2.0 ** -66),
-                        (128 * 128 - 37, 256, 1.0), (33000, 384, 1.0), (33000, 232, 1.0),
-                        (33000, 256, 2.0 ** -66)):
+    cases = ((300, 384, 2.0 ** -66), (300, 448, 1.0), (1000, 7168, 1.0), (300, 1000, 1.0),
+             (128 * 128 - 37, 232, 1.0), (16384, 256, 1.0), (33000, 384, 1.0), (33000, 256, 2.0 ** -66),
+             (300, 232, "negzero"), (33000, 200, "negzero"))
+    for G, H, scale in cases:
         say(f"[gate] dtype={dt} G={G} H={H} E=200 scale={scale}")
-        x = torch.from_numpy((rng.standard_normal((G, H)) * scale).astype(np.float32)).to(dt)
-        w = torch.from_numpy((rng.standard_normal((200, H)) * 0.05 * scale).astype(np.float32)).to(dt)
+        s = 1.0 if scale == "negzero" else scale
+        xf = (rng.standard_normal((G, H)) * s).astype(np.float32)
+        wf = (rng.standard_normal((200, H)) * 0.05 * s).astype(np.float32)
+        if scale == "negzero":
+            # rows 1, 5, 9, ...: only the last column is non-zero, and its products with
+            # every expert round to -0
+            xf[1::4] = 0.0
+            xf[1::4, H - 1] = -(2.0 ** -100)
+            wf[:, H - 1] = 2.0 ** -100
+        x = torch.from_numpy(xf).to(dt)
+        w = torch.from_numpy(wf).to(dt)
         rv = np.ones(G, dtype=np.int32)
         rv[::17] = 0
         xb = x.view(torch.int16).numpy().view(np.uint16) if dt == torch.bfloat16 else x.numpy()
         wb = w.view(torch.int16).numpy().view(np.uint16) if dt == torch.bfloat16 else w.numpy()
         ref = oracle.gate_logits(xb, wb, row_valid=rv)
-        xd, wd, rvd = x.cuda(), w.cuda(), torch.from_numpy(rv).cuda()
-        ws_bytes = m.moe_route_workspace_size(G, 200, H)
-        assert (ws_bytes > 0) == (G < 1000)
-        if scale < 1:
+        if scale == "negzero":
+            neg = ref[1::4][rv[1::4] != 0]
+            assert np.all(np.signbit(neg)) and np.all(neg == 0)
+        elif scale < 1:
             assert np.any((ref != 0) & (np.abs(ref) < np.finfo(np.float32).tiny))
-        for ws in ([None, torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")] if ws_bytes else [None]):
-            lg = torch.full((G, 200), float("nan"), device="cuda")
-            ids = torch.empty((G, 4), dtype=torch.int32, device="cuda")
-            tw = torch.empty((G, 4), dtype=torch.float32, device="cuda")
-            m.moe_route(xd, rvd, wd, None, cfg, lg, ids, tw, ws)
-            torch.cuda.synchronize()
-            assert np.array_equal(lg.cpu().numpy().view(np.uint32), ref.view(np.uint32)), ws is None
+        xd, wd, rvd = x.cuda(), w.cuda(), torch.from_numpy(rv).cuda()
+        lg = torch.full((G, 200), float("nan"), device="cuda")
+        ids = torch.empty((G, 4), dtype=torch.int32, device="cuda")
+        tw = torch.empty((G, 4), dtype=torch.float32, device="cuda")
+        m.moe_route(xd, rvd, wd, None, cfg, lg, ids, tw)
+        torch.cuda.synchronize()
+        assert np.array_equal(lg.cpu().numpy().view(np.uint32), ref.view(np.uint32))
 
 
 def test_route_from_logits_ties_and_fake_balance():

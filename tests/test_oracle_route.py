@@ -99,7 +99,7 @@ def test_gate_logits_order_closed_form():
 def test_gate_is_one_chain_not_chunked():
     # a chunked reading (128-wide fma chains, chunk sums added left to right) differs from
     # the single chain on ordinary inputs, so the pins above would catch an oracle that
-    # chunked h; count how many logits (and top-2 picks) the two readings disagree on
+    # chunked h
     rng = np.random.default_rng(5)
     x = moe_synth.to_bf16_bits(rng.standard_normal((64, 1024)).astype(np.float32))
     w = moe_synth.to_bf16_bits((rng.standard_normal((8, 1024)) * 0.02).astype(np.float32))
