@@ -22,7 +22,7 @@ __all__ = [
     "moe_gather_layout", "moe_gather", "moe_entry_gather", "moe_scatter", "moe_expert_load",
     "moe_physical_to_logical_count", "moe_eplb_balancedness", "moe_eplb_rebalance",
     "moe_eplb_logical_to_physical", "moe_route", "moe_route_from_logits",
-    "moe_dispatch", "moe_dispatch_workspace_size", "moe_expert_gemm", "moe_expert_gemm_up",
+    "moe_dispatch", "moe_dispatch_noalloc", "moe_dispatch_workspace_size", "moe_expert_gemm", "moe_expert_gemm_up",
     "moe_expert_gemm_down", "moe_expert_gemm_workspace_size", "moe_combine", "moe_version",
     "PlanBuffers", "make_route_cfg", "make_expert_map", "make_expert_weights", "MoEError",
     "GatherLayout", "RouteCfg", "ExpertMap", "ExpertWeights", "Plan",
@@ -253,6 +253,15 @@ def moe_dispatch(global_x: torch.Tensor, topk_ids: torch.Tensor, emap: ExpertMap
         _ptr(global_x), _ptr(topk_ids), G, k, H, _dtype_code(global_x), ctypes.byref(emap),
         ctypes.byref(plan.struct), _ptr(x_perm), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def moe_dispatch_noalloc(global_x: torch.Tensor, topk_ids: torch.Tensor, emap: ExpertMap,
+                         plan: PlanBuffers, x_perm: torch.Tensor, stream=None) -> None:
+    """moe_dispatch with the library's fixed per-GPU scratch instead of a workspace."""
+    G, H = global_x.shape
+    check("moe_dispatch_noalloc", lib().moe_dispatch_noalloc(
+        _ptr(global_x), _ptr(topk_ids), G, plan.k, H, _dtype_code(global_x), ctypes.byref(emap),
+        ctypes.byref(plan.struct), _ptr(x_perm), _stream(stream)))
 
 
 # ------------------------------------------------------------------ experts

@@ -7,7 +7,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe_hip.so")
 
-MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_CAPACITY, MOE_ERR_HIP = range(5)
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_CAPACITY, MOE_ERR_HIP, MOE_ERR_SCRATCH_LIMIT = range(6)
 MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
 MOE_PAD_AUTO, MOE_PAD_MAX_LEN, MOE_PAD_SUM_LEN = 0, 1, 2
 MOE_GATE_EXACT, MOE_GATE_FAST = 0, 1
@@ -66,6 +66,8 @@ SIGNATURES = {
     "moe_dispatch_workspace_size": (c_sz, [c_i64, c_i32, c_i32]),
     "moe_dispatch": (c_i32, [c_vp, c_vp, c_i64, c_i32, c_i64, c_i32, ctypes.POINTER(ExpertMap),
                              ctypes.POINTER(Plan), c_vp, c_vp, c_sz, c_vp]),
+    "moe_dispatch_noalloc": (c_i32, [c_vp, c_vp, c_i64, c_i32, c_i64, c_i32, ctypes.POINTER(ExpertMap),
+                                     ctypes.POINTER(Plan), c_vp, c_vp]),
     "moe_expert_gemm_workspace_size": (c_sz, [c_i64, c_i64, c_i64, c_i32, c_i32]),
     "moe_expert_gemm": (c_i32, [c_vp, c_i32, ctypes.POINTER(Plan), ctypes.POINTER(ExpertWeights),
                                 c_i64, c_i64, c_vp, c_vp, c_sz, c_vp]),

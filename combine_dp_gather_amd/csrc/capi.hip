@@ -8,6 +8,7 @@ extern "C" const char* moe_status_string(moe_status s) {
         case MOE_ERR_UNSUPPORTED: return "unsupported combination";
         case MOE_ERR_CAPACITY: return "caller buffer too small";
         case MOE_ERR_HIP: return "HIP launch failed";
+        case MOE_ERR_SCRATCH_LIMIT: return "problem larger than the fixed scratch of a no-allocation entry point";
     }
     return "unknown status";
 }

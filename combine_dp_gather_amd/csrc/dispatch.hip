@@ -20,6 +20,8 @@
 //               below with the same slot), so rows follow ascending pair index: stable;
 //   4. permute: x_perm[row] = global_x[sorted_pair[row] / k], one block per row, streaming
 //               16-byte vectors, rows bounded by the device-side num_rows (no host sync).
+#include <mutex>
+
 #include "moe_dev.h"
 
 namespace moe {
@@ -448,11 +450,13 @@ extern "C" size_t moe_dispatch_workspace_size(int64_t G, int32_t k, int32_t num_
     return static_cast<size_t>(2 * nb * num_slots) * sizeof(int32_t) + 256;
 }
 
-extern "C" moe_status moe_dispatch(const void* global_x, const int32_t* topk_ids, int64_t G,
-                                   int32_t k, int64_t H, moe_dtype dt, const moe_expert_map* map,
-                                   const moe_plan* plan, void* x_perm, void* workspace,
-                                   size_t workspace_bytes, hipStream_t stream) {
-    using namespace moe;
+namespace moe {
+namespace {
+
+// Argument checks shared by both entry points; nothing is enqueued on failure.
+moe_status check_dispatch_args(const void* global_x, const int32_t* topk_ids, int64_t G, int32_t k,
+                               int64_t H, moe_dtype dt, const moe_expert_map* map, const moe_plan* plan,
+                               const void* x_perm) {
     MOE_CHECK_ARG(map && plan);
     MOE_CHECK_ARG(G >= 0 && k >= 1 && H > 0);
     MOE_CHECK_ARG(dt == MOE_F32 || dt == MOE_BF16);
@@ -470,10 +474,18 @@ extern "C" moe_status moe_dispatch(const void* global_x, const int32_t* topk_ids
     MOE_CHECK_ARG(G * k < (int64_t(1) << 31));
     if (G > 0) MOE_CHECK_ARG(topk_ids && plan->pair_row && global_x);
     if (plan->cap > 0) MOE_CHECK_ARG(plan->sorted_pair && x_perm);
+    return MOE_OK;
+}
+
+// The four kernels on a checked call; `workspace` holds the per-block count and base tables
+// (2 * NB * E_l int32), every entry of which the count and scan kernels write before any
+// kernel reads it, so its previous contents never matter.
+moe_status run_dispatch(const void* global_x, const int32_t* topk_ids, int64_t G, int32_t k, int64_t H,
+                        moe_dtype dt, const moe_expert_map* map, const moe_plan* plan, void* x_perm,
+                        void* workspace, hipStream_t stream) {
     const int64_t P = G * k;
     const int64_t NB = num_blocks(G, k);
     const int El = map->num_slots;
-    if (workspace_bytes < moe_dispatch_workspace_size(G, k, El)) return MOE_ERR_CAPACITY;
     MOE_CHECK_ARG(NB == 0 || workspace != nullptr);
     MapArgs m{map->phys_of, map->n_rep, map->num_logical, map->max_rep, map->first_slot, El};
     int32_t* blk_counts = static_cast<int32_t*>(workspace);
@@ -510,4 +522,54 @@ extern "C" moe_status moe_dispatch(const void* global_x, const int32_t* topk_ids
     if (row_bytes % 4 == 0 && aligned(global_x, 4) && aligned(x_perm, 4))
         return launch_permute<uint32_t>(global_x, plan, row_bytes, x_perm, stream);
     return launch_permute<uint16_t>(global_x, plan, row_bytes, x_perm, stream);
+}
+
+// ---- the no-allocation variant's scratch: a fixed device array, one copy per GPU, kept
+// until the process ends.  In host code `scratch` names a host-side stand-in, never the
+// device memory: its device address is looked up once per device with that device current
+// and only that address is handed to kernels.
+static __device__ __align__(256) unsigned char scratch[MOE_DISPATCH_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices] = {};
+
+moe_status scratch_for_current_device(void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return MOE_ERR_HIP;
+        scratch_ptr[dev] = p;
+    }
+    *out = scratch_ptr[dev];
+    return MOE_OK;
+}
+
+}  // namespace
+}  // namespace moe
+
+extern "C" moe_status moe_dispatch(const void* global_x, const int32_t* topk_ids, int64_t G,
+                                   int32_t k, int64_t H, moe_dtype dt, const moe_expert_map* map,
+                                   const moe_plan* plan, void* x_perm, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream) {
+    const moe_status st = moe::check_dispatch_args(global_x, topk_ids, G, k, H, dt, map, plan, x_perm);
+    if (st != MOE_OK) return st;
+    if (workspace_bytes < moe_dispatch_workspace_size(G, k, map->num_slots)) return MOE_ERR_CAPACITY;
+    return moe::run_dispatch(global_x, topk_ids, G, k, H, dt, map, plan, x_perm, workspace, stream);
+}
+
+extern "C" moe_status moe_dispatch_noalloc(const void* global_x, const int32_t* topk_ids, int64_t G,
+                                           int32_t k, int64_t H, moe_dtype dt, const moe_expert_map* map,
+                                           const moe_plan* plan, void* x_perm, hipStream_t stream) {
+    moe_status st = moe::check_dispatch_args(global_x, topk_ids, G, k, H, dt, map, plan, x_perm);
+    if (st != MOE_OK) return st;
+    if (moe_dispatch_workspace_size(G, k, map->num_slots) > MOE_DISPATCH_NOALLOC_SCRATCH_BYTES)
+        return MOE_ERR_SCRATCH_LIMIT;
+    void* ws = nullptr;
+    st = moe::scratch_for_current_device(&ws);
+    if (st != MOE_OK) return st;
+    return moe::run_dispatch(global_x, topk_ids, G, k, H, dt, map, plan, x_perm, ws, stream);
 }

@@ -47,7 +47,9 @@ typedef enum {
     MOE_ERR_INVALID_ARG = 1,  /* a pointer, size or enum value is out of range; nothing enqueued */
     MOE_ERR_UNSUPPORTED = 2,  /* a valid combination this build does not implement */
     MOE_ERR_CAPACITY = 3,     /* a caller buffer (workspace, table) is too small */
-    MOE_ERR_HIP = 4           /* the HIP runtime refused a launch */
+    MOE_ERR_HIP = 4,          /* the HIP runtime refused a launch */
+    MOE_ERR_SCRATCH_LIMIT = 5 /* the problem needs more than a no-allocation entry point's
+                                 fixed scratch holds; nothing enqueued */
 } moe_status;
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
@@ -263,6 +265,24 @@ size_t moe_dispatch_workspace_size(int64_t G, int32_t k, int32_t num_slots);
 moe_status moe_dispatch(const void* global_x, const int32_t* topk_ids, int64_t G, int32_t k,
                         int64_t H, moe_dtype dt, const moe_expert_map* map, const moe_plan* plan,
                         void* x_perm, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of device scratch the library keeps for moe_dispatch_noalloc, one copy per GPU. */
+#define MOE_DISPATCH_NOALLOC_SCRATCH_BYTES (1u << 20)
+
+/* moe_dispatch_noalloc -- moe_dispatch for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments and results as moe_dispatch, without the workspace: the per-block count tables
+ * live in a fixed device array of MOE_DISPATCH_NOALLOC_SCRATCH_BYTES that the library holds
+ * on every GPU it runs on until the process ends (its address is looked up on a device's
+ * first call).  The call allocates nothing.  A problem whose
+ * moe_dispatch_workspace_size(G, k, E_l) exceeds the array returns MOE_ERR_SCRATCH_LIMIT
+ * with nothing enqueued (at E_l = 16 slots that is G*k above about 8.3 million pairs).
+ * Every call on one GPU shares that GPU's array: calls that overlap on one GPU (two
+ * streams, two threads) race and give undefined plans; serialise them.  The array keeps the
+ * last call's contents, which no later call depends on. */
+moe_status moe_dispatch_noalloc(const void* global_x, const int32_t* topk_ids, int64_t G, int32_t k,
+                                int64_t H, moe_dtype dt, const moe_expert_map* map,
+                                const moe_plan* plan, void* x_perm, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------------
  * Experts: per local slot e, over the rows of its segment,
