@@ -359,6 +359,55 @@ def dequant_block(q: np.ndarray, s: np.ndarray, block: int = 128) -> np.ndarray:
     return v * np.repeat(np.repeat(s.astype(np.float64), block, axis=-2), block, axis=-1)
 
 
+E4M3_MAX = 448.0
+ACT_GROUP = 128
+
+
+def e4m3_encode(v: np.ndarray) -> np.ndarray:
+    """OCP e4m3fn code of each value (|v| <= 448), rounded to nearest, ties to even.  A
+    binade [2^e, 2^(e+1)) with e >= -6 holds 8 codes 2^(e-3) apart; below 2^-6 the codes are
+    the multiples of 2^-9 (subnormals).  The sign bit is kept, so -0 encodes as 0x80."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    if np.any(a > E4M3_MAX) or np.any(np.isnan(v)):
+        raise ValueError("e4m3_encode takes finite values within +-448")
+    _, ex = np.frexp(a)                         # a = m 2^ex, m in [0.5, 1)
+    e = np.maximum(ex - 1, -6)                  # binade of a (subnormals share e = -6)
+    step = np.ldexp(1.0, e - 3)
+    n = np.rint(a / step)                       # a / step is exact; rint rounds ties to even
+    mag = n * step                              # rounded magnitude (may carry to 2^(e+1))
+    _, ex2 = np.frexp(mag)
+    e2 = ex2 - 1
+    normal = mag >= 2.0 ** -6
+    mant = np.where(normal, np.rint(mag / np.ldexp(1.0, np.where(normal, e2, 0) - 3)) - 8, 0)
+    field = np.where(normal, ((e2 + 7) << 3) + mant, np.rint(mag / 2.0 ** -9))
+    return (field.astype(np.uint8) | (np.signbit(v).astype(np.uint8) << 7)).astype(np.uint8)
+
+
+def quant_group_e4m3(a: np.ndarray, group: int = ACT_GROUP):
+    """Per-token-group activation quantisation (SGLang page, section "prefll 侧的一个必要步
+    骤：per-token-group 量化": fp8 activations with one scale per 128 consecutive values of a
+    token).  The pages fix the group, not the scale rule; the reading is absmax scaling, in
+    fp32 as the activations are stored:
+        s = amax(|x| over the group) / 448   (1 for an all-zero group)
+        q = e4m3_rne(clamp(x / s, -448, 448))
+    so that the group's largest value maps onto the largest e4m3 code.  `a` is fp32 (or bf16
+    bits) [R, K] with K a multiple of the group; returns codes uint8 [R, K] and scales fp32
+    [R, K / group]."""
+    x = as_f32(a)
+    R, K = x.shape
+    g = x.reshape(R, K // group, group)
+    amax = np.max(np.abs(g), axis=2)
+    s = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    y = np.clip(g / s[:, :, None], np.float32(-E4M3_MAX), np.float32(E4M3_MAX)).astype(np.float32)
+    return e4m3_encode(y).reshape(R, K), s
+
+
+def dequant_group(q: np.ndarray, s: np.ndarray, group: int = ACT_GROUP) -> np.ndarray:
+    """value = e4m3(q) * s[r, c // group], exact in float64."""
+    return e4m3_decode(q) * np.repeat(s.astype(np.float64), group, axis=1)
+
+
 def expert_weights_f64(inp, slot: int):
     """(Wg [I,H], Wu [I,H], Wd [H,I]) of one local slot in float64."""
     if inp.w13 is not None:
@@ -379,6 +428,18 @@ def swiglu(x: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray) -> np.
     u = x @ wu.T
     h = gt / (1.0 + np.exp(-gt)) * u
     return h @ wd.T
+
+
+def swiglu_e4m3_act(x: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray) -> np.ndarray:
+    """The expert with fp8 activations, as the pages' DeepGEMM path feeds it: the input rows
+    are quantised per 1x128 group (quant_group_e4m3) before the gate/up product, and the
+    intermediate h, stored as bf16, is quantised the same way before the down product.  The
+    products of the exactly dequantised operands are float64."""
+    xd = dequant_group(*quant_group_e4m3(x))
+    gt = xd @ wg.T
+    u = xd @ wu.T
+    h = bf16_rne(gt / (1.0 + np.exp(-gt)) * u)
+    return dequant_group(*quant_group_e4m3(h)) @ wd.T
 
 
 def expert_ffn(x_perm: np.ndarray, plan: dict, inp) -> np.ndarray:
@@ -648,3 +709,29 @@ def rel_err(got: np.ndarray, ref: np.ndarray) -> float:
     den = float(np.max(np.abs(ref)))
     num = float(np.max(np.abs(got - ref)))
     return num / den if den > 0 else num
+
+
+def row_rel_err(got: np.ndarray, ref: np.ndarray) -> float:
+    """Largest per-row error: max over rows r of max|got_r - ref_r| / max|ref_r|.  A row whose
+    reference is all zero contributes max|got_r|.  Unlike rel_err, one row with a small
+    magnitude cannot hide behind the largest value of the whole tensor."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if ref.size == 0:
+        return 0.0
+    got = got.reshape(ref.shape[0], -1)
+    ref = ref.reshape(ref.shape[0], -1)
+    num = np.max(np.abs(got - ref), axis=1)
+    den = np.max(np.abs(ref), axis=1)
+    per_row = np.where(den > 0, num / np.where(den > 0, den, 1.0), num)
+    return float(per_row.max())
+
+
+def bf16_ulp(v: np.ndarray) -> np.ndarray:
+    """Spacing of bf16 values at |v| (float64): 2^(e - 7) for |v| in [2^e, 2^(e+1)) with
+    e >= -126, and the subnormal spacing 2^-133 below 2^-126 (and at 0)."""
+    a = np.abs(np.asarray(v, dtype=np.float64))
+    _, ex = np.frexp(a)                   # a = m * 2^ex, m in [0.5, 1): floor(log2 a) = ex - 1
+    e = np.where(a > 0, np.maximum(ex - 1, -126), -126)
+    return np.ldexp(1.0, e - 7)
+

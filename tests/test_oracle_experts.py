@@ -146,3 +146,89 @@ def test_zero_gate_weights_give_zero_output():
     inp.w13[:, 0] = 0
     res = oracle.run_layer(inp, "sum")
     assert np.all(res["out"] == 0)
+
+
+# ---------------------------------------------------------------- fp8 activations
+
+def _finite_codes():
+    return np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+
+
+def test_e4m3_encode_round_trips_every_finite_code():
+    codes = _finite_codes()
+    assert np.array_equal(oracle.e4m3_encode(oracle.e4m3_decode(codes)), codes)
+    g = json.load(open(GOLD))
+    assert np.array_equal(oracle.e4m3_encode(np.array(g["values"])), np.array(g["codes"], dtype=np.uint8))
+
+
+def test_e4m3_encode_is_nearest_code_ties_to_even_brute_force():
+    # every positive value's nearest code by exhaustive search over the 127 positive codes,
+    # ties to the even code (the lower mantissa bit 0), at midpoints and just off them
+    pos = np.arange(0, 0x7F, dtype=np.uint8)
+    pv = oracle.e4m3_decode(pos)
+    mids = (pv[:-1] + pv[1:]) / 2
+    probes = np.concatenate([mids, np.nextafter(mids, 0), np.nextafter(mids, 1e9), pv,
+                             np.random.default_rng(1).uniform(0, 448, 5000)])
+    for v in probes:
+        d = np.abs(pv - v)
+        best = np.flatnonzero(d == d.min())
+        want = best[0] if len(best) == 1 else best[best % 2 == 0][0]
+        assert oracle.e4m3_encode(np.array([v]))[0] == want, v
+        assert oracle.e4m3_encode(np.array([-v]))[0] == (want | 0x80), v
+
+
+def test_quant_group_closed_forms():
+    rng = np.random.default_rng(5)
+    # a group of e4m3 values times 2^j whose largest is 448 * 2^j: scale 2^j exactly, codes
+    # returned unchanged, dequantisation exact
+    codes = rng.integers(0, 0x7F, size=(6, 256)).astype(np.uint8) | (rng.integers(0, 2, size=(6, 256)) << 7).astype(np.uint8)
+    codes[:, 5] = 0x7E
+    codes[:, 130] = 0xFE
+    j = rng.integers(-20, 20, size=(6, 1))
+    x = (oracle.e4m3_decode(codes) * np.ldexp(1.0, j)).astype(np.float32)
+    q, s = oracle.quant_group_e4m3(x)
+    assert np.array_equal(s, np.repeat(np.ldexp(1.0, j), 2, axis=1).astype(np.float32))
+    assert np.array_equal(q, codes)
+    assert np.array_equal(oracle.dequant_group(q, s), x.astype(np.float64))
+    # an all-zero group: scale 1, codes 0
+    z = np.zeros((1, 128), dtype=np.float32)
+    qz, sz = oracle.quant_group_e4m3(z)
+    assert sz[0, 0] == 1.0 and not qz.any()
+
+
+def test_quant_group_error_bound_and_amax_code():
+    rng = np.random.default_rng(6)
+    x = (rng.standard_normal((40, 384)) * np.exp(rng.uniform(-8, 8, (40, 1)))).astype(np.float32)
+    q, s = oracle.quant_group_e4m3(x)
+    # every group's largest magnitude lands on the largest code
+    g = x.reshape(40, 3, 128)
+    big = np.argmax(np.abs(g), axis=2)
+    qg = q.reshape(40, 3, 128)
+    assert np.all(np.take_along_axis(qg, big[..., None], axis=2)[..., 0] & 0x7F == 0x7E)
+    # |x - dequant| is at most half a code step: 2^-4 |x| in the normal range of x / s,
+    # 2^-10 s below it (subnormal step 2^-9), plus fp32 rounding of x / s
+    d = oracle.dequant_group(q, s)
+    ss = np.repeat(s.astype(np.float64), 128, axis=1)
+    y = np.abs(x.astype(np.float64)) / ss
+    bound = np.where(y >= 2.0 ** -6, 2.0 ** -4 * np.abs(x), 2.0 ** -10 * ss) * (1 + 2.0 ** -20)
+    assert np.all(np.abs(d - x) <= bound)
+
+
+def test_swiglu_e4m3_act_close_to_exact_and_exact_on_representable_input():
+    rng = np.random.default_rng(7)
+    H, I = 256, 128
+    wg, wu = rng.standard_normal((I, H)) * 0.05, rng.standard_normal((I, H)) * 0.05
+    wd = rng.standard_normal((H, I)) * 0.05
+    x = rng.standard_normal((12, H)).astype(np.float32)
+    y = oracle.swiglu_e4m3_act(x, wg, wu, wd)
+    ref = oracle.swiglu(x.astype(np.float64), wg, wu, wd)
+    assert oracle.rel_err(y, ref) < 0.1
+    # with representable inputs and an identity down projection of a representable h the
+    # fp8 path only rounds h to bf16 and to e4m3: compare against that composition
+    # (e4m3 values of moderate size, each group's largest at 448, all times 2^-6)
+    xs = (oracle.e4m3_decode(rng.integers(0x28, 0x48, size=(3, H)).astype(np.uint8))).astype(np.float32)
+    xs[:, ::128] = 448.0
+    xs *= np.float32(2.0 ** -6)
+    h = oracle.bf16_rne(oracle.swiglu(xs.astype(np.float64), wg, wu, np.eye(I)))
+    want = oracle.dequant_group(*oracle.quant_group_e4m3(h)) @ wd.T
+    assert np.array_equal(oracle.swiglu_e4m3_act(xs, wg, wu, wd), want)
