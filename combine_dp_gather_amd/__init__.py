@@ -22,7 +22,7 @@ __all__ = [
     "moe_gather_layout", "moe_gather", "moe_entry_gather", "moe_scatter", "moe_expert_load",
     "moe_physical_to_logical_count", "moe_eplb_balancedness", "moe_eplb_rebalance",
     "moe_eplb_logical_to_physical", "moe_route", "moe_route_from_logits",
-    "moe_dispatch", "moe_dispatch_noalloc", "moe_dispatch_workspace_size", "moe_expert_gemm", "moe_expert_gemm_up",
+    "moe_dispatch", "moe_dispatch_noalloc", "moe_dispatch_workspace_size", "moe_quant_act_fp8", "moe_expert_gemm", "moe_expert_gemm_up",
     "moe_expert_gemm_down", "moe_expert_gemm_workspace_size", "moe_combine", "moe_version",
     "PlanBuffers", "make_route_cfg", "make_expert_map", "make_expert_weights", "MoEError",
     "GatherLayout", "RouteCfg", "ExpertMap", "ExpertWeights", "Plan",
@@ -265,6 +265,14 @@ def moe_dispatch_noalloc(global_x: torch.Tensor, topk_ids: torch.Tensor, emap: E
 
 
 # ------------------------------------------------------------------ experts
+
+def moe_quant_act_fp8(act: torch.Tensor, num_rows: torch.Tensor, q: torch.Tensor, s_t: torch.Tensor,
+                      stream=None) -> None:
+    """Per-1x128-group e4m3 codes q [cap, K] (uint8) and transposed scales s_t [K/128, cap]
+    (fp32) of the first num_rows rows of act (bf16 [cap, K])."""
+    cap, K = act.shape
+    check("moe_quant_act_fp8", lib().moe_quant_act_fp8(_ptr(act), _ptr(num_rows), cap, K, _ptr(q),
+                                                       _ptr(s_t), _stream(stream)))
 
 def make_expert_weights(w13: torch.Tensor, w2: torch.Tensor, s13: Optional[torch.Tensor] = None,
                         s2: Optional[torch.Tensor] = None, fp8_act: str = "bf16") -> ExpertWeights:

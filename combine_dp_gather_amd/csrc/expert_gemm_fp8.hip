@@ -7,9 +7,11 @@
 // expert_alignment 128).  Values: weight = e4m3(q) * s_w[block], activation ~ e4m3(q) * s_a.
 //
 // quant kernel: one wave per row, one 128-column group per step: amax by wave reduction,
-//   scale = amax / 448 (1 for an all-zero group), codes = RNE(x * 448 / amax) clamped to
-//   +-448 (the hardware conversion turns larger magnitudes into NaN).  Scales are stored
-//   transposed, [K/128][cap], so a tile's 256 scales of one K group are contiguous.
+//   scale s = amax / 448 (1 for an all-zero group), codes = RNE(x / s) clamped to +-448 (the
+//   hardware conversion turns larger magnitudes into NaN), both in fp32 with correctly
+//   rounded divisions, so every code is decided exactly as the absmax reading of the page's
+//   per-token-group step defines it.  Scales are stored transposed, [K/128][cap], so a
+//   tile's 256 scales of one K group are contiguous.
 // GEMM kernel (gfx950 v_mfma_f32_32x32x64_f8f6f4, e4m3 x e4m3, fp32 accumulate):
 //   - block tile 256 rows x 128 columns (up: 64 gate + the same 64 up columns), 4 waves in
 //     2x2, each 128 x 64 = 4x2 MFMA blocks;
@@ -53,12 +55,12 @@ __global__ __launch_bounds__(256) void quant_fp8_kernel(const uint16_t* __restri
             float m = fmaxf(fabsf(x0), fabsf(x1));
 #pragma unroll
             for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-            const float inv = m > 0.f ? kE4M3Max / m : 1.f;
-            const float y0 = fminf(fmaxf(x0 * inv, -kE4M3Max), kE4M3Max);
-            const float y1 = fminf(fmaxf(x1 * inv, -kE4M3Max), kE4M3Max);
+            const float sc = m > 0.f ? __fdiv_rn(m, kE4M3Max) : 1.f;
+            const float y0 = fminf(fmaxf(__fdiv_rn(x0, sc), -kE4M3Max), kE4M3Max);
+            const float y1 = fminf(fmaxf(__fdiv_rn(x1, sc), -kE4M3Max), kE4M3Max);
             const int packed = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
             dst[g * (QB / 2) + lane] = static_cast<uint16_t>(packed & 0xffff);
-            if (lane == 0) s_t[g * cap + r] = m > 0.f ? m / kE4M3Max : 1.f;
+            if (lane == 0) s_t[g * cap + r] = sc;
         }
     }
 }
@@ -285,6 +287,16 @@ __global__ __launch_bounds__(gemm::kThreads, 1) void grouped_gemm_fp8_kernel(Fp8
 
 size_t align256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
 
+moe_status launch_quant(const void* act, const int64_t* num_rows, int64_t cap, int64_t K, uint8_t* q,
+                        float* s_t, hipStream_t stream) {
+    int64_t qblocks = ceil_div(cap, 4);
+    if (qblocks > 4096) qblocks = 4096;
+    hipLaunchKernelGGL(quant_fp8_kernel, dim3(static_cast<unsigned>(qblocks)), dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(act), num_rows, cap, K, q, s_t);
+    MOE_LAUNCH_CHECK();
+    return MOE_OK;
+}
+
 }  // namespace
 
 namespace gemm {
@@ -308,11 +320,8 @@ moe_status run_fp8_stage(bool up, const void* act, const moe_plan* plan,
     MOE_CHECK_ARG(workspace && aligned(workspace, 256));
     uint8_t* qa = static_cast<uint8_t*>(workspace);
     float* sa = reinterpret_cast<float*>(qa + align256(static_cast<size_t>(plan->cap * K)));
-    int64_t qblocks = ceil_div(plan->cap, 4);
-    if (qblocks > 4096) qblocks = 4096;
-    hipLaunchKernelGGL(quant_fp8_kernel, dim3(static_cast<unsigned>(qblocks)), dim3(256), 0, stream,
-                       static_cast<const uint16_t*>(act), plan->num_rows, plan->cap, K, qa, sa);
-    MOE_LAUNCH_CHECK();
+    const moe_status qs = launch_quant(act, plan->num_rows, plan->cap, K, qa, sa, stream);
+    if (qs != MOE_OK) return qs;
     Fp8Args g;
     g.A = qa;
     g.SA = sa;
@@ -338,3 +347,13 @@ moe_status run_fp8_stage(bool up, const void* act, const moe_plan* plan,
 
 }  // namespace gemm
 }  // namespace moe
+
+extern "C" moe_status moe_quant_act_fp8(const void* act, const int64_t* num_rows, int64_t cap, int64_t K,
+                                        uint8_t* q, float* s_t, hipStream_t stream) {
+    MOE_CHECK_ARG(cap >= 0 && K > 0 && K % moe::QB == 0);
+    if (cap == 0) return MOE_OK;
+    MOE_CHECK_ARG(act && num_rows && q && s_t);
+    MOE_CHECK_ARG(moe::aligned(act, 4) && moe::aligned(q, 2));
+    return moe::launch_quant(act, num_rows, cap, K, q, s_t, stream);
+}
+

@@ -311,6 +311,22 @@ typedef struct {
 } moe_expert_weights;
 /* fp8 weights: value = e4m3(q) * scale of its 128x128 block. */
 
+/* moe_quant_act_fp8 -- the per-token-group activation quantisation (the SGLang page,
+ * section "prefll 侧的一个必要步骤：per-token-group 量化") that moe_expert_gemm runs before each
+ * product when fp8_act is MOE_FP8_ACT_E4M3, exposed on its own.  Rows [0, min(*num_rows,
+ * cap)) of act are cut into groups of 128 consecutive values; per group, in fp32 with
+ * correctly rounded divisions,
+ *     s = amax / 448 (1 for an all-zero group),   code = e4m3 RNE of clamp(x / s, +-448)
+ * (OCP e4m3fn).  The pages fix the group, not the scale rule; absmax scaling is the reading.
+ *   act       device bf16 [cap, K], K a multiple of 128, 4-byte aligned
+ *   num_rows  device int64[1] (read on the device; rows past it are left untouched)
+ *   q         device uint8 [cap, K]: the codes
+ *   s_t       device fp32 [K / 128, cap]: the scales, transposed so that one group's scales
+ *             of consecutive rows are contiguous
+ * Returns MOE_ERR_INVALID_ARG for K not a multiple of 128 or a null or misaligned buffer. */
+moe_status moe_quant_act_fp8(const void* act, const int64_t* num_rows, int64_t cap, int64_t K,
+                             uint8_t* q, float* s_t, hipStream_t stream);
+
 /* Device workspace (bytes) moe_expert_gemm needs (the intermediate h and, for fp8 weights,
  * the quantised activations). */
 size_t moe_expert_gemm_workspace_size(int64_t cap, int64_t H, int64_t I, moe_dtype act_dt,

@@ -442,8 +442,10 @@ def swiglu_e4m3_act(x: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarra
     return dequant_group(*quant_group_e4m3(h)) @ wd.T
 
 
-def expert_ffn(x_perm: np.ndarray, plan: dict, inp) -> np.ndarray:
-    """y_perm rows of every segment; alignment pad rows stay 0.  float64."""
+def expert_ffn(x_perm: np.ndarray, plan: dict, inp, fp8_act: str = "bf16") -> np.ndarray:
+    """y_perm rows of every segment; alignment pad rows stay 0.  float64.  fp8_act = "e4m3"
+    quantises the activations per 1x128 group before each product (swiglu_e4m3_act)."""
+    ffn = swiglu_e4m3_act if fp8_act == "e4m3" else swiglu
     rows = len(plan["sorted_pair"])
     H = inp.cfg.hidden
     y = np.zeros((rows, H), dtype=np.float64)
@@ -455,7 +457,7 @@ def expert_ffn(x_perm: np.ndarray, plan: dict, inp) -> np.ndarray:
         if b <= a:
             continue
         wg, wu, wd = expert_weights_f64(inp, e)
-        y[a:b] = swiglu(xf[a:b], wg, wu, wd)
+        y[a:b] = ffn(xf[a:b], wg, wu, wd)
     return y
 
 
@@ -510,9 +512,10 @@ def token_output(inp, g: int, x_row: np.ndarray, ids_row: np.ndarray, w_row: np.
 # ============================================================================ whole layer
 
 def run_layer(inp, mode: str = "sum", align: int = 1, cap: Optional[int] = None,
-              seg_stride: int = 0) -> dict:
+              seg_stride: int = 0, fp8_act: str = "bf16") -> dict:
     """All six steps on the inputs of one workload; returns every intermediate.  seg_stride > 0
-    dispatches into the fixed-capacity layout (dispatch_masked) instead of packed segments."""
+    dispatches into the fixed-capacity layout (dispatch_masked) instead of packed segments;
+    fp8_act = "e4m3" runs the experts on per-group quantised activations."""
     cfg = inp.cfg
     dt = np.float32 if cfg.dtype == "f32" else np.uint16
     layout = gather_layout(cfg.num_tokens, mode, static_bound=cfg.static_bound)
@@ -524,7 +527,7 @@ def run_layer(inp, mode: str = "sum", align: int = 1, cap: Optional[int] = None,
     else:
         plan = dispatch(ids, inp.phys_of, inp.n_rep, cfg.first_local, cfg.num_local, align, cap)
     xp = permute_rows(gx, plan)
-    y = expert_ffn(xp, plan, inp)
+    y = expert_ffn(xp, plan, inp, fp8_act)
     out = combine(y, plan, w, G, cfg.routed_scale)
     return dict(layout=layout, global_x=gx, row_valid=valid, logits=logits, ids=ids, weights=w,
                 plan=plan, x_perm=xp, y_perm=y, out=out, replicas_out=scatter(layout, out))

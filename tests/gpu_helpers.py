@@ -60,3 +60,28 @@ def build_layer(inp, mode="sum", align=1, cap=None, fp8_act="bf16", seg_stride=0
     layer = MoELayer(spec_of(cfg), w, cfg.num_tokens, act_dtype(cfg), mode=mode,
                      static_bound=cfg.static_bound, align=align, cap=cap, seg_stride=seg_stride)
     return layer
+
+
+def check_combine_bound(out_dev, y_dev, w_dev, pair_row, k, scale=1.0, chunk=2048):
+    """The device's out against the float64 combine of the device's own y_perm and weights,
+    element by element: |out - ref| <= (one bf16 ulp of ref, for bf16 outputs) +
+    2 (k + 1) 2^-24 |scale| sum_j |w_j y_j| -- the rounding of the output plus the fp32
+    fused multiply-add chain over at most k terms and the scale.  Device arrays come as
+    numpy (bf16 as uint16 bits).  Returns the largest deviation as a fraction of its bound."""
+    import oracle
+    G = len(pair_row) // k
+    bf = out_dev.dtype == np.uint16
+    y = oracle.as_f32(y_dev).astype(np.float64)
+    w = np.asarray(w_dev, dtype=np.float64)
+    worst = 0.0
+    for g0 in range(0, G, chunk):
+        g1 = min(G, g0 + chunk)
+        pr = {"k": k, "pair_row": pair_row[g0 * k:g1 * k]}
+        ref = oracle.combine(y, pr, w[g0:g1], g1 - g0, scale)
+        mag = oracle.combine(np.abs(y), pr, np.abs(w[g0:g1]), g1 - g0, abs(scale))
+        bound = 2 * (k + 1) * 2.0 ** -24 * mag + (oracle.bf16_ulp(ref) if bf else 2.0 ** -149)
+        dev = np.abs(oracle.as_f32(out_dev[g0:g1]).astype(np.float64) - ref)
+        assert np.all(dev <= bound), f"rows {g0}..{g1}: {int(np.sum(dev > bound))} elements past the bound"
+        worst = max(worst, float(np.max(dev / bound)))
+    return worst
+
