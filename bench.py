@@ -6,9 +6,13 @@
 
 A step is one pass of all six C-ABI calls over one batch whose inputs are already resident
 in HBM.  By default the six calls are captured once in a HIP graph and each timed step is one
-replay (--eager launches them call by call).  Prints one JSON line: tokens/s, the roofline of the dominant kernel (timed with HIP
-events on the stream the kernels run on), per-kernel breakdown, and the CPU oracle timed on
-a bounded sample of the same workload.
+replay (--eager launches them call by call).  Before every timed step a kernel writes a
+512 MiB scratch buffer (outside the step's event pair), so the Infinity Cache and the L2 hold
+none of the step's data: the step figures are cold-cache ones, as median, p90 and mean over
+the timed steps; the same steps back to back give the warm figures beside them.  Prints one
+JSON line: tokens/s, the roofline of the dominant kernel (timed with HIP events on the stream
+the kernels run on), a per-call breakdown (cold, one eager step per flush), and the CPU
+oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -109,8 +113,19 @@ def eplb_cycle(cfg, inp, layer, reps, args, dev, act):
     return cfg2, inp2, w2, layer2, summary
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(inp, sample_per_replica: int):
-    """The oracle as it stands on the first rows of every replica (a bounded sample)."""
+    """The oracle as it stands on the first rows of every replica (a bounded sample): one
+    untimed run, then the median of three timed runs."""
     import oracle
     from dataclasses import replace
     import moe_synth
@@ -122,13 +137,19 @@ def cpu_baseline(inp, sample_per_replica: int):
                                w13_q=inp.w13_q, w13_s=inp.w13_s, w2_q=inp.w2_q, w2_s=inp.w2_s,
                                phys_of=inp.phys_of, n_rep=inp.n_rep)
     oracle.build()
-    t0 = time.perf_counter()
     oracle.run_layer(sinp, "sum")
-    dt = time.perf_counter() - t0
+    runs = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        oracle.run_layer(sinp, "sum")
+        runs.append(time.perf_counter() - t0)
+    dt = float(np.median(runs))
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     return {"value": round(sum(n) / dt, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(), "logical_cpus": os.cpu_count(),
             "sample": f"first {sample_per_replica} tokens of each replica ({sum(n)} tokens), all six "
-                      f"steps, oracle wall time {dt:.2f} s"}
+                      f"steps; one untimed run, median of 3 timed runs: {dt:.2f} s "
+                      f"(runs {', '.join(f'{r:.2f}' for r in runs)} s)"}
 
 
 def _time_ms(fn, iters=10):
@@ -195,11 +216,13 @@ def ceilings(cfg, R: int) -> dict:
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--flush-mib", type=int, default=512,
+                    help="scratch written before every timed step (0: no flush)")
     ap.add_argument("--workload", default="cfg4")
     ap.add_argument("--mode", default="sum", choices=["sum", "max", "auto"])
-    ap.add_argument("--cpu-sample", type=int, default=4096, help="tokens per replica for the oracle")
+    ap.add_argument("--cpu-sample", type=int, default=1024, help="tokens per replica for the oracle")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--fp8-act", default="bf16", choices=["bf16", "e4m3"],
                     help="fp8-weight workloads: keep activations bf16 (weights dequantised in the "
@@ -348,30 +371,60 @@ def main():
         torch.cuda.synchronize()
         stream = torch.cuda.current_stream()
 
-    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-           for _ in names] for _ in range(args.steps)]
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    t_wall = time.perf_counter()
-    for s in range(args.steps):
+    flush = torch.empty(args.flush_mib << 20, dtype=torch.uint8, device=dev) if args.flush_mib else None
+
+    def evict():
+        # a kernel writes the scratch buffer, so no earlier data stays in the caches
+        if flush is not None:
+            flush.fill_(1)
+
+    def new_events(n):
+        return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+
+    def run_step():
         if graph is not None:
             graph.replay()
         elif tbo is not None:
             tbo.forward(reps)
         else:
-            step(ev[s])
-    stop.record(stream)
+            step()
+
+    # the timed steps: K whole steps, each after the cache flush, each bracketed by its events
+    cold_ev = new_events(args.steps)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    for s in range(args.steps):
+        evict()
+        cold_ev[s][0].record(stream)
+        run_step()
+        cold_ev[s][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
-    total_ms = start.elapsed_time(stop)
-    if graph is not None or tbo is not None:
-        # the per-call breakdown comes from eager single-batch steps after the timed ones
-        for s in range(args.steps):
-            step(ev[s])
-        torch.cuda.synchronize()
-    per = {n: float(np.mean([ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)]))
-           for i, n in enumerate(names)}
+    cold = np.array([a.elapsed_time(b) for a, b in cold_ev])
+    total_ms = float(cold.sum())
+    # warm: the same steps back to back, no flush
+    warm_ev = new_events(args.steps)
+    torch.cuda.synchronize()
+    for s in range(args.steps):
+        warm_ev[s][0].record(stream)
+        run_step()
+        warm_ev[s][1].record(stream)
+    torch.cuda.synchronize()
+    warm = np.array([a.elapsed_time(b) for a, b in warm_ev])
+    # per call: K eager single-batch steps, each after the flush, with events around every call
+    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+           for _ in names] for _ in range(args.steps)]
+    for s in range(args.steps):
+        evict()
+        step(ev[s])
+    torch.cuda.synchronize()
+    per_all = {n: np.array([ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)])
+               for i, n in enumerate(names)}
+    per = {n: float(np.median(v)) for n, v in per_all.items()}
+
+    def stats(v):
+        return {"median_ms": round(float(np.median(v)), 4), "p90_ms": round(float(np.percentile(v, 90)), 4),
+                "mean_ms": round(float(np.mean(v)), 4)}
     ms_per_step = total_ms / args.steps
     T = cfg.T
     H, I, E, k, G = cfg.hidden, cfg.inter, cfg.num_experts, cfg.top_k, layer.G
@@ -415,7 +468,8 @@ def main():
         else:
             ach = amount / t_s / 1e12 if t_s > 0 else 0.0
             unit = "TFLOP/s"
-        kernels[n] = {"ms": round(per[n], 4), "bound": "mfma" if bound.startswith("mfma") else bound,
+        kernels[n] = {"ms": round(per[n], 4), "p90_ms": round(float(np.percentile(per_all[n], 90)), 4),
+                      "bound": "mfma" if bound.startswith("mfma") else bound,
                       "peak_kind": bound, "achieved": round(ach, 2), "peak": peaks[bound], "unit": unit,
                       "frac": round(ach / peaks[bound], 4)}
     if bf:
@@ -442,7 +496,10 @@ def main():
     dom = "gemm_up"
     roof = dict(kernels[dom])
     roof.pop("ms")
+    roof.pop("p90_ms")
     roof.pop("peak_kind")
+    roof["launch_ms"] = kernels[dom]["ms"]
+    roof["timing"] = "median over the timed steps' launches, each after the cache flush"
     fmt = "fp8" if mm == "mfma8" else "bf16"
     kname = ("grouped_gemm_fp8_kernel" if fmt == "fp8"
              else f"grouped_gemm_bf16_kernel<true, {'true' if fp8w else 'false'}>" if bf
@@ -462,6 +519,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step_median": round(float(np.median(cold)), 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -480,6 +538,10 @@ def main():
                    "tokens": T, "global_rows": G, "gather_mode": args.mode,
                    "routed_local_pairs": R, "parallelism": "one EP rank's share on 1 GPU",
                    **({"placement": eplb_info} if eplb_info is not None else {})},
+        "timing": {"cold": stats(cold), "warm": stats(warm),
+                   "flush": f"{args.flush_mib} MiB written by a kernel before every cold step, outside its events"
+                   if args.flush_mib else "none",
+                   "value_from": "timed cold steps: tokens x steps / sum of step times"},
         "roofline": roof,
         "kernels": kernels,
         "wall_s_timed": round(wall, 3),
