@@ -8,7 +8,11 @@
 //     h[r, i] = silu(sum_h x[r,h] Wg[e][i,h]) * (sum_h x[r,h] Wu[e][i,h])
 //     y[r, c] = sum_i h[r,i] Wd[e][c,i]
 //
-// bf16 path (gfx950 v_mfma_f32_32x32x16_bf16, fp32 accumulate):
+// bf16 weights run grouped_gemm_pp_kernel (below): the tiles, tile order and accumulation
+// order of the kernel described next, with 8 waves alternating between an MFMA phase and a
+// memory phase.  fp8 weights run the 4-wave kernel:
+//
+// 4-wave kernel (gfx950 v_mfma_f32_32x32x16_bf16, fp32 accumulate):
 //   - block tile 256 rows x 256 columns, 4 waves in a 2x2 grid, each wave 128x128 = 4x4 MFMA
 //     blocks (256 fp32 accumulators per lane, in AGPRs).  The weight fragment is the MFMAs'
 //     first operand, so each accumulator block holds its output block transposed and a lane
@@ -477,6 +481,230 @@ __global__ __launch_bounds__(M_THREADS, 1) void grouped_gemm_bf16_kernel(GemmArg
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
+// ------------------------------------------------------------------ bf16: 8-wave ping-pong
+// bf16 weights.  The same 256 x 256 tiles, tile order and accumulation order as
+// grouped_gemm_bf16_kernel (so the same bits), with 8 waves, two per SIMD: waves w and w + 4
+// share SIMD w % 4 and its 128 x 128 region, and each owns two of the region's four 32-column
+// blocks (up: gate block g and its up block g + 2; down: blocks 2g, 2g + 1), i.e. 128 x 64
+// outputs in 128 accumulators per lane, so two such waves fit in the register file.
+//   - The two groups of four waves (g = w / 4) alternate: while one group runs the 16 MFMAs of
+//     a 32-deep K slice, the other reads the fragments of its next slice and issues its DMAs,
+//     and a barrier between phases swaps them.  A wave that streams MFMAs then issues no
+//     vector-memory instruction (each costs such a wave tens of cycles of matrix-core time),
+//     and every SIMD's matrix core is fed by one wave of the pair or the other.
+//   - Operands come from L2 or HBM at a latency of thousands of cycles, so the LDS holds four
+//     32-deep stages (128 KB) and three slices are in flight: group 0 DMAs the A rows, group 1
+//     the weight rows, 4 instructions of 16 rows x 64 bytes per wave and slice.
+// Phases p = 0, 1, ...: group 0 computes slice n in phase 2n and group 1 in phase 2n + 1; each
+// wave reads slice n's fragments in the phase just before its own (group 0: 2n - 1, group 1:
+// 2n).  Slice n sits in stage n % 4.  In its memory phase for slice n every wave issues the
+// DMAs of slice n + 3 into stage (n + 3) % 4, whose last reads (slice n - 1, group 1, phase
+// 2n - 2) are behind a barrier; past the last slice it reloads the last slice there, never
+// read, so every phase issues the same number.  Before the barrier that ends phase 2n each
+// wave waits until only its two newest DMA groups (slices n + 2, n + 3) are in flight, so
+// slice n + 1 has landed when group 0 reads it in phase 2n + 1.  Group 1 starts one barrier
+// late and group 0 ends one barrier late, so every wave passes the same barriers.
+constexpr int PP_THREADS = 512;
+constexpr int PP_BK = 32;                        // K per slice
+constexpr int PP_STAGES = 4;
+constexpr int PP_CPR = PP_BK / 8;                // 16-byte chunks per LDS row
+constexpr int PP_RPB = 64 / PP_CPR;              // rows per 1 KB DMA block
+constexpr int PP_LPW = BM / PP_RPB / 4;          // DMAs per wave per slice
+static_assert(PP_LPW == 4 && PP_RPB == 16, "the wait counts below assume 4 DMAs of 16 rows");
+// the LDS serves a 16-byte-per-lane read 16 lanes at a time from 64 banks (256 bytes); a
+// fragment read has 16 consecutive 64-byte rows asking for the same logical chunk, and the
+// xor with (row / 4) mod 4 puts them on 16 distinct 16-byte slots of a 256-byte window
+__device__ __forceinline__ int pp_swz(int row) { return (row >> 2) & 3; }
+
+template <bool UP>
+__global__ __launch_bounds__(PP_THREADS, 1) void grouped_gemm_pp_kernel(GemmArgs a, gemm::TileOrder to) {
+    __shared__ __attribute__((aligned(1024))) uint16_t As[PP_STAGES][BM * PP_BK];
+    __shared__ __attribute__((aligned(1024))) uint16_t Bs[PP_STAGES][BN * PP_BK];
+    __shared__ int32_t tile_prefix[gemm::kMaxSlots + 1];
+    __shared__ int32_t part[PP_THREADS];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = wv >> 2;       // group
+    const int sq = wv & 3;       // SIMD and 128 x 128 region
+    const int wm = sq >> 1, wn = sq & 1;
+
+    const int32_t total_mt =
+        gemm::number_tiles<BM, PP_THREADS>(a.counts, a.seg, a.cap, a.El, tile_prefix, part);
+    const uint32_t row_bytes = static_cast<uint32_t>(a.K) * 2u;
+    const int nsn = a.NT / to.SN;
+    const int64_t total_super = static_cast<int64_t>((total_mt + to.SM - 1) / to.SM) * nsn;
+    const int xcd = blockIdx.x & 7;
+    const int q = blockIdx.x >> 3;
+    const int dma_row = lane / PP_CPR;
+    const int frow = lane & 31;
+    // fragment of MFMA step ks (16 deep) of a slice: row frow of a 32-row block, logical
+    // chunk 2 ks + lane / 32
+    int fchunk[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) fchunk[ks] = ((2 * ks + (lane >> 5)) ^ pp_swz(frow)) * 8;
+    // LDS rows of the wave's two weight column blocks
+    int brow[2];
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+        const int j = UP ? g + 2 * jj : 2 * g + jj;
+        brow[jj] = UP ? (j >> 1) * UP_COLS + wn * 64 + (j & 1) * 32 : wn * 128 + j * 32;
+    }
+
+    for (int64_t sup = xcd; sup < total_super; sup += 8) {
+        const int32_t em = static_cast<int32_t>(sup / nsn) * to.SM + q / to.SN;
+        const int32_t nt = static_cast<int32_t>(sup % nsn) * to.SN + q % to.SN;
+        if (em >= total_mt) continue;
+        const int e = gemm::slot_of_tile(tile_prefix, a.El, em);
+        const int32_t mtile = __builtin_amdgcn_readfirstlane(em - tile_prefix[e]);
+        const int64_t seg_start = a.seg[e];
+        int64_t seg_end = seg_start + a.counts[e];
+        seg_end = seg_end < a.cap ? seg_end : a.cap;
+        const int64_t row0 = seg_start + static_cast<int64_t>(mtile) * BM;
+        const int64_t nrows64 = seg_end - row0;
+        const uint32_t nrows = static_cast<uint32_t>(nrows64 < BM ? nrows64 : BM);
+
+        // group 0 streams A, group 1 streams B; wave sq of a group covers tile rows
+        // 64 sq .. 64 sq + 63 in 4 DMA blocks of 16 rows
+        const bool loads_a = g == 0;
+        const uint16_t* dbase;
+        uint32_t dbytes;
+        if (loads_a) {
+            // rows past the segment end fall outside the resource: they read as zeros
+            dbase = a.A + row0 * a.K;
+            dbytes = nrows * row_bytes;
+        } else if (UP) {
+            dbase = a.B + static_cast<int64_t>(e) * 2 * a.N * a.K;
+            dbytes = static_cast<uint32_t>(2 * a.N) * row_bytes;
+        } else {
+            dbase = a.B + static_cast<int64_t>(e) * a.N * a.K;
+            dbytes = static_cast<uint32_t>(a.N) * row_bytes;
+        }
+        const __amdgpu_buffer_rsrc_t rsrc = gemm::make_rsrc_uniform(dbase, dbytes);
+        // DMA p covers tile row r = 64 sq + 16 p + dma_row, global row that of p = 0 plus 16 p
+        // (up: a wave's 64 rows lie all in the gate half or all in the up half); the swizzle
+        // (r / 4) mod 4 is the same for every p
+        const int r0 = 64 * sq + dma_row;
+        uint32_t grow;
+        if (loads_a) grow = static_cast<uint32_t>(r0);
+        else if (UP) grow = static_cast<uint32_t>((r0 >= 128 ? a.N : 0) + nt * UP_COLS + (r0 & 127));
+        else grow = static_cast<uint32_t>(nt * BN + r0);
+        const uint32_t vbase = grow * row_bytes + static_cast<uint32_t>(((lane % PP_CPR) ^ pp_swz(r0)) * 16);
+        const uint32_t rstep = static_cast<uint32_t>(PP_RPB) * row_bytes;
+        auto issue = [&](int stage, int64_t kt) {
+            int off = stage * (BM * PP_BK) + sq * PP_LPW * 512;
+            uint32_t vb = vbase;
+            asm volatile("" : "+s"(off), "+v"(vb));
+            uint16_t* base = (loads_a ? &As[0][0] : &Bs[0][0]) + off;
+            const int soff = static_cast<int>(kt * PP_BK * 2);
+#pragma unroll
+            for (int p = 0; p < PP_LPW; ++p)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (gemm::lds_void_t*)(base + p * 512), 16,
+                                                        vb + static_cast<uint32_t>(p) * rstep, soff, 0, 0);
+        };
+
+        floatx16_t acc[4][2];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[i][jj][v] = 0.f;
+        const uint16_t* a_rd = &As[0][0] + (wm * 128 + frow) * PP_BK;
+        const uint16_t* b_rd = &Bs[0][0] + frow * PP_BK;
+        bf16x8_t fa[2][4], fb[2][2];
+        // fragments of the slice in `stage`: two 16-deep MFMA steps
+        auto read_slice = [&](int stage) {
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    fa[ks][i] = *reinterpret_cast<const bf16x8_t*>(a_rd + stage * (BM * PP_BK) + i * 32 * PP_BK +
+                                                                   fchunk[ks]);
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj)
+                    fb[ks][jj] = *reinterpret_cast<const bf16x8_t*>(b_rd + stage * (BN * PP_BK) + brow[jj] * PP_BK +
+                                                                    fchunk[ks]);
+            }
+        };
+        auto mfma_slice = [&]() {
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int jj = 0; jj < 2; ++jj)
+                        acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks][jj], fa[ks][i], acc[i][jj], 0,
+                                                                              0, 0);
+        };
+        // a barrier that neither the compiler nor the scheduler moves work across
+        auto phase_end = [&]() {
+            __builtin_amdgcn_sched_barrier(0);
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+        };
+
+        const int64_t KT = a.K / PP_BK;
+        // the previous tile's output stores are done; every wave passed the previous tile's
+        // last barrier, so no wave still reads a stage
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        issue(0, 0);
+        issue(1, KT > 1 ? 1 : KT - 1);
+        issue(2, KT > 2 ? 2 : KT - 1);
+        // slice 0 landed: each wave's two newest groups may still be in flight
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * PP_LPW) : "memory");
+        phase_end();
+        if (g == 1) phase_end();
+        for (int64_t n = 0; n < KT; ++n) {
+            const int st = static_cast<int>(n & (PP_STAGES - 1));
+            // memory phase: this slice's fragments, the DMAs of slice n + 3
+            read_slice(st);
+            issue((st + 3) & (PP_STAGES - 1), n + 3 < KT ? n + 3 : KT - 1);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            // group 1: slice n + 1 landed before the barrier that ends phase 2n
+            if (g == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * PP_LPW) : "memory");
+            phase_end();
+            // compute phase
+            mfma_slice();
+            if (g == 0) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * PP_LPW) : "memory");
+            phase_end();
+        }
+        if (g == 0) phase_end();
+
+        // ---- epilogue, as in grouped_gemm_bf16_kernel, over the wave's two column blocks
+        const int rloc = wm * 128 + (lane & 31);
+        const int64_t colbase = UP ? static_cast<int64_t>(nt) * UP_COLS + wn * 64 + (lane >> 5) * 4
+                                   : static_cast<int64_t>(nt) * BN + wn * 128 + (lane >> 5) * 4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (rloc + i * 32 >= static_cast<int>(nrows)) continue;
+            uint16_t* cp = a.C + (row0 + rloc + i * 32) * a.N + colbase;
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+                if (UP) {
+                    float h[4];
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) h[t] = silu_mul(acc[i][0][4 * qq + t], acc[i][1][4 * qq + t]);
+                    *reinterpret_cast<uint2*>(cp + g * 32 + qq * 8) =
+                        make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
+                } else {
+#pragma unroll
+                    for (int jj = 0; jj < 2; ++jj) {
+                        const floatx16_t& c = acc[i][jj];
+                        *reinterpret_cast<uint2*>(cp + (2 * g + jj) * 32 + qq * 8) =
+                            make_uint2(pack_bf16x2(c[4 * qq], c[4 * qq + 1]), pack_bf16x2(c[4 * qq + 2], c[4 * qq + 3]));
+                    }
+                }
+            }
+        }
+    }
+    // no DMA into LDS may outlive the workgroup
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 // ------------------------------------------------------------------ simple path
 // One thread per output element; used for fp32 activations and for shapes the MFMA tiles
 // do not cover.  Rows are looked up in seg_offsets by binary search.
@@ -606,8 +834,8 @@ moe_status run_stage(bool up, const void* A, moe_dtype act_dt, const moe_plan* p
             if (up) hipLaunchKernelGGL((grouped_gemm_bf16_kernel<true, true>), grid, dim3(M_THREADS), 0, stream, g, to);
             else hipLaunchKernelGGL((grouped_gemm_bf16_kernel<false, true>), grid, dim3(M_THREADS), 0, stream, g, to);
         } else {
-            if (up) hipLaunchKernelGGL((grouped_gemm_bf16_kernel<true, false>), grid, dim3(M_THREADS), 0, stream, g, to);
-            else hipLaunchKernelGGL((grouped_gemm_bf16_kernel<false, false>), grid, dim3(M_THREADS), 0, stream, g, to);
+            if (up) hipLaunchKernelGGL((grouped_gemm_pp_kernel<true>), grid, dim3(PP_THREADS), 0, stream, g, to);
+            else hipLaunchKernelGGL((grouped_gemm_pp_kernel<false>), grid, dim3(PP_THREADS), 0, stream, g, to);
         }
         MOE_LAUNCH_CHECK();
         return MOE_OK;

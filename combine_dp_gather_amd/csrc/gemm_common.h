@@ -42,17 +42,19 @@ struct TileOrder {
 };
 
 // Slot e owns ceil(min(counts[e], cap - seg[e]) / BM) m-tiles; tile_prefix[e] = m-tiles
-// before slot e, tile_prefix[El] = total.  Called by all kThreads threads; ends synced.
-template <int BM>
+// before slot e, tile_prefix[El] = total.  Called by all NTHR threads of the block (part
+// holds NTHR ints); ends synced.
+template <int BM, int NTHR = kThreads>
 __device__ __forceinline__ int32_t number_tiles(const int32_t* counts, const int64_t* seg,
                                                 int64_t cap, int El, int32_t* tile_prefix,
                                                 int32_t* part) {
+    static_assert(kMaxSlots % NTHR == 0, "whole slots per thread");
     const int tid = threadIdx.x;
-    int32_t loc[kMaxSlots / kThreads];
+    int32_t loc[kMaxSlots / NTHR];
     int32_t s = 0;
 #pragma unroll
-    for (int q = 0; q < kMaxSlots / kThreads; ++q) {
-        const int e = tid * (kMaxSlots / kThreads) + q;
+    for (int q = 0; q < kMaxSlots / NTHR; ++q) {
+        const int e = tid * (kMaxSlots / NTHR) + q;
         int32_t mt = 0;
         if (e < El) {
             int64_t c = counts[e];
@@ -65,7 +67,7 @@ __device__ __forceinline__ int32_t number_tiles(const int32_t* counts, const int
     }
     part[tid] = s;
     __syncthreads();
-    for (int off = 1; off < kThreads; off <<= 1) {
+    for (int off = 1; off < NTHR; off <<= 1) {
         const int32_t v = tid >= off ? part[tid - off] : 0;
         __syncthreads();
         part[tid] += v;
@@ -73,12 +75,12 @@ __device__ __forceinline__ int32_t number_tiles(const int32_t* counts, const int
     }
     int32_t run = part[tid] - s;
 #pragma unroll
-    for (int q = 0; q < kMaxSlots / kThreads; ++q) {
-        const int e = tid * (kMaxSlots / kThreads) + q;
+    for (int q = 0; q < kMaxSlots / NTHR; ++q) {
+        const int e = tid * (kMaxSlots / NTHR) + q;
         if (e < El) tile_prefix[e] = run;
         run += loc[q];
     }
-    if (tid == kThreads - 1) tile_prefix[El] = part[tid];
+    if (tid == NTHR - 1) tile_prefix[El] = part[tid];
     __syncthreads();
     return tile_prefix[El];
 }
