@@ -504,7 +504,7 @@ def main():
     kname = ("grouped_gemm_fp8_kernel" if fmt == "fp8"
              else "grouped_gemm_bf16_kernel<true, true>" if bf and fp8w
              else "grouped_gemm_pp_kernel<true>" if bf
-             else "simple_gemm_kernel<float, true>")
+             else "generic_gemm_kernel<float, true>")
     roof["kernel"] = kname + (" (gate+up SwiGLU" + (", with its activation quantisation" if fmt == "fp8" else "")
                               + ")")
     from combine_dp_gather_amd.profiling import read_traffic_summary

@@ -22,7 +22,7 @@ __all__ = [
     "moe_gather_layout", "moe_gather", "moe_entry_gather", "moe_scatter", "moe_expert_load",
     "moe_physical_to_logical_count", "moe_eplb_balancedness", "moe_eplb_rebalance",
     "moe_eplb_logical_to_physical", "moe_route", "moe_route_from_logits",
-    "moe_dispatch", "moe_dispatch_noalloc", "moe_dispatch_workspace_size", "moe_quant_act_fp8", "moe_expert_gemm", "moe_expert_gemm_up",
+    "moe_dispatch", "moe_dispatch_noalloc", "moe_dispatch_workspace_size", "moe_quant_act_fp8", "moe_expert_gemm_fast_path", "moe_expert_gemm", "moe_expert_gemm_up",
     "moe_expert_gemm_down", "moe_expert_gemm_workspace_size", "moe_combine", "moe_version",
     "PlanBuffers", "make_route_cfg", "make_expert_map", "make_expert_weights", "MoEError",
     "GatherLayout", "RouteCfg", "ExpertMap", "ExpertWeights", "Plan",
@@ -265,6 +265,13 @@ def moe_dispatch_noalloc(global_x: torch.Tensor, topk_ids: torch.Tensor, emap: E
 
 
 # ------------------------------------------------------------------ experts
+
+def moe_expert_gemm_fast_path(x_perm: torch.Tensor, w: ExpertWeights, H: int, I: int, h: torch.Tensor,
+                              y_perm: torch.Tensor) -> bool:
+    """True when both GEMM halves run the bf16 tile kernels on these buffers."""
+    return bool(lib().moe_expert_gemm_fast_path(_ptr(x_perm), _dtype_code(x_perm), ctypes.byref(w), H, I,
+                                                 _ptr(h), _ptr(y_perm)))
+
 
 def moe_quant_act_fp8(act: torch.Tensor, num_rows: torch.Tensor, q: torch.Tensor, s_t: torch.Tensor,
                       stream=None) -> None:

@@ -68,6 +68,7 @@ SIGNATURES = {
                              ctypes.POINTER(Plan), c_vp, c_vp, c_sz, c_vp]),
     "moe_dispatch_noalloc": (c_i32, [c_vp, c_vp, c_i64, c_i32, c_i64, c_i32, ctypes.POINTER(ExpertMap),
                                      ctypes.POINTER(Plan), c_vp, c_vp]),
+    "moe_expert_gemm_fast_path": (c_i32, [c_vp, c_i32, ctypes.POINTER(ExpertWeights), c_i64, c_i64, c_vp, c_vp]),
     "moe_quant_act_fp8": (c_i32, [c_vp, c_vp, c_i64, c_i64, c_vp, c_vp, c_vp]),
     "moe_expert_gemm_workspace_size": (c_sz, [c_i64, c_i64, c_i64, c_i32, c_i32]),
     "moe_expert_gemm": (c_i32, [c_vp, c_i32, ctypes.POINTER(Plan), ctypes.POINTER(ExpertWeights),

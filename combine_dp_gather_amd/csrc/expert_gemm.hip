@@ -705,70 +705,86 @@ __global__ __launch_bounds__(PP_THREADS, 1) void grouped_gemm_pp_kernel(GemmArgs
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-// ------------------------------------------------------------------ simple path
-// One thread per output element; used for fp32 activations and for shapes the MFMA tiles
-// do not cover.  Rows are looked up in seg_offsets by binary search.
-struct SimpleArgs {
-    const void* A;
-    const void* B;
-    void* C;
-    const int32_t* counts;
-    const int64_t* seg;
-    const int64_t* num_rows;
-    int64_t cap, K, N;
-    int32_t El;
-};
+// ------------------------------------------------------------------ generic path
+// Any shape, alignment or activation dtype (fp32 activations, bf16 buffers off 16 bytes, H
+// not a multiple of 256, I not a multiple of 128): 64-row x 64-column tiles on the fp32
+// matrix cores (v_mfma_f32_32x32x2f32), operands widened exactly to fp32 and staged through
+// LDS in 32-deep K slices by element loads (zeros past a segment's rows, past K or past N).
+// A block of 4 waves owns one tile at a time (wave (wm, wn): 32 rows x 32 columns; up: the
+// gate and the up accumulators of the same 32 i-columns) and walks the tiles grid-stride.
+// The fp32 matrix-core peak is a sixteenth of bf16's, so these shapes run well below the
+// bf16 tile kernels; moe_expert_gemm_fast_path tells a caller which path a call takes.
+constexpr int GN_BM = 64, GN_BN = 64, GN_BK = 32;
+constexpr int GN_LD = GN_BK + 1;  // odd stride: a column of reads falls on distinct banks
 
 template <typename T>
-__device__ __forceinline__ float ld(const T* p, int64_t i) {
+__device__ __forceinline__ float gn_ld(const T* p, int64_t i) {
     if constexpr (sizeof(T) == 2) return bf16_to_f32(p[i]);
     else return p[i];
 }
-template <typename T>
-__device__ __forceinline__ void st(T* p, int64_t i, float v) {
-    if constexpr (sizeof(T) == 2) p[i] = f32_to_bf16(v);
-    else p[i] = v;
-}
-
-__device__ __forceinline__ int find_slot(const int64_t* seg, int El, int64_t row) {
-    int lo = 0, hi = El;
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (seg[mid] <= row) lo = mid;
-        else hi = mid;
-    }
-    return lo;
-}
 
 template <typename T, bool UP>
-__global__ __launch_bounds__(256) void simple_gemm_kernel(SimpleArgs a) {
-    int64_t rows = *a.num_rows;
-    rows = rows < a.cap ? rows : a.cap;
-    const int64_t total = rows * a.N;
-    const T* A = static_cast<const T*>(a.A);
-    const T* B = static_cast<const T*>(a.B);
-    T* C = static_cast<T*>(a.C);
-    for (int64_t o = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; o < total;
-         o += static_cast<int64_t>(gridDim.x) * 256) {
-        const int64_t row = o / a.N, col = o % a.N;
-        const int e = find_slot(a.seg, a.El, row);
-        if (row >= a.seg[e] + a.counts[e]) continue;  // alignment pad row
-        const T* x = A + row * a.K;
-        if (UP) {
-            const T* wg = B + ((static_cast<int64_t>(e) * 2 + 0) * a.N + col) * a.K;
-            const T* wu = B + ((static_cast<int64_t>(e) * 2 + 1) * a.N + col) * a.K;
-            float g = 0.f, u = 0.f;
-            for (int64_t k = 0; k < a.K; ++k) {
-                const float xv = ld(x, k);
-                g = __builtin_fmaf(xv, ld(wg, k), g);
-                u = __builtin_fmaf(xv, ld(wu, k), u);
+__global__ __launch_bounds__(256) void generic_gemm_kernel(GemmArgs a, const void* Av, const void* Bv, void* Cv) {
+    __shared__ float As[GN_BM * GN_LD];
+    __shared__ float Bs[(UP ? 2 : 1) * GN_BN * GN_LD];
+    __shared__ int32_t tile_prefix[gemm::kMaxSlots + 1];
+    __shared__ int32_t part[gemm::kThreads];
+    const T* A = static_cast<const T*>(Av);
+    const T* B = static_cast<const T*>(Bv);
+    T* C = static_cast<T*>(Cv);
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int wm = wv >> 1, wn = wv & 1;
+    const int32_t total_mt = gemm::number_tiles<GN_BM>(a.counts, a.seg, a.cap, a.El, tile_prefix, part);
+    const int64_t NT = ceil_div(a.N, GN_BN);
+    const int64_t tiles = static_cast<int64_t>(total_mt) * NT;
+    for (int64_t t = blockIdx.x; t < tiles; t += gridDim.x) {
+        const int32_t em = static_cast<int32_t>(t / NT);
+        const int64_t n0 = (t % NT) * GN_BN;
+        const int e = gemm::slot_of_tile(tile_prefix, a.El, em);
+        const int64_t seg_start = a.seg[e];
+        int64_t seg_end = seg_start + a.counts[e];
+        seg_end = seg_end < a.cap ? seg_end : a.cap;
+        const int64_t row0 = seg_start + static_cast<int64_t>(em - tile_prefix[e]) * GN_BM;
+        const int64_t nrows = seg_end - row0 < GN_BM ? seg_end - row0 : GN_BM;
+        // weight rows of slot e: up -> gate rows [0, N) then up rows [N, 2N); down -> [0, N)
+        const T* Bw = B + static_cast<int64_t>(e) * (UP ? 2 : 1) * a.N * a.K;
+        floatx16_t acc[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[u][v] = 0.f;
+        for (int64_t k0 = 0; k0 < a.K; k0 += GN_BK) {
+            __syncthreads();  // the previous slice's reads are done
+            for (int idx = tid; idx < GN_BM * GN_BK; idx += 256) {
+                const int r = idx / GN_BK, c = idx % GN_BK;
+                As[r * GN_LD + c] = (r < nrows && k0 + c < a.K) ? gn_ld(A, (row0 + r) * a.K + k0 + c) : 0.f;
             }
-            st(C, row * a.N + col, g / (1.0f + expf(-g)) * u);
-        } else {
-            const T* wd = B + (static_cast<int64_t>(e) * a.N + col) * a.K;
-            float y = 0.f;
-            for (int64_t k = 0; k < a.K; ++k) y = __builtin_fmaf(ld(x, k), ld(wd, k), y);
-            st(C, row * a.N + col, y);
+            for (int idx = tid; idx < (UP ? 2 : 1) * GN_BN * GN_BK; idx += 256) {
+                const int r = idx / GN_BK, c = idx % GN_BK;
+                const int half = r / GN_BN, col = r % GN_BN;
+                const bool in = n0 + col < a.N && k0 + c < a.K;
+                Bs[r * GN_LD + c] = in ? gn_ld(Bw, (half * a.N + n0 + col) * a.K + k0 + c) : 0.f;
+            }
+            __syncthreads();
+            const float* ar = As + (wm * 32 + (lane & 31)) * GN_LD + (lane >> 5);
+            const float* br = Bs + (wn * 32 + (lane & 31)) * GN_LD + (lane >> 5);
+#pragma unroll
+            for (int kk = 0; kk < GN_BK; kk += 2) {
+                const float av = ar[kk];
+                acc[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, br[kk], acc[0], 0, 0, 0);
+                if (UP) acc[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, br[GN_BN * GN_LD + kk], acc[1], 0, 0, 0);
+            }
+        }
+        // lane l, register v: row 8 (v / 4) + 4 (l / 32) + v % 4, column l % 32 of the wave's block
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int64_t r = wm * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+            const int64_t c = n0 + wn * 32 + (lane & 31);
+            if (r < nrows && c < a.N) {
+                const float o = UP ? silu_mul(acc[0][v], acc[1][v]) : acc[0][v];
+                if constexpr (sizeof(T) == 2) C[(row0 + r) * a.N + c] = f32_to_bf16(o);
+                else C[(row0 + r) * a.N + c] = o;
+            }
         }
     }
 }
@@ -840,17 +856,20 @@ moe_status run_stage(bool up, const void* A, moe_dtype act_dt, const moe_plan* p
         MOE_LAUNCH_CHECK();
         return MOE_OK;
     }
-    SimpleArgs s{A, B, C, plan->counts, plan->seg_offsets, plan->num_rows, plan->cap, K, N,
-                 plan->num_slots};
-    int64_t blocks = ceil_div(plan->cap * N, 256);
-    if (blocks > 65536) blocks = 65536;
-    const dim3 grid(static_cast<unsigned>(blocks));
+    GemmArgs g{};
+    g.counts = plan->counts;
+    g.seg = plan->seg_offsets;
+    g.cap = plan->cap;
+    g.K = K;
+    g.N = N;
+    g.El = plan->num_slots;
+    const dim3 grid(static_cast<unsigned>(gemm::num_cus() * 4));
     if (act_dt == MOE_BF16) {
-        if (up) hipLaunchKernelGGL((simple_gemm_kernel<uint16_t, true>), grid, dim3(256), 0, stream, s);
-        else hipLaunchKernelGGL((simple_gemm_kernel<uint16_t, false>), grid, dim3(256), 0, stream, s);
+        if (up) hipLaunchKernelGGL((generic_gemm_kernel<uint16_t, true>), grid, dim3(256), 0, stream, g, A, B, C);
+        else hipLaunchKernelGGL((generic_gemm_kernel<uint16_t, false>), grid, dim3(256), 0, stream, g, A, B, C);
     } else {
-        if (up) hipLaunchKernelGGL((simple_gemm_kernel<float, true>), grid, dim3(256), 0, stream, s);
-        else hipLaunchKernelGGL((simple_gemm_kernel<float, false>), grid, dim3(256), 0, stream, s);
+        if (up) hipLaunchKernelGGL((generic_gemm_kernel<float, true>), grid, dim3(256), 0, stream, g, A, B, C);
+        else hipLaunchKernelGGL((generic_gemm_kernel<float, false>), grid, dim3(256), 0, stream, g, A, B, C);
     }
     MOE_LAUNCH_CHECK();
     return MOE_OK;
@@ -872,6 +891,12 @@ extern "C" size_t moe_expert_gemm_workspace_size(int64_t cap, int64_t H, int64_t
         n += a > b ? a : b;
     }
     return n;
+}
+
+extern "C" int32_t moe_expert_gemm_fast_path(const void* x_perm, moe_dtype act_dt, const moe_expert_weights* w,
+                                             int64_t H, int64_t I, const void* h, const void* y_perm) {
+    if (!w || H <= 0 || I <= 0) return 0;
+    return moe::mfma_ok(act_dt, H, I, x_perm, w->w13, h) && moe::mfma_ok(act_dt, H, I, h, w->w2, y_perm) ? 1 : 0;
 }
 
 extern "C" moe_status moe_expert_gemm_up(const void* x_perm, moe_dtype act_dt, const moe_plan* plan,

@@ -339,14 +339,23 @@ size_t moe_expert_gemm_workspace_size(int64_t cap, int64_t H, int64_t I, moe_dty
  *             rows >= num_rows are not written
  *   workspace device, >= moe_expert_gemm_workspace_size(...) bytes, 256-byte aligned
  * Accumulation is fp32; h and y are rounded to act_dt (nearest even).
- * bf16 / fp8 need H % 256 == 0 and I % 128 == 0, else MOE_ERR_UNSUPPORTED.
- * The matrix-core kernels also need x_perm, h and the weights 16-byte aligned and each
- * GEMM's output (h, y_perm) 8-byte aligned.  Otherwise bf16 weights run a slow per-element
- * kernel; fp8 weights return MOE_ERR_UNSUPPORTED with bf16 activations and
- * MOE_ERR_INVALID_ARG for misaligned inputs with e4m3 activations. */
+ * The bf16 tile kernels (bf16 matrix cores) need bf16 activations, H % 256 == 0,
+ * I % 128 == 0, x_perm, h and the weights 16-byte aligned and each GEMM's output (h, y_perm)
+ * 8-byte aligned.  Anything else with bf16 or fp32 weights runs a generic tiled kernel on the
+ * fp32 matrix cores (any shape and alignment, at the fp32 matrix-core rate);
+ * moe_expert_gemm_fast_path tells which one a call takes.  fp8 weights have no generic form:
+ * they return MOE_ERR_UNSUPPORTED with bf16 activations and MOE_ERR_INVALID_ARG for
+ * misaligned inputs with e4m3 activations. */
 moe_status moe_expert_gemm(const void* x_perm, moe_dtype act_dt, const moe_plan* plan,
                            const moe_expert_weights* w, int64_t H, int64_t I, void* y_perm,
                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* moe_expert_gemm_fast_path -- 1 if moe_expert_gemm on these buffers runs the tile kernels
+ * in both halves, 0 if either half runs the generic kernel (see moe_expert_gemm).  h is the
+ * buffer between the halves: the caller's for moe_expert_gemm_up / _down, the workspace for
+ * moe_expert_gemm.  Reads no device memory. */
+int32_t moe_expert_gemm_fast_path(const void* x_perm, moe_dtype act_dt, const moe_expert_weights* w,
+                                  int64_t H, int64_t I, const void* h, const void* y_perm);
 
 /* The two halves of moe_expert_gemm, for callers that time or overlap them separately.
  *   _up:   x_perm -> h      (h: device [cap, I] act_dt, caller memory)

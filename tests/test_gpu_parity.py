@@ -178,11 +178,11 @@ def test_multi_tile_ragged_segments():
     run_and_compare(cfg)
 
 
-def test_expert_gemm_unaligned_buffers_take_element_path():
+def test_expert_gemm_unaligned_buffers_take_generic_path():
     # an output 2 bytes off an 8-byte boundary cannot take the tile epilogue's 8-byte stores,
-    # nor an input off 16 bytes its DMAs: the bf16 GEMMs then run the per-element kernel,
-    # held to the same bar against the oracle
-    from combine_dp_gather_amd import moe_expert_gemm_down, moe_expert_gemm_up
+    # nor an input off 16 bytes its DMAs: the bf16 GEMMs then run the generic kernel on the
+    # fp32 matrix cores, held to the same bar against the oracle, and the query says so
+    from combine_dp_gather_amd import moe_expert_gemm_down, moe_expert_gemm_fast_path, moe_expert_gemm_up
     cfg = resized("cfg4", (300, 0, 517), hidden=2048, inter=1024, num_experts=64)
     layer, ref = run_and_compare(cfg)
     rp = ref["plan"]
@@ -198,7 +198,10 @@ def test_expert_gemm_unaligned_buffers_take_element_path():
     ybuf = torch.zeros(layer.y_perm.numel() + 1, dtype=layer.y_perm.dtype, device=layer.y_perm.device)
     y_odd = ybuf[1:].view(layer.y_perm.shape)
     layer.experts_up()  # h from the tile path
-    say("[parity] element-path GEMMs: h and y_perm 2 bytes off alignment")
+    assert moe_expert_gemm_fast_path(layer.x_perm, layer.w.ew, H, I, layer.h, layer.y_perm)
+    assert not moe_expert_gemm_fast_path(layer.x_perm, layer.w.ew, H, I, h_odd, layer.y_perm)
+    assert not moe_expert_gemm_fast_path(layer.x_perm, layer.w.ew, H, I, layer.h, y_odd)
+    say("[parity] generic-path GEMMs: h and y_perm 2 bytes off alignment")
     moe_expert_gemm_up(layer.x_perm, layer.plan, layer.w.ew, H, I, h_odd, layer.gemm_ws)
     moe_expert_gemm_down(h_odd, layer.plan, layer.w.ew, H, I, y_odd, layer.gemm_ws)
     torch.cuda.synchronize()
