@@ -42,7 +42,16 @@
 extern "C" {
 #endif
 
-typedef enum {
+/* Every enum of this interface is 32 bits wide.  C++ translation units give the enums that
+ * width as a fixed base type, so every int32 a C caller passes is a value of the type and the
+ * library's range checks on it are well defined. */
+#ifdef __cplusplus
+#define MOE_ENUM_BASE : int32_t
+#else
+#define MOE_ENUM_BASE
+#endif
+
+typedef enum MOE_ENUM_BASE {
     MOE_OK = 0,
     MOE_ERR_INVALID_ARG = 1,  /* a pointer, size or enum value is out of range; nothing enqueued */
     MOE_ERR_UNSUPPORTED = 2,  /* a valid combination this build does not implement */
@@ -52,11 +61,11 @@ typedef enum {
                                  fixed scratch holds; nothing enqueued */
 } moe_status;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
+typedef enum MOE_ENUM_BASE { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
 
 /* DpPaddingMode of the SGLang page, section "DpPaddingMode：补齐到最长还是补齐到总和":
  * MAX_LEN pads every replica to the longest one, SUM_LEN concatenates the replicas. */
-typedef enum { MOE_PAD_AUTO = 0, MOE_PAD_MAX_LEN = 1, MOE_PAD_SUM_LEN = 2 } moe_pad_mode;
+typedef enum MOE_ENUM_BASE { MOE_PAD_AUTO = 0, MOE_PAD_MAX_LEN = 1, MOE_PAD_SUM_LEN = 2 } moe_pad_mode;
 
 #define MOE_MAX_REPLICAS 256
 
@@ -154,14 +163,14 @@ moe_status moe_scatter(const moe_gather_layout_t* L, const void* out, int64_t H,
  * Routing (op_gate + op_select_experts of the SGLang page, section "operations 与 yield";
  * TopKOutput of section "normal dispatch 的调用链").
  * ---------------------------------------------------------------------------------------- */
-typedef enum { MOE_ROUTE_SOFTMAX = 0, MOE_ROUTE_GROUPED_SIGMOID = 1 } moe_route_kind;
+typedef enum MOE_ENUM_BASE { MOE_ROUTE_SOFTMAX = 0, MOE_ROUTE_GROUPED_SIGMOID = 1 } moe_route_kind;
 
 /* Gate arithmetic.  EXACT: the defined summation order below, so logits and ids are the same
  * bits on every run, every rank and the reference.  FAST: bf16 matrix-core products with fp32
  * accumulation in tile order -- the same products, summed in another order, so logits differ
  * in the last bits and an id can differ only where two keys are that close (a near tie).
  * FAST reads x once from HBM and takes bf16 inputs only. */
-typedef enum { MOE_GATE_EXACT = 0, MOE_GATE_FAST = 1 } moe_gate_mode;
+typedef enum MOE_ENUM_BASE { MOE_GATE_EXACT = 0, MOE_GATE_FAST = 1 } moe_gate_mode;
 
 typedef struct {
     int32_t kind;          /* moe_route_kind */
@@ -299,7 +308,7 @@ moe_status moe_dispatch_noalloc(const void* global_x, const int32_t* topk_ids, i
  *                     the per-token-group quantisation of the SGLang page, section "prefll 侧的
  *                     一个必要步骤：per-token-group 量化"), fp8 matrix cores, and each 128-deep K
  *                     group's partial sum is promoted by (activation scale * weight scale). */
-typedef enum { MOE_FP8_ACT_BF16 = 0, MOE_FP8_ACT_E4M3 = 1 } moe_fp8_act;
+typedef enum MOE_ENUM_BASE { MOE_FP8_ACT_BF16 = 0, MOE_FP8_ACT_E4M3 = 1 } moe_fp8_act;
 
 typedef struct {
     int32_t dtype;          /* MOE_F32, MOE_BF16 (same as activations) or MOE_FP8_E4M3 */
@@ -378,6 +387,10 @@ moe_status moe_expert_gemm_down(const void* h, moe_dtype act_dt, const moe_plan*
  * form: each output row is written by one owner, with no atomics, so results are
  * deterministic.
  *   y_perm device [cap, H] dt; topk_w device fp32[G, k]; out device [G, H] dt
+ * Rows move as 16-byte vectors (one block per row) when H is a whole number of 16-byte
+ * vectors and y_perm and out are 16-byte aligned.  Otherwise the same sums run element by
+ * element (one wave per row, each wave's accesses still contiguous), with 2- or 4-byte
+ * accesses instead of 16-byte ones; the result is the same either way.
  * ---------------------------------------------------------------------------------------- */
 moe_status moe_combine(const void* y_perm, moe_dtype dt, const moe_plan* plan,
                        const float* topk_w, float routed_scale, int64_t H, void* out,
