@@ -335,6 +335,9 @@ def main():
         step()
     torch.cuda.synchronize()
     R = int(layer.plan.counts.sum().item())
+    # only the slots that received rows have their weights read; an empty slot's weights
+    # are not part of the GEMMs' algorithmic bytes
+    E_active = int((layer.plan.counts > 0).sum().item())
     overflow = int(layer.plan.error_flag.item())
     log(f"[bench] warmup done; routed local pairs R={R} overflow={overflow}")
 
@@ -448,8 +451,8 @@ def main():
         "route": ("mfma32", 2.0 * G * E * H),                          # exact fp32 fma chain + select
         "dispatch": ("hbm", 2 * R * H * es + 3 * 4 * G * k + 8 * R),  # x_perm copy + id passes
         "gemm_up": gemm_work(mm, 4.0 * R * H * I,                     # gate+up: 2*R*H*2I
-                             E_slots * 2 * I * H * wb + R * H * es + R * I * es),
-        "gemm_down": gemm_work(mm, 2.0 * R * I * H, E_slots * H * I * wb + R * I * es + R * H * es),
+                             E_active * 2 * I * H * wb + R * H * es + R * I * es),
+        "gemm_down": gemm_work(mm, 2.0 * R * I * H, E_active * H * I * wb + R * I * es + R * H * es),
         "combine": ("hbm", R * H * es + G * H * es + 8 * G * k),      # read R rows, write G rows
         "scatter": ("hbm", 2 * T * H * es),
         # read R rows, write the T real rows straight to the replicas
@@ -511,7 +514,7 @@ def main():
     summary = os.path.join(ROOT, "profiles", f"grouped_gemm_{fmt}_up__{PROFILE_WORKLOAD[args.workload]}__traffic.txt")
     tb = read_traffic_summary(summary, GEMM_SOURCES[fmt])
     roof["traffic"] = round(tb) if tb is not None else None
-    roof["algorithmic_bytes"] = R * H * es + E_slots * 2 * I * H * (1 if fp8w else es) + R * I * es
+    roof["algorithmic_bytes"] = R * H * es + E_active * 2 * I * H * (1 if fp8w else es) + R * I * es
     result = {
         "metric": "MoE-layer tokens/s at 1 GPU; grouped-GEMM % peak MFMA; dispatch/combine % HBM",
         "value": round(T * args.steps / (total_ms / 1e3), 2),
@@ -537,7 +540,7 @@ def main():
                    "dispatch_layout": (f"fixed capacity, {args.seg_stride} rows per slot" if args.seg_stride
                                        else "packed segments"),
                    "tokens": T, "global_rows": G, "gather_mode": args.mode,
-                   "routed_local_pairs": R, "parallelism": "one EP rank's share on 1 GPU",
+                   "routed_local_pairs": R, "slots_with_rows": E_active, "parallelism": "one EP rank's share on 1 GPU",
                    **({"placement": eplb_info} if eplb_info is not None else {})},
         "timing": {"cold": stats(cold), "warm": stats(warm),
                    "flush": f"{args.flush_mib} MiB written by a kernel before every cold step, outside its events"

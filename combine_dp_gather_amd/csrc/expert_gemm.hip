@@ -504,6 +504,7 @@ __global__ __launch_bounds__(M_THREADS, 1) void grouped_gemm_bf16_kernel(GemmArg
 // wave waits until only its two newest DMA groups (slices n + 2, n + 3) are in flight, so
 // slice n + 1 has landed when group 0 reads it in phase 2n + 1.  Group 1 starts one barrier
 // late and group 0 ends one barrier late, so every wave passes the same barriers.
+constexpr int ST_BM_SPLIT = 64;  // slots with more rows than this run here, the rest in the streaming kernel
 constexpr int PP_THREADS = 512;
 constexpr int PP_BK = 32;                        // K per slice
 constexpr int PP_STAGES = 4;
@@ -531,7 +532,7 @@ __global__ __launch_bounds__(PP_THREADS, 1) void grouped_gemm_pp_kernel(GemmArgs
     const int wm = sq >> 1, wn = sq & 1;
 
     const int32_t total_mt =
-        gemm::number_tiles<BM, PP_THREADS>(a.counts, a.seg, a.cap, a.El, tile_prefix, part);
+        gemm::number_tiles<BM, PP_THREADS>(a.counts, a.seg, a.cap, a.El, tile_prefix, part, ST_BM_SPLIT);
     const uint32_t row_bytes = static_cast<uint32_t>(a.K) * 2u;
     const int nsn = a.NT / to.SN;
     const int64_t total_super = static_cast<int64_t>((total_mt + to.SM - 1) / to.SM) * nsn;
@@ -705,6 +706,182 @@ __global__ __launch_bounds__(PP_THREADS, 1) void grouped_gemm_pp_kernel(GemmArgs
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
+// ------------------------------------------------------------------ bf16: weight streaming
+// Slots with at most 64 rows (decode, and the many small slots of a DP-gathered batch) are
+// bound by streaming their weights, not by the matrix cores: a 256-row tile of the ping-pong
+// kernel spends its MFMAs on padding, and its 32-deep slices fetch half a 128-byte line per
+// row and request, while a CU keeps only a bounded number of L1 -> L2 requests in flight, so
+// its rate is set by the bytes per request.  Here a tile is 64 rows x 128 weight rows (up: 64
+// gate + the same 64 up columns; down: 128 columns), so a decode batch whose routed rows sit
+// in a few slots still has a tile for every CU, in 64-deep slices (whole lines, with the
+// swizzle of grouped_gemm_bf16_kernel): five 24 KB stages, four slices in flight.  Four
+// waves, one per SIMD: wave w owns rows 32 (w mod 2) .. + 31 and column group w / 2 (up:
+// gate block and up block of 32 columns; down: two 32-column blocks).  Per slice each wave
+// DMAs two activation blocks and four weight blocks of 8 rows (all gate or all up), one
+// barrier per slice.  The MFMAs see the K values in the same order as in the ping-pong kernel
+// (four 16-deep steps per slice) and the epilogue is its epilogue, so the bits are the same.
+// The ping-pong kernel takes the slots with more than 64 rows; the two kernels number their
+// own tiles on the device, so the host never reads the counts.
+constexpr int ST_THREADS = 256;
+// cache-policy operand of the weight DMAs: non-temporal (each weight line is read once).
+// Measured on the decode shape, cold: gate+up 0.148 -> 0.082 ms against plain loads.
+constexpr int kNonTemporal = 2;
+constexpr int ST_BM = ST_BM_SPLIT;               // rows per tile = largest slot taken
+constexpr int ST_BN = 128;                       // weight rows per tile
+constexpr int ST_UPC = ST_BN / 2;                // up: i-columns per tile
+constexpr int ST_STAGES = 5;
+constexpr int ST_RPB = 64 / CPR;                 // rows per 1 KB DMA block (8)
+constexpr int ST_ADMA = ST_BM / ST_RPB / 4;      // activation DMAs per wave and slice (2)
+constexpr int ST_BDMA = ST_BN / ST_RPB / 4;      // weight DMAs per wave and slice (4)
+constexpr int ST_VPS = ST_ADMA + ST_BDMA;        // DMAs per wave and slice
+static_assert(BK == 64 && CPR == 8, "whole 128-byte lines per row and slice");
+
+template <bool UP>
+__global__ __launch_bounds__(ST_THREADS, 1) void grouped_gemm_stream_kernel(GemmArgs a) {
+    __shared__ __attribute__((aligned(1024))) uint16_t As[ST_STAGES][ST_BM * BK];
+    __shared__ __attribute__((aligned(1024))) uint16_t Bs[ST_STAGES][ST_BN * BK];
+    __shared__ int32_t tile_prefix[gemm::kMaxSlots + 1];
+    __shared__ int32_t part[ST_THREADS];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int rbk = w & 1, cg = w >> 1;  // row block, column group
+    const int32_t total_mt =
+        gemm::number_tiles<ST_BM, ST_THREADS>(a.counts, a.seg, a.cap, a.El, tile_prefix, part, 0, ST_BM);
+    const uint32_t row_bytes = static_cast<uint32_t>(a.K) * 2u;
+    const int32_t NT = static_cast<int32_t>((UP ? 2 : 1) * a.N / ST_BN);
+    const int64_t tiles = static_cast<int64_t>(total_mt) * NT;
+    const int dma_row = lane / CPR;  // 0..7
+    const int frow = lane & 31;
+    // fragment of MFMA step ks (16 deep) of a slice: row frow of a 32-row block, logical
+    // chunk 2 ks + lane / 32
+    int fchunk[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) fchunk[ks] = ((2 * ks + (lane >> 5)) ^ swz(frow)) * 8;
+    // B-tile rows of the wave's two 32-row weight blocks
+    int brow[2];
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) brow[jj] = UP ? jj * ST_UPC + cg * 32 : cg * 64 + jj * 32;
+    // activation DMA p: tile rows 16 w + 8 p + dma_row; weight DMA p: tile rows 32 w + 8 p +
+    // dma_row.  The swizzle (row / 2) mod 8 of DMA p is that of p = 0 xor 4 (p mod 2).
+    const int ra = 16 * w + dma_row, rb = 32 * w + dma_row;
+    uint32_t achunk[2], bchunk[2];
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+        achunk[par] = static_cast<uint32_t>(((lane % CPR) ^ swz(ra + 8 * par)) * 16);
+        bchunk[par] = static_cast<uint32_t>(((lane % CPR) ^ swz(rb + 8 * par)) * 16);
+    }
+    const uint32_t rstep = static_cast<uint32_t>(ST_RPB) * row_bytes;
+
+    for (int64_t t = blockIdx.x; t < tiles; t += gridDim.x) {
+        const int32_t em = static_cast<int32_t>(t / NT);
+        const int32_t nt = static_cast<int32_t>(t % NT);
+        const int e = gemm::slot_of_tile(tile_prefix, a.El, em);
+        const int32_t mtile = __builtin_amdgcn_readfirstlane(em - tile_prefix[e]);
+        const int64_t seg_start = a.seg[e];
+        int64_t seg_end = seg_start + a.counts[e];
+        seg_end = seg_end < a.cap ? seg_end : a.cap;
+        const int64_t row0 = seg_start + static_cast<int64_t>(mtile) * ST_BM;
+        const int64_t nrows64 = seg_end - row0;
+        const uint32_t nrows = static_cast<uint32_t>(nrows64 < ST_BM ? nrows64 : ST_BM);
+
+        // rows past the segment end fall outside the resource: they read as zeros
+        const __amdgpu_buffer_rsrc_t arsrc = gemm::make_rsrc_uniform(a.A + row0 * a.K, nrows * row_bytes);
+        const uint16_t* bbase = a.B + static_cast<int64_t>(e) * (UP ? 2 : 1) * a.N * a.K;
+        const __amdgpu_buffer_rsrc_t brsrc =
+            gemm::make_rsrc_uniform(bbase, static_cast<uint32_t>((UP ? 2 : 1) * a.N) * row_bytes);
+        // up: waves 0, 1 stream gate rows, waves 2, 3 up rows (N further on)
+        const uint32_t grow = UP ? static_cast<uint32_t>((rb >= ST_UPC ? a.N : 0) + nt * ST_UPC + (rb & (ST_UPC - 1)))
+                                 : static_cast<uint32_t>(nt * ST_BN + rb);
+        const uint32_t avb = static_cast<uint32_t>(ra) * row_bytes, bvb = grow * row_bytes;
+        auto issue = [&](int stage, int64_t kt) {
+            gemm::lds_void_t* adst = (gemm::lds_void_t*)(&As[0][0] + stage * (ST_BM * BK) + w * ST_ADMA * 512);
+            gemm::lds_void_t* bdst = (gemm::lds_void_t*)(&Bs[0][0] + stage * (ST_BN * BK) + w * ST_BDMA * 512);
+            uint32_t va0 = avb + achunk[0], va1 = avb + achunk[1], vb0 = bvb + bchunk[0], vb1 = bvb + bchunk[1];
+            asm volatile("" : "+s"(adst), "+s"(bdst), "+v"(va0), "+v"(va1), "+v"(vb0), "+v"(vb1));
+            const int soff = static_cast<int>(kt * BK * 2);
+#pragma unroll
+            for (int p = 0; p < ST_ADMA; ++p)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    arsrc, (gemm::lds_void_t*)((char __attribute__((address_space(3)))*)adst + p * 1024), 16,
+                    ((p & 1) ? va1 : va0) + static_cast<uint32_t>(p) * rstep, soff, 0, 0);
+#pragma unroll
+            for (int p = 0; p < ST_BDMA; ++p)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    brsrc, (gemm::lds_void_t*)((char __attribute__((address_space(3)))*)bdst + p * 1024), 16,
+                    ((p & 1) ? vb1 : vb0) + static_cast<uint32_t>(p) * rstep, soff, 0, kNonTemporal);
+        };
+
+        floatx16_t acc[2];
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[jj][v] = 0.f;
+
+        const int64_t KT = a.K / BK;
+        // the previous tile's output stores are done (its reads ended at the barrier below)
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        // slices 0 .. S-2 (a short K reloads its last slice into the spare stages, never read)
+#pragma unroll
+        for (int s = 0; s < ST_STAGES - 1; ++s) issue(s, s < KT ? s : KT - 1);
+        int st = 0;
+        for (int64_t n = 0; n < KT; ++n) {
+            // slice n landed for this wave (its newest S - 2 slices may be in flight); after
+            // the barrier, for every wave, and no wave still reads stage (n - 1) mod S
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"((ST_STAGES - 2) * ST_VPS) : "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            bf16x8_t fa[4], fb[4][2];
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                fa[ks] = *reinterpret_cast<const bf16x8_t*>(&As[0][0] + st * (ST_BM * BK) +
+                                                            (rbk * 32 + frow) * BK + fchunk[ks]);
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj)
+                    fb[ks][jj] = *reinterpret_cast<const bf16x8_t*>(&Bs[0][0] + st * (ST_BN * BK) +
+                                                                    (brow[jj] + frow) * BK + fchunk[ks]);
+            }
+            const int refill = st == 0 ? ST_STAGES - 1 : st - 1;
+            issue(refill, n + ST_STAGES - 1 < KT ? n + ST_STAGES - 1 : KT - 1);
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj)
+                    acc[jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks][jj], fa[ks], acc[jj], 0, 0, 0);
+            st = st == ST_STAGES - 1 ? 0 : st + 1;
+        }
+        // every wave's reads of every stage are done before the next tile refills them
+        __syncthreads();
+
+        // ---- epilogue, as in grouped_gemm_pp_kernel
+        const int rloc = rbk * 32 + (lane & 31);
+        if (rloc < static_cast<int>(nrows)) {
+            const int64_t colbase = UP ? static_cast<int64_t>(nt) * ST_UPC + cg * 32 + (lane >> 5) * 4
+                                       : static_cast<int64_t>(nt) * ST_BN + cg * 64 + (lane >> 5) * 4;
+            uint16_t* cp = a.C + (row0 + rloc) * a.N + colbase;
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+                if (UP) {
+                    float h[4];
+#pragma unroll
+                    for (int tt = 0; tt < 4; ++tt) h[tt] = silu_mul(acc[0][4 * qq + tt], acc[1][4 * qq + tt]);
+                    *reinterpret_cast<uint2*>(cp + qq * 8) = make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
+                } else {
+#pragma unroll
+                    for (int jj = 0; jj < 2; ++jj) {
+                        const floatx16_t& c = acc[jj];
+                        *reinterpret_cast<uint2*>(cp + jj * 32 + qq * 8) =
+                            make_uint2(pack_bf16x2(c[4 * qq], c[4 * qq + 1]), pack_bf16x2(c[4 * qq + 2], c[4 * qq + 3]));
+                    }
+                }
+            }
+        }
+    }
+    // no DMA into LDS may outlive the workgroup
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 // ------------------------------------------------------------------ generic path
 // Any shape, alignment or activation dtype (fp32 activations, bf16 buffers off 16 bytes, H
 // not a multiple of 256, I not a multiple of 128): 64-row x 64-column tiles on the fp32
@@ -850,6 +1027,11 @@ moe_status run_stage(bool up, const void* A, moe_dtype act_dt, const moe_plan* p
             if (up) hipLaunchKernelGGL((grouped_gemm_bf16_kernel<true, true>), grid, dim3(M_THREADS), 0, stream, g, to);
             else hipLaunchKernelGGL((grouped_gemm_bf16_kernel<false, true>), grid, dim3(M_THREADS), 0, stream, g, to);
         } else {
+            // slots of at most 64 rows stream their weights in 64-row tiles, the rest run the
+            // ping-pong kernel; each kernel numbers its own slots' tiles on the device
+            if (up) hipLaunchKernelGGL((grouped_gemm_stream_kernel<true>), grid, dim3(ST_THREADS), 0, stream, g);
+            else hipLaunchKernelGGL((grouped_gemm_stream_kernel<false>), grid, dim3(ST_THREADS), 0, stream, g);
+            MOE_LAUNCH_CHECK();
             if (up) hipLaunchKernelGGL((grouped_gemm_pp_kernel<true>), grid, dim3(PP_THREADS), 0, stream, g, to);
             else hipLaunchKernelGGL((grouped_gemm_pp_kernel<false>), grid, dim3(PP_THREADS), 0, stream, g, to);
         }

@@ -41,13 +41,15 @@ struct TileOrder {
     int32_t SM, SN;  // super-tile = SM m-tiles x SN column tiles, SM*SN = blocks per XCD
 };
 
-// Slot e owns ceil(min(counts[e], cap - seg[e]) / BM) m-tiles; tile_prefix[e] = m-tiles
-// before slot e, tile_prefix[El] = total.  Called by all NTHR threads of the block (part
-// holds NTHR ints); ends synced.
+// Slot e owns ceil(c / BM) m-tiles, c = min(counts[e], cap - seg[e]), if lo < c <= hi and none
+// otherwise (two kernels can split the slots by size); tile_prefix[e] = m-tiles before slot e,
+// tile_prefix[El] = total.  Called by all NTHR threads of the block (part holds NTHR ints);
+// ends synced.
 template <int BM, int NTHR = kThreads>
 __device__ __forceinline__ int32_t number_tiles(const int32_t* counts, const int64_t* seg,
                                                 int64_t cap, int El, int32_t* tile_prefix,
-                                                int32_t* part) {
+                                                int32_t* part, int64_t lo = 0,
+                                                int64_t hi = INT64_MAX) {
     static_assert(kMaxSlots % NTHR == 0, "whole slots per thread");
     const int tid = threadIdx.x;
     int32_t loc[kMaxSlots / NTHR];
@@ -60,7 +62,7 @@ __device__ __forceinline__ int32_t number_tiles(const int32_t* counts, const int
             int64_t c = counts[e];
             const int64_t room = cap - seg[e];
             c = c < room ? c : (room > 0 ? room : 0);
-            mt = static_cast<int32_t>((c + BM - 1) / BM);
+            if (c > lo && c <= hi) mt = static_cast<int32_t>((c + BM - 1) / BM);
         }
         loc[q] = mt;
         s += mt;
