@@ -248,6 +248,10 @@ def main():
                     help="run each step as two micro-batches (each replica's tokens halved) on two "
                          "streams, pipelined by stages; the per-call breakdown comes from "
                          "single-batch steps run after the timed ones")
+    ap.add_argument("--cu-split", type=int, default=0, metavar="N",
+                    help="with --tbo: run both micro-batches' memory stages on a stream confined to "
+                         "CUs 0..N-1 (N a multiple of 8: N/8 on every XCD) and their expert GEMMs on a "
+                         "stream confined to the other CUs")
     ap.add_argument("--eplb", action="store_true",
                     help="skewed workload: count one step's expert load under the workload's own "
                          "slot table, place the experts with the library (288 slots, 8 groups, "
@@ -347,7 +351,7 @@ def main():
         if args.entry or args.exit or eplb_info is not None:
             raise SystemExit("--tbo runs the plain six-call step only")
         tbo = TwoBatchOverlap(spec_of(cfg), w, layer.sizes, act, mode=args.mode, device=dev,
-                              seg_stride=args.seg_stride)
+                              seg_stride=args.seg_stride, cu_split=args.cu_split)
         for _ in range(args.warmup):
             tbo.forward(reps)
         torch.cuda.synchronize()
@@ -533,8 +537,10 @@ def main():
         "data": "synthetic (seeded PCG64; random-init DeepSeek-V3-shaped expert weights)",
         "config": {"workload": WORKLOAD_TEXT[args.workload], "name": cfg.name,
                    "launch": "one HIP graph per step" if args.graph else "eager calls",
-                   "micro_batches": ("2, each replica halved, two streams pipelined by stages" if args.tbo
-                                     else "1"),
+                   "micro_batches": (("2, each replica halved, two streams pipelined by stages"
+                                      + (f"; memory stages on {args.cu_split} CUs, "
+                                         "GEMMs on the others" if args.cu_split else ""))
+                                     if args.tbo else "1"),
                    "first_step": "fused residual add + RMSNorm + gather" if args.entry else "plain gather",
                    "last_step": "fused combine + scatter" if args.exit else "combine, then scatter",
                    "dispatch_layout": (f"fixed capacity, {args.seg_stride} rows per slot" if args.seg_stride

@@ -26,6 +26,7 @@ __all__ = [
     "moe_expert_gemm_down", "moe_expert_gemm_workspace_size", "moe_combine", "moe_version",
     "PlanBuffers", "make_route_cfg", "make_expert_map", "make_expert_weights", "MoEError",
     "GatherLayout", "RouteCfg", "ExpertMap", "ExpertWeights", "Plan",
+    "moe_stream_create_cu_masked", "moe_stream_destroy",
 ]
 
 _MODES = {"auto": MOE_PAD_AUTO, "max": MOE_PAD_MAX_LEN, "sum": MOE_PAD_SUM_LEN}
@@ -342,3 +343,20 @@ def moe_combine_scatter(y_perm: torch.Tensor, plan: PlanBuffers, topk_w: torch.T
     check("moe_combine_scatter", lib().moe_combine_scatter(
         _ptr(y_perm), _dtype_code(y_perm), ctypes.byref(plan.struct), _ptr(topk_w),
         float(routed_scale), H, ctypes.byref(L), ctypes.cast(arr, ctypes.c_void_p), _stream(stream)))
+
+
+# ------------------------------------------------------------------ CU-partitioned streams
+
+def moe_stream_create_cu_masked(cu_mask) -> int:
+    """A new stream (default priority) confined to the CUs whose bits are set in cu_mask, a
+    sequence of 32-bit words (bit i of word i // 32 = CU i); returns the raw stream handle,
+    which torch.cuda.ExternalStream can wrap.  Release it with moe_stream_destroy."""
+    words = [int(x) & 0xFFFFFFFF for x in cu_mask]
+    arr = (ctypes.c_uint32 * max(len(words), 1))(*words)
+    out = ctypes.c_void_p()
+    check("moe_stream_create_cu_masked", lib().moe_stream_create_cu_masked(arr, len(words), ctypes.byref(out)))
+    return int(out.value)
+
+
+def moe_stream_destroy(handle: int) -> None:
+    check("moe_stream_destroy", lib().moe_stream_destroy(ctypes.c_void_p(handle)))

@@ -81,6 +81,8 @@ SIGNATURES = {
     "moe_combine": (c_i32, [c_vp, c_i32, ctypes.POINTER(Plan), c_vp, c_f32, c_i64, c_vp, c_vp]),
     "moe_combine_scatter": (c_i32, [c_vp, c_i32, ctypes.POINTER(Plan), c_vp, c_f32, c_i64,
                                     ctypes.POINTER(GatherLayout), c_vp, c_vp]),
+    "moe_stream_create_cu_masked": (c_i32, [c_vp, ctypes.c_uint32, ctypes.POINTER(c_vp)]),
+    "moe_stream_destroy": (c_i32, [c_vp]),
 }
 
 _lib = None

@@ -1,4 +1,6 @@
 // Host-only parts of the C ABI: status text, version, and the gather layout.
+#include <atomic>
+
 #include "moe_dev.h"
 
 extern "C" const char* moe_status_string(moe_status s) {
@@ -60,5 +62,59 @@ extern "C" moe_status moe_gather_layout(const int32_t* num_tokens, int32_t W, mo
         L.rows = static_cast<int64_t>(W) * mx;
     }
     *out = L;
+    return MOE_OK;
+}
+
+namespace moe {
+int device_cus() {
+    static std::atomic<int> cus[64];  // zero-initialised: not yet queried
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        (void)hipGetLastError();
+        return 256;
+    }
+    int v = cus[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) {
+            (void)hipGetLastError();
+            v = 256;
+        }
+        cus[dev].store(v, std::memory_order_relaxed);
+    }
+    return v;
+}
+
+int stream_cus(hipStream_t stream) {
+    const int all = device_cus();
+    const uint32_t words = static_cast<uint32_t>((all + 31) / 32);
+    uint32_t mask[32] = {};
+    if (words > 32 || hipExtStreamGetCUMask(stream, words, mask) != hipSuccess) {
+        (void)hipGetLastError();
+        return all;
+    }
+    int n = 0;
+    for (uint32_t i = 0; i < words; ++i) n += __builtin_popcount(mask[i]);
+    return n > 0 && n < all ? n : all;
+}
+}  // namespace moe
+
+extern "C" moe_status moe_stream_create_cu_masked(const uint32_t* cu_mask, uint32_t words, hipStream_t* out) {
+    MOE_CHECK_ARG(cu_mask && out && words >= 1 && words <= 32);
+    int n = 0;
+    for (uint32_t i = 0; i < words; ++i) n += __builtin_popcount(cu_mask[i]);
+    MOE_CHECK_ARG(n > 0);
+    if (hipExtStreamCreateWithCUMask(out, words, cu_mask) != hipSuccess) {
+        (void)hipGetLastError();
+        return MOE_ERR_HIP;
+    }
+    return MOE_OK;
+}
+
+extern "C" moe_status moe_stream_destroy(hipStream_t stream) {
+    MOE_CHECK_ARG(stream != nullptr);
+    if (hipStreamDestroy(stream) != hipSuccess) {
+        (void)hipGetLastError();
+        return MOE_ERR_HIP;
+    }
     return MOE_OK;
 }

@@ -43,17 +43,10 @@
 
 namespace moe {
 namespace gemm {
-int num_cus() {
-    static int cus[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cus[dev] == 0) {
-        int v = 0;
-        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
-            v = 256;
-        cus[dev] = v;
-    }
-    return cus[dev];
+int num_cus() { return device_cus(); }
+int grid_blocks(hipStream_t stream) {
+    const int n = stream_cus(stream) & ~7;  // whole XCD groups of 8 for the tile order
+    return n >= 8 ? n : 8;
 }
 }  // namespace gemm
 
@@ -1019,7 +1012,7 @@ moe_status run_stage(bool up, const void* A, moe_dtype act_dt, const moe_plan* p
         g.El = plan->num_slots;
         g.NT = static_cast<int32_t>(up ? I / UP_COLS : H / BN);
         // one block per CU, 8 XCDs: a super-tile of SM x SN tiles per XCD per round
-        const int blocks = gemm::num_cus();
+        const int blocks = gemm::grid_blocks(stream);
         gemm::TileOrder to;
         if (!gemm::pick_tile_order(g.NT, blocks, &to)) return MOE_ERR_UNSUPPORTED;
         const dim3 grid(static_cast<unsigned>(blocks));
@@ -1045,7 +1038,7 @@ moe_status run_stage(bool up, const void* A, moe_dtype act_dt, const moe_plan* p
     g.K = K;
     g.N = N;
     g.El = plan->num_slots;
-    const dim3 grid(static_cast<unsigned>(gemm::num_cus() * 4));
+    const dim3 grid(static_cast<unsigned>(gemm::grid_blocks(stream) * 4));
     if (act_dt == MOE_BF16) {
         if (up) hipLaunchKernelGGL((generic_gemm_kernel<uint16_t, true>), grid, dim3(256), 0, stream, g, A, B, C);
         else hipLaunchKernelGGL((generic_gemm_kernel<uint16_t, false>), grid, dim3(256), 0, stream, g, A, B, C);

@@ -335,7 +335,7 @@ moe_status run_fp8_stage(bool up, const void* act, const moe_plan* plan,
     g.N = N;
     g.El = plan->num_slots;
     g.NT = static_cast<int32_t>(up ? I / F_UP_COLS : H / F_BN);
-    const int blocks = num_cus();
+    const int blocks = grid_blocks(stream);
     TileOrder to;
     if (!pick_tile_order(g.NT, blocks, &to)) return MOE_ERR_UNSUPPORTED;
     const dim3 grid(static_cast<unsigned>(blocks));

@@ -99,6 +99,8 @@ __device__ __forceinline__ int slot_of_tile(const int32_t* tile_prefix, int El, 
 }
 
 int num_cus();
+// blocks of a persistent launch on `stream`: its usable CUs, rounded down to a multiple of 8
+int grid_blocks(hipStream_t stream);
 
 // Super-tile shape for NT column tiles and `blocks` blocks (8 XCDs); false if unusable.
 inline bool pick_tile_order(int NT, int blocks, TileOrder* to) {

@@ -20,6 +20,12 @@ namespace moe {
 
 constexpr int kWave = 64;
 
+// Compute units of the current device, and how many of them a stream may use (its CU mask,
+// all of them for an ordinary stream).  Persistent grids are sized by the latter, so a
+// kernel on a stream confined to part of the GPU keeps one block per usable CU.
+int device_cus();
+int stream_cus(hipStream_t stream);
+
 inline int dtype_size(moe_dtype dt) {
     switch (dt) {
         case MOE_F32: return 4;

@@ -575,19 +575,6 @@ __global__ __launch_bounds__(G_THREADS) void gate_fast_kernel(const uint16_t* __
         }
 }
 
-int gate_num_cus() {
-    static int cus[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cus[dev] == 0) {
-        int v = 0;
-        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
-            v = 256;
-        cus[dev] = v;
-    }
-    return cus[dev];
-}
-
 // ------------------------------------------------------------------ selection
 // One wave per global row.  Lane l holds the V consecutive experts e = l*V + j (V = E/64
 // rounded up to a power of two), so a group of E/n_group experts covers E/(n_group*V)
@@ -957,7 +944,7 @@ extern "C" moe_status moe_route(const void* global_x, const int32_t* row_valid, 
     // batch too small for its 128-row tiles to cover half the CUs takes the exact gate: its
     // few tiles would run the whole of h in sequence on part of the GPU, and the exact
     // logits are the better ones anyway.
-    const int64_t ncu = moe::gate_num_cus();
+    const int64_t ncu = moe::stream_cus(stream);
     const int64_t etiles = moe::ceil_div(E, moe::GB_N);
     const bool fills128 = moe::ceil_div(G, 128) * etiles >= ncu;
     const bool fills64 = moe::ceil_div(G, 64) * etiles >= ncu;

@@ -221,15 +221,48 @@ class TwoBatchOverlap:
     STAGES = (("gather", "route", "dispatch"), ("experts",), ("combine", "scatter"))
 
     def __init__(self, spec: LayerSpec, weights: DeviceWeights, num_tokens: Sequence[int],
-                 act_dtype: torch.dtype, mode: str = "sum", device="cuda", seg_stride: int = 0):
+                 act_dtype: torch.dtype, mode: str = "sum", device="cuda", seg_stride: int = 0,
+                 cu_split: int = 0):
+        """cu_split = n > 0 partitions the CUs (the vLLM page's SM allocation, section
+        "第八步：SM 的分配"): both micro-batches' memory stages (0 and 2) run on a stream
+        confined to CUs 0 .. n - 1, both micro-batches' expert GEMMs on a stream confined to the
+        others.  The runtime numbers CU i on XCD i mod 8 and refuses a mask that leaves an XCD
+        without CUs, so n is a multiple of 8 and each XCD gives n / 8 CUs to the small side."""
         self.num_tokens = [int(n) for n in num_tokens]
         self.slices = split_micro_batches(self.num_tokens)
         self.layers = [MoELayer(spec, weights, [b - a for a, b in sl], act_dtype, mode=mode, device=device,
                                 seg_stride=seg_stride) for sl in self.slices]
         H = spec.hidden
         self.replicas_out = [torch.empty((n, H), dtype=act_dtype, device=device) for n in self.num_tokens]
-        self.side = torch.cuda.Stream(device=device)
         self.events = [[torch.cuda.Event() for _ in self.STAGES] for _ in range(2)]
+        self.cu_split = int(cu_split)
+        self._owned = []
+        if self.cu_split > 0:
+            from . import moe_stream_create_cu_masked
+            cus = torch.cuda.get_device_properties(device).multi_processor_count
+            if not 0 < self.cu_split < cus or self.cu_split % 8:
+                raise ValueError(f"cu_split must be a multiple of 8 in 8..{cus - 8}")
+            small = set(range(self.cu_split))
+            words = (cus + 31) // 32
+            masks = []
+            for member in (lambda i: i in small, lambda i: i not in small):
+                m = [0] * words
+                for i in range(cus):
+                    if member(i):
+                        m[i // 32] |= 1 << (i % 32)
+                masks.append(m)
+            self._owned = [moe_stream_create_cu_masked(m) for m in masks]
+            self.mem_stream, self.gemm_stream = (torch.cuda.ExternalStream(h, device=device) for h in self._owned)
+        else:
+            self.side = torch.cuda.Stream(device=device)
+
+    def __del__(self):
+        if getattr(self, "_owned", None):
+            from . import moe_stream_destroy
+            torch.cuda.synchronize()
+            for h in self._owned:
+                moe_stream_destroy(h)
+            self._owned = []
 
     def _stage(self, mb: int, s: int, ins, outs):
         layer = self.layers[mb]
@@ -245,6 +278,8 @@ class TwoBatchOverlap:
         main = torch.cuda.current_stream()
         ins = [[r[a:b] for r, (a, b) in zip(replicas, sl)] for sl in self.slices]
         outs = [[y[a:b] for y, (a, b) in zip(self.replicas_out, sl)] for sl in self.slices]
+        if self.cu_split > 0:
+            return self._forward_partitioned(main, ins, outs)
         streams = (main, self.side)
         self.side.wait_stream(main)            # inputs written before the step are visible
         for s in range(len(self.STAGES)):
@@ -256,4 +291,24 @@ class TwoBatchOverlap:
                 self._stage(1, s, ins[1], outs[1])
                 self.events[1][s].record(streams[1])
         main.wait_event(self.events[1][-1])    # the step ends when both micro-batches have
+        return self.replicas_out
+
+    def _forward_partitioned(self, main, ins, outs) -> List[torch.Tensor]:
+        """Memory stages of both micro-batches in order on the small partition, GEMMs of both
+        in order on the large one; each stage waits for its micro-batch's previous stage, so
+        micro-batch 1's stage 0 runs beside micro-batch 0's GEMMs and micro-batch 0's stage 2
+        beside micro-batch 1's GEMMs."""
+        mem, gemm = self.mem_stream, self.gemm_stream
+        mem.wait_stream(main)
+        gemm.wait_stream(main)
+        # host issue order (micro-batch, stage); on each stream the work runs in this order
+        for mb, s in ((0, 0), (1, 0), (0, 1), (1, 1), (0, 2), (1, 2)):
+            st = gemm if s == 1 else mem
+            with torch.cuda.stream(st):
+                if s > 0:
+                    st.wait_event(self.events[mb][s - 1])
+                self._stage(mb, s, ins[mb], outs[mb])
+                self.events[mb][s].record(st)
+        main.wait_event(self.events[0][-1])
+        main.wait_event(self.events[1][-1])
         return self.replicas_out

@@ -487,6 +487,26 @@ moe_status moe_eplb_logical_to_physical(const int32_t* phy2log, const int32_t* p
                                         int32_t num_physical, int32_t num_logical, int32_t max_rep,
                                         int32_t* phys_of, int32_t* n_rep);
 
+/* ------------------------------------------------------------------------------------------
+ * CU-partitioned streams, for running two micro-batches side by side on one GPU (the vLLM
+ * walkthrough's two-micro-batch schedule gives the communication kernels a fixed share of the
+ * streaming multiprocessors and the GEMMs the rest: section "第八步：SM 的分配").
+ *
+ * moe_stream_create_cu_masked -- a new stream, at the default priority, whose kernels run only
+ * on the compute units whose bits are set in cu_mask (bit i of word i / 32 = CU i, in the
+ * runtime's CU numbering).  The library's persistent kernels (the grouped GEMMs, the gate)
+ * size their grids to the CUs of the stream they are launched on, so they can run on such a
+ * stream.  The caller owns the stream and releases it with moe_stream_destroy.
+ *   cu_mask  host uint32[words], at least one bit set;  1 <= words <= 32
+ *   out      host, the new stream on success
+ * Errors: MOE_ERR_INVALID_ARG for NULL pointers, words out of range or an empty mask;
+ * MOE_ERR_HIP if the runtime refuses the stream.
+ * ---------------------------------------------------------------------------------------- */
+moe_status moe_stream_create_cu_masked(const uint32_t* cu_mask, uint32_t words, hipStream_t* out);
+/* moe_stream_destroy -- releases a stream from moe_stream_create_cu_masked (after its work;
+ * the runtime waits for it).  MOE_ERR_INVALID_ARG for a NULL stream. */
+moe_status moe_stream_destroy(hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

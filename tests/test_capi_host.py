@@ -212,3 +212,18 @@ def test_fixed_capacity_plan_errors(m):
         plan = _lib.Plan(fake, fake, fake, fake, fake, fake, cap, 3, 2, 4, 1, stride)
         assert lib.moe_dispatch(fake, fake, 3, 2, 16, _lib.MOE_BF16, ctypes.byref(emap), ctypes.byref(plan),
                                 fake, ws, 64, None) == _lib.MOE_ERR_INVALID_ARG
+
+
+def test_cu_masked_stream_rejects_bad_masks(m):
+    """The stream helpers check their arguments before any HIP call."""
+    from combine_dp_gather_amd import _lib
+    lib = m.lib()
+    out = ctypes.c_void_p()
+    empty = (ctypes.c_uint32 * 8)()
+    assert lib.moe_stream_create_cu_masked(empty, 8, ctypes.byref(out)) == _lib.MOE_ERR_INVALID_ARG
+    one = (ctypes.c_uint32 * 1)(1)
+    assert lib.moe_stream_create_cu_masked(one, 0, ctypes.byref(out)) == _lib.MOE_ERR_INVALID_ARG
+    assert lib.moe_stream_create_cu_masked(one, 33, ctypes.byref(out)) == _lib.MOE_ERR_INVALID_ARG
+    assert lib.moe_stream_create_cu_masked(None, 1, ctypes.byref(out)) == _lib.MOE_ERR_INVALID_ARG
+    assert lib.moe_stream_create_cu_masked(one, 1, None) == _lib.MOE_ERR_INVALID_ARG
+    assert lib.moe_stream_destroy(None) == _lib.MOE_ERR_INVALID_ARG
