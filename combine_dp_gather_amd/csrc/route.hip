@@ -575,6 +575,147 @@ __global__ __launch_bounds__(G_THREADS) void gate_fast_kernel(const uint16_t* __
         }
 }
 
+// The same tile and the same K order (so the same logits) for H a multiple of 64 with 16-byte
+// aligned rows: 64-deep slices DMA'd straight into the LDS (`buffer_load ... lds`, whole
+// 128-byte lines per row and slice; the token rows, read once, with the non-temporal hint)
+// through three stages, two slices in flight, one barrier per slice.  The register-staged
+// form above keeps one slice in flight, which bounds its rate at ~21 GB/s per CU.  LDS rows
+// are 128 bytes with chunk c of row r stored at c xor ((r / 2) mod 8), so a fragment read (16
+// consecutive rows, one 16-byte chunk each) touches 16 distinct 16-byte slots of 256 bytes.
+constexpr int FD_STAGES = 3;
+constexpr int FD_CPR = FB_K / 8;                     // 16-byte chunks per row (8)
+constexpr int FD_RPB = 64 / FD_CPR;                  // rows per 1 KB DMA block (8)
+constexpr int FD_XDMA = FB_M / FD_RPB / 4;           // token-row DMAs per wave and slice (4)
+constexpr int FD_WDMA = FB_N / FD_RPB / 4;           // weight-row DMAs per wave and slice (8)
+constexpr int FD_VPS = FD_XDMA + FD_WDMA;
+__device__ __forceinline__ int fd_swz(int row) { return (row >> 1) & 7; }
+
+__global__ __launch_bounds__(G_THREADS, 1) void gate_fast_dma_kernel(const uint16_t* __restrict__ x,
+                                                                     const uint16_t* __restrict__ w,
+                                                                     const int32_t* __restrict__ row_valid,
+                                                                     int64_t G, int64_t E, int64_t H,
+                                                                     float* __restrict__ logits) {
+    __shared__ __attribute__((aligned(1024))) uint16_t xs[FD_STAGES][FB_M * FB_K];
+    __shared__ __attribute__((aligned(1024))) uint16_t ws[FD_STAGES][FB_N * FB_K];
+    const int64_t m0 = static_cast<int64_t>(blockIdx.x) * FB_M;
+    const int64_t n0 = static_cast<int64_t>(blockIdx.y) * FB_N;
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+    const int wm = wv >> 1, wn = wv & 1;
+    const int64_t xrows = G - m0 < FB_M ? G - m0 : FB_M;
+    const int64_t wrows = E - n0 < FB_N ? E - n0 : FB_N;
+    const uint32_t row_bytes = static_cast<uint32_t>(H) * 2u;
+    // rows past G or E fall outside the resources and read as zeros
+    const __amdgpu_buffer_rsrc_t rx = gemm::make_rsrc_uniform(x + m0 * H, static_cast<uint32_t>(xrows) * row_bytes);
+    const __amdgpu_buffer_rsrc_t rw = gemm::make_rsrc_uniform(w + n0 * H, static_cast<uint32_t>(wrows) * row_bytes);
+    // DMA p of this wave: token rows 32 wv + 8 p + lane / 8, weight rows 64 wv + 8 p + lane / 8;
+    // the global chunk (lane mod 8) xor swizzle, whose value depends on p only through p mod 2
+    const int dr = lane / FD_CPR;
+    const int xr0 = 32 * wv + dr, wr0 = 64 * wv + dr;
+    uint32_t xoff[2], woff[2];
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+        xoff[par] = static_cast<uint32_t>(xr0) * row_bytes + static_cast<uint32_t>(((lane % FD_CPR) ^ fd_swz(xr0 + 8 * par)) * 16);
+        woff[par] = static_cast<uint32_t>(wr0) * row_bytes + static_cast<uint32_t>(((lane % FD_CPR) ^ fd_swz(wr0 + 8 * par)) * 16);
+    }
+    const uint32_t rstep = static_cast<uint32_t>(FD_RPB) * row_bytes;
+    auto issue = [&](int stage, int64_t kt) {
+        gemm::lds_void_t* xd = (gemm::lds_void_t*)(&xs[0][0] + stage * (FB_M * FB_K) + wv * FD_XDMA * 512);
+        gemm::lds_void_t* wd = (gemm::lds_void_t*)(&ws[0][0] + stage * (FB_N * FB_K) + wv * FD_WDMA * 512);
+        uint32_t x0 = xoff[0], x1 = xoff[1], w0 = woff[0], w1 = woff[1];
+        asm volatile("" : "+s"(xd), "+s"(wd), "+v"(x0), "+v"(x1), "+v"(w0), "+v"(w1));
+        const int so = static_cast<int>(kt * FB_K * 2);
+#pragma unroll
+        for (int p = 0; p < FD_XDMA; ++p)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rx, (gemm::lds_void_t*)((char __attribute__((address_space(3)))*)xd + p * 1024), 16,
+                ((p & 1) ? x1 : x0) + static_cast<uint32_t>(p) * rstep, so, 0, 2 /* non-temporal */);
+#pragma unroll
+        for (int p = 0; p < FD_WDMA; ++p)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rw, (gemm::lds_void_t*)((char __attribute__((address_space(3)))*)wd + p * 1024), 16,
+                ((p & 1) ? w1 : w0) + static_cast<uint32_t>(p) * rstep, so, 0, 0);
+    };
+    floatx16_t acc[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[c][v] = 0.f;
+    // fragment reads: row lane mod 32 of each 32-row block, logical chunk 2 ks + lane / 32 of
+    // each 16-deep step (the K order of gate_fast_kernel)
+    const int fr = lane & 31;
+    int fch[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) fch[ks] = ((2 * ks + (lane >> 5)) ^ fd_swz(fr)) * 8;
+    const int64_t KT = H / FB_K;
+#pragma unroll
+    for (int s = 0; s < FD_STAGES - 1; ++s) issue(s, s < KT ? s : KT - 1);
+    int st = 0;
+    for (int64_t kt = 0; kt < KT; ++kt) {
+        // slice kt landed for this wave; after the barrier for every wave, and no wave still
+        // reads the stage refilled below (slice kt - 1's)
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((FD_STAGES - 2) * FD_VPS) : "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        const uint16_t* xa = &xs[0][0] + st * (FB_M * FB_K) + (wm * 64 + fr) * FB_K;
+        const uint16_t* wb = &ws[0][0] + st * (FB_N * FB_K) + (wn * 128 + fr) * FB_K;
+        gate_bf16x8_t fa[4][2], fb[4][4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) fa[ks][rb] = *reinterpret_cast<const gate_bf16x8_t*>(xa + rb * 32 * FB_K + fch[ks]);
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) fb[ks][cb] = *reinterpret_cast<const gate_bf16x8_t*>(wb + cb * 32 * FB_K + fch[ks]);
+        }
+        const int refill = st == 0 ? FD_STAGES - 1 : st - 1;
+        issue(refill, kt + FD_STAGES - 1 < KT ? kt + FD_STAGES - 1 : KT - 1);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                for (int cb = 0; cb < 4; ++cb)
+                    acc[rb * 4 + cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks][rb], fb[ks][cb], acc[rb * 4 + cb], 0, 0, 0);
+        st = st == FD_STAGES - 1 ? 0 : st + 1;
+    }
+    // no DMA into LDS may outlive the workgroup
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // the lane's 32 rows (row block rb, register v): their flags first, in one batch of loads
+    // (rows past G load row G - 1's flag, unused), then keep = -1 past G, else the flag
+    int keep[2][16];
+    if (row_valid != nullptr) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int64_t g = m0 + wm * 64 + 32 * rb + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                keep[rb][v] = row_valid[g < G ? g : G - 1];
+            }
+    } else {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) keep[rb][v] = 1;
+    }
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int64_t g = m0 + wm * 64 + 32 * rb + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+            keep[rb][v] = g >= G ? -1 : keep[rb][v] != 0 ? 1 : 0;
+        }
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            // accumulator c = 4 rb + cb, register v: row block rb, expert block cb
+            const int64_t e = n0 + wn * 128 + 32 * (c & 3) + (lane & 31);
+            const int64_t g = m0 + wm * 64 + 32 * (c >> 2) + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+            const int k = keep[c >> 2][v];
+            if (k >= 0 && e < E) logits[g * E + e] = k ? acc[c][v] : 0.f;
+        }
+}
+
 // ------------------------------------------------------------------ selection
 // One wave per global row.  Lane l holds the V consecutive experts e = l*V + j (V = E/64
 // rounded up to a power of two), so a group of E/n_group experts covers E/(n_group*V)
@@ -955,9 +1096,14 @@ extern "C" moe_status moe_route(const void* global_x, const int32_t* row_valid, 
         const bool fast = aligned && static_cast<int64_t>(moe::FB_N) * H * 2 < ((int64_t)1 << 31);
         const dim3 grid(static_cast<unsigned>(moe::ceil_div(G, moe::FB_M)),
                         static_cast<unsigned>(moe::ceil_div(E, moe::FB_N)));
-        hipLaunchKernelGGL(moe::gate_fast_kernel, grid, dim3(moe::G_THREADS), 0, stream,
-                           static_cast<const uint16_t*>(global_x), static_cast<const uint16_t*>(w_router),
-                           row_valid, G, E, H, fast, logits);
+        if (fast && H % moe::FB_K == 0)
+            hipLaunchKernelGGL(moe::gate_fast_dma_kernel, grid, dim3(moe::G_THREADS), 0, stream,
+                               static_cast<const uint16_t*>(global_x), static_cast<const uint16_t*>(w_router),
+                               row_valid, G, E, H, logits);
+        else
+            hipLaunchKernelGGL(moe::gate_fast_kernel, grid, dim3(moe::G_THREADS), 0, stream,
+                               static_cast<const uint16_t*>(global_x), static_cast<const uint16_t*>(w_router),
+                               row_valid, G, E, H, fast, logits);
     } else if (exact32 && (fills128 || fills64)) {
         // 32x32 chains; the kernel's descriptors span up to 256 rows, which must stay below
         // 2 GiB

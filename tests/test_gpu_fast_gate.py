@@ -101,3 +101,40 @@ def test_fast_mode_small_batch_is_exact():
     ref_l, ref_ids, ref_w = oracle.route(cfg, x, np.ones(G, np.int32), inp.router_w, inp.bias)
     assert np.array_equal(to_np(lg).view(np.uint32), ref_l.view(np.uint32))
     assert np.array_equal(to_np(ids), ref_ids)
+
+
+# FAST mode runs its own kernels once its 128-row x 256-expert tiles cover half the CUs
+@pytest.mark.parametrize("G,H,E", [(16384, 7168, 256), (8200, 2048, 320), (16400, 512, 256)])
+def test_fast_dma_kernel_equals_register_staged_kernel(G, H, E):
+    """FAST mode has two kernels with one tile and one K order: LDS-DMA staging for aligned
+    rows with H a multiple of 64, register staging otherwise.  The same rows run once from an
+    aligned buffer and once from a buffer offset by 2 bytes (which forces register staging):
+    the logits must agree bit for bit, invalid rows must be 0, and a ragged last tile (G not a
+    multiple of 128, E not a multiple of 256) must be covered."""
+    import combine_dp_gather_amd as m
+    rng = np.random.default_rng(7)
+    x = torch.from_numpy(rng.standard_normal((G, H), dtype=np.float32)).to(torch.bfloat16).cuda()
+    wr = torch.from_numpy((0.02 * rng.standard_normal((E, H))).astype(np.float32)).to(torch.bfloat16).cuda()
+    rv = torch.from_numpy((rng.random(G) > 0.1).astype(np.int32)).cuda()
+    rc = m.make_route_cfg("softmax", E, 8, 1, 1, 1, True, gate="fast")
+    outs = []
+    for shifted in (False, True):
+        if shifted:
+            buf = torch.empty(G * H + 1, dtype=torch.bfloat16, device="cuda")
+            xs = buf[1:].view(G, H)
+            xs.copy_(x)
+        else:
+            xs = x
+        lg = torch.full((G, E), float("nan"), device="cuda")
+        ids = torch.empty(G, 8, dtype=torch.int32, device="cuda")
+        w = torch.empty(G, 8, device="cuda")
+        m.moe_route(xs, rv, wr, None, rc, lg, ids, w)
+        torch.cuda.synchronize()
+        outs.append(to_np(lg))
+    say(f"[fast] G={G} H={H} E={E}: DMA and register-staged FAST logits compared")
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+    invalid = to_np(rv) == 0
+    assert np.all(outs[0][invalid] == 0.0)
+    ref = x.float() @ wr.float().t()
+    d = (torch.from_numpy(outs[0]).cuda() - ref).abs()[torch.from_numpy(~invalid).cuda()]
+    assert float(d.max()) < 1e-3 * float(ref.abs().max())
