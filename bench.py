@@ -509,8 +509,8 @@ def main():
     roof["timing"] = "median over the timed steps' launches, each after the cache flush"
     fmt = "fp8" if mm == "mfma8" else "bf16"
     kname = ("grouped_gemm_fp8_kernel" if fmt == "fp8"
-             else "grouped_gemm_bf16_kernel<true, true>" if bf and fp8w
-             else "grouped_gemm_pp_kernel<true>" if bf
+             else "grouped_gemm_pp_kernel<true, true>" if bf and fp8w
+             else "grouped_gemm_pp_kernel<true, false>" if bf
              else "generic_gemm_kernel<float, true>")
     roof["kernel"] = kname + (" (gate+up SwiGLU" + (", with its activation quantisation" if fmt == "fp8" else "")
                               + ")")

@@ -8,32 +8,22 @@
 //     h[r, i] = silu(sum_h x[r,h] Wg[e][i,h]) * (sum_h x[r,h] Wu[e][i,h])
 //     y[r, c] = sum_i h[r,i] Wd[e][c,i]
 //
-// bf16 weights run grouped_gemm_pp_kernel (below): the tiles, tile order and accumulation
-// order of the kernel described next, with 8 waves alternating between an MFMA phase and a
-// memory phase.  fp8 weights run the 4-wave kernel:
-//
-// 4-wave kernel (gfx950 v_mfma_f32_32x32x16_bf16, fp32 accumulate):
-//   - block tile 256 rows x 256 columns, 4 waves in a 2x2 grid, each wave 128x128 = 4x4 MFMA
-//     blocks (256 fp32 accumulators per lane, in AGPRs).  The weight fragment is the MFMAs'
-//     first operand, so each accumulator block holds its output block transposed and a lane
-//     writes four consecutive columns of one row per 8-byte store;
-//   - up kernel: the 256 columns are 128 gate columns and the same 128 up columns, so each
-//     lane holds gate and up for identical (row, i) and applies SiLU*up in registers;
-//   - operands move global -> LDS by buffer DMA (no register staging) in 64-deep K slices:
-//     each row contributes one whole 128-byte line per slice, which the DMA path moves about
-//     1.5x faster than half lines.  Two LDS stages of 64 KB: slice kt+1 is in flight while
-//     slice kt is consumed, in two halves whose fragments are read during the previous
-//     half's MFMAs; the reads and refill DMAs are spread between the MFMAs.  With bf16
-//     weights A is refilled after a mid-slice barrier and B after an end-of-slice barrier,
-//     so the other operand's DMAs are always in flight when a wave waits for its own;
-//   - persistent grid (one block per CU), XCD-grouped tile order (gemm_common.h); rows past
-//     a segment's end read as zeros and are never stored; each output tile has one owner.
-//
-// fp8 weights with bf16 activations (the default way for e4m3 weights) run in the same
-// kernel: weight rows are staged as fp8 (half the bytes), a lane reads one 16-byte chunk per
-// weight block and half slice and dequantises it (exact e4m3 -> fp32, times the block's
-// fp32 scale, RNE to bf16) into the fragments of two MFMA steps; the activation fragments
-// use the matching K assignment.  The tile's block scales are staged in LDS per tile.
+// Three kernels, all on gfx950 v_mfma_f32_32x32x16_bf16 with fp32 accumulation, all with the
+// weight fragment as the MFMAs' first operand (each accumulator block holds its output block
+// transposed, so a lane writes four consecutive columns of one row per 8-byte store), the
+// up GEMM's 256 weight rows being 128 gate rows and the same 128 up rows (SiLU * up in
+// registers, only h written), operands moved global -> LDS by buffer DMA, rows past a
+// segment's end read as zeros and never stored, and one owner per output tile:
+//   - grouped_gemm_pp_kernel: slots of more than 64 rows.  256 x 256 tiles, 8 waves in two
+//     groups that alternate between an MFMA phase and a memory phase; persistent grid, one
+//     block per CU, XCD-grouped tile order (gemm_common.h).  fp8 weights with bf16
+//     activations (the default for e4m3 weights) run here too: weight rows are staged as
+//     fp8 (half the bytes) and a lane's 16 weight bytes are dequantised (exact e4m3 -> fp32,
+//     times the block's fp32 scale, RNE to bf16) into the fragments of two MFMA steps.
+//   - grouped_gemm_stream_kernel: bf16 weights, slots of 1-64 rows, which stream their
+//     weights: 64 x 128 tiles, 64-deep slices, five stages, non-temporal weight loads.
+//   - generic_gemm_kernel: any other shape, alignment or activation dtype, on the fp32
+//     matrix cores.
 // fp8 weights with per-1x128-group e4m3 activations (fp8 matrix cores, fp32 promotion per K
 // group) live in expert_gemm_fp8.hip.
 #include <hip/hip_runtime.h>
@@ -56,9 +46,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx16_t __attribute__((ext_vector_type(16)));
 
 constexpr int BM = 256, BN = 256;
-constexpr int BK = 64;      // K slice per pipeline stage: whole 128-byte lines per row
-constexpr int STAGES = 2;   // LDS stages (2 x 64 KB)
-constexpr int M_THREADS = gemm::kThreads;
+constexpr int BK = 64;      // K slice of the weight-streaming kernel: whole 128-byte lines per row
 constexpr int UP_COLS = BN / 2;     // i-columns per up tile (gate and up each)
 constexpr int kMaxKG8 = 128;        // fp8 weights: at most 128 K groups (K <= 16384)
 
@@ -90,393 +78,17 @@ __device__ __forceinline__ bf16x8_t dequant8(uint2 u, float s) {
     return r;
 }
 
-// LDS layout of a stage: 256 rows x BK bf16 per operand, rows of BK/8 16-byte chunks.  The
-// LDS serves a 16-byte-per-lane read 16 lanes at a time from 64 banks (256 bytes); the
-// fragment reads have 16 consecutive rows asking for the same logical chunk, so the chunk
-// index is xor-ed with swz(row) = (row / rows-per-256-bytes) mod chunks-per-row, which puts
-// those 16 rows on 16 distinct 16-byte slots of the 256-byte bank window.
+// LDS rows of BK bf16 (128 bytes), of CPR 16-byte chunks.  The LDS serves a 16-byte-per-lane
+// read 16 lanes at a time from 64 banks (256 bytes); the fragment reads have 16 consecutive
+// rows asking for the same logical chunk, so the chunk index is xor-ed with swz(row) =
+// (row / 2) mod 8, which puts those 16 rows on 16 distinct 16-byte slots of the 256-byte
+// bank window.
 constexpr int CPR = BK / 8;            // 16-byte chunks per row
-constexpr int RPB = 64 / CPR;          // rows per 1 KB DMA block (one wave instruction)
-constexpr int NBLK = BM / RPB;         // DMA blocks per operand per stage
-constexpr int LPW = 2 * NBLK / 4;      // DMA instructions per wave per stage
-static_assert(BK == 32 || BK == 64, "swizzle written for 32- or 64-wide K slices");
-__device__ __forceinline__ int swz(int row) { return BK == 64 ? ((row >> 1) & 7) : ((row >> 2) & 3); }
-
-// W8: the weights are e4m3 with 128x128 block scales.  They are staged as fp8 (a weight
-// stage is 256 rows x 128 bytes = two 64-deep slices, refilled two slices ahead) and each
-// fragment is dequantised to bf16 on its way from LDS to the matrix cores; activations stay
-// bf16 and the same bf16 MFMAs run.
-template <bool UP, bool W8>
-__global__ __launch_bounds__(M_THREADS, 1) void grouped_gemm_bf16_kernel(GemmArgs a, gemm::TileOrder to) {
-    __shared__ __attribute__((aligned(1024))) uint16_t As[STAGES][BM * BK];
-    __shared__ __attribute__((aligned(1024))) uint16_t Bs[STAGES][BN * BK];
-    __shared__ int32_t tile_prefix[gemm::kMaxSlots + 1];  // m-tiles before slot e
-    __shared__ int32_t part[gemm::kThreads];
-    // fp8: the tile's weight block scales along K, [2][K/128] (up: gate, up half; down: the two
-    // 128-column blocks of the tile), staged at tile start so the K loop reads them from LDS
-    __shared__ float sbuf[2][kMaxKG8];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    // wave index as a scalar: the DMA's LDS destination must be wave-uniform
-    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wv >> 1, wn = wv & 1;
-
-    const int32_t total_mt = gemm::number_tiles<BM>(a.counts, a.seg, a.cap, a.El, tile_prefix, part);
-    const uint32_t row_bytes = static_cast<uint32_t>(a.K) * 2u;
-    const int64_t KG = a.K / 128;      // fp8 scale blocks along K
-    const int64_t NB = a.N / 128;      // fp8 scale blocks along the output dimension
-    const int nsn = a.NT / to.SN;
-    const int64_t total_super = static_cast<int64_t>((total_mt + to.SM - 1) / to.SM) * nsn;
-    const int xcd = blockIdx.x & 7;
-    const int q = blockIdx.x >> 3;
-    // this lane's 16-byte chunk inside a DMA block of RPB rows x CPR chunks
-    const int dma_row = lane / CPR;
-    // fragment reads: row lane%32 of a 32-row block, logical chunk 2*ks + lane/32
-    const int frow = lane & 31;
-    int fchunk[BK / 16];
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) fchunk[ks] = ((2 * ks + (lane >> 5)) ^ swz(frow)) * 8;
-    // fp8 weights: within half h of a slice, a lane reads one 16-byte weight chunk, 2h + lane/32,
-    // and feeds its first 8 values to step 0 and the last 8 to step 1.  The activation
-    // fragments follow the same K assignment (step ks of half h: the 8 values at 32h +
-    // 16 (lane/32) + 8 ks), so every product still pairs equal K.
-    int fchunk8[2][2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) fchunk8[h][ks] = ((4 * h + 2 * (lane >> 5) + ks) ^ swz(frow)) * 8;
-
-    for (int64_t sup = xcd; sup < total_super; sup += 8) {
-        const int32_t em = static_cast<int32_t>(sup / nsn) * to.SM + q / to.SN;
-        const int32_t nt = static_cast<int32_t>(sup % nsn) * to.SN + q % to.SN;
-        if (em >= total_mt) continue;
-        // the tile coordinates are block-uniform: scalar registers, scalar descriptors
-        const int e = gemm::slot_of_tile(tile_prefix, a.El, em);
-        const int32_t mtile = __builtin_amdgcn_readfirstlane(em - tile_prefix[e]);
-        const int64_t seg_start = a.seg[e];
-        int64_t seg_end = seg_start + a.counts[e];
-        seg_end = seg_end < a.cap ? seg_end : a.cap;
-        const int64_t row0 = seg_start + static_cast<int64_t>(mtile) * BM;
-        const int64_t nrows64 = seg_end - row0;
-        const uint32_t nrows = static_cast<uint32_t>(nrows64 < BM ? nrows64 : BM);
-
-        // waves 0,1 stream A (NBLK/2 blocks each), waves 2,3 stream B
-        const bool loads_a = wv < 2;
-        const uint16_t* dbase;
-        uint32_t dbytes;
-        if (loads_a) {
-            // rows past the segment end fall outside the resource: they read as zeros
-            dbase = a.A + row0 * a.K;
-            dbytes = nrows * row_bytes;
-        } else if (W8) {
-            const int64_t rows = UP ? 2 * a.N : a.N;
-            dbase = reinterpret_cast<const uint16_t*>(a.B8 + static_cast<int64_t>(e) * rows * a.K);
-            dbytes = static_cast<uint32_t>(rows * a.K);
-        } else if (UP) {
-            dbase = a.B + static_cast<int64_t>(e) * 2 * a.N * a.K;
-            dbytes = static_cast<uint32_t>(2 * a.N) * row_bytes;
-        } else {
-            dbase = a.B + static_cast<int64_t>(e) * a.N * a.K;
-            dbytes = static_cast<uint32_t>(a.N) * row_bytes;
-        }
-        const __amdgpu_buffer_rsrc_t rsrc = gemm::make_rsrc_uniform(dbase, dbytes);
-        // bytes per operand row: fp8 weight rows are K bytes
-        const uint32_t op_row_bytes = (W8 && !loads_a) ? static_cast<uint32_t>(a.K) : row_bytes;
-        // DMA p of this wave covers tile rows r = ((wv & 1) * LPW + p) * RPB + dma_row.  Its
-        // global row is row(p = 0) + p * RPB for every operand (A rows; up: gate or up half,
-        // chosen by wv & 1; down: w2 rows), and its swizzled chunk depends only on p's parity
-        // (swz(r) = (r / 2) mod 8 with RPB = 8), so two base offsets plus a scalar row step
-        // give all LPW offsets.  The row stays in voffset: the descriptor's range check on it
-        // is what zero-fills rows past the segment end.
-        static_assert(RPB == 8 && BK == 64, "offset scheme assumes 8-row DMA blocks");
-        uint32_t vbase[2];
-#pragma unroll
-        for (int par = 0; par < 2; ++par) {
-            const int r = ((wv & 1) * LPW + par) * RPB + dma_row;  // tile row of DMA p = par
-            uint32_t grow;
-            if (loads_a) grow = static_cast<uint32_t>(r - par * RPB);
-            else if (UP) grow = static_cast<uint32_t>((wv & 1) * a.N + nt * UP_COLS + dma_row);
-            else grow = static_cast<uint32_t>(nt * BN + (wv & 1) * LPW * RPB + dma_row);
-            vbase[par] = grow * op_row_bytes + static_cast<uint32_t>(((lane % CPR) ^ swz(r)) * 16);
-        }
-        const uint32_t rstep = static_cast<uint32_t>(RPB) * op_row_bytes;
-        // A waves: issue(buf, kt) fills stage kt % 2 (= buf) with slice kt, K bytes
-        // [128 kt, +128).  fp8 weight waves: a weight stage holds slices (2m, 2m+1), bytes
-        // [128 m, +128) of the fp8 rows, in stage m % 2; issue_b(t) loads the pair starting at
-        // even slice t.  It is called after the barrier of odd slices kt, for t = kt + 3: the
-        // stage's previous pair (kt - 1, kt) has been read by then, so the pair is in flight
-        // for two slices before its first half-slice is read.
-        auto issue_dma = [&](int stage_off, int soff) {
-            // the LDS base and the two offset bases are made opaque per call so the LPW
-            // offsets are recomputed here (one add each) instead of being hoisted out of the
-            // K loop into LPW registers
-            int off = stage_off + (wv & 1) * LPW * 512;
-            uint32_t vb0 = vbase[0], vb1 = vbase[1];
-            asm volatile("" : "+s"(off), "+v"(vb0), "+v"(vb1));
-            uint16_t* base = (loads_a ? &As[0][0] : &Bs[0][0]) + off;
-#pragma unroll
-            for (int p = 0; p < LPW; ++p) {
-                const uint32_t vo = ((p & 1) ? vb1 : vb0) + static_cast<uint32_t>(p) * rstep;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (gemm::lds_void_t*)(base + p * 512), 16, vo,
-                                                        soff, 0, 0);
-            }
-        };
-        auto issue = [&](int buf, int64_t kt) {
-            if (W8 && !loads_a) return;
-            issue_dma(buf * (BM * BK), static_cast<int>(kt * BK * 2));
-        };
-        auto issue_b = [&](int64_t t) {
-            if (!W8 || loads_a) return;
-            issue_dma(static_cast<int>((t >> 1) & 1) * (BN * BK), static_cast<int>(t * BK));
-        };
-
-        floatx16_t acc[4][4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-
-        const uint16_t* a_rd = &As[0][0] + (wm * 128 + frow) * BK;
-        const uint16_t* b_rd = &Bs[0][0] + frow * BK;
-        const uint8_t* b8_rd = reinterpret_cast<const uint8_t*>(&Bs[0][0]) + frow * 128;
-        // fp8 block scale of B block j for slice kt (K group kt / 2): up -> blocks 0,1 use
-        // the gate half's scale of i-block nt, 2,3 the up half's; down -> column block
-        // 2 nt + wn (the wave's 128 columns).  The prefetch after the last slice asks for
-        // slice KT: its fragments are never used, and the index stays inside the row.
-        auto wscale = [&](int j, int64_t kt) -> float {
-            if (!W8) return 1.f;
-            const int64_t kg = (kt >> 1) < KG ? (kt >> 1) : KG - 1;
-            return sbuf[UP ? (j >> 1) : wn][kg];
-        };
-        // B block j of the wave: up -> blocks 0,1 gate, 2,3 the matching up rows
-#define MOE_BROW(j) (UP ? ((j) >> 1) * UP_COLS + wn * 64 + ((j) & 1) * 32 : wn * 128 + (j) * 32)
-        // fragments of one half slice (K 32 = two 16-deep MFMA steps) from stage BUF
-#define MOE_LOAD_HALF(FA, FB, BUF, HALF, SLICE, SPAR)                                         \
-    do {                                                                                      \
-        const uint16_t* Ab_ = a_rd + (BUF) * (BM * BK);                                       \
-        const uint16_t* Bb_ = b_rd + (BUF) * (BN * BK);                                       \
-        if (W8) {                                                                             \
-            _Pragma("unroll") for (int ks_ = 0; ks_ < 2; ++ks_)                               \
-                _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) FA[ks_][i_] =                \
-                    *reinterpret_cast<const bf16x8_t*>(Ab_ + i_ * 32 * BK + fchunk8[HALF][ks_]); \
-            _Pragma("unroll") for (int j_ = 0; j_ < 4; ++j_) {                                \
-                const uint4 raw_ = *reinterpret_cast<const uint4*>(                           \
-                    b8_rd + (((SLICE) >> 1) & 1) * (BN * 128) + MOE_BROW(j_) * 128 +          \
-                    ((4 * (SPAR) + 2 * (HALF) + (lane >> 5)) ^ swz(frow)) * 16);              \
-                const float sc_ = wscale(j_, SLICE);                                          \
-                FB[0][j_] = dequant8(make_uint2(raw_.x, raw_.y), sc_);                        \
-                FB[1][j_] = dequant8(make_uint2(raw_.z, raw_.w), sc_);                        \
-            }                                                                                 \
-        } else {                                                                              \
-            _Pragma("unroll") for (int ks_ = 0; ks_ < 2; ++ks_) {                             \
-                _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) FA[ks_][i_] =                \
-                    *reinterpret_cast<const bf16x8_t*>(Ab_ + i_ * 32 * BK + fchunk[2 * (HALF) + ks_]); \
-                _Pragma("unroll") for (int j_ = 0; j_ < 4; ++j_) FB[ks_][j_] =                \
-                    *reinterpret_cast<const bf16x8_t*>(Bb_ + MOE_BROW(j_) * BK + fchunk[2 * (HALF) + ks_]); \
-            }                                                                                 \
-        }                                                                                     \
-    } while (0)
-#define MOE_MFMA_HALF(FA, FB)                                                                 \
-    do {                                                                                      \
-        _Pragma("unroll") for (int ks_ = 0; ks_ < 2; ++ks_)                                   \
-            _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_)                                  \
-                _Pragma("unroll") for (int j_ = 0; j_ < 4; ++j_) acc[i_][j_] =                \
-                    __builtin_amdgcn_mfma_f32_32x32x16_bf16(FB[ks_][j_], FA[ks_][i_],         \
-                                                            acc[i_][j_], 0, 0, 0);            \
-    } while (0)
-        // Pipeline: K slices of BK in two LDS stages; slice kt lives in stage kt % 2 and is
-        // consumed in two halves, each half's fragments read while the previous half's MFMAs
-        // run.  fp8 weights: one barrier per slice (before its second half) proves both that
-        // slice kt+1 has landed and that every wave has finished reading stage kt % 2, which
-        // is then refilled with slice kt+2.  bf16 weights: the same for A at the mid-slice
-        // barrier; B has its own barrier at the slice end, after which B(kt+1)'s first-half
-        // fragments are read and B(kt+2) is issued.  Every slice issues exactly one refill
-        // per operand (past the last slice it re-reads the last one, never consumed), so the
-        // in-flight count at each wait is known.
-        const int64_t KT = a.K / BK;
-        // the previous tile's trailing DMAs and every wave's reads of the stage buffers are done
-        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-        __syncthreads();
-        if (W8) {
-            for (int t = tid; t < 2 * KG; t += M_THREADS) {
-                const int r = t / static_cast<int>(KG), kg = t % static_cast<int>(KG);
-                sbuf[r][kg] = UP ? a.SB[((static_cast<int64_t>(e) * 2 + r) * NB + nt) * KG + kg]
-                                 : a.SB[(static_cast<int64_t>(e) * NB + 2 * nt + r) * KG + kg];
-            }
-            // the prologue barrier below publishes sbuf; its loads are drained here so the
-            // DMA counts that follow start from zero
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        }
-        if constexpr (W8) {
-            issue(0, 0);
-            issue(1, KT > 1 ? 1 : 0);
-            issue_b(0);
-            issue_b(KT > 2 ? 2 : 0);
-            // slice 0 landed: every wave has exactly LPW DMAs issued after it
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPW) : "memory");
-        } else {
-            // A waves: slices 0 and 1 in flight; B waves: slice 0 (slice 1 follows in slice 0)
-            issue(0, 0);
-            if (loads_a) {
-                issue(1, KT > 1 ? 1 : 0);
-                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPW) : "memory");
-            } else {
-                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            }
-        }
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-        bf16x8_t f0a[2][4], f0b[2][4], f1a[2][4], f1b[2][4];
-        MOE_LOAD_HALF(f0a, f0b, 0, 0, 0, 0);
-        // Within each half the scheduler interleaves one fragment read (and, in the second
-        // half, one DMA issue) with every two MFMAs, so LDS and DMA traffic spread over the
-        // half and few reads are outstanding when the next half starts.
-#define MOE_INTERLEAVE(WITH_DMA)                                                              \
-    do {                                                                                      \
-        _Pragma("unroll") for (int g_ = 0; g_ < 16; ++g_) {                                   \
-            if (WITH_DMA) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                  \
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                \
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                                \
-        }                                                                                     \
-    } while (0)
-        // one slice; PAR = kt % 2 is a compile-time constant (the loop below steps by two
-        // and KT is even), which is also the slice's stage
-#define MOE_SLICE(KT_, PAR)                                                                   \
-    do {                                                                                      \
-        __builtin_amdgcn_sched_barrier(0);                                                    \
-        MOE_LOAD_HALF(f1a, f1b, PAR, 1, KT_, PAR);                                            \
-        MOE_MFMA_HALF(f0a, f0b);                                                              \
-        MOE_INTERLEAVE(false);                                                                \
-        __builtin_amdgcn_sched_barrier(0);                                                    \
-        /* slice KT_+1 landed and every wave is done reading stage PAR; at even slices the   \
-           fp8 weight waves' newest pair is not needed before the next barrier */            \
-        if (W8 && (PAR) == 0 && !loads_a)                                                     \
-            asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(LPW) : "memory");            \
-        else                                                                                  \
-            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");                      \
-        __builtin_amdgcn_s_barrier();                                                         \
-        __builtin_amdgcn_sched_barrier(0);                                                    \
-        issue(PAR, (KT_) + 2 < KT ? (KT_) + 2 : KT - 1);                                      \
-        if ((PAR) == 1) issue_b((KT_) + 3 < KT ? (KT_) + 3 : KT - 2);                         \
-        MOE_LOAD_HALF(f0a, f0b, (PAR) ^ 1, 0, (KT_) + 1, (PAR) ^ 1);                          \
-        MOE_MFMA_HALF(f1a, f1b);                                                              \
-        MOE_INTERLEAVE(true);                                                                 \
-        __builtin_amdgcn_sched_barrier(0);                                                    \
-    } while (0)
-        if constexpr (W8) {
-            for (int64_t kt = 0; kt < KT; kt += 2) {
-                MOE_SLICE(kt, 0);
-                MOE_SLICE(kt + 1, 1);
-            }
-        } else {
-            // bf16 weights: A is refilled after a mid-slice barrier and B after an end-of-slice
-            // barrier, so at every barrier the other operand's DMAs are still in flight and
-            // the CU's memory queue never drains.  A-loading and B-loading waves run separate
-            // copies of the loop (their DMA points and waits differ) with the same barriers.
-#define MOE_LOAD_A(FA, BUF, HALF)                                                              \
-    _Pragma("unroll") for (int ks_ = 0; ks_ < 2; ++ks_)                                       \
-        _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) FA[ks_][i_] =                        \
-            *reinterpret_cast<const bf16x8_t*>(a_rd + (BUF) * (BM * BK) + i_ * 32 * BK + fchunk[2 * (HALF) + ks_])
-#define MOE_LOAD_B(FB, BUF, HALF)                                                              \
-    _Pragma("unroll") for (int ks_ = 0; ks_ < 2; ++ks_)                                       \
-        _Pragma("unroll") for (int j_ = 0; j_ < 4; ++j_) FB[ks_][j_] =                        \
-            *reinterpret_cast<const bf16x8_t*>(b_rd + (BUF) * (BN * BK) + MOE_BROW(j_) * BK + fchunk[2 * (HALF) + ks_])
-#define MOE_SLICE2(KT_, PAR, IS_A)                                                             \
-    do {                                                                                       \
-        __builtin_amdgcn_sched_barrier(0);                                                     \
-        MOE_LOAD_A(f1a, PAR, 1);                                                               \
-        MOE_LOAD_B(f1b, PAR, 1);                                                               \
-        if (!(IS_A)) issue((PAR) ^ 1, (KT_) + 1 < KT ? (KT_) + 1 : KT - 1);                   \
-        MOE_MFMA_HALF(f0a, f0b);                                                               \
-        _Pragma("unroll") for (int g_ = 0; g_ < 16; ++g_) {                                    \
-            if (!(IS_A)) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                    \
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                 \
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                                 \
-        }                                                                                      \
-        __builtin_amdgcn_sched_barrier(0);                                                     \
-        if (IS_A) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");                  \
-        else asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");                                \
-        __builtin_amdgcn_s_barrier();                                                          \
-        __builtin_amdgcn_sched_barrier(0);                                                     \
-        if (IS_A) issue(PAR, (KT_) + 2 < KT ? (KT_) + 2 : KT - 1);                             \
-        MOE_LOAD_A(f0a, (PAR) ^ 1, 0);                                                         \
-        MOE_MFMA_HALF(f1a, f1b);                                                               \
-        _Pragma("unroll") for (int g_ = 0; g_ < 16; ++g_) {                                    \
-            if (IS_A) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                       \
-            if (g_ % 2 == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                \
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                                 \
-        }                                                                                      \
-        __builtin_amdgcn_sched_barrier(0);                                                     \
-        if (IS_A) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");                           \
-        else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");                       \
-        __builtin_amdgcn_s_barrier();                                                          \
-        __builtin_amdgcn_sched_barrier(0);                                                     \
-        MOE_LOAD_B(f0b, (PAR) ^ 1, 0);                                                         \
-    } while (0)
-            if (loads_a) {
-                for (int64_t kt = 0; kt < KT; kt += 2) {
-                    MOE_SLICE2(kt, 0, true);
-                    MOE_SLICE2(kt + 1, 1, true);
-                }
-            } else {
-                for (int64_t kt = 0; kt < KT; kt += 2) {
-                    MOE_SLICE2(kt, 0, false);
-                    MOE_SLICE2(kt + 1, 1, false);
-                }
-            }
-#undef MOE_SLICE2
-#undef MOE_LOAD_A
-#undef MOE_LOAD_B
-        }
-#undef MOE_SLICE
-#undef MOE_INTERLEAVE
-#undef MOE_MFMA_HALF
-#undef MOE_LOAD_HALF
-#undef MOE_BROW
-
-        // ---- epilogue: the weight fragment is the MFMAs' first operand, so each 32x32
-        // accumulator block holds its output block transposed: lane l owns row l%32 of the
-        // block and, for q = 0..3, its four consecutive columns 8*q + 4*(l/32) + 0..3, which
-        // go out as one 8-byte store (a row's 16 bytes at each q come from lanes l and l+32).
-        const int rloc = wm * 128 + (lane & 31);
-        const int64_t colbase = UP ? static_cast<int64_t>(nt) * UP_COLS + wn * 64 + (lane >> 5) * 4
-                                   : static_cast<int64_t>(nt) * BN + wn * 128 + (lane >> 5) * 4;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if (rloc + i * 32 >= static_cast<int>(nrows)) continue;
-            uint16_t* cp = a.C + (row0 + rloc + i * 32) * a.N + colbase;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                if (UP) {
-#pragma unroll
-                    for (int j = 0; j < 2; ++j) {
-                        float h[4];
-#pragma unroll
-                        for (int t = 0; t < 4; ++t) h[t] = silu_mul(acc[i][j][4 * q + t], acc[i][j + 2][4 * q + t]);
-                        *reinterpret_cast<uint2*>(cp + j * 32 + q * 8) =
-                            make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
-                    }
-                } else {
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const floatx16_t& c = acc[i][j];
-                        *reinterpret_cast<uint2*>(cp + j * 32 + q * 8) =
-                            make_uint2(pack_bf16x2(c[4 * q], c[4 * q + 1]), pack_bf16x2(c[4 * q + 2], c[4 * q + 3]));
-                    }
-                }
-            }
-        }
-    }
-    // no DMA into LDS may outlive the workgroup
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-}
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
 // ------------------------------------------------------------------ bf16: 8-wave ping-pong
 // bf16 weights.  The same 256 x 256 tiles, tile order and accumulation order as
-// grouped_gemm_bf16_kernel (so the same bits), with 8 waves, two per SIMD: waves w and w + 4
+// the earlier 4-wave form (so the same bits), with 8 waves, two per SIMD: waves w and w + 4
 // share SIMD w % 4 and its 128 x 128 region, and each owns two of the region's four 32-column
 // blocks (up: gate block g and its up block g + 2; down: blocks 2g, 2g + 1), i.e. 128 x 64
 // outputs in 128 accumulators per lane, so two such waves fit in the register file.
@@ -497,6 +109,12 @@ __global__ __launch_bounds__(M_THREADS, 1) void grouped_gemm_bf16_kernel(GemmArg
 // wave waits until only its two newest DMA groups (slices n + 2, n + 3) are in flight, so
 // slice n + 1 has landed when group 0 reads it in phase 2n + 1.  Group 1 starts one barrier
 // late and group 0 ends one barrier late, so every wave passes the same barriers.
+// fp8 weights (W8): a stage's weight rows are 32 fp8 bytes (8 KB for the tile, 2 DMAs of 32
+// rows per group-1 wave and slice, so group 1 waits for vmcnt 4 where group 0 waits for 8);
+// in its memory phase a wave reads 16 bytes per weight block, dequantises them with the
+// block's scale (staged in LDS at tile start) into the fragments of both MFMA steps, and
+// reads its activation fragments in the matching K order.  The MFMAs are the bf16 ones.
+// fp8 weights take every slot (there is no streaming form for them).
 constexpr int ST_BM_SPLIT = 64;  // slots with more rows than this run here, the rest in the streaming kernel
 constexpr int PP_THREADS = 512;
 constexpr int PP_BK = 32;                        // K per slice
@@ -509,13 +127,21 @@ static_assert(PP_LPW == 4 && PP_RPB == 16, "the wait counts below assume 4 DMAs 
 // fragment read has 16 consecutive 64-byte rows asking for the same logical chunk, and the
 // xor with (row / 4) mod 4 puts them on 16 distinct 16-byte slots of a 256-byte window
 __device__ __forceinline__ int pp_swz(int row) { return (row >> 2) & 3; }
+// fp8 weights: a stage's weight rows are 32 bytes; a fragment read has 16 consecutive rows
+// asking for the same 16-byte half, and swapping the halves on every other group of 8 rows
+// puts them on 16 distinct 16-byte slots of a 256-byte window
+__device__ __forceinline__ int w8_swz(int row) { return (row >> 3) & 1; }
+constexpr int PP_W8DMA = 2;                      // fp8 weight DMAs (32 rows x 32 bytes) per wave and slice
 
-template <bool UP>
+template <bool UP, bool W8>
 __global__ __launch_bounds__(PP_THREADS, 1) void grouped_gemm_pp_kernel(GemmArgs a, gemm::TileOrder to) {
     __shared__ __attribute__((aligned(1024))) uint16_t As[PP_STAGES][BM * PP_BK];
     __shared__ __attribute__((aligned(1024))) uint16_t Bs[PP_STAGES][BN * PP_BK];
     __shared__ int32_t tile_prefix[gemm::kMaxSlots + 1];
     __shared__ int32_t part[PP_THREADS];
+    // fp8 weights: the tile's weight block scales along K, [2][K/128] (up: gate, up half;
+    // down: the two 128-column blocks of the tile), staged at tile start
+    __shared__ float sbuf[W8 ? 2 : 1][W8 ? kMaxKG8 : 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -525,7 +151,8 @@ __global__ __launch_bounds__(PP_THREADS, 1) void grouped_gemm_pp_kernel(GemmArgs
     const int wm = sq >> 1, wn = sq & 1;
 
     const int32_t total_mt =
-        gemm::number_tiles<BM, PP_THREADS>(a.counts, a.seg, a.cap, a.El, tile_prefix, part, ST_BM_SPLIT);
+        gemm::number_tiles<BM, PP_THREADS>(a.counts, a.seg, a.cap, a.El, tile_prefix, part,
+                                           W8 ? 0 : ST_BM_SPLIT);  // fp8 weights: every slot
     const uint32_t row_bytes = static_cast<uint32_t>(a.K) * 2u;
     const int nsn = a.NT / to.SN;
     const int64_t total_super = static_cast<int64_t>((total_mt + to.SM - 1) / to.SM) * nsn;
@@ -538,6 +165,14 @@ __global__ __launch_bounds__(PP_THREADS, 1) void grouped_gemm_pp_kernel(GemmArgs
     int fchunk[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) fchunk[ks] = ((2 * ks + (lane >> 5)) ^ pp_swz(frow)) * 8;
+    // fp8 weights: a lane reads 16 weight bytes of its row at K 16 (lane / 32) of the slice and
+    // feeds the first 8 to step 0, the last 8 to step 1; the activation fragments follow (step
+    // ks of lane half h: K 16 h + 8 ks .. + 8), so every product still pairs equal K
+    if constexpr (W8) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) fchunk[ks] = ((2 * (lane >> 5) + ks) ^ pp_swz(frow)) * 8;
+    }
+    const int64_t KG = a.K / 128, NB = a.N / 128;
     // LDS rows of the wave's two weight column blocks
     int brow[2];
 #pragma unroll
@@ -568,6 +203,10 @@ __global__ __launch_bounds__(PP_THREADS, 1) void grouped_gemm_pp_kernel(GemmArgs
             // rows past the segment end fall outside the resource: they read as zeros
             dbase = a.A + row0 * a.K;
             dbytes = nrows * row_bytes;
+        } else if (W8) {
+            const int64_t rows = UP ? 2 * a.N : a.N;
+            dbase = reinterpret_cast<const uint16_t*>(a.B8 + static_cast<int64_t>(e) * rows * a.K);
+            dbytes = static_cast<uint32_t>(rows * a.K);
         } else if (UP) {
             dbase = a.B + static_cast<int64_t>(e) * 2 * a.N * a.K;
             dbytes = static_cast<uint32_t>(2 * a.N) * row_bytes;
@@ -584,9 +223,32 @@ __global__ __launch_bounds__(PP_THREADS, 1) void grouped_gemm_pp_kernel(GemmArgs
         if (loads_a) grow = static_cast<uint32_t>(r0);
         else if (UP) grow = static_cast<uint32_t>((r0 >= 128 ? a.N : 0) + nt * UP_COLS + (r0 & 127));
         else grow = static_cast<uint32_t>(nt * BN + r0);
-        const uint32_t vbase = grow * row_bytes + static_cast<uint32_t>(((lane % PP_CPR) ^ pp_swz(r0)) * 16);
-        const uint32_t rstep = static_cast<uint32_t>(PP_RPB) * row_bytes;
+        uint32_t vbase = grow * row_bytes + static_cast<uint32_t>(((lane % PP_CPR) ^ pp_swz(r0)) * 16);
+        uint32_t rstep = static_cast<uint32_t>(PP_RPB) * row_bytes;
+        if (W8 && !loads_a) {
+            // fp8 weight rows are K bytes, 32 per slice: a DMA covers 32 rows x 32 bytes, lane
+            // pair per row, wave sq tile rows 64 sq + 32 p + lane / 2; the 16-byte halves of a
+            // row trade places on every other group of 8 rows (w8_swz), the same for both p
+            const int rr = 64 * sq + lane / 2;
+            const uint32_t g8 = UP ? static_cast<uint32_t>((rr >= 128 ? a.N : 0) + nt * UP_COLS + (rr & 127))
+                                   : static_cast<uint32_t>(nt * BN + rr);
+            vbase = g8 * static_cast<uint32_t>(a.K) + static_cast<uint32_t>(((lane & 1) ^ w8_swz(rr)) * 16);
+            rstep = 32u * static_cast<uint32_t>(a.K);
+        }
         auto issue = [&](int stage, int64_t kt) {
+            if constexpr (W8) {
+                if (!loads_a) {
+                    uint8_t* b8 = reinterpret_cast<uint8_t*>(&Bs[0][0]) + stage * (BN * PP_BK * 2) + sq * PP_W8DMA * 1024;
+                    uint32_t vb8 = vbase;
+                    asm volatile("" : "+s"(b8), "+v"(vb8));
+#pragma unroll
+                    for (int p = 0; p < PP_W8DMA; ++p)
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (gemm::lds_void_t*)(b8 + p * 1024), 16,
+                                                                vb8 + static_cast<uint32_t>(p) * rstep,
+                                                                static_cast<int>(kt * PP_BK), 0, 0);
+                    return;
+                }
+            }
             int off = stage * (BM * PP_BK) + sq * PP_LPW * 512;
             uint32_t vb = vbase;
             asm volatile("" : "+s"(off), "+v"(vb));
@@ -609,7 +271,31 @@ __global__ __launch_bounds__(PP_THREADS, 1) void grouped_gemm_pp_kernel(GemmArgs
         const uint16_t* b_rd = &Bs[0][0] + frow * PP_BK;
         bf16x8_t fa[2][4], fb[2][2];
         // fragments of the slice in `stage`: two 16-deep MFMA steps
-        auto read_slice = [&](int stage) {
+        // fp8 block scale of the wave's weight block jj in K group kg (up: gate half, up half;
+        // down: the 128-column block wn)
+        auto wscale = [&](int jj, int64_t kt) -> float {
+            const int64_t kg = kt / (128 / PP_BK);
+            return sbuf[UP ? jj : wn][kg];
+        };
+        auto read_slice = [&](int stage, int64_t kt) {
+            if constexpr (W8) {
+                const uint8_t* b8 = reinterpret_cast<const uint8_t*>(&Bs[0][0]) + stage * (BN * PP_BK * 2);
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        fa[ks][i] = *reinterpret_cast<const bf16x8_t*>(a_rd + stage * (BM * PP_BK) + i * 32 * PP_BK +
+                                                                       fchunk[ks]);
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj) {
+                    const int row = brow[jj] + frow;
+                    const uint4 raw = *reinterpret_cast<const uint4*>(b8 + row * 32 + (((lane >> 5) ^ w8_swz(row)) * 16));
+                    const float sc = wscale(jj, kt);
+                    fb[0][jj] = dequant8(make_uint2(raw.x, raw.y), sc);
+                    fb[1][jj] = dequant8(make_uint2(raw.z, raw.w), sc);
+                }
+                return;
+            }
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
@@ -643,23 +329,38 @@ __global__ __launch_bounds__(PP_THREADS, 1) void grouped_gemm_pp_kernel(GemmArgs
 
         const int64_t KT = a.K / PP_BK;
         // the previous tile's output stores are done; every wave passed the previous tile's
-        // last barrier, so no wave still reads a stage
-        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        // last barrier, so no wave still reads a stage.  The intrinsic (all counters to zero)
+        // rather than inline asm: the compiler's own wait tracking sees it, and no longer
+        // carries the epilogue's stores into the K loop (where it would drain every DMA in
+        // flight before reusing a register the stores read)
+        __builtin_amdgcn_s_waitcnt(0);
+        asm volatile("" ::: "memory");
+        if constexpr (W8) {
+            for (int t = tid; t < 2 * KG; t += PP_THREADS) {
+                const int r = t / static_cast<int>(KG), kg = t % static_cast<int>(KG);
+                sbuf[r][kg] = UP ? a.SB[((static_cast<int64_t>(e) * 2 + r) * NB + nt) * KG + kg]
+                                 : a.SB[(static_cast<int64_t>(e) * NB + 2 * nt + r) * KG + kg];
+            }
+            // the prologue barrier below publishes sbuf; its loads end here, so the DMA
+            // counts that follow start from zero
+            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        }
         issue(0, 0);
         issue(1, KT > 1 ? 1 : KT - 1);
         issue(2, KT > 2 ? 2 : KT - 1);
         // slice 0 landed: each wave's two newest groups may still be in flight
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * PP_LPW) : "memory");
+        if (W8 && g == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * PP_W8DMA) : "memory");
+        else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * PP_LPW) : "memory");
         phase_end();
         if (g == 1) phase_end();
         for (int64_t n = 0; n < KT; ++n) {
             const int st = static_cast<int>(n & (PP_STAGES - 1));
             // memory phase: this slice's fragments, the DMAs of slice n + 3
-            read_slice(st);
+            read_slice(st, n);
             issue((st + 3) & (PP_STAGES - 1), n + 3 < KT ? n + 3 : KT - 1);
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             // group 1: slice n + 1 landed before the barrier that ends phase 2n
-            if (g == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * PP_LPW) : "memory");
+            if (g == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * (W8 ? PP_W8DMA : PP_LPW)) : "memory");
             phase_end();
             // compute phase
             mfma_slice();
@@ -668,7 +369,7 @@ __global__ __launch_bounds__(PP_THREADS, 1) void grouped_gemm_pp_kernel(GemmArgs
         }
         if (g == 0) phase_end();
 
-        // ---- epilogue, as in grouped_gemm_bf16_kernel, over the wave's two column blocks
+        // ---- epilogue over the wave's two column blocks
         const int rloc = wm * 128 + (lane & 31);
         const int64_t colbase = UP ? static_cast<int64_t>(nt) * UP_COLS + wn * 64 + (lane >> 5) * 4
                                    : static_cast<int64_t>(nt) * BN + wn * 128 + (lane >> 5) * 4;
@@ -707,7 +408,7 @@ __global__ __launch_bounds__(PP_THREADS, 1) void grouped_gemm_pp_kernel(GemmArgs
 // its rate is set by the bytes per request.  Here a tile is 64 rows x 128 weight rows (up: 64
 // gate + the same 64 up columns; down: 128 columns), so a decode batch whose routed rows sit
 // in a few slots still has a tile for every CU, in 64-deep slices (whole lines, with the
-// swizzle of grouped_gemm_bf16_kernel): five 24 KB stages, four slices in flight.  Four
+// swizzle swz below): five 24 KB stages, four slices in flight.  Four
 // waves, one per SIMD: wave w owns rows 32 (w mod 2) .. + 31 and column group w / 2 (up:
 // gate block and up block of 32 columns; down: two 32-column blocks).  Per slice each wave
 // DMAs two activation blocks and four weight blocks of 8 rows (all gate or all up), one
@@ -1017,16 +718,16 @@ moe_status run_stage(bool up, const void* A, moe_dtype act_dt, const moe_plan* p
         if (!gemm::pick_tile_order(g.NT, blocks, &to)) return MOE_ERR_UNSUPPORTED;
         const dim3 grid(static_cast<unsigned>(blocks));
         if (w8) {
-            if (up) hipLaunchKernelGGL((grouped_gemm_bf16_kernel<true, true>), grid, dim3(M_THREADS), 0, stream, g, to);
-            else hipLaunchKernelGGL((grouped_gemm_bf16_kernel<false, true>), grid, dim3(M_THREADS), 0, stream, g, to);
+            if (up) hipLaunchKernelGGL((grouped_gemm_pp_kernel<true, true>), grid, dim3(PP_THREADS), 0, stream, g, to);
+            else hipLaunchKernelGGL((grouped_gemm_pp_kernel<false, true>), grid, dim3(PP_THREADS), 0, stream, g, to);
         } else {
             // slots of at most 64 rows stream their weights in 64-row tiles, the rest run the
             // ping-pong kernel; each kernel numbers its own slots' tiles on the device
             if (up) hipLaunchKernelGGL((grouped_gemm_stream_kernel<true>), grid, dim3(ST_THREADS), 0, stream, g);
             else hipLaunchKernelGGL((grouped_gemm_stream_kernel<false>), grid, dim3(ST_THREADS), 0, stream, g);
             MOE_LAUNCH_CHECK();
-            if (up) hipLaunchKernelGGL((grouped_gemm_pp_kernel<true>), grid, dim3(PP_THREADS), 0, stream, g, to);
-            else hipLaunchKernelGGL((grouped_gemm_pp_kernel<false>), grid, dim3(PP_THREADS), 0, stream, g, to);
+            if (up) hipLaunchKernelGGL((grouped_gemm_pp_kernel<true, false>), grid, dim3(PP_THREADS), 0, stream, g, to);
+            else hipLaunchKernelGGL((grouped_gemm_pp_kernel<false, false>), grid, dim3(PP_THREADS), 0, stream, g, to);
         }
         MOE_LAUNCH_CHECK();
         return MOE_OK;

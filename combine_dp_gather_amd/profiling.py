@@ -11,7 +11,7 @@
     # scaled by what the same counter reads for a plain device copy of known size made in the
     # same process (bench.py --copy-calibration MIB)
     python -m combine_dp_gather_amd.profiling traffic --fetch F.csv --write W.csv \
-        --copy-mib 1024 --kernel grouped_gemm_bf16_kernel<true> --sources a.hip b.h --cmd "..."
+        --copy-mib 1024 --kernel grouped_gemm_pp_kernel<true, false> --sources a.hip b.h --cmd "..."
 
 The traffic summary records a SHA-256 over the kernel's source files; bench.py reports the
 figure only while the sources still hash to it (counters taken on an older kernel say
