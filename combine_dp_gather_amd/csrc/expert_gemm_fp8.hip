@@ -66,13 +66,15 @@ __global__ __launch_bounds__(256) void quant_fp8_kernel(const uint16_t* __restri
 }
 
 // ------------------------------------------------------------------ fp8 grouped GEMM
-constexpr int F_BM = 256, F_BN = 128;
-constexpr int F_STAGES = 3;
+constexpr int F_BM = 256, F_BN = 256;
+constexpr int F_THREADS = 512;               // 8 waves, two per SIMD
+constexpr int F_STAGES = 2;
 constexpr int F_ROW = 128;                   // bytes per LDS row (one K group of fp8)
 constexpr int F_A_BLKS = F_BM * F_ROW / 1024;  // 1 KB DMA blocks of A per stage (32)
-constexpr int F_B_BLKS = F_BN * F_ROW / 1024;  // (16)
-constexpr int F_LPW = F_A_BLKS / 4 + F_B_BLKS / 4 + 1;  // DMAs per wave per stage (+1: scales)
-constexpr int F_UP_COLS = F_BN / 2;          // up: 64 gate + 64 up columns
+constexpr int F_B_BLKS = F_BN * F_ROW / 1024;  // (32)
+constexpr int F_DPW = (F_A_BLKS + F_B_BLKS) / 8;  // operand DMAs per wave per stage (8)
+constexpr int F_UP_COLS = F_BN / 2;          // up: 128 gate + 128 up columns
+constexpr int kMaxKG8 = 128;                 // K groups whose weight scales a tile stages (K <= 16384)
 
 __device__ __forceinline__ int fswz(int row) { return (row >> 1) & 7; }
 
@@ -90,20 +92,33 @@ struct Fp8Args {
 
 __device__ __forceinline__ float silu_mul8(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
 
+// 8 waves in a 2 x 4 grid over the 256 x 256 tile: wave w owns rows 128 (w mod 2) .. + 127
+// and column group w / 2 (up: gate block w / 2 of 32 columns and the same up block; down:
+// 64 columns, blocks 2 (w / 2), + 1): 4 x 2 accumulator blocks of 32 x 32, 128 per lane.
+// The weight fragment is the MFMAs' first operand, so a block's lane holds one token row
+// (lane mod 32) and four consecutive output columns per register group: one activation scale
+// per lane and row block, one weight scale per column block, and 8-byte output stores.  A
+// stage is one 128-deep K group (A and B 32 KB each, plus the group's 256 activation
+// scales); the group's two MFMAs per block accumulate into a fresh partial that is promoted
+// at once (acc += partial * s_a * s_w), so no second set of accumulators is held.  The
+// activation fragments are read one row block ahead of its MFMAs (32 registers), the weight
+// fragments for the whole group (32).  Two stages: group kg + 1 is DMA'd while group kg is
+// consumed; one barrier per group.
 template <bool UP>
-__global__ __launch_bounds__(gemm::kThreads, 1) void grouped_gemm_fp8_kernel(Fp8Args a, gemm::TileOrder to) {
+__global__ __launch_bounds__(F_THREADS, 1) void grouped_gemm_fp8_kernel(Fp8Args a, gemm::TileOrder to) {
     __shared__ __attribute__((aligned(1024))) uint8_t As[F_STAGES][F_BM * F_ROW];
     __shared__ __attribute__((aligned(1024))) uint8_t Bs[F_STAGES][F_BN * F_ROW];
     __shared__ __attribute__((aligned(16))) float Ss[F_STAGES][F_BM];
     __shared__ int32_t tile_prefix[gemm::kMaxSlots + 1];
-    __shared__ int32_t part[gemm::kThreads];
+    __shared__ int32_t part[F_THREADS];
+    __shared__ float sw_lds[2][kMaxKG8];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wv >> 1, wn = wv & 1;
+    const int wm = wv & 1, wn = wv >> 1;
 
-    const int32_t total_mt = gemm::number_tiles<F_BM>(a.counts, a.seg, a.cap, a.El, tile_prefix, part);
+    const int32_t total_mt = gemm::number_tiles<F_BM, F_THREADS>(a.counts, a.seg, a.cap, a.El, tile_prefix, part);
     const uint32_t row_bytes = static_cast<uint32_t>(a.K);
     const int64_t KG = a.K / QB;  // K groups = pipeline steps
     const int64_t SKG = a.N / QB;  // weight scale blocks along the output dimension
@@ -112,7 +127,7 @@ __global__ __launch_bounds__(gemm::kThreads, 1) void grouped_gemm_fp8_kernel(Fp8
     const int xcd = blockIdx.x & 7;
     const int q = blockIdx.x >> 3;
     const int frow = lane & 31;
-    // fragment k bytes of sub-step ks: 64*ks + 32*(lane/32) .. +32 = logical chunks c, c+1
+    // fragment bytes of MFMA step ks: 64 ks + 32 (lane / 32) .. + 32 = logical chunks c, c + 1
     int fch[2][2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
@@ -139,51 +154,53 @@ __global__ __launch_bounds__(gemm::kThreads, 1) void grouped_gemm_fp8_kernel(Fp8
         const __amdgpu_buffer_rsrc_t rb = gemm::make_rsrc_uniform(a.B + e * wslot, static_cast<uint32_t>(wslot));
         const __amdgpu_buffer_rsrc_t rs = gemm::make_rsrc_uniform(
             a.SA + row0, static_cast<uint32_t>((KG * a.cap - row0) * 4));
-        // per-lane DMA offsets: A blocks 8w..8w+7, B blocks 4w..4w+3, 64 scales at 64w
-        uint32_t aoff[F_A_BLKS / 4], boff[F_B_BLKS / 4];
+        // per-lane DMA offsets: A blocks 4w..4w+3 (rows 32 w ..), B blocks 4w..4w+3 (B tile rows
+        // 32 w ..: up, waves 0-3 gate rows, 4-7 up rows); waves 0-3 also DMA 64 scales each
+        uint32_t aoff[4], boff[4];
 #pragma unroll
-        for (int p = 0; p < F_A_BLKS / 4; ++p) {
-            const int r = (wv * (F_A_BLKS / 4) + p) * 8 + (lane >> 3);
+        for (int p = 0; p < 4; ++p) {
+            const int r = (wv * 4 + p) * 8 + (lane >> 3);
             aoff[p] = static_cast<uint32_t>(r) * row_bytes + static_cast<uint32_t>(((lane & 7) ^ fswz(r)) * 16);
-        }
-#pragma unroll
-        for (int p = 0; p < F_B_BLKS / 4; ++p) {
-            const int r = (wv * (F_B_BLKS / 4) + p) * 8 + (lane >> 3);  // B tile row 0..127
             uint32_t grow;
-            if (UP) grow = static_cast<uint32_t>((r >> 6) * a.N + nt * F_UP_COLS + (r & (F_UP_COLS - 1)));
+            if (UP) grow = static_cast<uint32_t>((r >> 7) * a.N + nt * F_UP_COLS + (r & (F_UP_COLS - 1)));
             else grow = static_cast<uint32_t>(nt * F_BN + r);
             boff[p] = grow * row_bytes + static_cast<uint32_t>(((lane & 7) ^ fswz(r)) * 16);
         }
         // the scale DMA carries its K-group offset in the per-lane offset, so the descriptor's
         // range check sees it (rows at or past cap in the last group read as zeros)
+        const bool sdma = wv < 4;
         const uint32_t soff_lane = static_cast<uint32_t>((wv * 64 + lane) * 4);
         const uint32_t scap_bytes = static_cast<uint32_t>(a.cap * 4);
+        // The LDS destinations are made opaque to the compiler: its wait tracking would
+        // otherwise treat every later LDS read as dependent on every DMA in flight and drain
+        // the next group's DMAs before this group's fragment reads.  The barrier protocol
+        // below orders them instead.
+        typedef __attribute__((address_space(3))) uint8_t lds_u8;
         auto issue = [&](int buf, int64_t kg) {
-            int abase = buf * (F_BM * F_ROW) + wv * (F_A_BLKS / 4) * 1024;
-            int bbase = buf * (F_BN * F_ROW) + wv * (F_B_BLKS / 4) * 1024;
-            int sbase = buf * F_BM + wv * 64;
-            asm volatile("" : "+s"(abase), "+s"(bbase), "+s"(sbase));
+            lds_u8* ad = (lds_u8*)(&As[0][0] + buf * (F_BM * F_ROW) + wv * 4 * 1024);
+            lds_u8* bd = (lds_u8*)(&Bs[0][0] + buf * (F_BN * F_ROW) + wv * 4 * 1024);
+            lds_u8* sd = (lds_u8*)(&Ss[0][0] + buf * F_BM + wv * 64);
+            asm volatile("" : "+s"(ad), "+s"(bd), "+s"(sd));
             const int koff = static_cast<int>(kg * QB);
 #pragma unroll
-            for (int p = 0; p < F_A_BLKS / 4; ++p)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (gemm::lds_void_t*)(&As[0][0] + abase + p * 1024), 16,
-                                                        aoff[p], koff, 0, 0);
+            for (int p = 0; p < 4; ++p)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (gemm::lds_void_t*)(ad + p * 1024), 16, aoff[p], koff, 0, 0);
 #pragma unroll
-            for (int p = 0; p < F_B_BLKS / 4; ++p)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (gemm::lds_void_t*)(&Bs[0][0] + bbase + p * 1024), 16,
-                                                        boff[p], koff, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (gemm::lds_void_t*)(&Ss[0][0] + sbase), 4,
-                                                    soff_lane + static_cast<uint32_t>(kg) * scap_bytes, 0, 0, 0);
+            for (int p = 0; p < 4; ++p)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (gemm::lds_void_t*)(bd + p * 1024), 16, boff[p], koff, 0, 0);
+            if (sdma)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (gemm::lds_void_t*)sd, 4,
+                                                        soff_lane + static_cast<uint32_t>(kg) * scap_bytes, 0, 0, 0);
         };
-        // weight block scale of column block j for K group kg
-        auto wscale = [&](int j, int64_t kg) -> float {
-            if (UP) {
-                const int64_t ib = (static_cast<int64_t>(nt) * F_UP_COLS) / QB;
-                return a.SB[((static_cast<int64_t>(e) * 2 + j) * SKG + ib) * KG + kg];
-            }
-            const int64_t cb = (static_cast<int64_t>(nt) * F_BN) / QB;
-            return a.SB[(static_cast<int64_t>(e) * SKG + cb) * KG + kg];
-        };
+        // the tile's weight block scales along K, staged in LDS: up -> gate (0) and up (1)
+        // halves of i-block nt; down -> the two 128-column blocks of the tile
+        for (int t = tid; t < 2 * KG; t += F_THREADS) {
+            const int r = t / static_cast<int>(KG), kgi = t % static_cast<int>(KG);
+            sw_lds[r][kgi] = UP ? a.SB[((static_cast<int64_t>(e) * 2 + r) * SKG + nt) * KG + kgi]
+                                : a.SB[(static_cast<int64_t>(e) * SKG + 2 * nt + r) * KG + kgi];
+        }
+        // weight block scale of the wave's column block j for K group kg
+        auto wscale = [&](int j, int64_t kg) -> float { return sw_lds[UP ? j : (wn >> 1)][kg]; };
 
         floatx16_t acc[4][2];
 #pragma unroll
@@ -195,89 +212,86 @@ __global__ __launch_bounds__(gemm::kThreads, 1) void grouped_gemm_fp8_kernel(Fp8
         const floatx16_t zero = {};
 
         const uint8_t* a_rd = &As[0][0] + (wm * 128 + frow) * F_ROW;
-        // B rows of the wave's two column blocks: up -> gate rows wn*32.., up rows 64+wn*32..
+        // B rows of the wave's two column blocks
         const int brow0 = UP ? wn * 32 : wn * 64;
         const int brow1 = UP ? F_UP_COLS + wn * 32 : wn * 64 + 32;
         const uint8_t* b_rd0 = &Bs[0][0] + (brow0 + frow) * F_ROW;
         const uint8_t* b_rd1 = &Bs[0][0] + (brow1 + frow) * F_ROW;
-        // scale rows of the lane: wm*128 + 32i + 8g + 4*(lane/32) + 0..3
-        const float* s_rd = &Ss[0][0] + wm * 128 + 4 * (lane >> 5);
+        // the lane's token row in row block i: wm*128 + 32 i + lane mod 32
+        const float* s_rd = &Ss[0][0] + wm * 128 + frow;
+        auto read8 = [&](const uint8_t* p, int ks) -> intx8_t {
+            const gemm::v4i_t lo = *reinterpret_cast<const gemm::v4i_t*>(p + fch[ks][0]);
+            const gemm::v4i_t hi = *reinterpret_cast<const gemm::v4i_t*>(p + fch[ks][1]);
+            return intx8_t{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        };
 
-        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        // the previous tile's stores and reads, and this tile's scale staging, are done; the
+        // intrinsic form keeps the compiler's wait tracking from carrying the epilogue's
+        // stores into the K loop
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        // prologue: K groups 0 .. STAGES-2 in flight
-#pragma unroll
-        for (int st = 0; st < F_STAGES - 1; ++st) issue(st, st < KG ? st : KG - 1);
+        issue(0, 0);
         for (int64_t kg = 0; kg < KG; ++kg) {
-            const int cur = static_cast<int>(kg % F_STAGES);
-            // group kg landed everywhere; every wave is done with group kg-1's buffer
-            asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"((F_STAGES - 2) * F_LPW) : "memory");
+            const int cur = static_cast<int>(kg & 1);
+            // group kg landed for this wave (nothing else is in flight); after the barrier for
+            // every wave, and every wave is done with group kg - 1's stage, refilled next
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
-            intx8_t fa[4][2], fb[2][2];
+            issue(cur ^ 1, kg + 1 < KG ? kg + 1 : KG - 1);
+            intx8_t fb[2][2], fa[2][2];
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const uint8_t* p = a_rd + cur * (F_BM * F_ROW) + i * 32 * F_ROW;
-                    const gemm::v4i_t lo = *reinterpret_cast<const gemm::v4i_t*>(p + fch[ks][0]);
-                    const gemm::v4i_t hi = *reinterpret_cast<const gemm::v4i_t*>(p + fch[ks][1]);
-                    fa[i][ks] = intx8_t{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-                }
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const uint8_t* p = (j ? b_rd1 : b_rd0) + cur * (F_BN * F_ROW);
-                    const gemm::v4i_t lo = *reinterpret_cast<const gemm::v4i_t*>(p + fch[ks][0]);
-                    const gemm::v4i_t hi = *reinterpret_cast<const gemm::v4i_t*>(p + fch[ks][1]);
-                    fb[j][ks] = intx8_t{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-                }
+                fb[0][ks] = read8(b_rd0 + cur * (F_BN * F_ROW), ks);
+                fb[1][ks] = read8(b_rd1 + cur * (F_BN * F_ROW), ks);
+                fa[0][ks] = read8(a_rd + cur * (F_BM * F_ROW), ks);
             }
-            float4 sa[4][4];
+            float sa[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int g = 0; g < 4; ++g)
-                    sa[i][g] = *reinterpret_cast<const float4*>(s_rd + cur * F_BM + 32 * i + 8 * g);
-            // refill the buffer group kg-1 used with group kg + STAGES - 1
-            const int64_t nxt = kg + F_STAGES - 1;
-            issue(static_cast<int>(nxt % F_STAGES), nxt < KG ? nxt : KG - 1);
+            for (int i = 0; i < 4; ++i) sa[i] = s_rd[cur * F_BM + 32 * i];
             const float sw0 = wscale(0, kg), sw1 = wscale(1, kg);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
+                const int c = i & 1;
+                if (i + 1 < 4) {
+#pragma unroll
+                    for (int ks = 0; ks < 2; ++ks)
+                        fa[c ^ 1][ks] = read8(a_rd + cur * (F_BM * F_ROW) + (i + 1) * 32 * F_ROW, ks);
+                }
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
-                    floatx16_t t = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i][0], fb[j][0], zero,
+                    floatx16_t t = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j][0], fa[c][0], zero,
                                                                                    0, 0, 0, 0, 0, 0);
-                    t = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i][1], fb[j][1], t, 0, 0, 0, 0, 0, 0);
-                    const float sw = j ? sw1 : sw0;
+                    t = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j][1], fa[c][1], t, 0, 0, 0, 0, 0, 0);
+                    const float sc = sa[i] * (j ? sw1 : sw0);
 #pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const float s4[4] = {sa[i][g].x, sa[i][g].y, sa[i][g].z, sa[i][g].w};
-#pragma unroll
-                        for (int u = 0; u < 4; ++u)
-                            acc[i][j][4 * g + u] = __builtin_fmaf(s4[u] * sw, t[4 * g + u], acc[i][j][4 * g + u]);
-                    }
+                    for (int v = 0; v < 16; ++v) acc[i][j][v] = __builtin_fmaf(sc, t[v], acc[i][j][v]);
                 }
             }
         }
-        // epilogue: lane holds rows 8*(v/4) + 4*(lane/32) + v%4 of column lane%32
-        int rbase = wm * 128 + (lane >> 5) * 4;
-        asm volatile("" : "+v"(rbase));
-        const int64_t colbase = UP ? static_cast<int64_t>(nt) * F_UP_COLS + wn * 32 + (lane & 31)
-                                   : static_cast<int64_t>(nt) * F_BN + wn * 64 + (lane & 31);
-        uint16_t* cbase = a.C + (row0 + rbase) * a.N + colbase;
+        // epilogue: in block (i, j) the lane holds token row wm*128 + 32 i + lane mod 32 and,
+        // for g = 0..3, columns 8 g + 4 (lane / 32) + 0..3 of the block: one 8-byte store each
+        const int rloc = wm * 128 + frow;
+        const int64_t colbase = UP ? static_cast<int64_t>(nt) * F_UP_COLS + wn * 32 + (lane >> 5) * 4
+                                   : static_cast<int64_t>(nt) * F_BN + wn * 64 + (lane >> 5) * 4;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
+            if (rloc + i * 32 >= static_cast<int>(nrows)) continue;
+            uint16_t* cp = a.C + (row0 + rloc + i * 32) * a.N + colbase;
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int roff = i * 32 + (v >> 2) * 8 + (v & 3);
-                if (rbase + roff >= static_cast<int>(nrows)) continue;
-                uint16_t* cp = cbase + static_cast<int64_t>(roff) * a.N;
+            for (int g = 0; g < 4; ++g) {
                 if (UP) {
-                    cp[0] = f32_to_bf16(silu_mul8(acc[i][0][v], acc[i][1][v]));
+                    float h[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) h[u] = silu_mul8(acc[i][0][4 * g + u], acc[i][1][4 * g + u]);
+                    *reinterpret_cast<uint2*>(cp + g * 8) = make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
                 } else {
-                    cp[0] = f32_to_bf16(acc[i][0][v]);
-                    cp[32] = f32_to_bf16(acc[i][1][v]);
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        const floatx16_t& c = acc[i][j];
+                        *reinterpret_cast<uint2*>(cp + j * 32 + g * 8) =
+                            make_uint2(pack_bf16x2(c[4 * g], c[4 * g + 1]), pack_bf16x2(c[4 * g + 2], c[4 * g + 3]));
+                    }
                 }
             }
         }
@@ -310,7 +324,8 @@ moe_status run_fp8_stage(bool up, const void* act, const moe_plan* plan,
                          void* workspace, size_t ws_bytes, hipStream_t stream) {
     if (plan->cap == 0) return MOE_OK;
     const int64_t K = up ? H : I, N = up ? I : H;
-    if (H % QB != 0 || I % QB != 0) return MOE_ERR_UNSUPPORTED;
+    if (H % F_BN != 0 || I % QB != 0) return MOE_ERR_UNSUPPORTED;  // whole 256-column down tiles
+    if (K / QB > kMaxKG8) return MOE_ERR_UNSUPPORTED;              // the staged weight scales
     if (2 * H * I >= (int64_t(1) << 32) || int64_t(F_BM) * K >= (int64_t(1) << 32) ||
         plan->cap * (K / QB) * 4 >= (int64_t(1) << 32))
         return MOE_ERR_UNSUPPORTED;  // descriptor ranges are 32-bit
@@ -339,8 +354,8 @@ moe_status run_fp8_stage(bool up, const void* act, const moe_plan* plan,
     TileOrder to;
     if (!pick_tile_order(g.NT, blocks, &to)) return MOE_ERR_UNSUPPORTED;
     const dim3 grid(static_cast<unsigned>(blocks));
-    if (up) hipLaunchKernelGGL(grouped_gemm_fp8_kernel<true>, grid, dim3(kThreads), 0, stream, g, to);
-    else hipLaunchKernelGGL(grouped_gemm_fp8_kernel<false>, grid, dim3(kThreads), 0, stream, g, to);
+    if (up) hipLaunchKernelGGL(grouped_gemm_fp8_kernel<true>, grid, dim3(F_THREADS), 0, stream, g, to);
+    else hipLaunchKernelGGL(grouped_gemm_fp8_kernel<false>, grid, dim3(F_THREADS), 0, stream, g, to);
     MOE_LAUNCH_CHECK();
     return MOE_OK;
 }
