@@ -353,8 +353,9 @@ size_t moe_expert_gemm_workspace_size(int64_t cap, int64_t H, int64_t I, moe_dty
  * 8-byte aligned.  Anything else with bf16 or fp32 weights runs a generic tiled kernel on the
  * fp32 matrix cores (any shape and alignment, at the fp32 matrix-core rate);
  * moe_expert_gemm_fast_path tells which one a call takes.  fp8 weights have no generic form:
- * they return MOE_ERR_UNSUPPORTED with bf16 activations and MOE_ERR_INVALID_ARG for
- * misaligned inputs with e4m3 activations. */
+ * they need bf16 activations, H % 256 == 0 and I % 128 == 0 in both modes (and K / 128 <= 128
+ * K groups), else MOE_ERR_UNSUPPORTED; with e4m3 activations a misaligned input or weight
+ * buffer is MOE_ERR_INVALID_ARG, with bf16 activations MOE_ERR_UNSUPPORTED. */
 moe_status moe_expert_gemm(const void* x_perm, moe_dtype act_dt, const moe_plan* plan,
                            const moe_expert_weights* w, int64_t H, int64_t I, void* y_perm,
                            void* workspace, size_t workspace_bytes, hipStream_t stream);
