@@ -6,19 +6,19 @@
 // "prefll 侧的一个必要步骤：per-token-group 量化" (group size hard-wired to 128, matching
 // expert_alignment 128).  Values: weight = e4m3(q) * s_w[block], activation ~ e4m3(q) * s_a.
 //
-// quant kernel: one wave per row, one 128-column group per step: amax by wave reduction,
+// quant kernel: a wave per row, four 128-column groups per step (16 lanes each): amax by reduction,
 //   scale s = amax / 448 (1 for an all-zero group), codes = RNE(x / s) clamped to +-448 (the
 //   hardware conversion turns larger magnitudes into NaN), both in fp32 with correctly
 //   rounded divisions, so every code is decided exactly as the absmax reading of the page's
 //   per-token-group step defines it.  Scales are stored transposed, [K/128][cap], so a
 //   tile's 256 scales of one K group are contiguous.
 // GEMM kernel (gfx950 v_mfma_f32_32x32x64_f8f6f4, e4m3 x e4m3, fp32 accumulate):
-//   - block tile 256 rows x 128 columns (up: 64 gate + the same 64 up columns), 4 waves in
-//     2x2, each 128 x 64 = 4x2 MFMA blocks;
-//   - one pipeline stage = one 128-deep K group = one scale block: the MFMAs of a stage
-//     accumulate into a fresh partial sum, then acc += (s_a[row] * s_w) * partial;
-//   - A, B and the stage's activation scales arrive in LDS by buffer DMA, 3 stages
-//     (2 in flight); 128-byte rows with 16-byte chunks xor-swizzled by (row/2) mod 8 for the
+//   - block tile 256 rows x 256 columns (up: 128 gate + the same 128 up columns), 8 waves
+//     in 2 x 4, each 128 x 64 = 4 x 2 MFMA blocks;
+//   - one pipeline stage = one 128-deep K group = one scale block: each block's MFMAs of a
+//     stage accumulate into a fresh partial sum, then acc += (s_a[row] * s_w) * partial;
+//   - A, B and the stage's activation scales arrive in LDS by buffer DMA, 2 stages
+//     (1 in flight); 128-byte rows with 16-byte chunks xor-swizzled by (row/2) mod 8 for the
 //     64-bank LDS;
 //   - same persistent XCD-grouped tile order and ragged-segment numbering as the bf16 path.
 #include <hip/hip_runtime.h>
@@ -36,6 +36,10 @@ constexpr int QB = 128;              // quantisation group / scale block
 constexpr float kE4M3Max = 448.0f;
 
 // ------------------------------------------------------------------ activation quant
+// A wave quantises four 128-wide groups of a row per step, 16 lanes per group, 8 values per
+// lane (one 16-byte load, one 8-byte store): amax by a 16-lane reduction, then the same
+// per-value arithmetic as the definition above.  A row's groups past the last whole step are
+// masked off.
 __global__ __launch_bounds__(256) void quant_fp8_kernel(const uint16_t* __restrict__ act,
                                                         const int64_t* __restrict__ num_rows,
                                                         int64_t cap, int64_t K,
@@ -44,23 +48,44 @@ __global__ __launch_bounds__(256) void quant_fp8_kernel(const uint16_t* __restri
     int64_t rows = *num_rows;
     rows = rows < cap ? rows : cap;
     const int lane = lane_id();
+    const int sub = lane >> 4, sl = lane & 15;  // group of the step, lane within the group
     const int64_t nw = static_cast<int64_t>(gridDim.x) * 4;
     const int64_t groups = K / QB;
     for (int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / kWave; r < rows; r += nw) {
-        const uint32_t* src = reinterpret_cast<const uint32_t*>(act + r * K);
-        uint16_t* dst = reinterpret_cast<uint16_t*>(q + r * K);
-        for (int64_t g = 0; g < groups; ++g) {
-            const uint32_t w = src[g * (QB / 2) + lane];
-            const float x0 = __uint_as_float(w << 16), x1 = __uint_as_float(w & 0xffff0000u);
-            float m = fmaxf(fabsf(x0), fabsf(x1));
+        const uint16_t* src = act + r * K;
+        uint8_t* dst = q + r * K;
+        for (int64_t g0 = 0; g0 < groups; g0 += 4) {
+            const int64_t g = g0 + sub;
+            const bool valid = g < groups;
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (valid) v = *reinterpret_cast<const uint4*>(src + g * QB + sl * 8);
+            const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+            float x[8];
 #pragma unroll
-            for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+            for (int t = 0; t < 4; ++t) {
+                x[2 * t] = __uint_as_float(u[t] << 16);
+                x[2 * t + 1] = __uint_as_float(u[t] & 0xffff0000u);
+            }
+            float m = 0.f;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) m = fmaxf(m, fabsf(x[t]));
+#pragma unroll
+            for (int off = 8; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
             const float sc = m > 0.f ? __fdiv_rn(m, kE4M3Max) : 1.f;
-            const float y0 = fminf(fmaxf(__fdiv_rn(x0, sc), -kE4M3Max), kE4M3Max);
-            const float y1 = fminf(fmaxf(__fdiv_rn(x1, sc), -kE4M3Max), kE4M3Max);
-            const int packed = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
-            dst[g * (QB / 2) + lane] = static_cast<uint16_t>(packed & 0xffff);
-            if (lane == 0) s_t[g * cap + r] = sc;
+            uint32_t packed[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                float y[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) y[t] = fminf(fmaxf(__fdiv_rn(x[4 * h + t], sc), -kE4M3Max), kE4M3Max);
+                int w = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+                w = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], w, true);
+                packed[h] = static_cast<uint32_t>(w);
+            }
+            if (valid) {
+                *reinterpret_cast<uint2*>(dst + g * QB + sl * 8) = make_uint2(packed[0], packed[1]);
+                if (sl == 0) s_t[g * cap + r] = sc;
+            }
         }
     }
 }
@@ -368,7 +393,7 @@ extern "C" moe_status moe_quant_act_fp8(const void* act, const int64_t* num_rows
     MOE_CHECK_ARG(cap >= 0 && K > 0 && K % moe::QB == 0);
     if (cap == 0) return MOE_OK;
     MOE_CHECK_ARG(act && num_rows && q && s_t);
-    MOE_CHECK_ARG(moe::aligned(act, 4) && moe::aligned(q, 2));
+    MOE_CHECK_ARG(moe::aligned(act, 16) && moe::aligned(q, 8));
     return moe::launch_quant(act, num_rows, cap, K, q, s_t, stream);
 }
 

@@ -129,7 +129,8 @@ def mfma_util(counter_csv: str, agent_csv: str) -> List[dict]:
         dur_ns = sum(spans[name].values()) / len(spans[name])
         cycles = mean["GRBM_GUI_ACTIVE"] / geo["xcds"]
         flops = 512.0 * sum(mean.get(k, 0.0) for k in ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F16",
-                                                       "SQ_INSTS_VALU_MFMA_MOPS_F32", "SQ_INSTS_VALU_MFMA_MOPS_F64"))
+                                                       "SQ_INSTS_VALU_MFMA_MOPS_F32", "SQ_INSTS_VALU_MFMA_MOPS_F64",
+                                                       "SQ_INSTS_VALU_MFMA_MOPS_FP8"))
         out.append({"name": name, "dispatches": len(spans[name]), "avg_us": dur_ns / 1e3,
                     "clock_mhz": cycles / dur_ns * 1e3,
                     "mfma_busy": mean["SQ_VALU_MFMA_BUSY_CYCLES"] / (cycles * geo["simds"]),

@@ -327,9 +327,9 @@ typedef struct {
  * correctly rounded divisions,
  *     s = amax / 448 (1 for an all-zero group),   code = e4m3 RNE of clamp(x / s, +-448)
  * (OCP e4m3fn).  The pages fix the group, not the scale rule; absmax scaling is the reading.
- *   act       device bf16 [cap, K], K a multiple of 128, 4-byte aligned
+ *   act       device bf16 [cap, K], K a multiple of 128, 16-byte aligned
  *   num_rows  device int64[1] (read on the device; rows past it are left untouched)
- *   q         device uint8 [cap, K]: the codes
+ *   q         device uint8 [cap, K], 8-byte aligned: the codes
  *   s_t       device fp32 [K / 128, cap]: the scales, transposed so that one group's scales
  *             of consecutive rows are contiguous
  * Returns MOE_ERR_INVALID_ARG for K not a multiple of 128 or a null or misaligned buffer. */

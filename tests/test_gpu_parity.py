@@ -141,14 +141,16 @@ def test_cfg5_fp8_block_scaled_small(fp8_act):
             f"{oracle.row_rel_err(ref['y_perm'][:rows], exact[:rows]):.3e}")
 
 
-def test_quant_act_fp8_bitwise():
+@pytest.mark.parametrize("K", [1024, 640, 7168])
+def test_quant_act_fp8_bitwise(K):
     """The per-token-group quantisation step on its own: every code and scale equals the
     oracle's, for rows of wildly different magnitudes, an all-zero group, a group of tiny
     values (subnormal codes) and a group whose values sit on code midpoints; rows past
-    num_rows stay untouched."""
+    num_rows stay untouched.  K = 640 has five groups, so the kernel's last four-group step
+    is partly masked."""
     import combine_dp_gather_amd as m
     rng = np.random.default_rng(17)
-    cap, K, nrows = 700, 1024, 613
+    cap, nrows = 700, 613
     x = (rng.standard_normal((cap, K)) * np.exp(rng.uniform(-30, 30, (cap, 1)))).astype(np.float32)
     x[5, 128:256] = 0.0
     x[6, :128] *= np.float32(2.0 ** -12)
@@ -325,8 +327,8 @@ def test_gate_kernels_bitwise(dt):
     # ragged row and expert tiles (E = 200) and every 17th row a pad row:
     #   - 16x16 chains, 16-byte loads (H a multiple of 64): G = 300 at H = 384 (subnormal
     #     products and partial sums), 448 and the model's 7168;
-    #   - 16x16 chains, element loads (ragged last slice): G = 300 at H = 1000, and a batch
-    #     large enough for 128-row blocks but with H = 232 (G = 16347);
+    #   - 16x16 chains, element loads (ragged last slice): G = 300 and 6000 at H = 1000, and a
+    #     batch large enough for 128-row blocks but with H = 232 (G = 16347);
     #   - the 32x32-chain kernels: G = 16384 (64-row blocks, 4 waves) and 33000 (128-row
     #     blocks, 8 waves) at H = 256 (also subnormal) and 384;
     #   - rows whose chain ends at -0 (one tiny negative product in the last real column of
@@ -334,7 +336,7 @@ def test_gate_kernels_bitwise(dt):
     import combine_dp_gather_amd as m
     rng = np.random.default_rng(21)
     cfg = m.make_route_cfg("softmax", 200, 4)
-    cases = ((300, 384, 2.0 ** -66), (300, 448, 1.0), (1000, 7168, 1.0), (300, 1000, 1.0),
+    cases = ((300, 384, 2.0 ** -66), (300, 448, 1.0), (1000, 7168, 1.0), (300, 1000, 1.0), (6000, 1000, 1.0),
              (128 * 128 - 37, 232, 1.0), (16384, 256, 1.0), (33000, 384, 1.0), (33000, 256, 2.0 ** -66),
              (300, 232, "negzero"), (33000, 200, "negzero"))
     for G, H, scale in cases:
