@@ -99,7 +99,8 @@ def eplb_cycle(cfg, inp, layer, reps, args, dev, act):
     torch.cuda.empty_cache()
     w2 = DeviceWeights(inp2, dev, fp8_act=args.fp8_act)
     layer2 = MoELayer(spec_of(cfg2), w2, cfg2.num_tokens, act, mode=args.mode,
-                      static_bound=cfg2.static_bound, device=dev, seg_stride=args.seg_stride)
+                      static_bound=cfg2.static_bound, device=dev, seg_stride=args.seg_stride,
+                      fuse_permute=not args.copy_permute)
     layer2.gather(reps)
     layer2.route()
     new = torch.zeros(EPLB["P"], dtype=torch.int64, device=dev)
@@ -257,6 +258,9 @@ def main():
                          "slot table, place the experts with the library (288 slots, 8 groups, "
                          "2 nodes x 9 GPUs; this GPU holds slots 0-15), and time the step under "
                          "the new table with the per-step load count included")
+    ap.add_argument("--copy-permute", action="store_true",
+                    help="dispatch writes the permuted copy x_perm and the up GEMM reads it (without "
+                         "this flag the up GEMM gathers its rows from the global buffer itself)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run a plain device copy of MIB MiB (reference for HBM counters)")
     args = ap.parse_args()
@@ -289,7 +293,8 @@ def main():
     act = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
     w = DeviceWeights(inp, dev, fp8_act=args.fp8_act)
     layer = MoELayer(spec_of(cfg), w, cfg.num_tokens, act, mode=args.mode,
-                     static_bound=cfg.static_bound, device=dev, seg_stride=args.seg_stride)
+                     static_bound=cfg.static_bound, device=dev, seg_stride=args.seg_stride,
+                     fuse_permute=not args.copy_permute)
     bf = cfg.dtype == "bf16"
     reps = []
     for r in inp.replicas:
@@ -351,7 +356,8 @@ def main():
         if args.entry or args.exit or eplb_info is not None:
             raise SystemExit("--tbo runs the plain six-call step only")
         tbo = TwoBatchOverlap(spec_of(cfg), w, layer.sizes, act, mode=args.mode, device=dev,
-                              seg_stride=args.seg_stride, cu_split=args.cu_split)
+                              seg_stride=args.seg_stride, cu_split=args.cu_split,
+                              fuse_permute=not args.copy_permute)
         for _ in range(args.warmup):
             tbo.forward(reps)
         torch.cuda.synchronize()
@@ -453,7 +459,8 @@ def main():
         # read attention output and residual, write residual and the gathered row; norm weight
         "entry": ("hbm", 3 * T * H * es + G * H * es + 4 * G + H * es),
         "route": ("mfma32", 2.0 * G * E * H),                          # exact fp32 fma chain + select
-        "dispatch": ("hbm", 2 * R * H * es + 3 * 4 * G * k + 8 * R),  # x_perm copy + id passes
+        # id passes (+ the x_perm copy when the up GEMM does not gather its rows itself)
+        "dispatch": ("hbm", (2 * R * H * es if args.copy_permute else 0) + 3 * 4 * G * k + 8 * R),
         "gemm_up": gemm_work(mm, 4.0 * R * H * I,                     # gate+up: 2*R*H*2I
                              E_active * 2 * I * H * wb + R * H * es + R * I * es),
         "gemm_down": gemm_work(mm, 2.0 * R * I * H, E_active * H * I * wb + R * I * es + R * H * es),
@@ -545,6 +552,8 @@ def main():
                    "last_step": "fused combine + scatter" if args.exit else "combine, then scatter",
                    "dispatch_layout": (f"fixed capacity, {args.seg_stride} rows per slot" if args.seg_stride
                                        else "packed segments"),
+                   "permute": ("copy to x_perm in dispatch" if args.copy_permute
+                               else "folded into the up GEMM's row loads"),
                    "tokens": T, "global_rows": G, "gather_mode": args.mode,
                    "routed_local_pairs": R, "slots_with_rows": E_active, "parallelism": "one EP rank's share on 1 GPU",
                    **({"placement": eplb_info} if eplb_info is not None else {})},

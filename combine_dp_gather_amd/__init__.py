@@ -22,7 +22,7 @@ __all__ = [
     "moe_gather_layout", "moe_gather", "moe_entry_gather", "moe_scatter", "moe_expert_load",
     "moe_physical_to_logical_count", "moe_eplb_balancedness", "moe_eplb_rebalance",
     "moe_eplb_logical_to_physical", "moe_route", "moe_route_from_logits",
-    "moe_dispatch", "moe_dispatch_noalloc", "moe_dispatch_workspace_size", "moe_quant_act_fp8", "moe_expert_gemm_fast_path", "moe_expert_gemm", "moe_expert_gemm_up",
+    "moe_dispatch", "moe_dispatch_noalloc", "moe_dispatch_workspace_size", "moe_quant_act_fp8", "moe_expert_gemm_fast_path", "moe_expert_gemm", "moe_expert_gemm_up", "moe_expert_gemm_up_gather",
     "moe_expert_gemm_down", "moe_expert_gemm_workspace_size", "moe_combine", "moe_version",
     "PlanBuffers", "make_route_cfg", "make_expert_map", "make_expert_weights", "MoEError",
     "GatherLayout", "RouteCfg", "ExpertMap", "ExpertWeights", "Plan",
@@ -246,8 +246,9 @@ def moe_dispatch_workspace_size(G: int, k: int, num_slots: int) -> int:
 
 
 def moe_dispatch(global_x: torch.Tensor, topk_ids: torch.Tensor, emap: ExpertMap,
-                 plan: PlanBuffers, x_perm: torch.Tensor, workspace: torch.Tensor,
+                 plan: PlanBuffers, x_perm: Optional[torch.Tensor], workspace: torch.Tensor,
                  stream=None) -> None:
+    """x_perm=None: the plan only (no permuted copy), for moe_expert_gemm_up_gather."""
     G, H = global_x.shape
     k = plan.k
     check("moe_dispatch", lib().moe_dispatch(
@@ -257,8 +258,9 @@ def moe_dispatch(global_x: torch.Tensor, topk_ids: torch.Tensor, emap: ExpertMap
 
 
 def moe_dispatch_noalloc(global_x: torch.Tensor, topk_ids: torch.Tensor, emap: ExpertMap,
-                         plan: PlanBuffers, x_perm: torch.Tensor, stream=None) -> None:
-    """moe_dispatch with the library's fixed per-GPU scratch instead of a workspace."""
+                         plan: PlanBuffers, x_perm: Optional[torch.Tensor], stream=None) -> None:
+    """moe_dispatch with the library's fixed per-GPU scratch instead of a workspace
+    (x_perm=None: the plan only)."""
     G, H = global_x.shape
     check("moe_dispatch_noalloc", lib().moe_dispatch_noalloc(
         _ptr(global_x), _ptr(topk_ids), G, plan.k, H, _dtype_code(global_x), ctypes.byref(emap),
@@ -312,6 +314,17 @@ def moe_expert_gemm_up(x_perm: torch.Tensor, plan: PlanBuffers, w: ExpertWeights
     ws = 0 if workspace is None else workspace.numel() * workspace.element_size()
     check("moe_expert_gemm_up", lib().moe_expert_gemm_up(
         _ptr(x_perm), _dtype_code(x_perm), ctypes.byref(plan.struct), ctypes.byref(w), H, I,
+        _ptr(h), _ptr(workspace), ws, _stream(stream)))
+
+
+def moe_expert_gemm_up_gather(global_x: torch.Tensor, plan: PlanBuffers, w: ExpertWeights, H: int,
+                              I: int, h: torch.Tensor, workspace: Optional[torch.Tensor] = None,
+                              stream=None) -> None:
+    """The up GEMM reading each permuted row from global_x through the plan's sorted_pair
+    (after moe_dispatch with x_perm=None): the same h as moe_expert_gemm_up on the copy."""
+    ws = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    check("moe_expert_gemm_up_gather", lib().moe_expert_gemm_up_gather(
+        _ptr(global_x), _dtype_code(global_x), ctypes.byref(plan.struct), ctypes.byref(w), H, I,
         _ptr(h), _ptr(workspace), ws, _stream(stream)))
 
 

@@ -75,6 +75,8 @@ SIGNATURES = {
                                 c_i64, c_i64, c_vp, c_vp, c_sz, c_vp]),
     "moe_expert_gemm_up": (c_i32, [c_vp, c_i32, ctypes.POINTER(Plan), ctypes.POINTER(ExpertWeights),
                                    c_i64, c_i64, c_vp, c_vp, c_sz, c_vp]),
+    "moe_expert_gemm_up_gather": (c_i32, [c_vp, c_i32, ctypes.POINTER(Plan), ctypes.POINTER(ExpertWeights),
+                                          c_i64, c_i64, c_vp, c_vp, c_sz, c_vp]),
     "moe_expert_gemm_down": (c_i32, [c_vp, c_i32, ctypes.POINTER(Plan),
                                      ctypes.POINTER(ExpertWeights), c_i64, c_i64, c_vp, c_vp, c_sz,
                                      c_vp]),

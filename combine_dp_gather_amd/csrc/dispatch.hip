@@ -20,6 +20,9 @@
 //               below with the same slot), so rows follow ascending pair index: stable;
 //   4. permute: x_perm[row] = global_x[sorted_pair[row] / k], one block per row, streaming
 //               16-byte vectors, rows bounded by the device-side num_rows (no host sync).
+//               Skipped when the caller passes no x_perm: the gathering up GEMM then reads
+//               each row from global_x through sorted_pair itself, and the copy's traffic
+//               (a read and a write of every routed row) is saved.
 #include <mutex>
 
 #include "moe_dev.h"
@@ -472,8 +475,8 @@ moe_status check_dispatch_args(const void* global_x, const int32_t* topk_ids, in
                       plan->cap >= static_cast<int64_t>(map->num_slots) * plan->seg_stride);
     MOE_CHECK_ARG(plan->counts && plan->seg_offsets && plan->num_rows && plan->error_flag);
     MOE_CHECK_ARG(G * k < (int64_t(1) << 31));
-    if (G > 0) MOE_CHECK_ARG(topk_ids && plan->pair_row && global_x);
-    if (plan->cap > 0) MOE_CHECK_ARG(plan->sorted_pair && x_perm);
+    if (G > 0) MOE_CHECK_ARG(topk_ids && plan->pair_row && (global_x || !x_perm));
+    if (plan->cap > 0) MOE_CHECK_ARG(plan->sorted_pair);
     return MOE_OK;
 }
 
@@ -515,7 +518,8 @@ moe_status run_dispatch(const void* global_x, const int32_t* topk_ids, int64_t G
                            plan->sorted_pair, plan->pair_row);
         MOE_LAUNCH_CHECK();
     }
-    if (plan->cap == 0) return MOE_OK;
+    // no x_perm: the plan only (the gathering up GEMM reads the rows in place)
+    if (plan->cap == 0 || x_perm == nullptr) return MOE_OK;
     const int64_t row_bytes = H * dtype_size(dt);
     if (row_bytes % 16 == 0 && aligned(global_x, 16) && aligned(x_perm, 16))
         return launch_permute<uint4>(global_x, plan, row_bytes, x_perm, stream);

@@ -63,7 +63,47 @@ struct GemmArgs {
     int64_t N;               // up: I; down: H
     int32_t El;
     int32_t NT;              // column tiles per m-tile
+    // gather form (amap != NULL): the permuted row r is row amap[r] / ak of A, which holds
+    // arows rows (A = the [G, H] global buffer, amap = the plan's sorted_pair); a negative
+    // entry reads as a zero row.  NULL: row r of A.
+    const int32_t* amap;
+    int32_t ak;
+    int64_t arows;
 };
+
+// Offset past every buffer resource this file builds (each covers under 2^31 bytes): a DMA
+// at it, plus its chunk and K offset, reads zeros.
+constexpr uint32_t kAOut = 0x80000000u;
+
+// Byte offsets of the A rows that tile-local rows r0 + p * rstep (permuted rows row0 + r)
+// read, p < P: from the tile's first row in the copy form, from A itself in the gather form;
+// kAOut past the tile's nrows rows or for an empty or out-of-range gather entry.  The P map
+// entries are loaded at once (clamped to the tile's last row), then checked, so a tile start
+// waits for one round trip, not P.
+template <int P>
+__device__ __forceinline__ void a_row_offsets(const GemmArgs& a, int64_t row0, uint32_t r0, uint32_t rstep,
+                                              uint32_t nrows, uint32_t row_bytes, uint32_t (&off)[P]) {
+    if (a.amap == nullptr || nrows == 0) {
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            const uint32_t r = r0 + p * rstep;
+            off[p] = r < nrows ? r * row_bytes : kAOut;
+        }
+        return;
+    }
+    int32_t f[P];
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+        const uint32_t r = r0 + p * rstep;
+        f[p] = a.amap[row0 + (r < nrows ? r : nrows - 1)];
+    }
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+        const uint32_t r = r0 + p * rstep;
+        const int64_t g = f[p] >= 0 ? f[p] / a.ak : a.arows;
+        off[p] = r < nrows && g < a.arows ? static_cast<uint32_t>(g) * row_bytes : kAOut;
+    }
+}
 
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
 
@@ -214,8 +254,8 @@ __global__ __launch_bounds__(PP_THREADS, 1) void grouped_gemm_pp_kernel(GemmArgs
         uint32_t dbytes;
         if (loads_a) {
             // rows past the segment end fall outside the resource: they read as zeros
-            dbase = a.A + row0 * a.K;
-            dbytes = nrows * row_bytes;
+            dbase = a.amap ? a.A : a.A + row0 * a.K;
+            dbytes = a.amap ? static_cast<uint32_t>(a.arows) * row_bytes : nrows * row_bytes;
         } else if (W8) {
             const int64_t rows = UP ? 2 * a.N : a.N;
             dbase = reinterpret_cast<const uint16_t*>(a.B8 + static_cast<int64_t>(e) * rows * a.K);
@@ -236,8 +276,20 @@ __global__ __launch_bounds__(PP_THREADS, 1) void grouped_gemm_pp_kernel(GemmArgs
         if (loads_a) grow = static_cast<uint32_t>(r0);
         else if (UP) grow = static_cast<uint32_t>((r0 >= 128 ? a.N : 0) + nt * UP_COLS + (r0 & 127));
         else grow = static_cast<uint32_t>(nt * BN + r0);
-        uint32_t vbase = grow * row_bytes + static_cast<uint32_t>(((lane % PP_CPR) ^ pp_swz(r0)) * 16);
+        const uint32_t chunk = static_cast<uint32_t>(((lane % PP_CPR) ^ pp_swz(r0)) * 16);
+        uint32_t vbase = grow * row_bytes + chunk;
         uint32_t rstep = static_cast<uint32_t>(PP_RPB) * row_bytes;
+        // the lane's offset in DMA p: weight rows step by 16 rows, activation rows are looked
+        // up (they are consecutive only in the copy form)
+        uint32_t voff[PP_LPW];
+        if (loads_a) {
+            a_row_offsets<PP_LPW>(a, row0, static_cast<uint32_t>(r0), PP_RPB, nrows, row_bytes, voff);
+#pragma unroll
+            for (int p = 0; p < PP_LPW; ++p) voff[p] += chunk;
+        } else {
+#pragma unroll
+            for (int p = 0; p < PP_LPW; ++p) voff[p] = vbase + static_cast<uint32_t>(p) * rstep;
+        }
         if (W8 && !loads_a) {
             // fp8 weight rows are K bytes, 32 per slice: a DMA covers 32 rows x 32 bytes, lane
             // pair per row, wave sq tile rows 64 sq + 32 p + lane / 2; the 16-byte halves of a
@@ -263,14 +315,15 @@ __global__ __launch_bounds__(PP_THREADS, 1) void grouped_gemm_pp_kernel(GemmArgs
                 }
             }
             int off = stage * (BM * PP_BK) + sq * PP_LPW * 512;
-            uint32_t vb = vbase;
-            asm volatile("" : "+s"(off), "+v"(vb));
+            uint32_t v0 = voff[0], v1 = voff[1], v2 = voff[2], v3 = voff[3];
+            asm volatile("" : "+s"(off), "+v"(v0), "+v"(v1), "+v"(v2), "+v"(v3));
+            const uint32_t vo[PP_LPW] = {v0, v1, v2, v3};
             uint16_t* base = (loads_a ? &As[0][0] : &Bs[0][0]) + off;
             const int soff = static_cast<int>(kt * PP_BK * 2);
 #pragma unroll
             for (int p = 0; p < PP_LPW; ++p)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (gemm::lds_void_t*)(base + p * 512), 16,
-                                                        vb + static_cast<uint32_t>(p) * rstep, soff, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (gemm::lds_void_t*)(base + p * 512), 16, vo[p],
+                                                        soff, 0, 0);
         };
 
         floatx16_t acc[4][2];
@@ -444,7 +497,7 @@ constexpr int ST_RPB = 64 / CPR;                 // rows per 1 KB DMA block (8)
 constexpr int ST_ADMA = ST_BM / ST_RPB / 4;      // activation DMAs per wave and slice (2)
 constexpr int ST_BDMA = ST_BN / ST_RPB / 4;      // weight DMAs per wave and slice (4)
 constexpr int ST_VPS = ST_ADMA + ST_BDMA;        // DMAs per wave and slice
-static_assert(BK == 64 && CPR == 8, "whole 128-byte lines per row and slice");
+static_assert(BK == 64 && CPR == 8 && ST_ADMA == 2, "whole 128-byte lines per row and slice");
 
 template <bool UP>
 __global__ __launch_bounds__(ST_THREADS, 1) void grouped_gemm_stream_kernel(GemmArgs a) {
@@ -497,25 +550,32 @@ __global__ __launch_bounds__(ST_THREADS, 1) void grouped_gemm_stream_kernel(Gemm
         const uint32_t nrows = static_cast<uint32_t>(nrows64 < ST_BM ? nrows64 : ST_BM);
 
         // rows past the segment end fall outside the resource: they read as zeros
-        const __amdgpu_buffer_rsrc_t arsrc = gemm::make_rsrc_uniform(a.A + row0 * a.K, nrows * row_bytes);
+        const __amdgpu_buffer_rsrc_t arsrc =
+            a.amap ? gemm::make_rsrc_uniform(a.A, static_cast<uint32_t>(a.arows) * row_bytes)
+                   : gemm::make_rsrc_uniform(a.A + row0 * a.K, nrows * row_bytes);
         const uint16_t* bbase = a.B + static_cast<int64_t>(e) * (UP ? 2 : 1) * a.N * a.K;
         const __amdgpu_buffer_rsrc_t brsrc =
             gemm::make_rsrc_uniform(bbase, static_cast<uint32_t>((UP ? 2 : 1) * a.N) * row_bytes);
         // up: waves 0, 1 stream gate rows, waves 2, 3 up rows (N further on)
         const uint32_t grow = UP ? static_cast<uint32_t>((rb >= ST_UPC ? a.N : 0) + nt * ST_UPC + (rb & (ST_UPC - 1)))
                                  : static_cast<uint32_t>(nt * ST_BN + rb);
-        const uint32_t avb = static_cast<uint32_t>(ra) * row_bytes, bvb = grow * row_bytes;
+        const uint32_t bvb = grow * row_bytes;
+        // activation DMA p reads tile row ra + 8 p (looked up in the gather form)
+        uint32_t aoff[ST_ADMA];
+        a_row_offsets<ST_ADMA>(a, row0, static_cast<uint32_t>(ra), ST_RPB, nrows, row_bytes, aoff);
+#pragma unroll
+        for (int p = 0; p < ST_ADMA; ++p) aoff[p] += achunk[p & 1];
         auto issue = [&](int stage, int64_t kt) {
             gemm::lds_void_t* adst = (gemm::lds_void_t*)(&As[0][0] + stage * (ST_BM * BK) + w * ST_ADMA * 512);
             gemm::lds_void_t* bdst = (gemm::lds_void_t*)(&Bs[0][0] + stage * (ST_BN * BK) + w * ST_BDMA * 512);
-            uint32_t va0 = avb + achunk[0], va1 = avb + achunk[1], vb0 = bvb + bchunk[0], vb1 = bvb + bchunk[1];
+            uint32_t va0 = aoff[0], va1 = aoff[1], vb0 = bvb + bchunk[0], vb1 = bvb + bchunk[1];
             asm volatile("" : "+s"(adst), "+s"(bdst), "+v"(va0), "+v"(va1), "+v"(vb0), "+v"(vb1));
             const int soff = static_cast<int>(kt * BK * 2);
 #pragma unroll
             for (int p = 0; p < ST_ADMA; ++p)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
                     arsrc, (gemm::lds_void_t*)((char __attribute__((address_space(3)))*)adst + p * 1024), 16,
-                    ((p & 1) ? va1 : va0) + static_cast<uint32_t>(p) * rstep, soff, 0, 0);
+                    (p & 1) ? va1 : va0, soff, 0, 0);
 #pragma unroll
             for (int p = 0; p < ST_BDMA; ++p)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -647,7 +707,12 @@ __global__ __launch_bounds__(256) void generic_gemm_kernel(GemmArgs a, const voi
             __syncthreads();  // the previous slice's reads are done
             for (int idx = tid; idx < GN_BM * GN_BK; idx += 256) {
                 const int r = idx / GN_BK, c = idx % GN_BK;
-                As[r * GN_LD + c] = (r < nrows && k0 + c < a.K) ? gn_ld(A, (row0 + r) * a.K + k0 + c) : 0.f;
+                int64_t src = row0 + r;  // the gather form looks the row up
+                if (a.amap != nullptr && r < nrows) {
+                    const int32_t f = a.amap[row0 + r];
+                    src = f < 0 || f / a.ak >= a.arows ? -1 : f / a.ak;
+                }
+                As[r * GN_LD + c] = (r < nrows && src >= 0 && k0 + c < a.K) ? gn_ld(A, src * a.K + k0 + c) : 0.f;
             }
             for (int idx = tid; idx < (UP ? 2 : 1) * GN_BN * GN_BK; idx += 256) {
                 const int r = idx / GN_BK, c = idx % GN_BK;
@@ -699,25 +764,31 @@ moe_status check_common(moe_dtype act_dt, const moe_plan* plan, const moe_expert
     return MOE_OK;
 }
 
-bool mfma_ok(moe_dtype act_dt, int64_t H, int64_t I, const void* A, const void* B, const void* C) {
-    // buffer resources cover one expert's weights and one 256-row A tile: < 4 GiB each
+// gather_rows > 0: the up GEMM gathers its rows from a [gather_rows, H] buffer
+bool mfma_ok(moe_dtype act_dt, int64_t H, int64_t I, const void* A, const void* B, const void* C,
+             int64_t gather_rows = 0) {
+    // buffer resources cover one expert's weights and one 256-row A tile (< 4 GiB each), or
+    // the whole gathered buffer (< 2 GiB, so that kAOut lies past it)
     const bool small = 2 * H * I * 2 < (int64_t(1) << 32) && int64_t(BM) * H * 2 < (int64_t(1) << 32) &&
-                       int64_t(BM) * I * 2 < (int64_t(1) << 32);
+                       int64_t(BM) * I * 2 < (int64_t(1) << 32) && gather_rows * H * 2 < (int64_t(1) << 31);
     return act_dt == MOE_BF16 && H % BN == 0 && I % UP_COLS == 0 && small && aligned(A, 16) &&
            aligned(B, 16) && aligned(C, 8);
 }
 
+// One GEMM half.  amap != NULL (up only): the gather form, A = the [arows, H] global buffer.
 moe_status run_stage(bool up, const void* A, moe_dtype act_dt, const moe_plan* plan,
-                     const moe_expert_weights* w, int64_t H, int64_t I, void* C, hipStream_t stream) {
+                     const moe_expert_weights* w, int64_t H, int64_t I, void* C, hipStream_t stream,
+                     const int32_t* amap = nullptr, int32_t ak = 1, int64_t arows = 0) {
     if (plan->cap == 0) return MOE_OK;
     MOE_CHECK_ARG(A && C);
     const void* B = up ? w->w13 : w->w2;
     const int64_t K = up ? H : I;
     const int64_t N = up ? I : H;
     const bool w8 = w->dtype == MOE_FP8_E4M3;
+    const bool tiles = mfma_ok(act_dt, H, I, A, B, C, amap ? arows : 0);
     // no fp8 fallback; the staged block scales hold up to kMaxKG8 K groups
-    if (w8 && (!mfma_ok(act_dt, H, I, A, B, C) || K / 128 > kMaxKG8)) return MOE_ERR_UNSUPPORTED;
-    if (mfma_ok(act_dt, H, I, A, B, C)) {
+    if (w8 && (!tiles || K / 128 > kMaxKG8)) return MOE_ERR_UNSUPPORTED;
+    if (tiles) {
         GemmArgs g;
         g.A = static_cast<const uint16_t*>(A);
         g.B = static_cast<const uint16_t*>(B);
@@ -731,6 +802,9 @@ moe_status run_stage(bool up, const void* A, moe_dtype act_dt, const moe_plan* p
         g.N = N;
         g.El = plan->num_slots;
         g.NT = static_cast<int32_t>(up ? I / UP_COLS : H / BN);
+        g.amap = amap;
+        g.ak = ak;
+        g.arows = arows;
         // one block per CU, 8 XCDs: a super-tile of SM x SN tiles per XCD per round
         const int blocks = gemm::grid_blocks(stream);
         gemm::TileOrder to;
@@ -758,6 +832,9 @@ moe_status run_stage(bool up, const void* A, moe_dtype act_dt, const moe_plan* p
     g.K = K;
     g.N = N;
     g.El = plan->num_slots;
+    g.amap = amap;
+    g.ak = ak;
+    g.arows = arows;
     const dim3 grid(static_cast<unsigned>(gemm::grid_blocks(stream) * 4));
     if (act_dt == MOE_BF16) {
         if (up) hipLaunchKernelGGL((generic_gemm_kernel<uint16_t, true>), grid, dim3(256), 0, stream, g, A, B, C);
@@ -802,6 +879,23 @@ extern "C" moe_status moe_expert_gemm_up(const void* x_perm, moe_dtype act_dt, c
     if (w->dtype == MOE_FP8_E4M3 && w->fp8_act == MOE_FP8_ACT_E4M3)
         return moe::gemm::run_fp8_stage(true, x_perm, plan, w, H, I, h, workspace, workspace_bytes, stream);
     return moe::run_stage(true, x_perm, act_dt, plan, w, H, I, h, stream);
+}
+
+extern "C" moe_status moe_expert_gemm_up_gather(const void* global_x, moe_dtype act_dt,
+                                                const moe_plan* plan, const moe_expert_weights* w,
+                                                int64_t H, int64_t I, void* h, void* workspace,
+                                                size_t workspace_bytes, hipStream_t stream) {
+    moe_status st = moe::check_common(act_dt, plan, w, H, I);
+    if (st != MOE_OK) return st;
+    if (plan->cap == 0) return MOE_OK;
+    MOE_CHECK_ARG(plan->sorted_pair && plan->top_k >= 1 && plan->G >= 0);
+    MOE_CHECK_ARG(plan->G == 0 || global_x);
+    if (plan->G == 0) return MOE_OK;  // no pairs, so no rows
+    if (w->dtype == MOE_FP8_E4M3 && w->fp8_act == MOE_FP8_ACT_E4M3)
+        return moe::gemm::run_fp8_stage(true, global_x, plan, w, H, I, h, workspace, workspace_bytes, stream,
+                                        plan->sorted_pair, plan->top_k, plan->G);
+    return moe::run_stage(true, global_x, act_dt, plan, w, H, I, h, stream, plan->sorted_pair, plan->top_k,
+                          plan->G);
 }
 
 extern "C" moe_status moe_expert_gemm_down(const void* h, moe_dtype act_dt, const moe_plan* plan,

@@ -44,7 +44,9 @@ __global__ __launch_bounds__(256) void quant_fp8_kernel(const uint16_t* __restri
                                                         const int64_t* __restrict__ num_rows,
                                                         int64_t cap, int64_t K,
                                                         uint8_t* __restrict__ q,
-                                                        float* __restrict__ s_t) {
+                                                        float* __restrict__ s_t,
+                                                        const int32_t* __restrict__ amap,
+                                                        int32_t ak, int64_t arows) {
     int64_t rows = *num_rows;
     rows = rows < cap ? rows : cap;
     const int lane = lane_id();
@@ -52,13 +54,19 @@ __global__ __launch_bounds__(256) void quant_fp8_kernel(const uint16_t* __restri
     const int64_t nw = static_cast<int64_t>(gridDim.x) * 4;
     const int64_t groups = K / QB;
     for (int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / kWave; r < rows; r += nw) {
-        const uint16_t* src = act + r * K;
+        // the gather form reads row amap[r] / ak of the global buffer (no row: zeros)
+        int64_t srow = r;
+        if (amap != nullptr) {
+            const int32_t f = amap[r];
+            srow = f < 0 || f / ak >= arows ? -1 : f / ak;
+        }
+        const uint16_t* src = act + (srow >= 0 ? srow : 0) * K;
         uint8_t* dst = q + r * K;
         for (int64_t g0 = 0; g0 < groups; g0 += 4) {
             const int64_t g = g0 + sub;
             const bool valid = g < groups;
             uint4 v = make_uint4(0, 0, 0, 0);
-            if (valid) v = *reinterpret_cast<const uint4*>(src + g * QB + sl * 8);
+            if (valid && srow >= 0) v = *reinterpret_cast<const uint4*>(src + g * QB + sl * 8);
             const uint32_t u[4] = {v.x, v.y, v.z, v.w};
             float x[8];
 #pragma unroll
@@ -327,11 +335,12 @@ __global__ __launch_bounds__(F_THREADS, 1) void grouped_gemm_fp8_kernel(Fp8Args 
 size_t align256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
 
 moe_status launch_quant(const void* act, const int64_t* num_rows, int64_t cap, int64_t K, uint8_t* q,
-                        float* s_t, hipStream_t stream) {
+                        float* s_t, hipStream_t stream, const int32_t* amap = nullptr, int32_t ak = 1,
+                        int64_t arows = 0) {
     int64_t qblocks = ceil_div(cap, 4);
     if (qblocks > 4096) qblocks = 4096;
     hipLaunchKernelGGL(quant_fp8_kernel, dim3(static_cast<unsigned>(qblocks)), dim3(256), 0, stream,
-                       static_cast<const uint16_t*>(act), num_rows, cap, K, q, s_t);
+                       static_cast<const uint16_t*>(act), num_rows, cap, K, q, s_t, amap, ak, arows);
     MOE_LAUNCH_CHECK();
     return MOE_OK;
 }
@@ -346,7 +355,8 @@ size_t fp8_stage_workspace(int64_t cap, int64_t K) {
 
 moe_status run_fp8_stage(bool up, const void* act, const moe_plan* plan,
                          const moe_expert_weights* w, int64_t H, int64_t I, void* out,
-                         void* workspace, size_t ws_bytes, hipStream_t stream) {
+                         void* workspace, size_t ws_bytes, hipStream_t stream,
+                         const int32_t* amap, int32_t ak, int64_t arows) {
     if (plan->cap == 0) return MOE_OK;
     const int64_t K = up ? H : I, N = up ? I : H;
     if (H % F_BN != 0 || I % QB != 0) return MOE_ERR_UNSUPPORTED;  // whole 256-column down tiles
@@ -360,7 +370,7 @@ moe_status run_fp8_stage(bool up, const void* act, const moe_plan* plan,
     MOE_CHECK_ARG(workspace && aligned(workspace, 256));
     uint8_t* qa = static_cast<uint8_t*>(workspace);
     float* sa = reinterpret_cast<float*>(qa + align256(static_cast<size_t>(plan->cap * K)));
-    const moe_status qs = launch_quant(act, plan->num_rows, plan->cap, K, qa, sa, stream);
+    const moe_status qs = launch_quant(act, plan->num_rows, plan->cap, K, qa, sa, stream, amap, ak, arows);
     if (qs != MOE_OK) return qs;
     Fp8Args g;
     g.A = qa;

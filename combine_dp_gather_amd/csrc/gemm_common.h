@@ -118,11 +118,14 @@ inline bool pick_tile_order(int NT, int blocks, TileOrder* to) {
 }
 
 // fp8 path (expert_gemm_fp8.hip): quantise the stage's activations, then the block-scaled
-// fp8 GEMM.  `act` is [cap, K] bf16; workspace holds the fp8 codes and scales.
+// fp8 GEMM.  `act` is [cap, K] bf16, or with amap != NULL (gather form, up only) the
+// [arows, K] global buffer whose row amap[r] / ak is permuted row r (a negative entry is a
+// zero row); workspace holds the fp8 codes and scales.
 size_t fp8_stage_workspace(int64_t cap, int64_t K);
 moe_status run_fp8_stage(bool up, const void* act, const moe_plan* plan,
                          const moe_expert_weights* w, int64_t H, int64_t I, void* out,
-                         void* workspace, size_t ws_bytes, hipStream_t stream);
+                         void* workspace, size_t ws_bytes, hipStream_t stream,
+                         const int32_t* amap = nullptr, int32_t ak = 1, int64_t arows = 0);
 
 }  // namespace gemm
 }  // namespace moe

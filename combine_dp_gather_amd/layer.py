@@ -16,7 +16,7 @@ import torch
 
 from . import (PlanBuffers, layout_offsets, layout_sizes, make_expert_map, make_expert_weights,
                make_route_cfg, moe_combine, moe_dispatch, moe_dispatch_workspace_size,
-               moe_expert_gemm, moe_expert_gemm_down, moe_expert_gemm_up,
+               moe_expert_gemm, moe_expert_gemm_down, moe_expert_gemm_up, moe_expert_gemm_up_gather,
                moe_entry_gather, moe_expert_gemm_workspace_size, moe_gather, moe_gather_layout, moe_route,
                moe_scatter, moe_combine_scatter)
 
@@ -80,13 +80,19 @@ def spec_of(cfg) -> LayerSpec:
 
 
 class MoELayer:
-    """Buffers for one step shape (replica counts, gather mode) and the six calls."""
+    """Buffers for one step shape (replica counts, gather mode) and the six calls.
+
+    ``fuse_permute`` (default): dispatch builds the plan only and the up GEMM reads its rows
+    from ``global_x`` through ``sorted_pair`` (moe_expert_gemm_up_gather), so no ``x_perm``
+    copy is made or allocated; False runs the permuted copy and the plain up GEMM.  The
+    results are the same bits."""
 
     def __init__(self, spec: LayerSpec, weights: DeviceWeights, num_tokens: Sequence[int],
                  act_dtype: torch.dtype, mode: str = "auto", static_bound: int = 0,
                  is_extend: bool = False, align: int = 1, cap: Optional[int] = None,
-                 device="cuda", seg_stride: int = 0):
+                 device="cuda", seg_stride: int = 0, fuse_permute: bool = True):
         self.spec, self.w, self.device, self.dt = spec, weights, device, act_dtype
+        self.fuse_permute = fuse_permute
         self.layout = moe_gather_layout(num_tokens, mode, is_extend=is_extend,
                                         static_bound=static_bound)
         G = int(self.layout.rows)
@@ -108,7 +114,8 @@ class MoELayer:
         cap = self.plan.cap
         self.dispatch_ws = torch.empty(max(moe_dispatch_workspace_size(G, k, spec.num_local), 16),
                                        dtype=torch.uint8, device=device)
-        self.x_perm = torch.empty((max(cap, 1), H), dtype=act_dtype, device=device)
+        self.x_perm = None if fuse_permute else torch.empty((max(cap, 1), H), dtype=act_dtype,
+                                                            device=device)
         self.h = torch.empty((max(cap, 1), I), dtype=act_dtype, device=device)
         self.y_perm = torch.empty((max(cap, 1), H), dtype=act_dtype, device=device)
         self.gemm_ws = torch.empty(max(moe_expert_gemm_workspace_size(cap, H, I, act_dtype,
@@ -139,7 +146,7 @@ class MoELayer:
         if not self.G:
             return
         s = self.spec
-        if split:
+        if split or self.fuse_permute:
             self.experts_up()
             self.experts_down()
         else:
@@ -147,7 +154,12 @@ class MoELayer:
                             self.gemm_ws)
 
     def experts_up(self):
-        if self.G:
+        if not self.G:
+            return
+        if self.fuse_permute:
+            moe_expert_gemm_up_gather(self.global_x, self.plan, self.w.ew, self.spec.hidden,
+                                      self.spec.inter, self.h, self.gemm_ws)
+        else:
             moe_expert_gemm_up(self.x_perm, self.plan, self.w.ew, self.spec.hidden, self.spec.inter,
                                self.h, self.gemm_ws)
 
@@ -222,7 +234,7 @@ class TwoBatchOverlap:
 
     def __init__(self, spec: LayerSpec, weights: DeviceWeights, num_tokens: Sequence[int],
                  act_dtype: torch.dtype, mode: str = "sum", device="cuda", seg_stride: int = 0,
-                 cu_split: int = 0):
+                 cu_split: int = 0, fuse_permute: bool = True):
         """cu_split = n > 0 partitions the CUs (the vLLM page's SM allocation, section
         "第八步：SM 的分配"): both micro-batches' memory stages (0 and 2) run on a stream
         confined to CUs 0 .. n - 1, both micro-batches' expert GEMMs on a stream confined to the
@@ -231,7 +243,7 @@ class TwoBatchOverlap:
         self.num_tokens = [int(n) for n in num_tokens]
         self.slices = split_micro_batches(self.num_tokens)
         self.layers = [MoELayer(spec, weights, [b - a for a, b in sl], act_dtype, mode=mode, device=device,
-                                seg_stride=seg_stride) for sl in self.slices]
+                                seg_stride=seg_stride, fuse_permute=fuse_permute) for sl in self.slices]
         H = spec.hidden
         self.replicas_out = [torch.empty((n, H), dtype=act_dtype, device=device) for n in self.num_tokens]
         self.events = [[torch.cuda.Event() for _ in self.STAGES] for _ in range(2)]

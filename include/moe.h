@@ -267,7 +267,8 @@ size_t moe_dispatch_workspace_size(int64_t G, int32_t k, int32_t num_slots);
  *   map       expert map (see above); plan: caller buffers, filled here
  *   x_perm    device [cap, H] dt: row r = global_x[sorted_pair[r] / k]; alignment pad rows 0;
  *             rows >= num_rows are not written, nor (fixed capacity) the unused rows of a
- *             segment past its counts[e] pairs
+ *             segment past its counts[e] pairs.  NULL: the plan alone, no copy (global_x is
+ *             then not read and may be NULL); moe_expert_gemm_up_gather reads the rows in place
  *   workspace device, >= moe_dispatch_workspace_size(G, k, E_l) bytes, 16-byte aligned
  * Packed: cap >= G*min(k, E_l) + E_l*(align-1) can never overflow.  Fixed capacity: cap must
  * be >= E_l*seg_stride (else MOE_ERR_INVALID_ARG), and E_l*seg_stride < 2^31. */
@@ -378,6 +379,23 @@ moe_status moe_expert_gemm_up(const void* x_perm, moe_dtype act_dt, const moe_pl
 moe_status moe_expert_gemm_down(const void* h, moe_dtype act_dt, const moe_plan* plan,
                                 const moe_expert_weights* w, int64_t H, int64_t I, void* y_perm,
                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* moe_expert_gemm_up_gather -- moe_expert_gemm_up with the permute folded into its loads:
+ * permuted row r is read straight from global_x[sorted_pair[r] / top_k] (the rows the copy of
+ * moe_dispatch would have put there), so moe_dispatch can run with x_perm = NULL and the
+ * copy's read and write of every routed row are saved.  The vLLM walkthrough "vLLM 源码完全拆
+ * 解(二十七): Dual Batch Overlap" (figure of the modular-kernel blocks) draws permute as its
+ * own block before MM1; the products are the same either way.
+ *   global_x  device [plan->G, H] act_dt, the buffer moe_dispatch was given
+ *   plan      as for moe_expert_gemm_up; sorted_pair, top_k and G are read as well
+ *   h         device [cap, I] act_dt: bit-identical to moe_expert_gemm_up on the copied x_perm
+ * Kernels, alignment rules and errors as moe_expert_gemm_up with global_x in place of x_perm
+ * (moe_expert_gemm_fast_path with global_x tells the kernel), except that the bf16 tile
+ * kernels here also need plan->G * H * 2 < 2^31 bytes (they address global_x through one
+ * buffer resource); beyond that the generic kernel runs (fp8 weights: MOE_ERR_UNSUPPORTED). */
+moe_status moe_expert_gemm_up_gather(const void* global_x, moe_dtype act_dt, const moe_plan* plan,
+                                     const moe_expert_weights* w, int64_t H, int64_t I, void* h,
+                                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------------
  * moe_combine -- out[g] = routed_scale * sum_{j = 0..k-1, pair_row[g*k+j] >= 0}

@@ -53,13 +53,29 @@ def resized(name, tokens, **kw):
     return replace(cfg, num_tokens=tuple(tokens), static_bound=0, name=f"{name}-{len(tokens)}r", **kw)
 
 
-def build_layer(inp, mode="sum", align=1, cap=None, fp8_act="bf16", seg_stride=0):
+def build_layer(inp, mode="sum", align=1, cap=None, fp8_act="bf16", seg_stride=0, fuse_permute=True):
     from combine_dp_gather_amd.layer import DeviceWeights, MoELayer, spec_of
     cfg = inp.cfg
     w = DeviceWeights(inp, fp8_act=fp8_act)
     layer = MoELayer(spec_of(cfg), w, cfg.num_tokens, act_dtype(cfg), mode=mode,
-                     static_bound=cfg.static_bound, align=align, cap=cap, seg_stride=seg_stride)
+                     static_bound=cfg.static_bound, align=align, cap=cap, seg_stride=seg_stride,
+                     fuse_permute=fuse_permute)
     return layer
+
+
+def copy_path_rows(layer):
+    """For a layer run with the permute folded into the up GEMM: the permuted copy (moe_dispatch
+    with an x_perm buffer, re-deriving the same plan from the same ids) and the plain up GEMM
+    on it.  Returns (x_perm, h) of the copy path, device tensors."""
+    import combine_dp_gather_amd as m
+    s = layer.spec
+    xp = torch.empty((max(layer.plan.cap, 1), s.hidden), dtype=layer.dt, device=layer.device)
+    h = torch.empty_like(layer.h)
+    m.moe_dispatch(layer.global_x, layer.topk_ids[:layer.G], layer.emap, layer.plan, xp,
+                   layer.dispatch_ws)
+    m.moe_expert_gemm_up(xp, layer.plan, layer.w.ew, s.hidden, s.inter, h, layer.gemm_ws)
+    torch.cuda.synchronize()
+    return xp, h
 
 
 def check_combine_bound(out_dev, y_dev, w_dev, pair_row, k, scale=1.0, chunk=2048):

@@ -136,6 +136,20 @@ def test_argument_errors_return_before_any_launch(m):
     w = _lib.ExpertWeights(_lib.MOE_F32, 0, 1, 1, None, None)
     assert lib.moe_expert_gemm(1, _lib.MOE_BF16, ctypes.byref(plan), ctypes.byref(w), 256, 128, 1, 1,
                                1 << 30, None) == _lib.MOE_ERR_INVALID_ARG
+    # the gathering up GEMM reads sorted_pair, top_k and G: a plan without sorted_pair, a
+    # zero top_k or a missing global buffer are rejected; with no global rows it is a no-op
+    w = _lib.ExpertWeights(_lib.MOE_BF16, 0, 1, 1, None, None)
+    nosp = _lib.Plan(1, 1, None, 1, 1, 1, 100, 10, 2, 16, 1, 0)
+    assert lib.moe_expert_gemm_up_gather(1, _lib.MOE_BF16, ctypes.byref(nosp), ctypes.byref(w), 256, 128, 1,
+                                         None, 0, None) == _lib.MOE_ERR_INVALID_ARG
+    k0 = _lib.Plan(1, 1, 1, 1, 1, 1, 100, 10, 0, 16, 1, 0)
+    assert lib.moe_expert_gemm_up_gather(1, _lib.MOE_BF16, ctypes.byref(k0), ctypes.byref(w), 256, 128, 1,
+                                         None, 0, None) == _lib.MOE_ERR_INVALID_ARG
+    assert lib.moe_expert_gemm_up_gather(None, _lib.MOE_BF16, ctypes.byref(plan), ctypes.byref(w), 256, 128,
+                                         1, None, 0, None) == _lib.MOE_ERR_INVALID_ARG
+    g0 = _lib.Plan(1, 1, 1, 1, 1, 1, 100, 0, 2, 16, 1, 0)
+    assert lib.moe_expert_gemm_up_gather(None, _lib.MOE_BF16, ctypes.byref(g0), ctypes.byref(w), 256, 128,
+                                         1, None, 0, None) == _lib.MOE_OK
     # combine: bad dtype
     assert lib.moe_combine(1, 9, ctypes.byref(plan), 1, 1.0, 64, 1, None) == _lib.MOE_ERR_INVALID_ARG
     # fused exit: bad dtype; layout rows that do not match the plan; an unaligned replica

@@ -17,7 +17,7 @@ import torch
 
 import moe_synth
 import oracle
-from gpu_helpers import act_dtype, build_layer, say, to_np
+from gpu_helpers import act_dtype, build_layer, copy_path_rows, say, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -171,7 +171,7 @@ def test_layer_step_with_entry():
     reps = [gx[offs[i]:offs[i] + n].copy() for i, n in enumerate(cfg.num_tokens)]
     ref = oracle.run_layer(replace(full, replicas=reps), "sum")
     assert np.array_equal(to_np(layer.topk_ids)[:layer.G], ref["ids"])
-    assert np.array_equal(to_np(layer.x_perm)[:ref["plan"]["num_rows"]], ref["x_perm"])
+    assert np.array_equal(to_np(copy_path_rows(layer)[0])[:ref["plan"]["num_rows"]], ref["x_perm"])
     out = oracle.as_f32(to_np(layer.out))
     err = oracle.rel_err(out, ref["out"])
     say(f"  out rel err {err:.3e}")

@@ -24,7 +24,7 @@ import torch
 
 import moe_synth
 import oracle
-from gpu_helpers import build_layer, check_combine_bound, replicas_to_device, say, to_np, tol_for
+from gpu_helpers import build_layer, check_combine_bound, copy_path_rows, replicas_to_device, say, to_np, tol_for
 
 pytestmark = pytest.mark.gpu
 
@@ -102,9 +102,18 @@ def test_prefill_fullsize(name):
     R = plan["num_rows"]
     assert np.array_equal(to_np(gp.sorted_pair)[:R], plan["sorted_pair"])
     assert np.array_equal(to_np(gp.pair_row)[:G * k], plan["pair_row"])
+    # the layer's up GEMM gathers its rows from global_x; the permuted copy runs beside it, is
+    # held to the oracle, and the copy path's h to the gathered one, every routed row bitwise
     xp = oracle.permute_rows(gx, plan)
-    assert np.array_equal(to_np(layer.x_perm)[:R], xp)
-    say(f"  plan and permuted rows bitwise (R={R})")
+    xp_dev, h_copy = copy_path_rows(layer)
+    assert np.array_equal(to_np(xp_dev)[:R], xp)
+    real = np.zeros(R, dtype=bool)
+    for e in range(cfg.num_local):
+        a = int(plan["seg_offsets"][e])
+        real[a:a + int(plan["counts"][e])] = True
+    assert np.array_equal(to_np(layer.h)[:R][real], to_np(h_copy)[:R][real])
+    del h_copy
+    say(f"  plan and permuted rows bitwise (R={R}); gathered h equals the copy path's")
 
     tol = tol_for(cfg)
     y_ref = _expert_rows(inp, xp, plan)
@@ -133,14 +142,18 @@ def test_prefill_fullsize(name):
     # against the unquantised experts is reported
     del layer, out_np
     torch.cuda.empty_cache()
+    # (xp_dev, the copied rows, is kept for the quantisation check below)
     layer = build_layer(inp, "sum", fp8_act="e4m3")
     layer.forward(replicas_to_device(inp))
     torch.cuda.synchronize()
     assert np.array_equal(to_np(layer.plan.sorted_pair)[:R], plan["sorted_pair"])
+    h_copy = copy_path_rows(layer)[1]  # the quantiser reads gathered rows: the same codes
+    assert np.array_equal(to_np(layer.h)[:R][real], to_np(h_copy)[:R][real])
+    del h_copy
     import combine_dp_gather_amd as m
     q = torch.empty((R, H), dtype=torch.uint8, device="cuda")
     st = torch.empty((H // 128, R), dtype=torch.float32, device="cuda")
-    m.moe_quant_act_fp8(layer.x_perm[:R], layer.plan.num_rows, q, st)
+    m.moe_quant_act_fp8(xp_dev[:R], layer.plan.num_rows, q, st)
     torch.cuda.synchronize()
     rq, rs = oracle.quant_group_e4m3(xp)
     assert np.array_equal(to_np(q), rq)

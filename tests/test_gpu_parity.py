@@ -12,23 +12,31 @@ import torch
 
 import moe_synth
 import oracle
-from gpu_helpers import (build_layer, check_combine_bound, replicas_to_device, resized, say, to_np, tol_for)
+from gpu_helpers import (build_layer, check_combine_bound, copy_path_rows, replicas_to_device, resized, say,
+                         to_np, tol_for)
 
 pytestmark = pytest.mark.gpu
 
 
-def run_and_compare(cfg, mode="sum", align=1, cap=None, check_mode_pair=None, fp8_act="bf16", seg_stride=0):
-    return run_and_compare_inputs(moe_synth.make_inputs(cfg), mode, align, cap, fp8_act, seg_stride)
+def run_and_compare(cfg, mode="sum", align=1, cap=None, check_mode_pair=None, fp8_act="bf16", seg_stride=0,
+                    fuse_permute=True):
+    return run_and_compare_inputs(moe_synth.make_inputs(cfg), mode, align, cap, fp8_act, seg_stride,
+                                  fuse_permute)
 
 
-def run_and_compare_inputs(inp, mode="sum", align=1, cap=None, fp8_act="bf16", seg_stride=0):
+def run_and_compare_inputs(inp, mode="sum", align=1, cap=None, fp8_act="bf16", seg_stride=0,
+                           fuse_permute=True):
     """The six steps on the GPU against the oracle on the same inputs (expert table included).
-    seg_stride > 0: the fixed-capacity dispatch layout on both sides."""
+    seg_stride > 0: the fixed-capacity dispatch layout on both sides.  fuse_permute (the
+    layer's default): the up GEMM gathers its rows from global_x; the permuted copy and the
+    plain up GEMM then run beside it, the copy is held to the oracle and the two h to each
+    other bit for bit."""
     cfg = inp.cfg
     say(f"[parity] {cfg.name} tokens={cfg.num_tokens} H={cfg.hidden} I={cfg.inter} "
-        f"E={cfg.num_experts} k={cfg.top_k} mode={mode} align={align} cap={cap} seg_stride={seg_stride}")
+        f"E={cfg.num_experts} k={cfg.top_k} mode={mode} align={align} cap={cap} seg_stride={seg_stride} "
+        f"fuse_permute={fuse_permute}")
     ref = oracle.run_layer(inp, mode, align=align, cap=cap, seg_stride=seg_stride, fp8_act=fp8_act)
-    layer = build_layer(inp, mode, align, cap, fp8_act, seg_stride)
+    layer = build_layer(inp, mode, align, cap, fp8_act, seg_stride, fuse_permute)
     reps = replicas_to_device(inp)
     layer.forward(reps)
     torch.cuda.synchronize()
@@ -55,7 +63,17 @@ def run_and_compare_inputs(inp, mode="sum", align=1, cap=None, fp8_act="bf16", s
     rows = min(rp["num_rows"], rp["cap"])
     assert np.array_equal(to_np(plan.sorted_pair)[:rows], rp["sorted_pair"])
     assert np.array_equal(to_np(plan.pair_row)[:G * cfg.top_k], rp["pair_row"])
-    xp_gpu = to_np(layer.x_perm)[:rows]
+    real = np.zeros(rows, dtype=bool)
+    for e in range(cfg.num_local):
+        a = int(rp["seg_offsets"][e])
+        real[a:min(a + int(rp["counts"][e]), rows)] = True
+    if layer.x_perm is None:
+        xp_dev, h_copy = copy_path_rows(layer)
+        assert np.array_equal(to_np(layer.h)[:rows][real], to_np(h_copy)[:rows][real])
+        say(f"  gathering up GEMM: h bitwise equal to the copy path's on {int(real.sum())} rows")
+    else:
+        xp_dev = layer.x_perm
+    xp_gpu = to_np(xp_dev)[:rows]
     if seg_stride:  # fixed capacity: rows past a segment's pairs are never written
         used = rp["sorted_pair"] >= 0
         assert np.array_equal(xp_gpu[used], ref["x_perm"][used])
@@ -65,10 +83,6 @@ def run_and_compare_inputs(inp, mode="sum", align=1, cap=None, fp8_act="bf16", s
     # too (the codes of x_perm are the same bits; those of h can differ by one step where the
     # two sides' h land on opposite sides of a rounding boundary), held to the fp8 bar
     tol = tol_for(cfg)
-    real = np.zeros(rows, dtype=bool)
-    for e in range(cfg.num_local):
-        a = int(rp["seg_offsets"][e])
-        real[a:min(a + int(rp["counts"][e]), rows)] = True
     if real.any():
         y_gpu = oracle.as_f32(to_np(layer.y_perm)[:rows])[real]
         err = oracle.rel_err(y_gpu, ref["y_perm"][real])
@@ -186,7 +200,7 @@ def test_expert_gemm_unaligned_buffers_take_generic_path():
     # fp32 matrix cores, held to the same bar against the oracle, and the query says so
     from combine_dp_gather_amd import moe_expert_gemm_down, moe_expert_gemm_fast_path, moe_expert_gemm_up
     cfg = resized("cfg4", (300, 0, 517), hidden=2048, inter=1024, num_experts=64)
-    layer, ref = run_and_compare(cfg)
+    layer, ref = run_and_compare(cfg, fuse_permute=False)
     rp = ref["plan"]
     rows = min(rp["num_rows"], rp["cap"])
     real = np.zeros(rows, dtype=bool)
@@ -301,7 +315,7 @@ def test_identity_experts_combine_returns_weighted_sum():
     import combine_dp_gather_amd as m
     cfg = resized("cfg3", (50, 31), hidden=1024, inter=512, num_experts=64, num_local=64)
     inp = moe_synth.make_inputs(cfg)
-    layer = build_layer(inp)
+    layer = build_layer(inp, fuse_permute=False)
     layer.gather(replicas_to_device(inp))
     layer.route()
     layer.dispatch()
