@@ -130,6 +130,14 @@ def test_prefill_fullsize(name):
     for i, y in enumerate(layer.replicas_out):
         a, n = offs[i], cfg.num_tokens[i]
         assert np.array_equal(to_np(y), out_np[a:a + n])
+    # the fused exit (what bench.py's step runs): the same bits in every replica's buffer
+    fresh = [torch.full_like(y, 5.0) for y in layer.replicas_out]
+    layer.combine_scatter(fresh)
+    torch.cuda.synchronize()
+    for y, f in zip(layer.replicas_out, fresh):
+        assert torch.equal(y.view(torch.int16), f.view(torch.int16))
+    del fresh
+    say("  fused exit: every replica row bitwise equal to combine, then scatter")
 
     if cfg.weight_format != "fp8_block":
         return
