@@ -4,11 +4,11 @@
 
     python bench.py [--steps K] [--warmup W] [--workload cfg4]
 
-A step is one pass of the whole path over one batch whose inputs are already resident in
-HBM: gather, route, dispatch (the plan; the up GEMM gathers its rows itself, --copy-permute
-writes the permuted copy instead), the two expert GEMMs, and combine + scatter as one fused
-call (--split-exit runs them as two).  By default the step's calls are captured once in a HIP
-graph and each timed step is one replay (--eager launches them call by call).  Before every timed step a kernel writes a
+A step is one pass of all six C-ABI calls over one batch whose inputs are already resident
+in HBM (dispatch builds the plan and the up GEMM gathers its rows from the global buffer;
+--copy-permute has dispatch write the permuted copy instead).  By default the six calls are
+captured once in a HIP graph and each timed step is one replay (--eager launches them call by
+call).  Before every timed step a kernel writes a
 512 MiB scratch buffer (outside the step's event pair), so the Infinity Cache and the L2 hold
 none of the step's data: the step figures are cold-cache ones, as median, p90 and mean over
 the timed steps; the same steps back to back give the warm figures beside them.  Prints one
@@ -241,9 +241,9 @@ def main():
     ap.add_argument("--entry", action="store_true",
                     help="run the fused entry step (residual add + RMSNorm + gather) in the step "
                          "in place of the plain gather; without it the fused step is timed apart")
-    ap.add_argument("--split-exit", action="store_true",
-                    help="run combine, then scatter, as two calls (without this flag the step runs "
-                         "the fused exit: combine written straight into the replicas' buffers)")
+    ap.add_argument("--exit", action="store_true",
+                    help="run the fused exit (combine written straight into the replicas' buffers) "
+                         "in place of combine + scatter")
     ap.add_argument("--seg-stride", type=int, default=0, metavar="ROWS",
                     help="dispatch into the fixed-capacity layout, ROWS rows per local slot (the "
                          "global row count never overflows); 0: packed segments")
@@ -321,7 +321,7 @@ def main():
         ("gather", lambda: layer.gather(reps))
     names = [first[0], "route", "dispatch", "gemm_up", "gemm_down"]
     calls = [first[1], layer.route, layer.dispatch, lambda: layer.experts_up(), lambda: layer.experts_down()]
-    if not args.split_exit:
+    if args.exit:
         names.append("combine_scatter")
         calls.append(layer.combine_scatter)
     else:
@@ -355,8 +355,8 @@ def main():
     tbo = None
     if args.tbo:
         from combine_dp_gather_amd.layer import TwoBatchOverlap
-        if args.entry or not args.split_exit or eplb_info is not None:
-            raise SystemExit("--tbo runs the plain six-call step only (with --split-exit)")
+        if args.entry or args.exit or eplb_info is not None:
+            raise SystemExit("--tbo runs the plain six-call step only")
         tbo = TwoBatchOverlap(spec_of(cfg), w, layer.sizes, act, mode=args.mode, device=dev,
                               seg_stride=args.seg_stride, cu_split=args.cu_split,
                               fuse_permute=not args.copy_permute)
@@ -551,7 +551,7 @@ def main():
                                          "GEMMs on the others" if args.cu_split else ""))
                                      if args.tbo else "1"),
                    "first_step": "fused residual add + RMSNorm + gather" if args.entry else "plain gather",
-                   "last_step": "combine, then scatter" if args.split_exit else "fused combine + scatter",
+                   "last_step": "fused combine + scatter" if args.exit else "combine, then scatter",
                    "dispatch_layout": (f"fixed capacity, {args.seg_stride} rows per slot" if args.seg_stride
                                        else "packed segments"),
                    "permute": ("copy to x_perm in dispatch" if args.copy_permute

@@ -28,8 +28,7 @@ def test_layer_step_graph_replays_bitwise(name):
     # fixed-capacity layout (16 slots x 384 rows), the decode workload with the fused
     # entry step (its residual is restored before every run, since the step updates it), the
     # decode workload with the fused exit (the global output buffer is then not written),
-    # and the whole prefill batch (8 x 4096 rows, H = 7168) with the fused exit, the step
-    # bench.py replays
+    # and the whole prefill batch (8 x 4096 rows, H = 7168), the step bench.py replays
     if name == "mid":
         cfg = resized("cfg4", (611, 0, 1203, 377), hidden=2048, inter=1024, num_experts=64)
     else:
@@ -50,7 +49,7 @@ def test_layer_step_graph_replays_bitwise(name):
             for a, b in zip(entry[0], res0):
                 a.copy_(b)
 
-    fused_exit = name in ("cfg3-exit", "cfg4")  # bench.py's step ends with the fused exit
+    fused_exit = name == "cfg3-exit"
 
     def outputs():
         return _outputs(layer, not fused_exit) + ([to_np(r).copy() for r in entry[0]] if entry else [])
