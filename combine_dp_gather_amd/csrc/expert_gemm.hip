@@ -14,14 +14,16 @@
 // up GEMM's 256 weight rows being 128 gate rows and the same 128 up rows (SiLU * up in
 // registers, only h written), operands moved global -> LDS by buffer DMA, rows past a
 // segment's end read as zeros and never stored, and one owner per output tile:
-//   - grouped_gemm_pp_kernel: slots of more than 64 rows.  256 x 256 tiles, 8 waves in two
+//   - grouped_gemm_pp_kernel: slots of more than 64 rows (not launched when no slot can hold
+//     more than 512 rows: the streaming kernel then takes every slot).  256 x 256 tiles, 8 waves in two
 //     groups that alternate between an MFMA phase and a memory phase; persistent grid, one
 //     block per CU, XCD-grouped tile order (gemm_common.h).  fp8 weights with bf16
 //     activations (the default for e4m3 weights) run here too: weight rows are staged as
 //     fp8 (half the bytes) and a lane's 16 weight bytes are dequantised (exact e4m3 -> fp32,
 //     times the block's fp32 scale, RNE to bf16) into the fragments of two MFMA steps.
-//   - grouped_gemm_stream_kernel: bf16 weights, slots of 1-64 rows, which stream their
-//     weights: 64 x 128 tiles, 64-deep slices, five stages, non-temporal weight loads.
+//   - grouped_gemm_stream_kernel: bf16 weights, slots of 1-64 rows (every slot for batches of
+//     at most 512 rows), which stream their weights: 64 x 128 tiles, 64-deep slices, five
+//     stages, non-temporal weight loads.
 //   - generic_gemm_kernel: any other shape, alignment or activation dtype, on the fp32
 //     matrix cores.
 // fp8 weights with per-1x128-group e4m3 activations (fp8 matrix cores, fp32 promotion per K
@@ -69,6 +71,9 @@ struct GemmArgs {
     const int32_t* amap;
     int32_t ak;
     int64_t arows;
+    // the streaming kernel takes the slots of at most st_hi rows (ST_BM_SPLIT, or every slot
+    // when no slot can outgrow a few of its tiles and the ping-pong kernel is not launched)
+    int64_t st_hi;
 };
 
 // Offset past every buffer resource this file builds (each covers under 2^31 bytes): a DMA
@@ -169,6 +174,10 @@ __device__ __forceinline__ int64_t k_start64(int e, int32_t tile256, int64_t ste
 }
 
 constexpr int ST_BM_SPLIT = 64;  // slots with more rows than this run here, the rest in the streaming kernel
+// When no slot can hold more rows than this (G, or the fixed capacity), the streaming kernel
+// takes every slot alone: at most 8 of its 64-row tiles per slot, whose repeated weight reads
+// come from the caches, against a ping-pong launch that would find few tiles or none.
+constexpr int64_t kStreamOnlyRows = 512;
 constexpr int PP_THREADS = 512;
 constexpr int PP_BK = 32;                        // K per slice
 constexpr int PP_STAGES = 4;
@@ -483,13 +492,14 @@ __global__ __launch_bounds__(PP_THREADS, 1) void grouped_gemm_pp_kernel(GemmArgs
 // DMAs two activation blocks and four weight blocks of 8 rows (all gate or all up), one
 // barrier per slice.  The MFMAs see the K values in the same order as in the ping-pong kernel
 // (four 16-deep steps per slice) and the epilogue is its epilogue, so the bits are the same.
-// The ping-pong kernel takes the slots with more than 64 rows; the two kernels number their
-// own tiles on the device, so the host never reads the counts.
+// The ping-pong kernel takes the slots with more than 64 rows, except in batches of at most
+// 512 rows, where this kernel takes every slot; the two kernels number their own tiles on the
+// device, so the host never reads the counts.
 constexpr int ST_THREADS = 256;
 // cache-policy operand of the weight DMAs: non-temporal (each weight line is read once).
 // Measured on the decode shape, cold: gate+up 0.148 -> 0.082 ms against plain loads.
 constexpr int kNonTemporal = 2;
-constexpr int ST_BM = ST_BM_SPLIT;               // rows per tile = largest slot taken
+constexpr int ST_BM = ST_BM_SPLIT;               // rows per tile (the largest slot taken, unless st_hi says more)
 constexpr int ST_BN = 128;                       // weight rows per tile
 constexpr int ST_UPC = ST_BN / 2;                // up: i-columns per tile
 constexpr int ST_STAGES = 5;
@@ -511,7 +521,7 @@ __global__ __launch_bounds__(ST_THREADS, 1) void grouped_gemm_stream_kernel(Gemm
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int rbk = w & 1, cg = w >> 1;  // row block, column group
     const int32_t total_mt =
-        gemm::number_tiles<ST_BM, ST_THREADS>(a.counts, a.seg, a.cap, a.El, tile_prefix, part, 0, ST_BM);
+        gemm::number_tiles<ST_BM, ST_THREADS>(a.counts, a.seg, a.cap, a.El, tile_prefix, part, 0, a.st_hi);
     const uint32_t row_bytes = static_cast<uint32_t>(a.K) * 2u;
     const int32_t NT = static_cast<int32_t>((UP ? 2 : 1) * a.N / ST_BN);
     const int64_t tiles = static_cast<int64_t>(total_mt) * NT;
@@ -805,6 +815,7 @@ moe_status run_stage(bool up, const void* A, moe_dtype act_dt, const moe_plan* p
         g.amap = amap;
         g.ak = ak;
         g.arows = arows;
+        g.st_hi = ST_BM_SPLIT;
         // one block per CU, 8 XCDs: a super-tile of SM x SN tiles per XCD per round
         const int blocks = gemm::grid_blocks(stream);
         gemm::TileOrder to;
@@ -815,12 +826,21 @@ moe_status run_stage(bool up, const void* A, moe_dtype act_dt, const moe_plan* p
             else hipLaunchKernelGGL((grouped_gemm_pp_kernel<false, true>), grid, dim3(PP_THREADS), 0, stream, g, to);
         } else {
             // slots of at most 64 rows stream their weights in 64-row tiles, the rest run the
-            // ping-pong kernel; each kernel numbers its own slots' tiles on the device
+            // ping-pong kernel; each kernel numbers its own slots' tiles on the device.  A slot
+            // holds at most G rows (a token picks a slot once), at most seg_stride with fixed
+            // capacity: when that bound is within kStreamOnlyRows the streaming kernel takes
+            // every slot (a few 64-row tiles each) and the ping-pong launch, which would find
+            // no tile or very few, is left out.  Both kernels give the same bits for a slot.
+            const int64_t max_rows = plan->seg_stride > 0 && plan->seg_stride < plan->G ? plan->seg_stride : plan->G;
+            const bool stream_only = max_rows <= kStreamOnlyRows;
+            g.st_hi = stream_only ? INT64_MAX : ST_BM_SPLIT;
             if (up) hipLaunchKernelGGL((grouped_gemm_stream_kernel<true>), grid, dim3(ST_THREADS), 0, stream, g);
             else hipLaunchKernelGGL((grouped_gemm_stream_kernel<false>), grid, dim3(ST_THREADS), 0, stream, g);
-            MOE_LAUNCH_CHECK();
-            if (up) hipLaunchKernelGGL((grouped_gemm_pp_kernel<true, false>), grid, dim3(PP_THREADS), 0, stream, g, to);
-            else hipLaunchKernelGGL((grouped_gemm_pp_kernel<false, false>), grid, dim3(PP_THREADS), 0, stream, g, to);
+            if (!stream_only) {
+                MOE_LAUNCH_CHECK();
+                if (up) hipLaunchKernelGGL((grouped_gemm_pp_kernel<true, false>), grid, dim3(PP_THREADS), 0, stream, g, to);
+                else hipLaunchKernelGGL((grouped_gemm_pp_kernel<false, false>), grid, dim3(PP_THREADS), 0, stream, g, to);
+            }
         }
         MOE_LAUNCH_CHECK();
         return MOE_OK;
