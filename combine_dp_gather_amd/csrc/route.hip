@@ -284,7 +284,7 @@ __global__ __launch_bounds__(128 * WMR, 1) void gate_exact8_kernel(const T* __re
 // fragments are spread between this slice's MFMAs.
 constexpr int C16_K = 64;           // h per slice
 constexpr int C16_RS = C16_K + 4;   // LDS row stride in floats
-constexpr int C16_D = 4;            // slices in flight (register sets), even
+constexpr int C16_D = 8;            // slices in flight (register sets), even
 constexpr int C16_WAVES = 4;        // independent waves per block, as 2 x 2 tiles
 
 template <typename T>
@@ -353,6 +353,31 @@ struct Chain16Stage {
 template <int Q>
 struct SliceIdx {
     static constexpr int kValue = Q;
+};
+
+// Slices sl + Q .. sl + D - 1 in order, each with its register set Q fixed at compile time:
+// all of them (full), or those before ns (tail).
+template <int Q, int D>
+struct SliceRun {
+    template <typename F>
+    __device__ static void full(F& f, int64_t sl) {
+        f(SliceIdx<Q>(), sl + Q);
+        SliceRun<Q + 1, D>::full(f, sl);
+    }
+    template <typename F>
+    __device__ static void tail(F& f, int64_t sl, int64_t ns) {
+        if (sl + Q < ns) {
+            f(SliceIdx<Q>(), sl + Q);
+            SliceRun<Q + 1, D>::tail(f, sl, ns);
+        }
+    }
+};
+template <int D>
+struct SliceRun<D, D> {
+    template <typename F>
+    __device__ static void full(F&, int64_t) {}
+    template <typename F>
+    __device__ static void tail(F&, int64_t, int64_t) {}
 };
 
 // FAST (whole slices, aligned rows) is a template parameter: a run-time branch around the
@@ -428,21 +453,211 @@ __global__ __launch_bounds__(64 * C16_WAVES) void gate_chain16_kernel(const T* _
         __builtin_amdgcn_sched_barrier(0);
     };
     int64_t sl = 0;
-    for (; sl + D <= ns; sl += D) {
-        slice(SliceIdx<0>(), sl);
-        slice(SliceIdx<1>(), sl + 1);
-        slice(SliceIdx<2>(), sl + 2);
-        slice(SliceIdx<3>(), sl + 3);
-    }
-    static_assert(D == 4, "the unrolled loop and its tail cover four register sets");
-    if (sl < ns) slice(SliceIdx<0>(), sl);
-    if (sl + 1 < ns) slice(SliceIdx<1>(), sl + 1);
-    if (sl + 2 < ns) slice(SliceIdx<2>(), sl + 2);
+    for (; sl + D <= ns; sl += D) SliceRun<0, D>::full(slice, sl);
+    SliceRun<0, D>::tail(slice, sl, ns);
     // lane l, register r: row 4 (l / 16) + r, expert l % 16 of the wave's block
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int64_t g = m0 + 4 * j + r;
         const int64_t e = n0 + i16;
+        if (g < G && e < E) {
+            const bool valid = row_valid == nullptr || row_valid[g] != 0;
+            logits[g * E + e] = valid ? acc[r] : 0.f;
+        }
+    }
+}
+
+// ---- small batches with chains on their own SIMDs
+// When a batch has at most one block per CU, each chain's time is the whole kernel's, and a
+// dependent 16x16x4 step costs its ~32-cycle issue plus every other instruction the wave
+// issues between steps: a vector-ALU or LDS instruction in the MFMA wave's stream is not
+// hidden behind the step but adds ~5 cycles to it (measured on this part: 13.4 ns per step
+// alone, 22.4 ns with four VALU instructions between steps).  Widening a slice to fp32 and
+// storing it takes ~80 such instructions per 16 steps.  So here a block of four waves (one
+// per SIMD) has two chain waves, which only read fragments and issue MFMAs, and two helper
+// waves, which load each slice from HBM, widen it and store it to the LDS.  The block covers
+// 16 rows x 32 experts (chain wave c: experts 16 c .. + 15); the LDS holds three stages of two
+// slices, each slice 16 x rows and 32 w rows in the layout of gate_chain16_kernel, and one
+// barrier per stage (a handover) passes slices from the helpers to the chains.  The MFMAs see
+// the operands and the order of gate_chain16_kernel: the same bits.  At 384 rows and 256
+// experts (H = 7168) the kernel takes 44 us against 59 us for gate_chain16_kernel; ~33 cycles
+// of its ~47 per step are the MFMA itself, the rest the chains' fragment reads and the LDS and
+// memory traffic of the helpers beside them.
+constexpr int C16P_STAGES = 3;
+constexpr int C16P_SPH = 2;  // slices per handover (stage)
+constexpr int C16P_LEAD = 3;  // handovers of helper loads in flight
+constexpr int C16P_D = C16P_LEAD * C16P_SPH;  // helper register sets (slice s in set s mod D)
+static_assert(C16P_LEAD >= 2, "the prologue fills two stages");
+
+template <typename T, bool FAST>
+__global__ __launch_bounds__(256, 1) void gate_chain16p_kernel(const T* __restrict__ x,
+                                                               const T* __restrict__ w,
+                                                               const int32_t* __restrict__ row_valid,
+                                                               int64_t G, int64_t E, int64_t H,
+                                                               float* __restrict__ logits) {
+    constexpr int C = GateIO<T>::kChunk;      // values per 16-byte piece
+    constexpr int PPR = C16_K / C;            // pieces per row and slice (8 bf16, 16 fp32)
+    constexpr int RPI = 64 / PPR;             // rows per load instruction (8, 4)
+    constexpr int NI = (16 + 32) / RPI / 2;   // load instructions per helper and slice (3, 6)
+    constexpr int XI = 16 / RPI;              // the first XI instructions of the block are x rows
+    constexpr int ROWS = 48;                  // stage rows: 16 x, then 32 w
+    constexpr int STAGE = ROWS * C16_RS;      // one slice
+    __shared__ __attribute__((aligned(16))) float lds[C16P_STAGES * C16P_SPH * STAGE];
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+    const int64_t m0 = static_cast<int64_t>(blockIdx.x) * 16;
+    const int64_t n0 = static_cast<int64_t>(blockIdx.y) * 32;
+    const int64_t ns = ceil_div(H, C16_K);
+    const int64_t nh = ceil_div(ns, C16P_SPH);  // handovers
+    const bool helper = wv >= 2;
+    // LDS slot of slice s: stage (s / SPH) mod 3, position s mod SPH in it
+    auto slot = [](int64_t s) {
+        return static_cast<int>(((s / C16P_SPH) % C16P_STAGES) * C16P_SPH + s % C16P_SPH);
+    };
+
+    // ---- helper state: instruction q of this helper is block instruction hq = NI (wv - 2) + q,
+    // rows RPI hq .. + RPI - 1 of the stage (x rows first, then w rows)
+    const int64_t xrows = G - m0 < 16 ? G - m0 : 16;
+    const int64_t wrows = E - n0 < 32 ? E - n0 : 32;
+    const __amdgpu_buffer_rsrc_t rx = gemm::make_rsrc_uniform(
+        x + m0 * H, static_cast<uint32_t>((xrows > 0 ? xrows : 0) * H * static_cast<int64_t>(sizeof(T))));
+    const __amdgpu_buffer_rsrc_t rw = gemm::make_rsrc_uniform(
+        w + n0 * H, static_cast<uint32_t>((wrows > 0 ? wrows : 0) * H * static_cast<int64_t>(sizeof(T))));
+    const int prow = lane / PPR, ppiece = lane % PPR;  // this lane's row in an instruction, piece
+    uint4 reg[C16P_D][NI];
+    // a slice past the last is staged as x = -0, w = +0: each of its steps adds a -0
+    // product, which leaves every accumulator's bits in place, so the chains run it blindly
+    const uint32_t xpad = sizeof(T) == 2 ? 0x80008000u : 0x80000000u;
+    auto hload = [&](int set, int64_t sl) {
+        // slices past the last re-read the last one (no branch around the loads: the
+        // compiler's wait counts would then drain every load in flight once per loop trip);
+        // hstore writes the padding in their place
+        const int64_t k0 = (sl < ns ? sl : ns - 1) * C16_K;
+#pragma unroll
+        for (int q = 0; q < NI; ++q) {
+            const int hq = NI * (wv - 2) + q;
+            const bool isx = hq < XI;
+            const int r = (isx ? hq : hq - XI) * RPI + prow;  // row within x (0..15) or w (0..31)
+            if constexpr (FAST) {
+                const int off = static_cast<int>((r * H + ppiece * C) * static_cast<int64_t>(sizeof(T)));
+                const int so = static_cast<int>(k0 * static_cast<int64_t>(sizeof(T)));
+                const gate_u32x4 v = isx ? __builtin_amdgcn_raw_buffer_load_b128(rx, off, so, 0)
+                                         : __builtin_amdgcn_raw_buffer_load_b128(rw, off, so, 0);
+                reg[set][q] = make_uint4(v.x, v.y, v.z, v.w);
+            } else {
+                reg[set][q] = isx ? load_piece<T>(x, G, H, m0 + r, k0 + ppiece * C, GateIO<T>::kNegZero)
+                                  : load_piece<T>(w, E, H, n0 + r, k0 + ppiece * C, T(0));
+            }
+        }
+    };
+    auto hstore = [&](int set, int sslot, int64_t sl) {
+        const uint32_t keep = sl < ns ? 0xffffffffu : 0u;
+#pragma unroll
+        for (int q = 0; q < NI; ++q) {
+            const int hq = NI * (wv - 2) + q;
+            const int srow = hq * RPI + prow;  // slice rows: x rows 0..15, w rows 16..47
+            const uint32_t pad = (hq < XI ? xpad : 0u) & ~keep;
+            const uint4 r = reg[set][q];
+            const uint4 v = make_uint4((r.x & keep) | pad, (r.y & keep) | pad, (r.z & keep) | pad,
+                                       (r.w & keep) | pad);
+            Chain16Stage<T>::put(lds + sslot * STAGE + srow * C16_RS, ppiece, v);
+        }
+    };
+
+    // ---- chain state: lane (i16, j) of chain wave c, as in gate_chain16_kernel
+    const int c = wv & 1;
+    const int i16 = lane & 15, j = lane >> 4;
+    const int aoff = i16 * C16_RS + j * 16;
+    const int boff = (16 + 16 * c + i16) * C16_RS + j * 16;
+    floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
+    float4 fa[2][4], fb[2][4];
+    auto read_frag = [&](int sslot, float4 (&a)[4], float4 (&b)[4]) {
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+            a[s4] = *reinterpret_cast<const float4*>(lds + sslot * STAGE + aoff + 4 * s4);
+            b[s4] = *reinterpret_cast<const float4*>(lds + sslot * STAGE + boff + 4 * s4);
+        }
+    };
+    auto mfma16 = [&](const float4 (&a)[4], const float4 (&b)[4]) {
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(f4_at(a[s4], u), f4_at(b[s4], u), acc, 0, 0, 0);
+    };
+
+    // the barrier that hands slices over: the helpers' stores are in the LDS (and the chains'
+    // reads done) before it; a plain barrier, since a block-wide fence would also drain the
+    // helpers' loads in flight
+    auto handover = [&]() {
+        __builtin_amdgcn_sched_barrier(0);  // a slice's MFMAs stay before its barrier
+        // lgkmcnt(0) (vmcnt and expcnt left at their maxima), as a builtin so that the
+        // compiler's own wait counts know every LDS access before it is done
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        // no work of one slice moves across a handover (the widening of a later slice's
+        // registers would otherwise be hoisted and wait for loads still in flight)
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // The two roles run separate loops (so that the compiler's wait counts see each role's
+    // loads alone) with the same barriers: one after the prologue, one per handover of
+    // SPH = 2 slices.  Slice s sits in register set s mod D (D = 6 = 3 handovers) and in LDS
+    // slot slot(s); handover h stores slices 2h + 4, 2h + 5 (the stage read last in handover
+    // h - 1) and runs slices 2h, 2h + 1.
+    if (helper) {
+        // prologue: slices 0 .. 3 stored (handovers 0, 1), slices 4 .. 9 in flight
+#pragma unroll
+        for (int q = 0; q < C16P_D; ++q) hload(q, q);
+#pragma unroll
+        for (int q = 0; q < 2 * C16P_SPH; ++q) {
+            hstore(q, slot(q), q);
+            hload(q, q + C16P_D);
+        }
+        handover();
+        int stg = 2;  // stage of handover h + 2 (32-bit counters: the loop's scalar work counts)
+        auto hstep = [&](auto QC, int64_t h) {
+            // set of slice 2h + 4 (h mod LEAD is QC)
+            constexpr int base = ((decltype(QC)::kValue + 2) % C16P_LEAD) * C16P_SPH;
+#pragma unroll
+            for (int i = 0; i < C16P_SPH; ++i) {
+                const int64_t sl = C16P_SPH * (h + 2) + i;
+                hstore(base + i, stg * C16P_SPH + i, sl);
+                hload(base + i, sl + C16P_D);
+            }
+            stg = stg == C16P_STAGES - 1 ? 0 : stg + 1;
+            handover();
+        };
+        int64_t h = 0;
+        for (; h + C16P_LEAD <= nh; h += C16P_LEAD) SliceRun<0, C16P_LEAD>::full(hstep, h);
+        SliceRun<0, C16P_LEAD>::tail(hstep, h, nh);
+        return;
+    }
+    handover();
+    read_frag(slot(0), fa[0], fb[0]);
+    // handover h: slice 2h + 1's fragments (stored before the previous barrier), slice 2h's
+    // steps, slice 2h + 2's fragments (into the set slice 2h used), slice 2h + 1's steps.
+    // Slices past the last are padding (see xpad), so the loop body is straight-line code,
+    // in which the compiler sees that each step's fragments arrived well before it.
+    int stg = 0;  // stage of handover h
+    for (int h = 0; h < static_cast<int>(nh); ++h) {
+        const int nxt = stg == C16P_STAGES - 1 ? 0 : stg + 1;
+        // each group of reads is issued whole, a full slice of steps before its first use
+        read_frag(stg * C16P_SPH + 1, fa[1], fb[1]);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma16(fa[0], fb[0]);
+        __builtin_amdgcn_sched_barrier(0);
+        read_frag(nxt * C16P_SPH, fa[0], fb[0]);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma16(fa[1], fb[1]);
+        stg = nxt;
+        handover();
+    }
+    // lane l, register r: row 4 (l / 16) + r, expert l % 16 of the wave's block
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int64_t g = m0 + 4 * j + r;
+        const int64_t e = n0 + 16 * c + i16;
         if (g < G && e < E) {
             const bool valid = row_valid == nullptr || row_valid[g] != 0;
             logits[g * E + e] = valid ? acc[r] : 0.f;
@@ -1125,6 +1340,26 @@ extern "C" moe_status moe_route(const void* global_x, const int32_t* row_valid, 
         else
             hipLaunchKernelGGL((moe::gate_exact8_kernel<float, 2>), grid, dim3(256), 0, stream, xf, wf, row_valid, G,
                                E, H, logits);
+    } else if (moe::ceil_div(G, 16) * moe::ceil_div(E, 32) <= ncu) {
+        // at most one block per CU: chains on their own SIMDs, fed by helper waves
+        const dim3 grid(static_cast<unsigned>(moe::ceil_div(G, 16)), static_cast<unsigned>(moe::ceil_div(E, 32)));
+        const bool fast = aligned && H % moe::C16_K == 0 && 32 * H * esz < ((int64_t)1 << 31);
+        const uint16_t* xb = static_cast<const uint16_t*>(global_x);
+        const uint16_t* wb = static_cast<const uint16_t*>(w_router);
+        const float* xf = static_cast<const float*>(global_x);
+        const float* wf = static_cast<const float*>(w_router);
+        if (dt == MOE_BF16 && fast)
+            hipLaunchKernelGGL((moe::gate_chain16p_kernel<uint16_t, true>), grid, dim3(256), 0, stream, xb, wb,
+                               row_valid, G, E, H, logits);
+        else if (dt == MOE_BF16)
+            hipLaunchKernelGGL((moe::gate_chain16p_kernel<uint16_t, false>), grid, dim3(256), 0, stream, xb, wb,
+                               row_valid, G, E, H, logits);
+        else if (fast)
+            hipLaunchKernelGGL((moe::gate_chain16p_kernel<float, true>), grid, dim3(256), 0, stream, xf, wf,
+                               row_valid, G, E, H, logits);
+        else
+            hipLaunchKernelGGL((moe::gate_chain16p_kernel<float, false>), grid, dim3(256), 0, stream, xf, wf,
+                               row_valid, G, E, H, logits);
     } else {
         const dim3 grid(static_cast<unsigned>(moe::ceil_div(G, 32)), static_cast<unsigned>(moe::ceil_div(E, 32)));
         // whole 64-wide slices and aligned rows take 16-byte buffer loads, whose per-wave

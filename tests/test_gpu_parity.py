@@ -339,10 +339,12 @@ def test_identity_experts_combine_returns_weighted_sum():
 def test_gate_kernels_bitwise(dt):
     # every gate kernel against the oracle's single ascending fma chain, bit for bit, with
     # ragged row and expert tiles (E = 200) and every 17th row a pad row:
-    #   - 16x16 chains, 16-byte loads (H a multiple of 64): G = 300 at H = 384 (subnormal
-    #     products and partial sums), 448 and the model's 7168;
-    #   - 16x16 chains, element loads (ragged last slice): G = 300 and 6000 at H = 1000, and a
-    #     batch large enough for 128-row blocks but with H = 232 (G = 16347);
+    #   - small batches (at most one block per CU: two chain waves fed by two helper waves):
+    #     G = 300 at H = 384 (subnormal products and partial sums), 448, 1000 (ragged last
+    #     slice) and 232, and G = 200 at the model's H = 7168;
+    #   - 16x16 chains, 16-byte loads (H a multiple of 64): G = 1000 at H = 7168;
+    #   - 16x16 chains, element loads (ragged last slice): G = 6000 at H = 1000, and a batch
+    #     large enough for 128-row blocks but with H = 232 (G = 16347);
     #   - the 32x32-chain kernels: G = 16384 (64-row blocks, 4 waves) and 33000 (128-row
     #     blocks, 8 waves) at H = 256 (also subnormal) and 384;
     #   - rows whose chain ends at -0 (one tiny negative product in the last real column of
@@ -350,7 +352,8 @@ def test_gate_kernels_bitwise(dt):
     import combine_dp_gather_amd as m
     rng = np.random.default_rng(21)
     cfg = m.make_route_cfg("softmax", 200, 4)
-    cases = ((300, 384, 2.0 ** -66), (300, 448, 1.0), (1000, 7168, 1.0), (300, 1000, 1.0), (6000, 1000, 1.0),
+    cases = ((300, 384, 2.0 ** -66), (300, 448, 1.0), (200, 7168, 1.0), (1000, 7168, 1.0), (300, 1000, 1.0),
+             (6000, 1000, 1.0),
              (128 * 128 - 37, 232, 1.0), (16384, 256, 1.0), (33000, 384, 1.0), (33000, 256, 2.0 ** -66),
              (300, 232, "negzero"), (33000, 200, "negzero"))
     for G, H, scale in cases:
