@@ -797,60 +797,92 @@ __global__ __launch_bounds__(G_THREADS) void gate_fast_kernel(const uint16_t* __
 // form above keeps one slice in flight, which bounds its rate at ~21 GB/s per CU.  LDS rows
 // are 128 bytes with chunk c of row r stored at c xor ((r / 2) mod 8), so a fragment read (16
 // consecutive rows, one 16-byte chunk each) touches 16 distinct 16-byte slots of 256 bytes.
+// Eight waves, two per SIMD: waves 0-3 run the MFMAs of the 128 x 256 tile (64 x 128 each)
+// and waves 4-7 issue every DMA.  A vector-memory instruction in a wave that streams MFMAs
+// costs it tens of cycles of matrix-core time, and each slice takes 48 of them; a wave beside
+// it on the same SIMD issues them at little cost to the MFMAs.
 constexpr int FD_STAGES = 3;
+constexpr int FD_THREADS = 512;
 constexpr int FD_CPR = FB_K / 8;                     // 16-byte chunks per row (8)
 constexpr int FD_RPB = 64 / FD_CPR;                  // rows per 1 KB DMA block (8)
-constexpr int FD_XDMA = FB_M / FD_RPB / 4;           // token-row DMAs per wave and slice (4)
-constexpr int FD_WDMA = FB_N / FD_RPB / 4;           // weight-row DMAs per wave and slice (8)
+constexpr int FD_XDMA = FB_M / FD_RPB / 4;           // token-row DMAs per DMA wave and slice (4)
+constexpr int FD_WDMA = FB_N / FD_RPB / 4;           // weight-row DMAs per DMA wave and slice (8)
 constexpr int FD_VPS = FD_XDMA + FD_WDMA;
 __device__ __forceinline__ int fd_swz(int row) { return (row >> 1) & 7; }
 
-__global__ __launch_bounds__(G_THREADS, 1) void gate_fast_dma_kernel(const uint16_t* __restrict__ x,
-                                                                     const uint16_t* __restrict__ w,
-                                                                     const int32_t* __restrict__ row_valid,
-                                                                     int64_t G, int64_t E, int64_t H,
-                                                                     float* __restrict__ logits) {
+__global__ __launch_bounds__(FD_THREADS, 1) void gate_fast_dma_kernel(const uint16_t* __restrict__ x,
+                                                                      const uint16_t* __restrict__ w,
+                                                                      const int32_t* __restrict__ row_valid,
+                                                                      int64_t G, int64_t E, int64_t H,
+                                                                      float* __restrict__ logits) {
     __shared__ __attribute__((aligned(1024))) uint16_t xs[FD_STAGES][FB_M * FB_K];
     __shared__ __attribute__((aligned(1024))) uint16_t ws[FD_STAGES][FB_N * FB_K];
     const int64_t m0 = static_cast<int64_t>(blockIdx.x) * FB_M;
     const int64_t n0 = static_cast<int64_t>(blockIdx.y) * FB_N;
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
-    const int wm = wv >> 1, wn = wv & 1;
-    const int64_t xrows = G - m0 < FB_M ? G - m0 : FB_M;
-    const int64_t wrows = E - n0 < FB_N ? E - n0 : FB_N;
-    const uint32_t row_bytes = static_cast<uint32_t>(H) * 2u;
-    // rows past G or E fall outside the resources and read as zeros
-    const __amdgpu_buffer_rsrc_t rx = gemm::make_rsrc_uniform(x + m0 * H, static_cast<uint32_t>(xrows) * row_bytes);
-    const __amdgpu_buffer_rsrc_t rw = gemm::make_rsrc_uniform(w + n0 * H, static_cast<uint32_t>(wrows) * row_bytes);
-    // DMA p of this wave: token rows 32 wv + 8 p + lane / 8, weight rows 64 wv + 8 p + lane / 8;
-    // the global chunk (lane mod 8) xor swizzle, whose value depends on p only through p mod 2
-    const int dr = lane / FD_CPR;
-    const int xr0 = 32 * wv + dr, wr0 = 64 * wv + dr;
-    uint32_t xoff[2], woff[2];
+    const int64_t KT = H / FB_K;
+    if (wv >= 4) {
+        // ---- DMA wave d = wv - 4: the DMAs the four waves of a 4-wave block would split
+        const int d = wv - 4;
+        const int64_t xrows = G - m0 < FB_M ? G - m0 : FB_M;
+        const int64_t wrows = E - n0 < FB_N ? E - n0 : FB_N;
+        const uint32_t row_bytes = static_cast<uint32_t>(H) * 2u;
+        // rows past G or E fall outside the resources and read as zeros
+        const __amdgpu_buffer_rsrc_t rx = gemm::make_rsrc_uniform(x + m0 * H, static_cast<uint32_t>(xrows) * row_bytes);
+        const __amdgpu_buffer_rsrc_t rw = gemm::make_rsrc_uniform(w + n0 * H, static_cast<uint32_t>(wrows) * row_bytes);
+        // DMA p: token rows 32 d + 8 p + lane / 8, weight rows 64 d + 8 p + lane / 8; the global
+        // chunk (lane mod 8) xor swizzle, whose value depends on p only through p mod 2
+        const int dr = lane / FD_CPR;
+        const int xr0 = 32 * d + dr, wr0 = 64 * d + dr;
+        uint32_t xoff[2], woff[2];
 #pragma unroll
-    for (int par = 0; par < 2; ++par) {
-        xoff[par] = static_cast<uint32_t>(xr0) * row_bytes + static_cast<uint32_t>(((lane % FD_CPR) ^ fd_swz(xr0 + 8 * par)) * 16);
-        woff[par] = static_cast<uint32_t>(wr0) * row_bytes + static_cast<uint32_t>(((lane % FD_CPR) ^ fd_swz(wr0 + 8 * par)) * 16);
+        for (int par = 0; par < 2; ++par) {
+            xoff[par] = static_cast<uint32_t>(xr0) * row_bytes + static_cast<uint32_t>(((lane % FD_CPR) ^ fd_swz(xr0 + 8 * par)) * 16);
+            woff[par] = static_cast<uint32_t>(wr0) * row_bytes + static_cast<uint32_t>(((lane % FD_CPR) ^ fd_swz(wr0 + 8 * par)) * 16);
+        }
+        const uint32_t rstep = static_cast<uint32_t>(FD_RPB) * row_bytes;
+        auto issue = [&](int stage, int64_t kt) {
+            gemm::lds_void_t* xd = (gemm::lds_void_t*)(&xs[0][0] + stage * (FB_M * FB_K) + d * FD_XDMA * 512);
+            gemm::lds_void_t* wd = (gemm::lds_void_t*)(&ws[0][0] + stage * (FB_N * FB_K) + d * FD_WDMA * 512);
+            uint32_t x0 = xoff[0], x1 = xoff[1], w0 = woff[0], w1 = woff[1];
+            asm volatile("" : "+s"(xd), "+s"(wd), "+v"(x0), "+v"(x1), "+v"(w0), "+v"(w1));
+            const int so = static_cast<int>(kt * FB_K * 2);
+#pragma unroll
+            for (int p = 0; p < FD_XDMA; ++p)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rx, (gemm::lds_void_t*)((char __attribute__((address_space(3)))*)xd + p * 1024), 16,
+                    ((p & 1) ? x1 : x0) + static_cast<uint32_t>(p) * rstep, so, 0, 2 /* non-temporal */);
+#pragma unroll
+            for (int p = 0; p < FD_WDMA; ++p)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rw, (gemm::lds_void_t*)((char __attribute__((address_space(3)))*)wd + p * 1024), 16,
+                    ((p & 1) ? w1 : w0) + static_cast<uint32_t>(p) * rstep, so, 0, 0);
+        };
+        auto clamp = [&](int64_t kt) { return kt < KT ? kt : KT - 1; };
+        // slice s goes to stage s mod 3; one barrier before the loop (slice 0 landed), then
+        // one per slice kt (slice kt + 1 landed), after which slice kt's stage is refilled:
+        // the MFMA waves read it before that barrier
+        issue(0, 0);
+        issue(1, clamp(1));
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(FD_VPS) : "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        issue(2, clamp(2));
+        int st = 0;  // stage of slice kt
+        for (int64_t kt = 0; kt < KT; ++kt) {
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(FD_VPS) : "memory");  // slice kt + 2 in flight
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            issue(st, clamp(kt + 3));
+            st = st == FD_STAGES - 1 ? 0 : st + 1;
+        }
+        // no DMA into LDS may outlive the workgroup
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        return;
     }
-    const uint32_t rstep = static_cast<uint32_t>(FD_RPB) * row_bytes;
-    auto issue = [&](int stage, int64_t kt) {
-        gemm::lds_void_t* xd = (gemm::lds_void_t*)(&xs[0][0] + stage * (FB_M * FB_K) + wv * FD_XDMA * 512);
-        gemm::lds_void_t* wd = (gemm::lds_void_t*)(&ws[0][0] + stage * (FB_N * FB_K) + wv * FD_WDMA * 512);
-        uint32_t x0 = xoff[0], x1 = xoff[1], w0 = woff[0], w1 = woff[1];
-        asm volatile("" : "+s"(xd), "+s"(wd), "+v"(x0), "+v"(x1), "+v"(w0), "+v"(w1));
-        const int so = static_cast<int>(kt * FB_K * 2);
-#pragma unroll
-        for (int p = 0; p < FD_XDMA; ++p)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rx, (gemm::lds_void_t*)((char __attribute__((address_space(3)))*)xd + p * 1024), 16,
-                ((p & 1) ? x1 : x0) + static_cast<uint32_t>(p) * rstep, so, 0, 2 /* non-temporal */);
-#pragma unroll
-        for (int p = 0; p < FD_WDMA; ++p)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rw, (gemm::lds_void_t*)((char __attribute__((address_space(3)))*)wd + p * 1024), 16,
-                ((p & 1) ? w1 : w0) + static_cast<uint32_t>(p) * rstep, so, 0, 0);
-    };
+    // ---- MFMA wave: 64 rows (wm) x 128 experts (wn) of the tile
+    const int wm = wv >> 1, wn = wv & 1;
     floatx16_t acc[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c)
@@ -862,39 +894,56 @@ __global__ __launch_bounds__(G_THREADS, 1) void gate_fast_dma_kernel(const uint1
     int fch[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) fch[ks] = ((2 * ks + (lane >> 5)) ^ fd_swz(fr)) * 8;
-    const int64_t KT = H / FB_K;
+    // k steps 0, 1 of a slice sit in fragment set 0, steps 2, 3 in set 1
+    gate_bf16x8_t fa[2][2][2], fb[2][2][4];
+    auto read = [&](int stage, int set) {
+        const uint16_t* xa = &xs[0][0] + stage * (FB_M * FB_K) + (wm * 64 + fr) * FB_K;
+        const uint16_t* wb = &ws[0][0] + stage * (FB_N * FB_K) + (wn * 128 + fr) * FB_K;
 #pragma unroll
-    for (int s = 0; s < FD_STAGES - 1; ++s) issue(s, s < KT ? s : KT - 1);
-    int st = 0;
-    for (int64_t kt = 0; kt < KT; ++kt) {
-        // slice kt landed for this wave; after the barrier for every wave, and no wave still
-        // reads the stage refilled below (slice kt - 1's)
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((FD_STAGES - 2) * FD_VPS) : "memory");
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-        const uint16_t* xa = &xs[0][0] + st * (FB_M * FB_K) + (wm * 64 + fr) * FB_K;
-        const uint16_t* wb = &ws[0][0] + st * (FB_N * FB_K) + (wn * 128 + fr) * FB_K;
-        gate_bf16x8_t fa[4][2], fb[4][4];
+        for (int h = 0; h < 2; ++h) {
+            const int ks = 2 * set + h;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
+            for (int rb = 0; rb < 2; ++rb) fa[set][h][rb] = *reinterpret_cast<const gate_bf16x8_t*>(xa + rb * 32 * FB_K + fch[ks]);
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb) fa[ks][rb] = *reinterpret_cast<const gate_bf16x8_t*>(xa + rb * 32 * FB_K + fch[ks]);
-#pragma unroll
-            for (int cb = 0; cb < 4; ++cb) fb[ks][cb] = *reinterpret_cast<const gate_bf16x8_t*>(wb + cb * 32 * FB_K + fch[ks]);
+            for (int cb = 0; cb < 4; ++cb) fb[set][h][cb] = *reinterpret_cast<const gate_bf16x8_t*>(wb + cb * 32 * FB_K + fch[ks]);
         }
-        const int refill = st == 0 ? FD_STAGES - 1 : st - 1;
-        issue(refill, kt + FD_STAGES - 1 < KT ? kt + FD_STAGES - 1 : KT - 1);
+    };
+    auto mfma = [&](int set) {
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
                 for (int cb = 0; cb < 4; ++cb)
-                    acc[rb * 4 + cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks][rb], fb[ks][cb], acc[rb * 4 + cb], 0, 0, 0);
-        st = st == FD_STAGES - 1 ? 0 : st + 1;
+                    acc[rb * 4 + cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][h][rb], fb[set][h][cb], acc[rb * 4 + cb], 0, 0, 0);
+    };
+    // the barrier that pairs with the DMA waves': this wave's reads are done before it (the
+    // DMA waves refill a stage it read after it); the compiler's own wait counts see the wait
+    auto barrier = [&]() {
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // Each slice's fragment reads run under the MFMAs of the half slice before them: steps 2, 3
+    // of slice kt under steps 0, 1, and, after the barrier that finds slice kt + 1 landed,
+    // steps 0, 1 of slice kt + 1 under steps 2, 3 of slice kt.  The MFMA order per
+    // accumulator is that of gate_fast_kernel.
+    barrier();
+    read(0, 0);
+    int st = 0;  // stage of slice kt
+    for (int64_t kt = 0; kt < KT; ++kt) {
+        const int nx = st == FD_STAGES - 1 ? 0 : st + 1;
+        read(st, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma(0);
+        barrier();
+        read(nx, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma(1);
+        st = nx;
     }
-    // no DMA into LDS may outlive the workgroup
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     // the lane's 32 rows (row block rb, register v): their flags first, in one batch of loads
     // (rows past G load row G - 1's flag, unused), then keep = -1 past G, else the flag
     int keep[2][16];
@@ -1312,7 +1361,7 @@ extern "C" moe_status moe_route(const void* global_x, const int32_t* row_valid, 
         const dim3 grid(static_cast<unsigned>(moe::ceil_div(G, moe::FB_M)),
                         static_cast<unsigned>(moe::ceil_div(E, moe::FB_N)));
         if (fast && H % moe::FB_K == 0)
-            hipLaunchKernelGGL(moe::gate_fast_dma_kernel, grid, dim3(moe::G_THREADS), 0, stream,
+            hipLaunchKernelGGL(moe::gate_fast_dma_kernel, grid, dim3(moe::FD_THREADS), 0, stream,
                                static_cast<const uint16_t*>(global_x), static_cast<const uint16_t*>(w_router),
                                row_valid, G, E, H, logits);
         else
