@@ -517,8 +517,12 @@ def main():
     roof["launch_ms"] = kernels[dom]["ms"]
     roof["timing"] = "median over the timed steps' launches, each after the cache flush"
     fmt = "fp8" if mm == "mfma8" else "bf16"
+    # bf16 weights: when no slot can hold more than 512 rows the streaming kernel takes every
+    # slot alone (the same rule as the library's launch)
+    slot_bound = args.seg_stride if 0 < args.seg_stride < G else G
     kname = ("grouped_gemm_fp8_kernel" if fmt == "fp8"
              else "grouped_gemm_pp_kernel<true, true>" if bf and fp8w
+             else "grouped_gemm_stream_kernel<true>" if bf and slot_bound <= 512
              else "grouped_gemm_pp_kernel<true, false>" if bf
              else "generic_gemm_kernel<float, true>")
     roof["kernel"] = kname + (" (gate+up SwiGLU" + (", with its activation quantisation" if fmt == "fp8" else "")
