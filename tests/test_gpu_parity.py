@@ -341,7 +341,8 @@ def test_gate_kernels_bitwise(dt):
     # ragged row and expert tiles (E = 200) and every 17th row a pad row:
     #   - small batches (at most one block per CU: two chain waves fed by two helper waves):
     #     G = 300 at H = 384 (subnormal products and partial sums), 448, 1000 (ragged last
-    #     slice) and 232, and G = 200 at the model's H = 7168;
+    #     slice) and 232, G = 200 at the model's H = 7168, and tiny shapes (one row; one slice,
+    #     whole or ragged: the helper waves stage mostly padding);
     #   - 16x16 chains, 16-byte loads (H a multiple of 64): G = 1000 at H = 7168;
     #   - 16x16 chains, element loads (ragged last slice): G = 6000 at H = 1000, and a batch
     #     large enough for 128-row blocks but with H = 232 (G = 16347);
@@ -353,7 +354,7 @@ def test_gate_kernels_bitwise(dt):
     rng = np.random.default_rng(21)
     cfg = m.make_route_cfg("softmax", 200, 4)
     cases = ((300, 384, 2.0 ** -66), (300, 448, 1.0), (200, 7168, 1.0), (1000, 7168, 1.0), (300, 1000, 1.0),
-             (6000, 1000, 1.0),
+             (6000, 1000, 1.0), (1, 64, 1.0), (5, 40, 1.0), (17, 130, 1.0),
              (128 * 128 - 37, 232, 1.0), (16384, 256, 1.0), (33000, 384, 1.0), (33000, 256, 2.0 ** -66),
              (300, 232, "negzero"), (33000, 200, "negzero"))
     for G, H, scale in cases:
@@ -370,7 +371,7 @@ def test_gate_kernels_bitwise(dt):
         x = torch.from_numpy(xf).to(dt)
         w = torch.from_numpy(wf).to(dt)
         rv = np.ones(G, dtype=np.int32)
-        rv[::17] = 0
+        rv[16::17] = 0
         xb = x.view(torch.int16).numpy().view(np.uint16) if dt == torch.bfloat16 else x.numpy()
         wb = w.view(torch.int16).numpy().view(np.uint16) if dt == torch.bfloat16 else w.numpy()
         ref = oracle.gate_logits(xb, wb, row_valid=rv)
