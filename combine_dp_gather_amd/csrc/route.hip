@@ -278,13 +278,13 @@ __global__ __launch_bounds__(128 * WMR, 1) void gate_exact8_kernel(const T* __re
 // fp32 in [j][t] order (column 4t + j at j * 16 + t, rows C16_RS floats apart): one 16-byte
 // read gives a lane its operands for four consecutive instructions.  A wave's LDS accesses
 // complete in order, so a slice's stores and the reads that follow them need no barrier.
-// A dependent 16x16x4 step takes about 44 cycles, so a slice of 16 steps is ~700 cycles
-// while an operand fetch from HBM can take ~1000: slices are loaded C16_D slices ahead
+// A dependent 16x16x4 step takes 32-33 cycles (its issue time), so a slice of 16 steps is
+// ~530 cycles while an operand fetch from HBM can take ~1000: slices are loaded C16_D ahead
 // into as many register sets, and the stores of the next slice and the reads of its
 // fragments are spread between this slice's MFMAs.
 constexpr int C16_K = 64;           // h per slice
 constexpr int C16_RS = C16_K + 4;   // LDS row stride in floats
-constexpr int C16_D = 8;            // slices in flight (register sets), even
+constexpr int C16_D = 4;            // slices in flight (register sets), even
 constexpr int C16_WAVES = 4;        // independent waves per block, as 2 x 2 tiles
 
 template <typename T>
@@ -480,8 +480,8 @@ __global__ __launch_bounds__(64 * C16_WAVES) void gate_chain16_kernel(const T* _
 // slices, each slice 16 x rows and 32 w rows in the layout of gate_chain16_kernel, and one
 // barrier per stage (a handover) passes slices from the helpers to the chains.  The MFMAs see
 // the operands and the order of gate_chain16_kernel: the same bits.  At 384 rows and 256
-// experts (H = 7168) the kernel takes 44 us against 59 us for gate_chain16_kernel; ~33 cycles
-// of its ~47 per step are the MFMA itself, the rest the chains' fragment reads and the LDS and
+// experts (H = 7168) the kernel takes 35 us against 59 us for gate_chain16_kernel; ~33 cycles
+// of its ~42 per step are the MFMA itself, the rest the chains' fragment reads and the LDS and
 // memory traffic of the helpers beside them.
 constexpr int C16P_STAGES = 3;
 constexpr int C16P_SPH = 2;  // slices per handover (stage)
@@ -635,24 +635,40 @@ __global__ __launch_bounds__(256, 1) void gate_chain16p_kernel(const T* __restri
     }
     handover();
     read_frag(slot(0), fa[0], fb[0]);
-    // handover h: slice 2h + 1's fragments (stored before the previous barrier), slice 2h's
-    // steps, slice 2h + 2's fragments (into the set slice 2h used), slice 2h + 1's steps.
-    // Slices past the last are padding (see xpad), so the loop body is straight-line code,
-    // in which the compiler sees that each step's fragments arrived well before it.
+    // slice 0's fragments in place before the loop: at every loop entry no LDS read is then
+    // outstanding, so the wait counts the compiler places in the loop stay off its MFMAs
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    // Handover h reads the fragments of slices 2h + 1 and 2h + 2 (stages h and h + 1, both
+    // stored before its barrier) at its start, then runs the steps of slice 2h (read in
+    // handover h - 1) and of slice 2h + 1.  Reading everything at the start keeps the chains'
+    // LDS reads apart from the helpers' stores, which come once their loads land: reading
+    // slice 2h + 2 after slice 2h's steps instead took the decode route from 46 to 52 us.
+    // Slice 2h + 2 lands in the set slice 2h used on odd h and in fa2 on even h, so the loop
+    // runs handovers in pairs; slices past the last are padding (see xpad), so the body is
+    // straight-line code.
+    float4 fa2[4], fb2[4];
     int stg = 0;  // stage of handover h
-    for (int h = 0; h < static_cast<int>(nh); ++h) {
+    auto step = [&](auto PAR) {
+        constexpr bool odd = decltype(PAR)::value;
         const int nxt = stg == C16P_STAGES - 1 ? 0 : stg + 1;
-        // each group of reads is issued whole, a full slice of steps before its first use
+        // all of the handover's reads at its start: slice 2h + 1, and slice 2h + 2 for the next
         read_frag(stg * C16P_SPH + 1, fa[1], fb[1]);
+        if (odd) read_frag(nxt * C16P_SPH, fa[0], fb[0]);
+        else read_frag(nxt * C16P_SPH, fa2, fb2);
         __builtin_amdgcn_sched_barrier(0);
-        mfma16(fa[0], fb[0]);
-        __builtin_amdgcn_sched_barrier(0);
-        read_frag(nxt * C16P_SPH, fa[0], fb[0]);
+        if (odd) mfma16(fa2, fb2);
+        else mfma16(fa[0], fb[0]);
         __builtin_amdgcn_sched_barrier(0);
         mfma16(fa[1], fb[1]);
         stg = nxt;
         handover();
+    };
+    int h = 0;
+    for (; h + 2 <= static_cast<int>(nh); h += 2) {
+        step(std::false_type());
+        step(std::true_type());
     }
+    if (h < static_cast<int>(nh)) step(std::false_type());
     // lane l, register r: row 4 (l / 16) + r, expert l % 16 of the wave's block
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
