@@ -365,20 +365,20 @@ __global__ __launch_bounds__(D_THREADS) void place_kernel(
     }
     __syncthreads();
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+    // bits of a slot index: the lanes sharing a lane's slot are found one bit at a time (one
+    // ballot per bit), whatever the number of distinct slots in the wave
+    const int sbits = El > 1 ? 32 - __builtin_clz(static_cast<uint32_t>(El - 1)) : 0;
 #pragma unroll
     for (int step = 0; step < STEPS; ++step) {
         const int64_t f = wstart + step * kWave + lane;
         const bool inb = f < P;
         const int s = slot[step];
-        // lanes with the same slot: one ballot per distinct slot in the wave
-        uint64_t pending = __ballot(s >= 0);
-        uint64_t mine = 0;
-        while (pending) {
-            const int leader = __ffsll(static_cast<long long>(pending)) - 1;
-            const int ls = __shfl(s, leader);
-            const uint64_t same = __ballot(s == ls);
-            if (s == ls) mine = same;
-            pending &= ~same;
+        // lanes with the same slot as this one (its own included), for s >= 0
+        uint64_t mine = __ballot(s >= 0);
+        for (int b = 0; b < sbits; ++b) {
+            const bool bit = (s >> b) & 1;
+            const uint64_t ones = __ballot(s >= 0 && bit);
+            mine &= bit ? ones : ~ones;
         }
         int64_t row = -1;
         if (s >= 0) row = wbase[wv][s] + __popcll(mine & below);
