@@ -200,11 +200,11 @@ extern "C" moe_status moe_combine(const void* y_perm, moe_dtype dt, const moe_pl
     MOE_CHECK_ARG(plan->pair_row && topk_w && out);
     MOE_CHECK_ARG(plan->cap == 0 || y_perm != nullptr);
     // vector path: one block per output row; element-wise fallback: one wave per row
-    MOE_CHECK_ARG(G < 0x7fffffff);
     const dim3 grid_rows(static_cast<unsigned>(G));
     const dim3 grid(static_cast<unsigned>(ceil_div(G, C_WAVES)));
     const int vec = dt == MOE_BF16 ? 8 : 4;
     const bool vec_ok = (H % vec == 0) && aligned(out, 16) && (y_perm == nullptr || aligned(y_perm, 16));
+    if (!grid_fits(vec_ok ? G : ceil_div(G, C_WAVES), C_THREADS)) return MOE_ERR_UNSUPPORTED;
     if (dt == MOE_BF16) {
         if (vec_ok)
             hipLaunchKernelGGL(combine_kernel<uint16_t>, grid_rows, dim3(C_THREADS), 0, stream,
@@ -255,7 +255,7 @@ extern "C" moe_status moe_combine_scatter(const void* y_perm, moe_dtype dt, cons
     MOE_CHECK_ARG(plan->pair_row && topk_w);
     MOE_CHECK_ARG(plan->cap == 0 || y_perm != nullptr);
     if (H % vec != 0 || (y_perm != nullptr && !aligned(y_perm, 16))) return MOE_ERR_UNSUPPORTED;
-    MOE_CHECK_ARG(real < 0x7fffffff);
+    if (!grid_fits(real, C_THREADS)) return MOE_ERR_UNSUPPORTED;
     for (int first = 0; first < L->num_replicas; first += kExitBatch) {
         const int cnt = (L->num_replicas - first) < kExitBatch ? (L->num_replicas - first) : kExitBatch;
         ExitBatch b{};

@@ -111,7 +111,7 @@ moe_status launch_slices(bool is_gather, const moe_gather_layout_t* L, const voi
     const int64_t row_units = row_bytes / static_cast<int64_t>(sizeof(V));
     const int64_t kChunk = kThreads * (is_gather ? kUnrollG : kUnrollS);  // vectors per block
     // every launch's block count fits the grid (checked before anything is enqueued)
-    if (ceil_div(L->rows * row_units, kChunk) + kBatch > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
+    if (!grid_fits(ceil_div(L->rows * row_units, kChunk) + kBatch, kThreads)) return MOE_ERR_UNSUPPORTED;
     for (int first = 0; first < L->num_replicas; first += kBatch) {
         const int cnt = (L->num_replicas - first) < kBatch ? (L->num_replicas - first) : kBatch;
         SliceBatch b{};

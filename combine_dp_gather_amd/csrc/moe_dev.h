@@ -94,6 +94,11 @@ __device__ __forceinline__ void st_stream(V* p, const V& v) {
 
 __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// a launch's x dimension counts its work-items in 32 bits: blocks * threads < 2^32
+inline bool grid_fits(int64_t blocks, int64_t threads) {
+    return blocks >= 0 && blocks <= static_cast<int64_t>(0xffffffffu) / threads;
+}
+
 inline bool aligned(const void* p, uintptr_t a) {
     return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
 }

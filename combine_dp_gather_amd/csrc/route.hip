@@ -1342,6 +1342,8 @@ extern "C" moe_status moe_route_from_logits(const float* logits, const int32_t* 
     if (G == 0) return MOE_OK;
     MOE_CHECK_ARG(logits && topk_ids && topk_w);
     MOE_CHECK_ARG(G <= (int64_t)1 << 31);
+    // the select launch (one wave per row) has the most work-items per row of any route launch
+    if (!moe::grid_fits(moe::ceil_div(G, moe::S_WAVES), moe::S_THREADS)) return MOE_ERR_UNSUPPORTED;
     return moe::launch_select(logits, row_valid, G, bias, cfg, topk_ids, topk_w, stream);
 }
 
@@ -1357,6 +1359,8 @@ extern "C" moe_status moe_route(const void* global_x, const int32_t* row_valid, 
     if (G == 0) return MOE_OK;
     MOE_CHECK_ARG(global_x && w_router && logits && topk_ids && topk_w);
     MOE_CHECK_ARG(G <= (int64_t)1 << 31);
+    // the select launch (one wave per row) has the most work-items per row of any route launch
+    if (!moe::grid_fits(moe::ceil_div(G, moe::S_WAVES), moe::S_THREADS)) return MOE_ERR_UNSUPPORTED;
     const int64_t E = cfg->num_experts;
     const int64_t esz = dt == MOE_BF16 ? 2 : 4;
     const bool aligned = moe::aligned(global_x, 16) && moe::aligned(w_router, 16) && (H * esz) % 16 == 0;

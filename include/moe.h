@@ -54,7 +54,10 @@ extern "C" {
 typedef enum MOE_ENUM_BASE {
     MOE_OK = 0,
     MOE_ERR_INVALID_ARG = 1,  /* a pointer, size or enum value is out of range; nothing enqueued */
-    MOE_ERR_UNSUPPORTED = 2,  /* a valid combination this build does not implement */
+    MOE_ERR_UNSUPPORTED = 2,  /* a valid combination this build does not implement, or a
+                                 size whose launch would need 2^32 or more work-items in one
+                                 grid dimension (moe_route: G >= 2^26 rows; moe_combine:
+                                 G >= 2^24 rows on the 16-byte path) */
     MOE_ERR_CAPACITY = 3,     /* a caller buffer (workspace, table) is too small */
     MOE_ERR_HIP = 4,          /* the HIP runtime refused a launch */
     MOE_ERR_SCRATCH_LIMIT = 5 /* the problem needs more than a no-allocation entry point's

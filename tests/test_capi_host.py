@@ -168,6 +168,29 @@ def test_argument_errors_return_before_any_launch(m):
                                    None) == _lib.MOE_ERR_INVALID_ARG
 
 
+def test_grid_limits_rejected_before_any_launch(m):
+    """A launch's x dimension counts work-items in 32 bits.  Sizes whose grid would need 2^32
+    or more are refused as unsupported before anything is enqueued (the pointers here are never
+    dereferenced)."""
+    from combine_dp_gather_amd import _lib
+    lib = m.lib()
+    c = m.make_route_cfg("grouped", 256, 8, 8, 4, 2, True)
+    # the select runs one 64-lane wave per row: G = 2^26 rows is 2^32 work-items
+    assert lib.moe_route_from_logits(256, None, 1 << 26, None, ctypes.byref(c), 256, 256, None) == \
+        _lib.MOE_ERR_UNSUPPORTED
+    assert lib.moe_route(256, None, 1 << 26, 64, _lib.MOE_BF16, 256, None, ctypes.byref(c), 256, 256, 256,
+                         None) == _lib.MOE_ERR_UNSUPPORTED
+    # combine, 16-byte path: one 256-thread block per row, so G = 2^24 rows is the first refused
+    big = _lib.Plan(1, 1, 1, 1, 1, 1, 16, 1 << 24, 2, 4, 1, 0)
+    assert lib.moe_combine(256, _lib.MOE_BF16, ctypes.byref(big), 256, 1.0, 64, 256, None) == \
+        _lib.MOE_ERR_UNSUPPORTED
+    # gather: 2^24 rows of 16 KB in 8 KB chunks, one per 256-thread block: 2^33 work-items
+    L = m.moe_gather_layout([1 << 24], "sum")
+    arr = (ctypes.c_void_p * 1)(256)
+    assert lib.moe_gather(ctypes.byref(L), ctypes.cast(arr, ctypes.c_void_p), 8192, _lib.MOE_BF16, 256, 256,
+                          None) == _lib.MOE_ERR_UNSUPPORTED
+
+
 def test_workspace_sizes(m):
     assert m.moe_dispatch_workspace_size(0, 8, 16) >= 0
     a = m.moe_dispatch_workspace_size(32768, 8, 16)
