@@ -203,7 +203,9 @@ moe_status launch_entry(const moe_gather_layout_t* L, const void* const* hid, vo
             if (b.slot_rows[j] > max_rows) max_rows = b.slot_rows[j];
         }
         if (max_rows == 0) continue;
-        const int64_t cap_x = (8192 / cnt) > 1 ? (8192 / cnt) : 1;
+        // up to 32768 blocks per launch: at the prefill shape (8 x 4096 rows) every block takes
+        // one row.  8192 blocks of four rows each took 0.339 ms there, 32768 blocks 0.317 ms.
+        const int64_t cap_x = (32768 / cnt) > 1 ? (32768 / cnt) : 1;
         const T* wt = static_cast<const T*>(w);
         T* out = static_cast<T*>(gx);
         if (!vec) {
