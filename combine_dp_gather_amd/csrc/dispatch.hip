@@ -17,7 +17,9 @@
 //               the count table is small, the place blocks do this themselves instead;
 //   3. place:   each wave of a block owns a quarter of the block's pairs, walks it 64 pairs
 //               at a time and ranks equal slots with ballots (rank = popcount of the lanes
-//               below with the same slot), so rows follow ascending pair index: stable;
+//               below with the same slot), so rows follow ascending pair index: stable.
+//               Up to 1024 pairs, one place block takes them all and counts them itself, so
+//               neither the count launch nor the scan runs;
 //   4. permute: x_perm[row] = global_x[sorted_pair[row] / k], one block per row, streaming
 //               16-byte vectors, rows bounded by the device-side num_rows (no host sync).
 //               Skipped when the caller passes no x_perm: the gathering up GEMM then reads
@@ -183,6 +185,10 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(
 // plan's counts, seg_offsets, num_rows and error_flag, and all blocks share the pad-row fill.
 // This saves the separate scan launch and the per-block base round trip through memory.
 constexpr int64_t kFusedScanLimit = 65536;  // NB * El entries each block adds up
+// Pairs one block places alone.  At 1020 pairs (170 tokens over 4 replicas, top-6) the dispatch
+// took 8.1 us this way against 12.8 us with the count launch; a form with 12 pairs per lane was
+// slower at 3072 pairs (14.4 against 12.4 us), so larger batches keep the count blocks.
+constexpr int64_t kSoloPairs = kChunk;
 
 struct ScanArgs {
     const int32_t* blk_counts;  // [NB][El]
@@ -195,7 +201,9 @@ struct ScanArgs {
     int32_t* error_flag;
 };
 
-template <bool FUSED>
+// SOLO (FUSED with one block): the block holds every pair, so the slot totals are its own wave
+// histograms and no count table is read; the count launch is left out.
+template <bool FUSED, bool SOLO = false>
 __global__ __launch_bounds__(D_THREADS) void place_kernel(
     const int32_t* __restrict__ ids, int64_t P, int k, MapArgs m,
     const int32_t* __restrict__ blk_base, const int64_t* __restrict__ seg_in, int64_t cap,
@@ -223,13 +231,14 @@ __global__ __launch_bounds__(D_THREADS) void place_kernel(
         if (tid == 0) over = 0;
     }
     __syncthreads();
+    static_assert(!SOLO || FUSED, "the single-block form derives the layout itself");
     const int64_t wstart = static_cast<int64_t>(blockIdx.x) * kChunk + wv * kWaveChunk;
     // FUSED: the first U count-table entries of this thread are loaded before the pass over
     // the ids, so the two global round trips overlap
     constexpr int U = 16;
-    const int64_t n_tab = FUSED ? sa.NB * El : 0;
+    const int64_t n_tab = FUSED && !SOLO ? sa.NB * El : 0;
     int32_t c0[U];
-    if constexpr (FUSED) {
+    if constexpr (FUSED && !SOLO) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t i = tid + u * D_THREADS;
@@ -253,6 +262,14 @@ __global__ __launch_bounds__(D_THREADS) void place_kernel(
         if (slot[step] >= 0) atomicAdd(&whist[wv][slot[step]], 1);
     }
     const int64_t* seg = seg_in;
+    if constexpr (SOLO) {
+        __syncthreads();
+        for (int e = tid; e < El; e += D_THREADS) {
+            int32_t t = 0;
+            for (int w = 0; w < D_WAVES; ++w) t += whist[w][e];
+            tot[e] = t;
+        }
+    }
     if constexpr (FUSED) {
         const int64_t mine_end = static_cast<int64_t>(blockIdx.x) * El;  // entries of earlier blocks
         // the thread's entries are i = tid + n * D_THREADS, n = 0, 1, ...; their slot i % El
@@ -267,8 +284,10 @@ __global__ __launch_bounds__(D_THREADS) void place_kernel(
             e_cur += e_step;
             if (e_cur >= El) e_cur -= El;
         };
+        if constexpr (!SOLO) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) add(tid + u * D_THREADS, c0[u]);
+            for (int u = 0; u < U; ++u) add(tid + u * D_THREADS, c0[u]);
+        }
         for (int64_t i0 = tid + U * D_THREADS; i0 < n_tab; i0 += D_THREADS * U) {
             int32_t c[U];
 #pragma unroll
@@ -480,7 +499,7 @@ moe_status check_dispatch_args(const void* global_x, const int32_t* topk_ids, in
     return MOE_OK;
 }
 
-// The four kernels on a checked call; `workspace` holds the per-block count and base tables
+// The kernels on a checked call; `workspace` holds the per-block count and base tables
 // (2 * NB * E_l int32), every entry of which the count and scan kernels write before any
 // kernel reads it, so its previous contents never matter.
 moe_status run_dispatch(const void* global_x, const int32_t* topk_ids, int64_t G, int32_t k, int64_t H,
@@ -493,20 +512,28 @@ moe_status run_dispatch(const void* global_x, const int32_t* topk_ids, int64_t G
     MapArgs m{map->phys_of, map->n_rep, map->num_logical, map->max_rep, map->first_slot, El};
     int32_t* blk_counts = static_cast<int32_t*>(workspace);
     int32_t* blk_base = blk_counts + NB * El;
-    if (NB > 0) {
+    ScanArgs sa{blk_counts, NB, plan->align, static_cast<int64_t>(plan->seg_stride), plan->counts,
+                plan->seg_offsets, plan->num_rows, plan->error_flag};
+    if (NB > 0 && P <= kSoloPairs) {
+        // one block holds every pair: no count table, no count launch
+        hipLaunchKernelGGL((place_kernel<true, true>), dim3(1), dim3(D_THREADS), 0, stream, topk_ids, P, k, m,
+                           nullptr, nullptr, plan->cap, sa, plan->sorted_pair, plan->pair_row);
+        MOE_LAUNCH_CHECK();
+    } else if (NB > 0 && NB * El <= kFusedScanLimit) {
+        // the place blocks derive the layout from the count table themselves
         hipLaunchKernelGGL(count_kernel, dim3(static_cast<unsigned>(NB)), dim3(D_THREADS), 0, stream,
                            topk_ids, P, k, m, blk_counts);
         MOE_LAUNCH_CHECK();
-    }
-    ScanArgs sa{blk_counts, NB, plan->align, static_cast<int64_t>(plan->seg_stride), plan->counts,
-                plan->seg_offsets, plan->num_rows, plan->error_flag};
-    if (NB > 0 && NB * El <= kFusedScanLimit) {
-        // the place blocks derive the layout from the count table themselves
         hipLaunchKernelGGL(place_kernel<true>, dim3(static_cast<unsigned>(NB)), dim3(D_THREADS), 0, stream,
                            topk_ids, P, k, m, nullptr, nullptr, plan->cap, sa, plan->sorted_pair,
                            plan->pair_row);
         MOE_LAUNCH_CHECK();
     } else {
+        if (NB > 0) {
+            hipLaunchKernelGGL(count_kernel, dim3(static_cast<unsigned>(NB)), dim3(D_THREADS), 0, stream,
+                               topk_ids, P, k, m, blk_counts);
+            MOE_LAUNCH_CHECK();
+        }
         hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(SCAN_THREADS), 0, stream, blk_counts, NB, El,
                            plan->align, static_cast<int64_t>(plan->seg_stride), plan->cap, blk_base,
                            plan->counts, plan->seg_offsets,

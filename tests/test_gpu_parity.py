@@ -496,14 +496,20 @@ def test_fixed_capacity_layout(name, stride):
 @pytest.mark.parametrize("tokens,align,stride", [((8192,), 1, 0), ((8200,), 1, 0), ((8200,), 128, 0),
                                                   ((8192,), 1, 64), ((8200,), 1, 64),
                                                   ((1024,), 1, 0), ((1025,), 1, 0), ((1024,), 128, 0),
-                                                  ((1024,), 1, 8), ((700, 0, 324), 1, 0)])
+                                                  ((1024,), 1, 8), ((700, 0, 324), 1, 0),
+                                                  ((128,), 1, 0), ((129,), 1, 0), ((256,), 1, 0),
+                                                  ((257,), 1, 0), ((512,), 1, 0), ((513,), 1, 0),
+                                                  ((128,), 128, 0), ((100,), 1, 2), ((70, 0, 57), 1, 0),
+                                                  ((512,), 128, 0), ((300,), 1, 2), ((200, 0, 57), 1, 0)])
 def test_dispatch_fused_and_scan_layouts(tokens, align, stride):
-    """The two ways dispatch derives the plan's layout: with 1024 local slots and top-8, 8192
+    """The three ways dispatch derives the plan's layout: with 1024 local slots and top-8, 8192
     rows make 64 count blocks of 1024 pairs, a 65536-entry count table that the place blocks
     add up themselves; 8200 rows make 65 blocks and take the separate scan kernel.  Small
-    batches (8 or 9 count blocks, one with an idle replica) take the first way.  All of them,
-    with alignment 128 and with the fixed-capacity layout (64 or 8 rows per slot, so slots
-    overflow), give the oracle's plan bit for bit."""
+    batches (8 or 9 count blocks, one with an idle replica) take the first way.  Up to 1024
+    pairs (128 rows) one place block takes every pair and counts them itself; 129 rows and up
+    (2 to 5 count blocks here) go back to the count blocks.  All of them, with alignment 128 and
+    with the fixed-capacity layout (64, 8 or 2 rows per slot, so slots overflow), give the
+    oracle's plan bit for bit."""
     cfg = replace(moe_synth.CONFIGS["cfg2"], num_tokens=tokens, hidden=256, inter=128,
                   num_experts=1024, num_local=1024, top_k=8, name=f"dispatch-{tokens[0]}")
     run_and_compare_inputs(moe_synth.make_inputs(cfg), "sum", align=align, seg_stride=stride)
