@@ -10,7 +10,8 @@
 //     row index: replica g mod n_rep.
 //
 // Kernels (one rank, one GPU, no atomics deciding any order):
-//   1. count:   each block takes kChunk consecutive pairs and builds a per-slot histogram in
+//   1. count:   each block takes 1024 consecutive pairs (256 for batches of up to
+//               kSmallPairs pairs) and builds a per-slot histogram in
 //               LDS (integer LDS atomics: the counts do not depend on their order);
 //   2. scan:    one block turns the per-block histograms into per-block bases (column prefix
 //               over blocks), per-slot counts and the aligned exclusive scan seg_offsets; when
@@ -34,9 +35,11 @@ namespace {
 
 constexpr int D_THREADS = 256;
 constexpr int D_WAVES = D_THREADS / kWave;
+// pairs per thread of the count and place blocks: 4 (1024 per block) for large batches, 1
+// (256 per block) up to kSmallPairs, where more, shorter blocks finish sooner
 constexpr int kPairsPerThread = 4;
 constexpr int kChunk = D_THREADS * kPairsPerThread;  // 1024 pairs per block
-constexpr int kWaveChunk = kChunk / D_WAVES;         // 256 pairs per wave
+constexpr int kSmallPairs = 16384;
 constexpr int kMaxSlots = 1024;
 
 struct MapArgs {
@@ -62,22 +65,23 @@ __device__ __forceinline__ int pair_slot(int32_t l, uint32_t f, uint32_t k, cons
     return (p >= 0 && p < m.El) ? p : -1;
 }
 
+template <int PPT>
 __global__ __launch_bounds__(D_THREADS) void count_kernel(const int32_t* __restrict__ ids,
                                                           int64_t P, int k, MapArgs m,
                                                           int32_t* __restrict__ blk_counts) {
     __shared__ int32_t hist[kMaxSlots];
     for (int e = threadIdx.x; e < m.El; e += D_THREADS) hist[e] = 0;
     __syncthreads();
-    const int64_t base = static_cast<int64_t>(blockIdx.x) * kChunk;
+    const int64_t base = static_cast<int64_t>(blockIdx.x) * (PPT * D_THREADS);
     // all of the thread's ids are loaded before the first LDS add
-    int32_t idv[kPairsPerThread];
+    int32_t idv[PPT];
 #pragma unroll
-    for (int i = 0; i < kPairsPerThread; ++i) {
+    for (int i = 0; i < PPT; ++i) {
         const int64_t f = base + i * D_THREADS + threadIdx.x;
         idv[i] = f < P ? ids[f] : -1;
     }
 #pragma unroll
-    for (int i = 0; i < kPairsPerThread; ++i) {
+    for (int i = 0; i < PPT; ++i) {
         const int64_t f = base + i * D_THREADS + threadIdx.x;
         if (f < P) {
             const int s = pair_slot(idv[i], static_cast<uint32_t>(f), static_cast<uint32_t>(k), m);
@@ -203,7 +207,7 @@ struct ScanArgs {
 
 // SOLO (FUSED with one block): the block holds every pair, so the slot totals are its own wave
 // histograms and no count table is read; the count launch is left out.
-template <bool FUSED, bool SOLO = false>
+template <bool FUSED, bool SOLO, int PPT>
 __global__ __launch_bounds__(D_THREADS) void place_kernel(
     const int32_t* __restrict__ ids, int64_t P, int k, MapArgs m,
     const int32_t* __restrict__ blk_base, const int64_t* __restrict__ seg_in, int64_t cap,
@@ -232,7 +236,8 @@ __global__ __launch_bounds__(D_THREADS) void place_kernel(
     }
     __syncthreads();
     static_assert(!SOLO || FUSED, "the single-block form derives the layout itself");
-    const int64_t wstart = static_cast<int64_t>(blockIdx.x) * kChunk + wv * kWaveChunk;
+    constexpr int STEPS = PPT;  // each wave owns PPT * 64 consecutive pairs
+    const int64_t wstart = (static_cast<int64_t>(blockIdx.x) * D_WAVES + wv) * (STEPS * kWave);
     // FUSED: the first U count-table entries of this thread are loaded before the pass over
     // the ids, so the two global round trips overlap
     constexpr int U = 16;
@@ -247,7 +252,6 @@ __global__ __launch_bounds__(D_THREADS) void place_kernel(
     }
     // per-wave histogram of its pairs; the ids are all loaded before the first LDS add, and
     // the slots stay in registers for the placement pass
-    constexpr int STEPS = kWaveChunk / kWave;
     int32_t idv[STEPS];
 #pragma unroll
     for (int step = 0; step < STEPS; ++step) {
@@ -461,7 +465,9 @@ moe_status launch_permute(const void* x, const moe_plan* plan, int64_t row_bytes
     return MOE_OK;
 }
 
-int64_t num_blocks(int64_t G, int32_t k) { return ceil_div(G * k, kChunk); }
+// pairs per thread, and blocks, of the count and place launches for G * k pairs
+int pairs_per_thread(int64_t P) { return P > kSoloPairs && P <= kSmallPairs ? 1 : kPairsPerThread; }
+int64_t num_blocks(int64_t G, int32_t k) { return ceil_div(G * k, D_THREADS * pairs_per_thread(G * k)); }
 
 }  // namespace
 }  // namespace moe
@@ -499,6 +505,36 @@ moe_status check_dispatch_args(const void* global_x, const int32_t* topk_ids, in
     return MOE_OK;
 }
 
+// The count blocks, then the place blocks (which scan a small count table themselves) or the
+// scan kernel and the place blocks; NB = 0 runs the scan alone (empty plan).
+template <int PPT>
+moe_status count_and_place(const int32_t* topk_ids, int64_t P, int32_t k, const MapArgs& m, int64_t NB,
+                           int El, const moe_plan* plan, const ScanArgs& sa, int32_t* blk_counts,
+                           int32_t* blk_base, hipStream_t stream) {
+    if (NB > 0) {
+        hipLaunchKernelGGL(count_kernel<PPT>, dim3(static_cast<unsigned>(NB)), dim3(D_THREADS), 0, stream,
+                           topk_ids, P, k, m, blk_counts);
+        MOE_LAUNCH_CHECK();
+    }
+    if (NB > 0 && NB * El <= kFusedScanLimit) {
+        hipLaunchKernelGGL((place_kernel<true, false, PPT>), dim3(static_cast<unsigned>(NB)), dim3(D_THREADS), 0,
+                           stream, topk_ids, P, k, m, nullptr, nullptr, plan->cap, sa, plan->sorted_pair,
+                           plan->pair_row);
+        MOE_LAUNCH_CHECK();
+        return MOE_OK;
+    }
+    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(SCAN_THREADS), 0, stream, blk_counts, NB, El, plan->align,
+                       static_cast<int64_t>(plan->seg_stride), plan->cap, blk_base, plan->counts,
+                       plan->seg_offsets, plan->num_rows, plan->error_flag, plan->sorted_pair);
+    MOE_LAUNCH_CHECK();
+    if (NB == 0) return MOE_OK;
+    hipLaunchKernelGGL((place_kernel<false, false, PPT>), dim3(static_cast<unsigned>(NB)), dim3(D_THREADS), 0,
+                       stream, topk_ids, P, k, m, blk_base, plan->seg_offsets, plan->cap, sa, plan->sorted_pair,
+                       plan->pair_row);
+    MOE_LAUNCH_CHECK();
+    return MOE_OK;
+}
+
 // The kernels on a checked call; `workspace` holds the per-block count and base tables
 // (2 * NB * E_l int32), every entry of which the count and scan kernels write before any
 // kernel reads it, so its previous contents never matter.
@@ -516,34 +552,16 @@ moe_status run_dispatch(const void* global_x, const int32_t* topk_ids, int64_t G
                 plan->seg_offsets, plan->num_rows, plan->error_flag};
     if (NB > 0 && P <= kSoloPairs) {
         // one block holds every pair: no count table, no count launch
-        hipLaunchKernelGGL((place_kernel<true, true>), dim3(1), dim3(D_THREADS), 0, stream, topk_ids, P, k, m,
-                           nullptr, nullptr, plan->cap, sa, plan->sorted_pair, plan->pair_row);
-        MOE_LAUNCH_CHECK();
-    } else if (NB > 0 && NB * El <= kFusedScanLimit) {
-        // the place blocks derive the layout from the count table themselves
-        hipLaunchKernelGGL(count_kernel, dim3(static_cast<unsigned>(NB)), dim3(D_THREADS), 0, stream,
-                           topk_ids, P, k, m, blk_counts);
-        MOE_LAUNCH_CHECK();
-        hipLaunchKernelGGL(place_kernel<true>, dim3(static_cast<unsigned>(NB)), dim3(D_THREADS), 0, stream,
+        hipLaunchKernelGGL((place_kernel<true, true, kPairsPerThread>), dim3(1), dim3(D_THREADS), 0, stream,
                            topk_ids, P, k, m, nullptr, nullptr, plan->cap, sa, plan->sorted_pair,
                            plan->pair_row);
         MOE_LAUNCH_CHECK();
     } else {
-        if (NB > 0) {
-            hipLaunchKernelGGL(count_kernel, dim3(static_cast<unsigned>(NB)), dim3(D_THREADS), 0, stream,
-                               topk_ids, P, k, m, blk_counts);
-            MOE_LAUNCH_CHECK();
-        }
-        hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(SCAN_THREADS), 0, stream, blk_counts, NB, El,
-                           plan->align, static_cast<int64_t>(plan->seg_stride), plan->cap, blk_base,
-                           plan->counts, plan->seg_offsets,
-                           plan->num_rows, plan->error_flag, plan->sorted_pair);
-        MOE_LAUNCH_CHECK();
-        if (NB == 0) return MOE_OK;
-        hipLaunchKernelGGL(place_kernel<false>, dim3(static_cast<unsigned>(NB)), dim3(D_THREADS), 0, stream,
-                           topk_ids, P, k, m, blk_base, plan->seg_offsets, plan->cap, sa,
-                           plan->sorted_pair, plan->pair_row);
-        MOE_LAUNCH_CHECK();
+        const moe_status st = pairs_per_thread(P) == 1
+                                  ? count_and_place<1>(topk_ids, P, k, m, NB, El, plan, sa, blk_counts, blk_base, stream)
+                                  : count_and_place<kPairsPerThread>(topk_ids, P, k, m, NB, El, plan, sa, blk_counts,
+                                                                     blk_base, stream);
+        if (st != MOE_OK || NB == 0) return st;
     }
     // no x_perm: the plan only (the gathering up GEMM reads the rows in place)
     if (plan->cap == 0 || x_perm == nullptr) return MOE_OK;

@@ -504,12 +504,12 @@ def test_fixed_capacity_layout(name, stride):
 def test_dispatch_fused_and_scan_layouts(tokens, align, stride):
     """The three ways dispatch derives the plan's layout: with 1024 local slots and top-8, 8192
     rows make 64 count blocks of 1024 pairs, a 65536-entry count table that the place blocks
-    add up themselves; 8200 rows make 65 blocks and take the separate scan kernel.  Small
-    batches (8 or 9 count blocks, one with an idle replica) take the first way.  Up to 1024
-    pairs (128 rows) one place block takes every pair and counts them itself; 129 rows and up
-    (2 to 5 count blocks here) go back to the count blocks.  All of them, with alignment 128 and
-    with the fixed-capacity layout (64, 8 or 2 rows per slot, so slots overflow), give the
-    oracle's plan bit for bit."""
+    add up themselves; 8200 rows make 65 blocks and take the separate scan kernel.  Batches of
+    up to 16384 pairs use blocks of 256 pairs (1024 or 1025 rows: 32 or 33 blocks, one case
+    with an idle replica) and take the first way.  Up to 1024 pairs (128 rows) one place block
+    takes every pair and counts them itself; 129 to 513 rows make 5 to 17 blocks of 256 pairs.
+    All of them, with alignment 128 and with the fixed-capacity layout (64, 8 or 2 rows per
+    slot, so slots overflow), give the oracle's plan bit for bit."""
     cfg = replace(moe_synth.CONFIGS["cfg2"], num_tokens=tokens, hidden=256, inter=128,
                   num_experts=1024, num_local=1024, top_k=8, name=f"dispatch-{tokens[0]}")
     run_and_compare_inputs(moe_synth.make_inputs(cfg), "sum", align=align, seg_stride=stride)
