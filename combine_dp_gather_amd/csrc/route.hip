@@ -1121,8 +1121,12 @@ struct SelectArgs {
     float* w;
 };
 
+// up to 256 experts (V <= 4) the kernel fits 64 registers without spilling, and eight waves
+// per SIMD instead of six took the prefill select (32768 rows, 256 experts) from ~74 to ~65 us;
+// wider rows keep the compiler's default
 template <int V>
-__global__ __launch_bounds__(S_THREADS) void select_kernel(SelectArgs a) {
+__global__ __launch_bounds__(S_THREADS) __attribute__((amdgpu_waves_per_eu(V <= 4 ? 8 : 1)))
+void select_kernel(SelectArgs a) {
     const int lane = lane_id();
     const int64_t g = static_cast<int64_t>(blockIdx.x) * S_WAVES + threadIdx.x / kWave;
     if (g >= a.G) return;  // no block barrier below
